@@ -1,0 +1,232 @@
+"""Brute-force pin of the oracle's lazy loops (CPU only, tiny shapes).
+
+The brute force below states the lazy method with whole matrices: full K/V
+arrays per loop whose non-recomputed rows are copied from the previous loop's
+reconstruction, boolean attention masks built from the column set S and the
+window, and selection by a full Python sort.  The oracle instead uses slot
+maps, compact residual stores and per-row column lists, so a dropped term, a
+wrong index or a transposed operand in either shows up as a mismatch.
+Quantization uses the oracle's quantizer, which is pinned on its own.
+"""
+import numpy as np
+import pytest
+
+from cross_loop_kv_amd import inputs as I
+from oracle import quant
+from oracle.model import LoopedOracle
+from oracle.select import n_selected
+
+F32 = np.float32
+
+
+def _rms(x, eps=1e-5):
+    return x / np.sqrt((x.astype(np.float64) ** 2).mean(-1, keepdims=True) + eps).astype(F32)
+
+
+def _rope(x, pos, theta=10000.0):
+    hd = x.shape[-1]
+    half = hd // 2
+    f = theta ** (-np.arange(half) * 2.0 / hd)
+    a = np.outer(pos, f)
+    c, s = np.cos(a)[:, None, :], np.sin(a)[:, None, :]
+    x1, x2 = x[..., :half].astype(np.float64), x[..., half:].astype(np.float64)
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], -1).astype(F32)
+
+
+def _ffn(Wl, x, act):
+    b = _rms(x)
+    if act == "swiglu":
+        g = b @ Wl["w_gate"].T
+        return x + ((g / (1 + np.exp(-g))) * (b @ Wl["w_up"].T)) @ Wl["w_down"].T
+    from scipy.special import erf
+    u = b @ Wl["w_up"].T
+    return x + (0.5 * u * (1 + erf(u / np.sqrt(2)))) @ Wl["w_down"].T
+
+
+def _masked_attn(q, Kf, Vf, mask):
+    """q [n, H, hd], Kf/Vf [T, Hkv, hd], mask [Hkv, n, T] bool."""
+    n, H, hd = q.shape
+    Hkv = Kf.shape[1]
+    G = H // Hkv
+    o = np.zeros((n, H, hd), np.float64)
+    for h in range(H):
+        g = h // G
+        sc = (q[:, h].astype(np.float64) @ Kf[:, g].T.astype(np.float64)) / np.sqrt(hd)
+        sc = np.where(mask[g], sc, -np.inf)
+        p = np.exp(sc - sc.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        o[:, h] = p @ Vf[:, g].astype(np.float64)
+    return o.astype(F32), None
+
+
+def _store(x, prev, bits, group=32):
+    """New stored value of rows ``x`` given the previous reconstruction ``prev``."""
+    if bits == 16:
+        return x.copy()
+    c, s = quant.quantize(x - prev, bits, group)
+    return prev + quant.dequantize(c, s, group)
+
+
+def brute_lazy(shape, lz, W, ids, dec):
+    """One sequence: returns (prefill output [T, d], decode outputs [steps, d], sel, S)."""
+    P, R, K, Q = shape.n_prelude, shape.n_shared, shape.n_loops, shape.n_coda
+    Hkv, hd, H = shape.n_kv_heads, shape.head_dim, shape.n_heads
+    L = W["layers"]
+    T = len(ids)
+    full_ids = np.concatenate([ids, dec])
+
+    def proj(li, x, pos):
+        a = _rms(x) * L[li]["attn_norm"]
+        q = (a @ L[li]["wq"].T).reshape(len(x), H, hd)
+        k = (a @ L[li]["wk"].T).reshape(len(x), Hkv, hd)
+        v = (a @ L[li]["wv"].T).reshape(len(x), Hkv, hd)
+        return _rope(q, pos), _rope(k, pos), v.astype(F32)
+
+    def out_ffn(li, x, o):
+        x = x + o.reshape(len(x), -1) @ L[li]["wo"].T
+        return _ffn(L[li], x, shape.ffn_act).astype(F32)
+
+    def dense_layer(li, x):
+        """Causal layer over the whole sequence x [N, d] (prelude/coda/dense)."""
+        N = len(x)
+        q, k, v = proj(li, x, np.arange(N))
+        m = np.tril(np.ones((N, N), bool))[None].repeat(Hkv, 0)
+        return out_ffn(li, x, _masked_attn(q, k, v, m)[0])
+
+    # prelude over prompt + decode tokens at once (causal, so prefix-consistent)
+    h = W["tok_emb"][full_ids].astype(F32)
+    for li in range(P):
+        h = dense_layer(li, h)
+    N = len(full_ids)
+    h0 = h
+    # ---- prompt: loop 1 dense with base quantization and column mass
+    x = h0[:T] + W["loop_emb"][0]
+    recon = {}
+    S = {}
+    for r in range(R):
+        li = P + r
+        q, k, v = proj(li, x, np.arange(T))
+        kb = _store(k, np.zeros_like(k), lz.base_bits if lz.base_bits != 16 else 16)
+        vb = _store(v, np.zeros_like(v), lz.base_bits if lz.base_bits != 16 else 16)
+        m = np.tril(np.ones((T, T), bool))[None].repeat(Hkv, 0)
+        o, _ = _masked_attn(q, kb, vb, m)
+        # mass: probabilities summed over queries and the heads of each group
+        G = H // Hkv
+        S[r] = []
+        for g in range(Hkv):
+            tot = np.zeros(T)
+            for h_ in range(g * G, (g + 1) * G):
+                sc = (q[:, h_].astype(np.float64) @ kb[:, g].T.astype(np.float64)) / np.sqrt(hd)
+                sc = np.where(m[0], sc, -np.inf)
+                p = np.exp(sc - sc.max(1, keepdims=True))
+                p /= p.sum(1, keepdims=True)
+                tot += p.sum(0)
+            if T <= lz.top_s:
+                S[r].append(list(range(T)))
+            else:
+                S[r].append(sorted(sorted(range(T), key=lambda j: (-tot[j], j))[: lz.top_s]))
+        recon[(1, r)] = (kb, vb)
+        x = out_ffn(li, x, o)
+    hist = [h0[:T], x]
+    n = n_selected(lz.rho, T)
+    sel = {}
+    for kk in range(2, K + 1):
+        key = ((hist[-1].astype(np.float64) - hist[-2]) ** 2).sum(-1)
+        Ik = sorted(sorted(range(T), key=lambda i: (-key[i], i))[:n])
+        sel[kk] = Ik
+        xs = hist[-1][Ik] + W["loop_emb"][kk - 1]
+        for r in range(R):
+            li = P + r
+            q, k, v = proj(li, xs, np.array(Ik))
+            kp, vp = recon[(kk - 1, r)]
+            kr, vr = kp.copy(), vp.copy()
+            kr[Ik] = _store(k, kp[Ik], lz.res_bits)
+            vr[Ik] = _store(v, vp[Ik], lz.res_bits)
+            recon[(kk, r)] = (kr, vr)
+            mask = np.zeros((Hkv, n, T), bool)
+            for g in range(Hkv):
+                for a, i in enumerate(Ik):
+                    for j in range(T):
+                        mask[g, a, j] = j <= i and (j in S[r][g] or j > i - lz.window)
+            o, _ = _masked_attn(q, kr, vr, mask)
+            xs = out_ffn(li, xs, o)
+        hn = hist[-1].copy()
+        hn[Ik] = xs
+        hist.append(hn)
+    hK = hist[-1]
+    # ---- decode tokens, one at a time, all loops
+    dec_out = []
+    full_recon = {key_: (np.concatenate([a, np.zeros((N - T,) + a.shape[1:], F32)]),
+                         np.concatenate([b, np.zeros((N - T,) + b.shape[1:], F32)]))
+                  for key_, (a, b) in recon.items()}
+    hdec = []
+    for t in range(T, N):
+        x = h0[t:t + 1]
+        for kk in range(1, K + 1):
+            x = x + W["loop_emb"][kk - 1]
+            for r in range(R):
+                li = P + r
+                q, k, v = proj(li, x, np.array([t]))
+                kc, vc = full_recon[(kk, r)]
+                if kk == 1:
+                    bits, kp, vp = lz.base_bits, np.zeros_like(k), np.zeros_like(v)
+                else:
+                    bits, kp, vp = lz.res_bits, full_recon[(kk - 1, r)][0][t:t + 1], \
+                        full_recon[(kk - 1, r)][1][t:t + 1]
+                kc[t] = _store(k, kp, bits)[0]
+                vc[t] = _store(v, vp, bits)[0]
+                mask = np.zeros((Hkv, 1, N), bool)
+                for g in range(Hkv):
+                    for j in range(t + 1):
+                        mask[g, 0, j] = kk == 1 or (j in S[r][g] or j > t - lz.window)
+                o, _ = _masked_attn(q, kc, vc, mask)
+                x = out_ffn(li, x, o)
+        hdec.append(x[0])
+    # coda over [prompt rows after the loops ; decode rows] causally
+    hc = np.concatenate([hK, np.array(hdec).reshape(-1, hK.shape[1])]) if hdec else hK
+    for j in range(Q):
+        hc = dense_layer(P + R + j, hc)
+    outn = _rms(hc) * W["final_norm"]
+    return outn[:T], outn[T:], sel, S
+
+
+CASES = [
+    ("tiny", dict(), I.Lazy(mode="lazy", rho=0.5, top_s=8, window=4, base_bits=16, res_bits=8)),
+    ("gqa_int4_int8base", dict(n_heads=4, n_kv_heads=2, ffn_act="swiglu", n_loops=3),
+     I.Lazy(mode="lazy", rho=0.3, top_s=6, window=3, base_bits=8, res_bits=4)),
+    ("gqa_res16", dict(n_heads=4, n_kv_heads=1, ffn_act="swiglu", n_loops=3, n_prelude=0),
+     I.Lazy(mode="lazy", rho=0.25, top_s=5, window=2, base_bits=16, res_bits=16)),
+]
+
+
+@pytest.mark.parametrize("name,kw,lz", CASES, ids=[c[0] for c in CASES])
+def test_lazy_oracle_matches_brute_force(name, kw, lz):
+    s = I.workload("tiny_1p2x2c1_t32").shape
+    for k, v in kw.items():
+        setattr(s, k, v)
+    W = I.gen_weights(s, seed=21)
+    W["loop_emb"] *= np.float32(20.0)
+    T, steps, B = 28, 3, 2
+    ids = I.gen_prompt_ids(s, B, T, seed=22)
+    dec = I.gen_decode_ids(s, B, steps, seed=23)
+    m = LoopedOracle(s, lz, W, B, T + steps)
+    out = m.prefill(ids)
+    douts = np.stack([m.decode(d) for d in dec], 1)     # [B, steps, d]
+    for b in range(B):
+        ref, dref, sel, S = brute_lazy(s, lz, W, ids[b], dec[:, b])
+        for k_, Ik in sel.items():
+            assert list(m.sel[(k_, b)]) == Ik
+        for r in range(s.n_shared):
+            for g in range(s.n_kv_heads):
+                assert list(m.S[r][b][g]) == list(S[r][g])
+        scale = np.max(np.abs(ref))
+        assert np.max(np.abs(out[b] - ref)) / scale < 1e-4
+        assert np.max(np.abs(douts[b] - dref)) / np.max(np.abs(dref)) < 1e-4
+        # carried rows: only the kept rows of loop 2 may differ from the loop-1 state
+        assert len(sel[2]) == n_selected(lz.rho, T)
+    # the slot maps hold exactly the kept prompt rows plus every decode token
+    for k_ in range(2, s.n_loops + 1):
+        for b in range(B):
+            stored = np.nonzero(m.slot[k_ - 1, b] >= 0)[0]
+            exp = sorted(list(m.sel[(k_, b)]) + list(range(T, T + steps)))
+            assert list(stored) == exp
