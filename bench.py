@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Lazy looped-Transformer decode benchmark on one MI355X.
+
+Workload (default): 48 shared layers x 4 loops (192 layer applications per
+token), d_model 2048, 16 query / 4 KV heads of 128, SwiGLU FFN 5632, batch 8,
+32768-token seeded random prompt; lazy cache with rho 0.1, 1024 stable columns
++ 512-token window, int8 base and int4 residuals (group 32, float16 scales).
+Weights are seeded N(0, 0.02) rounded to bf16; data is synthetic.
+
+A step is one decode step: every sequence appends one token that runs the whole
+looped stack through the library's C ABI.  The prompt is prefilled once (timed
+separately).  Prints one JSON line with decode tokens/s, KV bytes per token, the
+roofline of the dominant kernel (decode attention over the base KV, timed live
+with HIP events on the library's stream) and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+import argparse
+import copy
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "looped-decode tokens/s + KV bytes/token at K=4, 32k ctx; % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="deep_48x4_b8_ctx32k")
+    ap.add_argument("--mode", default=None, choices=["per_loop", "last_loop", "lazy"])
+    ap.add_argument("--prompt", type=int, default=None, help="override the prompt length")
+    ap.add_argument("--base-bits", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 2 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def decode_attention_bytes(shape, lazy, batch, t):
+    """Algorithmic bytes of one loop-1 decode-attention launch at context length t+1:
+    K and V rows of every (sequence, KV head) read once, q read, partials written."""
+    hd, Hkv, H = shape.head_dim, shape.n_kv_heads, shape.n_heads
+    if lazy.mode == "lazy" and lazy.base_bits == 8:
+        per_elem = 1.0 + 2.0 / 32
+    else:
+        per_elem = 2.0
+    kv = batch * Hkv * (t + 1) * 2 * hd * per_elem
+    return kv + batch * H * hd * 2
+
+
+def cpu_baseline(wl, rng_seed=3):
+    """The oracle on a bounded sample: one decode step of the full batch at the full
+    context through ONE shared layer x K loops, on a synthetic store state (what a
+    prefill leaves: base, kept-row residuals, slot maps, column sets), scaled to
+    the R shared layers of the workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from cross_loop_kv_amd import inputs as I
+    from oracle.model import LoopedOracle
+    from oracle.select import n_selected
+
+    s1 = copy.deepcopy(wl.shape)
+    s1.n_shared = 1
+    R_full = wl.shape.n_shared
+    W = I.gen_weights(s1)
+    B, T, lz = wl.batch, wl.prompt, wl.lazy
+    m = LoopedOracle(s1, lz, W, B, T + 1)
+    rng = np.random.default_rng(rng_seed)
+    Hkv, hd = s1.n_kv_heads, s1.head_dim
+    m.T, m.t = T, T
+    if lz.mode == "lazy":
+        m.n_sel = n_selected(lz.rho, T)
+        m._alloc_residuals(m.n_sel + 1)
+        for kv in range(2):
+            if lz.base_bits == 16:
+                m.base[0][kv][:] = rng.standard_normal(m.base[0][kv].shape, np.float32)
+            else:
+                m.base[0][kv][0][:] = rng.integers(-127, 128, m.base[0][kv][0].shape, dtype=np.int8)
+                m.base[0][kv][1][:] = np.float16(0.01)
+        for k in range(2, s1.n_loops + 1):
+            for b in range(B):
+                idx = np.sort(rng.choice(T, m.n_sel, replace=False))
+                m.slot[k - 1, b, idx] = np.arange(m.n_sel, dtype=np.int32)
+            for kv in range(2):
+                st = m.res[(k, 0, kv)]
+                if lz.res_bits == 16:
+                    st[:] = rng.standard_normal(st.shape, np.float32)
+                else:
+                    q = 2 ** (lz.res_bits - 1) - 1
+                    st[0][:] = rng.integers(-q, q + 1, st[0].shape, dtype=np.int8)
+                    st[1][:] = np.float16(0.001)
+        ncols = min(lz.top_s, T)
+        m.S = [[[np.sort(rng.choice(T, ncols, replace=False)).astype(np.int32) for _ in range(Hkv)]
+                for _ in range(B)]]
+    else:
+        for arrs in (getattr(m, "loop_k", None), getattr(m, "last_k", None)):
+            pass
+    ids = I.gen_decode_ids(s1, B, 1)[0]
+    t0 = time.time()
+    m.decode(ids)
+    dt = time.time() - t0
+    step_s = dt * R_full
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": B / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"one decode step of batch {B} at context {T + 1} through 1 shared layer x "
+                       f"{s1.n_loops} loops ({s1.n_loops} layer applications) on a synthetic store, "
+                       f"{dt:.1f} s, scaled x{R_full} to the {R_full}-layer stack")}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the path runs on a single MI355X and has no multi-GPU "
+              "mode (sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from cross_loop_kv_amd import binding as B
+    from cross_loop_kv_amd import inputs as I
+
+    assert torch.cuda.is_available(), "needs a GPU"
+    torch.cuda.set_device(0)
+    wl = I.workload(args.workload)
+    if args.prompt:
+        wl.prompt = args.prompt
+    if args.mode:
+        wl.lazy.mode = args.mode
+    if args.base_bits:
+        wl.lazy.base_bits = args.base_bits
+    s, lz = wl.shape, wl.lazy
+    Bsz, T = wl.batch, wl.prompt
+    total_tokens = T + args.warmup + args.steps
+
+    t0 = time.time()
+    model = B.LoopedModel(s, lz, I.iter_weights(s))
+    torch.cuda.synchronize()
+    log(f"weights: {model.weight_bytes() / 1e9:.2f} GB in {time.time() - t0:.1f}s")
+    store = model.store(Bsz, T, total_tokens)
+    log(f"store: {store.need / 1e9:.2f} GB allocated for {total_tokens} tokens")
+    ids = torch.from_numpy(I.gen_prompt_ids(s, Bsz, T)).cuda()
+    dec = torch.from_numpy(I.gen_decode_ids(s, Bsz, args.warmup + args.steps)).cuda()
+    torch.cuda.synchronize()
+    t0 = time.time()
+    out = model.prefill(store, ids)
+    torch.cuda.synchronize()
+    prefill_s = time.time() - t0
+    assert torch.isfinite(out).all().item(), "non-finite prefill output"
+    del out
+    log(f"prefill {Bsz}x{T}: {prefill_s:.2f}s")
+
+    dout = torch.empty(Bsz, s.d_model, dtype=torch.float32, device="cuda")
+    for i in range(args.warmup):
+        model.decode(store, dec[i], out=dout)
+    torch.cuda.synchronize()
+    B.lk_timing_enable(model.h, "attn_decode_dense")
+    t_first = store.length()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        model.decode(store, dec[args.warmup + i], out=dout)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    launches, kern_ms = B.lk_timing_read(model.h)
+    B.lk_timing_enable(model.h, None)
+    assert torch.isfinite(dout).all().item(), "non-finite decode output"
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = Bsz * args.steps / elapsed
+
+    # roofline of the dominant kernel: loop-1 (dense) decode attention
+    per_step_launches = launches / args.steps if args.steps else 0
+    bytes_tot = sum(decode_attention_bytes(s, lz, Bsz, t_first + i) for i in range(args.steps)) \
+        * per_step_launches
+    avg_ms = kern_ms / max(launches, 1)
+    bytes_per_launch = bytes_tot / max(launches, 1)
+    achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9 if launches else 0.0
+
+    shared, total = store.bytes_used()
+    t_now = store.length()
+    kv_tok_shared = shared / (Bsz * t_now)
+    E = 2 * s.n_kv_heads * s.head_dim
+    dense_per_loop = 2 * s.n_shared * s.n_loops * E
+    if args.calibrate_copy:
+        x = torch.empty(2 ** 29, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random ids, seeded N(0,0.02) bf16 weights)",
+        "config": {"workload": args.workload, "batch": Bsz, "context": T,
+                   "shared_layers": s.n_shared, "loops": s.n_loops, "prelude": s.n_prelude,
+                   "coda": s.n_coda, "d_model": s.d_model, "heads": s.n_heads,
+                   "kv_heads": s.n_kv_heads, "ffn": s.ffn_dim, "mode": lz.mode, "rho": lz.rho,
+                   "top_s": lz.top_s, "window": lz.window, "base_bits": lz.base_bits,
+                   "res_bits": lz.res_bits, "layer_applications": model.effective_depth()},
+        "kv_bytes_per_token": round(kv_tok_shared, 1),
+        "kv_bytes_per_token_dense_per_loop": dense_per_loop,
+        "kv_reduction_vs_dense_per_loop": round(dense_per_loop / kv_tok_shared, 3),
+        "kv_bytes_total_per_token": round(total / (Bsz * t_now), 1),
+        "prefill_s": round(prefill_s, 3),
+        "prefill_tokens_per_s": round(Bsz * T / prefill_s, 1),
+        "roofline": {"kernel": "attn_rows_kernel (decode attention over the loop-1 base)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launches": launches, "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": int(bytes_per_launch),
+                     "share_of_step": round(kern_ms / (elapsed * 1e3), 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle sample)...")
+        res["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,378 @@
+"""ctypes binding of ``liblooped_kv.so`` (the C ABI in include/looped_kv.h).
+
+Argument marshalling only: every step of the computation runs in the library's
+HIP kernels.  PyTorch provides device memory (``tensor.data_ptr()``) and the
+stream.  If the library is missing this module raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, Iterable, Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblooped_kv.so")
+
+LK_OK = 0
+LK_ERR = {-1: "LK_ERR_INVALID_ARG", -2: "LK_ERR_UNSUPPORTED", -3: "LK_ERR_CAPACITY",
+          -4: "LK_ERR_HIP", -5: "LK_ERR_STATE"}
+MODES = {"per_loop": 0, "last_loop": 1, "lazy": 2}
+ACTS = {"gelu": 0, "swiglu": 1}
+
+
+class LKError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{LK_ERR.get(code, code)}: {msg}")
+        self.code = code
+
+
+class lk_model_cfg(C.Structure):
+    _fields_ = [("vocab", C.c_int32), ("d_model", C.c_int32), ("n_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn_dim", C.c_int32),
+                ("ffn_act", C.c_int32), ("n_prelude", C.c_int32), ("n_shared", C.c_int32),
+                ("n_loops", C.c_int32), ("n_coda", C.c_int32), ("rms_eps", C.c_float),
+                ("rope_theta", C.c_float)]
+
+
+class lk_lazy_cfg(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("rho", C.c_double), ("top_s", C.c_int32),
+                ("window", C.c_int32), ("base_bits", C.c_int32), ("res_bits", C.c_int32),
+                ("group", C.c_int32)]
+
+
+class lk_layer_weights(C.Structure):
+    _fields_ = [("attn_norm", C.c_void_p), ("wqkv", C.c_void_p), ("wo", C.c_void_p),
+                ("ffn_norm", C.c_void_p), ("w_in", C.c_void_p), ("w_down", C.c_void_p)]
+
+
+class lk_weights(C.Structure):
+    _fields_ = [("tok_emb", C.c_void_p), ("loop_emb", C.c_void_p), ("final_norm", C.c_void_p),
+                ("layers", C.POINTER(lk_layer_weights))]
+
+
+class lk_store_view(C.Structure):
+    _fields_ = [("dense", C.c_void_p), ("loop_rows", C.c_void_p), ("base_codes", C.c_void_p),
+                ("base_scales", C.c_void_p), ("res_codes", C.c_void_p), ("res_scales", C.c_void_p),
+                ("slot_maps", C.c_void_p), ("columns", C.c_void_p), ("slots", C.c_int64),
+                ("n_selected", C.c_int32), ("n_columns", C.c_int32), ("res_row_bytes", C.c_int64)]
+
+
+_SIGS = {
+    "lk_create": (C.c_int, [C.POINTER(lk_model_cfg), C.POINTER(lk_lazy_cfg), C.POINTER(lk_weights),
+                            C.POINTER(C.c_void_p)]),
+    "lk_destroy": (None, [C.c_void_p]),
+    "lk_kv_store_alloc": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                    C.c_size_t, C.c_void_p, C.POINTER(C.c_void_p),
+                                    C.POINTER(C.c_size_t)]),
+    "lk_kv_store_release": (None, [C.c_void_p]),
+    "lk_kv_store_bytes_used": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
+    "lk_kv_store_length": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32)]),
+    "lk_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.POINTER(C.c_size_t)]),
+    "lk_looped_prefill": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                                    C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "lk_looped_decode_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                        C.c_size_t, C.c_void_p]),
+    "lk_effective_depth": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32)]),
+    "lk_last_error": (C.c_char_p, []),
+    "lk_kv_store_view": (C.c_int, [C.c_void_p, C.POINTER(lk_store_view)]),
+    "lk_kv_store_force_selection": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
+    "lk_timing_enable": (C.c_int, [C.c_void_p, C.c_char_p]),
+    "lk_timing_read": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
+    "lk_dbg_topk": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
+    "lk_dbg_quantize": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                  C.c_void_p, C.c_void_p]),
+    "lk_dbg_delta": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
+    "lk_dbg_gemm": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
+                              C.c_void_p]),
+}
+
+EXPORTED = tuple(_SIGS)
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load the in-tree library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with python -m cross_loop_kv_amd.build")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(code: int) -> None:
+    if code != LK_OK:
+        raise LKError(code, lib().lk_last_error().decode())
+
+
+def _stream(stream=None) -> Optional[int]:
+    """The caller's stream, or torch's current stream (None = the null stream)."""
+    if stream is None:
+        import torch
+        if not torch.cuda.is_available():
+            return None
+        return torch.cuda.current_stream().cuda_stream or None
+    return stream
+
+
+# ---- same-name wrappers ----------------------------------------------------------
+def lk_create(cfg: lk_model_cfg, lazy: lk_lazy_cfg, weights: lk_weights) -> int:
+    h = C.c_void_p()
+    _check(lib().lk_create(C.byref(cfg), C.byref(lazy), C.byref(weights), C.byref(h)))
+    return h.value
+
+
+def lk_destroy(h: int) -> None:
+    lib().lk_destroy(h)
+
+
+def lk_kv_store_alloc(h, batch, prompt_tokens, max_tokens, dev_buf=None, buf_bytes=0, stream=None):
+    """Returns (store handle or None, need_bytes)."""
+    need = C.c_size_t()
+    out = C.c_void_p()
+    _check(lib().lk_kv_store_alloc(h, batch, prompt_tokens, max_tokens, dev_buf, buf_bytes,
+                                   _stream(stream) if dev_buf else None, C.byref(out), C.byref(need)))
+    return (out.value if dev_buf else None), need.value
+
+
+def lk_kv_store_release(s: int) -> None:
+    lib().lk_kv_store_release(s)
+
+
+def lk_kv_store_bytes_used(s: int) -> Tuple[int, int]:
+    a, b = C.c_size_t(), C.c_size_t()
+    _check(lib().lk_kv_store_bytes_used(s, C.byref(a), C.byref(b)))
+    return a.value, b.value
+
+
+def lk_kv_store_length(s: int) -> int:
+    t = C.c_int32()
+    _check(lib().lk_kv_store_length(s, C.byref(t)))
+    return t.value
+
+
+def lk_workspace_bytes(h: int, batch: int, tokens: int) -> int:
+    n = C.c_size_t()
+    _check(lib().lk_workspace_bytes(h, batch, tokens, C.byref(n)))
+    return n.value
+
+
+def lk_looped_prefill(h, s, d_ids, B, T, d_out, d_ws, ws_bytes, stream=None) -> None:
+    _check(lib().lk_looped_prefill(h, s, d_ids, B, T, d_out, d_ws, ws_bytes, _stream(stream)))
+
+
+def lk_looped_decode_step(h, s, d_ids, d_out, d_ws, ws_bytes, stream=None) -> None:
+    _check(lib().lk_looped_decode_step(h, s, d_ids, d_out, d_ws, ws_bytes, _stream(stream)))
+
+
+def lk_effective_depth(h: int) -> int:
+    d = C.c_int32()
+    _check(lib().lk_effective_depth(h, C.byref(d)))
+    return d.value
+
+
+def lk_kv_store_view(s: int) -> lk_store_view:
+    v = lk_store_view()
+    _check(lib().lk_kv_store_view(s, C.byref(v)))
+    return v
+
+
+def lk_kv_store_force_selection(s: int, d_tokens, d_columns) -> None:
+    _check(lib().lk_kv_store_force_selection(s, d_tokens, d_columns))
+
+
+def lk_timing_enable(h: int, kernel_class: Optional[str]) -> None:
+    _check(lib().lk_timing_enable(h, kernel_class.encode() if kernel_class else None))
+
+
+def lk_timing_read(h: int) -> Tuple[int, float]:
+    n, ms = C.c_int32(), C.c_double()
+    _check(lib().lk_timing_read(h, C.byref(n), C.byref(ms)))
+    return n.value, ms.value
+
+
+def lk_dbg_topk(d_keys, rows, cols, n, d_idx, stream=None) -> None:
+    _check(lib().lk_dbg_topk(d_keys, rows, cols, n, d_idx, _stream(stream)))
+
+
+def lk_dbg_quantize(d_x, rows, hd, bits, d_codes, d_scales, stream=None) -> None:
+    _check(lib().lk_dbg_quantize(d_x, rows, hd, bits, d_codes, d_scales, _stream(stream)))
+
+
+def lk_dbg_delta(d_a, d_b, rows, d, d_key, stream=None) -> None:
+    _check(lib().lk_dbg_delta(d_a, d_b, rows, d, d_key, _stream(stream)))
+
+
+def lk_dbg_gemm(d_a, d_w, d_c, M, N, K, stream=None) -> None:
+    _check(lib().lk_dbg_gemm(d_a, d_w, d_c, M, N, K, _stream(stream)))
+
+
+# ---- model / store objects (device memory from torch) ----------------------------------
+def model_cfg(shape) -> lk_model_cfg:
+    return lk_model_cfg(shape.vocab, shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim,
+                        shape.ffn_dim, ACTS[shape.ffn_act], shape.n_prelude, shape.n_shared,
+                        shape.n_loops, shape.n_coda, shape.rms_eps, shape.rope_theta)
+
+
+def lazy_cfg(lz) -> lk_lazy_cfg:
+    return lk_lazy_cfg(MODES[lz.mode], float(lz.rho), int(lz.top_s), int(lz.window),
+                       int(lz.base_bits), int(lz.res_bits), int(lz.group))
+
+
+def _aligned_bytes(nbytes: int, device):
+    """A torch uint8 buffer of at least nbytes whose data pointer is 256-byte aligned."""
+    import torch
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf, buf[off:off + nbytes]
+
+
+class Store:
+    def __init__(self, model: "LoopedModel", batch: int, prompt: int, max_tokens: int):
+        self.model = model
+        self.batch, self.prompt, self.max_tokens = batch, prompt, max_tokens
+        _, need = lk_kv_store_alloc(model.h, batch, prompt, max_tokens)
+        self._raw, self.buf = _aligned_bytes(max(need, 256), model.device)
+        self.need = need
+        self.s, _ = lk_kv_store_alloc(model.h, batch, prompt, max_tokens, self.buf.data_ptr(), need)
+
+    def view(self) -> lk_store_view:
+        return lk_kv_store_view(self.s)
+
+    def bytes_used(self) -> Tuple[int, int]:
+        return lk_kv_store_bytes_used(self.s)
+
+    def length(self) -> int:
+        return lk_kv_store_length(self.s)
+
+    def force_selection(self, tokens=None, columns=None):
+        """tokens: int32 cuda [K-1, B, n]; columns: int32 cuda [R, B, Hkv, n_cols] (or None)."""
+        self._forced = (tokens, columns)
+        lk_kv_store_force_selection(self.s, tokens.data_ptr() if tokens is not None else None,
+                                    columns.data_ptr() if columns is not None else None)
+
+    def close(self):
+        if getattr(self, "s", None):
+            lk_kv_store_release(self.s)
+            self.s = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class LoopedModel:
+    """Weights on the GPU in the library's packed bf16 layout plus a handle."""
+
+    def __init__(self, shape, lazy, weights: Iterable, device: str = "cuda"):
+        import torch
+        self.shape, self.lazy, self.device = shape, lazy, device
+        bf = torch.bfloat16
+
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=torch.float32).to(bf)
+
+        self.t: Dict = {}
+        layers: Dict[int, Dict] = {}
+        items = weights.items() if isinstance(weights, dict) else None
+        if items is not None and "layers" in weights:
+            self.t["tok_emb"] = dev(weights["tok_emb"])
+            self.t["loop_emb"] = dev(weights["loop_emb"])
+            self.t["final_norm"] = dev(weights["final_norm"])
+            src_layers = list(enumerate(weights["layers"]))
+        else:
+            src_layers = []
+            ones = np.ones(shape.d_model, np.float32)
+            for name, li, arr in weights:
+                if li < 0:
+                    self.t[name] = dev(arr)
+                else:
+                    layers.setdefault(li, {"attn_norm": ones, "ffn_norm": ones})[name] = arr
+                    if name == "w_down":
+                        src_layers.append((li, layers.pop(li)))
+            self.t["final_norm"] = dev(ones)
+        self.layers = []
+        for li, L in src_layers:
+            packed = {
+                "attn_norm": dev(L["attn_norm"]), "ffn_norm": dev(L["ffn_norm"]),
+                "wqkv": torch.cat([dev(L["wq"]), dev(L["wk"]), dev(L["wv"])], 0).contiguous(),
+                "wo": dev(L["wo"]),
+                "w_in": (torch.cat([dev(L["w_gate"]), dev(L["w_up"])], 0).contiguous()
+                         if shape.ffn_act == "swiglu" else dev(L["w_up"])),
+                "w_down": dev(L["w_down"]),
+            }
+            self.layers.append(packed)
+        n = len(self.layers)
+        assert n == shape.n_prelude + shape.n_shared + shape.n_coda, "layer count mismatch"
+        self._lw = (lk_layer_weights * n)()
+        for i, L in enumerate(self.layers):
+            self._lw[i] = lk_layer_weights(L["attn_norm"].data_ptr(), L["wqkv"].data_ptr(),
+                                           L["wo"].data_ptr(), L["ffn_norm"].data_ptr(),
+                                           L["w_in"].data_ptr(), L["w_down"].data_ptr())
+        self._w = lk_weights(self.t["tok_emb"].data_ptr(), self.t["loop_emb"].data_ptr(),
+                             self.t["final_norm"].data_ptr(), self._lw)
+        self._cfg = model_cfg(shape)
+        self._lz = lazy_cfg(lazy)
+        self.h = lk_create(self._cfg, self._lz, self._w)
+        self._ws = None
+        self._ws_bytes = 0
+
+    def weight_bytes(self) -> int:
+        tot = sum(t.numel() * t.element_size() for t in self.t.values())
+        for L in self.layers:
+            tot += sum(t.numel() * t.element_size() for t in L.values())
+        return tot
+
+    def effective_depth(self) -> int:
+        return lk_effective_depth(self.h)
+
+    def workspace(self, batch: int, tokens: int):
+        need = lk_workspace_bytes(self.h, batch, tokens)
+        if self._ws is None or self._ws_bytes < need:
+            self._ws = None
+            self._ws_raw, self._ws = _aligned_bytes(need, self.device)
+            self._ws_bytes = need
+        return self._ws, need
+
+    def store(self, batch: int, prompt: int, max_tokens: int) -> Store:
+        return Store(self, batch, prompt, max_tokens)
+
+    def prefill(self, store: Store, ids, out=None):
+        import torch
+        B, T = ids.shape
+        ids = ids.to(device=self.device, dtype=torch.int32).contiguous()
+        if out is None:
+            out = torch.empty(B, T, self.shape.d_model, dtype=torch.float32, device=self.device)
+        ws, nbytes = self.workspace(B, T)
+        lk_looped_prefill(self.h, store.s, ids.data_ptr(), B, T, out.data_ptr(), ws.data_ptr(), nbytes)
+        return out
+
+    def decode(self, store: Store, ids, out=None):
+        import torch
+        ids = ids.to(device=self.device, dtype=torch.int32).contiguous().view(-1)
+        B = ids.shape[0]
+        if out is None:
+            out = torch.empty(B, self.shape.d_model, dtype=torch.float32, device=self.device)
+        ws, nbytes = self.workspace(B, 1)
+        lk_looped_decode_step(self.h, store.s, ids.data_ptr(), out.data_ptr(), ws.data_ptr(), nbytes)
+        return out
+
+    def close(self):
+        if getattr(self, "h", None):
+            lk_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,401 @@
+// Elementwise, selection and KV-store-write kernels for gfx950.
+//
+// Token-sparse update and residual quantization follow the FlashLoop abstract
+// (arxivdaily.com, "FlashLoop: Fast and Memory-Efficient Looped Transformers
+// via Lazy Updates"); the loop embedding and RoPE follow the FlashLoop
+// walk-through (discosf.com, section 3.2).
+#include "lk_kernels.h"
+
+namespace lk {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void embed_kernel(const int32_t* ids, const u16* tok, float* h,
+                                                         int d, int vocab) {
+    const int r = blockIdx.x;
+    const int id = min(max(ids[r], 0), vocab - 1);  // out-of-range ids read row 0 / vocab-1
+    const long long src = (long long)id * d;
+    float* dst = h + (long long)r * d;
+    for (int j = threadIdx.x; j < d; j += kThreads) dst[j] = bf2f(tok[src + j]);
+}
+
+__global__ __launch_bounds__(kThreads) void rmsnorm_kernel(float* x, const u16* add, const u16* gain,
+                                                           float eps, int d, u16* out_bf,
+                                                           float* out_f32) {
+    __shared__ float red[16];
+    const int r = blockIdx.x;
+    float* row = x + (long long)r * d;
+    float ss = 0.f;
+    for (int j = threadIdx.x; j < d; j += kThreads) {
+        float v = row[j];
+        if (add) {
+            v = v + bf2f(add[j]);
+            row[j] = v;
+        }
+        ss += v * v;
+    }
+    ss = block_sum(ss, red);
+    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+    for (int j = threadIdx.x; j < d; j += kThreads) {
+        const float y = (row[j] * inv) * bf2f(gain[j]);
+        if (out_bf) out_bf[(long long)r * d + j] = f2bf(y);
+        else out_f32[(long long)r * d + j] = y;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void add_rows_kernel(float* x, const u16* add, int d) {
+    float* row = x + (long long)blockIdx.x * d;
+    for (int j = threadIdx.x; j < d; j += kThreads) row[j] = row[j] + bf2f(add[j]);
+}
+
+__global__ void copy_f32_kernel(const float* s, float* d, long long n) {
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+         i += (long long)gridDim.x * blockDim.x)
+        d[i] = s[i];
+}
+__global__ void fill_i32_kernel(int32_t* p, int32_t v, long long n) {
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+         i += (long long)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+__global__ void fill_f32_kernel(float* p, float v, long long n) {
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+         i += (long long)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+__global__ __launch_bounds__(kThreads) void delta_kernel(const float* a, const float* b, int d,
+                                                         float* key) {
+    __shared__ float red[16];
+    const long long off = (long long)blockIdx.x * d;
+    float s = 0.f;
+    for (int j = threadIdx.x; j < d; j += kThreads) {
+        const float t = a[off + j] - b[off + j];
+        s += t * t;
+    }
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) key[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(kThreads) void gather_kernel(const float* h, const int32_t* idx, int n,
+                                                          int T, int d, const u16* add, float* xc,
+                                                          int32_t* slot_map, int Tmax) {
+    const int r = blockIdx.x;  // compact row b*n + j
+    const int b = r / n, j = r % n;
+    const int i = idx[r];
+    const float* src = h + ((long long)b * T + i) * d;
+    float* dst = xc + (long long)r * d;
+    for (int c = threadIdx.x; c < d; c += kThreads) dst[c] = src[c] + (add ? bf2f(add[c]) : 0.f);
+    if (slot_map && threadIdx.x == 0) slot_map[(long long)b * Tmax + i] = j;
+}
+
+__global__ __launch_bounds__(kThreads) void scatter_kernel(const float* xc, const int32_t* idx, int n,
+                                                           int T, int d, float* h, float* key) {
+    __shared__ float red[16];
+    const int r = blockIdx.x;
+    const int b = r / n;
+    const int i = idx[r];
+    float* dst = h + ((long long)b * T + i) * d;
+    const float* src = xc + (long long)r * d;
+    float s = 0.f;
+    for (int c = threadIdx.x; c < d; c += kThreads) {
+        const float t = src[c] - dst[c];
+        s += t * t;
+    }
+    if (key) {
+        s = block_sum(s, red);
+        if (threadIdx.x == 0) key[(long long)b * T + i] = s;
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < d; c += kThreads) dst[c] = src[c];
+}
+
+// ---------------------------------------------------------------- top-n selector
+// Order-preserving map of a finite float to uint32 (larger float -> larger key);
+// -0 is mapped like +0 so that equal floats give equal keys.
+__device__ __forceinline__ uint32_t ord_key(float f) {
+    if (f == 0.f) f = 0.f;
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive block scan of one int per thread (256 threads); *total = block sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    __syncthreads();
+    if (lane == 63) sh[w] = x;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) {
+        if (i < w) off += sh[i];
+        tot += sh[i];
+    }
+    *total = tot;
+    return off + x - v;
+}
+
+// Radix select of the n-th largest key, then an index-ordered compaction that keeps
+// every key above it and the lowest-index ties: the result equals a stable sort by
+// (key descending, index ascending) cut at n, listed in ascending index order.
+__global__ __launch_bounds__(kThreads) void topk_kernel(const float* keys, int cols, int n, int32_t* out) {
+    __shared__ int hist[256];
+    __shared__ int sh[8];
+    __shared__ uint32_t s_prefix;
+    __shared__ int s_need;
+    const int row = blockIdx.x;
+    const float* k = keys + (long long)row * cols;
+    int32_t* o = out + (long long)row * n;
+    uint32_t prefix = 0, mask = 0;
+    int need = n;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = threadIdx.x; i < 256; i += kThreads) hist[i] = 0;
+        __syncthreads();
+        for (int i = threadIdx.x; i < cols; i += kThreads) {
+            const uint32_t u = ord_key(k[i]);
+            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int cum = 0, dsel = 0;
+            for (int dg = 255; dg >= 0; --dg) {
+                if (cum + hist[dg] >= need) {
+                    dsel = dg;
+                    break;
+                }
+                cum += hist[dg];
+            }
+            s_prefix = prefix | ((uint32_t)dsel << shift);
+            s_need = need - cum;
+        }
+        __syncthreads();
+        prefix = s_prefix;
+        need = s_need;
+        mask |= 255u << shift;
+        __syncthreads();
+    }
+    const uint32_t tau = prefix;  // n-th largest key; `need` ties of it are kept
+    int taken = 0, eq_seen = 0;
+    for (int c0 = 0; c0 < cols; c0 += kThreads) {
+        const int i = c0 + threadIdx.x;
+        uint32_t u = 0;
+        if (i < cols) u = ord_key(k[i]);
+        const int gt = (i < cols) && (u > tau);
+        const int eq = (i < cols) && (u == tau);
+        int eq_tot, take_tot;
+        const int eq_rank = block_excl_scan(eq, sh, &eq_tot) + eq_seen;
+        const int take = gt || (eq && eq_rank < need);
+        const int p = block_excl_scan(take, sh + 4, &take_tot) + taken;
+        if (take && p < n) o[p] = i;
+        taken += take_tot;
+        eq_seen += eq_tot;
+    }
+}
+
+// ---------------------------------------------------------------- quantizer (test entry)
+__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const float* x, long long groups,
+                                                                 int hd, int bits, uint8_t* codes,
+                                                                 u16* scales) {
+    const long long gi = (long long)blockIdx.x * (kThreads / 32) + (threadIdx.x >> 5);
+    if (gi >= groups) return;  // whole 32-lane groups leave together
+    const int lane = threadIdx.x & 31;
+    const int gpr = hd / 32;
+    const long long row = gi / gpr;
+    const int e = (int)(gi % gpr) * 32 + lane;
+    const float r = x[row * hd + e];
+    u16 sb;
+    const int qmax = (1 << (bits - 1)) - 1;
+    const int c = quant_group32(r, qmax, &sb);
+    if (lane == 0) scales[gi] = sb;
+    if (bits == 8) {
+        codes[row * hd + e] = (uint8_t)(int8_t)c;
+    } else {
+        const int other = __shfl_xor(c, 1);
+        if ((lane & 1) == 0)
+            codes[row * (hd / 2) + e / 2] = (uint8_t)((c & 0xF) | ((other & 0xF) << 4));
+    }
+}
+
+// ---------------------------------------------------------------- RoPE + KV write
+}  // namespace
+
+// RoPE angles: inv_freq (float64) is passed by value.
+struct InvFreq {
+    double v[64];
+};
+
+namespace {
+
+__global__ __launch_bounds__(kThreads) void rope_kv_write_kernel(const float* qkv, int rows_per_seq,
+                                                                 const int32_t* pos_arr, int pos_offset,
+                                                                 int H, int Hkv,
+                                                                 int hd, InvFreq inv, u16* q_out,
+                                                                 KVWrite w) {
+    __shared__ float cs[64], sn[64];
+    __shared__ float kvbuf[2 * 32 * 128];  // 2 * Hkv * hd <= 8192
+    const int r = blockIdx.x;
+    const int b = r / rows_per_seq;
+    const int iseq = r % rows_per_seq;
+    const int pos = pos_arr ? pos_arr[r] : pos_offset + iseq;
+    const int half = hd / 2;
+    const int width = (H + 2 * Hkv) * hd;
+    const float* src = qkv + (long long)r * width;
+    for (int i = threadIdx.x; i < half; i += kThreads) {
+        double s, c;
+        sincos((double)pos * inv.v[i], &s, &c);
+        cs[i] = (float)c;
+        sn[i] = (float)s;
+    }
+    __syncthreads();
+    // q heads
+    for (int idx = threadIdx.x; idx < H * half; idx += kThreads) {
+        const int hh = idx / half, i = idx % half;
+        const float x1 = src[hh * hd + i], x2 = src[hh * hd + i + half];
+        u16* dq = q_out + (long long)r * H * hd + hh * hd;
+        dq[i] = f2bf(x1 * cs[i] - x2 * sn[i]);
+        dq[i + half] = f2bf(x2 * cs[i] + x1 * sn[i]);
+    }
+    // k heads (roped) and v heads into LDS
+    for (int idx = threadIdx.x; idx < Hkv * half; idx += kThreads) {
+        const int g = idx / half, i = idx % half;
+        const float x1 = src[(H + g) * hd + i], x2 = src[(H + g) * hd + i + half];
+        kvbuf[g * hd + i] = x1 * cs[i] - x2 * sn[i];
+        kvbuf[g * hd + i + half] = x2 * cs[i] + x1 * sn[i];
+    }
+    for (int idx = threadIdx.x; idx < Hkv * hd; idx += kThreads)
+        kvbuf[Hkv * hd + idx] = src[(H + Hkv) * hd + idx];
+    __syncthreads();
+    const KVLayer& L = w.layer;
+    const int total = 2 * Hkv * hd;  // multiple of 64
+    const long long slot = w.slot_base + iseq;
+    for (int e0 = 0; e0 < total; e0 += kThreads) {
+        const int lin = e0 + threadIdx.x;
+        if (lin >= total) break;  // whole waves leave together (total % 64 == 0)
+        const int kv = lin / (Hkv * hd);
+        const int g = (lin / hd) % Hkv;
+        const int e = lin % hd;
+        const float x = kvbuf[lin];
+        const long long row = kv_row(L, b, g, pos);
+        if (w.kind == 0 || (w.kind == 1 && L.base_bits == 16)) {
+            ((u16*)L.base[kv])[row * hd + e] = f2bf(x);
+        } else if (w.kind == 1) {  // int8 base: residual against a zero reconstruction
+            u16 sb;
+            const int c = quant_group32(x, 127, &sb);
+            ((int8_t*)L.base[kv])[row * hd + e] = (int8_t)c;
+            if ((threadIdx.x & 31) == 0) ((u16*)L.base_scale[kv])[row * (hd / 32) + e / 32] = sb;
+        } else {
+            const long long rr = res_row(L, b, g, slot);
+            if (L.res_bits == 16) {
+                ((u16*)L.res[w.loop - 2][kv])[rr * hd + e] = f2bf(x);
+            } else {
+                const float prev = kv_recon_elem(L, kv, b, g, pos, e, w.loop - 1);
+                u16 sb;
+                const int qmax = (1 << (L.res_bits - 1)) - 1;
+                const int c = quant_group32(x - prev, qmax, &sb);
+                if ((threadIdx.x & 31) == 0)
+                    ((u16*)L.res_scale[w.loop - 2][kv])[rr * (hd / 32) + e / 32] = sb;
+                if (L.res_bits == 8) {
+                    ((int8_t*)L.res[w.loop - 2][kv])[rr * hd + e] = (int8_t)c;
+                } else {
+                    const int other = __shfl_xor(c, 1);
+                    if ((threadIdx.x & 1) == 0)
+                        ((uint8_t*)L.res[w.loop - 2][kv])[rr * (hd / 2) + e / 2] =
+                            (uint8_t)((c & 0xF) | ((other & 0xF) << 4));
+                }
+            }
+        }
+    }
+    if (w.kind == 2 && w.slot_map_k && threadIdx.x == 0)
+        w.slot_map_k[(long long)b * L.Tmax + pos] = (int32_t)slot;
+}
+
+inline int grid_for(long long n) {
+    long long g = (n + kThreads - 1) / kThreads;
+    return (int)(g > 65536 ? 65536 : (g < 1 ? 1 : g));
+}
+
+}  // namespace
+
+hipError_t embed(const int32_t* ids, const u16* tok_emb, float* h, int rows, int d, int vocab,
+                 hipStream_t st) {
+    hipLaunchKernelGGL(embed_kernel, dim3(rows), dim3(kThreads), 0, st, ids, tok_emb, h, d, vocab);
+    return hipGetLastError();
+}
+
+hipError_t rmsnorm(float* x, const u16* add, const u16* gain, float eps, int rows, int d, u16* out_bf,
+                   float* out_f32, hipStream_t st) {
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(kThreads), 0, st, x, add, gain, eps, d, out_bf,
+                       out_f32);
+    return hipGetLastError();
+}
+
+hipError_t add_rows(float* x, const u16* add, int rows, int d, hipStream_t st) {
+    hipLaunchKernelGGL(add_rows_kernel, dim3(rows), dim3(kThreads), 0, st, x, add, d);
+    return hipGetLastError();
+}
+
+hipError_t copy_f32(const float* src, float* dst, long long n, hipStream_t st) {
+    hipLaunchKernelGGL(copy_f32_kernel, dim3(grid_for(n)), dim3(kThreads), 0, st, src, dst, n);
+    return hipGetLastError();
+}
+hipError_t fill_i32(int32_t* p, int32_t v, long long n, hipStream_t st) {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(n)), dim3(kThreads), 0, st, p, v, n);
+    return hipGetLastError();
+}
+hipError_t fill_f32(float* p, float v, long long n, hipStream_t st) {
+    hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n)), dim3(kThreads), 0, st, p, v, n);
+    return hipGetLastError();
+}
+
+hipError_t delta_keys(const float* a, const float* b, int rows, int d, float* key, hipStream_t st) {
+    hipLaunchKernelGGL(delta_kernel, dim3(rows), dim3(kThreads), 0, st, a, b, d, key);
+    return hipGetLastError();
+}
+
+hipError_t gather_rows(const float* h, const int32_t* idx, int B, int n, int T, int d, const u16* add,
+                       float* xc, int32_t* slot_map, int Tmax, hipStream_t st) {
+    hipLaunchKernelGGL(gather_kernel, dim3(B * n), dim3(kThreads), 0, st, h, idx, n, T, d, add, xc,
+                       slot_map, Tmax);
+    return hipGetLastError();
+}
+
+hipError_t scatter_rows(const float* xc, const int32_t* idx, int B, int n, int T, int d, float* h,
+                        float* key, hipStream_t st) {
+    hipLaunchKernelGGL(scatter_kernel, dim3(B * n), dim3(kThreads), 0, st, xc, idx, n, T, d, h, key);
+    return hipGetLastError();
+}
+
+hipError_t topk_rows(const float* keys, int rows, int cols, int n, int32_t* out, hipStream_t st) {
+    hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kThreads), 0, st, keys, cols, n, out);
+    return hipGetLastError();
+}
+
+hipError_t quantize_rows(const float* x, int rows, int hd, int bits, uint8_t* codes, u16* scales,
+                         hipStream_t st) {
+    const long long groups = (long long)rows * (hd / 32);
+    const int per_block = kThreads / 32;
+    const long long blocks = (groups + per_block - 1) / per_block;
+    hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, x, groups,
+                       hd, bits, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t rope_kv_write(const float* qkv, int rows, int rows_per_seq, const int32_t* pos, int pos_offset,
+                         int H, int Hkv, int hd, const double* inv_freq, u16* q_out, const KVWrite& kvw,
+                         hipStream_t st) {
+    InvFreq inv;
+    for (int i = 0; i < hd / 2; ++i) inv.v[i] = inv_freq[i];
+    hipLaunchKernelGGL(rope_kv_write_kernel, dim3(rows), dim3(kThreads), 0, st, qkv, rows_per_seq, pos,
+                       pos_offset, H, Hkv, hd, inv, q_out, kvw);
+    return hipGetLastError();
+}
+
+}  // namespace lk

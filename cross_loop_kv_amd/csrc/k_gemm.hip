@@ -1,0 +1,226 @@
+// bf16 GEMMs on gfx950 MFMA for the shared-block projections.
+//
+// Every loop is "another Transformer pass" over the rows it recomputes
+// (FlashLoop abstract, arxivdaily.com); in the lazy loops only the kept rows
+// reach these kernels.  C = A[M, K] * W[N, K]^T with bf16 operands and fp32
+// accumulation; epilogues fuse the residual add, SwiGLU and GELU.
+//
+// * Tiled kernel (M > 16): 128 x 128 x 32 tiles, 4 waves each owning 64 x 64 as
+//   2 x 2 v_mfma_f32_32x32x16_bf16 tiles, LDS double buffering with one barrier
+//   per k-step, rows padded to 80 bytes so the 16-byte operand reads of a wave
+//   spread over the LDS banks.
+// * Skinny kernel (M <= 16, decode): the weights stream straight from HBM into
+//   v_mfma_f32_16x16x32_bf16 B operands.  Each lane reads a contiguous run of its
+//   weight row (the reduction order over k is free, so A and B use the same
+//   permuted k order), 8 waves split K and meet in LDS.
+#include "lk_kernels.h"
+
+namespace lk {
+
+namespace {
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+
+// ---------------------------------------------------------------- tiled kernel
+constexpr int BM = 128, BN = 128, BK = 32, LDK = BK + 8;
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_tiled_kernel(const u16* __restrict__ A,
+                                                         const u16* __restrict__ W, int M, int N,
+                                                         int K, float* __restrict__ C,
+                                                         u16* __restrict__ Obf) {
+    __shared__ __attribute__((aligned(16))) u16 As[2][BM * LDK];
+    __shared__ __attribute__((aligned(16))) u16 Bs[2][BN * LDK];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int l32 = lane & 31, kg = lane >> 5;
+    const int row0 = blockIdx.y * BM;
+    // rows of W loaded into the B tile
+    const int wrows = (EPI == EPI_SWIGLU) ? 2 * N : N;
+
+    uint4 ra[2], rb[2];
+    int a_row[2], a_ch[2], b_wrow[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int c = tid + p * 256;
+        const int rr = c >> 2;
+        a_row[p] = rr;
+        a_ch[p] = c & 3;
+        int wr;
+        if (EPI == EPI_SWIGLU) {
+            const int blk = rr >> 5;
+            wr = ((blk & 1) ? N : 0) + blockIdx.x * 64 + (blk >> 1) * 32 + (rr & 31);
+        } else {
+            wr = blockIdx.x * BN + rr;
+        }
+        b_wrow[p] = wr;
+    }
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int gr = row0 + a_row[p];
+            ra[p] = (gr < M) ? *(const uint4*)(A + (long long)gr * K + k0 + a_ch[p] * 8)
+                             : make_uint4(0, 0, 0, 0);
+            rb[p] = (b_wrow[p] < wrows) ? *(const uint4*)(W + (long long)b_wrow[p] * K + k0 + a_ch[p] * 8)
+                                        : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            *(uint4*)&As[buf][a_row[p] * LDK + a_ch[p] * 8] = ra[p];
+            *(uint4*)&Bs[buf][a_row[p] * LDK + a_ch[p] * 8] = rb[p];
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[t][u][i] = 0.f;
+
+    const int nk = K / BK;
+    load(0);
+    store(0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        __syncthreads();
+        if (kt + 1 < nk) load((kt + 1) * BK);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            bf16x8 a[2], b[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                a[t] = as_bf16x8(*(const uint4*)&As[cur][(wm * 64 + t * 32 + l32) * LDK + ks * 16 + kg * 8]);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                b[u] = as_bf16x8(*(const uint4*)&Bs[cur][(wn * 64 + u * 32 + l32) * LDK + ks * 16 + kg * 8]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], b[u], acc[t][u], 0, 0, 0);
+        }
+        if (kt + 1 < nk) store(cur ^ 1);
+    }
+
+    // epilogue: acc[t][u][i] = C[row0 + wm*64 + t*32 + 8*(i/4) + 4*kg + i%4][col(u) + l32]
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = row0 + wm * 64 + t * 32 + 8 * (i >> 2) + 4 * kg + (i & 3);
+            if (r >= M) continue;
+            if (EPI == EPI_SWIGLU) {
+                const int col = blockIdx.x * 64 + wn * 32 + l32;
+                if (col < N) Obf[(long long)r * N + col] = f2bf(silu_f(acc[t][0][i]) * acc[t][1][i]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int col = blockIdx.x * BN + wn * 64 + u * 32 + l32;
+                    if (col >= N) continue;
+                    const long long o = (long long)r * N + col;
+                    if (EPI == EPI_STORE) C[o] = acc[t][u][i];
+                    else if (EPI == EPI_ADD) C[o] = C[o] + acc[t][u][i];
+                    else Obf[o] = f2bf(gelu_f(acc[t][u][i]));
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- skinny kernel
+template <int EPI, int J>
+__global__ __launch_bounds__(512) void gemm_skinny_kernel(const u16* __restrict__ A,
+                                                          const u16* __restrict__ W, int M, int N,
+                                                          int K, float* __restrict__ C,
+                                                          u16* __restrict__ Obf) {
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    __shared__ f32x4 red[8][64][DUAL ? 2 : 1];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int c16 = lane & 15, grp = lane >> 4;
+    const int n = blockIdx.x * 16 + c16;
+    constexpr int CH = 32 * J;  // k per chunk (4 lane groups x 8J)
+    const int nch = K / CH;
+    const int cb = w * nch / 8, ce = (w + 1) * nch / 8;
+    const bool nvalid = n < N;
+    const u16* w0 = W + (long long)(nvalid ? n : 0) * K;
+    const u16* w1 = W + (long long)(nvalid ? N + n : 0) * K;
+    const bool mvalid = c16 < M;
+    const u16* ar = A + (long long)(mvalid ? c16 : 0) * K;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    for (int c = cb; c < ce; ++c) {
+        const int k0 = c * CH + grp * 8 * J;
+        uint4 wv[J], av[J], wv1[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            wv[j] = *(const uint4*)(w0 + k0 + j * 8);
+            if (DUAL) wv1[j] = *(const uint4*)(w1 + k0 + j * 8);
+            av[j] = mvalid ? *(const uint4*)(ar + k0 + j * 8) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[j]), as_bf16x8(wv[j]), acc0, 0, 0, 0);
+            if (DUAL)
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[j]), as_bf16x8(wv1[j]), acc1, 0, 0, 0);
+        }
+    }
+    red[w][lane][0] = acc0;
+    if (DUAL) red[w][lane][DUAL ? 1 : 0] = acc1;
+    __syncthreads();
+    if (w != 0) return;
+    f32x4 s0 = red[0][lane][0], s1 = DUAL ? red[0][lane][DUAL ? 1 : 0] : s0;
+#pragma unroll
+    for (int ww = 1; ww < 8; ++ww) {
+        s0 += red[ww][lane][0];
+        if (DUAL) s1 += red[ww][lane][DUAL ? 1 : 0];
+    }
+    if (!nvalid) return;
+    // acc lane l: D[row = (l/16)*4 + i][col = l%16]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = grp * 4 + i;
+        if (m >= M) continue;
+        const long long o = (long long)m * N + n;
+        if (EPI == EPI_STORE) C[o] = s0[i];
+        else if (EPI == EPI_ADD) C[o] = C[o] + s0[i];
+        else if (EPI == EPI_SWIGLU) Obf[o] = f2bf(silu_f(s0[i]) * s1[i]);
+        else Obf[o] = f2bf(gelu_f(s0[i]));
+    }
+}
+
+template <int EPI>
+hipError_t launch_gemm(const u16* A, const u16* W, int M, int N, int K, float* c, u16* out_bf,
+                       hipStream_t st) {
+    if (M <= 16) {
+        dim3 grid((N + 15) / 16);
+        if (K % 128 == 0)
+            hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 4>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf);
+        else if (K % 64 == 0)
+            hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 2>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf);
+        else
+            hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 1>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf);
+    } else {
+        const int bn = (EPI == EPI_SWIGLU) ? 64 : BN;
+        dim3 grid((N + bn - 1) / bn, (M + BM - 1) / BM);
+        hipLaunchKernelGGL((gemm_tiled_kernel<EPI>), grid, dim3(256), 0, st, A, W, M, N, K, c, out_bf);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t gemm(const u16* A, const u16* W, int M, int N, int K, int epi, float* c, u16* out_bf,
+                hipStream_t st) {
+    switch (epi) {
+        case EPI_STORE: return launch_gemm<EPI_STORE>(A, W, M, N, K, c, out_bf, st);
+        case EPI_ADD: return launch_gemm<EPI_ADD>(A, W, M, N, K, c, out_bf, st);
+        case EPI_SWIGLU: return launch_gemm<EPI_SWIGLU>(A, W, M, N, K, c, out_bf, st);
+        default: return launch_gemm<EPI_GELU>(A, W, M, N, K, c, out_bf, st);
+    }
+}
+
+}  // namespace lk

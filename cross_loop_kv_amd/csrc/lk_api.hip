@@ -1,0 +1,789 @@
+// Host runtime of the looped-KV library: configuration checks, KV-store layout,
+// workspace layout and the prefill / decode loop drivers behind the C ABI.
+//
+// Loop structure: embed -> P prelude layers -> K passes of the R shared layers,
+// the loop embedding added before each pass -> Q coda layers -> final RMSNorm
+// (FlashLoop walk-through, discosf.com, sections 3.1 and 4.1).  KV modes
+// per_loop / last_loop: Looped Transformer tutorial (aiboss88.com, step 4).
+// Lazy mode: FlashLoop abstract (arxivdaily.com) -- token-sparse loop updates,
+// sparse attention over stable key columns, quantized KV residuals.
+#include <cmath>
+#include <cstdio>
+#include <algorithm>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/looped_kv.h"
+#include "lk_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+    g_err = msg;
+    return code;
+}
+
+#define LK_HIP(call)                                                                        \
+    do {                                                                                    \
+        hipError_t e_ = (call);                                                             \
+        if (e_ != hipSuccess) return fail(LK_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+    } while (0)
+
+#define LK_TRY(call)          \
+    do {                      \
+        int r_ = (call);      \
+        if (r_ != LK_OK) return r_; \
+    } while (0)
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int n_selected(double rho, int T) {
+    if (T <= 0) return 0;
+    long long n = (long long)std::ceil(rho * (double)T - 1e-9);
+    if (n < 1) n = 1;
+    if (n > T) n = T;
+    return (int)n;
+}
+
+// Columns per split and the split-count ceiling of the row-attention kernel.
+constexpr int kRowChunk = 256;
+constexpr int kMaxSplits = 256;
+
+}  // namespace
+
+// Kernel classes that can be bracketed with HIP events (instrumentation).
+enum TimedClass { TC_NONE = -1, TC_ATTN_DECODE_DENSE = 0, TC_ATTN_DECODE_SPARSE, TC_ATTN_PREFILL,
+                  TC_COLUMN_MASS, TC_ATTN_PREFILL_SPARSE, TC_GEMM_DECODE, TC_GEMM_PREFILL, TC_COUNT };
+static const char* kTimedNames[TC_COUNT] = {"attn_decode_dense", "attn_decode_sparse", "attn_prefill",
+                                            "column_mass", "attn_prefill_sparse", "gemm_decode",
+                                            "gemm_prefill"};
+
+struct EventTimer {
+    int cls = TC_NONE;
+    std::vector<hipEvent_t> pool;
+    size_t used = 0;
+    hipError_t mark(hipStream_t st) {
+        if (used == pool.size()) {
+            hipEvent_t e;
+            hipError_t r = hipEventCreate(&e);
+            if (r != hipSuccess) return r;
+            pool.push_back(e);
+        }
+        return hipEventRecord(pool[used++], st);
+    }
+    ~EventTimer() {
+        for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+    }
+};
+
+struct lk_handle {
+    lk_model_cfg c;
+    lk_lazy_cfg z;
+    EventTimer timer;
+    const u16 *tok, *lemb, *fnorm;
+    std::vector<lk_layer_weights> L;
+    double inv_freq[64];
+    int qkv_w() const { return (c.n_heads + 2 * c.n_kv_heads) * c.head_dim; }
+    int G() const { return c.n_heads / c.n_kv_heads; }
+    bool lazy() const { return z.mode == LK_MODE_LAZY; }
+};
+
+struct StoreLayout {
+    size_t dense, loop_rows, base, base_sc, res, res_sc, slot, cols, total;
+    long long slots;
+    int n_sel, n_cols;
+    long long res_row_b;
+};
+
+struct lk_kv_store {
+    lk_handle* h;
+    int B, Tp, Tmax, t;
+    bool prefilled;
+    StoreLayout lay;
+    char* buf;
+    const int32_t* f_tok;
+    const int32_t* f_cols;
+};
+
+namespace {
+
+StoreLayout store_layout(const lk_handle* h, int B, int Tp, int Tmax) {
+    const lk_model_cfg& c = h->c;
+    StoreLayout s{};
+    const long long hd = c.head_dim, Hkv = c.n_kv_heads;
+    const long long kvrows = (long long)B * Hkv * Tmax;  // rows of one K or V region of a layer
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    s.dense = take((size_t)(c.n_prelude + c.n_coda) * 2 * kvrows * hd * 2);
+    s.loop_rows = s.base = s.base_sc = s.res = s.res_sc = s.slot = s.cols = off;
+    s.slots = 0;
+    s.n_sel = 0;
+    s.n_cols = 0;
+    s.res_row_b = 0;
+    if (h->z.mode == LK_MODE_PER_LOOP) {
+        s.loop_rows = take((size_t)c.n_loops * c.n_shared * 2 * kvrows * hd * 2);
+    } else if (h->z.mode == LK_MODE_LAST_LOOP) {
+        s.loop_rows = take((size_t)c.n_shared * 2 * kvrows * hd * 2);
+    } else {
+        const int bb = h->z.base_bits == 16 ? 2 : 1;
+        s.base = take((size_t)c.n_shared * 2 * kvrows * hd * bb);
+        s.base_sc = take(h->z.base_bits == 16 ? 0 : (size_t)c.n_shared * 2 * kvrows * (hd / 32) * 2);
+        s.n_sel = n_selected(h->z.rho, Tp);
+        s.slots = (long long)s.n_sel + (Tmax - Tp);
+        s.res_row_b = h->z.res_bits == 16 ? hd * 2 : hd * h->z.res_bits / 8;
+        const long long res_rows = (long long)(c.n_loops - 1) * c.n_shared * 2 * B * Hkv * s.slots;
+        s.res = take((size_t)res_rows * s.res_row_b);
+        s.res_sc = take(h->z.res_bits == 16 ? 0 : (size_t)res_rows * (hd / 32) * 2);
+        s.slot = take((size_t)(c.n_loops - 1) * B * Tmax * 4);
+        s.n_cols = h->z.top_s < Tp ? h->z.top_s : Tp;
+        s.cols = take((size_t)c.n_shared * B * Hkv * s.n_cols * 4);
+    }
+    s.total = off;
+    return s;
+}
+
+// Bytes of stored data at length t (closed form, no alignment padding).
+void store_bytes(const lk_kv_store* s, size_t* shared, size_t* total) {
+    const lk_handle* h = s->h;
+    const lk_model_cfg& c = h->c;
+    const long long E = 2LL * c.n_kv_heads * c.head_dim;
+    const long long t = s->t;
+    const long long B = s->B;
+    const long long dense = (long long)(c.n_prelude + c.n_coda) * B * t * E * 2;
+    long long sh = 0;
+    auto rowb = [&](long long n, int bits) -> long long {
+        return bits == 16 ? 2 * n : n * bits / 8 + (n / 32) * 2;
+    };
+    if (h->z.mode == LK_MODE_PER_LOOP) {
+        sh = (long long)c.n_shared * c.n_loops * B * t * E * 2;
+    } else if (h->z.mode == LK_MODE_LAST_LOOP) {
+        sh = (long long)c.n_shared * B * t * E * 2;
+    } else if (t > 0) {
+        const long long stored = (long long)s->lay.n_sel + (t - s->Tp);
+        sh = (long long)c.n_shared * B * t * rowb(E, h->z.base_bits) +
+             (long long)(c.n_loops - 1) * c.n_shared * B * stored * rowb(E, h->z.res_bits) +
+             (long long)(c.n_loops - 1) * B * t * 4 + (long long)c.n_shared * B * c.n_kv_heads * s->lay.n_cols * 4;
+    }
+    *shared = (size_t)sh;
+    *total = (size_t)(sh + dense);
+}
+
+// K/V row pointers ------------------------------------------------------------
+long long kv_region_elems(const lk_kv_store* s) {
+    return (long long)s->B * s->h->c.n_kv_heads * s->Tmax * s->h->c.head_dim;
+}
+
+KVLayer plain_layer(const lk_kv_store* s, u16* k_rows, u16* v_rows) {
+    KVLayer L{};
+    const lk_model_cfg& c = s->h->c;
+    L.lazy = 0;
+    L.B = s->B;
+    L.Hkv = c.n_kv_heads;
+    L.hd = c.head_dim;
+    L.Tmax = s->Tmax;
+    L.base_bits = 16;
+    L.res_bits = 16;
+    L.n_loops = c.n_loops;
+    L.base[0] = k_rows;
+    L.base[1] = v_rows;
+    return L;
+}
+
+KVLayer dense_layer(const lk_kv_store* s, int ci) {
+    u16* base = (u16*)(s->buf + s->lay.dense);
+    const long long n = kv_region_elems(s);
+    return plain_layer(s, base + (2LL * ci) * n, base + (2LL * ci + 1) * n);
+}
+
+KVLayer loop_layer(const lk_kv_store* s, int k, int r) {
+    u16* base = (u16*)(s->buf + s->lay.loop_rows);
+    const long long n = kv_region_elems(s);
+    const long long idx = s->h->z.mode == LK_MODE_PER_LOOP ? ((long long)(k - 1) * s->h->c.n_shared + r) : r;
+    return plain_layer(s, base + (2 * idx) * n, base + (2 * idx + 1) * n);
+}
+
+KVLayer lazy_layer(const lk_kv_store* s, int r) {
+    const lk_handle* h = s->h;
+    const lk_model_cfg& c = h->c;
+    KVLayer L{};
+    L.lazy = 1;
+    L.B = s->B;
+    L.Hkv = c.n_kv_heads;
+    L.hd = c.head_dim;
+    L.Tmax = s->Tmax;
+    L.slots = s->lay.slots;
+    L.base_bits = h->z.base_bits;
+    L.res_bits = h->z.res_bits;
+    L.n_loops = c.n_loops;
+    const long long n = kv_region_elems(s);
+    const long long bb = h->z.base_bits == 16 ? 2 : 1;
+    const long long nsc = n / c.head_dim * (c.head_dim / 32);
+    for (int kv = 0; kv < 2; ++kv) {
+        L.base[kv] = s->buf + s->lay.base + (2LL * r + kv) * n * bb;
+        L.base_scale[kv] = h->z.base_bits == 16 ? nullptr : (const u16*)(s->buf + s->lay.base_sc) + (2LL * r + kv) * nsc;
+    }
+    const long long rows = (long long)s->B * c.n_kv_heads * s->lay.slots;  // rows of one (k, r, kv) region
+    for (int kk = 2; kk <= c.n_loops; ++kk)
+        for (int kv = 0; kv < 2; ++kv) {
+            const long long reg = ((long long)(kk - 2) * c.n_shared + r) * 2 + kv;
+            L.res[kk - 2][kv] = s->buf + s->lay.res + reg * rows * s->lay.res_row_b;
+            L.res_scale[kk - 2][kv] =
+                h->z.res_bits == 16 ? nullptr : (const u16*)(s->buf + s->lay.res_sc) + reg * rows * (c.head_dim / 32);
+        }
+    L.slot = (const int32_t*)(s->buf + s->lay.slot);
+    return L;
+}
+
+int32_t* slot_map(const lk_kv_store* s, int k) {
+    return (int32_t*)(s->buf + s->lay.slot) + (long long)(k - 2) * s->B * s->Tmax;
+}
+int32_t* col_sets(const lk_kv_store* s, int r) {
+    return (int32_t*)(s->buf + s->lay.cols) + (long long)r * s->B * s->h->c.n_kv_heads * s->lay.n_cols;
+}
+
+// Workspace -------------------------------------------------------------------
+struct WS {
+    float *h, *h0, *xc, *qkv, *lse, *mass, *keys, *part;
+    u16 *xn, *q, *att, *act;
+    int32_t* sel;
+    size_t total;
+    long long part_floats;
+};
+
+WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
+    const lk_model_cfg& c = hd_->c;
+    const long long M = (long long)B * T;
+    const long long d = c.d_model;
+    const long long n = hd_->lazy() ? n_selected(hd_->z.rho, T) : T;
+    const long long Hhd = (long long)c.n_heads * c.head_dim;
+    WS w{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return base ? (void*)(base + o) : nullptr;
+    };
+    w.h = (float*)take(M * d * 4);
+    w.h0 = (float*)take(hd_->lazy() ? M * d * 4 : 0);
+    w.xc = (float*)take(hd_->lazy() ? (long long)B * n * d * 4 : 0);
+    w.xn = (u16*)take(M * d * 2);
+    w.qkv = (float*)take(M * hd_->qkv_w() * 4);
+    w.q = (u16*)take(M * Hhd * 2);
+    w.att = (u16*)take(M * Hhd * 2);
+    w.act = (u16*)take(M * (long long)c.ffn_dim * 2);
+    w.lse = (float*)take(M * c.n_heads * 4);
+    w.mass = (float*)take(hd_->lazy() ? M * c.n_kv_heads * 4 : 0);
+    w.keys = (float*)take(hd_->lazy() ? M * 4 : 0);
+    w.sel = (int32_t*)take(hd_->lazy() ? (long long)B * n * 4 : 0);
+    // row-attention partials: decode rows use up to kMaxSplits splits; token-sparse
+    // prefill rows need ceil((columns + window) / chunk) splits.
+    long long pf = (long long)B * c.n_heads * kMaxSplits * (c.head_dim + 2);
+    if (hd_->lazy() && T > 1) {
+        const long long ncol = std::min((long long)std::min(hd_->z.top_s, T) + hd_->z.window, (long long)T);
+        const long long sp = (ncol + kRowChunk - 1) / kRowChunk;
+        pf = std::max(pf, (long long)B * n * c.n_heads * sp * (c.head_dim + 2));
+    }
+    w.part_floats = pf;
+    w.part = (float*)take(pf * 4);
+    w.total = off;
+    return w;
+}
+
+int check_cfg(const lk_model_cfg* c, const lk_lazy_cfg* z) {
+    if (!c || !z) return fail(LK_ERR_INVALID_ARG, "null config");
+    if (c->vocab < 1 || c->d_model < 64 || c->n_heads < 1 || c->n_kv_heads < 1 || c->ffn_dim < 64)
+        return fail(LK_ERR_INVALID_ARG, "bad model sizes");
+    if (c->n_prelude < 0 || c->n_coda < 0 || c->n_shared < 1 || c->n_loops < 1)
+        return fail(LK_ERR_INVALID_ARG, "bad layer counts");
+    if (c->n_loops > LK_MAX_LOOPS + 1) return fail(LK_ERR_UNSUPPORTED, "at most 17 loops");
+    if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+        return fail(LK_ERR_UNSUPPORTED, "head_dim must be 32, 64 or 128");
+    if (c->n_heads % c->n_kv_heads) return fail(LK_ERR_INVALID_ARG, "n_heads % n_kv_heads != 0");
+    const int G = c->n_heads / c->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return fail(LK_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8");
+    if (c->d_model % 64 || c->ffn_dim % 64) return fail(LK_ERR_UNSUPPORTED, "d_model and ffn_dim must be multiples of 64");
+    if ((c->n_heads * c->head_dim) % 64) return fail(LK_ERR_UNSUPPORTED, "n_heads * head_dim must be a multiple of 64");
+    if (c->n_kv_heads * c->head_dim > 4096) return fail(LK_ERR_UNSUPPORTED, "n_kv_heads * head_dim > 4096");
+    if (c->ffn_act != LK_ACT_GELU && c->ffn_act != LK_ACT_SWIGLU) return fail(LK_ERR_INVALID_ARG, "bad ffn_act");
+    if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(LK_ERR_INVALID_ARG, "bad eps / theta");
+    if (z->mode != LK_MODE_PER_LOOP && z->mode != LK_MODE_LAST_LOOP && z->mode != LK_MODE_LAZY)
+        return fail(LK_ERR_INVALID_ARG, "bad mode");
+    if (z->mode == LK_MODE_LAZY) {
+        if (!(z->rho > 0.0 && z->rho <= 1.0)) return fail(LK_ERR_INVALID_ARG, "rho must be in (0, 1]");
+        if (z->top_s < 1 || z->window < 1) return fail(LK_ERR_INVALID_ARG, "top_s and window must be >= 1");
+        if (z->base_bits != 16 && z->base_bits != 8) return fail(LK_ERR_INVALID_ARG, "base_bits must be 16 or 8");
+        if (z->res_bits != 16 && z->res_bits != 8 && z->res_bits != 4)
+            return fail(LK_ERR_INVALID_ARG, "res_bits must be 16, 8 or 4");
+        if (z->group != 32) return fail(LK_ERR_UNSUPPORTED, "group must be 32");
+    }
+    return LK_OK;
+}
+
+// One Transformer layer ---------------------------------------------------------
+struct LayerIO {
+    float* x;                // rows [M, d], updated in place
+    int M;                   // rows
+    int rows_per_seq;        // rows of each sequence in x
+    const int32_t* pos;      // positions (nullptr: pos_offset + row index within the sequence)
+    int pos_offset;
+    const u16* add;          // loop embedding added before the layer (nullptr: none)
+};
+
+enum AttnKind { ATTN_PREFILL_DENSE, ATTN_ROWS_DENSE, ATTN_ROWS_SPARSE };
+
+struct AttnPlan {
+    AttnKind kind;
+    KVLayer read;        // where attention reads K/V
+    int k_loop;              // reconstruction loop for lazy reads
+    const int32_t* cols;     // sparse column sets of the layer
+    int n_cols, window;
+    int B, T;                // prefill: batch and tokens per sequence
+    int pos;                 // decode position (rows attention)
+    float* mass;             // lazy loop 1: column mass output
+};
+
+// Launch `fn` bracketed by timer events when its class is the instrumented one.
+template <typename F>
+int timed(lk_handle* h, int cls, hipStream_t st, F fn) {
+    const bool on = h->timer.cls == cls;
+    if (on) LK_HIP(h->timer.mark(st));
+    LK_HIP(fn());
+    if (on) LK_HIP(h->timer.mark(st));
+    return LK_OK;
+}
+
+int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, const AttnPlan& ap,
+              const WS& w, hipStream_t st) {
+    const lk_model_cfg& c = h->c;
+    const int gcls = ap.kind == ATTN_PREFILL_DENSE || io.rows_per_seq > 1 ? TC_GEMM_PREFILL : TC_GEMM_DECODE;
+    const lk_layer_weights& W = h->L[li];
+    const int d = c.d_model, H = c.n_heads, hd = c.head_dim, Hhd = H * hd;
+    LK_HIP(lk::rmsnorm(io.x, io.add, (const u16*)W.attn_norm, c.rms_eps, io.M, d, w.xn, nullptr, st));
+    LK_TRY(timed(h, gcls, st, [&] {
+        return lk::gemm(w.xn, (const u16*)W.wqkv, io.M, h->qkv_w(), d, lk::EPI_STORE, w.qkv, nullptr, st);
+    }));
+    // RoPE positions: explicit, or the row index within the sequence (+ offset for decode)
+    const int32_t* pos = io.pos;
+    lk::KVWrite kw = kvw;
+    LK_HIP(lk::rope_kv_write(w.qkv, io.M, io.rows_per_seq, pos, io.pos_offset, H, c.n_kv_heads, hd,
+                             h->inv_freq, w.q, kw, st));
+    if (ap.kind == ATTN_PREFILL_DENSE) {
+        LK_TRY(timed(h, TC_ATTN_PREFILL, st,
+                     [&] { return lk::attn_prefill(w.q, ap.read, ap.B, ap.T, H, w.att, w.lse, st); }));
+        if (ap.mass)
+            LK_TRY(timed(h, TC_COLUMN_MASS, st,
+                         [&] { return lk::column_mass(w.q, ap.read, w.lse, ap.B, ap.T, H, ap.mass, st); }));
+    } else {
+        lk::RowsAttn a{};
+        a.q = w.q;
+        a.qpos = io.pos;
+        a.pos = ap.pos;
+        a.B = io.M / io.rows_per_seq;
+        a.n_rows = io.rows_per_seq;
+        a.H = H;
+        a.kv = ap.read;
+        a.k_loop = ap.k_loop;
+        long long ncol_max;
+        if (ap.kind == ATTN_ROWS_SPARSE) {
+            a.cols = ap.cols;
+            a.n_cols = ap.n_cols;
+            a.window = ap.window;
+            const long long limit = ap.T > 0 ? ap.T : (long long)ap.pos + 1;
+            ncol_max = std::min((long long)ap.n_cols + ap.window, limit);
+        } else {
+            a.cols = nullptr;
+            ncol_max = (long long)ap.pos + 1;
+        }
+        int chunk = kRowChunk;
+        while ((ncol_max + chunk - 1) / chunk > kMaxSplits) chunk *= 2;
+        a.chunk = chunk;
+        a.n_splits = (int)((ncol_max + chunk - 1) / chunk);
+        if ((long long)a.B * a.n_rows * H * a.n_splits * (hd + 2) > w.part_floats)
+            return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
+        a.part = w.part;
+        a.out = w.att;
+        const int acls = io.rows_per_seq > 1 ? TC_ATTN_PREFILL_SPARSE
+                         : (ap.kind == ATTN_ROWS_SPARSE ? TC_ATTN_DECODE_SPARSE : TC_ATTN_DECODE_DENSE);
+        LK_TRY(timed(h, acls, st, [&] { return lk::attn_rows_main(a, st); }));
+        LK_HIP(lk::attn_rows_combine(a, st));
+    }
+    LK_TRY(timed(h, gcls, st,
+                 [&] { return lk::gemm(w.att, (const u16*)W.wo, io.M, d, Hhd, lk::EPI_ADD, io.x, nullptr, st); }));
+    LK_HIP(lk::rmsnorm(io.x, nullptr, (const u16*)W.ffn_norm, c.rms_eps, io.M, d, w.xn, nullptr, st));
+    const int act = c.ffn_act == LK_ACT_SWIGLU ? lk::EPI_SWIGLU : lk::EPI_GELU;
+    LK_TRY(timed(h, gcls, st,
+                 [&] { return lk::gemm(w.xn, (const u16*)W.w_in, io.M, c.ffn_dim, d, act, nullptr, w.act, st); }));
+    LK_TRY(timed(h, gcls, st, [&] {
+        return lk::gemm(w.act, (const u16*)W.w_down, io.M, d, c.ffn_dim, lk::EPI_ADD, io.x, nullptr, st);
+    }));
+    return LK_OK;
+}
+
+lk::KVWrite plain_write(const KVLayer& L) {
+    lk::KVWrite k{};
+    k.kind = 0;
+    k.layer = L;
+    return k;
+}
+
+}  // namespace
+
+// =============================================================================
+extern "C" {
+
+const char* lk_last_error(void) { return g_err.c_str(); }
+
+int lk_create(const lk_model_cfg* cfg, const lk_lazy_cfg* lazy, const lk_weights* w, lk_handle** out) {
+    if (!out) return fail(LK_ERR_INVALID_ARG, "null out");
+    *out = nullptr;
+    LK_TRY(check_cfg(cfg, lazy));
+    if (!w || !w->tok_emb || !w->loop_emb || !w->final_norm || !w->layers)
+        return fail(LK_ERR_INVALID_ARG, "null weight pointer");
+    const int L = cfg->n_prelude + cfg->n_shared + cfg->n_coda;
+    for (int i = 0; i < L; ++i) {
+        const lk_layer_weights& l = w->layers[i];
+        if (!l.attn_norm || !l.wqkv || !l.wo || !l.ffn_norm || !l.w_in || !l.w_down)
+            return fail(LK_ERR_INVALID_ARG, "null layer weight pointer in layer " + std::to_string(i));
+    }
+    lk_handle* h = new lk_handle();
+    h->c = *cfg;
+    h->z = *lazy;
+    h->tok = (const u16*)w->tok_emb;
+    h->lemb = (const u16*)w->loop_emb;
+    h->fnorm = (const u16*)w->final_norm;
+    h->L.assign(w->layers, w->layers + L);
+    for (int i = 0; i < cfg->head_dim / 2; ++i)
+        h->inv_freq[i] = std::pow((double)cfg->rope_theta, -2.0 * i / (double)cfg->head_dim);
+    *out = h;
+    return LK_OK;
+}
+
+void lk_destroy(lk_handle* h) { delete h; }
+
+int lk_effective_depth(const lk_handle* h, int32_t* depth) {
+    if (!h || !depth) return fail(LK_ERR_INVALID_ARG, "null argument");
+    *depth = h->c.n_prelude + h->c.n_shared * h->c.n_loops + h->c.n_coda;
+    return LK_OK;
+}
+
+int lk_kv_store_alloc(lk_handle* h, int32_t batch, int32_t prompt_tokens, int32_t max_tokens, void* dev_buf,
+                      size_t buf_bytes, void* stream, lk_kv_store** out, size_t* need_bytes) {
+    if (!h || !need_bytes) return fail(LK_ERR_INVALID_ARG, "null argument");
+    if (batch < 1 || prompt_tokens < 1 || max_tokens < prompt_tokens)
+        return fail(LK_ERR_INVALID_ARG, "need batch >= 1 and 1 <= prompt_tokens <= max_tokens");
+    const StoreLayout lay = store_layout(h, batch, prompt_tokens, max_tokens);
+    *need_bytes = lay.total;
+    if (!dev_buf) return LK_OK;
+    if (!out) return fail(LK_ERR_INVALID_ARG, "null out");
+    if (buf_bytes < lay.total) return fail(LK_ERR_CAPACITY, "store buffer too small");
+    if ((uintptr_t)dev_buf % kAlign) return fail(LK_ERR_INVALID_ARG, "store buffer must be 256-byte aligned");
+    lk_kv_store* s = new lk_kv_store();
+    s->h = h;
+    s->B = batch;
+    s->Tp = prompt_tokens;
+    s->Tmax = max_tokens;
+    s->t = 0;
+    s->prefilled = false;
+    s->lay = lay;
+    s->buf = (char*)dev_buf;
+    s->f_tok = s->f_cols = nullptr;
+    if (h->lazy()) {
+        hipError_t e = lk::fill_i32(slot_map(s, 2), -1, (long long)(h->c.n_loops - 1) * batch * max_tokens,
+                                    (hipStream_t)stream);
+        if (e != hipSuccess) {
+            delete s;
+            return fail(LK_ERR_HIP, std::string("slot map clear: ") + hipGetErrorString(e));
+        }
+    }
+    *out = s;
+    return LK_OK;
+}
+
+void lk_kv_store_release(lk_kv_store* s) { delete s; }
+
+int lk_kv_store_bytes_used(const lk_kv_store* s, size_t* shared, size_t* total) {
+    if (!s || !shared || !total) return fail(LK_ERR_INVALID_ARG, "null argument");
+    store_bytes(s, shared, total);
+    return LK_OK;
+}
+
+int lk_kv_store_length(const lk_kv_store* s, int32_t* tokens) {
+    if (!s || !tokens) return fail(LK_ERR_INVALID_ARG, "null argument");
+    *tokens = s->t;
+    return LK_OK;
+}
+
+int lk_kv_store_view(const lk_kv_store* s, lk_store_view* v) {
+    if (!s || !v) return fail(LK_ERR_INVALID_ARG, "null argument");
+    std::memset(v, 0, sizeof(*v));
+    const lk_handle* h = s->h;
+    if (h->c.n_prelude + h->c.n_coda > 0) v->dense = s->buf + s->lay.dense;
+    if (h->z.mode != LK_MODE_LAZY) {
+        v->loop_rows = s->buf + s->lay.loop_rows;
+        return LK_OK;
+    }
+    v->base_codes = s->buf + s->lay.base;
+    v->base_scales = h->z.base_bits == 16 ? nullptr : s->buf + s->lay.base_sc;
+    v->res_codes = s->buf + s->lay.res;
+    v->res_scales = h->z.res_bits == 16 ? nullptr : s->buf + s->lay.res_sc;
+    v->slot_maps = (int32_t*)(s->buf + s->lay.slot);
+    v->columns = (int32_t*)(s->buf + s->lay.cols);
+    v->slots = s->lay.slots;
+    v->n_selected = s->lay.n_sel;
+    v->n_columns = s->lay.n_cols;
+    v->res_row_bytes = s->lay.res_row_b;
+    return LK_OK;
+}
+
+int lk_kv_store_force_selection(lk_kv_store* s, const int32_t* d_tokens, const int32_t* d_columns) {
+    if (!s) return fail(LK_ERR_INVALID_ARG, "null store");
+    if (!s->h->lazy()) return fail(LK_ERR_STATE, "selection exists only in lazy mode");
+    s->f_tok = d_tokens;
+    s->f_cols = d_columns;
+    return LK_OK;
+}
+
+int lk_workspace_bytes(lk_handle* h, int32_t batch, int32_t tokens, size_t* bytes) {
+    if (!h || !bytes) return fail(LK_ERR_INVALID_ARG, "null argument");
+    if (batch < 1 || tokens < 1) return fail(LK_ERR_INVALID_ARG, "batch and tokens must be >= 1");
+    *bytes = ws_layout(h, batch, tokens, nullptr).total;
+    return LK_OK;
+}
+
+int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_t B, int32_t T, float* d_out,
+                      void* d_ws, size_t ws_bytes, void* stream) {
+    if (!h || !s || !d_ids || !d_out || !d_ws) return fail(LK_ERR_INVALID_ARG, "null argument");
+    if (s->h != h) return fail(LK_ERR_INVALID_ARG, "store belongs to another handle");
+    if (B != s->B || T != s->Tp) return fail(LK_ERR_INVALID_ARG, "B and T must match the store");
+    const WS w = ws_layout(h, B, T, (char*)d_ws);
+    if (ws_bytes < w.total) return fail(LK_ERR_CAPACITY, "workspace too small");
+    if ((uintptr_t)d_ws % kAlign) return fail(LK_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    const lk_model_cfg& c = h->c;
+    const int P = c.n_prelude, R = c.n_shared, K = c.n_loops, Q = c.n_coda, d = c.d_model;
+    const int M = B * T;
+    if (h->lazy())
+        LK_HIP(lk::fill_i32(slot_map(s, 2), -1, (long long)(K - 1) * B * s->Tmax, st));
+    s->t = 0;
+    s->prefilled = false;
+    LK_HIP(lk::embed(d_ids, h->tok, w.h, M, d, c.vocab, st));
+
+    LayerIO io{w.h, M, T, nullptr, 0, nullptr};
+    AttnPlan dense_plan{};
+    dense_plan.kind = ATTN_PREFILL_DENSE;
+    dense_plan.B = B;
+    dense_plan.T = T;
+    for (int li = 0; li < P; ++li) {
+        dense_plan.read = dense_layer(s, li);
+        LK_TRY(run_layer(h, li, io, plain_write(dense_plan.read), dense_plan, w, st));
+    }
+    if (!h->lazy()) {
+        for (int k = 1; k <= K; ++k)
+            for (int r = 0; r < R; ++r) {
+                io.add = (r == 0) ? h->lemb + (long long)(k - 1) * d : nullptr;
+                dense_plan.read = loop_layer(s, k, r);
+                LK_TRY(run_layer(h, P + r, io, plain_write(dense_plan.read), dense_plan, w, st));
+            }
+        io.add = nullptr;
+    } else {
+        const int n = s->lay.n_sel;
+        LK_HIP(lk::copy_f32(w.h, w.h0, (long long)M * d, st));
+        // loop 1: dense over every token; writes the base and picks the column sets
+        for (int r = 0; r < R; ++r) {
+            io.add = (r == 0) ? h->lemb : nullptr;
+            AttnPlan ap = dense_plan;
+            ap.read = lazy_layer(s, r);
+            ap.mass = w.mass;
+            lk::KVWrite kw{};
+            kw.kind = 1;
+            kw.layer = ap.read;
+            LK_TRY(run_layer(h, P + r, io, kw, ap, w, st));
+            int32_t* cols = col_sets(s, r);
+            const int nc = s->lay.n_cols;
+            if (s->f_cols) {
+                LK_HIP(hipMemcpyAsync(cols, s->f_cols + (long long)r * B * c.n_kv_heads * nc,
+                                      (size_t)B * c.n_kv_heads * nc * 4, hipMemcpyDeviceToDevice, st));
+            } else {
+                LK_HIP(lk::topk_rows(w.mass, B * c.n_kv_heads, T, nc, cols, st));
+            }
+        }
+        io.add = nullptr;
+        if (K >= 2) LK_HIP(lk::delta_keys(w.h, w.h0, M, d, w.keys, st));
+        for (int k = 2; k <= K; ++k) {
+            if (s->f_tok) {
+                LK_HIP(hipMemcpyAsync(w.sel, s->f_tok + (long long)(k - 2) * B * n, (size_t)B * n * 4,
+                                      hipMemcpyDeviceToDevice, st));
+            } else {
+                LK_HIP(lk::topk_rows(w.keys, B, T, n, w.sel, st));
+            }
+            LK_HIP(lk::gather_rows(w.h, w.sel, B, n, T, d, h->lemb + (long long)(k - 1) * d, w.xc,
+                                   slot_map(s, k), s->Tmax, st));
+            LayerIO cio{w.xc, B * n, n, w.sel, 0, nullptr};
+            for (int r = 0; r < R; ++r) {
+                AttnPlan ap{};
+                ap.kind = ATTN_ROWS_SPARSE;
+                ap.read = lazy_layer(s, r);
+                ap.k_loop = k;
+                ap.cols = col_sets(s, r);
+                ap.n_cols = s->lay.n_cols;
+                ap.window = h->z.window;
+                ap.T = T;
+                lk::KVWrite kw{};
+                kw.kind = 2;
+                kw.layer = ap.read;
+                kw.loop = k;
+                kw.slot_base = 0;
+                LK_TRY(run_layer(h, P + r, cio, kw, ap, w, st));
+            }
+            if (k < K) {
+                LK_HIP(lk::fill_f32(w.keys, 0.f, (long long)M, st));
+                LK_HIP(lk::scatter_rows(w.xc, w.sel, B, n, T, d, w.h, w.keys, st));
+            } else {
+                LK_HIP(lk::scatter_rows(w.xc, w.sel, B, n, T, d, w.h, nullptr, st));
+            }
+        }
+    }
+    for (int j = 0; j < Q; ++j) {
+        dense_plan.read = dense_layer(s, P + j);
+        LK_TRY(run_layer(h, P + R + j, io, plain_write(dense_plan.read), dense_plan, w, st));
+    }
+    LK_HIP(lk::rmsnorm(w.h, nullptr, h->fnorm, c.rms_eps, M, d, nullptr, d_out, st));
+    s->t = T;
+    s->prefilled = true;
+    return LK_OK;
+}
+
+int lk_looped_decode_step(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, float* d_out, void* d_ws,
+                          size_t ws_bytes, void* stream) {
+    if (!h || !s || !d_ids || !d_out || !d_ws) return fail(LK_ERR_INVALID_ARG, "null argument");
+    if (s->h != h) return fail(LK_ERR_INVALID_ARG, "store belongs to another handle");
+    if (!s->prefilled) return fail(LK_ERR_STATE, "decode before prefill");
+    if (s->t >= s->Tmax) return fail(LK_ERR_CAPACITY, "store is full (max_tokens reached)");
+    const int B = s->B;
+    const WS w = ws_layout(h, B, 1, (char*)d_ws);
+    if (ws_bytes < w.total) return fail(LK_ERR_CAPACITY, "workspace too small");
+    if ((uintptr_t)d_ws % kAlign) return fail(LK_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    const lk_model_cfg& c = h->c;
+    const int P = c.n_prelude, R = c.n_shared, K = c.n_loops, Q = c.n_coda, d = c.d_model;
+    const int t = s->t;
+    LK_HIP(lk::embed(d_ids, h->tok, w.h, B, d, c.vocab, st));
+    LayerIO io{w.h, B, 1, nullptr, t, nullptr};
+    AttnPlan dense{};
+    dense.kind = ATTN_ROWS_DENSE;
+    dense.k_loop = 1;
+    dense.pos = t;
+    for (int li = 0; li < P; ++li) {
+        dense.read = dense_layer(s, li);
+        LK_TRY(run_layer(h, li, io, plain_write(dense.read), dense, w, st));
+    }
+    for (int k = 1; k <= K; ++k) {
+        for (int r = 0; r < R; ++r) {
+            io.add = (r == 0) ? h->lemb + (long long)(k - 1) * d : nullptr;
+            if (!h->lazy()) {
+                dense.read = loop_layer(s, k, r);
+                LK_TRY(run_layer(h, P + r, io, plain_write(dense.read), dense, w, st));
+                continue;
+            }
+            AttnPlan ap{};
+            ap.read = lazy_layer(s, r);
+            ap.pos = t;
+            lk::KVWrite kw{};
+            kw.layer = ap.read;
+            if (k == 1) {
+                ap.kind = ATTN_ROWS_DENSE;
+                ap.k_loop = 1;
+                kw.kind = 1;
+            } else {
+                ap.kind = ATTN_ROWS_SPARSE;
+                ap.k_loop = k;
+                ap.cols = col_sets(s, r);
+                ap.n_cols = s->lay.n_cols;
+                ap.window = h->z.window;
+                kw.kind = 2;
+                kw.loop = k;
+                kw.slot_base = (long long)s->lay.n_sel + (t - s->Tp);
+                kw.slot_map_k = slot_map(s, k);
+            }
+            LK_TRY(run_layer(h, P + r, io, kw, ap, w, st));
+        }
+    }
+    io.add = nullptr;
+    for (int j = 0; j < Q; ++j) {
+        dense.read = dense_layer(s, P + j);
+        LK_TRY(run_layer(h, P + R + j, io, plain_write(dense.read), dense, w, st));
+    }
+    LK_HIP(lk::rmsnorm(w.h, nullptr, h->fnorm, c.rms_eps, B, d, nullptr, d_out, st));
+    s->t = t + 1;
+    return LK_OK;
+}
+
+int lk_timing_enable(lk_handle* h, const char* kernel_class) {
+    if (!h) return fail(LK_ERR_INVALID_ARG, "null handle");
+    h->timer.used = 0;
+    h->timer.cls = TC_NONE;
+    if (!kernel_class) return LK_OK;
+    for (int i = 0; i < TC_COUNT; ++i)
+        if (std::strcmp(kernel_class, kTimedNames[i]) == 0) {
+            h->timer.cls = i;
+            return LK_OK;
+        }
+    return fail(LK_ERR_INVALID_ARG, std::string("unknown kernel class ") + kernel_class);
+}
+
+int lk_timing_read(lk_handle* h, int32_t* launches, double* total_ms) {
+    if (!h || !launches || !total_ms) return fail(LK_ERR_INVALID_ARG, "null argument");
+    double tot = 0.0;
+    const size_t n = h->timer.used / 2;
+    for (size_t i = 0; i < n; ++i) {
+        LK_HIP(hipEventSynchronize(h->timer.pool[2 * i + 1]));
+        float ms = 0.f;
+        LK_HIP(hipEventElapsedTime(&ms, h->timer.pool[2 * i], h->timer.pool[2 * i + 1]));
+        tot += ms;
+    }
+    *launches = (int32_t)n;
+    *total_ms = tot;
+    return LK_OK;
+}
+
+// ---- test entry points ----------------------------------------------------------
+int lk_dbg_topk(const float* d_keys, int32_t rows, int32_t cols, int32_t n, int32_t* d_idx, void* stream) {
+    if (!d_keys || !d_idx) return fail(LK_ERR_INVALID_ARG, "null argument");
+    if (rows < 1 || cols < 1 || n < 1 || n > cols) return fail(LK_ERR_INVALID_ARG, "need 1 <= n <= cols");
+    LK_HIP(lk::topk_rows(d_keys, rows, cols, n, d_idx, (hipStream_t)stream));
+    return LK_OK;
+}
+
+int lk_dbg_quantize(const float* d_x, int32_t rows, int32_t hd, int32_t bits, uint8_t* d_codes,
+                    uint16_t* d_scales, void* stream) {
+    if (!d_x || !d_codes || !d_scales) return fail(LK_ERR_INVALID_ARG, "null argument");
+    if (rows < 1 || hd < 32 || hd % 32) return fail(LK_ERR_INVALID_ARG, "hd must be a positive multiple of 32");
+    if (bits != 4 && bits != 8) return fail(LK_ERR_INVALID_ARG, "bits must be 4 or 8");
+    LK_HIP(lk::quantize_rows(d_x, rows, hd, bits, d_codes, d_scales, (hipStream_t)stream));
+    return LK_OK;
+}
+
+int lk_dbg_delta(const float* d_a, const float* d_b, int32_t rows, int32_t d, float* d_key, void* stream) {
+    if (!d_a || !d_b || !d_key) return fail(LK_ERR_INVALID_ARG, "null argument");
+    if (rows < 1 || d < 1) return fail(LK_ERR_INVALID_ARG, "bad sizes");
+    LK_HIP(lk::delta_keys(d_a, d_b, rows, d, d_key, (hipStream_t)stream));
+    return LK_OK;
+}
+
+int lk_dbg_gemm(const void* d_a, const void* d_w, float* d_c, int32_t M, int32_t N, int32_t K, void* stream) {
+    if (!d_a || !d_w || !d_c) return fail(LK_ERR_INVALID_ARG, "null argument");
+    if (M < 1 || N < 16 || N % 16 || K < 32 || K % 32)
+        return fail(LK_ERR_INVALID_ARG, "need M >= 1, N a multiple of 16, K a multiple of 32");
+    LK_HIP(lk::gemm((const u16*)d_a, (const u16*)d_w, M, N, K, lk::EPI_STORE, d_c, nullptr, (hipStream_t)stream));
+    return LK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,145 @@
+// Device helpers shared by the gfx950 kernels of the looped-KV library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define LK_MAX_LOOPS 16
+#define LK_WAVE 64
+
+// ---------------------------------------------------------------- bfloat16
+__device__ __forceinline__ float bf2f(u16 v) { return __uint_as_float((uint32_t)v << 16); }
+
+// Round to nearest even (inputs are finite).
+__device__ __forceinline__ u16 f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (u16)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+    return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+// Eight bf16 (16 bytes) reinterpreted as an MFMA operand.
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---------------------------------------------------------------- float16
+__device__ __forceinline__ u16 f2h_bits(float f) {
+    _Float16 h = (_Float16)f;  // IEEE round to nearest even
+    return __builtin_bit_cast(u16, h);
+}
+__device__ __forceinline__ float h2f(u16 bits) {
+    return (float)__builtin_bit_cast(_Float16, bits);
+}
+
+// ---------------------------------------------------------------- reductions
+// Butterfly reductions: every lane ends with the same, run-to-run identical value.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// Block-wide sum (blockDim.x multiple of 64, <= 1024); `red` holds >= 16 floats.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    v = wave_sum(v);
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float t = 0.f;
+    for (int i = 0; i < nw; ++i) t += red[i];
+    return t;
+}
+
+// ---------------------------------------------------------------- residual quantizer
+// One group of 32 values held by 32 consecutive lanes (lane & 31 = element).
+// scale = fp16_rne(min(amax / qmax, 65504)); code = 0 if scale == 0 else
+// clamp(rint_half_even(r / scale), -qmax, qmax).  Divisions are IEEE float32.
+__device__ __forceinline__ int quant_group32(float r, int qmax, u16* scale_bits) {
+    float a = fabsf(r);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+    float s32 = __fdiv_rn(a, (float)qmax);
+    s32 = fminf(s32, 65504.f);
+    u16 sb = f2h_bits(s32);
+    float s = h2f(sb);
+    *scale_bits = sb;
+    if (s == 0.f) return 0;
+    float c = rintf(__fdiv_rn(r, s));
+    c = fminf(fmaxf(c, (float)-qmax), (float)qmax);
+    return (int)c;
+}
+
+// ---------------------------------------------------------------- KV store views
+// Address arithmetic of one shared layer of a lazy store (or a plain bf16 row
+// cache when lazy == 0).  Rows are [b][g][pos][hd] for the base/dense part and
+// [b][g][slot][row_bytes] for the loop-k residual part.
+struct KVLayer {
+    int lazy;            // 0: plain bf16 rows in base[]; 1: lazy store
+    int B, Hkv, hd, Tmax;
+    long long slots;     // residual slots per (b, g)
+    int base_bits;       // 16 or 8
+    int res_bits;        // 16, 8 or 4
+    int n_loops;         // K
+    const void* base[2];          // [K|V]: bf16 rows or int8 codes
+    const u16* base_scale[2];     // fp16 bits, [b][g][pos][hd/32]
+    const void* res[LK_MAX_LOOPS][2];        // index kk-2 for loop kk
+    const u16* res_scale[LK_MAX_LOOPS][2];
+    const int32_t* slot;          // [K-1][B][Tmax]
+};
+
+__device__ __forceinline__ long long kv_row(const KVLayer& v, int b, int g, int pos) {
+    return ((long long)(b * v.Hkv + g) * v.Tmax + pos);
+}
+__device__ __forceinline__ long long res_row(const KVLayer& v, int b, int g, long long slot) {
+    return ((long long)(b * v.Hkv + g) * v.slots + slot);
+}
+__device__ __forceinline__ int res_row_bytes(const KVLayer& v) {
+    return v.res_bits == 16 ? v.hd * 2 : v.hd * v.res_bits / 8;
+}
+
+// Value of element e of row (b, g, pos) of K (kv=0) or V (kv=1) reconstructed
+// at loop `k`: base, then loop 2..k residuals (16-bit residual rows replace).
+__device__ __forceinline__ float kv_recon_elem(const KVLayer& v, int kv, int b, int g, int pos,
+                                               int e, int k) {
+    const long long row = kv_row(v, b, g, pos);
+    float x;
+    if (!v.lazy || v.base_bits == 16) {
+        x = bf2f(((const u16*)v.base[kv])[row * v.hd + e]);
+    } else {
+        const int8_t c = ((const int8_t*)v.base[kv])[row * v.hd + e];
+        x = (float)c * h2f(v.base_scale[kv][row * (v.hd / 32) + e / 32]);
+    }
+    if (!v.lazy) return x;
+    for (int kk = 2; kk <= k; ++kk) {
+        const int sl = v.slot[((long long)(kk - 2) * v.B + b) * v.Tmax + pos];
+        if (sl < 0) continue;
+        const long long rr = res_row(v, b, g, sl);
+        if (v.res_bits == 16) {
+            x = bf2f(((const u16*)v.res[kk - 2][kv])[rr * v.hd + e]);
+        } else {
+            int c;
+            if (v.res_bits == 8) {
+                c = ((const int8_t*)v.res[kk - 2][kv])[rr * v.hd + e];
+            } else {
+                const uint8_t byte = ((const uint8_t*)v.res[kk - 2][kv])[rr * (v.hd / 2) + e / 2];
+                int nib = (e & 1) ? (byte >> 4) : (byte & 0xF);
+                c = nib >= 8 ? nib - 16 : nib;
+            }
+            x = x + (float)c * h2f(v.res_scale[kk - 2][kv][rr * (v.hd / 32) + e / 32]);
+        }
+    }
+    return x;
+}

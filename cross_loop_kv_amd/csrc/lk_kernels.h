@@ -1,0 +1,86 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+// Every launcher enqueues on `st` and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lk_common.h"
+
+namespace lk {
+
+// ---- elementwise / selection (k_elem.hip)
+// h[r] = tok_emb[clamp(ids[r], 0, vocab-1)] as float32.
+hipError_t embed(const int32_t* ids, const u16* tok_emb, float* h, int rows, int d, int vocab,
+                 hipStream_t st);
+// if add != nullptr: x += add (written back).  Then y = x / sqrt(mean(x^2) + eps) * gain,
+// stored as bf16 (out_bf) or float32 (out_f32).
+hipError_t rmsnorm(float* x, const u16* add, const u16* gain, float eps, int rows, int d,
+                   u16* out_bf, float* out_f32, hipStream_t st);
+hipError_t add_rows(float* x, const u16* add, int rows, int d, hipStream_t st);
+hipError_t copy_f32(const float* src, float* dst, long long n, hipStream_t st);
+hipError_t fill_i32(int32_t* p, int32_t v, long long n, hipStream_t st);
+hipError_t fill_f32(float* p, float v, long long n, hipStream_t st);
+hipError_t delta_keys(const float* a, const float* b, int rows, int d, float* key, hipStream_t st);
+// xc[b*n + j] = h[b*T + idx[b*n + j]] + add; slot_map[b*Tmax + idx] = j when slot_map != nullptr.
+hipError_t gather_rows(const float* h, const int32_t* idx, int B, int n, int T, int d, const u16* add,
+                       float* xc, int32_t* slot_map, int Tmax, hipStream_t st);
+// key[b*T + idx] = ||xc - h[idx]||^2 (when key != nullptr), then h[b*T + idx] = xc.
+hipError_t scatter_rows(const float* xc, const int32_t* idx, int B, int n, int T, int d, float* h,
+                        float* key, hipStream_t st);
+// Top-n of each of `rows` rows of `cols` keys (ties to lower index), ascending indices.
+hipError_t topk_rows(const float* keys, int rows, int cols, int n, int32_t* out, hipStream_t st);
+// Quantize float32 rows [rows, hd] with a zero previous value (test entry point).
+hipError_t quantize_rows(const float* x, int rows, int hd, int bits, uint8_t* codes, u16* scales,
+                         hipStream_t st);
+
+// RoPE + KV-store write.  qkv float32 [rows, (H + 2 Hkv) hd]; q_out bf16 [rows, H hd].
+// Row r belongs to sequence b = r / rows_per_seq, at position pos[r] (or pos_offset +
+// r % rows_per_seq when pos == nullptr).  kvw describes where K/V go:
+struct KVWrite {
+    int kind;             // 0: bf16 rows at (b,g,pos); 1: lazy base; 2: lazy loop-k residual
+    KVLayer layer;        // destination layer (base/res pointers writable)
+    int loop;             // loop k of a residual write
+    const int32_t* slot_of_row;  // kind 2: slot per row (nullptr: slot = slot_base + row index in seq)
+    long long slot_base;
+    int32_t* slot_map_k;  // kind 2 decode: slot map of loop k to write (nullptr: already written)
+};
+hipError_t rope_kv_write(const float* qkv, int rows, int rows_per_seq, const int32_t* pos,
+                         int pos_offset, int H, int Hkv, int hd, const double* inv_freq, u16* q_out,
+                         const KVWrite& kvw, hipStream_t st);
+
+// ---- GEMM (k_gemm.hip).  C = A[M,K] * W[N,K]^T, bf16 inputs, fp32 accumulation.
+enum Epi { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2, EPI_GELU = 3 };
+// STORE/ADD: c float32 [M, N] (ldc = N).  SWIGLU: W = [gate (N rows); up (N rows)],
+// out bf16 [M, N].  GELU: out bf16 [M, N].
+hipError_t gemm(const u16* A, const u16* W, int M, int N, int K, int epi, float* c, u16* out_bf,
+                hipStream_t st);
+
+// ---- attention (k_attn.hip)
+// Dense causal prefill over a bf16 (or int8-base) layer: q bf16 [B*T, H*hd] (row b*T+i),
+// out bf16 [B*T, H*hd], lse float32 [B, H, T] (log2 units of the scaled scores).
+hipError_t attn_prefill(const u16* q, const KVLayer& kv, int B, int T, int H, u16* out, float* lse,
+                        hipStream_t st);
+// Column mass of loop-1 attention: mass float32 [B, Hkv, T].
+hipError_t column_mass(const u16* q, const KVLayer& kv, const float* lse, int B, int T, int H,
+                       float* mass, hipStream_t st);
+
+// Row attention over explicit column sets (decode and token-sparse prefill).
+struct RowsAttn {
+    const u16* q;          // bf16 [B * n_rows, H * hd]
+    const int32_t* qpos;   // [B * n_rows] positions (nullptr: all rows at `pos`)
+    int pos;
+    int B, n_rows, H;
+    KVLayer kv;
+    int k_loop;            // reconstruction loop (1 = base / plain rows)
+    const int32_t* cols;   // sparse: [B][Hkv][n_cols] ascending (nullptr: dense causal)
+    int n_cols, window;
+    int chunk, n_splits;   // columns per split, splits per row
+    float* part;           // [B*n_rows][Hkv][n_splits][G][hd + 2]
+    u16* out;              // bf16 [B * n_rows, H * hd]
+};
+// attn_rows_main writes the per-split partials; attn_rows_combine merges them into `out`.
+hipError_t attn_rows_main(const RowsAttn& a, hipStream_t st);
+hipError_t attn_rows_combine(const RowsAttn& a, hipStream_t st);
+
+}  // namespace lk

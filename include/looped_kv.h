@@ -1,0 +1,217 @@
+/*
+ * looped_kv.h -- C ABI of the MI355X (gfx950) library for lazy looped-Transformer
+ * inference.
+ *
+ * A looped Transformer runs P prelude layers, a block of R shared layers K times
+ * (a learned loop embedding added to the state before each loop), Q coda layers
+ * and a final RMSNorm; effective depth P + R*K + Q ("FlashLoop" walk-through,
+ * discosf.com, sections 3.1, 3.2, 4.1).  Each extra loop costs one more pass and,
+ * with a per-loop KV cache, one more KV set (FlashLoop abstract, arxivdaily.com;
+ * per_loop / last_loop modes: Looped Transformer tutorial, aiboss88.com, step 4).
+ * The lazy mode applies the three reductions named in the FlashLoop abstract:
+ * token-sparse loop updates, sparse attention over a stable subset of key
+ * columns, and low-bit quantized KV residuals between adjacent loops.  The
+ * abstract gives no exact rules; the rules implemented are:
+ *
+ *   loop 1 is dense and writes the base KV (bf16, or int8 group-32 codes with
+ *   float16 scales); its causal attention probabilities, summed over all
+ *   prompt queries and over the query heads of each KV head, rank the key
+ *   columns, and the top_s columns (ties to the lower index) form the stable
+ *   set S of that (sequence, shared layer, KV head);
+ *   at loop k >= 2 the n = clamp(ceil(rho*T - 1e-9), 1, T) tokens with the
+ *   largest ||h_{k-1} - h_{k-2}||^2 (h_0 = prelude output; ties to the lower
+ *   index) are recomputed and the others carry forward; a recomputed query at
+ *   position i attends over (S intersect [0, i]) union [i-window+1, i];
+ *   the loop-k KV of a recomputed row is stored as the quantized residual
+ *   against the loop-(k-1) reconstruction (int4 or int8 codes, one float16
+ *   scale per 32 elements, scale = fp16_rne(amax / qmax), code =
+ *   rint_half_even(r / scale) clamped to +-qmax); 16 bits stores the row.
+ *   A decode token runs every loop and is always stored.
+ *
+ * Memory: the caller owns all device memory (weights, ids, outputs, the KV-store
+ * buffer and the workspace); the library never allocates device memory.  All
+ * work is enqueued on the caller's HIP stream (passed as void*; NULL means the
+ * default stream) with no host synchronisation.  Every call returns LK_OK (0) or
+ * a negative LK_ERR_* code and leaves a message for lk_last_error() (thread
+ * local); errors detected on the host are reported before anything is launched.
+ * Calls that share a store or workspace must be ordered on one stream.
+ */
+#ifndef LOOPED_KV_H
+#define LOOPED_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LK_OK 0
+#define LK_ERR_INVALID_ARG (-1)  /* null pointer, bad size, inconsistent config */
+#define LK_ERR_UNSUPPORTED (-2)  /* valid but not implemented (e.g. head_dim 96) */
+#define LK_ERR_CAPACITY (-3)     /* store or workspace too small, decode past max */
+#define LK_ERR_HIP (-4)          /* a HIP runtime call or launch failed */
+#define LK_ERR_STATE (-5)        /* call out of order (decode before prefill, ...) */
+
+#define LK_MODE_PER_LOOP 0
+#define LK_MODE_LAST_LOOP 1
+#define LK_MODE_LAZY 2
+
+#define LK_ACT_GELU 0   /* exact erf GELU, FFN = W_down gelu(W_up x) */
+#define LK_ACT_SWIGLU 1 /* FFN = W_down (silu(W_gate x) * W_up x) */
+
+/* Model shape.  head_dim must be 32, 64 or 128; n_heads a multiple of
+ * n_kv_heads with n_heads / n_kv_heads in {1, 2, 4, 8}; d_model and ffn_dim
+ * multiples of 64.  RMSNorm epsilon and RoPE base (rotate-half) as given. */
+typedef struct {
+    int32_t vocab, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, ffn_act;
+    int32_t n_prelude, n_shared, n_loops, n_coda;
+    float rms_eps, rope_theta;
+} lk_model_cfg;
+
+/* Cache/update policy.  mode LK_MODE_*; rho in (0, 1] (kept-token fraction at
+ * loops >= 2), top_s >= 1 stable columns, window >= 1, base_bits 16 | 8,
+ * res_bits 16 | 8 | 4, group must be 32.  Only mode LK_MODE_LAZY reads the
+ * other fields. */
+typedef struct {
+    int32_t mode;
+    double rho;
+    int32_t top_s, window, base_bits, res_bits, group;
+} lk_lazy_cfg;
+
+/* Device pointers of one layer, all bfloat16 row-major:
+ *   attn_norm, ffn_norm  [d]
+ *   wqkv  [(H + 2 Hkv) * hd, d]  rows: q heads, then k heads, then v heads
+ *   wo    [d, H * hd]
+ *   w_in  SwiGLU: [2F, d] (gate rows 0..F-1, up rows F..2F-1); GELU: [F, d]
+ *   w_down [d, F] */
+typedef struct {
+    const void *attn_norm, *wqkv, *wo, *ffn_norm, *w_in, *w_down;
+} lk_layer_weights;
+
+/* tok_emb bf16 [vocab, d]; loop_emb bf16 [n_loops, d]; final_norm bf16 [d];
+ * layers: HOST array of P + R + Q entries (prelude, shared block, coda). */
+typedef struct {
+    const void *tok_emb, *loop_emb, *final_norm;
+    const lk_layer_weights *layers;
+} lk_weights;
+
+typedef struct lk_handle lk_handle;
+typedef struct lk_kv_store lk_kv_store;
+
+/* Validate the configuration and bind the weights (pointers are kept, not
+ * copied: they must stay valid until lk_destroy). */
+int lk_create(const lk_model_cfg *cfg, const lk_lazy_cfg *lazy, const lk_weights *w,
+              lk_handle **out);
+void lk_destroy(lk_handle *h);
+
+/* KV store for `batch` sequences: one prefill of `prompt_tokens` tokens, then
+ * decode steps up to `max_tokens` tokens per sequence.  Layout of the caller's
+ * device buffer (all regions 256-byte aligned), per mode:
+ *   dense prelude/coda layers: bf16 [P+Q][K|V][batch][Hkv][max_tokens][hd];
+ *   per_loop: bf16 [n_loops][R][K|V][batch][Hkv][max_tokens][hd];
+ *   last_loop: bf16 [R][K|V][batch][Hkv][max_tokens][hd];
+ *   lazy: base [R][K|V][batch][Hkv][max_tokens][hd] as bf16, or int8 codes plus
+ *   float16 scales [...][hd/32]; residuals [n_loops-1][R][K|V][batch][Hkv][slots]
+ *   rows (int4 packed two per byte low nibble first, int8, or bf16) plus float16
+ *   scales; slot maps int32 [n_loops-1][batch][max_tokens] (-1 = not stored);
+ *   column sets int32 [R][batch][Hkv][min(top_s, prompt_tokens)];
+ *   slots = n_selected(prompt_tokens) + max_tokens - prompt_tokens.
+ * With dev_buf == NULL only *need_bytes is written (size query).  Otherwise
+ * buf_bytes must be >= *need_bytes; the slot maps are cleared on `stream`
+ * (void*, may be NULL) and *out receives a host handle. */
+int lk_kv_store_alloc(lk_handle *h, int32_t batch, int32_t prompt_tokens, int32_t max_tokens,
+                      void *dev_buf, size_t buf_bytes, void *stream, lk_kv_store **out,
+                      size_t *need_bytes);
+void lk_kv_store_release(lk_kv_store *s);
+
+/* Bytes the store holds for its current length t (prompt + decoded tokens):
+ * *shared = shared-block KV (base, residual rows, slot maps, column sets, or
+ * the dense per-loop / last-loop rows); *total adds the prelude/coda rows.
+ * Per-token figures divide by batch * t. */
+int lk_kv_store_bytes_used(const lk_kv_store *s, size_t *shared, size_t *total);
+/* Current tokens per sequence (0 before prefill). */
+int lk_kv_store_length(const lk_kv_store *s, int32_t *tokens);
+
+/* Workspace bytes for a prefill of batch x tokens (tokens = 1 for decode). */
+int lk_workspace_bytes(lk_handle *h, int32_t batch, int32_t tokens, size_t *bytes);
+
+/* Prefill.  d_ids int32 [B, T] (device), B = store batch, T = store
+ * prompt_tokens; d_out float32 [B, T, d] receives the final-normed hidden
+ * states.  Runs embed, prelude, the K loops (lazy: dense loop 1 with column
+ * selection, then token-sparse loops 2..K), coda and the final norm. */
+int lk_looped_prefill(lk_handle *h, lk_kv_store *s, const int32_t *d_ids, int32_t B, int32_t T,
+                      float *d_out, void *d_ws, size_t ws_bytes, void *stream);
+
+/* One decode step: d_ids int32 [B] (device, the next token of every sequence),
+ * d_out float32 [B, d].  Appends one token per sequence at position t = current
+ * length; LK_ERR_CAPACITY once t == max_tokens, LK_ERR_STATE before prefill. */
+int lk_looped_decode_step(lk_handle *h, lk_kv_store *s, const int32_t *d_ids, float *d_out,
+                          void *d_ws, size_t ws_bytes, void *stream);
+
+/* Layer applications one prefill/decode pass runs per token: P + R*K + Q. */
+int lk_effective_depth(const lk_handle *h, int32_t *depth);
+
+const char *lk_last_error(void);
+
+/* Instrumentation: bracket every launch of one kernel class with HIP events on
+ * the stream of the call that launches it.  Classes: "attn_decode_dense" (decode
+ * attention over dense / base rows), "attn_decode_sparse", "attn_prefill",
+ * "column_mass", "attn_prefill_sparse", "gemm_decode", "gemm_prefill"; NULL
+ * disables.  Enabling clears the record.  Not thread-safe per handle. */
+int lk_timing_enable(lk_handle *h, const char *kernel_class);
+/* Launches recorded since lk_timing_enable and their summed event time in ms
+ * (waits for the recorded events). */
+int lk_timing_read(lk_handle *h, int32_t *launches, double *total_ms);
+
+/* ---------------------------------------------------------------------------
+ * Test and inspection entry points (same error conventions).
+ * ------------------------------------------------------------------------- */
+
+/* Device addresses of a store's regions (NULL where the mode has none). */
+typedef struct {
+    void *dense;            /* prelude/coda rows */
+    void *loop_rows;        /* per_loop or last_loop rows */
+    void *base_codes;       /* lazy base: bf16 rows or int8 codes */
+    void *base_scales;      /* lazy base scales (int8 base only) */
+    void *res_codes;        /* residual rows/codes */
+    void *res_scales;       /* residual scales (4/8-bit residuals) */
+    int32_t *slot_maps;     /* [n_loops-1][batch][max_tokens] */
+    int32_t *columns;       /* [R][batch][Hkv][n_columns] */
+    int64_t slots;          /* residual slots per (loop, layer, K|V, seq, head) */
+    int32_t n_selected;     /* kept tokens per sequence at loops >= 2 */
+    int32_t n_columns;      /* min(top_s, prompt_tokens) */
+    int64_t res_row_bytes;  /* bytes of one residual row (hd elements) */
+} lk_store_view;
+int lk_kv_store_view(const lk_kv_store *s, lk_store_view *v);
+
+/* Override the selections of the next prefill with caller data (device
+ * pointers read during lk_looped_prefill; NULL restores natural selection):
+ * tokens int32 [n_loops-1][batch][n_selected] ascending per row;
+ * columns int32 [R][batch][Hkv][n_columns] ascending per row. */
+int lk_kv_store_force_selection(lk_kv_store *s, const int32_t *d_tokens, const int32_t *d_columns);
+
+/* Top-n selector: for each of `rows` rows of `cols` float32 keys, the n largest
+ * (ties to the lower index) as ascending int32 indices [rows, n]. */
+int lk_dbg_topk(const float *d_keys, int32_t rows, int32_t cols, int32_t n, int32_t *d_idx,
+                void *stream);
+
+/* Residual quantizer on float32 rows [rows, hd] (hd multiple of 32):
+ * codes uint8 [rows, hd*bits/8] (int4 packed low nibble first, or int8) and
+ * float16 scales [rows, hd/32] (raw bits as uint16). */
+int lk_dbg_quantize(const float *d_x, int32_t rows, int32_t hd, int32_t bits, uint8_t *d_codes,
+                    uint16_t *d_scales, void *stream);
+
+/* Delta keys: d_key[m] = sum_j (a[m, j] - b[m, j])^2 over float32 rows [rows, d]. */
+int lk_dbg_delta(const float *d_a, const float *d_b, int32_t rows, int32_t d, float *d_key,
+                 void *stream);
+
+/* C[M, N] = A[M, K] * W[N, K]^T with bf16 A and W and float32 C (row-major). */
+int lk_dbg_gemm(const void *d_a, const void *d_w, float *d_c, int32_t M, int32_t N, int32_t K,
+                void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOOPED_KV_H */

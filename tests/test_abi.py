@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: symbols, struct layouts, validation, size queries."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from cross_loop_kv_amd import binding as B
+from cross_loop_kv_amd import inputs as I
+from oracle import accounting
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "looped_kv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lk_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    lib = B.lib()
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in B.EXPORTED, n
+
+
+def test_struct_layouts_match_the_header():
+    prog = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "looped_kv.h"
+#define P(T, f) printf("%s.%s %zu\n", #T, #f, offsetof(T, f));
+int main(void) {
+  printf("lk_model_cfg %zu\nlk_lazy_cfg %zu\nlk_layer_weights %zu\nlk_weights %zu\nlk_store_view %zu\n",
+         sizeof(lk_model_cfg), sizeof(lk_lazy_cfg), sizeof(lk_layer_weights), sizeof(lk_weights),
+         sizeof(lk_store_view));
+  P(lk_model_cfg, ffn_act) P(lk_model_cfg, rms_eps) P(lk_model_cfg, rope_theta)
+  P(lk_lazy_cfg, rho) P(lk_lazy_cfg, top_s) P(lk_lazy_cfg, group)
+  P(lk_weights, layers) P(lk_layer_weights, w_down)
+  P(lk_store_view, slots) P(lk_store_view, n_selected) P(lk_store_view, res_row_bytes)
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "p.c")
+        exe = os.path.join(d, "p")
+        open(c, "w").write(prog)
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    got = dict(line.rsplit(" ", 1) for line in out.strip().splitlines())
+    for name in ("lk_model_cfg", "lk_lazy_cfg", "lk_layer_weights", "lk_weights", "lk_store_view"):
+        assert int(got[name]) == ctypes.sizeof(getattr(B, name)), name
+    for key, val in got.items():
+        if "." in key:
+            t, f = key.split(".")
+            assert getattr(getattr(B, t), f).offset == int(val), key
+
+
+def _handle(shape, lazy):
+    cfg = B.model_cfg(shape)
+    lz = B.lazy_cfg(lazy)
+    n = shape.n_prelude + shape.n_shared + shape.n_coda
+    lw = (B.lk_layer_weights * n)()
+    for i in range(n):
+        lw[i] = B.lk_layer_weights(16, 16, 16, 16, 16, 16)   # never dereferenced on the host
+    w = B.lk_weights(16, 16, 16, lw)
+    return B.lk_create(cfg, lz, w)
+
+
+@pytest.mark.parametrize("name", list(I.WORKLOADS))
+def test_store_size_query_matches_closed_form(name):
+    wl = I.workload(name)
+    for mode in ("per_loop", "last_loop", "lazy"):
+        lz = I.Lazy(**{**wl.lazy.__dict__, "mode": mode})
+        h = _handle(wl.shape, lz)
+        try:
+            T, Tm = min(wl.prompt, 4096), min(wl.prompt, 4096) + 64
+            _, need = B.lk_kv_store_alloc(h, wl.batch, T, Tm)
+            exp = accounting.kv_bytes(wl.shape, lz, wl.batch, T, Tm)["total"]
+            assert exp <= need <= exp + 256 * 12, (mode, need, exp)
+            assert B.lk_effective_depth(h) == accounting.effective_depth(wl.shape)
+            ws1 = B.lk_workspace_bytes(h, wl.batch, 1)
+            wsT = B.lk_workspace_bytes(h, wl.batch, T)
+            assert 0 < ws1 <= wsT
+        finally:
+            B.lk_destroy(h)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 96, -2), ("n_kv_heads", 3, -1), ("n_shared", 0, -1), ("d_model", 100, -2),
+    ("n_loops", 0, -1), ("ffn_act", "relu", None),
+])
+def test_create_rejects_bad_model_configs(field, value, code):
+    s = I.workload("tiny_1p2x2c1_t32").shape
+    if value == "relu":
+        with pytest.raises(KeyError):
+            B.model_cfg(I.Shape(**{**s.__dict__, "ffn_act": "relu"}))
+        return
+    setattr(s, field, value)
+    with pytest.raises(B.LKError) as e:
+        _handle(s, I.Lazy(mode="per_loop"))
+    assert e.value.code == code
+
+
+@pytest.mark.parametrize("kw", [dict(rho=0.0), dict(rho=1.5), dict(window=0), dict(top_s=0),
+                                dict(base_bits=4), dict(res_bits=2), dict(group=16)])
+def test_create_rejects_bad_lazy_configs(kw):
+    s = I.workload("tiny_1p2x2c1_t32").shape
+    lz = I.Lazy(mode="lazy", rho=0.5, top_s=8, window=4, base_bits=16, res_bits=8)
+    for k, v in kw.items():
+        setattr(lz, k, v)
+    with pytest.raises(B.LKError) as e:
+        _handle(s, lz)
+    assert e.value.code in (-1, -2)
+
+
+def test_alloc_and_workspace_argument_errors():
+    wl = I.workload("tiny_1p2x2c1_t32")
+    h = _handle(wl.shape, wl.lazy)
+    try:
+        for args in ((0, 8, 8), (1, 0, 8), (1, 9, 8)):
+            with pytest.raises(B.LKError) as e:
+                B.lk_kv_store_alloc(h, *args)
+            assert e.value.code == -1
+        _, need = B.lk_kv_store_alloc(h, 1, 8, 8)
+        with pytest.raises(B.LKError) as e:   # buffer too small: refused before any launch
+            B.lk_kv_store_alloc(h, 1, 8, 8, dev_buf=256, buf_bytes=need - 1)
+        assert e.value.code == -3
+        with pytest.raises(B.LKError):
+            B.lk_workspace_bytes(h, 0, 1)
+    finally:
+        B.lk_destroy(h)
+
+
+def test_null_arguments_are_errors():
+    lib = B.lib()
+    assert lib.lk_looped_prefill(None, None, None, 1, 1, None, None, 0, None) == -1
+    assert lib.lk_looped_decode_step(None, None, None, None, None, 0, None) == -1
+    assert lib.lk_dbg_topk(None, 1, 1, 1, None, None) == -1
+    assert b"null" in lib.lk_last_error()
