@@ -56,7 +56,8 @@ class lk_store_view(C.Structure):
     _fields_ = [("dense", C.c_void_p), ("loop_rows", C.c_void_p), ("base_codes", C.c_void_p),
                 ("base_scales", C.c_void_p), ("res_codes", C.c_void_p), ("res_scales", C.c_void_p),
                 ("slot_maps", C.c_void_p), ("columns", C.c_void_p), ("slots", C.c_int64),
-                ("n_selected", C.c_int32), ("n_columns", C.c_int32), ("res_row_bytes", C.c_int64)]
+                ("n_selected", C.c_int32), ("n_columns", C.c_int32), ("res_row_bytes", C.c_int64),
+                ("row_stride", C.c_int32)]
 
 
 _SIGS = {
@@ -78,6 +79,7 @@ _SIGS = {
     "lk_last_error": (C.c_char_p, []),
     "lk_kv_store_view": (C.c_int, [C.c_void_p, C.POINTER(lk_store_view)]),
     "lk_kv_store_force_selection": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
+    "lk_kv_store_keep_codes": (C.c_int, [C.c_void_p, C.c_int32]),
     "lk_timing_enable": (C.c_int, [C.c_void_p, C.c_char_p]),
     "lk_timing_read": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
     "lk_dbg_topk": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
@@ -188,6 +190,10 @@ def lk_kv_store_force_selection(s: int, d_tokens, d_columns) -> None:
     _check(lib().lk_kv_store_force_selection(s, d_tokens, d_columns))
 
 
+def lk_kv_store_keep_codes(s: int, enable: bool) -> None:
+    _check(lib().lk_kv_store_keep_codes(s, 1 if enable else 0))
+
+
 def lk_timing_enable(h: int, kernel_class: Optional[str]) -> None:
     _check(lib().lk_timing_enable(h, kernel_class.encode() if kernel_class else None))
 
@@ -257,6 +263,9 @@ class Store:
         self._forced = (tokens, columns)
         lk_kv_store_force_selection(self.s, tokens.data_ptr() if tokens is not None else None,
                                     columns.data_ptr() if columns is not None else None)
+
+    def keep_codes(self, enable: bool = True):
+        lk_kv_store_keep_codes(self.s, enable)
 
     def close(self):
         if getattr(self, "s", None):

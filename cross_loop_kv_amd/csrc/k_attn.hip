@@ -5,58 +5,138 @@
 // key columns, so loops k >= 2 attend over that subset plus a recent window,
 // reading a KV that is the previous loop's plus quantized residuals.
 //
-// * attn_prefill: causal flash attention, v_mfma_f32_32x32x16_bf16.  Scores are
-//   formed transposed (S^T = K Q^T) so that every lane owns one query column: the
-//   softmax statistics stay per lane (pairs of lanes l, l+32 share a query).  The
-//   P^T operand of O^T = V^T P^T comes straight from the score accumulators; the
-//   key order inside each 16-key MFMA step is permuted to match the accumulator
-//   layout, and V^T is read from the LDS tile with the same permutation.
+// Scores are kept in log2 units (q.k * log2(e) / sqrt(hd)) everywhere, so that the
+// split partials (m, l, o) of every kernel combine the same way.
+//
+// * attn_prefill: causal flash attention with v_mfma_f32_32x32x16_bf16.  Scores
+//   are formed transposed (S^T = K Q^T) so every lane owns one query column and
+//   the softmax statistics stay per lane (lanes l and l+32 share a query).  The
+//   K rows of a tile are staged in LDS in a permuted order chosen so that each
+//   lane's score accumulators cover 8 consecutive keys per 16-key step; those
+//   accumulators are then directly the P^T operand of O^T = V^T P^T, and the V^T
+//   operand is one 16-byte LDS read out of the 8-key-interleaved V tile.
 // * column_mass: the per-column sum of the loop-1 softmax probabilities, keys
 //   outer / queries inner, so each column is reduced in one fixed order.
-// * attn_rows: one query row (decode token or kept prefill token) over its own
-//   column list, split over columns; reconstructs K/V from the store in fp32
-//   (base + loop residuals), lanes own keys for q.k and head dims for p.V.
+// * attn_decode_dense: one query token over contiguous rows (base / dense
+//   caches), split over the context.  v_mfma_f32_16x16x32 (f16 for int8 rows,
+//   bf16 for bf16 rows) with both operands loaded straight from HBM: K rows for
+//   S^T = K Q^T, the 8-key-interleaved V for O^T = V^T P^T.  int8 codes become
+//   f16 with a byte-permute "magic number" conversion and are scaled by their
+//   float16 group scales in packed f16.
+// * attn_rows: query rows over explicit sparse column sets (decode loops >= 2
+//   and kept prefill tokens); reconstructs K/V from the store in fp32 (base +
+//   loop residuals); lanes own keys for q.k and head dims for p.V.
 #include "lk_kernels.h"
 
 namespace lk {
 
 namespace {
 
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
 constexpr float kLog2e = 1.4426950408889634f;
 
-// 8 consecutive elements of K or V row (b, g, pos) as bf16 (dequantized if int8).
+__device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(half8, v); }
+
+// 8 signed bytes -> 8 float16 (exact), multiplied by per-pair scales (packed f16).
+// Byte j of the input becomes element j.  Each byte is biased to u = c + 128 and
+// placed under the float16 exponent of 1024 (bits 0x64uu = 1024 + u); subtracting
+// 1152 leaves c exactly.
+__device__ __forceinline__ uint4 i8x8_to_f16(uint2 c, uint4 scale_pairs) {
+    const uint32_t u0 = c.x ^ 0x80808080u, u1 = c.y ^ 0x80808080u;
+    uint32_t w[4];
+    w[0] = __builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u);
+    w[1] = __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u);
+    w[2] = __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u);
+    w[3] = __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u);
+    const uint32_t sc[4] = {scale_pairs.x, scale_pairs.y, scale_pairs.z, scale_pairs.w};
+    const half2v bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        half2v h = __builtin_bit_cast(half2v, w[j]) - bias;
+        h = h * __builtin_bit_cast(half2v, sc[j]);
+        o[j] = __builtin_bit_cast(uint32_t, h);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// 8 consecutive K elements of row (b, g, pos) as bf16 (dequantized if int8).
 template <int HD, bool I8>
-__device__ __forceinline__ uint4 load_kv8(const KVLayer& kv, int which, int b, int g, int pos, int e0) {
+__device__ __forceinline__ uint4 load_k8_bf16(const KVLayer& kv, int b, int g, int pos, int e0) {
     const long long row = kv_row(kv, b, g, pos);
-    if (!I8) return *(const uint4*)((const u16*)kv.base[which] + row * HD + e0);
-    const uint2 c = *(const uint2*)((const int8_t*)kv.base[which] + row * HD + e0);
-    const float s = h2f(kv.base_scale[which][row * (HD / 32) + e0 / 32]);
-    uint32_t w[2] = {c.x, c.y};
-    uint4 out;
-    uint32_t* o = (uint32_t*)&out;
+    if (!I8) return *(const uint4*)((const u16*)kv.base[0] + row * HD + e0);
+    const uint2 c = *(const uint2*)((const int8_t*)kv.base[0] + row * HD + e0);
+    const float s = h2f(kv.base_scale[0][row * (HD / 32) + e0 / 32]);
+    const uint32_t wv[2] = {c.x, c.y};
+    uint32_t o[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const uint32_t word = w[q >> 1];
+        const uint32_t word = wv[q >> 1];
         const int sh = (q & 1) * 16;
-        const float a = (float)(int8_t)((word >> sh) & 0xFF) * s;
-        const float bb = (float)(int8_t)((word >> (sh + 8)) & 0xFF) * s;
-        o[q] = pack_bf2(a, bb);
+        o[q] = pack_bf2((float)(int8_t)((word >> sh) & 0xFF) * s, (float)(int8_t)((word >> (sh + 8)) & 0xFF) * s);
     }
-    return out;
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Zero the bf16/f16 elements j >= valid of an 8-element operand.
+__device__ __forceinline__ uint4 mask_tail8(uint4 v, int valid) {
+    if (valid >= 8) return v;
+    uint32_t o[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (2 * q >= valid) o[q] &= 0xFFFF0000u;
+        if (2 * q + 1 >= valid) o[q] &= 0x0000FFFFu;
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Eight keys [pos0, pos0+8) of V at head dim e as bf16 (pos0 multiple of 8), keys >= valid zeroed.
+template <int HD, bool I8>
+__device__ __forceinline__ uint4 load_v8_bf16(const KVLayer& kv, int b, int g, int pos0, int e, int valid) {
+    const long long idx = v_elem(kv, b, g, pos0, e);
+    uint4 out;
+    if (!I8) {
+        out = *(const uint4*)((const u16*)kv.base[1] + idx);
+    } else {
+        const uint2 c = *(const uint2*)((const int8_t*)kv.base[1] + idx);
+        const u16* sp = kv.base_scale[1] + v_scale_idx(kv, b, g, pos0, e / 32);
+        const uint32_t wv[2] = {c.x, c.y};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t word = wv[q >> 1];
+            const int sh = (q & 1) * 16;
+            o[q] = pack_bf2((float)(int8_t)((word >> sh) & 0xFF) * h2f(sp[2 * q]),
+                            (float)(int8_t)((word >> (sh + 8)) & 0xFF) * h2f(sp[2 * q + 1]));
+        }
+        out = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    return mask_tail8(out, valid);
 }
 
 // ---------------------------------------------------------------- flash prefill
+// Key held by LDS row r of a 32-key K tile: lane group kg of the 32x32 score
+// accumulator then owns keys 8kg..8kg+7 (accumulators 0..7) and 16+8kg.. (8..15).
+__device__ __forceinline__ int flash_key_of_row(int r) {
+    const int a = r >> 3;
+    return ((a >= 2) ? 16 : 0) + 8 * ((r >> 2) & 1) + 4 * (a & 1) + (r & 3);
+}
+
 template <int HD, bool I8>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(const u16* __restrict__ Q, KVLayer kv,
                                                            int T, int H, u16* __restrict__ O,
                                                            float* __restrict__ LSE, float sl2) {
     constexpr int KT = 32;
-    constexpr int LDV = HD + 8;
+    constexpr int LDK = HD + 8;       // K tile row (keys x hd)
+    constexpr int LDV = KT + 8;       // V^T tile row (hd x keys)
     constexpr int CPR = HD / 8;
-    constexpr int NCH = 2 * KT * CPR;
-    constexpr int PER = (NCH + 255) / 256;
-    __shared__ __attribute__((aligned(16))) u16 Ks[2][KT * LDV];
-    __shared__ __attribute__((aligned(16))) u16 Vs[2][KT * LDV];
+    constexpr int NKC = KT * CPR;     // 16-byte K chunks per tile
+    constexpr int NVC = (KT / 8) * HD;  // 16-byte V chunks per tile (8 keys x one e)
+    constexpr int PER = (NKC + NVC + 255) / 256;
+    __shared__ __attribute__((aligned(16))) u16 Ks[2][KT * LDK];
+    __shared__ __attribute__((aligned(16))) u16 Vt[2][HD * LDV];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int kg = lane >> 5, l32 = lane & 31;
     const int h = blockIdx.y, b = blockIdx.z;
@@ -88,11 +168,14 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const u16* __restrict
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * 256;
             regs[p] = make_uint4(0, 0, 0, 0);
-            if (c < NCH) {
-                const int which = c / (KT * CPR);
-                const int rem = c % (KT * CPR);
-                const int key = t * KT + rem / CPR;
-                if (key < T) regs[p] = load_kv8<HD, I8>(kv, which, b, g, key, (rem % CPR) * 8);
+            if (c < NKC) {
+                const int key = t * KT + flash_key_of_row(c / CPR);
+                if (key < T) regs[p] = load_k8_bf16<HD, I8>(kv, b, g, key, (c % CPR) * 8);
+            } else if (c < NKC + NVC) {
+                const int cc = c - NKC;
+                const int blk = cc / HD, e = cc % HD;
+                const int pos0 = t * KT + blk * 8;
+                if (pos0 < T) regs[p] = load_v8_bf16<HD, I8>(kv, b, g, pos0, e, T - pos0);
             }
         }
     };
@@ -100,11 +183,11 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const u16* __restrict
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * 256;
-            if (c < NCH) {
-                const int which = c / (KT * CPR);
-                const int rem = c % (KT * CPR);
-                u16* dst = (which ? Vs[buf] : Ks[buf]) + (rem / CPR) * LDV + (rem % CPR) * 8;
-                *(uint4*)dst = regs[p];
+            if (c < NKC) {
+                *(uint4*)&Ks[buf][(c / CPR) * LDK + (c % CPR) * 8] = regs[p];
+            } else if (c < NKC + NVC) {
+                const int cc = c - NKC;
+                *(uint4*)&Vt[buf][(cc % HD) * LDV + (cc / HD) * 8] = regs[p];
             }
         }
     };
@@ -121,13 +204,13 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const u16* __restrict
             for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < HD / 16; ++ks) {
-                const bf16x8 a = as_bf16x8(*(const uint4*)&Ks[cur][l32 * LDV + ks * 16 + kg * 8]);
+                const bf16x8 a = as_bf16x8(*(const uint4*)&Ks[cur][l32 * LDK + ks * 16 + kg * 8]);
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
             }
             float mx = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int key = kbase + 8 * (i >> 2) + 4 * kg + (i & 3);
+                const int key = kbase + ((i < 8) ? 8 * kg + i : 16 + 8 * kg + (i - 8));
                 const float v = (key <= qi && key < T) ? s[i] * sl2 : -INFINITY;
                 s[i] = v;
                 mx = fmaxf(mx, v);
@@ -161,18 +244,9 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const u16* __restrict
             const bf16x8 pb0 = as_bf16x8(pu0), pb1 = as_bf16x8(pu1);
 #pragma unroll
             for (int c = 0; c < HD / 32; ++c) {
-                const int e = c * 32 + l32;
-                uint32_t v0[4], v1[4];
-#pragma unroll
-                for (int jj = 0; jj < 8; jj += 2) {
-                    const int ka = (jj < 4) ? 4 * kg + jj : 8 + 4 * kg + (jj - 4);
-                    const int kb = ka + 1;
-                    v0[jj >> 1] = (uint32_t)Vs[cur][ka * LDV + e] | ((uint32_t)Vs[cur][kb * LDV + e] << 16);
-                    v1[jj >> 1] = (uint32_t)Vs[cur][(16 + ka) * LDV + e] |
-                                  ((uint32_t)Vs[cur][(16 + kb) * LDV + e] << 16);
-                }
-                const bf16x8 va0 = as_bf16x8(make_uint4(v0[0], v0[1], v0[2], v0[3]));
-                const bf16x8 va1 = as_bf16x8(make_uint4(v1[0], v1[1], v1[2], v1[3]));
+                const u16* vrow = &Vt[cur][(c * 32 + l32) * LDV];
+                const bf16x8 va0 = as_bf16x8(*(const uint4*)(vrow + 8 * kg));
+                const bf16x8 va1 = as_bf16x8(*(const uint4*)(vrow + 16 + 8 * kg));
                 oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pb0, oacc[c], 0, 0, 0);
                 oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pb1, oacc[c], 0, 0, 0);
             }
@@ -217,7 +291,7 @@ __global__ __launch_bounds__(256) void column_mass_kernel(const u16* __restrict_
 #pragma unroll
         for (int ks = 0; ks < HD / 16; ++ks) {
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (key < T) v = load_kv8<HD, I8>(kv, 0, b, g, key, ks * 16 + kg * 8);
+            if (key < T) v = load_k8_bf16<HD, I8>(kv, b, g, key, ks * 16 + kg * 8);
             kf[ks] = as_bf16x8(v);
         }
     }
@@ -273,14 +347,279 @@ __global__ __launch_bounds__(256) void column_mass_kernel(const u16* __restrict_
     }
 }
 
-// ---------------------------------------------------------------- row attention
-// Reconstruct 32 consecutive elements [e0, e0+32) of K/V row (b, g, pos) at loop k.
+// ---------------------------------------------------------------- dense decode (MFMA)
+// Row types of the dense decode kernel.
+enum { RT_BF16 = 0, RT_I8 = 1, RT_F16 = 2 };
+
+template <int HD, int G, int RT>
+__global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
+    constexpr bool I8 = RT == RT_I8;
+    constexpr bool HALF = RT != RT_BF16;  // f16 MFMA (int8 codes are converted to f16)
+    constexpr int NQ = HD / 32;   // 32-wide k-steps over hd (= scale groups)
+    constexpr int NE = HD / 16;   // 16-row tiles of O^T
+    const int split = blockIdx.x, bg = blockIdx.y;
+    const KVLayer& kv = a.kv;
+    const int Hkv = kv.Hkv, b = bg / Hkv, g = bg % Hkv;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c16 = lane & 15, kgrp = lane >> 4;
+    const int ncols = a.lens ? a.lens[bg] : a.pos + 1;
+    const int c_begin = split * a.chunk;
+    const int c_end = min(ncols, c_begin + a.chunk);
+    const float sl2 = kLog2e / sqrtf((float)HD);
+
+    // Q^T operand: lane (head c16, kgrp) holds q[h][32j + 8kgrp .. +8]
+    uint4 qop[NQ];
+    const bool hvalid = c16 < G;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (hvalid) v = *(const uint4*)(a.q + (long long)b * a.H * HD + (g * G + c16) * HD + 32 * j + 8 * kgrp);
+        if (HALF) {  // bf16 -> f16
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                o[t] = (uint32_t)f2h_bits(__uint_as_float(wv[t] << 16)) |
+                       ((uint32_t)f2h_bits(__uint_as_float(wv[t] & 0xFFFF0000u)) << 16);
+            v = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        qop[j] = v;
+    }
+    f32x4 oacc[NE];
+#pragma unroll
+    for (int et = 0; et < NE; ++et) oacc[et] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+
+    for (int kb = c_begin + 32 * w; kb < c_end; kb += 128) {
+        // ---- S^T = K Q^T: n-tile nt covers keys kb + 8*(r/4) + 4*nt + r%4 for row r
+        f32x4 sacc[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int key = min(kb + 8 * (c16 >> 2) + 4 * nt + (c16 & 3), ncols - 1);
+            const long long row = kv_row(kv, b, g, key);
+            sacc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            if (I8) {
+                const u16* ks = kv.base_scale[0] + row * NQ;
+#pragma unroll
+                for (int j = 0; j < NQ; ++j) {
+                    const uint2 c = *(const uint2*)((const int8_t*)kv.base[0] + row * HD + 32 * j + 8 * kgrp);
+                    const uint32_t s1 = ks[j];
+                    const uint32_t sp = s1 | (s1 << 16);
+                    const uint4 kf = i8x8_to_f16(c, make_uint4(sp, sp, sp, sp));
+                    sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kf), as_half8(qop[j]), sacc[nt], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NQ; ++j) {
+                    const uint4 kf = *(const uint4*)((const u16*)kv.base[0] + row * HD + 32 * j + 8 * kgrp);
+                    if (HALF)
+                        sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kf), as_half8(qop[j]), sacc[nt], 0, 0, 0);
+                    else
+                        sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qop[j]), sacc[nt], 0, 0, 0);
+                }
+            }
+        }
+        // lane (kgrp, head c16) holds keys kb + 8kgrp + 4nt + i
+        float s[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = kb + 8 * kgrp + 4 * nt + i;
+                const float v = key < c_end ? sacc[nt][i] * sl2 : -INFINITY;
+                s[nt * 4 + i] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);
+        const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - m_new);
+        float p[8];
+        float rs = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[j] = (s[j] == -INFINITY) ? 0.f : exp2f(s[j] - m_new);
+            rs += p[j];
+        }
+        rs += __shfl_xor(rs, 16);
+        rs += __shfl_xor(rs, 32);
+        l = l * alpha + rs;
+        m = m_new;
+#pragma unroll
+        for (int et = 0; et < NE; ++et) oacc[et] *= alpha;
+        // ---- O^T += V^T P^T; lane (e, kgrp): V[keys kb+8kgrp .. +8][e] is one contiguous run
+        uint4 pu;
+        if (HALF) {
+            pu.x = (uint32_t)f2h_bits(p[0]) | ((uint32_t)f2h_bits(p[1]) << 16);
+            pu.y = (uint32_t)f2h_bits(p[2]) | ((uint32_t)f2h_bits(p[3]) << 16);
+            pu.z = (uint32_t)f2h_bits(p[4]) | ((uint32_t)f2h_bits(p[5]) << 16);
+            pu.w = (uint32_t)f2h_bits(p[6]) | ((uint32_t)f2h_bits(p[7]) << 16);
+        } else {
+            pu.x = pack_bf2(p[0], p[1]);
+            pu.y = pack_bf2(p[2], p[3]);
+            pu.z = pack_bf2(p[4], p[5]);
+            pu.w = pack_bf2(p[6], p[7]);
+        }
+        const int valid = c_end - (kb + 8 * kgrp);
+        // rows past the end of the context are unwritten: clamp the block address, zero the values
+        const int pos0 = min(kb + 8 * kgrp, ((ncols - 1) >> 3) << 3);
+#pragma unroll
+        for (int et = 0; et < NE; ++et) {
+            const int e = 16 * et + c16;
+            const long long vi = v_elem(kv, b, g, pos0, e);
+            uint4 vf;
+            if (I8) {
+                const uint2 c = *(const uint2*)((const int8_t*)kv.base[1] + vi);
+                const uint4 sp = *(const uint4*)(kv.base_scale[1] + v_scale_idx(kv, b, g, pos0, e >> 5));
+                vf = i8x8_to_f16(c, sp);
+            } else {
+                vf = *(const uint4*)((const u16*)kv.base[1] + vi);
+            }
+            vf = mask_tail8(vf, valid);
+            if (HALF)
+                oacc[et] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(vf), as_half8(pu), oacc[et], 0, 0, 0);
+            else
+                oacc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), as_bf16x8(pu), oacc[et], 0, 0, 0);
+        }
+    }
+    // ---- merge the four waves: O^T lane holds e = 16et + 4kgrp + i for head c16
+    __shared__ float sm_m[4][16], sm_l[4][16];
+    __shared__ float sm_o[4][G][HD];
+    if (kgrp == 0) {
+        sm_m[w][c16] = m;
+        sm_l[w][c16] = l;
+    }
+    if (hvalid) {
+#pragma unroll
+        for (int et = 0; et < NE; ++et)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm_o[w][c16][16 * et + 4 * kgrp + i] = oacc[et][i];
+    }
+    __syncthreads();
+    float* P = a.part + ((long long)bg * a.n_splits + split) * G * (HD + 2);
+    for (int idx = threadIdx.x; idx < G * HD; idx += 256) {
+        const int hh = idx / HD, e = idx % HD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+        float L = 0.f, acc = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int ww = 0; ww < 4; ++ww) {
+                if (sm_m[ww][hh] == -INFINITY) continue;
+                const float f = exp2f(sm_m[ww][hh] - M);
+                L += f * sm_l[ww][hh];
+                acc += f * sm_o[ww][hh][e];
+            }
+        }
+        P[hh * (HD + 2) + e] = acc;
+        if (e == 0) {
+            P[hh * (HD + 2) + HD] = M;
+            P[hh * (HD + 2) + HD + 1] = L;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- sparse decode: gather
+// 8 consecutive elements [e0, e0+8) of residual row rr (loop kk): added to x, or
+// substituted for 16-bit residual rows.
 template <int HD>
-__device__ __forceinline__ void recon32(const KVLayer& v, int kv, int b, int g, int pos, int e0, int k,
-                                        float* x) {
+__device__ __forceinline__ void res8_apply(const KVLayer& v, int kv, int kk, long long rr, int e0, float* x) {
+    if (v.res_bits == 16) {
+        const uint4 u = *(const uint4*)((const u16*)v.res[kk - 2][kv] + rr * HD + e0);
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = __uint_as_float(w4[j] << 16);
+            x[2 * j + 1] = __uint_as_float(w4[j] & 0xFFFF0000u);
+        }
+        return;
+    }
+    const float s = h2f(v.res_scale[kk - 2][kv][rr * (HD / 32) + e0 / 32]);
+    if (v.res_bits == 8) {
+        const uint2 u = *(const uint2*)((const int8_t*)v.res[kk - 2][kv] + rr * HD + e0);
+        const uint32_t w2[2] = {u.x, u.y};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = x[j] + (float)(int8_t)((w2[j >> 2] >> (8 * (j & 3))) & 0xFF) * s;
+    } else {
+        const uint32_t u = *(const uint32_t*)((const uint8_t*)v.res[kk - 2][kv] + rr * (HD / 2) + e0 / 2);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int nib = (int)((u >> (4 * j)) & 0xF);
+            nib = nib >= 8 ? nib - 16 : nib;
+            x[j] = x[j] + (float)nib * s;
+        }
+    }
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void gather_recon_kernel(RowsAttn a, int ncap, u16* __restrict__ kc,
+                                                           u16* __restrict__ vc, int32_t* __restrict__ lens) {
+    constexpr int LPC = HD / 8;       // lanes per column (8 elements each)
+    constexpr int CPB = 256 / LPC;    // columns per block
+    __shared__ u16 vt[HD][CPB + 2];
+    const KVLayer& v = a.kv;
+    const int bg = blockIdx.y, Hkv = v.Hkv, b = bg / Hkv, g = bg % Hkv;
+    const int pos = a.pos;
+    const int32_t* S = a.cols + (long long)bg * a.n_cols;
+    const int lim = pos - a.window;
+    int lo = 0, hi = a.n_cols;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (S[mid] <= lim) lo = mid + 1;
+        else hi = mid;
+    }
+    const int cntS = lo;
+    const int win_lo = max(0, pos - a.window + 1);
+    const int ncols = cntS + (pos - win_lo + 1);
+    if (blockIdx.x == 0 && threadIdx.x == 0) lens[bg] = ncols;
+    const int cl = threadIdx.x / LPC, m = threadIdx.x % LPC;
+    const int c = blockIdx.x * CPB + cl;
+    const int e0 = 8 * m;
+    float kx[8], vx[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kx[j] = vx[j] = 0.f;
+    if (c < ncols) {
+        const int col = c < cntS ? S[c] : win_lo + (c - cntS);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            kx[j] = kv_base_elem(v, 0, b, g, col, e0 + j);
+            vx[j] = kv_base_elem(v, 1, b, g, col, e0 + j);
+        }
+        for (int kk = 2; kk <= a.k_loop; ++kk) {
+            const int sl = v.slot[((long long)(kk - 2) * v.B + b) * v.Tmax + col];
+            if (sl < 0) continue;
+            const long long rr = res_row(v, b, g, sl);
+            res8_apply<HD>(v, 0, kk, rr, e0, kx);
+            res8_apply<HD>(v, 1, kk, rr, e0, vx);
+        }
+    }
+    uint32_t ko[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ko[j] = (uint32_t)f2h_bits(kx[2 * j]) | ((uint32_t)f2h_bits(kx[2 * j + 1]) << 16);
+    *(uint4*)(kc + ((long long)bg * ncap + c) * HD + e0) = make_uint4(ko[0], ko[1], ko[2], ko[3]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vt[e0 + j][cl] = f2h_bits(vx[j]);
+    __syncthreads();
+    // thread t writes 8 interleaved keys of one head dim: (e, group of 8 columns)
+    const int e = threadIdx.x % HD, grp = threadIdx.x / HD;
+    uint32_t vo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vo[j] = (uint32_t)vt[e][grp * 8 + 2 * j] | ((uint32_t)vt[e][grp * 8 + 2 * j + 1] << 16);
+    const long long blk = (long long)bg * (ncap / 8) + blockIdx.x * (CPB / 8) + grp;
+    *(uint4*)(vc + (blk * HD + e) * 8) = make_uint4(vo[0], vo[1], vo[2], vo[3]);
+}
+
+// ---------------------------------------------------------------- sparse rows (VALU)
+// 32 consecutive K elements [e0, e0+32) of row (b, g, pos) reconstructed at loop k,
+// given that row's loop-2..k slots.
+template <int HD>
+__device__ __forceinline__ void recon_k32(const KVLayer& v, int b, int g, int pos, int e0, int k,
+                                          const int* slots, float* x) {
     const long long row = kv_row(v, b, g, pos);
     if (!v.lazy || v.base_bits == 16) {
-        const uint4* src = (const uint4*)((const u16*)v.base[kv] + row * HD + e0);
+        const uint4* src = (const uint4*)((const u16*)v.base[0] + row * HD + e0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const uint4 u = src[q];
@@ -292,8 +631,8 @@ __device__ __forceinline__ void recon32(const KVLayer& v, int kv, int b, int g, 
             }
         }
     } else {
-        const float s = h2f(v.base_scale[kv][row * (HD / 32) + e0 / 32]);
-        const uint4* src = (const uint4*)((const int8_t*)v.base[kv] + row * HD + e0);
+        const float s = h2f(v.base_scale[0][row * (HD / 32) + e0 / 32]);
+        const uint4* src = (const uint4*)((const int8_t*)v.base[0] + row * HD + e0);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const uint4 u = src[q];
@@ -306,11 +645,11 @@ __device__ __forceinline__ void recon32(const KVLayer& v, int kv, int b, int g, 
     }
     if (!v.lazy) return;
     for (int kk = 2; kk <= k; ++kk) {
-        const int sl = v.slot[((long long)(kk - 2) * v.B + b) * v.Tmax + pos];
+        const int sl = slots[kk - 2];
         if (sl < 0) continue;
         const long long rr = res_row(v, b, g, sl);
         if (v.res_bits == 16) {
-            const uint4* src = (const uint4*)((const u16*)v.res[kk - 2][kv] + rr * HD + e0);
+            const uint4* src = (const uint4*)((const u16*)v.res[kk - 2][0] + rr * HD + e0);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const uint4 u = src[q];
@@ -322,9 +661,9 @@ __device__ __forceinline__ void recon32(const KVLayer& v, int kv, int b, int g, 
                 }
             }
         } else {
-            const float s = h2f(v.res_scale[kk - 2][kv][rr * (HD / 32) + e0 / 32]);
+            const float s = h2f(v.res_scale[kk - 2][0][rr * (HD / 32) + e0 / 32]);
             if (v.res_bits == 8) {
-                const uint4* src = (const uint4*)((const int8_t*)v.res[kk - 2][kv] + rr * HD + e0);
+                const uint4* src = (const uint4*)((const int8_t*)v.res[kk - 2][0] + rr * HD + e0);
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
                     const uint4 u = src[q];
@@ -337,7 +676,7 @@ __device__ __forceinline__ void recon32(const KVLayer& v, int kv, int b, int g, 
                                                     (float)(int8_t)((w4[j] >> (8 * t)) & 0xFF) * s;
                 }
             } else {
-                const uint4 u = *(const uint4*)((const uint8_t*)v.res[kk - 2][kv] + rr * (HD / 2) + e0 / 2);
+                const uint4 u = *(const uint4*)((const uint8_t*)v.res[kk - 2][0] + rr * (HD / 2) + e0 / 2);
                 const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -352,7 +691,18 @@ __device__ __forceinline__ void recon32(const KVLayer& v, int kv, int b, int g, 
     }
 }
 
-template <int HD, int G, bool SPARSE>
+// V element e of column (b, g, pos) at loop k; slots[(kk-2) * 64] is the column's loop-kk slot.
+__device__ __forceinline__ float recon_v(const KVLayer& v, int b, int g, int pos, int e, int k, const int* slots) {
+    float x = kv_base_elem(v, 1, b, g, pos, e);
+    if (!v.lazy) return x;
+    for (int kk = 2; kk <= k; ++kk) {
+        const int sl = slots[(kk - 2) * 64];
+        if (sl >= 0) x = kv_apply_res(v, 1, b, g, kk, sl, e, x);
+    }
+    return x;
+}
+
+template <int HD, int G>
 __global__ __launch_bounds__(64) void attn_rows_kernel(RowsAttn a) {
     constexpr int DPL = HD >= 64 ? HD / 64 : 1;   // head dims per lane in p.V
     const int row = blockIdx.x, split = blockIdx.y, bg = blockIdx.z;
@@ -361,28 +711,26 @@ __global__ __launch_bounds__(64) void attn_rows_kernel(RowsAttn a) {
     const int lane = threadIdx.x;
     const long long qrow = (long long)b * a.n_rows + row;
     const int pos = a.qpos ? a.qpos[qrow] : a.pos;
+    const int nres = a.kv.lazy ? a.k_loop - 1 : 0;
     __shared__ float qs[G][HD];
     __shared__ float ps[G][64];
     __shared__ int cs[64];
-    const float scale = 1.0f / sqrtf((float)HD);
+    __shared__ int slot_s[LK_MAX_LOOPS][64];
+    const float scale = kLog2e / sqrtf((float)HD);
     for (int idx = lane; idx < G * HD; idx += 64) {
         const int hh = idx / HD, e = idx % HD;
         qs[hh][e] = bf2f(a.q[qrow * a.H * HD + (g * G + hh) * HD + e]) * scale;
     }
-    int cntS = 0, win_lo = 0;
-    const int32_t* S = nullptr;
-    if (SPARSE) {
-        S = a.cols + ((long long)b * Hkv + g) * a.n_cols;
-        const int lim = pos - a.window;  // S columns at or below lim lie outside the window
-        int lo = 0, hi = a.n_cols;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (S[mid] <= lim) lo = mid + 1;
-            else hi = mid;
-        }
-        cntS = lo;
-        win_lo = max(0, pos - a.window + 1);
+    const int32_t* S = a.cols + ((long long)b * Hkv + g) * a.n_cols;
+    const int lim = pos - a.window;  // S columns at or below lim lie outside the window
+    int lo = 0, hi = a.n_cols;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (S[mid] <= lim) lo = mid + 1;
+        else hi = mid;
     }
+    const int cntS = lo;
+    const int win_lo = max(0, pos - a.window + 1);
     const int ncols = cntS + (pos - win_lo + 1);
     const int c_begin = split * a.chunk;
     const int c_end = min(ncols, c_begin + a.chunk);
@@ -399,13 +747,18 @@ __global__ __launch_bounds__(64) void attn_rows_kernel(RowsAttn a) {
         const int c = c0 + lane;
         const bool valid = c < c_end;
         const int col = valid ? (c < cntS ? S[c] : win_lo + (c - cntS)) : 0;
+        int myslots[LK_MAX_LOOPS];
+        for (int kk = 0; kk < nres; ++kk) {
+            myslots[kk] = valid ? a.kv.slot[((long long)kk * a.kv.B + b) * a.kv.Tmax + col] : -1;
+            slot_s[kk][lane] = myslots[kk];
+        }
         float s[G];
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) s[hh] = 0.f;
         if (valid) {
             for (int e0 = 0; e0 < HD; e0 += 32) {
                 float x[32];
-                recon32<HD>(a.kv, 0, b, g, col, e0, a.k_loop, x);
+                recon_k32<HD>(a.kv, b, g, col, e0, a.k_loop, myslots, x);
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh)
 #pragma unroll
@@ -417,8 +770,8 @@ __global__ __launch_bounds__(64) void attn_rows_kernel(RowsAttn a) {
             const float sv = valid ? s[hh] : -INFINITY;
             const float mx = wave_max(sv);
             const float m_new = fmaxf(m[hh], mx);
-            const float alpha = (m[hh] == -INFINITY) ? 0.f : expf(m[hh] - m_new);
-            const float p = valid ? expf(sv - m_new) : 0.f;
+            const float alpha = (m[hh] == -INFINITY) ? 0.f : exp2f(m[hh] - m_new);
+            const float p = valid ? exp2f(sv - m_new) : 0.f;
             l[hh] = l[hh] * alpha + wave_sum(p);
             m[hh] = m_new;
 #pragma unroll
@@ -430,11 +783,12 @@ __global__ __launch_bounds__(64) void attn_rows_kernel(RowsAttn a) {
         const int cnt = min(64, c_end - c0);
         const int e = lane * DPL;
         if (e < HD) {
+#pragma unroll 4
             for (int cc = 0; cc < cnt; ++cc) {
                 const int colv = cs[cc];
                 float vv[DPL];
 #pragma unroll
-                for (int dd = 0; dd < DPL; ++dd) vv[dd] = kv_recon_elem(a.kv, 1, b, g, colv, e + dd, a.k_loop);
+                for (int dd = 0; dd < DPL; ++dd) vv[dd] = recon_v(a.kv, b, g, colv, e + dd, a.k_loop, &slot_s[0][cc]);
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) {
                     const float pp = ps[hh][cc];
@@ -474,7 +828,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
             const float* ps = base + (long long)s * G * (HD + 2) + hh * (HD + 2);
             const float ms = ps[HD];
             if (ms == -INFINITY) continue;
-            const float wgt = expf(ms - M);
+            const float wgt = exp2f(ms - M);
             L += wgt * ps[HD + 1];
             acc += wgt * ps[e];
         }
@@ -507,12 +861,30 @@ hipError_t mass_hd(const u16* q, const KVLayer& kv, const float* lse, int B, int
 }
 
 template <int HD, int G>
+void dense_launch(const RowsAttn& a, hipStream_t st) {
+    dim3 grid(a.n_splits, a.B * a.kv.Hkv);
+    if (a.kv.lazy && a.kv.base_bits == 8)
+        hipLaunchKernelGGL((attn_decode_dense_kernel<HD, G, RT_I8>), grid, dim3(256), 0, st, a);
+    else if (!a.kv.lazy && a.kv.f16)
+        hipLaunchKernelGGL((attn_decode_dense_kernel<HD, G, RT_F16>), grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((attn_decode_dense_kernel<HD, G, RT_BF16>), grid, dim3(256), 0, st, a);
+}
+
+template <int HD>
+void dense_hd(const RowsAttn& a, int G, hipStream_t st) {
+    switch (G) {
+        case 1: dense_launch<HD, 1>(a, st); break;
+        case 2: dense_launch<HD, 2>(a, st); break;
+        case 4: dense_launch<HD, 4>(a, st); break;
+        default: dense_launch<HD, 8>(a, st); break;
+    }
+}
+
+template <int HD, int G>
 void rows_launch(const RowsAttn& a, hipStream_t st) {
     dim3 grid(a.n_rows, a.n_splits, a.B * a.kv.Hkv);
-    if (a.cols)
-        hipLaunchKernelGGL((attn_rows_kernel<HD, G, true>), grid, dim3(64), 0, st, a);
-    else
-        hipLaunchKernelGGL((attn_rows_kernel<HD, G, false>), grid, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((attn_rows_kernel<HD, G>), grid, dim3(64), 0, st, a);
 }
 
 template <int HD>
@@ -547,10 +919,30 @@ hipError_t column_mass(const u16* q, const KVLayer& kv, const float* lse, int B,
 
 hipError_t attn_rows_main(const RowsAttn& a, hipStream_t st) {
     const int G = a.H / a.kv.Hkv;
-    switch (a.kv.hd) {
-        case 32: rows_hd<32>(a, G, st); break;
-        case 64: rows_hd<64>(a, G, st); break;
-        default: rows_hd<128>(a, G, st); break;
+    if (a.cols) {
+        switch (a.kv.hd) {
+            case 32: rows_hd<32>(a, G, st); break;
+            case 64: rows_hd<64>(a, G, st); break;
+            default: rows_hd<128>(a, G, st); break;
+        }
+    } else {
+        switch (a.kv.hd) {
+            case 32: dense_hd<32>(a, G, st); break;
+            case 64: dense_hd<64>(a, G, st); break;
+            default: dense_hd<128>(a, G, st); break;
+        }
+    }
+    return hipGetLastError();
+}
+
+hipError_t gather_recon(const RowsAttn& a, int ncap, u16* kc, u16* vc, int32_t* lens, hipStream_t st) {
+    const int hd = a.kv.hd;
+    const int cpb = 256 / (hd / 8);
+    dim3 grid(ncap / cpb, a.B * a.kv.Hkv);
+    switch (hd) {
+        case 32: hipLaunchKernelGGL(gather_recon_kernel<32>, grid, dim3(256), 0, st, a, ncap, kc, vc, lens); break;
+        case 64: hipLaunchKernelGGL(gather_recon_kernel<64>, grid, dim3(256), 0, st, a, ncap, kc, vc, lens); break;
+        default: hipLaunchKernelGGL(gather_recon_kernel<128>, grid, dim3(256), 0, st, a, ncap, kc, vc, lens); break;
     }
     return hipGetLastError();
 }

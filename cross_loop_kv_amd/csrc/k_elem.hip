@@ -284,18 +284,23 @@ __global__ __launch_bounds__(kThreads) void rope_kv_write_kernel(const float* qk
         const int e = lin % hd;
         const float x = kvbuf[lin];
         const long long row = kv_row(L, b, g, pos);
+        const long long idx = kv == 0 ? row * hd + e : v_elem(L, b, g, pos, e);
         if (w.kind == 0 || (w.kind == 1 && L.base_bits == 16)) {
-            ((u16*)L.base[kv])[row * hd + e] = f2bf(x);
+            ((u16*)L.base[kv])[idx] = f2bf(x);
         } else if (w.kind == 1) {  // int8 base: residual against a zero reconstruction
+            if (w.keep_codes) continue;
             u16 sb;
             const int c = quant_group32(x, 127, &sb);
-            ((int8_t*)L.base[kv])[row * hd + e] = (int8_t)c;
-            if ((threadIdx.x & 31) == 0) ((u16*)L.base_scale[kv])[row * (hd / 32) + e / 32] = sb;
+            ((int8_t*)L.base[kv])[idx] = (int8_t)c;
+            if ((threadIdx.x & 31) == 0) {
+                const long long si = kv == 0 ? row * (hd / 32) + e / 32 : v_scale_idx(L, b, g, pos, e / 32);
+                ((u16*)L.base_scale[kv])[si] = sb;
+            }
         } else {
             const long long rr = res_row(L, b, g, slot);
             if (L.res_bits == 16) {
                 ((u16*)L.res[w.loop - 2][kv])[rr * hd + e] = f2bf(x);
-            } else {
+            } else if (!w.keep_codes) {
                 const float prev = kv_recon_elem(L, kv, b, g, pos, e, w.loop - 1);
                 u16 sb;
                 const int qmax = (1 << (L.res_bits - 1)) - 1;

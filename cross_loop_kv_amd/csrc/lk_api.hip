@@ -102,20 +102,27 @@ struct StoreLayout {
 struct lk_kv_store {
     lk_handle* h;
     int B, Tp, Tmax, t;
+    int Tpad;  // row stride: Tmax rounded up to a multiple of 8
     bool prefilled;
     StoreLayout lay;
     char* buf;
     const int32_t* f_tok;
     const int32_t* f_cols;
+    int keep_codes;
 };
 
 namespace {
+
+// Positions per (sequence, KV head) are padded to a multiple of 8: V rows are
+// stored in blocks of 8 interleaved keys.
+inline int pad8(int t) { return (t + 7) / 8 * 8; }
 
 StoreLayout store_layout(const lk_handle* h, int B, int Tp, int Tmax) {
     const lk_model_cfg& c = h->c;
     StoreLayout s{};
     const long long hd = c.head_dim, Hkv = c.n_kv_heads;
-    const long long kvrows = (long long)B * Hkv * Tmax;  // rows of one K or V region of a layer
+    const int Tpad = pad8(Tmax);
+    const long long kvrows = (long long)B * Hkv * Tpad;  // rows of one K or V region of a layer
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -142,7 +149,7 @@ StoreLayout store_layout(const lk_handle* h, int B, int Tp, int Tmax) {
         const long long res_rows = (long long)(c.n_loops - 1) * c.n_shared * 2 * B * Hkv * s.slots;
         s.res = take((size_t)res_rows * s.res_row_b);
         s.res_sc = take(h->z.res_bits == 16 ? 0 : (size_t)res_rows * (hd / 32) * 2);
-        s.slot = take((size_t)(c.n_loops - 1) * B * Tmax * 4);
+        s.slot = take((size_t)(c.n_loops - 1) * B * Tpad * 4);
         s.n_cols = h->z.top_s < Tp ? h->z.top_s : Tp;
         s.cols = take((size_t)c.n_shared * B * Hkv * s.n_cols * 4);
     }
@@ -178,7 +185,7 @@ void store_bytes(const lk_kv_store* s, size_t* shared, size_t* total) {
 
 // K/V row pointers ------------------------------------------------------------
 long long kv_region_elems(const lk_kv_store* s) {
-    return (long long)s->B * s->h->c.n_kv_heads * s->Tmax * s->h->c.head_dim;
+    return (long long)s->B * s->h->c.n_kv_heads * s->Tpad * s->h->c.head_dim;
 }
 
 KVLayer plain_layer(const lk_kv_store* s, u16* k_rows, u16* v_rows) {
@@ -188,7 +195,7 @@ KVLayer plain_layer(const lk_kv_store* s, u16* k_rows, u16* v_rows) {
     L.B = s->B;
     L.Hkv = c.n_kv_heads;
     L.hd = c.head_dim;
-    L.Tmax = s->Tmax;
+    L.Tmax = s->Tpad;
     L.base_bits = 16;
     L.res_bits = 16;
     L.n_loops = c.n_loops;
@@ -218,7 +225,7 @@ KVLayer lazy_layer(const lk_kv_store* s, int r) {
     L.B = s->B;
     L.Hkv = c.n_kv_heads;
     L.hd = c.head_dim;
-    L.Tmax = s->Tmax;
+    L.Tmax = s->Tpad;
     L.slots = s->lay.slots;
     L.base_bits = h->z.base_bits;
     L.res_bits = h->z.res_bits;
@@ -243,7 +250,7 @@ KVLayer lazy_layer(const lk_kv_store* s, int r) {
 }
 
 int32_t* slot_map(const lk_kv_store* s, int k) {
-    return (int32_t*)(s->buf + s->lay.slot) + (long long)(k - 2) * s->B * s->Tmax;
+    return (int32_t*)(s->buf + s->lay.slot) + (long long)(k - 2) * s->B * s->Tpad;
 }
 int32_t* col_sets(const lk_kv_store* s, int r) {
     return (int32_t*)(s->buf + s->lay.cols) + (long long)r * s->B * s->h->c.n_kv_heads * s->lay.n_cols;
@@ -253,7 +260,9 @@ int32_t* col_sets(const lk_kv_store* s, int r) {
 struct WS {
     float *h, *h0, *xc, *qkv, *lse, *mass, *keys, *part;
     u16 *xn, *q, *att, *act;
-    int32_t* sel;
+    u16 *kc, *vc;      // decode, loops >= 2: materialized reconstruction of the column lists
+    int32_t *sel, *lens;
+    int ncap;          // column capacity of kc / vc per (sequence, KV head)
     size_t total;
     long long part_floats;
 };
@@ -293,6 +302,11 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
     }
     w.part_floats = pf;
     w.part = (float*)take(pf * 4);
+    w.ncap = hd_->lazy() ? (hd_->z.top_s + hd_->z.window + 63) / 64 * 64 : 0;
+    const long long kvc = (long long)B * c.n_kv_heads * w.ncap * c.head_dim * 2;
+    w.kc = (u16*)take(kvc);
+    w.vc = (u16*)take(kvc);
+    w.lens = (int32_t*)take(hd_->lazy() ? (long long)B * c.n_kv_heads * 4 : 0);
     w.total = off;
     return w;
 }
@@ -402,18 +416,59 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
             a.cols = nullptr;
             ncol_max = (long long)ap.pos + 1;
         }
-        int chunk = kRowChunk;
-        while ((ncol_max + chunk - 1) / chunk > kMaxSplits) chunk *= 2;
-        a.chunk = chunk;
-        a.n_splits = (int)((ncol_max + chunk - 1) / chunk);
-        if ((long long)a.B * a.n_rows * H * a.n_splits * (hd + 2) > w.part_floats)
-            return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
+        // dense decode: one workgroup per (sequence, KV head, chunk), about 1536 workgroups
+        auto dense_chunk = [&](long long ncol) {
+            const long long pairs = (long long)a.B * c.n_kv_heads;
+            const long long want = (ncol * pairs + 1535) / 1536;
+            int ch = (int)std::max(128LL, (want + 127) / 128 * 128);
+            while ((ncol + ch - 1) / ch > kMaxSplits) ch *= 2;
+            return ch;
+        };
         a.part = w.part;
         a.out = w.att;
-        const int acls = io.rows_per_seq > 1 ? TC_ATTN_PREFILL_SPARSE
-                         : (ap.kind == ATTN_ROWS_SPARSE ? TC_ATTN_DECODE_SPARSE : TC_ATTN_DECODE_DENSE);
-        LK_TRY(timed(h, acls, st, [&] { return lk::attn_rows_main(a, st); }));
-        LK_HIP(lk::attn_rows_combine(a, st));
+        if (ap.kind == ATTN_ROWS_SPARSE && io.rows_per_seq == 1) {
+            // decode, loops >= 2: materialize the loop-k reconstruction of every column
+            // list as float16 rows, then run the dense MFMA kernel over them
+            const int ncap = (ap.n_cols + ap.window + 63) / 64 * 64;
+            if (ncap > w.ncap) return fail(LK_ERR_CAPACITY, "workspace too small for the column lists");
+            lk::RowsAttn d = a;
+            d.cols = nullptr;
+            d.lens = w.lens;
+            d.pos = ncap - 1;
+            d.kv = KVLayer{};
+            d.kv.lazy = 0;
+            d.kv.f16 = 1;
+            d.kv.B = a.B;
+            d.kv.Hkv = c.n_kv_heads;
+            d.kv.hd = hd;
+            d.kv.Tmax = ncap;
+            d.kv.base_bits = 16;
+            d.kv.res_bits = 16;
+            d.kv.n_loops = c.n_loops;
+            d.kv.base[0] = w.kc;
+            d.kv.base[1] = w.vc;
+            d.chunk = dense_chunk(ncap);
+            d.n_splits = (ncap + d.chunk - 1) / d.chunk;
+            if ((long long)a.B * H * d.n_splits * (hd + 2) > w.part_floats)
+                return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
+            LK_TRY(timed(h, TC_ATTN_DECODE_SPARSE, st, [&] {
+                hipError_t e = lk::gather_recon(a, ncap, w.kc, w.vc, w.lens, st);
+                return e != hipSuccess ? e : lk::attn_rows_main(d, st);
+            }));
+            LK_HIP(lk::attn_rows_combine(d, st));
+        } else {
+            int chunk = kRowChunk;
+            if (ap.kind == ATTN_ROWS_DENSE) chunk = dense_chunk(ncol_max);
+            while ((ncol_max + chunk - 1) / chunk > kMaxSplits) chunk *= 2;
+            a.chunk = chunk;
+            a.n_splits = (int)((ncol_max + chunk - 1) / chunk);
+            if ((long long)a.B * a.n_rows * H * a.n_splits * (hd + 2) > w.part_floats)
+                return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
+            const int acls = io.rows_per_seq > 1 ? TC_ATTN_PREFILL_SPARSE
+                             : (ap.kind == ATTN_ROWS_SPARSE ? TC_ATTN_DECODE_SPARSE : TC_ATTN_DECODE_DENSE);
+            LK_TRY(timed(h, acls, st, [&] { return lk::attn_rows_main(a, st); }));
+            LK_HIP(lk::attn_rows_combine(a, st));
+        }
     }
     LK_TRY(timed(h, gcls, st,
                  [&] { return lk::gemm(w.att, (const u16*)W.wo, io.M, d, Hhd, lk::EPI_ADD, io.x, nullptr, st); }));
@@ -490,13 +545,15 @@ int lk_kv_store_alloc(lk_handle* h, int32_t batch, int32_t prompt_tokens, int32_
     s->B = batch;
     s->Tp = prompt_tokens;
     s->Tmax = max_tokens;
+    s->Tpad = pad8(max_tokens);
     s->t = 0;
     s->prefilled = false;
     s->lay = lay;
     s->buf = (char*)dev_buf;
     s->f_tok = s->f_cols = nullptr;
+    s->keep_codes = 0;
     if (h->lazy()) {
-        hipError_t e = lk::fill_i32(slot_map(s, 2), -1, (long long)(h->c.n_loops - 1) * batch * max_tokens,
+        hipError_t e = lk::fill_i32(slot_map(s, 2), -1, (long long)(h->c.n_loops - 1) * batch * s->Tpad,
                                     (hipStream_t)stream);
         if (e != hipSuccess) {
             delete s;
@@ -525,6 +582,7 @@ int lk_kv_store_view(const lk_kv_store* s, lk_store_view* v) {
     if (!s || !v) return fail(LK_ERR_INVALID_ARG, "null argument");
     std::memset(v, 0, sizeof(*v));
     const lk_handle* h = s->h;
+    v->row_stride = s->Tpad;
     if (h->c.n_prelude + h->c.n_coda > 0) v->dense = s->buf + s->lay.dense;
     if (h->z.mode != LK_MODE_LAZY) {
         v->loop_rows = s->buf + s->lay.loop_rows;
@@ -551,6 +609,13 @@ int lk_kv_store_force_selection(lk_kv_store* s, const int32_t* d_tokens, const i
     return LK_OK;
 }
 
+int lk_kv_store_keep_codes(lk_kv_store* s, int32_t enable) {
+    if (!s) return fail(LK_ERR_INVALID_ARG, "null store");
+    if (!s->h->lazy()) return fail(LK_ERR_STATE, "codes exist only in lazy mode");
+    s->keep_codes = enable ? 1 : 0;
+    return LK_OK;
+}
+
 int lk_workspace_bytes(lk_handle* h, int32_t batch, int32_t tokens, size_t* bytes) {
     if (!h || !bytes) return fail(LK_ERR_INVALID_ARG, "null argument");
     if (batch < 1 || tokens < 1) return fail(LK_ERR_INVALID_ARG, "batch and tokens must be >= 1");
@@ -571,7 +636,7 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
     const int P = c.n_prelude, R = c.n_shared, K = c.n_loops, Q = c.n_coda, d = c.d_model;
     const int M = B * T;
     if (h->lazy())
-        LK_HIP(lk::fill_i32(slot_map(s, 2), -1, (long long)(K - 1) * B * s->Tmax, st));
+        LK_HIP(lk::fill_i32(slot_map(s, 2), -1, (long long)(K - 1) * B * s->Tpad, st));
     s->t = 0;
     s->prefilled = false;
     LK_HIP(lk::embed(d_ids, h->tok, w.h, M, d, c.vocab, st));
@@ -605,6 +670,7 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
             lk::KVWrite kw{};
             kw.kind = 1;
             kw.layer = ap.read;
+            kw.keep_codes = s->keep_codes;
             LK_TRY(run_layer(h, P + r, io, kw, ap, w, st));
             int32_t* cols = col_sets(s, r);
             const int nc = s->lay.n_cols;
@@ -625,7 +691,7 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
                 LK_HIP(lk::topk_rows(w.keys, B, T, n, w.sel, st));
             }
             LK_HIP(lk::gather_rows(w.h, w.sel, B, n, T, d, h->lemb + (long long)(k - 1) * d, w.xc,
-                                   slot_map(s, k), s->Tmax, st));
+                                   slot_map(s, k), s->Tpad, st));
             LayerIO cio{w.xc, B * n, n, w.sel, 0, nullptr};
             for (int r = 0; r < R; ++r) {
                 AttnPlan ap{};
@@ -641,6 +707,7 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
                 kw.layer = ap.read;
                 kw.loop = k;
                 kw.slot_base = 0;
+                kw.keep_codes = s->keep_codes;
                 LK_TRY(run_layer(h, P + r, cio, kw, ap, w, st));
             }
             if (k < K) {
@@ -698,6 +765,7 @@ int lk_looped_decode_step(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, fl
             ap.pos = t;
             lk::KVWrite kw{};
             kw.layer = ap.read;
+            kw.keep_codes = s->keep_codes;
             if (k == 1) {
                 ap.kind = ATTN_ROWS_DENSE;
                 ap.k_loop = 1;

@@ -84,17 +84,24 @@ __device__ __forceinline__ int quant_group32(float r, int qmax, u16* scale_bits)
 
 // ---------------------------------------------------------------- KV store views
 // Address arithmetic of one shared layer of a lazy store (or a plain bf16 row
-// cache when lazy == 0).  Rows are [b][g][pos][hd] for the base/dense part and
-// [b][g][slot][row_bytes] for the loop-k residual part.
+// cache when lazy == 0).  Positions are padded to Tmax (a multiple of 8).
+//  * K rows: [b][g][pos][hd];  int8 K scales: [b][g][pos][hd/32].
+//  * V rows: 8-key interleaved [b][g][pos/8][hd][8] (element (pos, e) at
+//    ((b*Hkv + g)*Tmax/8 + pos/8)*hd*8 + e*8 + pos%8), so that the 8 keys of
+//    one head dimension are contiguous -- the k-operand layout of the PV MFMA;
+//    int8 V scales: [b][g][pos/8][hd/32][8].
+//  * loop-k residual rows (K and V alike): [b][g][slot][row_bytes] with float16
+//    scales [b][g][slot][hd/32].
 struct KVLayer {
-    int lazy;            // 0: plain bf16 rows in base[]; 1: lazy store
+    int lazy;            // 0: plain rows in base[] (bf16, or f16 when f16 != 0); 1: lazy store
+    int f16;             // plain rows hold float16 (a materialized reconstruction)
     int B, Hkv, hd, Tmax;
     long long slots;     // residual slots per (b, g)
     int base_bits;       // 16 or 8
     int res_bits;        // 16, 8 or 4
     int n_loops;         // K
     const void* base[2];          // [K|V]: bf16 rows or int8 codes
-    const u16* base_scale[2];     // fp16 bits, [b][g][pos][hd/32]
+    const u16* base_scale[2];     // fp16 bits
     const void* res[LK_MAX_LOOPS][2];        // index kk-2 for loop kk
     const u16* res_scale[LK_MAX_LOOPS][2];
     const int32_t* slot;          // [K-1][B][Tmax]
@@ -103,6 +110,12 @@ struct KVLayer {
 __device__ __forceinline__ long long kv_row(const KVLayer& v, int b, int g, int pos) {
     return ((long long)(b * v.Hkv + g) * v.Tmax + pos);
 }
+__device__ __forceinline__ long long v_elem(const KVLayer& v, int b, int g, int pos, int e) {
+    return ((((long long)(b * v.Hkv + g) * (v.Tmax >> 3) + (pos >> 3)) * v.hd + e) << 3) + (pos & 7);
+}
+__device__ __forceinline__ long long v_scale_idx(const KVLayer& v, int b, int g, int pos, int q) {
+    return ((((long long)(b * v.Hkv + g) * (v.Tmax >> 3) + (pos >> 3)) * (v.hd >> 5) + q) << 3) + (pos & 7);
+}
 __device__ __forceinline__ long long res_row(const KVLayer& v, int b, int g, long long slot) {
     return ((long long)(b * v.Hkv + g) * v.slots + slot);
 }
@@ -110,36 +123,39 @@ __device__ __forceinline__ int res_row_bytes(const KVLayer& v) {
     return v.res_bits == 16 ? v.hd * 2 : v.hd * v.res_bits / 8;
 }
 
-// Value of element e of row (b, g, pos) of K (kv=0) or V (kv=1) reconstructed
-// at loop `k`: base, then loop 2..k residuals (16-bit residual rows replace).
-__device__ __forceinline__ float kv_recon_elem(const KVLayer& v, int kv, int b, int g, int pos,
-                                               int e, int k) {
-    const long long row = kv_row(v, b, g, pos);
-    float x;
-    if (!v.lazy || v.base_bits == 16) {
-        x = bf2f(((const u16*)v.base[kv])[row * v.hd + e]);
+// Base (loop-1 / plain-row) value of element e of K (kv=0) or V (kv=1) at (b, g, pos).
+__device__ __forceinline__ float kv_base_elem(const KVLayer& v, int kv, int b, int g, int pos, int e) {
+    const long long idx = kv == 0 ? kv_row(v, b, g, pos) * v.hd + e : v_elem(v, b, g, pos, e);
+    if (!v.lazy || v.base_bits == 16) return bf2f(((const u16*)v.base[kv])[idx]);
+    const int8_t c = ((const int8_t*)v.base[kv])[idx];
+    const long long si = kv == 0 ? kv_row(v, b, g, pos) * (v.hd / 32) + e / 32 : v_scale_idx(v, b, g, pos, e / 32);
+    return (float)c * h2f(v.base_scale[kv][si]);
+}
+
+// Add (or, for 16-bit residuals, substitute) the loop-kk entry of element e.
+__device__ __forceinline__ float kv_apply_res(const KVLayer& v, int kv, int b, int g, int kk, int sl, int e,
+                                              float x) {
+    const long long rr = res_row(v, b, g, sl);
+    if (v.res_bits == 16) return bf2f(((const u16*)v.res[kk - 2][kv])[rr * v.hd + e]);
+    int c;
+    if (v.res_bits == 8) {
+        c = ((const int8_t*)v.res[kk - 2][kv])[rr * v.hd + e];
     } else {
-        const int8_t c = ((const int8_t*)v.base[kv])[row * v.hd + e];
-        x = (float)c * h2f(v.base_scale[kv][row * (v.hd / 32) + e / 32]);
+        const uint8_t byte = ((const uint8_t*)v.res[kk - 2][kv])[rr * (v.hd / 2) + e / 2];
+        const int nib = (e & 1) ? (byte >> 4) : (byte & 0xF);
+        c = nib >= 8 ? nib - 16 : nib;
     }
+    return x + (float)c * h2f(v.res_scale[kk - 2][kv][rr * (v.hd / 32) + e / 32]);
+}
+
+// Value of element e of row (b, g, pos) reconstructed at loop `k`: base, then the
+// loop 2..k residuals (16-bit residual rows replace).
+__device__ __forceinline__ float kv_recon_elem(const KVLayer& v, int kv, int b, int g, int pos, int e, int k) {
+    float x = kv_base_elem(v, kv, b, g, pos, e);
     if (!v.lazy) return x;
     for (int kk = 2; kk <= k; ++kk) {
         const int sl = v.slot[((long long)(kk - 2) * v.B + b) * v.Tmax + pos];
-        if (sl < 0) continue;
-        const long long rr = res_row(v, b, g, sl);
-        if (v.res_bits == 16) {
-            x = bf2f(((const u16*)v.res[kk - 2][kv])[rr * v.hd + e]);
-        } else {
-            int c;
-            if (v.res_bits == 8) {
-                c = ((const int8_t*)v.res[kk - 2][kv])[rr * v.hd + e];
-            } else {
-                const uint8_t byte = ((const uint8_t*)v.res[kk - 2][kv])[rr * (v.hd / 2) + e / 2];
-                int nib = (e & 1) ? (byte >> 4) : (byte & 0xF);
-                c = nib >= 8 ? nib - 16 : nib;
-            }
-            x = x + (float)c * h2f(v.res_scale[kk - 2][kv][rr * (v.hd / 32) + e / 32]);
-        }
+        if (sl >= 0) x = kv_apply_res(v, kv, b, g, kk, sl, e, x);
     }
     return x;
 }

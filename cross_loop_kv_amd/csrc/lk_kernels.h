@@ -44,6 +44,7 @@ struct KVWrite {
     const int32_t* slot_of_row;  // kind 2: slot per row (nullptr: slot = slot_base + row index in seq)
     long long slot_base;
     int32_t* slot_map_k;  // kind 2 decode: slot map of loop k to write (nullptr: already written)
+    int keep_codes;       // leave int8/int4 codes and their scales in the store untouched
 };
 hipError_t rope_kv_write(const float* qkv, int rows, int rows_per_seq, const int32_t* pos,
                          int pos_offset, int H, int Hkv, int hd, const double* inv_freq, u16* q_out,
@@ -78,7 +79,13 @@ struct RowsAttn {
     int chunk, n_splits;   // columns per split, splits per row
     float* part;           // [B*n_rows][Hkv][n_splits][G][hd + 2]
     u16* out;              // bf16 [B * n_rows, H * hd]
+    const int32_t* lens;   // dense: columns per (b, g) (nullptr: pos + 1 for all)
 };
+// Decode, loops >= 2: write the loop-k reconstruction of each (b, g)'s column list
+// (S intersect [0, pos-window] then [pos-window+1, pos]) as float16 rows into
+// kc [B*Hkv][ncap][hd] and 8-key-interleaved vc [B*Hkv][ncap/8][hd][8], and the
+// column count into lens[B*Hkv]; rows past the count are zero.
+hipError_t gather_recon(const RowsAttn& a, int ncap, u16* kc, u16* vc, int32_t* lens, hipStream_t st);
 // attn_rows_main writes the per-split partials; attn_rows_combine merges them into `out`.
 hipError_t attn_rows_main(const RowsAttn& a, hipStream_t st);
 hipError_t attn_rows_combine(const RowsAttn& a, hipStream_t st);

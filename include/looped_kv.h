@@ -182,6 +182,7 @@ typedef struct {
     int32_t n_selected;     /* kept tokens per sequence at loops >= 2 */
     int32_t n_columns;      /* min(top_s, prompt_tokens) */
     int64_t res_row_bytes;  /* bytes of one residual row (hd elements) */
+    int32_t row_stride;     /* Tp: positions per (sequence, KV head), max_tokens padded to 8 */
 } lk_store_view;
 int lk_kv_store_view(const lk_kv_store *s, lk_store_view *v);
 
@@ -190,6 +191,13 @@ int lk_kv_store_view(const lk_kv_store *s, lk_store_view *v);
  * tokens int32 [n_loops-1][batch][n_selected] ascending per row;
  * columns int32 [R][batch][Hkv][n_columns] ascending per row. */
 int lk_kv_store_force_selection(lk_kv_store *s, const int32_t *d_tokens, const int32_t *d_columns);
+
+/* When enabled, prefill and decode leave the int8 base codes and the 4/8-bit
+ * residual codes, with their float16 scales, that the caller wrote into the
+ * store (through lk_kv_store_view) in place instead of quantizing; 16-bit rows
+ * are still written.  Lets a test inject another implementation's integer
+ * quantization decisions, as lk_kv_store_force_selection does for indices. */
+int lk_kv_store_keep_codes(lk_kv_store *s, int32_t enable);
 
 /* Top-n selector: for each of `rows` rows of `cols` float32 keys, the n largest
  * (ties to the lower index) as ascending int32 indices [rows, n]. */

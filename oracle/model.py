@@ -40,6 +40,14 @@ not given on any page):
   recon_k = recon_{k-1} + dequant(r) on those rows and recon_{k-1} elsewhere.
   Residual rows live in compact slots addressed by a per-(loop, sequence) slot
   map.  A decode token runs every loop and is always stored.
+
+Operand precision: by default every tensor is float32.  With
+``operand_precision="bf16"`` the oracle rounds (to nearest even) exactly the
+tensors that a bf16-operand implementation holds in bfloat16 -- the inputs of
+every projection GEMM (normed activations, attention output, FFN activation),
+the rotated queries and every K/V row kept at 16 bits -- and computes
+everything else in float32.  This measures how much of a bf16 implementation's
+distance from the float32 result is the rounding of its operands.
 """
 from __future__ import annotations
 
@@ -55,6 +63,13 @@ F32 = np.float32
 # ----------------------------------------------------------------------------
 # Building blocks
 # ----------------------------------------------------------------------------
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Float32 values rounded to the nearest bfloat16 (ties to even), as float32."""
+    u = np.ascontiguousarray(x, dtype=F32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+    return u.view(F32).reshape(np.shape(x))
+
 
 def rmsnorm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
     x = np.asarray(x, dtype=F32)
@@ -138,7 +153,11 @@ class LoopedOracle:
     ``decode(ids[B])`` appends one token per sequence and returns [B, d].
     """
 
-    def __init__(self, shape, lazy, weights, batch: int, max_tokens: int):
+    def __init__(self, shape, lazy, weights, batch: int, max_tokens: int,
+                 operand_precision: str = "fp32"):
+        if operand_precision not in ("fp32", "bf16"):
+            raise ValueError("operand_precision must be fp32 or bf16")
+        self.bf16 = operand_precision == "bf16"
         self.s = shape
         self.lz = lazy
         self.w = weights
@@ -156,6 +175,7 @@ class LoopedOracle:
             if shape.head_dim % lazy.group:
                 raise ValueError("head_dim must be a multiple of the group")
         self.depth = 0           # layer applications in the last call
+        self.forced_codes_from = None  # another LoopedOracle whose quantized codes are reused
         self.forced_tokens = None    # {(k, b): kept indices} overrides selection
         self.forced_S = None         # [r][b][g] column lists override top-s
         self.mass = {}               # (r, b) -> loop-1 column mass [Hkv, T]
@@ -163,6 +183,10 @@ class LoopedOracle:
         self.T = None            # prompt length
         self.t = 0               # tokens held per sequence
         self._alloc()
+
+    def _rb(self, x):
+        """Round an operand to bf16 in bf16-operand mode (identity otherwise)."""
+        return round_bf16(x) if self.bf16 else x
 
     # ---------------------------------------------------------------- store
     def _alloc(self):
@@ -211,9 +235,13 @@ class LoopedOracle:
         """kvals/vvals [Hkv, n, hd] for positions ``rows``."""
         for kv, x in ((0, kvals), (1, vvals)):
             if self.lz.base_bits == 16:
-                self.base[r][kv][b][:, rows, :] = x
+                self.base[r][kv][b][:, rows, :] = self._rb(x)
             else:
-                codes, sc = quant.quantize(x, 8, self.lz.group)   # residual vs zero
+                if self.forced_codes_from is not None:
+                    src = self.forced_codes_from.base[r][kv]
+                    codes, sc = src[0][b][:, rows, :], src[1][b][:, rows, :]
+                else:
+                    codes, sc = quant.quantize(x, 8, self.lz.group)   # residual vs zero
                 self.base[r][kv][0][b][:, rows, :] = codes
                 self.base[r][kv][1][b][:, rows, :] = sc
 
@@ -244,7 +272,12 @@ class LoopedOracle:
         for kv, x in ((0, kvals), (1, vvals)):
             store = self.res[(k, r, kv)]
             if self.lz.res_bits == 16:
-                store[b][:, slots, :] = x
+                store[b][:, slots, :] = self._rb(x)
+            elif self.forced_codes_from is not None:
+                src = self.forced_codes_from.res[(k, r, kv)]
+                codes, sc = src[0][b][:, slots, :], src[1][b][:, slots, :]
+                store[0][b][:, slots, :] = codes
+                store[1][b][:, slots, :] = sc
             else:
                 prev = self.recon(k - 1, r, b, kv, rows)
                 codes, sc = quant.quantize(x - prev, self.lz.res_bits, self.lz.group)
@@ -255,23 +288,23 @@ class LoopedOracle:
     def _qkv(self, li, x, pos):
         s, W = self.s, self.w["layers"][li]
         n = x.shape[0]
-        a = rmsnorm(x, W["attn_norm"], s.rms_eps)
+        a = self._rb(rmsnorm(x, W["attn_norm"], s.rms_eps))
         q = (a @ W["wq"].T).reshape(n, s.n_heads, s.head_dim)
         k = (a @ W["wk"].T).reshape(n, s.n_kv_heads, s.head_dim)
         v = (a @ W["wv"].T).reshape(n, s.n_kv_heads, s.head_dim)
         cos, sin = rope_cos_sin(pos, s.head_dim, s.rope_theta)
-        return apply_rope(q, cos, sin), apply_rope(k, cos, sin), v.astype(F32)
+        return self._rb(apply_rope(q, cos, sin)), apply_rope(k, cos, sin), v.astype(F32)
 
     def _out_ffn(self, li, x, o):
         s, W = self.s, self.w["layers"][li]
         n = x.shape[0]
-        x = (x + o.reshape(n, -1) @ W["wo"].T).astype(F32)
-        b = rmsnorm(x, W["ffn_norm"], s.rms_eps)
+        x = (x + self._rb(o.reshape(n, -1)) @ W["wo"].T).astype(F32)
+        b = self._rb(rmsnorm(x, W["ffn_norm"], s.rms_eps))
         if s.ffn_act == "swiglu":
             f = silu(b @ W["w_gate"].T) * (b @ W["w_up"].T)
         else:
             f = gelu_erf(b @ W["w_up"].T)
-        return (x + f.astype(F32) @ W["w_down"].T).astype(F32)
+        return (x + self._rb(f.astype(F32)) @ W["w_down"].T).astype(F32)
 
     # -------------------------------------------------------------- prefill
     def prefill(self, ids: np.ndarray) -> np.ndarray:
@@ -330,8 +363,8 @@ class LoopedOracle:
 
     def _shared_dense(self, li, h, pos, kc, vc, b):
         q, k, v = self._qkv(li, h, pos)
-        kc[b][:, pos, :] = k.transpose(1, 0, 2)
-        vc[b][:, pos, :] = v.transpose(1, 0, 2)
+        kc[b][:, pos, :] = self._rb(k.transpose(1, 0, 2))
+        vc[b][:, pos, :] = self._rb(v.transpose(1, 0, 2))
         hi = int(pos.max()) + 1
         o = attend(q, kc[b][:, :hi], vc[b][:, :hi], lambda i, g: causal_cols(int(pos[i])))
         self.depth += 1

@@ -42,7 +42,7 @@ def gpu_selection(store, shape, batch, prompt):
     """Kept prompt tokens per loop read back from the store's slot maps, and the column sets."""
     v = store.view()
     K, R, Hkv = shape.n_loops, shape.n_shared, shape.n_kv_heads
-    Tm = store.max_tokens
+    Tm = v.row_stride
     torch.cuda.synchronize()
     sm = store_region(store, v.slot_maps, (K - 1) * batch * Tm * 4, torch.int32)
     cols = store_region(store, v.columns, R * batch * Hkv * v.n_columns * 4, torch.int32)
@@ -51,8 +51,62 @@ def gpu_selection(store, shape, batch, prompt):
     return sel, cols.view(R, batch, Hkv, v.n_columns).cpu().numpy()
 
 
-def run_pair(shape, lazy, batch, prompt, steps, seed=0, force=True, weights=None):
-    """Prefill + `steps` decode steps on the oracle and the GPU; returns a result dict."""
+def _pad_t(a, tpad):
+    """Pad axis 2 (positions) of [B, Hkv, T, ...] to tpad."""
+    out = np.zeros(a.shape[:2] + (tpad,) + a.shape[3:], a.dtype)
+    out[:, :, : a.shape[2]] = a
+    return out
+
+
+def _interleave8(a):
+    """[B, Hkv, Tp, X] -> [B, Hkv, Tp/8, X, 8] (blocks of 8 interleaved positions)."""
+    B_, H_, Tp, X = a.shape
+    return np.ascontiguousarray(a.reshape(B_, H_, Tp // 8, 8, X).transpose(0, 1, 2, 4, 3))
+
+
+def _write(store, ptr, arr):
+    raw = np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
+    store_region(store, ptr, raw.size, torch.uint8).copy_(torch.from_numpy(raw))
+
+
+def inject_oracle_codes(store, m, shape, lazy):
+    """Copy the oracle's int8 base codes and 4/8-bit residual codes (with their float16
+    scales) into the GPU store, in the store's documented layout."""
+    from oracle import quant
+    v = store.view()
+    B_, Hkv, hd = m.B, shape.n_kv_heads, shape.head_dim
+    R, K, Tp = shape.n_shared, shape.n_loops, v.row_stride
+    ng = hd // lazy.group
+    if lazy.base_bits == 8:
+        reg = B_ * Hkv * Tp * hd               # int8 elements of one (layer, K|V) region
+        sreg = B_ * Hkv * Tp * ng * 2          # bytes of its scale region
+        for r in range(R):
+            for kv in range(2):
+                codes, sc = m.base[r][kv]
+                codes, sc = _pad_t(codes, Tp), _pad_t(sc.view(np.uint16), Tp)
+                if kv == 1:
+                    codes, sc = _interleave8(codes), _interleave8(sc)
+                _write(store, v.base_codes + (2 * r + kv) * reg, codes)
+                _write(store, v.base_scales + (2 * r + kv) * sreg, sc)
+    if lazy.res_bits in (4, 8):
+        rows = B_ * Hkv * v.slots
+        for k in range(2, K + 1):
+            for r in range(R):
+                for kv in range(2):
+                    codes, sc = m.res[(k, r, kv)]
+                    reg = ((k - 2) * R + r) * 2 + kv
+                    packed = quant.pack_int4(codes) if lazy.res_bits == 4 else codes.view(np.uint8)
+                    _write(store, v.res_codes + reg * rows * v.res_row_bytes, packed)
+                    _write(store, v.res_scales + reg * rows * ng * 2, sc.view(np.uint16))
+    torch.cuda.synchronize()
+    store.keep_codes(True)
+
+
+def run_pair(shape, lazy, batch, prompt, steps, seed=0, force=True, weights=None, force_codes=None):
+    """Prefill + `steps` decode steps on the oracle and the GPU; returns a result dict.
+
+    force: inject the oracle's token and column selections.  force_codes (default:
+    when the residuals are 4-bit): also inject the oracle's quantized codes."""
     W = weights if weights is not None else I.gen_weights(shape, seed=seed)
     ids = I.gen_prompt_ids(shape, batch, prompt)
     dec = I.gen_decode_ids(shape, batch, steps)
@@ -67,11 +121,27 @@ def run_pair(shape, lazy, batch, prompt, steps, seed=0, force=True, weights=None
         tok, cols = oracle_selection(m, shape, batch)
         store.force_selection(torch.from_numpy(tok).cuda() if tok.size else None,
                               torch.from_numpy(cols).cuda())
+        if force_codes is None:
+            force_codes = lazy.res_bits == 4
+        if force_codes:
+            inject_oracle_codes(store, m, shape, lazy)
     g_out = model.prefill(store, torch.from_numpy(ids)).cpu().numpy()
     g_dec = [model.decode(store, torch.from_numpy(d)).cpu().numpy() for d in dec]
     torch.cuda.synchronize()
+    # the same computation with bf16 operands, on the same integer decisions as the GPU run
+    m16 = LoopedOracle(shape, lazy, W, batch, prompt + steps, operand_precision="bf16")
+    if lazy.mode == "lazy" and force:
+        m16.forced_tokens = dict(m.sel)
+        m16.forced_S = m.S
+        if force_codes:
+            m16.forced_codes_from = m
+    o16_out = m16.prefill(ids)
+    o16_dec = [m16.decode(d) for d in dec]
     res = dict(oracle=m, model=model, store=store, o_out=o_out, g_out=g_out, o_dec=o_dec, g_dec=g_dec,
-               t_oracle=t_oracle, ids=ids, dec=dec)
+               t_oracle=t_oracle, ids=ids, dec=dec, forced_codes=bool(force and force_codes))
     res["err_prefill"] = max_abs_rel(g_out, o_out)
     res["err_decode"] = [max_abs_rel(g, o) for g, o in zip(g_dec, o_dec)]
+    res["err16_prefill"] = max_abs_rel(g_out, o16_out)
+    res["err16_decode"] = [max_abs_rel(g, o) for g, o in zip(g_dec, o16_dec)]
+    res["bf16_drift"] = max_abs_rel(o16_out, o_out)
     return res

@@ -45,7 +45,7 @@ int main(void) {
   P(lk_model_cfg, ffn_act) P(lk_model_cfg, rms_eps) P(lk_model_cfg, rope_theta)
   P(lk_lazy_cfg, rho) P(lk_lazy_cfg, top_s) P(lk_lazy_cfg, group)
   P(lk_weights, layers) P(lk_layer_weights, w_down)
-  P(lk_store_view, slots) P(lk_store_view, n_selected) P(lk_store_view, res_row_bytes)
+  P(lk_store_view, slots) P(lk_store_view, n_selected) P(lk_store_view, res_row_bytes) P(lk_store_view, row_stride)
   return 0;
 }
 """

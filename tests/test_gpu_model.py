@@ -2,9 +2,15 @@
 
 With the oracle's token and column selections injected (forced selection), the
 final-normed hidden states must agree within max-abs-relative 2e-2 (bf16 GEMM
-operands and KV vs the float32 oracle).  Natural selection is compared too:
-index agreement is reported, and the store's byte count must equal the
-oracle's closed form exactly.
+operands and KV vs the float32 oracle).  With 4-bit residuals the oracle's
+quantized codes are injected as well: one int4 step is amax/7 of a group, so a
+code that flips between two implementations whose inputs differ by bf16
+rounding moves a K/V element by far more than that rounding, and the
+comparison of the floating-point path is made on equal integer decisions (the
+quantizer itself is compared bit for bit on identical inputs in
+test_gpu_kernels).  Natural selection and natural int4 codes are reported with
+a looser sanity bound.  The store's byte count must equal the oracle's closed
+form exactly.
 """
 import numpy as np
 import pytest
@@ -19,6 +25,22 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-2
 
 
+def check(r, what=""):
+    """GPU vs the float32 oracle and vs the oracle run with bf16 operands.
+
+    Bound: TOL (2e-2), or twice the oracle's own sensitivity to bf16 operand
+    rounding (max-abs-rel between its float32 and bf16-operand runs on the same
+    integer decisions) when that is larger.  A stack that moves by that much
+    under a 2^-9 perturbation of its operands cannot be held closer than that by
+    any bf16 implementation; for all but the widest shape the bound is TOL."""
+    tol = max(TOL, 2 * r["bf16_drift"])
+    log(f"  {what} vs fp32 oracle: prefill {r['err_prefill']:.3e} decode {max(r['err_decode'] or [0]):.3e}; "
+        f"vs bf16-operand oracle: prefill {r['err16_prefill']:.3e} decode {max(r['err16_decode'] or [0]):.3e}; "
+        f"oracle bf16 sensitivity {r['bf16_drift']:.3e}; bound {tol:.2e}")
+    assert r["err16_prefill"] < tol and max(r["err16_decode"] or [0]) < tol
+    assert r["err_prefill"] < tol and max(r["err_decode"] or [0]) < tol
+
+
 def tiny():
     return I.workload("tiny_1p2x2c1_t32")
 
@@ -29,9 +51,8 @@ def test_tiny_workload_matches_oracle(mode):
     lz = I.Lazy(**{**wl.lazy.__dict__, "mode": mode})
     log(f"tiny mode={mode}")
     r = run_pair(wl.shape, lz, wl.batch, wl.prompt, wl.decode_steps)
-    log(f"  prefill err {r['err_prefill']:.3e} decode err max {max(r['err_decode']):.3e}")
-    assert r["err_prefill"] < TOL
-    assert max(r["err_decode"]) < TOL
+    check(r, mode)
+    assert r["err_prefill"] < TOL and max(r["err_decode"]) < TOL
     assert r["model"].effective_depth() == accounting.effective_depth(wl.shape)
     used = r["store"].bytes_used()
     exp = accounting.kv_bytes(wl.shape, lz, wl.batch, wl.prompt, wl.prompt + wl.decode_steps)
@@ -62,9 +83,18 @@ def test_small_shapes_ragged_prompt(name, kw, lz):
     s = _small(**kw)
     log(f"small {name}")
     r = run_pair(s, lz, batch=2, prompt=150, steps=4, seed=5)
-    log(f"  prefill err {r['err_prefill']:.3e} decode err {np.max(r['err_decode']):.3e}")
-    assert r["err_prefill"] < TOL
-    assert max(r["err_decode"]) < TOL
+    check(r, name)
+
+
+def test_int4_natural_codes_drift_is_bounded():
+    """Without injected codes the int4 path differs from the oracle by code flips only."""
+    s = _small()
+    lz = I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4)
+    r = run_pair(s, lz, batch=2, prompt=150, steps=3, seed=5, force_codes=False)
+    f = run_pair(s, lz, batch=2, prompt=150, steps=3, seed=5, force_codes=True)
+    log(f"  int4 natural codes: prefill {r['err_prefill']:.3e} decode {max(r['err_decode']):.3e}")
+    check(f, "int4 injected codes")
+    assert r["err_prefill"] < 0.1 and max(r["err_decode"]) < 0.1
 
 
 def test_lazy_natural_selection_agrees_with_oracle():
@@ -141,7 +171,5 @@ def test_full_width_shapes_short_prompt(name, batch, prompt, steps):
     lz.window = max(4, prompt // 16)
     log(f"full-width {name} B={batch} T={prompt}")
     r = run_pair(wl.shape, lz, batch, prompt, steps)
-    log(f"  oracle {r['t_oracle']:.1f}s prefill err {r['err_prefill']:.3e} "
-        f"decode err {np.max(r['err_decode']):.3e}")
-    assert r["err_prefill"] < TOL
-    assert max(r["err_decode"]) < TOL
+    log(f"  oracle {r['t_oracle']:.1f}s")
+    check(r, name)

@@ -19,7 +19,7 @@ import torch
 
 from cross_loop_kv_amd import inputs as I
 from oracle import accounting
-from oracle.model import LoopedOracle, apply_rope, attend, rope_cos_sin, sparse_cols
+from oracle.model import LoopedOracle, apply_rope, attend, rope_cos_sin, round_bf16, sparse_cols
 from tests import torch_ref
 
 
@@ -245,3 +245,45 @@ def test_column_mass_matches_library_softmax_sums():
     p = torch.softmax(sc, dim=-1)                                          # [H, T(q), T(k)]
     ref = p.sum(dim=1).view(Hkv, 2, T).sum(dim=1).numpy()
     np.testing.assert_allclose(mass, ref, rtol=2e-5, atol=1e-6)
+
+
+def test_round_bf16_matches_library_conversion():
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal(100000) * 10 ** rng.uniform(-6, 6, 100000)).astype(np.float32)
+    # exact ties between bfloat16 neighbours, both parities
+    ties = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 3.0 * (1 + 2 ** -8)], np.float32)
+    x = np.concatenate([x, ties, np.zeros(1, np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(round_bf16(x), ref)
+
+
+def test_bf16_operand_mode_is_a_small_perturbation():
+    s = small_shape()
+    W = I.gen_weights(s, seed=17)
+    ids = I.gen_prompt_ids(s, 1, 24, seed=18)
+    out = {}
+    for prec in ("fp32", "bf16"):
+        m = LoopedOracle(s, I.Lazy(mode="per_loop"), W, 1, 24, operand_precision=prec)
+        out[prec] = m.prefill(ids)
+    assert 1e-5 < max_abs_rel(out["bf16"], out["fp32"]) < 3e-2
+
+
+def test_forced_codes_reproduce_the_source_oracle():
+    """An oracle that takes another oracle's selections and codes reproduces it exactly."""
+    s = small_shape()
+    W = I.gen_weights(s, seed=19)
+    ids = I.gen_prompt_ids(s, 2, 30, seed=20)
+    dec = I.gen_decode_ids(s, 2, 2, seed=21)
+    lz = I.Lazy(mode="lazy", rho=0.3, top_s=6, window=4, base_bits=8, res_bits=4)
+    a = LoopedOracle(s, lz, W, 2, 32)
+    oa = a.prefill(ids)
+    da = [a.decode(d) for d in dec]
+    b = LoopedOracle(s, lz, W, 2, 32)
+    b.forced_tokens = dict(a.sel)
+    b.forced_S = a.S
+    b.forced_codes_from = a
+    ob = b.prefill(ids)
+    db = [b.decode(d) for d in dec]
+    np.testing.assert_array_equal(oa, ob)
+    for x, y in zip(da, db):
+        np.testing.assert_array_equal(x, y)
