@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
     const int Hkv = kv.Hkv, b = bg / Hkv, g = bg % Hkv;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int c16 = lane & 15, kgrp = lane >> 4;
-    const int ncols = a.lens ? a.lens[bg] : a.pos + 1;
+    const int ncols = a.lens ? a.lens[bg] : (a.dpos ? *a.dpos : a.pos) + 1;
     const int c_begin = split * a.chunk;
     const int c_end = min(ncols, c_begin + a.chunk);
     const float sl2 = kLog2e / sqrtf((float)HD);
@@ -553,15 +553,26 @@ __device__ __forceinline__ void res8_apply(const KVLayer& v, int kv, int kk, lon
     }
 }
 
+// Block = 64 consecutive entries of one (b, g) column list.  The entries' positions
+// and loop-2..k slots are staged in LDS.  K: 4 threads per entry, row-major, one
+// contiguous run of hd/4 elements each.  V: 32 threads per 8 consecutive entries,
+// each owning hd/32 head dims; when the 8 entries are 8 consecutive positions
+// starting at a multiple of 8 (window, runs of S) the 8 keys of a head dim are one
+// vector load from the 8-key-interleaved store.
 template <int HD>
 __global__ __launch_bounds__(256) void gather_recon_kernel(RowsAttn a, int ncap, u16* __restrict__ kc,
                                                            u16* __restrict__ vc, int32_t* __restrict__ lens) {
-    constexpr int LPC = HD / 8;       // lanes per column (8 elements each)
-    constexpr int CPB = 256 / LPC;    // columns per block
-    __shared__ u16 vt[HD][CPB + 2];
+    constexpr int NCOL = 64;
+    constexpr int TPC = 256 / NCOL;        // threads per entry for K
+    constexpr int EPT = HD / TPC;          // K elements per thread (multiple of 8)
+    constexpr int TPG = 256 / (NCOL / 8);  // threads per group of 8 entries for V
+    constexpr int EPV = HD / TPG;          // V head dims per thread
+    __shared__ int s_col[NCOL];
+    __shared__ int s_slot[LK_MAX_LOOPS][NCOL];
     const KVLayer& v = a.kv;
+    const int t = threadIdx.x;
     const int bg = blockIdx.y, Hkv = v.Hkv, b = bg / Hkv, g = bg % Hkv;
-    const int pos = a.pos;
+    const int pos = a.dpos ? *a.dpos : a.pos;
     const int32_t* S = a.cols + (long long)bg * a.n_cols;
     const int lim = pos - a.window;
     int lo = 0, hi = a.n_cols;
@@ -573,42 +584,125 @@ __global__ __launch_bounds__(256) void gather_recon_kernel(RowsAttn a, int ncap,
     const int cntS = lo;
     const int win_lo = max(0, pos - a.window + 1);
     const int ncols = cntS + (pos - win_lo + 1);
-    if (blockIdx.x == 0 && threadIdx.x == 0) lens[bg] = ncols;
-    const int cl = threadIdx.x / LPC, m = threadIdx.x % LPC;
-    const int c = blockIdx.x * CPB + cl;
-    const int e0 = 8 * m;
-    float kx[8], vx[8];
+    if (blockIdx.x == 0 && t == 0) lens[bg] = ncols;
+    const int c0 = blockIdx.x * NCOL;
+    const int nres = v.lazy ? a.k_loop - 1 : 0;
+    if (t < NCOL) {
+        const int c = c0 + t;
+        int col = -1;
+        if (c < ncols) col = c < cntS ? S[c] : win_lo + (c - cntS);
+        s_col[t] = col;
+        for (int kk = 0; kk < nres; ++kk)
+            s_slot[kk][t] = col >= 0 ? v.slot[((long long)kk * v.B + b) * v.Tmax + col] : -1;
+    }
+    __syncthreads();
+    {   // ---- K rows
+        const int i = t / TPC, e0 = (t % TPC) * EPT;
+        const int col = s_col[i];
+        float x[EPT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kx[j] = vx[j] = 0.f;
-    if (c < ncols) {
-        const int col = c < cntS ? S[c] : win_lo + (c - cntS);
+        for (int j = 0; j < EPT; ++j) x[j] = 0.f;
+        if (col >= 0) {
+            const long long row = kv_row(v, b, g, col);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            kx[j] = kv_base_elem(v, 0, b, g, col, e0 + j);
-            vx[j] = kv_base_elem(v, 1, b, g, col, e0 + j);
+            for (int j8 = 0; j8 < EPT / 8; ++j8) {
+                const int e = e0 + 8 * j8;
+                if (!v.lazy || v.base_bits == 16) {
+                    const uint4 u = *(const uint4*)((const u16*)v.base[0] + row * HD + e);
+                    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        x[8 * j8 + 2 * q] = __uint_as_float(w4[q] << 16);
+                        x[8 * j8 + 2 * q + 1] = __uint_as_float(w4[q] & 0xFFFF0000u);
+                    }
+                } else {
+                    const uint2 u = *(const uint2*)((const int8_t*)v.base[0] + row * HD + e);
+                    const float sc = h2f(v.base_scale[0][row * (HD / 32) + e / 32]);
+                    const uint32_t w2[2] = {u.x, u.y};
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) x[8 * j8 + q] = (float)(int8_t)((w2[q >> 2] >> (8 * (q & 3))) & 0xFF) * sc;
+                }
+            }
+            for (int kk = 2; kk <= nres + 1; ++kk) {
+                const int sl = s_slot[kk - 2][i];
+                if (sl < 0) continue;
+                const long long rr = res_row(v, b, g, sl);
+#pragma unroll
+                for (int j8 = 0; j8 < EPT / 8; ++j8) res8_apply<HD>(v, 0, kk, rr, e0 + 8 * j8, x + 8 * j8);
+            }
         }
-        for (int kk = 2; kk <= a.k_loop; ++kk) {
-            const int sl = v.slot[((long long)(kk - 2) * v.B + b) * v.Tmax + col];
-            if (sl < 0) continue;
-            const long long rr = res_row(v, b, g, sl);
-            res8_apply<HD>(v, 0, kk, rr, e0, kx);
-            res8_apply<HD>(v, 1, kk, rr, e0, vx);
+        u16* dst = kc + ((long long)bg * ncap + c0 + i) * HD + e0;
+#pragma unroll
+        for (int j8 = 0; j8 < EPT / 8; ++j8) {
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = (uint32_t)f2h_bits(x[8 * j8 + 2 * q]) | ((uint32_t)f2h_bits(x[8 * j8 + 2 * q + 1]) << 16);
+            *(uint4*)(dst + 8 * j8) = make_uint4(o[0], o[1], o[2], o[3]);
         }
     }
-    uint32_t ko[4];
+    {   // ---- V, 8 entries at a time, written 8-key interleaved
+        const int grp = t / TPG, e0 = (t % TPG) * EPV;
+        const int cb = grp * 8;
+        const int p0 = s_col[cb];
+        bool run = p0 >= 0 && (p0 & 7) == 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ko[j] = (uint32_t)f2h_bits(kx[2 * j]) | ((uint32_t)f2h_bits(kx[2 * j + 1]) << 16);
-    *(uint4*)(kc + ((long long)bg * ncap + c) * HD + e0) = make_uint4(ko[0], ko[1], ko[2], ko[3]);
+        for (int j = 1; j < 8; ++j) run = run && s_col[cb + j] == p0 + j;
+        float vx[8][EPV];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) vt[e0 + j][cl] = f2h_bits(vx[j]);
-    __syncthreads();
-    // thread t writes 8 interleaved keys of one head dim: (e, group of 8 columns)
-    const int e = threadIdx.x % HD, grp = threadIdx.x / HD;
-    uint32_t vo[4];
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vo[j] = (uint32_t)vt[e][grp * 8 + 2 * j] | ((uint32_t)vt[e][grp * 8 + 2 * j + 1] << 16);
-    const long long blk = (long long)bg * (ncap / 8) + blockIdx.x * (CPB / 8) + grp;
-    *(uint4*)(vc + (blk * HD + e) * 8) = make_uint4(vo[0], vo[1], vo[2], vo[3]);
+            for (int q = 0; q < EPV; ++q) vx[j][q] = 0.f;
+        if (run) {
+#pragma unroll
+            for (int q = 0; q < EPV; ++q) {
+                const int e = e0 + q;
+                const long long vi = v_elem(v, b, g, p0, e);
+                if (!v.lazy || v.base_bits == 16) {
+                    const uint4 u = *(const uint4*)((const u16*)v.base[1] + vi);
+                    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        vx[2 * j][q] = __uint_as_float(w4[j] << 16);
+                        vx[2 * j + 1][q] = __uint_as_float(w4[j] & 0xFFFF0000u);
+                    }
+                } else {
+                    const uint2 u = *(const uint2*)((const int8_t*)v.base[1] + vi);
+                    const u16* sp = v.base_scale[1] + v_scale_idx(v, b, g, p0, e / 32);
+                    const uint32_t w2[2] = {u.x, u.y};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) vx[j][q] = (float)(int8_t)((w2[j >> 2] >> (8 * (j & 3))) & 0xFF) * h2f(sp[j]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int col = s_col[cb + j];
+                if (col < 0) continue;
+#pragma unroll
+                for (int q = 0; q < EPV; ++q) vx[j][q] = kv_base_elem(v, 1, b, g, col, e0 + q);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (s_col[cb + j] < 0) continue;
+            for (int kk = 2; kk <= nres + 1; ++kk) {
+                const int sl = s_slot[kk - 2][cb + j];
+                if (sl < 0) continue;
+#pragma unroll
+                for (int q = 0; q < EPV; ++q) vx[j][q] = kv_apply_res(v, 1, b, g, kk, sl, e0 + q, vx[j][q]);
+            }
+        }
+        const long long blk = (long long)bg * (ncap / 8) + (c0 + cb) / 8;
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) {
+            uint32_t o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = (uint32_t)f2h_bits(vx[2 * j][q]) | ((uint32_t)f2h_bits(vx[2 * j + 1][q]) << 16);
+            *(uint4*)(vc + (blk * HD + e0 + q) * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
 }
 
 // ---------------------------------------------------------------- sparse rows (VALU)
@@ -813,19 +907,21 @@ __global__ __launch_bounds__(64) void attn_rows_kernel(RowsAttn a) {
     }
 }
 
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part, int n_splits,
+// One block per (query row, KV head, query head of the group); thread e merges the
+// split partials of head dim e in split order.
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part, int n_splits,
                                                            int G, int HD, int H, int Hkv,
                                                            u16* __restrict__ out) {
     const long long qrow = blockIdx.x;
-    const int g = blockIdx.y;
-    const float* base = part + (qrow * Hkv + g) * (long long)n_splits * G * (HD + 2);
-    for (int idx = threadIdx.x; idx < G * HD; idx += 256) {
-        const int hh = idx / HD, e = idx % HD;
-        float M = -INFINITY;
-        for (int s = 0; s < n_splits; ++s) M = fmaxf(M, base[(long long)s * G * (HD + 2) + hh * (HD + 2) + HD]);
+    const int g = blockIdx.y, hh = blockIdx.z;
+    const long long stride = (long long)G * (HD + 2);
+    const float* base = part + (qrow * Hkv + g) * (long long)n_splits * stride + hh * (HD + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, base[s * stride + HD]);
+    for (int e = threadIdx.x; e < HD; e += blockDim.x) {
         float L = 0.f, acc = 0.f;
         for (int s = 0; s < n_splits; ++s) {
-            const float* ps = base + (long long)s * G * (HD + 2) + hh * (HD + 2);
+            const float* ps = base + s * stride;
             const float ms = ps[HD];
             if (ms == -INFINITY) continue;
             const float wgt = exp2f(ms - M);
@@ -937,8 +1033,7 @@ hipError_t attn_rows_main(const RowsAttn& a, hipStream_t st) {
 
 hipError_t gather_recon(const RowsAttn& a, int ncap, u16* kc, u16* vc, int32_t* lens, hipStream_t st) {
     const int hd = a.kv.hd;
-    const int cpb = 256 / (hd / 8);
-    dim3 grid(ncap / cpb, a.B * a.kv.Hkv);
+    dim3 grid(ncap / 64, a.B * a.kv.Hkv);
     switch (hd) {
         case 32: hipLaunchKernelGGL(gather_recon_kernel<32>, grid, dim3(256), 0, st, a, ncap, kc, vc, lens); break;
         case 64: hipLaunchKernelGGL(gather_recon_kernel<64>, grid, dim3(256), 0, st, a, ncap, kc, vc, lens); break;
@@ -949,8 +1044,8 @@ hipError_t gather_recon(const RowsAttn& a, int ncap, u16* kc, u16* vc, int32_t* 
 
 hipError_t attn_rows_combine(const RowsAttn& a, hipStream_t st) {
     const int G = a.H / a.kv.Hkv;
-    dim3 grid(a.B * a.n_rows, a.kv.Hkv);
-    hipLaunchKernelGGL(attn_combine_kernel, grid, dim3(256), 0, st, a.part, a.n_splits, G, a.kv.hd, a.H,
+    dim3 grid(a.B * a.n_rows, a.kv.Hkv, G);
+    hipLaunchKernelGGL(attn_combine_kernel, grid, dim3(a.kv.hd), 0, st, a.part, a.n_splits, G, a.kv.hd, a.H,
                        a.kv.Hkv, a.out);
     return hipGetLastError();
 }

@@ -60,6 +60,9 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t v, long long n) {
          i += (long long)gridDim.x * blockDim.x)
         p[i] = v;
 }
+__global__ void add_i32_kernel(int32_t* p, int32_t v) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) *p += v;
+}
 __global__ void fill_f32_kernel(float* p, float v, long long n) {
     for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
          i += (long long)gridDim.x * blockDim.x)
@@ -234,92 +237,85 @@ struct InvFreq {
 
 namespace {
 
-__global__ __launch_bounds__(kThreads) void rope_kv_write_kernel(const float* qkv, int rows_per_seq,
-                                                                 const int32_t* pos_arr, int pos_offset,
-                                                                 int H, int Hkv,
-                                                                 int hd, InvFreq inv, u16* q_out,
-                                                                 KVWrite w) {
-    __shared__ float cs[64], sn[64];
-    __shared__ float kvbuf[2 * 32 * 128];  // 2 * Hkv * hd <= 8192
-    const int r = blockIdx.x;
+// Block (row r, unit u), 128 threads.  Units [0, nq) rotate q heads (256/hd heads per
+// unit, one (head, pair index) per thread); unit nq + kv*Hkv + g handles K (kv = 0,
+// rotated) or V (kv = 1) head g: thread e owns element e and writes it to the store
+// (32-lane groups quantize together).
+__global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, int rows_per_seq,
+                                                            const int32_t* pos_arr, int pos_offset,
+                                                            int H, int Hkv, int hd, InvFreq inv,
+                                                            u16* q_out, KVWrite w) {
+    const int r = blockIdx.x, u = blockIdx.y, t = threadIdx.x;
     const int b = r / rows_per_seq;
     const int iseq = r % rows_per_seq;
-    const int pos = pos_arr ? pos_arr[r] : pos_offset + iseq;
+    const int t0 = w.dpos ? *w.dpos : pos_offset;
+    const int pos = pos_arr ? pos_arr[r] : t0 + iseq;
     const int half = hd / 2;
-    const int width = (H + 2 * Hkv) * hd;
-    const float* src = qkv + (long long)r * width;
-    for (int i = threadIdx.x; i < half; i += kThreads) {
-        double s, c;
-        sincos((double)pos * inv.v[i], &s, &c);
-        cs[i] = (float)c;
-        sn[i] = (float)s;
-    }
-    __syncthreads();
-    // q heads
-    for (int idx = threadIdx.x; idx < H * half; idx += kThreads) {
-        const int hh = idx / half, i = idx % half;
+    const float* src = qkv + (long long)r * (H + 2 * Hkv) * hd;
+    const int qpb = 256 / hd;
+    const int nq = (H + qpb - 1) / qpb;
+    if (u < nq) {
+        const int hh = u * qpb + t / half, i = t % half;
+        if (hh >= H) return;
+        double sd, cd;
+        sincos((double)pos * inv.v[i], &sd, &cd);
+        const float c = (float)cd, sn = (float)sd;
         const float x1 = src[hh * hd + i], x2 = src[hh * hd + i + half];
         u16* dq = q_out + (long long)r * H * hd + hh * hd;
-        dq[i] = f2bf(x1 * cs[i] - x2 * sn[i]);
-        dq[i + half] = f2bf(x2 * cs[i] + x1 * sn[i]);
+        dq[i] = f2bf(x1 * c - x2 * sn);
+        dq[i + half] = f2bf(x2 * c + x1 * sn);
+        return;
     }
-    // k heads (roped) and v heads into LDS
-    for (int idx = threadIdx.x; idx < Hkv * half; idx += kThreads) {
-        const int g = idx / half, i = idx % half;
+    const int kv = (u - nq) / Hkv, g = (u - nq) % Hkv;
+    const int e = t;
+    if (e >= hd) return;  // whole 32-lane groups (hd is a multiple of 32)
+    float x;
+    if (kv == 0) {
+        const int i = e % half;
+        double sd, cd;
+        sincos((double)pos * inv.v[i], &sd, &cd);
+        const float c = (float)cd, sn = (float)sd;
         const float x1 = src[(H + g) * hd + i], x2 = src[(H + g) * hd + i + half];
-        kvbuf[g * hd + i] = x1 * cs[i] - x2 * sn[i];
-        kvbuf[g * hd + i + half] = x2 * cs[i] + x1 * sn[i];
+        x = e < half ? x1 * c - x2 * sn : x2 * c + x1 * sn;
+    } else {
+        x = src[(H + Hkv + g) * hd + e];
     }
-    for (int idx = threadIdx.x; idx < Hkv * hd; idx += kThreads)
-        kvbuf[Hkv * hd + idx] = src[(H + Hkv) * hd + idx];
-    __syncthreads();
     const KVLayer& L = w.layer;
-    const int total = 2 * Hkv * hd;  // multiple of 64
-    const long long slot = w.slot_base + iseq;
-    for (int e0 = 0; e0 < total; e0 += kThreads) {
-        const int lin = e0 + threadIdx.x;
-        if (lin >= total) break;  // whole waves leave together (total % 64 == 0)
-        const int kv = lin / (Hkv * hd);
-        const int g = (lin / hd) % Hkv;
-        const int e = lin % hd;
-        const float x = kvbuf[lin];
-        const long long row = kv_row(L, b, g, pos);
-        const long long idx = kv == 0 ? row * hd + e : v_elem(L, b, g, pos, e);
-        if (w.kind == 0 || (w.kind == 1 && L.base_bits == 16)) {
-            ((u16*)L.base[kv])[idx] = f2bf(x);
-        } else if (w.kind == 1) {  // int8 base: residual against a zero reconstruction
-            if (w.keep_codes) continue;
+    const long long slot = w.slot_base + (w.dpos ? *w.dpos : 0) + iseq;
+    const long long row = kv_row(L, b, g, pos);
+    const long long idx = kv == 0 ? row * hd + e : v_elem(L, b, g, pos, e);
+    if (w.kind == 0 || (w.kind == 1 && L.base_bits == 16)) {
+        ((u16*)L.base[kv])[idx] = f2bf(x);
+    } else if (w.kind == 1) {  // int8 base: residual against a zero reconstruction
+        if (!w.keep_codes) {
             u16 sb;
             const int c = quant_group32(x, 127, &sb);
             ((int8_t*)L.base[kv])[idx] = (int8_t)c;
-            if ((threadIdx.x & 31) == 0) {
+            if ((t & 31) == 0) {
                 const long long si = kv == 0 ? row * (hd / 32) + e / 32 : v_scale_idx(L, b, g, pos, e / 32);
                 ((u16*)L.base_scale[kv])[si] = sb;
             }
-        } else {
-            const long long rr = res_row(L, b, g, slot);
-            if (L.res_bits == 16) {
-                ((u16*)L.res[w.loop - 2][kv])[rr * hd + e] = f2bf(x);
-            } else if (!w.keep_codes) {
-                const float prev = kv_recon_elem(L, kv, b, g, pos, e, w.loop - 1);
-                u16 sb;
-                const int qmax = (1 << (L.res_bits - 1)) - 1;
-                const int c = quant_group32(x - prev, qmax, &sb);
-                if ((threadIdx.x & 31) == 0)
-                    ((u16*)L.res_scale[w.loop - 2][kv])[rr * (hd / 32) + e / 32] = sb;
-                if (L.res_bits == 8) {
-                    ((int8_t*)L.res[w.loop - 2][kv])[rr * hd + e] = (int8_t)c;
-                } else {
-                    const int other = __shfl_xor(c, 1);
-                    if ((threadIdx.x & 1) == 0)
-                        ((uint8_t*)L.res[w.loop - 2][kv])[rr * (hd / 2) + e / 2] =
-                            (uint8_t)((c & 0xF) | ((other & 0xF) << 4));
-                }
+        }
+    } else {
+        const long long rr = res_row(L, b, g, slot);
+        if (L.res_bits == 16) {
+            ((u16*)L.res[w.loop - 2][kv])[rr * hd + e] = f2bf(x);
+        } else if (!w.keep_codes) {
+            const float prev = kv_recon_elem(L, kv, b, g, pos, e, w.loop - 1);
+            u16 sb;
+            const int qmax = (1 << (L.res_bits - 1)) - 1;
+            const int c = quant_group32(x - prev, qmax, &sb);
+            if ((t & 31) == 0) ((u16*)L.res_scale[w.loop - 2][kv])[rr * (hd / 32) + e / 32] = sb;
+            if (L.res_bits == 8) {
+                ((int8_t*)L.res[w.loop - 2][kv])[rr * hd + e] = (int8_t)c;
+            } else {
+                const int other = __shfl_xor(c, 1);
+                if ((t & 1) == 0)
+                    ((uint8_t*)L.res[w.loop - 2][kv])[rr * (hd / 2) + e / 2] = (uint8_t)((c & 0xF) | ((other & 0xF) << 4));
             }
         }
+        if (w.slot_map_k && u == nq && t == 0) w.slot_map_k[(long long)b * L.Tmax + pos] = (int32_t)slot;
     }
-    if (w.kind == 2 && w.slot_map_k && threadIdx.x == 0)
-        w.slot_map_k[(long long)b * L.Tmax + pos] = (int32_t)slot;
 }
 
 inline int grid_for(long long n) {
@@ -353,6 +349,10 @@ hipError_t copy_f32(const float* src, float* dst, long long n, hipStream_t st) {
 }
 hipError_t fill_i32(int32_t* p, int32_t v, long long n, hipStream_t st) {
     hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(n)), dim3(kThreads), 0, st, p, v, n);
+    return hipGetLastError();
+}
+hipError_t add_i32(int32_t* p, int32_t v, hipStream_t st) {
+    hipLaunchKernelGGL(add_i32_kernel, dim3(1), dim3(64), 0, st, p, v);
     return hipGetLastError();
 }
 hipError_t fill_f32(float* p, float v, long long n, hipStream_t st) {
@@ -398,7 +398,9 @@ hipError_t rope_kv_write(const float* qkv, int rows, int rows_per_seq, const int
                          hipStream_t st) {
     InvFreq inv;
     for (int i = 0; i < hd / 2; ++i) inv.v[i] = inv_freq[i];
-    hipLaunchKernelGGL(rope_kv_write_kernel, dim3(rows), dim3(kThreads), 0, st, qkv, rows_per_seq, pos,
+    const int qpb = 256 / hd;
+    const int units = (H + qpb - 1) / qpb + 2 * Hkv;
+    hipLaunchKernelGGL(rope_kv_write_kernel, dim3(rows, units), dim3(128), 0, st, qkv, rows_per_seq, pos,
                        pos_offset, H, Hkv, hd, inv, q_out, kvw);
     return hipGetLastError();
 }

@@ -133,13 +133,18 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const u16* __restrict__
 }
 
 // ---------------------------------------------------------------- skinny kernel
-template <int EPI, int J>
-__global__ __launch_bounds__(512) void gemm_skinny_kernel(const u16* __restrict__ A,
+// NORM: the A operand is RMSNorm(X) * gain computed on the fly from float32 rows X:
+// the kernel multiplies by bf16(X * gain), reduces the row sums of squares in the same
+// pass and scales the result by 1 / sqrt(mean(X^2) + eps) in the epilogue.
+template <int EPI, int J, bool NORM>
+__global__ __launch_bounds__(512) void gemm_skinny_kernel(const u16* __restrict__ A, const float* __restrict__ X,
+                                                          const u16* __restrict__ gain, float eps,
                                                           const u16* __restrict__ W, int M, int N,
                                                           int K, float* __restrict__ C,
                                                           u16* __restrict__ Obf) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
     __shared__ f32x4 red[8][64][DUAL ? 2 : 1];
+    __shared__ float ssq[8][64];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int c16 = lane & 15, grp = lane >> 4;
     const int n = blockIdx.x * 16 + c16;
@@ -151,7 +156,9 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(const u16* __restrict_
     const u16* w1 = W + (long long)(nvalid ? N + n : 0) * K;
     const bool mvalid = c16 < M;
     const u16* ar = A + (long long)(mvalid ? c16 : 0) * K;
+    const float* xr = X + (long long)(mvalid ? c16 : 0) * K;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
     for (int c = cb; c < ce; ++c) {
         const int k0 = c * CH + grp * 8 * J;
         uint4 wv[J], av[J], wv1[J];
@@ -159,7 +166,29 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(const u16* __restrict_
         for (int j = 0; j < J; ++j) {
             wv[j] = *(const uint4*)(w0 + k0 + j * 8);
             if (DUAL) wv1[j] = *(const uint4*)(w1 + k0 + j * 8);
-            av[j] = mvalid ? *(const uint4*)(ar + k0 + j * 8) : make_uint4(0, 0, 0, 0);
+            if (!NORM) av[j] = mvalid ? *(const uint4*)(ar + k0 + j * 8) : make_uint4(0, 0, 0, 0);
+        }
+        if (NORM) {
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                if (!mvalid) {
+                    av[j] = make_uint4(0, 0, 0, 0);
+                    continue;
+                }
+                const float4 xa = *(const float4*)(xr + k0 + j * 8);
+                const float4 xb = *(const float4*)(xr + k0 + j * 8 + 4);
+                const uint4 gv = *(const uint4*)(gain + k0 + j * 8);
+                const float xs[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+                const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+                uint32_t o[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    ss += xs[2 * q] * xs[2 * q] + xs[2 * q + 1] * xs[2 * q + 1];
+                    o[q] = pack_bf2(xs[2 * q] * __uint_as_float(gw[q] << 16),
+                                    xs[2 * q + 1] * __uint_as_float(gw[q] & 0xFFFF0000u));
+                }
+                av[j] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
         }
 #pragma unroll
         for (int j = 0; j < J; ++j) {
@@ -170,6 +199,7 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(const u16* __restrict_
     }
     red[w][lane][0] = acc0;
     if (DUAL) red[w][lane][DUAL ? 1 : 0] = acc1;
+    if (NORM) ssq[w][lane] = ss;
     __syncthreads();
     if (w != 0) return;
     f32x4 s0 = red[0][lane][0], s1 = DUAL ? red[0][lane][DUAL ? 1 : 0] : s0;
@@ -178,31 +208,51 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(const u16* __restrict_
         s0 += red[ww][lane][0];
         if (DUAL) s1 += red[ww][lane][DUAL ? 1 : 0];
     }
-    if (!nvalid) return;
     // acc lane l: D[row = (l/16)*4 + i][col = l%16]
+    float inv[4] = {1.f, 1.f, 1.f, 1.f};
+    if (NORM) {
+        // row m's partial sums sit in lanes m, m+16, m+32, m+48 of every wave
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = grp * 4 + i;
+            float t = 0.f;
+            for (int ww = 0; ww < 8; ++ww)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) t += ssq[ww][m + 16 * gq];
+            inv[i] = 1.0f / sqrtf(t / (float)K + eps);
+        }
+    }
+    if (!nvalid) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int m = grp * 4 + i;
         if (m >= M) continue;
         const long long o = (long long)m * N + n;
-        if (EPI == EPI_STORE) C[o] = s0[i];
-        else if (EPI == EPI_ADD) C[o] = C[o] + s0[i];
-        else if (EPI == EPI_SWIGLU) Obf[o] = f2bf(silu_f(s0[i]) * s1[i]);
-        else Obf[o] = f2bf(gelu_f(s0[i]));
+        const float v0 = s0[i] * inv[i];
+        if (EPI == EPI_STORE) C[o] = v0;
+        else if (EPI == EPI_ADD) C[o] = C[o] + v0;
+        else if (EPI == EPI_SWIGLU) Obf[o] = f2bf(silu_f(v0) * (s1[i] * inv[i]));
+        else Obf[o] = f2bf(gelu_f(v0));
     }
+}
+
+template <int EPI, bool NORM>
+void launch_skinny(const u16* A, const float* X, const u16* gain, float eps, const u16* W, int M, int N, int K,
+                   float* c, u16* out_bf, hipStream_t st) {
+    dim3 grid((N + 15) / 16);
+    if (K % 128 == 0)
+        hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 4, NORM>), grid, dim3(512), 0, st, A, X, gain, eps, W, M, N, K, c, out_bf);
+    else if (K % 64 == 0)
+        hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 2, NORM>), grid, dim3(512), 0, st, A, X, gain, eps, W, M, N, K, c, out_bf);
+    else
+        hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 1, NORM>), grid, dim3(512), 0, st, A, X, gain, eps, W, M, N, K, c, out_bf);
 }
 
 template <int EPI>
 hipError_t launch_gemm(const u16* A, const u16* W, int M, int N, int K, float* c, u16* out_bf,
                        hipStream_t st) {
     if (M <= 16) {
-        dim3 grid((N + 15) / 16);
-        if (K % 128 == 0)
-            hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 4>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf);
-        else if (K % 64 == 0)
-            hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 2>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf);
-        else
-            hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 1>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf);
+        launch_skinny<EPI, false>(A, nullptr, nullptr, 0.f, W, M, N, K, c, out_bf, st);
     } else {
         const int bn = (EPI == EPI_SWIGLU) ? 64 : BN;
         dim3 grid((N + bn - 1) / bn, (M + BM - 1) / BM);
@@ -212,6 +262,17 @@ hipError_t launch_gemm(const u16* A, const u16* W, int M, int N, int K, float* c
 }
 
 }  // namespace
+
+hipError_t gemm_rmsnorm(const float* X, const u16* gain, float eps, const u16* W, int M, int N, int K, int epi,
+                        float* c, u16* out_bf, hipStream_t st) {
+    switch (epi) {
+        case EPI_STORE: launch_skinny<EPI_STORE, true>(nullptr, X, gain, eps, W, M, N, K, c, out_bf, st); break;
+        case EPI_ADD: launch_skinny<EPI_ADD, true>(nullptr, X, gain, eps, W, M, N, K, c, out_bf, st); break;
+        case EPI_SWIGLU: launch_skinny<EPI_SWIGLU, true>(nullptr, X, gain, eps, W, M, N, K, c, out_bf, st); break;
+        default: launch_skinny<EPI_GELU, true>(nullptr, X, gain, eps, W, M, N, K, c, out_bf, st); break;
+    }
+    return hipGetLastError();
+}
 
 hipError_t gemm(const u16* A, const u16* W, int M, int N, int K, int epi, float* c, u16* out_bf,
                 hipStream_t st) {

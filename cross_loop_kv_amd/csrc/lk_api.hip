@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <algorithm>
 #include <cstring>
+#include <functional>
 #include <string>
 #include <vector>
 
@@ -64,7 +65,7 @@ static const char* kTimedNames[TC_COUNT] = {"attn_decode_dense", "attn_decode_sp
 
 struct EventTimer {
     int cls = TC_NONE;
-    std::vector<hipEvent_t> pool;
+    std::vector<hipEvent_t> pool;  // pairs (start, end), one per timed launch
     size_t used = 0;
     hipError_t mark(hipStream_t st) {
         if (used == pool.size()) {
@@ -80,10 +81,39 @@ struct EventTimer {
     }
 };
 
+// A decode step prepared for replay: captured HIP graphs, cut around every launch
+// of the timed kernel class (those are launched directly, between two recorded
+// events, so that their duration is measured on the stream), plus the key it was
+// prepared for.  With timing off the step is one graph.
+struct DecodeGraph {
+    struct Seg {
+        hipGraphExec_t exec = nullptr;           // a captured run of launches, or
+        std::function<hipError_t()> direct;      // one timed launch
+    };
+    std::vector<Seg> segs;
+    const void* store = nullptr;
+    const void* ws = nullptr;
+    hipStream_t stream = nullptr;
+    int timer_cls = -2;
+    int keep_codes = 0;
+    void reset() {
+        for (Seg& g : segs)
+            if (g.exec) (void)hipGraphExecDestroy(g.exec);
+        segs.clear();
+        store = ws = nullptr;
+        stream = nullptr;
+        timer_cls = -2;
+    }
+    ~DecodeGraph() { reset(); }
+};
+
 struct lk_handle {
     lk_model_cfg c;
     lk_lazy_cfg z;
     EventTimer timer;
+    DecodeGraph graph;
+    DecodeGraph* building = nullptr;  // set while a decode step is being captured
+    int use_graphs = 1;
     const u16 *tok, *lemb, *fnorm;
     std::vector<lk_layer_weights> L;
     double inv_freq[64];
@@ -93,7 +123,7 @@ struct lk_handle {
 };
 
 struct StoreLayout {
-    size_t dense, loop_rows, base, base_sc, res, res_sc, slot, cols, total;
+    size_t dense, loop_rows, base, base_sc, res, res_sc, slot, cols, state, total;
     long long slots;
     int n_sel, n_cols;
     long long res_row_b;
@@ -153,6 +183,7 @@ StoreLayout store_layout(const lk_handle* h, int B, int Tp, int Tmax) {
         s.n_cols = h->z.top_s < Tp ? h->z.top_s : Tp;
         s.cols = take((size_t)c.n_shared * B * Hkv * s.n_cols * 4);
     }
+    s.state = take(64);  // int32 decode position t (device copy of the store length)
     s.total = off;
     return s;
 }
@@ -252,6 +283,8 @@ KVLayer lazy_layer(const lk_kv_store* s, int r) {
 int32_t* slot_map(const lk_kv_store* s, int k) {
     return (int32_t*)(s->buf + s->lay.slot) + (long long)(k - 2) * s->B * s->Tpad;
 }
+int32_t* dev_pos(const lk_kv_store* s) { return (int32_t*)(s->buf + s->lay.state); }
+
 int32_t* col_sets(const lk_kv_store* s, int r) {
     return (int32_t*)(s->buf + s->lay.cols) + (long long)r * s->B * s->h->c.n_kv_heads * s->lay.n_cols;
 }
@@ -262,6 +295,8 @@ struct WS {
     u16 *xn, *q, *att, *act;
     u16 *kc, *vc;      // decode, loops >= 2: materialized reconstruction of the column lists
     int32_t *sel, *lens;
+    int32_t* ids;      // decode: the step's token ids (fixed address for graph replay)
+    float* out;        // decode: the step's output rows
     int ncap;          // column capacity of kc / vc per (sequence, KV head)
     size_t total;
     long long part_floats;
@@ -307,6 +342,8 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
     w.kc = (u16*)take(kvc);
     w.vc = (u16*)take(kvc);
     w.lens = (int32_t*)take(hd_->lazy() ? (long long)B * c.n_kv_heads * 4 : 0);
+    w.ids = (int32_t*)take((long long)B * 4);
+    w.out = (float*)take((long long)B * d * 4);
     w.total = off;
     return w;
 }
@@ -349,6 +386,7 @@ struct LayerIO {
     const int32_t* pos;      // positions (nullptr: pos_offset + row index within the sequence)
     int pos_offset;
     const u16* add;          // loop embedding added before the layer (nullptr: none)
+    const int32_t* dpos;     // decode: device position t (replaces pos_offset)
 };
 
 enum AttnKind { ATTN_PREFILL_DENSE, ATTN_ROWS_DENSE, ATTN_ROWS_SPARSE };
@@ -360,14 +398,40 @@ struct AttnPlan {
     const int32_t* cols;     // sparse column sets of the layer
     int n_cols, window;
     int B, T;                // prefill: batch and tokens per sequence
-    int pos;                 // decode position (rows attention)
+    int pos;                 // decode: capacity - 1 (splits are sized for the full store)
+    const int32_t* dpos;     // decode: device position t
     float* mass;             // lazy loop 1: column mass output
 };
 
+// End the capture running on `st` and append what it recorded (if anything) as a
+// graph segment of the step being built.
+int cut_segment(lk_handle* h, hipStream_t st) {
+    hipGraph_t graph = nullptr;
+    LK_HIP(hipStreamEndCapture(st, &graph));
+    size_t n = 0;
+    hipError_t e = hipGraphGetNodes(graph, nullptr, &n);
+    DecodeGraph::Seg seg;
+    if (e == hipSuccess && n > 0) e = hipGraphInstantiate(&seg.exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(LK_ERR_HIP, std::string("decode graph: ") + hipGetErrorString(e));
+    if (seg.exec) h->building->segs.push_back(std::move(seg));
+    return LK_OK;
+}
+
 // Launch `fn` bracketed by timer events when its class is the instrumented one.
+// While a decode step is being captured, such a launch becomes a direct segment
+// of the step instead (`fn` captures its arguments by value).
 template <typename F>
 int timed(lk_handle* h, int cls, hipStream_t st, F fn) {
     const bool on = h->timer.cls == cls;
+    if (on && h->building) {
+        LK_TRY(cut_segment(h, st));
+        DecodeGraph::Seg seg;
+        seg.direct = fn;
+        h->building->segs.push_back(std::move(seg));
+        LK_HIP(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal));
+        return LK_OK;
+    }
     if (on) LK_HIP(h->timer.mark(st));
     LK_HIP(fn());
     if (on) LK_HIP(h->timer.mark(st));
@@ -380,26 +444,38 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
     const int gcls = ap.kind == ATTN_PREFILL_DENSE || io.rows_per_seq > 1 ? TC_GEMM_PREFILL : TC_GEMM_DECODE;
     const lk_layer_weights& W = h->L[li];
     const int d = c.d_model, H = c.n_heads, hd = c.head_dim, Hhd = H * hd;
-    LK_HIP(lk::rmsnorm(io.x, io.add, (const u16*)W.attn_norm, c.rms_eps, io.M, d, w.xn, nullptr, st));
-    LK_TRY(timed(h, gcls, st, [&] {
-        return lk::gemm(w.xn, (const u16*)W.wqkv, io.M, h->qkv_w(), d, lk::EPI_STORE, w.qkv, nullptr, st);
-    }));
+    // decode-sized row counts fold the RMSNorm into the skinny GEMMs
+    const bool fused_norm = io.M <= 16;
+    if (fused_norm) {
+        if (io.add) LK_HIP(lk::add_rows(io.x, io.add, io.M, d, st));
+        LK_TRY(timed(h, gcls, st, [=] {
+            return lk::gemm_rmsnorm(io.x, (const u16*)W.attn_norm, c.rms_eps, (const u16*)W.wqkv, io.M, h->qkv_w(),
+                                    d, lk::EPI_STORE, w.qkv, nullptr, st);
+        }));
+    } else {
+        LK_HIP(lk::rmsnorm(io.x, io.add, (const u16*)W.attn_norm, c.rms_eps, io.M, d, w.xn, nullptr, st));
+        LK_TRY(timed(h, gcls, st, [=] {
+            return lk::gemm(w.xn, (const u16*)W.wqkv, io.M, h->qkv_w(), d, lk::EPI_STORE, w.qkv, nullptr, st);
+        }));
+    }
     // RoPE positions: explicit, or the row index within the sequence (+ offset for decode)
     const int32_t* pos = io.pos;
     lk::KVWrite kw = kvw;
+    kw.dpos = io.dpos;
     LK_HIP(lk::rope_kv_write(w.qkv, io.M, io.rows_per_seq, pos, io.pos_offset, H, c.n_kv_heads, hd,
                              h->inv_freq, w.q, kw, st));
     if (ap.kind == ATTN_PREFILL_DENSE) {
         LK_TRY(timed(h, TC_ATTN_PREFILL, st,
-                     [&] { return lk::attn_prefill(w.q, ap.read, ap.B, ap.T, H, w.att, w.lse, st); }));
+                     [=] { return lk::attn_prefill(w.q, ap.read, ap.B, ap.T, H, w.att, w.lse, st); }));
         if (ap.mass)
             LK_TRY(timed(h, TC_COLUMN_MASS, st,
-                         [&] { return lk::column_mass(w.q, ap.read, w.lse, ap.B, ap.T, H, ap.mass, st); }));
+                         [=] { return lk::column_mass(w.q, ap.read, w.lse, ap.B, ap.T, H, ap.mass, st); }));
     } else {
         lk::RowsAttn a{};
         a.q = w.q;
         a.qpos = io.pos;
         a.pos = ap.pos;
+        a.dpos = ap.dpos;
         a.B = io.M / io.rows_per_seq;
         a.n_rows = io.rows_per_seq;
         a.H = H;
@@ -417,7 +493,7 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
             ncol_max = (long long)ap.pos + 1;
         }
         // dense decode: one workgroup per (sequence, KV head, chunk), about 1536 workgroups
-        auto dense_chunk = [&](long long ncol) {
+        auto dense_chunk = [=](long long ncol) {
             const long long pairs = (long long)a.B * c.n_kv_heads;
             const long long want = (ncol * pairs + 1535) / 1536;
             int ch = (int)std::max(128LL, (want + 127) / 128 * 128);
@@ -451,7 +527,7 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
             d.n_splits = (ncap + d.chunk - 1) / d.chunk;
             if ((long long)a.B * H * d.n_splits * (hd + 2) > w.part_floats)
                 return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
-            LK_TRY(timed(h, TC_ATTN_DECODE_SPARSE, st, [&] {
+            LK_TRY(timed(h, TC_ATTN_DECODE_SPARSE, st, [=] {
                 hipError_t e = lk::gather_recon(a, ncap, w.kc, w.vc, w.lens, st);
                 return e != hipSuccess ? e : lk::attn_rows_main(d, st);
             }));
@@ -466,17 +542,24 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
                 return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
             const int acls = io.rows_per_seq > 1 ? TC_ATTN_PREFILL_SPARSE
                              : (ap.kind == ATTN_ROWS_SPARSE ? TC_ATTN_DECODE_SPARSE : TC_ATTN_DECODE_DENSE);
-            LK_TRY(timed(h, acls, st, [&] { return lk::attn_rows_main(a, st); }));
+            LK_TRY(timed(h, acls, st, [=] { return lk::attn_rows_main(a, st); }));
             LK_HIP(lk::attn_rows_combine(a, st));
         }
     }
     LK_TRY(timed(h, gcls, st,
-                 [&] { return lk::gemm(w.att, (const u16*)W.wo, io.M, d, Hhd, lk::EPI_ADD, io.x, nullptr, st); }));
-    LK_HIP(lk::rmsnorm(io.x, nullptr, (const u16*)W.ffn_norm, c.rms_eps, io.M, d, w.xn, nullptr, st));
+                 [=] { return lk::gemm(w.att, (const u16*)W.wo, io.M, d, Hhd, lk::EPI_ADD, io.x, nullptr, st); }));
     const int act = c.ffn_act == LK_ACT_SWIGLU ? lk::EPI_SWIGLU : lk::EPI_GELU;
-    LK_TRY(timed(h, gcls, st,
-                 [&] { return lk::gemm(w.xn, (const u16*)W.w_in, io.M, c.ffn_dim, d, act, nullptr, w.act, st); }));
-    LK_TRY(timed(h, gcls, st, [&] {
+    if (fused_norm) {
+        LK_TRY(timed(h, gcls, st, [=] {
+            return lk::gemm_rmsnorm(io.x, (const u16*)W.ffn_norm, c.rms_eps, (const u16*)W.w_in, io.M, c.ffn_dim, d,
+                                    act, nullptr, w.act, st);
+        }));
+    } else {
+        LK_HIP(lk::rmsnorm(io.x, nullptr, (const u16*)W.ffn_norm, c.rms_eps, io.M, d, w.xn, nullptr, st));
+        LK_TRY(timed(h, gcls, st,
+                     [=] { return lk::gemm(w.xn, (const u16*)W.w_in, io.M, c.ffn_dim, d, act, nullptr, w.act, st); }));
+    }
+    LK_TRY(timed(h, gcls, st, [=] {
         return lk::gemm(w.act, (const u16*)W.w_down, io.M, d, c.ffn_dim, lk::EPI_ADD, io.x, nullptr, st);
     }));
     return LK_OK;
@@ -564,7 +647,14 @@ int lk_kv_store_alloc(lk_handle* h, int32_t batch, int32_t prompt_tokens, int32_
     return LK_OK;
 }
 
-void lk_kv_store_release(lk_kv_store* s) { delete s; }
+void lk_kv_store_release(lk_kv_store* s) {
+    if (!s) return;
+    if (s->h && s->h->graph.store == s) {  // its captured decode step refers to this store
+        (void)hipDeviceSynchronize();
+        s->h->graph.reset();
+    }
+    delete s;
+}
 
 int lk_kv_store_bytes_used(const lk_kv_store* s, size_t* shared, size_t* total) {
     if (!s || !shared || !total) return fail(LK_ERR_INVALID_ARG, "null argument");
@@ -723,31 +813,31 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
         LK_TRY(run_layer(h, P + R + j, io, plain_write(dense_plan.read), dense_plan, w, st));
     }
     LK_HIP(lk::rmsnorm(w.h, nullptr, h->fnorm, c.rms_eps, M, d, nullptr, d_out, st));
+    LK_HIP(lk::fill_i32(dev_pos(s), T, 1, st));
     s->t = T;
     s->prefilled = true;
     return LK_OK;
 }
 
-int lk_looped_decode_step(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, float* d_out, void* d_ws,
-                          size_t ws_bytes, void* stream) {
-    if (!h || !s || !d_ids || !d_out || !d_ws) return fail(LK_ERR_INVALID_ARG, "null argument");
-    if (s->h != h) return fail(LK_ERR_INVALID_ARG, "store belongs to another handle");
-    if (!s->prefilled) return fail(LK_ERR_STATE, "decode before prefill");
-    if (s->t >= s->Tmax) return fail(LK_ERR_CAPACITY, "store is full (max_tokens reached)");
-    const int B = s->B;
-    const WS w = ws_layout(h, B, 1, (char*)d_ws);
-    if (ws_bytes < w.total) return fail(LK_ERR_CAPACITY, "workspace too small");
-    if ((uintptr_t)d_ws % kAlign) return fail(LK_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    hipStream_t st = (hipStream_t)stream;
+}  // extern "C"
+
+namespace {
+
+// Enqueue one decode step: ids from w.ids, output rows to w.out, position from the
+// store's device counter (incremented at the end).  Nothing here depends on the
+// host's copy of the position, so the same launches serve every step.
+int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
     const lk_model_cfg& c = h->c;
     const int P = c.n_prelude, R = c.n_shared, K = c.n_loops, Q = c.n_coda, d = c.d_model;
-    const int t = s->t;
-    LK_HIP(lk::embed(d_ids, h->tok, w.h, B, d, c.vocab, st));
-    LayerIO io{w.h, B, 1, nullptr, t, nullptr};
+    const int B = s->B;
+    const int32_t* dpos = dev_pos(s);
+    LK_HIP(lk::embed(w.ids, h->tok, w.h, B, d, c.vocab, st));
+    LayerIO io{w.h, B, 1, nullptr, 0, nullptr, dpos};
     AttnPlan dense{};
     dense.kind = ATTN_ROWS_DENSE;
     dense.k_loop = 1;
-    dense.pos = t;
+    dense.pos = s->Tmax - 1;
+    dense.dpos = dpos;
     for (int li = 0; li < P; ++li) {
         dense.read = dense_layer(s, li);
         LK_TRY(run_layer(h, li, io, plain_write(dense.read), dense, w, st));
@@ -762,7 +852,8 @@ int lk_looped_decode_step(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, fl
             }
             AttnPlan ap{};
             ap.read = lazy_layer(s, r);
-            ap.pos = t;
+            ap.pos = s->Tmax - 1;
+            ap.dpos = dpos;
             lk::KVWrite kw{};
             kw.layer = ap.read;
             kw.keep_codes = s->keep_codes;
@@ -778,7 +869,7 @@ int lk_looped_decode_step(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, fl
                 ap.window = h->z.window;
                 kw.kind = 2;
                 kw.loop = k;
-                kw.slot_base = (long long)s->lay.n_sel + (t - s->Tp);
+                kw.slot_base = (long long)s->lay.n_sel - s->Tp;  // slot = n_sel + (t - T)
                 kw.slot_map_k = slot_map(s, k);
             }
             LK_TRY(run_layer(h, P + r, io, kw, ap, w, st));
@@ -789,22 +880,94 @@ int lk_looped_decode_step(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, fl
         dense.read = dense_layer(s, P + j);
         LK_TRY(run_layer(h, P + R + j, io, plain_write(dense.read), dense, w, st));
     }
-    LK_HIP(lk::rmsnorm(w.h, nullptr, h->fnorm, c.rms_eps, B, d, nullptr, d_out, st));
-    s->t = t + 1;
+    LK_HIP(lk::rmsnorm(w.h, nullptr, h->fnorm, c.rms_eps, B, d, nullptr, w.out, st));
+    LK_HIP(lk::add_i32(dev_pos(s), 1, st));
+    return LK_OK;
+}
+
+// Capture one decode step on `st` into h->graph (segments as described there).
+int capture_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
+    LK_HIP(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal));
+    h->building = &h->graph;
+    int rc = enqueue_decode(h, s, w, st);
+    if (rc == LK_OK) rc = cut_segment(h, st);
+    h->building = nullptr;
+    if (rc != LK_OK) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone) {
+            hipGraph_t g = nullptr;
+            (void)hipStreamEndCapture(st, &g);
+            if (g) (void)hipGraphDestroy(g);
+        }
+        h->graph.reset();
+    }
+    return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lk_looped_decode_step(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, float* d_out, void* d_ws,
+                          size_t ws_bytes, void* stream) {
+    if (!h || !s || !d_ids || !d_out || !d_ws) return fail(LK_ERR_INVALID_ARG, "null argument");
+    if (s->h != h) return fail(LK_ERR_INVALID_ARG, "store belongs to another handle");
+    if (!s->prefilled) return fail(LK_ERR_STATE, "decode before prefill");
+    if (s->t >= s->Tmax) return fail(LK_ERR_CAPACITY, "store is full (max_tokens reached)");
+    const int B = s->B;
+    const WS w = ws_layout(h, B, 1, (char*)d_ws);
+    if (ws_bytes < w.total) return fail(LK_ERR_CAPACITY, "workspace too small");
+    if ((uintptr_t)d_ws % kAlign) return fail(LK_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    const int d = h->c.d_model;
+    LK_HIP(hipMemcpyAsync(w.ids, d_ids, (size_t)B * 4, hipMemcpyDeviceToDevice, st));
+    if (st && h->use_graphs) {
+        DecodeGraph& g = h->graph;
+        if (g.store != s || g.ws != d_ws || g.stream != st || g.timer_cls != h->timer.cls ||
+            g.keep_codes != s->keep_codes) {
+            g.reset();
+            LK_TRY(capture_decode(h, s, w, st));
+            g.store = s;
+            g.ws = d_ws;
+            g.stream = st;
+            g.timer_cls = h->timer.cls;
+            g.keep_codes = s->keep_codes;
+        }
+        for (const DecodeGraph::Seg& seg : g.segs) {
+            if (seg.exec) {
+                LK_HIP(hipGraphLaunch(seg.exec, st));
+            } else {
+                LK_HIP(h->timer.mark(st));
+                LK_HIP(seg.direct());
+                LK_HIP(h->timer.mark(st));
+            }
+        }
+    } else {
+        LK_TRY(enqueue_decode(h, s, w, st));
+    }
+    LK_HIP(hipMemcpyAsync(d_out, w.out, (size_t)B * d * 4, hipMemcpyDeviceToDevice, st));
+    s->t += 1;
+    return LK_OK;
+}
+
+int lk_set_decode_graphs(lk_handle* h, int32_t enable) {
+    if (!h) return fail(LK_ERR_INVALID_ARG, "null handle");
+    h->use_graphs = enable ? 1 : 0;
+    h->graph.reset();
     return LK_OK;
 }
 
 int lk_timing_enable(lk_handle* h, const char* kernel_class) {
     if (!h) return fail(LK_ERR_INVALID_ARG, "null handle");
+    int cls = TC_NONE;
+    if (kernel_class) {
+        for (int i = 0; i < TC_COUNT; ++i)
+            if (std::strcmp(kernel_class, kTimedNames[i]) == 0) cls = i;
+        if (cls == TC_NONE) return fail(LK_ERR_INVALID_ARG, std::string("unknown kernel class ") + kernel_class);
+    }
     h->timer.used = 0;
-    h->timer.cls = TC_NONE;
-    if (!kernel_class) return LK_OK;
-    for (int i = 0; i < TC_COUNT; ++i)
-        if (std::strcmp(kernel_class, kTimedNames[i]) == 0) {
-            h->timer.cls = i;
-            return LK_OK;
-        }
-    return fail(LK_ERR_INVALID_ARG, std::string("unknown kernel class ") + kernel_class);
+    h->timer.cls = cls;
+    return LK_OK;
 }
 
 int lk_timing_read(lk_handle* h, int32_t* launches, double* total_ms) {
@@ -817,6 +980,7 @@ int lk_timing_read(lk_handle* h, int32_t* launches, double* total_ms) {
         LK_HIP(hipEventElapsedTime(&ms, h->timer.pool[2 * i], h->timer.pool[2 * i + 1]));
         tot += ms;
     }
+    h->timer.used = 0;
     *launches = (int32_t)n;
     *total_ms = tot;
     return LK_OK;

@@ -21,6 +21,7 @@ hipError_t add_rows(float* x, const u16* add, int rows, int d, hipStream_t st);
 hipError_t copy_f32(const float* src, float* dst, long long n, hipStream_t st);
 hipError_t fill_i32(int32_t* p, int32_t v, long long n, hipStream_t st);
 hipError_t fill_f32(float* p, float v, long long n, hipStream_t st);
+hipError_t add_i32(int32_t* p, int32_t v, hipStream_t st);  // *p += v (one thread)
 hipError_t delta_keys(const float* a, const float* b, int rows, int d, float* key, hipStream_t st);
 // xc[b*n + j] = h[b*T + idx[b*n + j]] + add; slot_map[b*Tmax + idx] = j when slot_map != nullptr.
 hipError_t gather_rows(const float* h, const int32_t* idx, int B, int n, int T, int d, const u16* add,
@@ -45,6 +46,7 @@ struct KVWrite {
     long long slot_base;
     int32_t* slot_map_k;  // kind 2 decode: slot map of loop k to write (nullptr: already written)
     int keep_codes;       // leave int8/int4 codes and their scales in the store untouched
+    const int32_t* dpos;  // decode: device position t (replaces pos_offset; slot = slot_base + t + row)
 };
 hipError_t rope_kv_write(const float* qkv, int rows, int rows_per_seq, const int32_t* pos,
                          int pos_offset, int H, int Hkv, int hd, const double* inv_freq, u16* q_out,
@@ -56,6 +58,10 @@ enum Epi { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2, EPI_GELU = 3 };
 // out bf16 [M, N].  GELU: out bf16 [M, N].
 hipError_t gemm(const u16* A, const u16* W, int M, int N, int K, int epi, float* c, u16* out_bf,
                 hipStream_t st);
+// M <= 16 only: C = (RMSNorm(X) * gain)[M,K] * W[N,K]^T with X float32 rows; the norm
+// is folded into the GEMM (A operand bf16(X * gain), rows scaled by 1/rms at the end).
+hipError_t gemm_rmsnorm(const float* X, const u16* gain, float eps, const u16* W, int M, int N, int K, int epi,
+                        float* c, u16* out_bf, hipStream_t st);
 
 // ---- attention (k_attn.hip)
 // Dense causal prefill over a bf16 (or int8-base) layer: q bf16 [B*T, H*hd] (row b*T+i),
@@ -80,6 +86,7 @@ struct RowsAttn {
     float* part;           // [B*n_rows][Hkv][n_splits][G][hd + 2]
     u16* out;              // bf16 [B * n_rows, H * hd]
     const int32_t* lens;   // dense: columns per (b, g) (nullptr: pos + 1 for all)
+    const int32_t* dpos;   // decode: device position t (replaces pos)
 };
 // Decode, loops >= 2: write the loop-k reconstruction of each (b, g)'s column list
 // (S intersect [0, pos-window] then [pos-window+1, pos]) as float16 rows into

@@ -145,9 +145,17 @@ int lk_looped_prefill(lk_handle *h, lk_kv_store *s, const int32_t *d_ids, int32_
 
 /* One decode step: d_ids int32 [B] (device, the next token of every sequence),
  * d_out float32 [B, d].  Appends one token per sequence at position t = current
- * length; LK_ERR_CAPACITY once t == max_tokens, LK_ERR_STATE before prefill. */
+ * length; LK_ERR_CAPACITY once t == max_tokens, LK_ERR_STATE before prefill.
+ * The step's launches read t from the store's device counter and the ids/output
+ * through fixed workspace rows, so on a non-null stream the step is captured
+ * once as a HIP graph (per store, workspace, stream and timing class) and
+ * replayed on later calls; the results equal those of the launched kernels. */
 int lk_looped_decode_step(lk_handle *h, lk_kv_store *s, const int32_t *d_ids, float *d_out,
                           void *d_ws, size_t ws_bytes, void *stream);
+
+/* Graph replay of decode steps on (enable != 0, the default) or off (every
+ * step launches its kernels one by one).  Drops any captured step. */
+int lk_set_decode_graphs(lk_handle *h, int32_t enable);
 
 /* Layer applications one prefill/decode pass runs per token: P + R*K + Q. */
 int lk_effective_depth(const lk_handle *h, int32_t *depth);
@@ -160,8 +168,10 @@ const char *lk_last_error(void);
  * "column_mass", "attn_prefill_sparse", "gemm_decode", "gemm_prefill"; NULL
  * disables.  Enabling clears the record.  Not thread-safe per handle. */
 int lk_timing_enable(lk_handle *h, const char *kernel_class);
-/* Launches recorded since lk_timing_enable and their summed event time in ms
- * (waits for the recorded events). */
+/* Launches recorded since lk_timing_enable or the previous read, and their
+ * summed event time in ms (waits for the recorded events; clears the record).
+ * A replayed decode step launches its timed-class kernels directly between two
+ * events and the rest of the step from captured graphs. */
 int lk_timing_read(lk_handle *h, int32_t *launches, double *total_ms);
 
 /* ---------------------------------------------------------------------------

@@ -173,3 +173,42 @@ def test_full_width_shapes_short_prompt(name, batch, prompt, steps):
     r = run_pair(wl.shape, lz, batch, prompt, steps)
     log(f"  oracle {r['t_oracle']:.1f}s")
     check(r, name)
+
+
+@pytest.mark.parametrize("mode,timed", [("lazy", True), ("lazy", False), ("per_loop", True)])
+def test_decode_graph_replay_matches_eager_launches(mode, timed):
+    """Decode steps replayed from a captured HIP graph (non-null stream) equal the
+    same steps launched kernel by kernel (null stream) bit for bit, replay after
+    replay, with unrelated eager work and host synchronisation in between; the
+    timer sees every replayed launch of its class."""
+    s = _small()
+    lz = (I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4)
+          if mode == "lazy" else I.Lazy(mode="per_loop"))
+    T, steps, Bsz = 150, 6, 2
+    W = I.gen_weights(s, seed=9)
+    ids = torch.from_numpy(I.gen_prompt_ids(s, Bsz, T))
+    dec = torch.from_numpy(I.gen_decode_ids(s, Bsz, steps)).cuda()
+    model = B.LoopedModel(s, lz, W)
+    sa, sb = model.store(Bsz, T, T + steps), model.store(Bsz, T, T + steps)
+    pa, pb = model.prefill(sa, ids), model.prefill(sb, ids)
+    assert torch.equal(pa, pb)
+    side = torch.cuda.Stream()
+    B.lk_timing_enable(model.h, "attn_decode_dense" if timed else None)
+    junk = torch.randn(512, 512, device="cuda")
+    for i in range(steps):
+        with torch.cuda.stream(side):
+            og = model.decode(sa, dec[i])
+        side.synchronize()
+        junk = (junk @ junk).clamp_(-1, 1)
+        oe = model.decode(sb, dec[i])
+        torch.cuda.synchronize()
+        assert torch.equal(og, oe), f"step {i}"
+    n, ms = B.lk_timing_read(model.h)
+    B.lk_timing_enable(model.h, None)
+    P, R, K, Q = s.n_prelude, s.n_shared, s.n_loops, s.n_coda
+    per_step = P + Q + (R if mode == "lazy" else R * K)
+    if timed:
+        assert n == 2 * steps * per_step and ms > 0   # replayed steps + eager steps
+    else:
+        assert n == 0
+    assert sa.length() == sb.length() == T + steps
