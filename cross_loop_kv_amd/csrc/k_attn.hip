@@ -909,26 +909,43 @@ __global__ __launch_bounds__(64) void attn_rows_kernel(RowsAttn a) {
 
 // One block per (query row, KV head, query head of the group); thread e merges the
 // split partials of head dim e in split order.
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part, int n_splits,
+// One workgroup per (query row, KV head): the split weights exp2(m_s - M) of every
+// head go to LDS first, then each (head, e) output sums its splits with independent
+// loads.  Splits that saw no key carry m = -inf and weigh 0.
+constexpr int kCombineMaxSplits = 256, kCombineMaxG = 8;
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part, int n_splits,
                                                            int G, int HD, int H, int Hkv,
                                                            u16* __restrict__ out) {
+    __shared__ float wts[kCombineMaxSplits * kCombineMaxG];
+    __shared__ float lsum[kCombineMaxG];
     const long long qrow = blockIdx.x;
-    const int g = blockIdx.y, hh = blockIdx.z;
+    const int g = blockIdx.y;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const long long stride = (long long)G * (HD + 2);
-    const float* base = part + (qrow * Hkv + g) * (long long)n_splits * stride + hh * (HD + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, base[s * stride + HD]);
-    for (int e = threadIdx.x; e < HD; e += blockDim.x) {
-        float L = 0.f, acc = 0.f;
-        for (int s = 0; s < n_splits; ++s) {
-            const float* ps = base + s * stride;
-            const float ms = ps[HD];
-            if (ms == -INFINITY) continue;
-            const float wgt = exp2f(ms - M);
-            L += wgt * ps[HD + 1];
-            acc += wgt * ps[e];
+    const float* base = part + (qrow * Hkv + g) * (long long)n_splits * stride;
+    for (int hh = w; hh < G; hh += 4) {
+        const float* ph = base + hh * (HD + 2);
+        float mx = -INFINITY;
+        for (int s = lane; s < n_splits; s += 64) mx = fmaxf(mx, ph[s * stride + HD]);
+        const float M = wave_max(mx);
+        float l = 0.f;
+        for (int s = lane; s < n_splits; s += 64) {
+            const float ms = ph[s * stride + HD];
+            const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+            wts[s * G + hh] = wgt;
+            l += wgt * ph[s * stride + HD + 1];
         }
-        out[qrow * H * HD + (g * G + hh) * HD + e] = f2bf(acc / L);
+        l = wave_sum(l);
+        if (lane == 0) lsum[hh] = l;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * HD; idx += 256) {
+        const int hh = idx / HD, e = idx % HD;
+        const float* pe = base + hh * (HD + 2) + e;
+        float acc = 0.f;
+#pragma unroll 8
+        for (int s = 0; s < n_splits; ++s) acc += wts[s * G + hh] * pe[s * stride];
+        out[qrow * H * HD + (g * G + hh) * HD + e] = f2bf(acc / lsum[hh]);
     }
 }
 
@@ -1044,8 +1061,9 @@ hipError_t gather_recon(const RowsAttn& a, int ncap, u16* kc, u16* vc, int32_t* 
 
 hipError_t attn_rows_combine(const RowsAttn& a, hipStream_t st) {
     const int G = a.H / a.kv.Hkv;
-    dim3 grid(a.B * a.n_rows, a.kv.Hkv, G);
-    hipLaunchKernelGGL(attn_combine_kernel, grid, dim3(a.kv.hd), 0, st, a.part, a.n_splits, G, a.kv.hd, a.H,
+    if (a.n_splits > kCombineMaxSplits || G > kCombineMaxG) return hipErrorInvalidValue;
+    dim3 grid(a.B * a.n_rows, a.kv.Hkv);
+    hipLaunchKernelGGL(attn_combine_kernel, grid, dim3(256), 0, st, a.part, a.n_splits, G, a.kv.hd, a.H,
                        a.kv.Hkv, a.out);
     return hipGetLastError();
 }

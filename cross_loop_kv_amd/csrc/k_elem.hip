@@ -21,6 +21,26 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(const int32_t* ids, con
     for (int j = threadIdx.x; j < d; j += kThreads) dst[j] = bf2f(tok[src + j]);
 }
 
+// x += add (optional); xg = bf16(x * gain); ps[r] = sum of x^2 over the row.
+__global__ __launch_bounds__(kThreads) void norm_prep_kernel(float* x, const u16* add, const u16* gain, int d,
+                                                             u16* xg, float* ps) {
+    __shared__ float red[16];
+    const int r = blockIdx.x;
+    float* row = x + (long long)r * d;
+    float ss = 0.f;
+    for (int j = threadIdx.x; j < d; j += kThreads) {
+        float v = row[j];
+        if (add) {
+            v = v + bf2f(add[j]);
+            row[j] = v;
+        }
+        xg[(long long)r * d + j] = f2bf(v * bf2f(gain[j]));
+        ss += v * v;
+    }
+    ss = block_sum(ss, red);
+    if (threadIdx.x == 0) ps[r] = ss;
+}
+
 __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(float* x, const u16* add, const u16* gain,
                                                            float eps, int d, u16* out_bf,
                                                            float* out_f32) {
@@ -335,6 +355,13 @@ hipError_t rmsnorm(float* x, const u16* add, const u16* gain, float eps, int row
                    float* out_f32, hipStream_t st) {
     hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(kThreads), 0, st, x, add, gain, eps, d, out_bf,
                        out_f32);
+    return hipGetLastError();
+}
+
+hipError_t norm_prep(float* x, const u16* add, const u16* gain, int rows, int d, u16* xg, float* ps,
+                     hipStream_t st) {
+    if (rows > 8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(norm_prep_kernel, dim3(rows), dim3(kThreads), 0, st, x, add, gain, d, xg, ps);
     return hipGetLastError();
 }
 

@@ -9,10 +9,18 @@
 //   2 x 2 v_mfma_f32_32x32x16_bf16 tiles, LDS double buffering with one barrier
 //   per k-step, rows padded to 80 bytes so the 16-byte operand reads of a wave
 //   spread over the LDS banks.
-// * Skinny kernel (M <= 16, decode): the weights stream straight from HBM into
-//   v_mfma_f32_16x16x32_bf16 B operands.  Each lane reads a contiguous run of its
-//   weight row (the reduction order over k is free, so A and B use the same
-//   permuted k order), 8 waves split K and meet in LDS.
+// * Skinny kernels (decode, weight streaming; HBM bound).  The weights stream
+//   straight from HBM into v_mfma_f32_16x16x32_bf16 B operands; the reduction
+//   order over k is free, so A and B use the same permuted k order.
+//   - Folded kernel (M <= 8): the 16 MFMA rows and columns are (K half, row)
+//     pairs.  A row 8h + m holds activation row m over the h-th half of K, B
+//     column 8h + n holds weight row n over the same half; the two diagonal 8x8
+//     blocks of D summed are the product.  A tile is 8 weight rows, so there are
+//     twice as many workgroups as with 16-row tiles, and the MFMA rows that M <= 8
+//     would leave empty carry the second half of K instead of zeros.
+//   - 16-row kernel (8 < M <= 16): one 16-row weight tile per workgroup.
+//   In both, 8 waves split K and meet in LDS; every load of a wave covers 64
+//   contiguous bytes of each of its rows.
 #include "lk_kernels.h"
 
 namespace lk {
@@ -236,9 +244,138 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(const u16* __restrict_
     }
 }
 
+
+// ---------------------------------------------------------------- folded skinny kernel
+// Requires M <= 8 and K % 64 == 0.  Wave w takes the 32-element k chunks c = w, w + 8,
+// ... of each half, NL chunks per batch of loads.
+//
+// NORM (RMSNorm folded in): A holds bf16(x * gain) and ps_in [nparts][8] partial sums
+// of x^2 per row; the product is scaled by 1 / sqrt(sum / K + eps).
+// PREP (with EPI_ADD): besides x += A W^T (+ add_vec), write what the next NORM
+// product needs: xg_out = bf16(x * next_gain) and, per workgroup, the row sums of x^2
+// over its 8 columns into ps_out [N / 8][8].
+template <int EPI, int NL, bool NORM, bool PREP>
+__global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ A, const u16* __restrict__ W,
+                                                        int M, int N, int K, float* __restrict__ C,
+                                                        u16* __restrict__ Obf, FoldIO io) {
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    constexpr int NWV = 8;
+    __shared__ f32x4 red[NWV][64][DUAL ? 2 : 1];
+    __shared__ float s_inv[8];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int c16 = lane & 15, grp = lane >> 4;
+    const int h = c16 >> 3, r8 = c16 & 7;
+    const int Kh = K >> 1, nch = Kh >> 5;
+    const int n = blockIdx.x * 8 + r8;  // grid = N / 8 (N % 8 == 0)
+    const u16* w0 = W + (long long)n * K + h * Kh + grp * 8;
+    const u16* w1 = W + (long long)(N + n) * K + h * Kh + grp * 8;
+    const bool mvalid = r8 < M;
+    const u16* ar = A + (long long)(mvalid ? r8 : 0) * K + h * Kh + grp * 8;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = w; c0 < nch; c0 += NWV * NL) {
+        uint4 wv[NL], wv1[NL], av[NL];
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int c = c0 + j * NWV;
+            const bool ok = c < nch;
+            wv[j] = ok ? *(const uint4*)(w0 + c * 32) : make_uint4(0, 0, 0, 0);
+            if (DUAL) wv1[j] = ok ? *(const uint4*)(w1 + c * 32) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int c = c0 + j * NWV;
+            av[j] = (c < nch && mvalid) ? *(const uint4*)(ar + c * 32) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[j]), as_bf16x8(wv[j]), acc0, 0, 0, 0);
+            if (DUAL)
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[j]), as_bf16x8(wv1[j]), acc1, 0, 0, 0);
+        }
+    }
+    if (NORM && w < M) {  // wave w: row w's sum of squares, partials in a fixed order
+        float t = 0.f;
+        for (int p = lane; p < io.nparts; p += 64) t += io.ps_in[p * 8 + w];
+        t = wave_sum(t);
+        if (lane == 0) s_inv[w] = 1.0f / sqrtf(t / (float)K + io.eps);
+    }
+    red[w][lane][0] = acc0;
+    if (DUAL) red[w][lane][DUAL ? 1 : 0] = acc1;
+    __syncthreads();
+    if (w != 0) return;
+    f32x4 s0 = red[0][lane][0], s1 = DUAL ? red[0][lane][DUAL ? 1 : 0] : s0;
+#pragma unroll
+    for (int ww = 1; ww < NWV; ++ww) {
+        s0 += red[ww][lane][0];
+        if (DUAL) s1 += red[ww][lane][DUAL ? 1 : 0];
+    }
+    // lane holds D[row 4 grp + i][col c16]; rows 8..15 and columns 8..15 are the second
+    // K half: lane l (grp < 2, c16 < 8) adds lane l + 40 (rows +8, columns +8).
+    f32x4 o0, o1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o0[i] = __shfl(s0[i], (lane + 40) & 63);
+        if (DUAL) o1[i] = __shfl(s1[i], (lane + 40) & 63);
+    }
+    const bool out_lane = grp < 2 && c16 < 8;
+    const int col = blockIdx.x * 8 + (c16 & 7);
+    float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = (grp & 1) * 4 + i;
+        if (!out_lane || m >= M) continue;
+        const long long o = (long long)m * N + col;
+        const float inv = NORM ? s_inv[m] : 1.f;
+        const float v0 = (s0[i] + o0[i]) * inv;
+        if (EPI == EPI_STORE) {
+            C[o] = v0;
+        } else if (EPI == EPI_ADD) {
+            float x = C[o] + v0;
+            if (PREP && io.add_vec) x = x + bf2f(io.add_vec[col]);
+            C[o] = x;
+            if (PREP) {
+                io.xg_out[o] = f2bf(x * bf2f(io.next_gain[col]));
+                sq[i] = x * x;
+            }
+        } else if (EPI == EPI_SWIGLU) {
+            Obf[o] = f2bf(silu_f(v0) * ((s1[i] + o1[i]) * inv));
+        } else {
+            Obf[o] = f2bf(gelu_f(v0));
+        }
+    }
+    if (PREP) {
+        // sum the 8 columns of this workgroup: lanes c16 = 0..7 of the same grp
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int off = 1; off < 8; off <<= 1) sq[i] += __shfl_xor(sq[i], off);
+        if (out_lane && c16 == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) io.ps_out[blockIdx.x * 8 + grp * 4 + i] = sq[i];
+    }
+}
+
+template <int EPI, bool NORM, bool PREP>
+void launch_fold(const u16* A, const u16* W, int M, int N, int K, float* c, u16* out_bf, const FoldIO& io,
+                 hipStream_t st) {
+    // one batch of loads per wave at K = 2048 (4 chunks) and K = 5632 (11 chunks)
+    const int per_wave = (K / 64 + 7) / 8;
+    dim3 grid(N / 8);
+    if (per_wave > 4)
+        hipLaunchKernelGGL((gemm_fold_kernel<EPI, 11, NORM, PREP>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf, io);
+    else
+        hipLaunchKernelGGL((gemm_fold_kernel<EPI, 4, NORM, PREP>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf, io);
+}
+
+bool fold_ok(int M, int N, int K) { return M <= 8 && K % 64 == 0 && N % 8 == 0; }
+
 template <int EPI, bool NORM>
 void launch_skinny(const u16* A, const float* X, const u16* gain, float eps, const u16* W, int M, int N, int K,
                    float* c, u16* out_bf, hipStream_t st) {
+    if (!NORM && fold_ok(M, N, K)) {
+        launch_fold<EPI, false, false>(A, W, M, N, K, c, out_bf, FoldIO{}, st);
+        return;
+    }
     dim3 grid((N + 15) / 16);
     if (K % 128 == 0)
         hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 4, NORM>), grid, dim3(512), 0, st, A, X, gain, eps, W, M, N, K, c, out_bf);
@@ -271,6 +408,38 @@ hipError_t gemm_rmsnorm(const float* X, const u16* gain, float eps, const u16* W
         case EPI_SWIGLU: launch_skinny<EPI_SWIGLU, true>(nullptr, X, gain, eps, W, M, N, K, c, out_bf, st); break;
         default: launch_skinny<EPI_GELU, true>(nullptr, X, gain, eps, W, M, N, K, c, out_bf, st); break;
     }
+    return hipGetLastError();
+}
+
+bool gemm_fold_supported(int M, int N, int K) { return fold_ok(M, N, K); }
+
+hipError_t gemm_fold_norm(const u16* xg, const float* ps, int nparts, float eps, const u16* W, int M, int N, int K,
+                          int epi, float* c, u16* out_bf, hipStream_t st) {
+    if (!fold_ok(M, N, K)) return hipErrorInvalidValue;
+    FoldIO io{};
+    io.ps_in = ps;
+    io.nparts = nparts;
+    io.eps = eps;
+    switch (epi) {
+        case EPI_STORE: launch_fold<EPI_STORE, true, false>(xg, W, M, N, K, c, out_bf, io, st); break;
+        case EPI_SWIGLU: launch_fold<EPI_SWIGLU, true, false>(xg, W, M, N, K, c, out_bf, io, st); break;
+        case EPI_GELU: launch_fold<EPI_GELU, true, false>(xg, W, M, N, K, c, out_bf, io, st); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t gemm_fold_add(const u16* A, const u16* W, int M, int N, int K, float* x, const u16* add_vec,
+                         const u16* next_gain, u16* xg_out, float* ps_out, hipStream_t st) {
+    if (!fold_ok(M, N, K)) return hipErrorInvalidValue;
+    FoldIO io{};
+    io.add_vec = add_vec;
+    io.next_gain = next_gain;
+    io.xg_out = xg_out;
+    io.ps_out = ps_out;
+    if (next_gain) launch_fold<EPI_ADD, false, true>(A, W, M, N, K, x, nullptr, io, st);
+    else if (add_vec) return hipErrorInvalidValue;
+    else launch_fold<EPI_ADD, false, false>(A, W, M, N, K, x, nullptr, io, st);
     return hipGetLastError();
 }
 

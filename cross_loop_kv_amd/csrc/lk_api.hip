@@ -297,6 +297,7 @@ struct WS {
     int32_t *sel, *lens;
     int32_t* ids;      // decode: the step's token ids (fixed address for graph replay)
     float* out;        // decode: the step's output rows
+    float* ps;         // decode: per-workgroup row sums of x^2 for the next RMSNorm ([d/8][8])
     int ncap;          // column capacity of kc / vc per (sequence, KV head)
     size_t total;
     long long part_floats;
@@ -343,6 +344,7 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
     w.vc = (u16*)take(kvc);
     w.lens = (int32_t*)take(hd_->lazy() ? (long long)B * c.n_kv_heads * 4 : 0);
     w.ids = (int32_t*)take((long long)B * 4);
+    w.ps = (float*)take((d / 8 + 1) * 8 * 4);
     w.out = (float*)take((long long)B * d * 4);
     w.total = off;
     return w;
@@ -380,13 +382,21 @@ int check_cfg(const lk_model_cfg* c, const lk_lazy_cfg* z) {
 
 // One Transformer layer ---------------------------------------------------------
 struct LayerIO {
-    float* x;                // rows [M, d], updated in place
+    float* x;                // residual stream [M, d]
     int M;                   // rows
-    int rows_per_seq;        // rows of each sequence in x
+    int rows_per_seq;        // rows per sequence (1 for decode)
     const int32_t* pos;      // positions (nullptr: pos_offset + row index within the sequence)
     int pos_offset;
     const u16* add;          // loop embedding added before the layer (nullptr: none)
     const int32_t* dpos;     // decode: device position t (replaces pos_offset)
+    // Decode with folded norms (fold == true): x already holds `add`, and xn / ps hold
+    // bf16(x * attn gain) and nparts row sums of x^2 from the producer of x.  The
+    // layer's down projection leaves the same for the next layer (next_gain, after
+    // adding next_add), or nothing when next_gain is null.
+    bool fold;
+    int nparts;
+    const u16* next_gain;
+    const u16* next_add;
 };
 
 enum AttnKind { ATTN_PREFILL_DENSE, ATTN_ROWS_DENSE, ATTN_ROWS_SPARSE };
@@ -446,7 +456,12 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
     const int d = c.d_model, H = c.n_heads, hd = c.head_dim, Hhd = H * hd;
     // decode-sized row counts fold the RMSNorm into the skinny GEMMs
     const bool fused_norm = io.M <= 16;
-    if (fused_norm) {
+    if (io.fold) {
+        LK_TRY(timed(h, gcls, st, [=] {
+            return lk::gemm_fold_norm(w.xn, w.ps, io.nparts, c.rms_eps, (const u16*)W.wqkv, io.M, h->qkv_w(), d,
+                                      lk::EPI_STORE, w.qkv, nullptr, st);
+        }));
+    } else if (fused_norm) {
         if (io.add) LK_HIP(lk::add_rows(io.x, io.add, io.M, d, st));
         LK_TRY(timed(h, gcls, st, [=] {
             return lk::gemm_rmsnorm(io.x, (const u16*)W.attn_norm, c.rms_eps, (const u16*)W.wqkv, io.M, h->qkv_w(),
@@ -546,9 +561,24 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
             LK_HIP(lk::attn_rows_combine(a, st));
         }
     }
+    const int act = c.ffn_act == LK_ACT_SWIGLU ? lk::EPI_SWIGLU : lk::EPI_GELU;
+    if (io.fold) {
+        LK_TRY(timed(h, gcls, st, [=] {
+            return lk::gemm_fold_add(w.att, (const u16*)W.wo, io.M, d, Hhd, io.x, nullptr, (const u16*)W.ffn_norm,
+                                     w.xn, w.ps, st);
+        }));
+        LK_TRY(timed(h, gcls, st, [=] {
+            return lk::gemm_fold_norm(w.xn, w.ps, d / 8, c.rms_eps, (const u16*)W.w_in, io.M, c.ffn_dim, d, act,
+                                      nullptr, w.act, st);
+        }));
+        LK_TRY(timed(h, gcls, st, [=] {
+            return lk::gemm_fold_add(w.act, (const u16*)W.w_down, io.M, d, c.ffn_dim, io.x, io.next_add,
+                                     io.next_gain, w.xn, w.ps, st);
+        }));
+        return LK_OK;
+    }
     LK_TRY(timed(h, gcls, st,
                  [=] { return lk::gemm(w.att, (const u16*)W.wo, io.M, d, Hhd, lk::EPI_ADD, io.x, nullptr, st); }));
-    const int act = c.ffn_act == LK_ACT_SWIGLU ? lk::EPI_SWIGLU : lk::EPI_GELU;
     if (fused_norm) {
         LK_TRY(timed(h, gcls, st, [=] {
             return lk::gemm_rmsnorm(io.x, (const u16*)W.ffn_norm, c.rms_eps, (const u16*)W.w_in, io.M, c.ffn_dim, d,
@@ -831,23 +861,30 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
     const int P = c.n_prelude, R = c.n_shared, K = c.n_loops, Q = c.n_coda, d = c.d_model;
     const int B = s->B;
     const int32_t* dpos = dev_pos(s);
-    LK_HIP(lk::embed(w.ids, h->tok, w.h, B, d, c.vocab, st));
-    LayerIO io{w.h, B, 1, nullptr, 0, nullptr, dpos};
+    // The layer applications of one step, in order.
+    struct App {
+        int li;
+        const u16* add;
+        lk::KVWrite kw;
+        AttnPlan ap;
+    };
+    std::vector<App> apps;
+    apps.reserve((size_t)P + (size_t)R * K + Q);
     AttnPlan dense{};
     dense.kind = ATTN_ROWS_DENSE;
     dense.k_loop = 1;
-    dense.pos = s->Tmax - 1;
+    dense.pos = s->Tmax - 1;  // splits are sized for the store's capacity
     dense.dpos = dpos;
     for (int li = 0; li < P; ++li) {
         dense.read = dense_layer(s, li);
-        LK_TRY(run_layer(h, li, io, plain_write(dense.read), dense, w, st));
+        apps.push_back({li, nullptr, plain_write(dense.read), dense});
     }
     for (int k = 1; k <= K; ++k) {
         for (int r = 0; r < R; ++r) {
-            io.add = (r == 0) ? h->lemb + (long long)(k - 1) * d : nullptr;
+            const u16* add = (r == 0) ? h->lemb + (long long)(k - 1) * d : nullptr;
             if (!h->lazy()) {
                 dense.read = loop_layer(s, k, r);
-                LK_TRY(run_layer(h, P + r, io, plain_write(dense.read), dense, w, st));
+                apps.push_back({P + r, add, plain_write(dense.read), dense});
                 continue;
             }
             AttnPlan ap{};
@@ -872,13 +909,30 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
                 kw.slot_base = (long long)s->lay.n_sel - s->Tp;  // slot = n_sel + (t - T)
                 kw.slot_map_k = slot_map(s, k);
             }
-            LK_TRY(run_layer(h, P + r, io, kw, ap, w, st));
+            apps.push_back({P + r, add, kw, ap});
         }
     }
-    io.add = nullptr;
     for (int j = 0; j < Q; ++j) {
         dense.read = dense_layer(s, P + j);
-        LK_TRY(run_layer(h, P + R + j, io, plain_write(dense.read), dense, w, st));
+        apps.push_back({P + R + j, nullptr, plain_write(dense.read), dense});
+    }
+    // Folded norms: every projection input is prepared by the kernel that produced x.
+    const int qkv = h->qkv_w(), Hhd = c.n_heads * c.head_dim;
+    const bool fold = lk::gemm_fold_supported(B, qkv, d) && lk::gemm_fold_supported(B, d, Hhd) &&
+                      lk::gemm_fold_supported(B, c.ffn_dim, d) && lk::gemm_fold_supported(B, d, c.ffn_dim);
+    LK_HIP(lk::embed(w.ids, h->tok, w.h, B, d, c.vocab, st));
+    if (fold)
+        LK_HIP(lk::norm_prep(w.h, apps[0].add, (const u16*)h->L[apps[0].li].attn_norm, B, d, w.xn, w.ps, st));
+    for (size_t i = 0; i < apps.size(); ++i) {
+        const App& a = apps[i];
+        LayerIO io{w.h, B, 1, nullptr, 0, fold ? nullptr : a.add, dpos};
+        io.fold = fold;
+        io.nparts = i == 0 ? 1 : d / 8;
+        if (i + 1 < apps.size()) {
+            io.next_gain = (const u16*)h->L[apps[i + 1].li].attn_norm;
+            io.next_add = apps[i + 1].add;
+        }
+        LK_TRY(run_layer(h, a.li, io, a.kw, a.ap, w, st));
     }
     LK_HIP(lk::rmsnorm(w.h, nullptr, h->fnorm, c.rms_eps, B, d, nullptr, w.out, st));
     LK_HIP(lk::add_i32(dev_pos(s), 1, st));

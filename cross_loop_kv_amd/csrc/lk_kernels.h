@@ -63,6 +63,29 @@ hipError_t gemm(const u16* A, const u16* W, int M, int N, int K, int epi, float*
 hipError_t gemm_rmsnorm(const float* X, const u16* gain, float eps, const u16* W, int M, int N, int K, int epi,
                         float* c, u16* out_bf, hipStream_t st);
 
+// Decode-sized products (M <= 8 rows, K % 64 == 0, N % 8 == 0) with the RMSNorm
+// carried between kernels: a producer adds its product into the residual stream x
+// and leaves xg = bf16(x * next_gain) plus per-workgroup row sums of x^2 (ps, [nparts][8]);
+// the consumer multiplies xg by W and scales by 1 / sqrt(sum(ps) / K + eps).
+struct FoldIO {
+    const float* ps_in;    // NORM: partial sums of x^2 [nparts][8]
+    int nparts;
+    float eps;
+    const u16* add_vec;    // PREP: bf16 [N] added to x after the product (nullptr: none)
+    const u16* next_gain;  // PREP: bf16 [N] gain of the next RMSNorm
+    u16* xg_out;           // PREP: bf16 [M, N]
+    float* ps_out;         // PREP: [N / 8][8]
+};
+bool gemm_fold_supported(int M, int N, int K);
+hipError_t gemm_fold_norm(const u16* xg, const float* ps, int nparts, float eps, const u16* W, int M, int N, int K,
+                          int epi, float* c, u16* out_bf, hipStream_t st);
+// x[M, N] += A W^T (+ add_vec); with next_gain also writes xg_out and ps_out (N / 8 parts).
+hipError_t gemm_fold_add(const u16* A, const u16* W, int M, int N, int K, float* x, const u16* add_vec,
+                         const u16* next_gain, u16* xg_out, float* ps_out, hipStream_t st);
+// x += add (optional); xg = bf16(x * gain); ps[0][r] = sum of x^2 of row r (one part).
+hipError_t norm_prep(float* x, const u16* add, const u16* gain, int rows, int d, u16* xg, float* ps,
+                     hipStream_t st);
+
 // ---- attention (k_attn.hip)
 // Dense causal prefill over a bf16 (or int8-base) layer: q bf16 [B*T, H*hd] (row b*T+i),
 // out bf16 [B*T, H*hd], lse float32 [B, H, T] (log2 units of the scaled scores).
