@@ -198,8 +198,10 @@ def main():
     achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9 if launches else 0.0
 
     shared, total = store.bytes_used()
+    cache = store.cache_bytes()
     t_now = store.length()
     kv_tok_shared = shared / (Bsz * t_now)
+    kv_tok_resident = (shared + cache) / (Bsz * t_now)
     E = 2 * s.n_kv_heads * s.head_dim
     dense_per_loop = 2 * s.n_shared * s.n_loops * E
     if args.calibrate_copy:
@@ -221,9 +223,12 @@ def main():
                    "kv_heads": s.n_kv_heads, "ffn": s.ffn_dim, "mode": lz.mode, "rho": lz.rho,
                    "top_s": lz.top_s, "window": lz.window, "base_bits": lz.base_bits,
                    "res_bits": lz.res_bits, "layer_applications": model.effective_depth()},
-        "kv_bytes_per_token": round(kv_tok_shared, 1),
+        "kv_bytes_per_token": round(kv_tok_resident, 1),
         "kv_bytes_per_token_dense_per_loop": dense_per_loop,
-        "kv_reduction_vs_dense_per_loop": round(dense_per_loop / kv_tok_shared, 3),
+        "kv_reduction_vs_dense_per_loop": round(dense_per_loop / kv_tok_resident, 3),
+        "kv_bytes_per_token_store_only": round(kv_tok_shared, 1),
+        "kv_reduction_store_only": round(dense_per_loop / kv_tok_shared, 3),
+        "decode_cache_bytes": cache,
         "kv_bytes_total_per_token": round(total / (Bsz * t_now), 1),
         "prefill_s": round(prefill_s, 3),
         "prefill_tokens_per_s": round(Bsz * T / prefill_s, 1),

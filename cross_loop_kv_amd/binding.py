@@ -69,6 +69,7 @@ _SIGS = {
                                     C.POINTER(C.c_size_t)]),
     "lk_kv_store_release": (None, [C.c_void_p]),
     "lk_kv_store_bytes_used": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
+    "lk_kv_store_cache_bytes": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t)]),
     "lk_kv_store_length": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32)]),
     "lk_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.POINTER(C.c_size_t)]),
     "lk_looped_prefill": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
@@ -153,6 +154,12 @@ def lk_kv_store_bytes_used(s: int) -> Tuple[int, int]:
     a, b = C.c_size_t(), C.c_size_t()
     _check(lib().lk_kv_store_bytes_used(s, C.byref(a), C.byref(b)))
     return a.value, b.value
+
+
+def lk_kv_store_cache_bytes(s: int) -> int:
+    n = C.c_size_t()
+    _check(lib().lk_kv_store_cache_bytes(s, C.byref(n)))
+    return n.value
 
 
 def lk_kv_store_length(s: int) -> int:
@@ -262,6 +269,9 @@ class Store:
 
     def length(self) -> int:
         return lk_kv_store_length(self.s)
+
+    def cache_bytes(self) -> int:
+        return lk_kv_store_cache_bytes(self.s)
 
     def force_selection(self, tokens=None, columns=None):
         """tokens: int32 cuda [K-1, B, n]; columns: int32 cuda [R, B, Hkv, n_cols] (or None)."""

@@ -349,22 +349,47 @@ __global__ __launch_bounds__(256) void column_mass_kernel(const u16* __restrict_
 
 // ---------------------------------------------------------------- dense decode (MFMA)
 // Row types of the dense decode kernel.
-enum { RT_BF16 = 0, RT_I8 = 1, RT_F16 = 2 };
+enum { RT_BF16 = 0, RT_I8 = 1, RT_F16 = 2, RT_F16_2SEG = 3 };
 
 template <int HD, int G, int RT>
 __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
     constexpr bool I8 = RT == RT_I8;
     constexpr bool HALF = RT != RT_BF16;  // f16 MFMA (int8 codes are converted to f16)
+    constexpr bool SEG = RT == RT_F16_2SEG;
     constexpr int NQ = HD / 32;   // 32-wide k-steps over hd (= scale groups)
     constexpr int NE = HD / 16;   // 16-row tiles of O^T
     const int split = blockIdx.x, bg = blockIdx.y;
-    const KVLayer& kv = a.kv;
+    const bool seg2 = SEG && split >= a.seg_split;
+    const KVLayer& kv = seg2 ? a.kv2 : a.kv;
     const int Hkv = kv.Hkv, b = bg / Hkv, g = bg % Hkv;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int c16 = lane & 15, kgrp = lane >> 4;
-    const int ncols = a.lens ? a.lens[bg] : (a.dpos ? *a.dpos : a.pos) + 1;
-    const int c_begin = split * a.chunk;
-    const int c_end = min(ncols, c_begin + a.chunk);
+    // keys [c_lo, c_end) of rows [c_begin, c_begin + chunk) take part
+    int c_begin, c_lo, c_end, ring0 = 0;
+    if (!SEG) {
+        const int ncols = a.lens ? a.lens[bg] : (a.dpos ? *a.dpos : a.pos) + 1;
+        c_begin = c_lo = split * a.chunk;
+        c_end = min(ncols, c_begin + a.chunk);
+    } else if (!seg2) {  // S rows: the ascending columns up to pos - window form a prefix
+        const int pos = a.dpos ? *a.dpos : a.pos;
+        __shared__ int s_cnt[4];
+        c_begin = c_lo = split * a.chunk;
+        const int i = c_begin + threadIdx.x;
+        const bool in = threadIdx.x < a.chunk && i < a.n_cols && a.cols[(long long)bg * a.n_cols + i] <= pos - a.window;
+        const unsigned long long bal = __ballot(in);
+        if (lane == 0) s_cnt[w] = __popcll(bal);
+        __syncthreads();
+        c_end = c_begin + s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+    } else {  // window keys start at the 8-aligned position below the window
+        const int pos = a.dpos ? *a.dpos : a.pos;
+        const int wlo = max(0, pos - a.window + 1);
+        ring0 = wlo & ~7;
+        c_begin = (split - a.seg_split) * a.chunk;
+        c_lo = max(c_begin, wlo - ring0);
+        c_end = min(c_begin + a.chunk, pos - ring0 + 1);
+    }
+    // row of key `key` in kv (window ring: position ring0 + key at row % Tmax)
+    auto row_of = [&](int key) { return seg2 ? (ring0 + key) % kv.Tmax : key; };
     const float sl2 = kLog2e / sqrtf((float)HD);
 
     // Q^T operand: lane (head c16, kgrp) holds q[h][32j + 8kgrp .. +8]
@@ -395,8 +420,8 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
         f32x4 sacc[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            const int key = min(kb + 8 * (c16 >> 2) + 4 * nt + (c16 & 3), ncols - 1);
-            const long long row = kv_row(kv, b, g, key);
+            const int key = min(kb + 8 * (c16 >> 2) + 4 * nt + (c16 & 3), c_end - 1);
+            const long long row = kv_row(kv, b, g, row_of(key));
             sacc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
             if (I8) {
                 const u16* ks = kv.base_scale[0] + row * NQ;
@@ -427,7 +452,7 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = kb + 8 * kgrp + 4 * nt + i;
-                const float v = key < c_end ? sacc[nt][i] * sl2 : -INFINITY;
+                const float v = (key >= c_lo && key < c_end) ? sacc[nt][i] * sl2 : -INFINITY;
                 s[nt * 4 + i] = v;
                 mx = fmaxf(mx, v);
             }
@@ -463,7 +488,7 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
         }
         const int valid = c_end - (kb + 8 * kgrp);
         // rows past the end of the context are unwritten: clamp the block address, zero the values
-        const int pos0 = min(kb + 8 * kgrp, ((ncols - 1) >> 3) << 3);
+        const int pos0 = row_of(min(kb + 8 * kgrp, ((c_end - 1) >> 3) << 3));
 #pragma unroll
         for (int et = 0; et < NE; ++et) {
             const int e = 16 * et + c16;
@@ -560,8 +585,8 @@ __device__ __forceinline__ void res8_apply(const KVLayer& v, int kv, int kk, lon
 // starting at a multiple of 8 (window, runs of S) the 8 keys of a head dim are one
 // vector load from the 8-key-interleaved store.
 template <int HD>
-__global__ __launch_bounds__(256) void gather_recon_kernel(RowsAttn a, int ncap, u16* __restrict__ kc,
-                                                           u16* __restrict__ vc, int32_t* __restrict__ lens) {
+__global__ __launch_bounds__(256) void gather_recon_kernel(RowsAttn a, int mode, int ncap, u16* __restrict__ kc,
+                                                           u16* __restrict__ vc) {
     constexpr int NCOL = 64;
     constexpr int TPC = 256 / NCOL;        // threads per entry for K
     constexpr int EPT = HD / TPC;          // K elements per thread (multiple of 8)
@@ -572,19 +597,20 @@ __global__ __launch_bounds__(256) void gather_recon_kernel(RowsAttn a, int ncap,
     const KVLayer& v = a.kv;
     const int t = threadIdx.x;
     const int bg = blockIdx.y, Hkv = v.Hkv, b = bg / Hkv, g = bg % Hkv;
-    const int pos = a.dpos ? *a.dpos : a.pos;
-    const int32_t* S = a.cols + (long long)bg * a.n_cols;
-    const int lim = pos - a.window;
-    int lo = 0, hi = a.n_cols;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (S[mid] <= lim) lo = mid + 1;
-        else hi = mid;
+    const int32_t* S = a.cols ? a.cols + (long long)bg * a.n_cols : nullptr;
+    const bool ring = mode == GATHER_RING;
+    int cntS, ncols, win_lo;
+    if (!ring) {
+        cntS = ncols = a.n_cols;
+        win_lo = 0;
+    } else {
+        const int T = (a.dpos ? *a.dpos : a.pos) + 1;
+        cntS = 0;
+        win_lo = (max(0, T - ncap) + 7) & ~7;
+        ncols = T - win_lo;
     }
-    const int cntS = lo;
-    const int win_lo = max(0, pos - a.window + 1);
-    const int ncols = cntS + (pos - win_lo + 1);
-    if (blockIdx.x == 0 && t == 0) lens[bg] = ncols;
+    // destination row of entry c (ring rows keep 8-aligned groups contiguous)
+    auto dst_row = [&](int c) { return ring ? (win_lo + c) % ncap : c; };
     const int c0 = blockIdx.x * NCOL;
     const int nres = v.lazy ? a.k_loop - 1 : 0;
     if (t < NCOL) {
@@ -631,9 +657,10 @@ __global__ __launch_bounds__(256) void gather_recon_kernel(RowsAttn a, int ncap,
                 for (int j8 = 0; j8 < EPT / 8; ++j8) res8_apply<HD>(v, 0, kk, rr, e0 + 8 * j8, x + 8 * j8);
             }
         }
-        u16* dst = kc + ((long long)bg * ncap + c0 + i) * HD + e0;
+        u16* dst = kc + ((long long)bg * ncap + dst_row(c0 + i)) * HD + e0;
 #pragma unroll
         for (int j8 = 0; j8 < EPT / 8; ++j8) {
+            if (ring && c0 + i >= ncols) break;
             uint32_t o[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -693,9 +720,10 @@ __global__ __launch_bounds__(256) void gather_recon_kernel(RowsAttn a, int ncap,
                 for (int q = 0; q < EPV; ++q) vx[j][q] = kv_apply_res(v, 1, b, g, kk, sl, e0 + q, vx[j][q]);
             }
         }
-        const long long blk = (long long)bg * (ncap / 8) + (c0 + cb) / 8;
+        const long long blk = (long long)bg * (ncap / 8) + dst_row(c0 + cb) / 8;
 #pragma unroll
         for (int q = 0; q < EPV; ++q) {
+            if (ring && c0 + cb >= ncols) break;
             uint32_t o[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -976,7 +1004,9 @@ hipError_t mass_hd(const u16* q, const KVLayer& kv, const float* lse, int B, int
 template <int HD, int G>
 void dense_launch(const RowsAttn& a, hipStream_t st) {
     dim3 grid(a.n_splits, a.B * a.kv.Hkv);
-    if (a.kv.lazy && a.kv.base_bits == 8)
+    if (a.seg_split > 0)
+        hipLaunchKernelGGL((attn_decode_dense_kernel<HD, G, RT_F16_2SEG>), grid, dim3(256), 0, st, a);
+    else if (a.kv.lazy && a.kv.base_bits == 8)
         hipLaunchKernelGGL((attn_decode_dense_kernel<HD, G, RT_I8>), grid, dim3(256), 0, st, a);
     else if (!a.kv.lazy && a.kv.f16)
         hipLaunchKernelGGL((attn_decode_dense_kernel<HD, G, RT_F16>), grid, dim3(256), 0, st, a);
@@ -1032,7 +1062,7 @@ hipError_t column_mass(const u16* q, const KVLayer& kv, const float* lse, int B,
 
 hipError_t attn_rows_main(const RowsAttn& a, hipStream_t st) {
     const int G = a.H / a.kv.Hkv;
-    if (a.cols) {
+    if (a.cols && a.seg_split == 0) {
         switch (a.kv.hd) {
             case 32: rows_hd<32>(a, G, st); break;
             case 64: rows_hd<64>(a, G, st); break;
@@ -1048,13 +1078,13 @@ hipError_t attn_rows_main(const RowsAttn& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t gather_recon(const RowsAttn& a, int ncap, u16* kc, u16* vc, int32_t* lens, hipStream_t st) {
-    const int hd = a.kv.hd;
+hipError_t gather_recon(const RowsAttn& a, int mode, int ncap, u16* kc, u16* vc, hipStream_t st) {
+    if (ncap % 64 || (mode != GATHER_ALL_S && mode != GATHER_RING)) return hipErrorInvalidValue;
     dim3 grid(ncap / 64, a.B * a.kv.Hkv);
-    switch (hd) {
-        case 32: hipLaunchKernelGGL(gather_recon_kernel<32>, grid, dim3(256), 0, st, a, ncap, kc, vc, lens); break;
-        case 64: hipLaunchKernelGGL(gather_recon_kernel<64>, grid, dim3(256), 0, st, a, ncap, kc, vc, lens); break;
-        default: hipLaunchKernelGGL(gather_recon_kernel<128>, grid, dim3(256), 0, st, a, ncap, kc, vc, lens); break;
+    switch (a.kv.hd) {
+        case 32: hipLaunchKernelGGL(gather_recon_kernel<32>, grid, dim3(256), 0, st, a, mode, ncap, kc, vc); break;
+        case 64: hipLaunchKernelGGL(gather_recon_kernel<64>, grid, dim3(256), 0, st, a, mode, ncap, kc, vc); break;
+        default: hipLaunchKernelGGL(gather_recon_kernel<128>, grid, dim3(256), 0, st, a, mode, ncap, kc, vc); break;
     }
     return hipGetLastError();
 }

@@ -318,21 +318,35 @@ __global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, in
         }
     } else {
         const long long rr = res_row(L, b, g, slot);
+        float recon;  // the row's loop-k reconstruction
         if (L.res_bits == 16) {
-            ((u16*)L.res[w.loop - 2][kv])[rr * hd + e] = f2bf(x);
-        } else if (!w.keep_codes) {
+            const u16 xb = f2bf(x);
+            ((u16*)L.res[w.loop - 2][kv])[rr * hd + e] = xb;
+            recon = bf2f(xb);
+        } else {
             const float prev = kv_recon_elem(L, kv, b, g, pos, e, w.loop - 1);
-            u16 sb;
-            const int qmax = (1 << (L.res_bits - 1)) - 1;
-            const int c = quant_group32(x - prev, qmax, &sb);
-            if ((t & 31) == 0) ((u16*)L.res_scale[w.loop - 2][kv])[rr * (hd / 32) + e / 32] = sb;
-            if (L.res_bits == 8) {
-                ((int8_t*)L.res[w.loop - 2][kv])[rr * hd + e] = (int8_t)c;
-            } else {
-                const int other = __shfl_xor(c, 1);
-                if ((t & 1) == 0)
-                    ((uint8_t*)L.res[w.loop - 2][kv])[rr * (hd / 2) + e / 2] = (uint8_t)((c & 0xF) | ((other & 0xF) << 4));
+            if (!w.keep_codes) {
+                u16 sb;
+                const int qmax = (1 << (L.res_bits - 1)) - 1;
+                const int c = quant_group32(x - prev, qmax, &sb);
+                if ((t & 31) == 0) ((u16*)L.res_scale[w.loop - 2][kv])[rr * (hd / 32) + e / 32] = sb;
+                if (L.res_bits == 8) {
+                    ((int8_t*)L.res[w.loop - 2][kv])[rr * hd + e] = (int8_t)c;
+                } else {
+                    const int other = __shfl_xor(c, 1);
+                    if ((t & 1) == 0)
+                        ((uint8_t*)L.res[w.loop - 2][kv])[rr * (hd / 2) + e / 2] = (uint8_t)((c & 0xF) | ((other & 0xF) << 4));
+                }
+                recon = prev + (float)c * h2f(sb);
+            } else {  // codes already in the store
+                recon = kv_apply_res(L, kv, b, g, w.loop, (int)slot, e, prev);
             }
+        }
+        if (w.ring_on) {
+            const KVLayer& Rg = w.ring;
+            const int rp = pos % Rg.Tmax;
+            const long long ri = kv == 0 ? kv_row(Rg, b, g, rp) * hd + e : v_elem(Rg, b, g, rp, e);
+            ((u16*)Rg.base[kv])[ri] = f2h_bits(recon);
         }
         if (w.slot_map_k && u == nq && t == 0) w.slot_map_k[(long long)b * L.Tmax + pos] = (int32_t)slot;
     }

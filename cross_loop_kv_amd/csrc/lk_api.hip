@@ -123,9 +123,12 @@ struct lk_handle {
 };
 
 struct StoreLayout {
-    size_t dense, loop_rows, base, base_sc, res, res_sc, slot, cols, state, total;
+    size_t dense, loop_rows, base, base_sc, res, res_sc, slot, cols, state, scache, total;
     long long slots;
     int n_sel, n_cols;
+    int ncs;                 // rows per (b, g) of the stable-column cache (n_cols rounded up to 128)
+    int wr;                  // rows per (b, g) of the window ring (window + 16 rounded up to 128)
+    size_t scache_bytes;     // stable-column cache and window rings together
     long long res_row_b;
 };
 
@@ -184,6 +187,21 @@ StoreLayout store_layout(const lk_handle* h, int B, int Tp, int Tmax) {
         s.cols = take((size_t)c.n_shared * B * Hkv * s.n_cols * 4);
     }
     s.state = take(64);  // int32 decode position t (device copy of the store length)
+    // Decode cache: for every loop k >= 2 and shared layer r, the float16 loop-k
+    // reconstruction of the stable columns S (fixed once prefill has run), K rows
+    // [B][Hkv][ncs][hd] then 8-key-interleaved V [B][Hkv][ncs/8][hd][8].
+    // Then the window rings: per loop k >= 2 and shared layer r, the float16 loop-k
+    // reconstruction of the last wr positions (position p at row p % wr), K then V as
+    // above; prefill fills them, every decode step writes its own row.
+    s.ncs = s.wr = 0;
+    s.scache_bytes = 0;
+    s.scache = off;
+    if (h->z.mode == LK_MODE_LAZY && c.n_loops >= 2) {
+        s.ncs = (s.n_cols + 127) / 128 * 128;
+        s.wr = (h->z.window + 16 + 127) / 128 * 128;
+        s.scache_bytes = (size_t)(c.n_loops - 1) * c.n_shared * 2 * B * Hkv * ((size_t)s.ncs + s.wr) * hd * 2;
+        s.scache = take(s.scache_bytes);
+    }
     s.total = off;
     return s;
 }
@@ -285,6 +303,30 @@ int32_t* slot_map(const lk_kv_store* s, int k) {
 }
 int32_t* dev_pos(const lk_kv_store* s) { return (int32_t*)(s->buf + s->lay.state); }
 
+// Stable-column cache (ring == false) or window ring (ring == true) of loop k >= 2,
+// shared layer r, as float16 plain rows.
+KVLayer scache_layer(const lk_kv_store* s, int k, int r, bool ring = false) {
+    const lk_model_cfg& c = s->h->c;
+    const int rows = ring ? s->lay.wr : s->lay.ncs;
+    const size_t one = (size_t)s->B * c.n_kv_heads * rows * c.head_dim * 2;  // K or V of one (k, r)
+    size_t off = s->lay.scache + ((size_t)(k - 2) * c.n_shared + r) * 2 * one;
+    if (ring) off += (size_t)(c.n_loops - 1) * c.n_shared * 2 * s->B * c.n_kv_heads * s->lay.ncs * c.head_dim * 2;
+    char* base = s->buf + off;
+    KVLayer L{};
+    L.lazy = 0;
+    L.f16 = 1;
+    L.B = s->B;
+    L.Hkv = c.n_kv_heads;
+    L.hd = c.head_dim;
+    L.Tmax = rows;
+    L.base_bits = 16;
+    L.res_bits = 16;
+    L.n_loops = c.n_loops;
+    L.base[0] = base;
+    L.base[1] = base + one;
+    return L;
+}
+
 int32_t* col_sets(const lk_kv_store* s, int r) {
     return (int32_t*)(s->buf + s->lay.cols) + (long long)r * s->B * s->h->c.n_kv_heads * s->lay.n_cols;
 }
@@ -293,12 +335,10 @@ int32_t* col_sets(const lk_kv_store* s, int r) {
 struct WS {
     float *h, *h0, *xc, *qkv, *lse, *mass, *keys, *part;
     u16 *xn, *q, *att, *act;
-    u16 *kc, *vc;      // decode, loops >= 2: materialized reconstruction of the column lists
-    int32_t *sel, *lens;
+    int32_t* sel;
     int32_t* ids;      // decode: the step's token ids (fixed address for graph replay)
     float* out;        // decode: the step's output rows
     float* ps;         // decode: per-workgroup row sums of x^2 for the next RMSNorm ([d/8][8])
-    int ncap;          // column capacity of kc / vc per (sequence, KV head)
     size_t total;
     long long part_floats;
 };
@@ -338,11 +378,6 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
     }
     w.part_floats = pf;
     w.part = (float*)take(pf * 4);
-    w.ncap = hd_->lazy() ? (hd_->z.top_s + hd_->z.window + 63) / 64 * 64 : 0;
-    const long long kvc = (long long)B * c.n_kv_heads * w.ncap * c.head_dim * 2;
-    w.kc = (u16*)take(kvc);
-    w.vc = (u16*)take(kvc);
-    w.lens = (int32_t*)take(hd_->lazy() ? (long long)B * c.n_kv_heads * 4 : 0);
     w.ids = (int32_t*)take((long long)B * 4);
     w.ps = (float*)take((d / 8 + 1) * 8 * 4);
     w.out = (float*)take((long long)B * d * 4);
@@ -411,6 +446,8 @@ struct AttnPlan {
     int pos;                 // decode: capacity - 1 (splits are sized for the full store)
     const int32_t* dpos;     // decode: device position t
     float* mass;             // lazy loop 1: column mass output
+    KVLayer scache;          // decode, loops >= 2: float16 reconstruction of the stable columns
+    KVLayer ring;            // decode, loops >= 2: float16 window ring
 };
 
 // End the capture running on `st` and append what it recorded (if anything) as a
@@ -518,34 +555,20 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
         a.part = w.part;
         a.out = w.att;
         if (ap.kind == ATTN_ROWS_SPARSE && io.rows_per_seq == 1) {
-            // decode, loops >= 2: materialize the loop-k reconstruction of every column
-            // list as float16 rows, then run the dense MFMA kernel over them
-            const int ncap = (ap.n_cols + ap.window + 63) / 64 * 64;
-            if (ncap > w.ncap) return fail(LK_ERR_CAPACITY, "workspace too small for the column lists");
+            // decode, loops >= 2: the stable columns come from the float16 cache filled at
+            // the end of prefill, the window from the float16 ring that prefill filled and
+            // each decode step extends (rope_kv_write).  One launch runs over both
+            // segments and the combine merges their splits.
+            constexpr int kSegChunk = 128;
             lk::RowsAttn d = a;
-            d.cols = nullptr;
-            d.lens = w.lens;
-            d.pos = ncap - 1;
-            d.kv = KVLayer{};
-            d.kv.lazy = 0;
-            d.kv.f16 = 1;
-            d.kv.B = a.B;
-            d.kv.Hkv = c.n_kv_heads;
-            d.kv.hd = hd;
-            d.kv.Tmax = ncap;
-            d.kv.base_bits = 16;
-            d.kv.res_bits = 16;
-            d.kv.n_loops = c.n_loops;
-            d.kv.base[0] = w.kc;
-            d.kv.base[1] = w.vc;
-            d.chunk = dense_chunk(ncap);
-            d.n_splits = (ncap + d.chunk - 1) / d.chunk;
+            d.kv = ap.scache;
+            d.kv2 = ap.ring;
+            d.chunk = kSegChunk;
+            d.seg_split = ap.scache.Tmax / kSegChunk;
+            d.n_splits = d.seg_split + ap.ring.Tmax / kSegChunk;
             if ((long long)a.B * H * d.n_splits * (hd + 2) > w.part_floats)
                 return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
-            LK_TRY(timed(h, TC_ATTN_DECODE_SPARSE, st, [=] {
-                hipError_t e = lk::gather_recon(a, ncap, w.kc, w.vc, w.lens, st);
-                return e != hipSuccess ? e : lk::attn_rows_main(d, st);
-            }));
+            LK_TRY(timed(h, TC_ATTN_DECODE_SPARSE, st, [=] { return lk::attn_rows_main(d, st); }));
             LK_HIP(lk::attn_rows_combine(d, st));
         } else {
             int chunk = kRowChunk;
@@ -689,6 +712,12 @@ void lk_kv_store_release(lk_kv_store* s) {
 int lk_kv_store_bytes_used(const lk_kv_store* s, size_t* shared, size_t* total) {
     if (!s || !shared || !total) return fail(LK_ERR_INVALID_ARG, "null argument");
     store_bytes(s, shared, total);
+    return LK_OK;
+}
+
+int lk_kv_store_cache_bytes(const lk_kv_store* s, size_t* bytes) {
+    if (!s || !bytes) return fail(LK_ERR_INVALID_ARG, "null argument");
+    *bytes = s->lay.scache_bytes;
     return LK_OK;
 }
 
@@ -837,6 +866,23 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
                 LK_HIP(lk::scatter_rows(w.xc, w.sel, B, n, T, d, w.h, nullptr, st));
             }
         }
+        // The stable columns' and the prompt tail's loop-k reconstructions are final
+        // now: cache them (float16) for decode.  Rows not written here stay zero.
+        LK_HIP(lk::fill_i32((int32_t*)(s->buf + s->lay.scache), 0, (long long)(s->lay.scache_bytes / 4), st));
+        for (int k = 2; k <= K; ++k)
+            for (int r = 0; r < R; ++r) {
+                lk::RowsAttn g{};
+                g.B = B;
+                g.kv = lazy_layer(s, r);
+                g.k_loop = k;
+                g.cols = col_sets(s, r);
+                g.n_cols = s->lay.n_cols;
+                g.pos = T - 1;
+                const KVLayer L = scache_layer(s, k, r);
+                LK_HIP(lk::gather_recon(g, lk::GATHER_ALL_S, s->lay.ncs, (u16*)L.base[0], (u16*)L.base[1], st));
+                const KVLayer Rg = scache_layer(s, k, r, true);
+                LK_HIP(lk::gather_recon(g, lk::GATHER_RING, s->lay.wr, (u16*)Rg.base[0], (u16*)Rg.base[1], st));
+            }
     }
     for (int j = 0; j < Q; ++j) {
         dense_plan.read = dense_layer(s, P + j);
@@ -904,6 +950,10 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
                 ap.cols = col_sets(s, r);
                 ap.n_cols = s->lay.n_cols;
                 ap.window = h->z.window;
+                ap.scache = scache_layer(s, k, r);
+                ap.ring = scache_layer(s, k, r, true);
+                kw.ring = ap.ring;
+                kw.ring_on = 1;
                 kw.kind = 2;
                 kw.loop = k;
                 kw.slot_base = (long long)s->lay.n_sel - s->Tp;  // slot = n_sel + (t - T)

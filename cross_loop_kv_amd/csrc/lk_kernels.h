@@ -47,6 +47,10 @@ struct KVWrite {
     int32_t* slot_map_k;  // kind 2 decode: slot map of loop k to write (nullptr: already written)
     int keep_codes;       // leave int8/int4 codes and their scales in the store untouched
     const int32_t* dpos;  // decode: device position t (replaces pos_offset; slot = slot_base + t + row)
+    // kind 2 decode: also write the row's float16 loop-k reconstruction into this
+    // window ring (plain rows, position p at row p % ring.Tmax), when ring_on != 0.
+    KVLayer ring;
+    int ring_on;
 };
 hipError_t rope_kv_write(const float* qkv, int rows, int rows_per_seq, const int32_t* pos,
                          int pos_offset, int H, int Hkv, int hd, const double* inv_freq, u16* q_out,
@@ -110,12 +114,22 @@ struct RowsAttn {
     u16* out;              // bf16 [B * n_rows, H * hd]
     const int32_t* lens;   // dense: columns per (b, g) (nullptr: pos + 1 for all)
     const int32_t* dpos;   // decode: device position t (replaces pos)
+    // Two-segment sparse decode (seg_split > 0): splits [0, seg_split) run over kv, the
+    // float16 reconstruction of the column set S (row i = column cols[i]; rows with
+    // cols[i] > pos - window are masked); splits from seg_split on run over kv2, a
+    // ring of float16 window rows (position p at row p % kv2.Tmax), keys taken from
+    // position (max(0, pos-window+1) & ~7) with those below the window masked.
+    KVLayer kv2;
+    int seg_split;
 };
-// Decode, loops >= 2: write the loop-k reconstruction of each (b, g)'s column list
-// (S intersect [0, pos-window] then [pos-window+1, pos]) as float16 rows into
-// kc [B*Hkv][ncap][hd] and 8-key-interleaved vc [B*Hkv][ncap/8][hd][8], and the
-// column count into lens[B*Hkv]; rows past the count are zero.
-hipError_t gather_recon(const RowsAttn& a, int ncap, u16* kc, u16* vc, int32_t* lens, hipStream_t st);
+// Write loop-k reconstructions as float16 rows into kc [B*Hkv][ncap][hd] and
+// 8-key-interleaved vc [B*Hkv][ncap/8][hd][8] (rows past the count are zero):
+//  GATHER_ALL_S:  row i = column cols[i] of the (b, g) column set, i < n_cols;
+//  GATHER_RING:   positions p in [roundup8(max(0, T - ncap)), T) for T = pos + 1,
+//                 each at row p % ncap (the window ring at the end of prefill; other
+//                 rows are left as they are).
+enum { GATHER_ALL_S = 1, GATHER_RING = 3 };
+hipError_t gather_recon(const RowsAttn& a, int mode, int ncap, u16* kc, u16* vc, hipStream_t st);
 // attn_rows_main writes the per-split partials; attn_rows_combine merges them into `out`.
 hipError_t attn_rows_main(const RowsAttn& a, hipStream_t st);
 hipError_t attn_rows_combine(const RowsAttn& a, hipStream_t st);

@@ -130,6 +130,15 @@ void lk_kv_store_release(lk_kv_store *s);
  * the dense per-loop / last-loop rows); *total adds the prelude/coda rows.
  * Per-token figures divide by batch * t. */
 int lk_kv_store_bytes_used(const lk_kv_store *s, size_t *shared, size_t *total);
+/* Bytes of the lazy store's decode cache (0 in the other modes): for every loop
+ * k >= 2 and shared layer, the float16 loop-k reconstruction of (1) the stable
+ * columns S, written at the end of prefill (S and those reconstructions do not
+ * change afterwards), and (2) a ring of the last window + 16 positions (rounded up
+ * to 128), filled at the end of prefill and extended by every decode step.  The
+ * token-sparse decode attention reads these instead of reconstructing its
+ * columns from base + residuals every step.  It is derived data, allocated with
+ * the store (included in need_bytes) and not counted by lk_kv_store_bytes_used. */
+int lk_kv_store_cache_bytes(const lk_kv_store *s, size_t *bytes);
 /* Current tokens per sequence (0 before prefill). */
 int lk_kv_store_length(const lk_kv_store *s, int32_t *tokens);
 

@@ -212,3 +212,13 @@ def test_decode_graph_replay_matches_eager_launches(mode, timed):
     else:
         assert n == 0
     assert sa.length() == sb.length() == T + steps
+
+
+def test_decode_window_ring_wraps_during_decode():
+    """Decode positions cross the end of the float16 window ring (window 16 -> 128 rows):
+    prompt 100, 40 steps, positions 100..139."""
+    s = _small()
+    lz = I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4)
+    log("ring wrap: prompt 100, 40 decode steps")
+    r = run_pair(s, lz, batch=2, prompt=100, steps=40, seed=11)
+    check(r, "ring wrap")
