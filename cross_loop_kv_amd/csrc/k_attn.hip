@@ -489,16 +489,26 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
         const int valid = c_end - (kb + 8 * kgrp);
         // rows past the end of the context are unwritten: clamp the block address, zero the values
         const int pos0 = row_of(min(kb + 8 * kgrp, ((c_end - 1) >> 3) << 3));
+        // int8 V: one 16-byte load per pair of O^T tiles; tile et's row r is head dim
+        // vdim(et, r) = 32 (et/2) + 2 r + et%2 (the 8 keys of dims e and e + 1 are adjacent)
+        uint4 vpair[NE / 2], vsc[NE / 2];
+        if (I8) {
+#pragma unroll
+            for (int pp = 0; pp < NE / 2; ++pp) {
+                vpair[pp] = *(const uint4*)((const int8_t*)kv.base[1] + v_elem(kv, b, g, pos0, 32 * pp + 2 * c16));
+                vsc[pp] = *(const uint4*)(kv.base_scale[1] + v_scale_idx(kv, b, g, pos0, pp));
+            }
+        }
 #pragma unroll
         for (int et = 0; et < NE; ++et) {
             const int e = 16 * et + c16;
-            const long long vi = v_elem(kv, b, g, pos0, e);
             uint4 vf;
             if (I8) {
-                const uint2 c = *(const uint2*)((const int8_t*)kv.base[1] + vi);
-                const uint4 sp = *(const uint4*)(kv.base_scale[1] + v_scale_idx(kv, b, g, pos0, e >> 5));
-                vf = i8x8_to_f16(c, sp);
+                const uint4 c4 = vpair[et >> 1];
+                const uint2 c = (et & 1) ? make_uint2(c4.z, c4.w) : make_uint2(c4.x, c4.y);
+                vf = i8x8_to_f16(c, vsc[et >> 1]);
             } else {
+                const long long vi = v_elem(kv, b, g, pos0, e);
                 vf = *(const uint4*)((const u16*)kv.base[1] + vi);
             }
             vf = mask_tail8(vf, valid);
@@ -508,7 +518,8 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
                 oacc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), as_bf16x8(pu), oacc[et], 0, 0, 0);
         }
     }
-    // ---- merge the four waves: O^T lane holds e = 16et + 4kgrp + i for head c16
+    // ---- merge the four waves: O^T lane holds row r = 4kgrp + i of tile et for head c16
+    //      (head dim 16et + r; int8 rows: 32 (et/2) + 2r + et%2)
     __shared__ float sm_m[4][16], sm_l[4][16];
     __shared__ float sm_o[4][G][HD];
     if (kgrp == 0) {
@@ -519,7 +530,10 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
 #pragma unroll
         for (int et = 0; et < NE; ++et)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sm_o[w][c16][16 * et + 4 * kgrp + i] = oacc[et][i];
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * kgrp + i;
+                sm_o[w][c16][I8 ? 32 * (et >> 1) + 2 * r + (et & 1) : 16 * et + r] = oacc[et][i];
+            }
     }
     __syncthreads();
     float* P = a.part + ((long long)bg * a.n_splits + split) * G * (HD + 2);

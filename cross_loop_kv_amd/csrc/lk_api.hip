@@ -544,10 +544,11 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
             a.cols = nullptr;
             ncol_max = (long long)ap.pos + 1;
         }
-        // dense decode: one workgroup per (sequence, KV head, chunk), about 1536 workgroups
+        // dense decode: one workgroup per (sequence, KV head, chunk), about 768 workgroups
+        // (three per CU; longer chunks keep each wave streaming longer)
         auto dense_chunk = [=](long long ncol) {
             const long long pairs = (long long)a.B * c.n_kv_heads;
-            const long long want = (ncol * pairs + 1535) / 1536;
+            const long long want = (ncol * pairs + 767) / 768;
             int ch = (int)std::max(128LL, (want + 127) / 128 * 128);
             while ((ncol + ch - 1) / ch > kMaxSplits) ch *= 2;
             return ch;
