@@ -60,11 +60,32 @@ def decode_attention_bytes(shape, lazy, batch, t):
     return kv + batch * H * hd * 2
 
 
-def cpu_baseline(wl, rng_seed=3):
-    """The oracle on a bounded sample: one decode step of the full batch at the full
-    context through ONE shared layer x K loops, on a synthetic store state (what a
-    prefill leaves: base, kept-row residuals, slot maps, column sets), scaled to
-    the R shared layers of the workload."""
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_dense_i8_deep_48x4_b8_ctx32k_traffic.md")
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the loop-1 int8 decode attention from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (copy-calibrated), or None when the
+    summary is for another workload or the kernel source changed since it was taken."""
+    import hashlib
+    import re
+    if workload != "deep_48x4_b8_ctx32k" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    src = re.search(r"^kernel_source: (\S+)$", txt, re.M)
+    sha = re.search(r"^kernel_source_sha256_16: ([0-9a-f]+)$", txt, re.M)
+    val = re.search(r"^traffic_bytes_per_launch: (\d+)$", txt, re.M)
+    if not (src and sha and val):
+        return None
+    cur = hashlib.sha256(open(os.path.join(ROOT, src.group(1)), "rb").read()).hexdigest()[:16]
+    return int(val.group(1)) if cur == sha.group(1) else None
+
+
+def cpu_baseline(wl, n_steps=8, rng_seed=3):
+    """The oracle on a bounded sample: ``n_steps`` decode steps of the full batch at
+    the full context through ONE shared layer x K loops, on a synthetic store state
+    (what a prefill leaves: base, kept-row residuals, slot maps, column sets),
+    scaled to the R shared layers of the workload."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -77,13 +98,13 @@ def cpu_baseline(wl, rng_seed=3):
     R_full = wl.shape.n_shared
     W = I.gen_weights(s1)
     B, T, lz = wl.batch, wl.prompt, wl.lazy
-    m = LoopedOracle(s1, lz, W, B, T + 1)
+    m = LoopedOracle(s1, lz, W, B, T + n_steps)
     rng = np.random.default_rng(rng_seed)
     Hkv, hd = s1.n_kv_heads, s1.head_dim
     m.T, m.t = T, T
     if lz.mode == "lazy":
         m.n_sel = n_selected(lz.rho, T)
-        m._alloc_residuals(m.n_sel + 1)
+        m._alloc_residuals(m.n_sel + n_steps)
         for kv in range(2):
             if lz.base_bits == 16:
                 m.base[0][kv][:] = rng.standard_normal(m.base[0][kv].shape, np.float32)
@@ -105,18 +126,16 @@ def cpu_baseline(wl, rng_seed=3):
         ncols = min(lz.top_s, T)
         m.S = [[[np.sort(rng.choice(T, ncols, replace=False)).astype(np.int32) for _ in range(Hkv)]
                 for _ in range(B)]]
-    else:
-        for arrs in (getattr(m, "loop_k", None), getattr(m, "last_k", None)):
-            pass
-    ids = I.gen_decode_ids(s1, B, 1)[0]
+    ids = I.gen_decode_ids(s1, B, n_steps)
     t0 = time.time()
-    m.decode(ids)
+    for i in range(n_steps):
+        m.decode(ids[i])
     dt = time.time() - t0
-    step_s = dt * R_full
+    step_s = dt / n_steps * R_full
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": B / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"one decode step of batch {B} at context {T + 1} through 1 shared layer x "
-                       f"{s1.n_loops} loops ({s1.n_loops} layer applications) on a synthetic store, "
+            "sample": (f"{n_steps} decode steps of batch {B} at context {T + 1}..{T + n_steps} through 1 shared "
+                       f"layer x {s1.n_loops} loops ({s1.n_loops} layer applications each) on a synthetic store, "
                        f"{dt:.1f} s, scaled x{R_full} to the {R_full}-layer stack")}
 
 
@@ -234,7 +253,8 @@ def main():
         "prefill_tokens_per_s": round(Bsz * T / prefill_s, 1),
         "roofline": {"kernel": "attn_decode_dense_kernel (decode attention over the loop-1 base)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload) if lz.mode == "lazy" and lz.base_bits == 8 else None,
                      "launches": launches, "avg_launch_us": round(avg_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": int(bytes_per_launch),
                      "share_of_step": round(kern_ms / (elapsed * 1e3), 4)},
