@@ -63,22 +63,32 @@ def decode_attention_bytes(shape, lazy, batch, t):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_dense_i8_deep_48x4_b8_ctx32k_traffic.md")
 
 
+def kernel_source_hash():
+    """Hash of the source the loop-1 decode-attention kernel is built from: the
+    attention file up to the sparse-gather section (helpers, prefill and dense decode
+    kernels) and the KV-store address arithmetic of the common header."""
+    import hashlib
+    att = open(os.path.join(ROOT, "cross_loop_kv_amd", "csrc", "k_attn.hip")).read()
+    com = open(os.path.join(ROOT, "cross_loop_kv_amd", "csrc", "lk_common.h")).read()
+    a = att.index("typedef _Float16 half8")
+    b = att.index("// ---------------------------------------------------------------- sparse decode: gather")
+    c = com.index("// ---------------------------------------------------------------- KV store views")
+    return hashlib.sha256((att[a:b] + com[c:]).encode()).hexdigest()[:16]
+
+
 def measured_traffic(workload):
     """HBM bytes per launch of the loop-1 int8 decode attention from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary (copy-calibrated), or None when the
     summary is for another workload or the kernel source changed since it was taken."""
-    import hashlib
     import re
     if workload != "deep_48x4_b8_ctx32k" or not os.path.exists(TRAFFIC_FILE):
         return None
     txt = open(TRAFFIC_FILE).read()
-    src = re.search(r"^kernel_source: (\S+)$", txt, re.M)
-    sha = re.search(r"^kernel_source_sha256_16: ([0-9a-f]+)$", txt, re.M)
+    sha = re.search(r"^kernel_source_hash: ([0-9a-f]+)$", txt, re.M)
     val = re.search(r"^traffic_bytes_per_launch: (\d+)$", txt, re.M)
-    if not (src and sha and val):
+    if not (sha and val):
         return None
-    cur = hashlib.sha256(open(os.path.join(ROOT, src.group(1)), "rb").read()).hexdigest()[:16]
-    return int(val.group(1)) if cur == sha.group(1) else None
+    return int(val.group(1)) if kernel_source_hash() == sha.group(1) else None
 
 
 def cpu_baseline(wl, n_steps=8, rng_seed=3):

@@ -83,6 +83,7 @@ _SIGS = {
     "lk_kv_store_keep_codes": (C.c_int, [C.c_void_p, C.c_int32]),
     "lk_timing_enable": (C.c_int, [C.c_void_p, C.c_char_p]),
     "lk_set_decode_graphs": (C.c_int, [C.c_void_p, C.c_int32]),
+    "lk_decode_weight_bytes": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t)]),
     "lk_timing_read": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
     "lk_dbg_topk": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
     "lk_dbg_quantize": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
@@ -200,6 +201,12 @@ def lk_kv_store_force_selection(s: int, d_tokens, d_columns) -> None:
 
 def lk_kv_store_keep_codes(s: int, enable: bool) -> None:
     _check(lib().lk_kv_store_keep_codes(s, 1 if enable else 0))
+
+
+def lk_decode_weight_bytes(h: int) -> int:
+    n = C.c_size_t()
+    _check(lib().lk_decode_weight_bytes(h, C.byref(n)))
+    return n.value
 
 
 def lk_set_decode_graphs(h: int, enable: bool) -> None:

@@ -957,7 +957,7 @@ __global__ __launch_bounds__(64) void attn_rows_kernel(RowsAttn a) {
 constexpr int kCombineMaxSplits = 256, kCombineMaxG = 8;
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part, int n_splits,
                                                            int G, int HD, int H, int Hkv,
-                                                           u16* __restrict__ out) {
+                                                           u16* __restrict__ out, bool packed) {
     __shared__ float wts[kCombineMaxSplits * kCombineMaxG];
     __shared__ float lsum[kCombineMaxG];
     const long long qrow = blockIdx.x;
@@ -987,7 +987,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
         float acc = 0.f;
 #pragma unroll 8
         for (int s = 0; s < n_splits; ++s) acc += wts[s * G + hh] * pe[s * stride];
-        out[qrow * H * HD + (g * G + hh) * HD + e] = f2bf(acc / lsum[hh]);
+        const int k = (g * G + hh) * HD + e;
+        out[packed ? pk_index((int)qrow, k, H * HD) : qrow * H * HD + k] = f2bf(acc / lsum[hh]);
     }
 }
 
@@ -1103,12 +1104,13 @@ hipError_t gather_recon(const RowsAttn& a, int mode, int ncap, u16* kc, u16* vc,
     return hipGetLastError();
 }
 
-hipError_t attn_rows_combine(const RowsAttn& a, hipStream_t st) {
+hipError_t attn_rows_combine(const RowsAttn& a, hipStream_t st, bool packed_out) {
     const int G = a.H / a.kv.Hkv;
     if (a.n_splits > kCombineMaxSplits || G > kCombineMaxG) return hipErrorInvalidValue;
+    if (packed_out && (a.B * a.n_rows > 8 || (a.H * a.kv.hd) % 64)) return hipErrorInvalidValue;
     dim3 grid(a.B * a.n_rows, a.kv.Hkv);
     hipLaunchKernelGGL(attn_combine_kernel, grid, dim3(256), 0, st, a.part, a.n_splits, G, a.kv.hd, a.H,
-                       a.kv.Hkv, a.out);
+                       a.kv.Hkv, a.out, packed_out);
     return hipGetLastError();
 }
 

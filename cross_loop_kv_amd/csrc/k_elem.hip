@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kThreads) void norm_prep_kernel(float* x, const u16
             v = v + bf2f(add[j]);
             row[j] = v;
         }
-        xg[(long long)r * d + j] = f2bf(v * bf2f(gain[j]));
+        xg[pk_index(r, j, d)] = f2bf(v * bf2f(gain[j]));
         ss += v * v;
     }
     ss = block_sum(ss, red);
@@ -374,7 +374,7 @@ hipError_t rmsnorm(float* x, const u16* add, const u16* gain, float eps, int row
 
 hipError_t norm_prep(float* x, const u16* add, const u16* gain, int rows, int d, u16* xg, float* ps,
                      hipStream_t st) {
-    if (rows > 8) return hipErrorInvalidValue;
+    if (rows > 8 || d % 64) return hipErrorInvalidValue;
     hipLaunchKernelGGL(norm_prep_kernel, dim3(rows), dim3(kThreads), 0, st, x, add, gain, d, xg, ps);
     return hipGetLastError();
 }

@@ -21,6 +21,8 @@
 //   - 16-row kernel (8 < M <= 16): one 16-row weight tile per workgroup.
 //   In both, 8 waves split K and meet in LDS; every load of a wave covers 64
 //   contiguous bytes of each of its rows.
+#include <algorithm>
+
 #include "lk_kernels.h"
 
 namespace lk {
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(const u16* __restrict_
 // PREP (with EPI_ADD): besides x += A W^T (+ add_vec), write what the next NORM
 // product needs: xg_out = bf16(x * next_gain) and, per workgroup, the row sums of x^2
 // over its 8 columns into ps_out [N / 8][8].
-template <int EPI, int NL, bool NORM, bool PREP>
+template <int EPI, int NL, bool NORM, bool PREP, bool PK>
 __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ A, const u16* __restrict__ W,
                                                         int M, int N, int K, float* __restrict__ C,
                                                         u16* __restrict__ Obf, FoldIO io) {
@@ -267,10 +269,13 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
     const int h = c16 >> 3, r8 = c16 & 7;
     const int Kh = K >> 1, nch = Kh >> 5;
     const int n = blockIdx.x * 8 + r8;  // grid = N / 8 (N % 8 == 0)
-    const u16* w0 = W + (long long)n * K + h * Kh + grp * 8;
-    const u16* w1 = W + (long long)(N + n) * K + h * Kh + grp * 8;
+    // PK: operands in the lane-packed order (chunk c of tile t at ((t nch + c) 64 + lane) 8)
+    const u16* w0 = PK ? W + ((long long)blockIdx.x * nch * 64 + lane) * 8 : W + (long long)n * K + h * Kh + grp * 8;
+    const u16* w1 = PK ? W + ((long long)(N / 8 + blockIdx.x) * nch * 64 + lane) * 8
+                       : W + (long long)(N + n) * K + h * Kh + grp * 8;
+    const int wstep = PK ? 512 : 32;  // elements between consecutive chunks
     const bool mvalid = r8 < M;
-    const u16* ar = A + (long long)(mvalid ? r8 : 0) * K + h * Kh + grp * 8;
+    const u16* ar = PK ? A + lane * 8 : A + (long long)(mvalid ? r8 : 0) * K + h * Kh + grp * 8;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = w; c0 < nch; c0 += NWV * NL) {
         uint4 wv[NL], wv1[NL], av[NL];
@@ -278,13 +283,13 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
         for (int j = 0; j < NL; ++j) {
             const int c = c0 + j * NWV;
             const bool ok = c < nch;
-            wv[j] = ok ? *(const uint4*)(w0 + c * 32) : make_uint4(0, 0, 0, 0);
-            if (DUAL) wv1[j] = ok ? *(const uint4*)(w1 + c * 32) : make_uint4(0, 0, 0, 0);
+            wv[j] = ok ? *(const uint4*)(w0 + (long long)c * wstep) : make_uint4(0, 0, 0, 0);
+            if (DUAL) wv1[j] = ok ? *(const uint4*)(w1 + (long long)c * wstep) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             const int c = c0 + j * NWV;
-            av[j] = (c < nch && mvalid) ? *(const uint4*)(ar + c * 32) : make_uint4(0, 0, 0, 0);
+            av[j] = (c < nch && mvalid) ? *(const uint4*)(ar + (long long)c * wstep) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
@@ -334,13 +339,13 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
             if (PREP && io.add_vec) x = x + bf2f(io.add_vec[col]);
             C[o] = x;
             if (PREP) {
-                io.xg_out[o] = f2bf(x * bf2f(io.next_gain[col]));
+                io.xg_out[PK ? pk_index(m, col, N) : o] = f2bf(x * bf2f(io.next_gain[col]));
                 sq[i] = x * x;
             }
         } else if (EPI == EPI_SWIGLU) {
-            Obf[o] = f2bf(silu_f(v0) * ((s1[i] + o1[i]) * inv));
+            Obf[PK ? pk_index(m, col, N) : o] = f2bf(silu_f(v0) * ((s1[i] + o1[i]) * inv));
         } else {
-            Obf[o] = f2bf(gelu_f(v0));
+            Obf[PK ? pk_index(m, col, N) : o] = f2bf(gelu_f(v0));
         }
     }
     if (PREP) {
@@ -355,16 +360,25 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
     }
 }
 
-template <int EPI, bool NORM, bool PREP>
+template <int EPI, bool NORM, bool PREP, bool PK = false>
 void launch_fold(const u16* A, const u16* W, int M, int N, int K, float* c, u16* out_bf, const FoldIO& io,
                  hipStream_t st) {
     // one batch of loads per wave at K = 2048 (4 chunks) and K = 5632 (11 chunks)
     const int per_wave = (K / 64 + 7) / 8;
     dim3 grid(N / 8);
     if (per_wave > 4)
-        hipLaunchKernelGGL((gemm_fold_kernel<EPI, 11, NORM, PREP>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf, io);
+        hipLaunchKernelGGL((gemm_fold_kernel<EPI, 11, NORM, PREP, PK>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf, io);
     else
-        hipLaunchKernelGGL((gemm_fold_kernel<EPI, 4, NORM, PREP>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf, io);
+        hipLaunchKernelGGL((gemm_fold_kernel<EPI, 4, NORM, PREP, PK>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf, io);
+}
+
+__global__ void pack_rows_kernel(const u16* __restrict__ W, long long rows, int K, u16* __restrict__ Wp) {
+    const long long n8 = rows * K / 8;  // 16-byte pieces
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n8; i += (long long)gridDim.x * blockDim.x) {
+        const long long row = i / (K / 8);
+        const int k = (int)(i % (K / 8)) * 8;
+        *(uint4*)(Wp + pk_index((int)row, k, K)) = *(const uint4*)(W + row * K + k);
+    }
 }
 
 bool fold_ok(int M, int N, int K) { return M <= 8 && K % 64 == 0 && N % 8 == 0; }
@@ -413,7 +427,7 @@ hipError_t gemm_rmsnorm(const float* X, const u16* gain, float eps, const u16* W
 
 bool gemm_fold_supported(int M, int N, int K) { return fold_ok(M, N, K); }
 
-hipError_t gemm_fold_norm(const u16* xg, const float* ps, int nparts, float eps, const u16* W, int M, int N, int K,
+hipError_t gemm_fold_norm(const u16* xg, const float* ps, int nparts, float eps, const u16* Wp, int M, int N, int K,
                           int epi, float* c, u16* out_bf, hipStream_t st) {
     if (!fold_ok(M, N, K)) return hipErrorInvalidValue;
     FoldIO io{};
@@ -421,15 +435,15 @@ hipError_t gemm_fold_norm(const u16* xg, const float* ps, int nparts, float eps,
     io.nparts = nparts;
     io.eps = eps;
     switch (epi) {
-        case EPI_STORE: launch_fold<EPI_STORE, true, false>(xg, W, M, N, K, c, out_bf, io, st); break;
-        case EPI_SWIGLU: launch_fold<EPI_SWIGLU, true, false>(xg, W, M, N, K, c, out_bf, io, st); break;
-        case EPI_GELU: launch_fold<EPI_GELU, true, false>(xg, W, M, N, K, c, out_bf, io, st); break;
+        case EPI_STORE: launch_fold<EPI_STORE, true, false, true>(xg, Wp, M, N, K, c, out_bf, io, st); break;
+        case EPI_SWIGLU: launch_fold<EPI_SWIGLU, true, false, true>(xg, Wp, M, N, K, c, out_bf, io, st); break;
+        case EPI_GELU: launch_fold<EPI_GELU, true, false, true>(xg, Wp, M, N, K, c, out_bf, io, st); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t gemm_fold_add(const u16* A, const u16* W, int M, int N, int K, float* x, const u16* add_vec,
+hipError_t gemm_fold_add(const u16* A, const u16* Wp, int M, int N, int K, float* x, const u16* add_vec,
                          const u16* next_gain, u16* xg_out, float* ps_out, hipStream_t st) {
     if (!fold_ok(M, N, K)) return hipErrorInvalidValue;
     FoldIO io{};
@@ -437,9 +451,17 @@ hipError_t gemm_fold_add(const u16* A, const u16* W, int M, int N, int K, float*
     io.next_gain = next_gain;
     io.xg_out = xg_out;
     io.ps_out = ps_out;
-    if (next_gain) launch_fold<EPI_ADD, false, true>(A, W, M, N, K, x, nullptr, io, st);
+    if (next_gain) launch_fold<EPI_ADD, false, true, true>(A, Wp, M, N, K, x, nullptr, io, st);
     else if (add_vec) return hipErrorInvalidValue;
-    else launch_fold<EPI_ADD, false, false>(A, W, M, N, K, x, nullptr, io, st);
+    else launch_fold<EPI_ADD, false, false, true>(A, Wp, M, N, K, x, nullptr, io, st);
+    return hipGetLastError();
+}
+
+hipError_t pack_weights(const u16* W, long long rows, int K, u16* Wp, hipStream_t st) {
+    if (rows % 8 || K % 64) return hipErrorInvalidValue;
+    const long long n8 = rows * K / 8;
+    const long long blocks = std::min<long long>((n8 + 255) / 256, 16384);
+    hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, W, rows, K, Wp);
     return hipGetLastError();
 }
 

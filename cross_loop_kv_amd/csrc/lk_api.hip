@@ -114,6 +114,17 @@ struct lk_handle {
     DecodeGraph graph;
     DecodeGraph* building = nullptr;  // set while a decode step is being captured
     int use_graphs = 1;
+    // Decode copy of the layer projections in the lane-packed operand order, made on
+    // the first decode step (one device allocation, freed by lk_destroy).
+    struct Packed {
+        const u16 *wqkv, *wo, *w_in, *w_down;
+    };
+    std::vector<Packed> PL;
+    void* pk_buf = nullptr;
+    size_t pk_bytes = 0;
+    ~lk_handle() {
+        if (pk_buf) (void)hipFree(pk_buf);
+    }
     const u16 *tok, *lemb, *fnorm;
     std::vector<lk_layer_weights> L;
     double inv_freq[64];
@@ -359,11 +370,13 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
     w.h = (float*)take(M * d * 4);
     w.h0 = (float*)take(hd_->lazy() ? M * d * 4 : 0);
     w.xc = (float*)take(hd_->lazy() ? (long long)B * n * d * 4 : 0);
-    w.xn = (u16*)take(M * d * 2);
+    // bf16 operands of the decode products are lane-packed over 8 rows: at least 8 rows
+    const long long M8 = M < 8 ? 8 : M;
+    w.xn = (u16*)take(M8 * d * 2);
     w.qkv = (float*)take(M * hd_->qkv_w() * 4);
     w.q = (u16*)take(M * Hhd * 2);
-    w.att = (u16*)take(M * Hhd * 2);
-    w.act = (u16*)take(M * (long long)c.ffn_dim * 2);
+    w.att = (u16*)take(M8 * Hhd * 2);
+    w.act = (u16*)take(M8 * (long long)c.ffn_dim * 2);
     w.lse = (float*)take(M * c.n_heads * 4);
     w.mass = (float*)take(hd_->lazy() ? M * c.n_kv_heads * 4 : 0);
     w.keys = (float*)take(hd_->lazy() ? M * 4 : 0);
@@ -493,9 +506,10 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
     const int d = c.d_model, H = c.n_heads, hd = c.head_dim, Hhd = H * hd;
     // decode-sized row counts fold the RMSNorm into the skinny GEMMs
     const bool fused_norm = io.M <= 16;
+    const lk_handle::Packed PW = io.fold ? h->PL[li] : lk_handle::Packed{};
     if (io.fold) {
         LK_TRY(timed(h, gcls, st, [=] {
-            return lk::gemm_fold_norm(w.xn, w.ps, io.nparts, c.rms_eps, (const u16*)W.wqkv, io.M, h->qkv_w(), d,
+            return lk::gemm_fold_norm(w.xn, w.ps, io.nparts, c.rms_eps, PW.wqkv, io.M, h->qkv_w(), d,
                                       lk::EPI_STORE, w.qkv, nullptr, st);
         }));
     } else if (fused_norm) {
@@ -570,7 +584,7 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
             if ((long long)a.B * H * d.n_splits * (hd + 2) > w.part_floats)
                 return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
             LK_TRY(timed(h, TC_ATTN_DECODE_SPARSE, st, [=] { return lk::attn_rows_main(d, st); }));
-            LK_HIP(lk::attn_rows_combine(d, st));
+            LK_HIP(lk::attn_rows_combine(d, st, io.fold));
         } else {
             int chunk = kRowChunk;
             if (ap.kind == ATTN_ROWS_DENSE) chunk = dense_chunk(ncol_max);
@@ -582,22 +596,22 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
             const int acls = io.rows_per_seq > 1 ? TC_ATTN_PREFILL_SPARSE
                              : (ap.kind == ATTN_ROWS_SPARSE ? TC_ATTN_DECODE_SPARSE : TC_ATTN_DECODE_DENSE);
             LK_TRY(timed(h, acls, st, [=] { return lk::attn_rows_main(a, st); }));
-            LK_HIP(lk::attn_rows_combine(a, st));
+            LK_HIP(lk::attn_rows_combine(a, st, io.fold));
         }
     }
     const int act = c.ffn_act == LK_ACT_SWIGLU ? lk::EPI_SWIGLU : lk::EPI_GELU;
     if (io.fold) {
         LK_TRY(timed(h, gcls, st, [=] {
-            return lk::gemm_fold_add(w.att, (const u16*)W.wo, io.M, d, Hhd, io.x, nullptr, (const u16*)W.ffn_norm,
-                                     w.xn, w.ps, st);
+            return lk::gemm_fold_add(w.att, PW.wo, io.M, d, Hhd, io.x, nullptr, (const u16*)W.ffn_norm, w.xn, w.ps,
+                                     st);
         }));
         LK_TRY(timed(h, gcls, st, [=] {
-            return lk::gemm_fold_norm(w.xn, w.ps, d / 8, c.rms_eps, (const u16*)W.w_in, io.M, c.ffn_dim, d, act,
-                                      nullptr, w.act, st);
+            return lk::gemm_fold_norm(w.xn, w.ps, d / 8, c.rms_eps, PW.w_in, io.M, c.ffn_dim, d, act, nullptr,
+                                      w.act, st);
         }));
         LK_TRY(timed(h, gcls, st, [=] {
-            return lk::gemm_fold_add(w.act, (const u16*)W.w_down, io.M, d, c.ffn_dim, io.x, io.next_add,
-                                     io.next_gain, w.xn, w.ps, st);
+            return lk::gemm_fold_add(w.act, PW.w_down, io.M, d, c.ffn_dim, io.x, io.next_add, io.next_gain, w.xn,
+                                     w.ps, st);
         }));
         return LK_OK;
     }
@@ -900,6 +914,46 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
 
 namespace {
 
+// Bytes of the packed decode weights (0 when the shapes do not take the folded products).
+size_t packed_weight_bytes(const lk_handle* h) {
+    const lk_model_cfg& c = h->c;
+    const int d = c.d_model, Hhd = c.n_heads * c.head_dim, F = c.ffn_dim;
+    const int fin = c.ffn_act == LK_ACT_SWIGLU ? 2 : 1;
+    if (!lk::gemm_fold_supported(8, h->qkv_w(), d) || !lk::gemm_fold_supported(8, d, Hhd) ||
+        !lk::gemm_fold_supported(8, F, d) || !lk::gemm_fold_supported(8, d, F))
+        return 0;
+    const size_t per = ((size_t)h->qkv_w() * d + (size_t)d * Hhd + (size_t)fin * F * d + (size_t)d * F) * 2;
+    return per * h->L.size();
+}
+
+int prepare_packed(lk_handle* h, hipStream_t st) {
+    if (h->pk_buf) return LK_OK;
+    const size_t bytes = packed_weight_bytes(h);
+    if (!bytes) return LK_OK;
+    LK_HIP(hipMalloc(&h->pk_buf, bytes));
+    h->pk_bytes = bytes;
+    const lk_model_cfg& c = h->c;
+    const int d = c.d_model, Hhd = c.n_heads * c.head_dim, F = c.ffn_dim;
+    const int fin = c.ffn_act == LK_ACT_SWIGLU ? 2 : 1;
+    u16* p = (u16*)h->pk_buf;
+    h->PL.resize(h->L.size());
+    for (size_t i = 0; i < h->L.size(); ++i) {
+        const lk_layer_weights& W = h->L[i];
+        lk_handle::Packed& P = h->PL[i];
+        auto pack = [&](const void* src, long long rows, int K, const u16** dst) {
+            hipError_t e = lk::pack_weights((const u16*)src, rows, K, p, st);
+            *dst = p;
+            p += (size_t)rows * K;
+            return e;
+        };
+        LK_HIP(pack(W.wqkv, h->qkv_w(), d, &P.wqkv));
+        LK_HIP(pack(W.wo, d, Hhd, &P.wo));
+        LK_HIP(pack(W.w_in, (long long)fin * F, d, &P.w_in));
+        LK_HIP(pack(W.w_down, d, F, &P.w_down));
+    }
+    return LK_OK;
+}
+
 // Enqueue one decode step: ids from w.ids, output rows to w.out, position from the
 // store's device counter (incremented at the end).  Nothing here depends on the
 // host's copy of the position, so the same launches serve every step.
@@ -968,9 +1022,7 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
         apps.push_back({P + R + j, nullptr, plain_write(dense.read), dense});
     }
     // Folded norms: every projection input is prepared by the kernel that produced x.
-    const int qkv = h->qkv_w(), Hhd = c.n_heads * c.head_dim;
-    const bool fold = lk::gemm_fold_supported(B, qkv, d) && lk::gemm_fold_supported(B, d, Hhd) &&
-                      lk::gemm_fold_supported(B, c.ffn_dim, d) && lk::gemm_fold_supported(B, d, c.ffn_dim);
+    const bool fold = B <= 8 && h->pk_buf != nullptr;
     LK_HIP(lk::embed(w.ids, h->tok, w.h, B, d, c.vocab, st));
     if (fold)
         LK_HIP(lk::norm_prep(w.h, apps[0].add, (const u16*)h->L[apps[0].li].attn_norm, B, d, w.xn, w.ps, st));
@@ -1025,6 +1077,7 @@ int lk_looped_decode_step(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, fl
     if ((uintptr_t)d_ws % kAlign) return fail(LK_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     hipStream_t st = (hipStream_t)stream;
     const int d = h->c.d_model;
+    LK_TRY(prepare_packed(h, st));
     LK_HIP(hipMemcpyAsync(w.ids, d_ids, (size_t)B * 4, hipMemcpyDeviceToDevice, st));
     if (st && h->use_graphs) {
         DecodeGraph& g = h->graph;
@@ -1052,6 +1105,12 @@ int lk_looped_decode_step(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, fl
     }
     LK_HIP(hipMemcpyAsync(d_out, w.out, (size_t)B * d * 4, hipMemcpyDeviceToDevice, st));
     s->t += 1;
+    return LK_OK;
+}
+
+int lk_decode_weight_bytes(const lk_handle* h, size_t* bytes) {
+    if (!h || !bytes) return fail(LK_ERR_INVALID_ARG, "null argument");
+    *bytes = packed_weight_bytes(h);
     return LK_OK;
 }
 

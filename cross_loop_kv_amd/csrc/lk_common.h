@@ -82,6 +82,19 @@ __device__ __forceinline__ int quant_group32(float r, int qmax, u16* scale_bits)
     return (int)c;
 }
 
+// ---------------------------------------------------------------- decode operand layout
+// Decode products (at most 8 activation rows, K % 64 == 0) read their operands in a
+// "lane-packed" order: for 8-row tile t and 32-element chunk c of each half of K,
+// the 16-byte operand of MFMA lane l = 16 grp + 8 h + r (row 8t + r, elements
+// h K/2 + 32 c + 8 grp .. +8) is stored at ((t * K/64 + c) * 64 + l) * 8, so every
+// wave load is 1 KB contiguous.  Activations use tile 0 (rows < 8).
+__host__ __device__ __forceinline__ long long pk_index(int row, int k, int K) {
+    const int Kh = K >> 1, h = k >= Kh ? 1 : 0, kk = k - h * Kh;
+    const long long tile = row >> 3;
+    const int lane = ((kk >> 3) & 3) * 16 + h * 8 + (row & 7);
+    return ((tile * (K >> 6) + (kk >> 5)) * 64 + lane) * 8 + (k & 7);
+}
+
 // ---------------------------------------------------------------- KV store views
 // Address arithmetic of one shared layer of a lazy store (or a plain bf16 row
 // cache when lazy == 0).  Positions are padded to Tmax (a multiple of 8).

@@ -71,6 +71,8 @@ hipError_t gemm_rmsnorm(const float* X, const u16* gain, float eps, const u16* W
 // carried between kernels: a producer adds its product into the residual stream x
 // and leaves xg = bf16(x * next_gain) plus per-workgroup row sums of x^2 (ps, [nparts][8]);
 // the consumer multiplies xg by W and scales by 1 / sqrt(sum(ps) / K + eps).
+// Weights (Wp) and bf16 activations (xg, A, and the bf16 outputs) are in the
+// lane-packed order of pk_index (weights: rows = N, or 2N for SwiGLU's [gate; up]).
 struct FoldIO {
     const float* ps_in;    // NORM: partial sums of x^2 [nparts][8]
     int nparts;
@@ -81,12 +83,14 @@ struct FoldIO {
     float* ps_out;         // PREP: [N / 8][8]
 };
 bool gemm_fold_supported(int M, int N, int K);
-hipError_t gemm_fold_norm(const u16* xg, const float* ps, int nparts, float eps, const u16* W, int M, int N, int K,
+hipError_t gemm_fold_norm(const u16* xg, const float* ps, int nparts, float eps, const u16* Wp, int M, int N, int K,
                           int epi, float* c, u16* out_bf, hipStream_t st);
 // x[M, N] += A W^T (+ add_vec); with next_gain also writes xg_out and ps_out (N / 8 parts).
-hipError_t gemm_fold_add(const u16* A, const u16* W, int M, int N, int K, float* x, const u16* add_vec,
+hipError_t gemm_fold_add(const u16* A, const u16* Wp, int M, int N, int K, float* x, const u16* add_vec,
                          const u16* next_gain, u16* xg_out, float* ps_out, hipStream_t st);
-// x += add (optional); xg = bf16(x * gain); ps[0][r] = sum of x^2 of row r (one part).
+// Row-major W [rows, K] -> lane-packed Wp (rows % 8 == 0, K % 64 == 0).
+hipError_t pack_weights(const u16* W, long long rows, int K, u16* Wp, hipStream_t st);
+// x += add (optional); xg = bf16(x * gain) (lane-packed); ps[0][r] = sum of x^2 of row r.
 hipError_t norm_prep(float* x, const u16* add, const u16* gain, int rows, int d, u16* xg, float* ps,
                      hipStream_t st);
 
@@ -132,6 +136,7 @@ enum { GATHER_ALL_S = 1, GATHER_RING = 3 };
 hipError_t gather_recon(const RowsAttn& a, int mode, int ncap, u16* kc, u16* vc, hipStream_t st);
 // attn_rows_main writes the per-split partials; attn_rows_combine merges them into `out`.
 hipError_t attn_rows_main(const RowsAttn& a, hipStream_t st);
-hipError_t attn_rows_combine(const RowsAttn& a, hipStream_t st);
+// packed_out: out in the lane-packed order of the decode products (at most 8 rows).
+hipError_t attn_rows_combine(const RowsAttn& a, hipStream_t st, bool packed_out = false);
 
 }  // namespace lk

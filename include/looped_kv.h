@@ -166,6 +166,15 @@ int lk_looped_decode_step(lk_handle *h, lk_kv_store *s, const int32_t *d_ids, fl
  * step launches its kernels one by one).  Drops any captured step. */
 int lk_set_decode_graphs(lk_handle *h, int32_t enable);
 
+/* Device bytes of the decode copy of the layer projections (0 if the shapes do
+ * not take it: it needs d_model, heads*head_dim and ffn_dim multiples of 64).
+ * Decode steps with at most 8 sequences multiply by the weights in an operand
+ * order packed for the MFMA lanes (every wave load reads 1 KB contiguous); the
+ * first decode step allocates this copy (hipMalloc) and fills it from the
+ * caller's weights on the step's stream.  lk_destroy frees it.  The caller's
+ * weights must not change afterwards. */
+int lk_decode_weight_bytes(const lk_handle *h, size_t *bytes);
+
 /* Layer applications one prefill/decode pass runs per token: P + R*K + Q. */
 int lk_effective_depth(const lk_handle *h, int32_t *depth);
 
