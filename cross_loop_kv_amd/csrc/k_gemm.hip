@@ -399,12 +399,183 @@ void launch_skinny(const u16* A, const float* X, const u16* gain, float eps, con
         hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 1, NORM>), grid, dim3(512), 0, st, A, X, gain, eps, W, M, N, K, c, out_bf);
 }
 
+
+// ---------------------------------------------------------------- big-tile kernel
+// 256 x 256 x 32 workgroup tiles, 4 waves as 2 x 2, each wave 128 x 128 as 4 x 4
+// v_mfma_f32_32x32x16_bf16 tiles (256 accumulator registers per lane, one wave per
+// SIMD).  Operands reach LDS by global_load_lds (16 bytes per lane, no register
+// staging) into four LDS stages, three k-tiles ahead of the MFMAs.  Each stage is its
+// own LDS array, so the compiler can tell the stages apart and waits only for the tile
+// it reads (explicit vmcnt waits + a bare barrier per k-tile).  Within a row of 32
+// bf16 (four 16-byte chunks) chunk c of row r sits at slot c ^ ((r / 4) % 4), so the
+// rows read by eight consecutive lanes land in distinct banks.  Tiles go to workgroups
+// XCD by XCD, grouped 8 M-tiles tall.  SwiGLU: the 256 W rows of a tile are
+// [gate 0..63 | up 0..63 | gate 64..127 | up 64..127] of 128 output columns, so each
+// wave holds gate and up of its 64 output columns.
+// Requires K % 32 == 0 and N % 256 == 0 (SwiGLU: N % 128 == 0).
+constexpr int GB_M = 256, GB_N = 256, GB_K = 32, GB_STAGE = (GB_M + GB_N) * GB_K;
+__shared__ __attribute__((aligned(1024))) u16 gb_s0[GB_STAGE];
+__shared__ __attribute__((aligned(1024))) u16 gb_s1[GB_STAGE];
+__shared__ __attribute__((aligned(1024))) u16 gb_s2[GB_STAGE];
+__shared__ __attribute__((aligned(1024))) u16 gb_s3[GB_STAGE];
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void bare_barrier() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ int gb_swz(int r) { return (r >> 2) & 3; }
+
+// One k-tile into stage `st`: wave w issues loads w, w+4, w+8, w+12 of A and of B (each
+// load = 16 rows x 64 bytes = 1 KB of LDS).
+__device__ __forceinline__ void gb_issue(u16* st, const u16* const* ga, const u16* const* gb, int k0, int w) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        __builtin_amdgcn_global_load_lds((const void*)(ga[p] + k0), (lds_void*)(st + (w + 4 * p) * 512), 16, 0, 0);
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        __builtin_amdgcn_global_load_lds((const void*)(gb[p] + k0), (lds_void*)(st + GB_M * GB_K + (w + 4 * p) * 512),
+                                         16, 0, 0);
+}
+
+__device__ __forceinline__ void gb_compute(const u16* st, f32x16 (&acc)[4][4], int wm, int wn, int l32, int kg) {
+#pragma unroll
+    for (int ks = 0; ks < GB_K / 16; ++ks) {
+        const int kc = 2 * ks + kg;
+        bf16x8 a[4], b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wm * 128 + 32 * i + l32;
+            a[i] = as_bf16x8(*(const uint4*)(st + r * GB_K + ((kc ^ gb_swz(r)) * 8)));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = wn * 128 + 32 * j + l32;
+            b[j] = as_bf16x8(*(const uint4*)(st + GB_M * GB_K + r * GB_K + ((kc ^ gb_swz(r)) * 8)));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_big_kernel(const u16* __restrict__ A, const u16* __restrict__ W,
+                                                          int M, int N, int K, float* __restrict__ C,
+                                                          u16* __restrict__ Obf, int tiles_m, int tiles_n) {
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    constexpr int STAGES = 4;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1, l32 = lane & 31, kg = lane >> 5;
+    // tile order: XCD-major (grid is a multiple of 8), then groups of 8 M-tiles
+    const int ntiles = tiles_m * tiles_n;
+    const int per_xcd = gridDim.x / 8;
+    const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (t >= ntiles) return;
+    constexpr int GROUP = 8;
+    const int group_size = GROUP * tiles_n;
+    const int gid = t / group_size, first_m = gid * GROUP;
+    const int gm = min(tiles_m - first_m, GROUP);
+    const int tm = first_m + (t % group_size) % gm;
+    const int tn = (t % group_size) / gm;
+    const int row0 = tm * GB_M;
+    const u16* ga[4];
+    const u16* gb[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int r = (w + 4 * p) * 16 + lane / 4;  // tile row of this lane's 16 bytes
+        const int kc = (lane % 4) ^ gb_swz(r);      // the chunk that lands in slot lane % 4
+        ga[p] = A + (long long)min(row0 + r, M - 1) * K + kc * 8;
+        int wr;
+        if (DUAL) {
+            const int q = r >> 6;  // 0: gate lo, 1: up lo, 2: gate hi, 3: up hi
+            wr = ((q & 1) ? N : 0) + tn * 128 + (q >> 1) * 64 + (r & 63);
+        } else {
+            wr = tn * GB_N + r;
+        }
+        gb[p] = W + (long long)wr * K + kc * 8;
+    }
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    u16* const bufs[STAGES] = {gb_s0, gb_s1, gb_s2, gb_s3};
+    const int nk = K / GB_K;
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) gb_issue(bufs[s], ga, gb, s * GB_K, w);
+    for (int kt = 0; kt < nk; ++kt) {
+        // k-tile kt has landed once at most (tiles issued after it) x 8 loads remain
+        const int ahead = min(nk - 1 - kt, STAGES - 2);
+        if (ahead >= 2) wait_vmcnt<16>();
+        else if (ahead == 1) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
+        bare_barrier();  // every wave's part of tile kt is in; stage (kt - 1) is free
+        const int nx = kt + STAGES - 1;
+        const int sc = kt % STAGES;
+#pragma unroll
+        for (int s = 0; s < STAGES; ++s) {
+            if (sc == s) {
+                if (nx < nk) gb_issue(bufs[(s + STAGES - 1) % STAGES], ga, gb, nx * GB_K, w);
+                gb_compute(bufs[s], acc, wm, wn, l32, kg);
+            }
+        }
+    }
+    // epilogue: acc[i][j][e] = C[row0 + wm*128 + 32 i + 8 (e/4) + 4 kg + e%4][col(j) + l32]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int r = row0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * kg + (e & 3);
+            if (r >= M) continue;
+            if (DUAL) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int col = tn * 128 + wn * 64 + 32 * j + l32;
+                    Obf[(long long)r * N + col] = f2bf(silu_f(acc[i][j][e]) * acc[i][j + 2][e]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int col = tn * GB_N + wn * 128 + 32 * j + l32;
+                    const long long o = (long long)r * N + col;
+                    if (EPI == EPI_STORE) C[o] = acc[i][j][e];
+                    else if (EPI == EPI_ADD) C[o] = C[o] + acc[i][j][e];
+                    else Obf[o] = f2bf(gelu_f(acc[i][j][e]));
+                }
+            }
+        }
+    }
+}
+
+template <int EPI>
+bool launch_big(const u16* A, const u16* W, int M, int N, int K, float* c, u16* out_bf, hipStream_t st) {
+    const int nspan = (EPI == EPI_SWIGLU) ? 128 : GB_N;
+    if (M < 256 || K % GB_K || N % nspan) return false;
+    const int tiles_m = (M + GB_M - 1) / GB_M, tiles_n = N / nspan;
+    // grid: a multiple of 8 so that tile t = (pid % 8) * (grid / 8) + pid / 8 covers every tile once
+    const int grid = (tiles_m * tiles_n + 7) / 8 * 8;
+    hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(grid), dim3(256), 0, st, A, W, M, N, K, c, out_bf, tiles_m,
+                       tiles_n);
+    return true;
+}
+
 template <int EPI>
 hipError_t launch_gemm(const u16* A, const u16* W, int M, int N, int K, float* c, u16* out_bf,
                        hipStream_t st) {
     if (M <= 16) {
         launch_skinny<EPI, false>(A, nullptr, nullptr, 0.f, W, M, N, K, c, out_bf, st);
-    } else {
+    } else if (!launch_big<EPI>(A, W, M, N, K, c, out_bf, st)) {
         const int bn = (EPI == EPI_SWIGLU) ? 64 : BN;
         dim3 grid((N + bn - 1) / bn, (M + BM - 1) / BM);
         hipLaunchKernelGGL((gemm_tiled_kernel<EPI>), grid, dim3(256), 0, st, A, W, M, N, K, c, out_bf);
