@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--prompt", type=int, default=None, help="override the prompt length")
     ap.add_argument("--base-bits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timer", action="store_true",
+                    help="replay the decode step as one graph with no timed kernel class")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 2 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -195,10 +197,13 @@ def main():
     dout = torch.empty(Bsz, s.d_model, dtype=torch.float32, device="cuda")
     # Decode runs on a dedicated stream (default priority): the library captures the
     # step as HIP graphs there during warmup and replays them, launching the timed
-    # attention kernel directly between two events.  The timer is on from the
-    # start; the read after warmup clears the warmup launches.
+    # attention kernel (one launch per step) directly between two events.  The timer
+    # is on from the start; the read after warmup clears the warmup launches.
     stream = torch.cuda.Stream()
-    B.lk_timing_enable(model.h, "attn_decode_dense")
+    B.lk_timing_enable(model.h, None if args.no_kernel_timer else "attn_decode_dense")
+    # time the first loop-1 attention launch of every step: every launch of a step has
+    # the same size, and one timed launch keeps the replayed step in two graphs
+    B.lk_timing_sample(model.h, 1)
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             model.decode(store, dec[i], out=dout)
@@ -219,6 +224,7 @@ def main():
     value = Bsz * args.steps / elapsed
 
     # roofline of the dominant kernel: loop-1 (dense) decode attention
+    n_class = s.n_prelude + s.n_coda + (s.n_shared if lz.mode == "lazy" else s.n_shared * s.n_loops)
     per_step_launches = launches / args.steps if args.steps else 0
     bytes_tot = sum(decode_attention_bytes(s, lz, Bsz, t_first + i) for i in range(args.steps)) \
         * per_step_launches
@@ -265,9 +271,10 @@ def main():
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.workload) if lz.mode == "lazy" and lz.base_bits == 8 else None,
-                     "launches": launches, "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "launches_timed": launches, "launches_per_step": n_class,
+                     "avg_launch_us": round(avg_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": int(bytes_per_launch),
-                     "share_of_step": round(kern_ms / (elapsed * 1e3), 4)},
+                     "share_of_step": round(avg_ms * n_class / ms_per_step, 4)},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)...")

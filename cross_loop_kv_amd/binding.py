@@ -82,6 +82,7 @@ _SIGS = {
     "lk_kv_store_force_selection": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
     "lk_kv_store_keep_codes": (C.c_int, [C.c_void_p, C.c_int32]),
     "lk_timing_enable": (C.c_int, [C.c_void_p, C.c_char_p]),
+    "lk_timing_sample": (C.c_int, [C.c_void_p, C.c_int32]),
     "lk_set_decode_graphs": (C.c_int, [C.c_void_p, C.c_int32]),
     "lk_decode_weight_bytes": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t)]),
     "lk_timing_read": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
@@ -211,6 +212,10 @@ def lk_decode_weight_bytes(h: int) -> int:
 
 def lk_set_decode_graphs(h: int, enable: bool) -> None:
     _check(lib().lk_set_decode_graphs(h, 1 if enable else 0))
+
+
+def lk_timing_sample(h: int, per_call: int) -> None:
+    _check(lib().lk_timing_sample(h, per_call))
 
 
 def lk_timing_enable(h: int, kernel_class: Optional[str]) -> None:

@@ -65,6 +65,8 @@ static const char* kTimedNames[TC_COUNT] = {"attn_decode_dense", "attn_decode_sp
 
 struct EventTimer {
     int cls = TC_NONE;
+    int per_call = 0;   // launches of the class timed per prefill / decode call (0: all)
+    int in_call = 0;    // launches of the class seen in the current call
     std::vector<hipEvent_t> pool;  // pairs (start, end), one per timed launch
     size_t used = 0;
     hipError_t mark(hipStream_t st) {
@@ -95,6 +97,7 @@ struct DecodeGraph {
     const void* ws = nullptr;
     hipStream_t stream = nullptr;
     int timer_cls = -2;
+    int timer_per_call = -1;
     int keep_codes = 0;
     void reset() {
         for (Seg& g : segs)
@@ -483,7 +486,8 @@ int cut_segment(lk_handle* h, hipStream_t st) {
 // of the step instead (`fn` captures its arguments by value).
 template <typename F>
 int timed(lk_handle* h, int cls, hipStream_t st, F fn) {
-    const bool on = h->timer.cls == cls;
+    bool on = h->timer.cls == cls;
+    if (on) on = h->timer.per_call == 0 || h->timer.in_call++ < h->timer.per_call;
     if (on && h->building) {
         LK_TRY(cut_segment(h, st));
         DecodeGraph::Seg seg;
@@ -799,6 +803,7 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
     const lk_model_cfg& c = h->c;
     const int P = c.n_prelude, R = c.n_shared, K = c.n_loops, Q = c.n_coda, d = c.d_model;
     const int M = B * T;
+    h->timer.in_call = 0;
     if (h->lazy())
         LK_HIP(lk::fill_i32(slot_map(s, 2), -1, (long long)(K - 1) * B * s->Tpad, st));
     s->t = 0;
@@ -962,6 +967,7 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
     const int P = c.n_prelude, R = c.n_shared, K = c.n_loops, Q = c.n_coda, d = c.d_model;
     const int B = s->B;
     const int32_t* dpos = dev_pos(s);
+    h->timer.in_call = 0;
     // The layer applications of one step, in order.
     struct App {
         int li;
@@ -1082,13 +1088,14 @@ int lk_looped_decode_step(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, fl
     if (st && h->use_graphs) {
         DecodeGraph& g = h->graph;
         if (g.store != s || g.ws != d_ws || g.stream != st || g.timer_cls != h->timer.cls ||
-            g.keep_codes != s->keep_codes) {
+            g.timer_per_call != h->timer.per_call || g.keep_codes != s->keep_codes) {
             g.reset();
             LK_TRY(capture_decode(h, s, w, st));
             g.store = s;
             g.ws = d_ws;
             g.stream = st;
             g.timer_cls = h->timer.cls;
+            g.timer_per_call = h->timer.per_call;
             g.keep_codes = s->keep_codes;
         }
         for (const DecodeGraph::Seg& seg : g.segs) {
@@ -1131,6 +1138,12 @@ int lk_timing_enable(lk_handle* h, const char* kernel_class) {
     }
     h->timer.used = 0;
     h->timer.cls = cls;
+    return LK_OK;
+}
+
+int lk_timing_sample(lk_handle* h, int32_t per_call) {
+    if (!h || per_call < 0) return fail(LK_ERR_INVALID_ARG, "null handle or negative count");
+    h->timer.per_call = per_call;
     return LK_OK;
 }
 

@@ -186,6 +186,10 @@ const char *lk_last_error(void);
  * "column_mass", "attn_prefill_sparse", "gemm_decode", "gemm_prefill"; NULL
  * disables.  Enabling clears the record.  Not thread-safe per handle. */
 int lk_timing_enable(lk_handle *h, const char *kernel_class);
+/* Time only the first per_call launches of the class in each prefill or decode
+ * call (0, the default: all of them).  Fewer timed launches cut the decode step
+ * into fewer replayed graphs. */
+int lk_timing_sample(lk_handle *h, int32_t per_call);
 /* Launches recorded since lk_timing_enable or the previous read, and their
  * summed event time in ms (waits for the recorded events; clears the record).
  * A replayed decode step launches its timed-class kernels directly between two
