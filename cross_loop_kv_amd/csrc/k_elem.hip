@@ -304,9 +304,14 @@ __global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, in
     const long long slot = w.slot_base + (w.dpos ? *w.dpos : 0) + iseq;
     const long long row = kv_row(L, b, g, pos);
     const long long idx = kv == 0 ? row * hd + e : v_elem(L, b, g, pos, e);
+    // decode: this row's reconstruction at the current loop, carried to the next loop
+    float* tr = w.tok_recon ? w.tok_recon + (((long long)b * 2 + kv) * Hkv + g) * hd + e : nullptr;
     if (w.kind == 0 || (w.kind == 1 && L.base_bits == 16)) {
-        ((u16*)L.base[kv])[idx] = f2bf(x);
+        const u16 xb = f2bf(x);
+        ((u16*)L.base[kv])[idx] = xb;
+        if (tr) *tr = bf2f(xb);
     } else if (w.kind == 1) {  // int8 base: residual against a zero reconstruction
+        float recon;
         if (!w.keep_codes) {
             u16 sb;
             const int c = quant_group32(x, 127, &sb);
@@ -315,7 +320,11 @@ __global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, in
                 const long long si = kv == 0 ? row * (hd / 32) + e / 32 : v_scale_idx(L, b, g, pos, e / 32);
                 ((u16*)L.base_scale[kv])[si] = sb;
             }
+            recon = (float)c * h2f(sb);
+        } else {
+            recon = tr ? kv_base_elem(L, kv, b, g, pos, e) : 0.f;
         }
+        if (tr) *tr = recon;
     } else {
         const long long rr = res_row(L, b, g, slot);
         float recon;  // the row's loop-k reconstruction
@@ -324,7 +333,7 @@ __global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, in
             ((u16*)L.res[w.loop - 2][kv])[rr * hd + e] = xb;
             recon = bf2f(xb);
         } else {
-            const float prev = kv_recon_elem(L, kv, b, g, pos, e, w.loop - 1);
+            const float prev = tr ? *tr : kv_recon_elem(L, kv, b, g, pos, e, w.loop - 1);
             if (!w.keep_codes) {
                 u16 sb;
                 const int qmax = (1 << (L.res_bits - 1)) - 1;
@@ -342,6 +351,7 @@ __global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, in
                 recon = kv_apply_res(L, kv, b, g, w.loop, (int)slot, e, prev);
             }
         }
+        if (tr) *tr = recon;
         if (w.ring_on) {
             const KVLayer& Rg = w.ring;
             const int rp = pos % Rg.Tmax;

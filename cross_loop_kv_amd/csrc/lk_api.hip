@@ -353,6 +353,7 @@ struct WS {
     int32_t* ids;      // decode: the step's token ids (fixed address for graph replay)
     float* out;        // decode: the step's output rows
     float* ps;         // decode: per-workgroup row sums of x^2 for the next RMSNorm ([d/8][8])
+    float* tokrec;     // decode, lazy: float32 K/V reconstruction of the step's rows [R][B][2][Hkv][hd]
     size_t total;
     long long part_floats;
 };
@@ -396,6 +397,7 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
     w.part = (float*)take(pf * 4);
     w.ids = (int32_t*)take((long long)B * 4);
     w.ps = (float*)take((d / 8 + 1) * 8 * 4);
+    w.tokrec = (float*)take(hd_->lazy() && T == 1 ? (long long)c.n_shared * B * 2 * c.n_kv_heads * c.head_dim * 4 : 0);
     w.out = (float*)take((long long)B * d * 4);
     w.total = off;
     return w;
@@ -1001,6 +1003,7 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
             lk::KVWrite kw{};
             kw.layer = ap.read;
             kw.keep_codes = s->keep_codes;
+            kw.tok_recon = w.tokrec + (long long)r * B * 2 * c.n_kv_heads * c.head_dim;
             if (k == 1) {
                 ap.kind = ATTN_ROWS_DENSE;
                 ap.k_loop = 1;

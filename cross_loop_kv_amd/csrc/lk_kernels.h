@@ -51,6 +51,10 @@ struct KVWrite {
     // window ring (plain rows, position p at row p % ring.Tmax), when ring_on != 0.
     KVLayer ring;
     int ring_on;
+    // decode (kinds 1 and 2): float32 [B][2][Hkv][hd] reconstruction of the row at the
+    // previous loop of this layer (read by kind 2) and at this loop (written), in place
+    // of re-reading base + residuals through the slot maps.
+    float* tok_recon;
 };
 hipError_t rope_kv_write(const float* qkv, int rows, int rows_per_seq, const int32_t* pos,
                          int pos_offset, int H, int Hkv, int hd, const double* inv_freq, u16* q_out,
