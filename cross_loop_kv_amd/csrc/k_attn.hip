@@ -392,13 +392,18 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
     auto row_of = [&](int key) { return seg2 ? (ring0 + key) % kv.Tmax : key; };
     const float sl2 = kLog2e / sqrtf((float)HD);
 
-    // Q^T operand: lane (head c16, kgrp) holds q[h][32j + 8kgrp .. +8]
+    // int8 rows (hd >= 64): lane (key, kgrp) reads 16 bytes at 64h + 16 kgrp of its K row
+    // for h < NQ / 2, so every load covers 64 contiguous bytes of each key; k-step j
+    // takes elements 64 (j/2) + 16 kgrp + 8 (j%2) .. +8.  Other rows: 32 j + 8 kgrp.
+    constexpr bool KPERM = I8 && NQ % 2 == 0;
+    auto kslice = [&](int j) { return KPERM ? 64 * (j >> 1) + 16 * kgrp + 8 * (j & 1) : 32 * j + 8 * kgrp; };
+    // Q^T operand: lane (head c16, kgrp) holds q[h][kslice(j) .. +8]
     uint4 qop[NQ];
     const bool hvalid = c16 < G;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (hvalid) v = *(const uint4*)(a.q + (long long)b * a.H * HD + (g * G + c16) * HD + 32 * j + 8 * kgrp);
+        if (hvalid) v = *(const uint4*)(a.q + (long long)b * a.H * HD + (g * G + c16) * HD + kslice(j));
         if (HALF) {  // bf16 -> f16
             const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
             uint32_t o[4];
@@ -416,14 +421,52 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
     float m = -INFINITY, l = 0.f;
 
     for (int kb = c_begin + 32 * w; kb < c_end; kb += 128) {
+        // V operands of the tile are loaded first, so that K and V are in flight together.
+        // int8 V: one 16-byte load per pair of O^T tiles; tile et's row r is head dim
+        // vdim(et, r) = 32 (et/2) + 2 r + et%2 (the 8 keys of dims e and e + 1 are adjacent)
+        const int pos0 = row_of(min(kb + 8 * kgrp, ((c_end - 1) >> 3) << 3));
+        uint4 vraw[I8 ? NE / 2 : NE], vsc[I8 ? NE / 2 : 1];
+        if (I8) {
+#pragma unroll
+            for (int pp = 0; pp < NE / 2; ++pp) {
+                vraw[pp] = *(const uint4*)((const int8_t*)kv.base[1] + v_elem(kv, b, g, pos0, 32 * pp + 2 * c16));
+                vsc[pp] = *(const uint4*)(kv.base_scale[1] + v_scale_idx(kv, b, g, pos0, pp));
+            }
+        } else {
+#pragma unroll
+            for (int et = 0; et < NE; ++et) vraw[et] = *(const uint4*)((const u16*)kv.base[1] + v_elem(kv, b, g, pos0, 16 * et + c16));
+        }
         // ---- S^T = K Q^T: n-tile nt covers keys kb + 8*(r/4) + 4*nt + r%4 for row r
         f32x4 sacc[2];
+        long long krow[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+            krow[nt] = kv_row(kv, b, g, row_of(min(kb + 8 * (c16 >> 2) + 4 * nt + (c16 & 3), c_end - 1)));
+        uint4 kraw[2][KPERM ? NQ / 2 : 1];
+        uint32_t kscl[2][KPERM ? NQ / 2 : 1];
+        if (KPERM) {  // all K codes and scales of the tile first
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int hh = 0; hh < NQ / 2; ++hh) {
+                    kraw[nt][hh] = *(const uint4*)((const int8_t*)kv.base[0] + krow[nt] * HD + 64 * hh + 16 * kgrp);
+                    kscl[nt][hh] = kv.base_scale[0][krow[nt] * NQ + 2 * hh + (kgrp >> 1)];
+                }
+        }
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            const int key = min(kb + 8 * (c16 >> 2) + 4 * nt + (c16 & 3), c_end - 1);
-            const long long row = kv_row(kv, b, g, row_of(key));
+            const long long row = krow[nt];
             sacc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            if (I8) {
+            if (KPERM) {
+#pragma unroll
+                for (int j = 0; j < NQ; ++j) {
+                    const uint4 c4 = kraw[nt][j >> 1];
+                    const uint2 c = (j & 1) ? make_uint2(c4.z, c4.w) : make_uint2(c4.x, c4.y);
+                    const uint32_t sp = kscl[nt][j >> 1] | (kscl[nt][j >> 1] << 16);
+                    const uint4 kf = i8x8_to_f16(c, make_uint4(sp, sp, sp, sp));
+                    sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kf), as_half8(qop[j]), sacc[nt], 0, 0, 0);
+                }
+            } else if (I8) {
                 const u16* ks = kv.base_scale[0] + row * NQ;
 #pragma unroll
                 for (int j = 0; j < NQ; ++j) {
@@ -488,28 +531,15 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
         }
         const int valid = c_end - (kb + 8 * kgrp);
         // rows past the end of the context are unwritten: clamp the block address, zero the values
-        const int pos0 = row_of(min(kb + 8 * kgrp, ((c_end - 1) >> 3) << 3));
-        // int8 V: one 16-byte load per pair of O^T tiles; tile et's row r is head dim
-        // vdim(et, r) = 32 (et/2) + 2 r + et%2 (the 8 keys of dims e and e + 1 are adjacent)
-        uint4 vpair[NE / 2], vsc[NE / 2];
-        if (I8) {
-#pragma unroll
-            for (int pp = 0; pp < NE / 2; ++pp) {
-                vpair[pp] = *(const uint4*)((const int8_t*)kv.base[1] + v_elem(kv, b, g, pos0, 32 * pp + 2 * c16));
-                vsc[pp] = *(const uint4*)(kv.base_scale[1] + v_scale_idx(kv, b, g, pos0, pp));
-            }
-        }
 #pragma unroll
         for (int et = 0; et < NE; ++et) {
-            const int e = 16 * et + c16;
             uint4 vf;
             if (I8) {
-                const uint4 c4 = vpair[et >> 1];
+                const uint4 c4 = vraw[et >> 1];
                 const uint2 c = (et & 1) ? make_uint2(c4.z, c4.w) : make_uint2(c4.x, c4.y);
                 vf = i8x8_to_f16(c, vsc[et >> 1]);
             } else {
-                const long long vi = v_elem(kv, b, g, pos0, e);
-                vf = *(const uint4*)((const u16*)kv.base[1] + vi);
+                vf = vraw[et];
             }
             vf = mask_tail8(vf, valid);
             if (HALF)
