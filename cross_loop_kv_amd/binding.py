@@ -92,6 +92,8 @@ _SIGS = {
     "lk_dbg_delta": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
     "lk_dbg_gemm": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
                               C.c_void_p]),
+    "lk_dbg_gemm_epi": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32,
+                                  C.c_int32, C.c_int32, C.c_void_p]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -242,6 +244,10 @@ def lk_dbg_delta(d_a, d_b, rows, d, d_key, stream=None) -> None:
 
 def lk_dbg_gemm(d_a, d_w, d_c, M, N, K, stream=None) -> None:
     _check(lib().lk_dbg_gemm(d_a, d_w, d_c, M, N, K, _stream(stream)))
+
+
+def lk_dbg_gemm_epi(d_a, d_w, epi, d_c, d_out, M, N, K, stream=None) -> None:
+    _check(lib().lk_dbg_gemm_epi(d_a, d_w, epi, d_c, d_out, M, N, K, _stream(stream)))
 
 
 # ---- model / store objects (device memory from torch) ----------------------------------

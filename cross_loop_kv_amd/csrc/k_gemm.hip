@@ -5,7 +5,9 @@
 // reach these kernels.  C = A[M, K] * W[N, K]^T with bf16 operands and fp32
 // accumulation; epilogues fuse the residual add, SwiGLU and GELU.
 //
-// * Tiled kernel (M > 16): 128 x 128 x 32 tiles, 4 waves each owning 64 x 64 as
+// * Big-tile kernel (M >= 256, K % 128 == 0, N % 256 == 0): 256 x 256 x 64 tiles fed
+//   by buffer loads straight into LDS; described at the kernel.
+// * Tiled kernel (other M > 16): 128 x 128 x 32 tiles, 4 waves each owning 64 x 64 as
 //   2 x 2 v_mfma_f32_32x32x16_bf16 tiles, LDS double buffering with one barrier
 //   per k-step, rows padded to 80 bytes so the 16-byte operand reads of a wave
 //   spread over the LDS banks.
@@ -401,23 +403,24 @@ void launch_skinny(const u16* A, const float* X, const u16* gain, float eps, con
 
 
 // ---------------------------------------------------------------- big-tile kernel
-// 256 x 256 x 32 workgroup tiles, 4 waves as 2 x 2, each wave 128 x 128 as 4 x 4
-// v_mfma_f32_32x32x16_bf16 tiles (256 accumulator registers per lane, one wave per
-// SIMD).  Operands reach LDS by global_load_lds (16 bytes per lane, no register
-// staging) into four LDS stages, three k-tiles ahead of the MFMAs.  Each stage is its
-// own LDS array, so the compiler can tell the stages apart and waits only for the tile
-// it reads (explicit vmcnt waits + a bare barrier per k-tile).  Within a row of 32
-// bf16 (four 16-byte chunks) chunk c of row r sits at slot c ^ ((r / 4) % 4), so the
-// rows read by eight consecutive lanes land in distinct banks.  Tiles go to workgroups
-// XCD by XCD, grouped 8 M-tiles tall.  SwiGLU: the 256 W rows of a tile are
-// [gate 0..63 | up 0..63 | gate 64..127 | up 64..127] of 128 output columns, so each
-// wave holds gate and up of its 64 output columns.
-// Requires K % 32 == 0 and N % 256 == 0 (SwiGLU: N % 128 == 0).
-constexpr int GB_M = 256, GB_N = 256, GB_K = 32, GB_STAGE = (GB_M + GB_N) * GB_K;
+// 256 x 256 workgroup tiles stepped 64 deep in k, 4 waves as 2 x 2, each wave 128 x 128
+// as 4 x 4 v_mfma_f32_32x32x16_bf16 tiles (256 accumulators per lane, one wave per SIMD).
+// Operands reach LDS by buffer loads with the LDS bit (16 bytes per lane, no register
+// staging): a tile row is 64 bf16 = one 128-byte line, one load instruction moves 8
+// whole rows, and the k offset rides in the scalar offset, so a load costs one M0 move.
+// Two LDS stages of 64 KB: the next slab streams in while the current one is consumed.
+// Within a stage, 16-byte chunk c of row r sits at slot c ^ (r % 8), so the rows read by
+// eight consecutive lanes land in distinct banks.  The k loop is unrolled over the two
+// stages (stage indices are compile-time, which keeps the compiler's LDS-DMA tracking
+// exact), the LDS reads of the next k-slice are interleaved with the MFMAs of the
+// current one, and there is one barrier per slab.  Tiles go to workgroups XCD by XCD,
+// grouped 8 M-tiles tall.  Rows past M load as zeros (buffer range check).  SwiGLU: the
+// 256 W rows of a tile are [gate 0..63 | up 0..63 | gate 64..127 | up 64..127] of 128
+// output columns, so each wave holds gate and up of its 64 output columns.
+// Requires K % 128 == 0 and N % 256 == 0 (SwiGLU: N % 128 == 0).
+constexpr int GB_M = 256, GB_N = 256, GB_K = 64, GB_STAGE = (GB_M + GB_N) * GB_K;
 __shared__ __attribute__((aligned(1024))) u16 gb_s0[GB_STAGE];
 __shared__ __attribute__((aligned(1024))) u16 gb_s1[GB_STAGE];
-__shared__ __attribute__((aligned(1024))) u16 gb_s2[GB_STAGE];
-__shared__ __attribute__((aligned(1024))) u16 gb_s3[GB_STAGE];
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int N>
@@ -429,40 +432,91 @@ __device__ __forceinline__ void bare_barrier() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
-__device__ __forceinline__ int gb_swz(int r) { return (r >> 2) & 3; }
+template <int U>
+__device__ __forceinline__ u16* gb_stage() { return U == 0 ? gb_s0 : gb_s1; }
 
-// One k-tile into stage `st`: wave w issues loads w, w+4, w+8, w+12 of A and of B (each
-// load = 16 rows x 64 bytes = 1 KB of LDS).
-__device__ __forceinline__ void gb_issue(u16* st, const u16* const* ga, const u16* const* gb, int k0, int w) {
+// Buffer resources of the A and W rows of one tile and this lane's byte offsets.
+struct GbSrc {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    uint32_t va[8], vb[8];
+};
+
+// One 64-deep slab into a stage: wave ws moves 1 KB blocks ws + 4q of A and of W.
+__device__ __forceinline__ void gb_issue(u16* st, const GbSrc& d, int k0, int ws) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-        __builtin_amdgcn_global_load_lds((const void*)(ga[p] + k0), (lds_void*)(st + (w + 4 * p) * 512), 16, 0, 0);
+    for (int q = 0; q < 8; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_void*)(st + (ws + 4 * q) * 512), 16, d.va[q], k0 * 2, 0, 0);
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-        __builtin_amdgcn_global_load_lds((const void*)(gb[p] + k0), (lds_void*)(st + GB_M * GB_K + (w + 4 * p) * 512),
-                                         16, 0, 0);
+    for (int q = 0; q < 8; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rb, (lds_void*)(st + GB_M * GB_K + (ws + 4 * q) * 512), 16, d.vb[q],
+                                                 k0 * 2, 0, 0);
+}
+// Operands of k-slice c (chunk index 0..7 = 16-element group incl. the lane's k half).
+__device__ __forceinline__ void gb_read(const u16* st, bf16x8 (&fa)[4], bf16x8 (&fb)[4], int wm, int wn, int l32,
+                                        int c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = wm * 128 + 32 * i + l32;
+        fa[i] = as_bf16x8(*(const uint4*)(st + r * GB_K + ((c ^ (r & 7)) * 8)));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = wn * 128 + 32 * j + l32;
+        fb[j] = as_bf16x8(*(const uint4*)(st + GB_M * GB_K + r * GB_K + ((c ^ (r & 7)) * 8)));
+    }
+}
+__device__ __forceinline__ void gb_mma(f32x16 (&acc)[4][4], const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+}
+// scheduling: one LDS read after each of the first eight MFMAs of a group
+__device__ __forceinline__ void gb_sched_reads() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 }
 
-__device__ __forceinline__ void gb_compute(const u16* st, f32x16 (&acc)[4][4], int wm, int wn, int l32, int kg) {
+// One slab in stage U.  On entry x holds k-slice 0 of the slab.  NEXT: another slab
+// follows (wait for it, barrier, read its k-slice 0 into x); DMA: refill stage U with
+// the slab after next once every wave is past the barrier.
+template <int U, bool NEXT, bool DMA>
+__device__ __forceinline__ void gb_slab(f32x16 (&acc)[4][4], bf16x8 (&xa)[4], bf16x8 (&xb)[4], bf16x8 (&ya)[4],
+                                        bf16x8 (&yb)[4], const GbSrc& src, int s, int ws, int wm, int wn, int l32,
+                                        int kg) {
+    gb_read(gb_stage<U>(), ya, yb, wm, wn, l32, 2 + kg);
+    gb_mma(acc, xa, xb);
+    gb_sched_reads();
+    gb_read(gb_stage<U>(), xa, xb, wm, wn, l32, 4 + kg);
+    gb_mma(acc, ya, yb);
+    gb_sched_reads();
+    gb_read(gb_stage<U>(), ya, yb, wm, wn, l32, 6 + kg);
+    gb_mma(acc, xa, xb);
+    gb_sched_reads();
+    if (NEXT) {
+        wait_vmcnt<0>();  // this wave's part of slab s + 1 is in LDS
+        bare_barrier();   // ... and every wave's; every wave is done reading stage U
+        if (DMA) gb_issue(gb_stage<U>(), src, (s + 2) * GB_K, ws);
+        gb_read(gb_stage<U ^ 1>(), xa, xb, wm, wn, l32, kg);
+    }
+    gb_mma(acc, ya, yb);
+    if (NEXT) {
+        if (DMA) {
 #pragma unroll
-    for (int ks = 0; ks < GB_K / 16; ++ks) {
-        const int kc = 2 * ks + kg;
-        bf16x8 a[4], b[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wm * 128 + 32 * i + l32;
-            a[i] = as_bf16x8(*(const uint4*)(st + r * GB_K + ((kc ^ gb_swz(r)) * 8)));
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // buffer loads
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        } else {
+            gb_sched_reads();
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = wn * 128 + 32 * j + l32;
-            b[j] = as_bf16x8(*(const uint4*)(st + GB_M * GB_K + r * GB_K + ((kc ^ gb_swz(r)) * 8)));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
 }
 
@@ -471,9 +525,9 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const u16* __restrict_
                                                           int M, int N, int K, float* __restrict__ C,
                                                           u16* __restrict__ Obf, int tiles_m, int tiles_n) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
-    constexpr int STAGES = 4;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1, l32 = lane & 31, kg = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int ws = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = ws >> 1, wn = ws & 1, l32 = lane & 31, kg = lane >> 5;
     // tile order: XCD-major (grid is a multiple of 8), then groups of 8 M-tiles
     const int ntiles = tiles_m * tiles_n;
     const int per_xcd = gridDim.x / 8;
@@ -486,21 +540,23 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const u16* __restrict_
     const int tm = first_m + (t % group_size) % gm;
     const int tn = (t % group_size) / gm;
     const int row0 = tm * GB_M;
-    const u16* ga[4];
-    const u16* gb[4];
+    GbSrc src;
+    src.ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long long)row0 * K), (short)0,
+                                               min(M - row0, GB_M) * K * 2, 0x00020000);
+    const long long wrow0 = DUAL ? (long long)tn * 128 : (long long)tn * GB_N;
+    const int wspan = DUAL ? N + 128 : GB_N;  // W rows the tile reaches from wrow0
+    src.rb = __builtin_amdgcn_make_buffer_rsrc((void*)(W + wrow0 * K), (short)0, wspan * K * 2, 0x00020000);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int r = (w + 4 * p) * 16 + lane / 4;  // tile row of this lane's 16 bytes
-        const int kc = (lane % 4) ^ gb_swz(r);      // the chunk that lands in slot lane % 4
-        ga[p] = A + (long long)min(row0 + r, M - 1) * K + kc * 8;
-        int wr;
+    for (int q = 0; q < 8; ++q) {
+        const int r = 8 * (ws + 4 * q) + lane / 8;  // tile row of this lane's 16 bytes
+        const int c = (lane % 8) ^ (r & 7);         // the chunk that lands in slot lane % 8
+        src.va[q] = (uint32_t)(r * K * 2 + c * 16);
+        int wr = r;
         if (DUAL) {
-            const int q = r >> 6;  // 0: gate lo, 1: up lo, 2: gate hi, 3: up hi
-            wr = ((q & 1) ? N : 0) + tn * 128 + (q >> 1) * 64 + (r & 63);
-        } else {
-            wr = tn * GB_N + r;
+            const int h = r >> 6;  // 0: gate lo, 1: up lo, 2: gate hi, 3: up hi
+            wr = ((h & 1) ? N : 0) + (h >> 1) * 64 + (r & 63);
         }
-        gb[p] = W + (long long)wr * K + kc * 8;
+        src.vb[q] = (uint32_t)(wr * K * 2 + c * 16);
     }
     f32x16 acc[4][4];
 #pragma unroll
@@ -509,28 +565,20 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const u16* __restrict_
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    u16* const bufs[STAGES] = {gb_s0, gb_s1, gb_s2, gb_s3};
-    const int nk = K / GB_K;
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk) gb_issue(bufs[s], ga, gb, s * GB_K, w);
-    for (int kt = 0; kt < nk; ++kt) {
-        // k-tile kt has landed once at most (tiles issued after it) x 8 loads remain
-        const int ahead = min(nk - 1 - kt, STAGES - 2);
-        if (ahead >= 2) wait_vmcnt<16>();
-        else if (ahead == 1) wait_vmcnt<8>();
-        else wait_vmcnt<0>();
-        bare_barrier();  // every wave's part of tile kt is in; stage (kt - 1) is free
-        const int nx = kt + STAGES - 1;
-        const int sc = kt % STAGES;
-#pragma unroll
-        for (int s = 0; s < STAGES; ++s) {
-            if (sc == s) {
-                if (nx < nk) gb_issue(bufs[(s + STAGES - 1) % STAGES], ga, gb, nx * GB_K, w);
-                gb_compute(bufs[s], acc, wm, wn, l32, kg);
-            }
-        }
+    const int ns = K / GB_K;  // even, >= 2
+    gb_issue(gb_s0, src, 0, ws);
+    gb_issue(gb_s1, src, GB_K, ws);
+    wait_vmcnt<16>();
+    bare_barrier();
+    bf16x8 xa[4], xb[4], ya[4], yb[4];
+    gb_read(gb_s0, xa, xb, wm, wn, l32, kg);
+    int s = 0;
+    for (; s < ns - 2; s += 2) {
+        gb_slab<0, true, true>(acc, xa, xb, ya, yb, src, s, ws, wm, wn, l32, kg);
+        gb_slab<1, true, true>(acc, xa, xb, ya, yb, src, s + 1, ws, wm, wn, l32, kg);
     }
+    gb_slab<0, true, false>(acc, xa, xb, ya, yb, src, s, ws, wm, wn, l32, kg);
+    gb_slab<1, false, false>(acc, xa, xb, ya, yb, src, s + 1, ws, wm, wn, l32, kg);
     // epilogue: acc[i][j][e] = C[row0 + wm*128 + 32 i + 8 (e/4) + 4 kg + e%4][col(j) + l32]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -561,7 +609,10 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const u16* __restrict_
 template <int EPI>
 bool launch_big(const u16* A, const u16* W, int M, int N, int K, float* c, u16* out_bf, hipStream_t st) {
     const int nspan = (EPI == EPI_SWIGLU) ? 128 : GB_N;
-    if (M < 256 || K % GB_K || N % nspan) return false;
+    if (M < 256 || K % (2 * GB_K) || N % nspan) return false;
+    // buffer offsets and ranges are 32-bit: the rows one tile reaches must stay below 2 GiB
+    const long long wspan = (EPI == EPI_SWIGLU) ? (long long)N + 128 : GB_N;
+    if (wspan * K * 2 >= (1LL << 31) || (long long)GB_M * K * 2 >= (1LL << 31)) return false;
     const int tiles_m = (M + GB_M - 1) / GB_M, tiles_n = N / nspan;
     // grid: a multiple of 8 so that tile t = (pid % 8) * (grid / 8) + pid / 8 covers every tile once
     const int grid = (tiles_m * tiles_n + 7) / 8 * 8;

@@ -1198,4 +1198,15 @@ int lk_dbg_gemm(const void* d_a, const void* d_w, float* d_c, int32_t M, int32_t
     return LK_OK;
 }
 
+int lk_dbg_gemm_epi(const void* d_a, const void* d_w, int32_t epi, float* d_c, void* d_out, int32_t M, int32_t N,
+                    int32_t K, void* stream) {
+    if (!d_a || !d_w) return fail(LK_ERR_INVALID_ARG, "null argument");
+    if (epi < lk::EPI_STORE || epi > lk::EPI_GELU) return fail(LK_ERR_INVALID_ARG, "epi must be 0..3");
+    if (epi <= lk::EPI_ADD ? !d_c : !d_out) return fail(LK_ERR_INVALID_ARG, "null output for this epilogue");
+    if (M < 1 || N < 16 || N % 16 || K < 32 || K % 32)
+        return fail(LK_ERR_INVALID_ARG, "need M >= 1, N a multiple of 16, K a multiple of 32");
+    LK_HIP(lk::gemm((const u16*)d_a, (const u16*)d_w, M, N, K, epi, d_c, (u16*)d_out, (hipStream_t)stream));
+    return LK_OK;
+}
+
 }  // extern "C"

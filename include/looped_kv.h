@@ -250,6 +250,17 @@ int lk_dbg_delta(const float *d_a, const float *d_b, int32_t rows, int32_t d, fl
 int lk_dbg_gemm(const void *d_a, const void *d_w, float *d_c, int32_t M, int32_t N, int32_t K,
                 void *stream);
 
+/* The same product with one of the fused epilogues of the projections:
+ *   epi 0 (store):  d_c float32 [M, N] = A W^T;
+ *   epi 1 (add):    d_c float32 [M, N] += A W^T (the residual-stream update);
+ *   epi 2 (SwiGLU): W bf16 [2N, K] = [gate rows; up rows],
+ *                   d_out bf16 [M, N] = silu(A Wg^T) * (A Wu^T);
+ *   epi 3 (GELU):   d_out bf16 [M, N] = gelu(A W^T) with the exact erf form.
+ * d_c is used by epi 0 and 1, d_out by epi 2 and 3 (the other may be NULL).
+ * Same size rules as lk_dbg_gemm. */
+int lk_dbg_gemm_epi(const void *d_a, const void *d_w, int32_t epi, float *d_c, void *d_out,
+                    int32_t M, int32_t N, int32_t K, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -4,6 +4,8 @@ Bit-exact: the top-n selector (indices) and the residual quantizer (codes and
 float16 scales) against the oracle on identical float32 inputs.  Tolerance:
 delta keys and the bf16 GEMM against float32/float64 references.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -91,6 +93,40 @@ def test_gemm_against_float64(M, N, K):
     torch.cuda.synchronize()
     ref = a.double() @ w.double().T
     assert max_abs_rel(c.cpu().numpy(), ref.numpy()) < 1e-4
+
+
+@pytest.mark.parametrize("epi", [0, 1, 2, 3])
+@pytest.mark.parametrize("M,N,K", [(513, 1024, 2048), (256, 256, 5632), (300, 192, 64), (8, 256, 128)])
+def test_gemm_epilogues_against_float64(epi, M, N, K):
+    """Fused epilogues (store, residual add, SwiGLU, exact-erf GELU) on the big-tile path
+    (M >= 256, K % 128 == 0), the tiled path and the decode path, against float64."""
+    rng = np.random.default_rng(epi * 131 + M + N)
+    rows = 2 * N if epi == 2 else N
+    a = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((rng.standard_normal((rows, K)) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    c0 = rng.standard_normal((M, N)).astype(np.float32)
+    log(f"gemm epi={epi} M={M} N={N} K={K}")
+    d_a, d_w = a.cuda(), w.cuda()
+    d_c = torch.from_numpy(c0).cuda()
+    d_o = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    B.lk_dbg_gemm_epi(d_a.data_ptr(), d_w.data_ptr(), epi, d_c.data_ptr(), d_o.data_ptr(), M, N, K)
+    torch.cuda.synchronize()
+    p = a.double() @ w.double().T
+    if epi == 0:
+        assert max_abs_rel(d_c.cpu().numpy(), p.numpy()) < 1e-4
+    elif epi == 1:
+        ref = c0.astype(np.float64) + p.numpy()
+        assert max_abs_rel(d_c.cpu().numpy(), ref) < 1e-4
+    else:
+        if epi == 2:
+            g, u = p[:, :N].numpy(), p[:, N:].numpy()
+            ref = g / (1.0 + np.exp(-g)) * u
+        else:
+            x = p.numpy()
+            ref = 0.5 * x * (1.0 + np.vectorize(math.erf)(x / math.sqrt(2.0)))
+        out = d_o.float().cpu().numpy().astype(np.float64)
+        # bf16 output: half an ulp (2^-9 relative) plus the fp32 accumulation error
+        assert np.all(np.abs(out - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max())
 
 
 def test_entry_points_reject_bad_sizes():
