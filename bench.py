@@ -47,7 +47,74 @@ def parse():
                     help="replay the decode step as one graph with no timed kernel class")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 2 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--no-drift", action="store_true",
+                    help="skip the lazy-versus-dense drift comparison")
+    ap.add_argument("--drift-batch", type=int, default=2,
+                    help="sequences of the prompt compared lazy versus dense (full context)")
+    ap.add_argument("--drift-steps", type=int, default=8)
     return ap.parse_args()
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def kept_rows(rho, T):
+    """Tokens recomputed per sequence at loops k >= 2: ceil(rho T) clamped to [1, T]."""
+    return max(1, min(T, math.ceil(rho * T - 1e-9)))
+
+
+def prefill_gemm_flops(shape, lazy, batch, T):
+    """Algorithmic flops of the projection GEMMs (QKV, O, FFN in and out) of one prefill:
+    every layer application multiplies its rows by the four weight matrices; prelude,
+    coda and dense loops run all B*T rows, lazy loops k >= 2 only the kept rows."""
+    s = shape
+    qkv_w = (s.n_heads + 2 * s.n_kv_heads) * s.head_dim
+    fin = 2 if s.ffn_act == "swiglu" else 1
+    per_row = 2 * (qkv_w * s.d_model + s.d_model * s.n_heads * s.head_dim
+                   + fin * s.ffn_dim * s.d_model + s.d_model * s.ffn_dim)
+    if lazy.mode == "lazy":
+        dense_apps = s.n_prelude + s.n_coda + s.n_shared
+        sparse_rows = batch * kept_rows(lazy.rho, T) * s.n_shared * (s.n_loops - 1)
+    else:
+        dense_apps = s.n_prelude + s.n_coda + s.n_shared * s.n_loops
+        sparse_rows = 0
+    return per_row * (batch * T * dense_apps + sparse_rows)
+
+
+def drift_stats(a, b):
+    """Lazy output a against the dense reference b (final-normed hidden states, last dim
+    d): max |a - b| / max |b|, mean per-token cosine similarity, relative L2."""
+    import torch
+    a64, b64 = a.double(), b.double()
+    d = a64.shape[-1]
+    cos = torch.nn.functional.cosine_similarity(a64.reshape(-1, d), b64.reshape(-1, d), dim=1)
+    return {"max_abs_rel": float((a64 - b64).abs().max() / b64.abs().max()),
+            "mean_cos": float(cos.mean()),
+            "rel_l2": float((a64 - b64).norm() / b64.norm())}
+
+
+def measure_drift(model, wl, ids, dec, nb, steps):
+    """Prefill the first nb sequences of the prompt at full context and decode `steps`
+    tokens, once with the lazy model and once with the dense per-loop model over the same
+    weights; compare the outputs."""
+    import torch
+    from cross_loop_kv_amd import inputs as I
+    T = ids.shape[1]
+    dense = model.sibling(I.Lazy(mode="per_loop"))
+    outs = {}
+    for name, m in (("lazy", model), ("dense", dense)):
+        st = m.store(nb, T, T + steps)
+        p = m.prefill(st, ids[:nb])
+        d = [m.decode(st, dec[i][:nb]).clone() for i in range(steps)]
+        torch.cuda.synchronize()
+        outs[name] = (p, torch.stack(d, 1) if d else None)
+        del st
+    dense.close()
+    res = {"vs": "per_loop (dense looped inference over the same weights)", "batch": nb, "context": T,
+           "decode_steps": steps, "prefill_out": drift_stats(outs["lazy"][0], outs["dense"][0])}
+    if steps:
+        res["decode_out"] = drift_stats(outs["lazy"][1], outs["dense"][1])
+    return res
 
 
 def decode_attention_bytes(shape, lazy, batch, t):
@@ -186,13 +253,19 @@ def main():
     ids = torch.from_numpy(I.gen_prompt_ids(s, Bsz, T)).cuda()
     dec = torch.from_numpy(I.gen_decode_ids(s, Bsz, args.warmup + args.steps)).cuda()
     torch.cuda.synchronize()
+    # every projection GEMM of the prefill runs between two HIP events
+    B.lk_timing_enable(model.h, "gemm_prefill")
+    B.lk_timing_sample(model.h, 0)
     t0 = time.time()
     out = model.prefill(store, ids)
     torch.cuda.synchronize()
     prefill_s = time.time() - t0
+    g_launches, g_ms = B.lk_timing_read(model.h)
     assert torch.isfinite(out).all().item(), "non-finite prefill output"
     del out
-    log(f"prefill {Bsz}x{T}: {prefill_s:.2f}s")
+    log(f"prefill {Bsz}x{T}: {prefill_s:.2f}s (projection GEMMs {g_ms / 1e3:.2f}s over {g_launches} launches)")
+    g_flops = prefill_gemm_flops(s, lz, Bsz, T)
+    g_tflops = g_flops / (g_ms * 1e-3) / 1e12 if g_ms > 0 else 0.0
 
     dout = torch.empty(Bsz, s.d_model, dtype=torch.float32, device="cuda")
     # Decode runs on a dedicated stream (default priority): the library captures the
@@ -276,6 +349,15 @@ def main():
                      "algorithmic_bytes_per_launch": int(bytes_per_launch),
                      "share_of_step": round(avg_ms * n_class / ms_per_step, 4)},
     }
+    res["roofline_gemm"] = {
+        "kernel": "gemm_big_kernel (prefill QKV, O, gate/up, down)", "bound": "mfma",
+        "achieved": round(g_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(g_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "launches_timed": g_launches,
+        "algorithmic_flops": int(g_flops), "time_ms": round(g_ms, 2)}
+    if not args.no_drift:
+        del store
+        log(f"drift: lazy vs dense per-loop, {args.drift_batch} sequences at context {T}...")
+        res["drift"] = measure_drift(model, wl, ids, dec, min(args.drift_batch, Bsz), args.drift_steps)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)...")
         res["cpu_baseline"] = cpu_baseline(wl)

@@ -368,6 +368,19 @@ class LoopedModel:
         self._ws = None
         self._ws_bytes = 0
 
+    def sibling(self, lazy) -> "LoopedModel":
+        """A second handle over the same device weights with another lazy configuration
+        (e.g. the dense per-loop reference of a lazy model).  Keeps this model alive."""
+        m = object.__new__(LoopedModel)
+        m.shape, m.lazy, m.device = self.shape, lazy, self.device
+        m.t, m.layers, m._lw, m._w, m._cfg = self.t, self.layers, self._lw, self._w, self._cfg
+        m._parent = self
+        m._lz = lazy_cfg(lazy)
+        m.h = lk_create(m._cfg, m._lz, m._w)
+        m._ws = None
+        m._ws_bytes = 0
+        return m
+
     def weight_bytes(self) -> int:
         tot = sum(t.numel() * t.element_size() for t in self.t.values())
         for L in self.layers:

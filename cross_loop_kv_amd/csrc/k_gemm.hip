@@ -580,6 +580,29 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const u16* __restrict_
     gb_slab<0, true, false>(acc, xa, xb, ya, yb, src, s, ws, wm, wn, l32, kg);
     gb_slab<1, false, false>(acc, xa, xb, ya, yb, src, s + 1, ws, wm, wn, l32, kg);
     // epilogue: acc[i][j][e] = C[row0 + wm*128 + 32 i + 8 (e/4) + 4 kg + e%4][col(j) + l32]
+    if (EPI == EPI_ADD) {
+        // residual add: all 64 loads of a 32-row group are in flight before the first store
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float cv[16][4];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = row0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * kg + (e & 3);
+                const float* crow = C + (long long)min(r, M - 1) * N + tn * GB_N + wn * 128 + l32;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) cv[e][j] = crow[32 * j];
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = row0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * kg + (e & 3);
+                if (r >= M) continue;
+                float* crow = C + (long long)r * N + tn * GB_N + wn * 128 + l32;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) crow[32 * j] = cv[e][j] + acc[i][j][e];
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
