@@ -985,40 +985,69 @@ __global__ __launch_bounds__(64) void attn_rows_kernel(RowsAttn a) {
 // head go to LDS first, then each (head, e) output sums its splits with independent
 // loads.  Splits that saw no key carry m = -inf and weigh 0.
 constexpr int kCombineMaxSplits = 256, kCombineMaxG = 8;
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part, int n_splits,
-                                                           int G, int HD, int H, int Hkv,
-                                                           u16* __restrict__ out, bool packed) {
-    __shared__ float wts[kCombineMaxSplits * kCombineMaxG];
-    __shared__ float lsum[kCombineMaxG];
+// One block per (query row, query head), 128 threads.  Split s holds, for each of the G
+// heads of its KV group, the unnormalised output o_s (hd floats) followed by its running
+// max m_s (log2 units) and sum l_s.  Weights w_s = 2^(m_s - max m); out = sum w_s o_s /
+// sum w_s l_s.  Every load of the first 32 splits (o_s[e] per thread and output dim,
+// m_s and l_s per thread and split) is issued before the block reductions, so a launch
+// with up to 32 splits waits on one memory round trip.
+constexpr int kCombinePre = 32;
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part, int n_splits, int G,
+                                                           int HD, int H, int Hkv, u16* __restrict__ out,
+                                                           bool packed) {
+    __shared__ float wts[kCombineMaxSplits];
+    __shared__ float red[2];
     const long long qrow = blockIdx.x;
-    const int g = blockIdx.y;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int head = blockIdx.y, g = head / G, hh = head % G;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const long long stride = (long long)G * (HD + 2);
-    const float* base = part + (qrow * Hkv + g) * (long long)n_splits * stride;
-    for (int hh = w; hh < G; hh += 4) {
-        const float* ph = base + hh * (HD + 2);
-        float mx = -INFINITY;
-        for (int s = lane; s < n_splits; s += 64) mx = fmaxf(mx, ph[s * stride + HD]);
-        const float M = wave_max(mx);
-        float l = 0.f;
-        for (int s = lane; s < n_splits; s += 64) {
-            const float ms = ph[s * stride + HD];
-            const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-            wts[s * G + hh] = wgt;
-            l += wgt * ph[s * stride + HD + 1];
-        }
-        l = wave_sum(l);
-        if (lane == 0) lsum[hh] = l;
+    const float* ph = part + (qrow * Hkv + g) * (long long)n_splits * stride + hh * (HD + 2);
+    const bool has_e = tid < HD;
+    const float* pe = ph + (has_e ? tid : 0);
+    float v[kCombinePre];
+#pragma unroll
+    for (int u = 0; u < kCombinePre; ++u) v[u] = (has_e && u < n_splits) ? pe[u * stride] : 0.f;
+    float m_own = -INFINITY, l_own = 0.f;
+    if (tid < n_splits) {
+        m_own = ph[tid * stride + HD];
+        l_own = ph[tid * stride + HD + 1];
     }
+    float mx = m_own;
+    for (int s = tid + 128; s < n_splits; s += 128) mx = fmaxf(mx, ph[s * stride + HD]);
+    mx = wave_max(mx);
+    if (lane == 0) red[w] = mx;
     __syncthreads();
-    for (int idx = threadIdx.x; idx < G * HD; idx += 256) {
-        const int hh = idx / HD, e = idx % HD;
-        const float* pe = base + hh * (HD + 2) + e;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int s = 0; s < n_splits; ++s) acc += wts[s * G + hh] * pe[s * stride];
-        const int k = (g * G + hh) * HD + e;
-        out[packed ? pk_index((int)qrow, k, H * HD) : qrow * H * HD + k] = f2bf(acc / lsum[hh]);
+    const float M = fmaxf(red[0], red[1]);
+    __syncthreads();
+    float l = 0.f;
+    if (tid < n_splits) {
+        const float wgt = (m_own == -INFINITY) ? 0.f : exp2f(m_own - M);
+        wts[tid] = wgt;
+        l = wgt * l_own;
+    }
+    for (int s = tid + 128; s < n_splits; s += 128) {
+        const float ms = ph[s * stride + HD];
+        const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+        wts[s] = wgt;
+        l += wgt * ph[s * stride + HD + 1];
+    }
+    l = wave_sum(l);
+    if (lane == 0) red[w] = l;
+    __syncthreads();
+    const float inv = 1.0f / (red[0] + red[1]);
+    for (int e = tid; e < HD; e += 128) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        if (e == tid) {
+#pragma unroll
+            for (int u = 0; u < kCombinePre; ++u)
+                if (u < n_splits) acc[u & 3] += wts[u] * v[u];
+            for (int s = kCombinePre; s < n_splits; ++s) acc[s & 3] += wts[s] * ph[s * stride + e];
+        } else {
+            for (int s = 0; s < n_splits; ++s) acc[s & 3] += wts[s] * ph[s * stride + e];
+        }
+        const float o = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * inv;
+        const int k = head * HD + e;
+        out[packed ? pk_index((int)qrow, k, H * HD) : qrow * H * HD + k] = f2bf(o);
     }
 }
 
@@ -1138,8 +1167,8 @@ hipError_t attn_rows_combine(const RowsAttn& a, hipStream_t st, bool packed_out)
     const int G = a.H / a.kv.Hkv;
     if (a.n_splits > kCombineMaxSplits || G > kCombineMaxG) return hipErrorInvalidValue;
     if (packed_out && (a.B * a.n_rows > 8 || (a.H * a.kv.hd) % 64)) return hipErrorInvalidValue;
-    dim3 grid(a.B * a.n_rows, a.kv.Hkv);
-    hipLaunchKernelGGL(attn_combine_kernel, grid, dim3(256), 0, st, a.part, a.n_splits, G, a.kv.hd, a.H,
+    dim3 grid(a.B * a.n_rows, a.H);
+    hipLaunchKernelGGL(attn_combine_kernel, grid, dim3(128), 0, st, a.part, a.n_splits, G, a.kv.hd, a.H,
                        a.kv.Hkv, a.out, packed_out);
     return hipGetLastError();
 }

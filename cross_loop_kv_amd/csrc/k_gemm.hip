@@ -278,6 +278,32 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
     const int wstep = PK ? 512 : 32;  // elements between consecutive chunks
     const bool mvalid = r8 < M;
     const u16* ar = PK ? A + lane * 8 : A + (long long)(mvalid ? r8 : 0) * K + h * Kh + grp * 8;
+    // The epilogue's inputs (partial sums of x^2 for the norm, the residual rows, the
+    // added vector and the next norm's gain) are loaded before the weight stream so that
+    // they do not cost a memory round trip after it.
+    constexpr int PSR = 8;  // partial sums held in registers per lane (nparts <= 512)
+    float ps_pre[PSR];
+    const bool norm_wave = NORM && w < M;
+    if (norm_wave) {
+#pragma unroll
+        for (int q = 0; q < PSR; ++q) {
+            const int p = lane + 64 * q;
+            ps_pre[q] = p < io.nparts ? io.ps_in[p * 8 + w] : 0.f;
+        }
+    }
+    const bool out_lane = grp < 2 && c16 < 8;
+    const int col = blockIdx.x * 8 + (c16 & 7);
+    float c_pre[4] = {0.f, 0.f, 0.f, 0.f};
+    float addv = 0.f, gainv = 0.f;
+    if (EPI == EPI_ADD && w == 0 && out_lane) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = (grp & 1) * 4 + i;
+            if (m < M) c_pre[i] = C[(long long)m * N + col];
+        }
+        if (PREP && io.add_vec) addv = bf2f(io.add_vec[col]);
+        if (PREP) gainv = bf2f(io.next_gain[col]);
+    }
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = w; c0 < nch; c0 += NWV * NL) {
         uint4 wv[NL], wv1[NL], av[NL];
@@ -300,9 +326,11 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
                 acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[j]), as_bf16x8(wv1[j]), acc1, 0, 0, 0);
         }
     }
-    if (NORM && w < M) {  // wave w: row w's sum of squares, partials in a fixed order
+    if (norm_wave) {  // wave w: row w's sum of squares, partials in a fixed order
         float t = 0.f;
-        for (int p = lane; p < io.nparts; p += 64) t += io.ps_in[p * 8 + w];
+#pragma unroll
+        for (int q = 0; q < PSR; ++q) t += ps_pre[q];
+        for (int p = lane + 64 * PSR; p < io.nparts; p += 64) t += io.ps_in[p * 8 + w];
         t = wave_sum(t);
         if (lane == 0) s_inv[w] = 1.0f / sqrtf(t / (float)K + io.eps);
     }
@@ -324,8 +352,6 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
         o0[i] = __shfl(s0[i], (lane + 40) & 63);
         if (DUAL) o1[i] = __shfl(s1[i], (lane + 40) & 63);
     }
-    const bool out_lane = grp < 2 && c16 < 8;
-    const int col = blockIdx.x * 8 + (c16 & 7);
     float sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -337,11 +363,11 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
         if (EPI == EPI_STORE) {
             C[o] = v0;
         } else if (EPI == EPI_ADD) {
-            float x = C[o] + v0;
-            if (PREP && io.add_vec) x = x + bf2f(io.add_vec[col]);
+            float x = c_pre[i] + v0;
+            if (PREP && io.add_vec) x = x + addv;
             C[o] = x;
             if (PREP) {
-                io.xg_out[PK ? pk_index(m, col, N) : o] = f2bf(x * bf2f(io.next_gain[col]));
+                io.xg_out[PK ? pk_index(m, col, N) : o] = f2bf(x * gainv);
                 sq[i] = x * x;
             }
         } else if (EPI == EPI_SWIGLU) {
