@@ -85,6 +85,7 @@ _SIGS = {
     "lk_timing_sample": (C.c_int, [C.c_void_p, C.c_int32]),
     "lk_set_decode_graphs": (C.c_int, [C.c_void_p, C.c_int32]),
     "lk_decode_weight_bytes": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t)]),
+    "lk_set_decode_weights": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "lk_timing_read": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
     "lk_dbg_topk": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
     "lk_dbg_quantize": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
@@ -206,6 +207,10 @@ def lk_kv_store_keep_codes(s: int, enable: bool) -> None:
     _check(lib().lk_kv_store_keep_codes(s, 1 if enable else 0))
 
 
+def lk_set_decode_weights(h: int, d_buf, nbytes: int, stream=None) -> None:
+    _check(lib().lk_set_decode_weights(h, d_buf, nbytes, _stream(stream)))
+
+
 def lk_decode_weight_bytes(h: int) -> int:
     n = C.c_size_t()
     _check(lib().lk_decode_weight_bytes(h, C.byref(n)))
@@ -313,7 +318,11 @@ class Store:
 
 
 class LoopedModel:
-    """Weights on the GPU in the library's packed bf16 layout plus a handle."""
+    """Weights on the GPU in the library's packed bf16 layout plus a handle.
+
+    Every prefill and decode call of a model uses the model's one workspace buffer, on
+    the caller's current stream: calls issued on different streams must be ordered by
+    the caller (torch's side streams do not wait for the null stream)."""
 
     def __init__(self, shape, lazy, weights: Iterable, device: str = "cuda"):
         import torch
@@ -367,6 +376,24 @@ class LoopedModel:
         self.h = lk_create(self._cfg, self._lz, self._w)
         self._ws = None
         self._ws_bytes = 0
+        self._pk = None
+        self.pack_decode_weights(True)
+
+    def pack_decode_weights(self, enable: bool = True, share=None) -> None:
+        """Give the handle the packed decode copy of the weights (a device buffer owned
+        here, or `share`'s), or detach it (decode then uses the row-major weights)."""
+        if not enable:
+            lk_set_decode_weights(self.h, None, 0)
+            self._pk = None
+            return
+        nbytes = lk_decode_weight_bytes(self.h)
+        if nbytes == 0:
+            return
+        if share is not None and share._pk is not None:
+            self._pk = share._pk
+        elif self._pk is None:
+            self._pk = _aligned_bytes(nbytes, self.device)
+        lk_set_decode_weights(self.h, self._pk[1].data_ptr(), nbytes)
 
     def sibling(self, lazy) -> "LoopedModel":
         """A second handle over the same device weights with another lazy configuration
@@ -379,6 +406,8 @@ class LoopedModel:
         m.h = lk_create(m._cfg, m._lz, m._w)
         m._ws = None
         m._ws_bytes = 0
+        m._pk = None
+        m.pack_decode_weights(True, share=self)
         return m
 
     def weight_bytes(self) -> int:

@@ -117,17 +117,14 @@ struct lk_handle {
     DecodeGraph graph;
     DecodeGraph* building = nullptr;  // set while a decode step is being captured
     int use_graphs = 1;
-    // Decode copy of the layer projections in the lane-packed operand order, made on
-    // the first decode step (one device allocation, freed by lk_destroy).
+    // Decode copy of the layer projections in the lane-packed operand order, in a
+    // caller-owned buffer given by lk_set_decode_weights (nullptr: decode multiplies by
+    // the row-major weights).
     struct Packed {
         const u16 *wqkv, *wo, *w_in, *w_down;
     };
     std::vector<Packed> PL;
     void* pk_buf = nullptr;
-    size_t pk_bytes = 0;
-    ~lk_handle() {
-        if (pk_buf) (void)hipFree(pk_buf);
-    }
     const u16 *tok, *lemb, *fnorm;
     std::vector<lk_layer_weights> L;
     double inv_freq[64];
@@ -933,16 +930,12 @@ size_t packed_weight_bytes(const lk_handle* h) {
     return per * h->L.size();
 }
 
-int prepare_packed(lk_handle* h, hipStream_t st) {
-    if (h->pk_buf) return LK_OK;
-    const size_t bytes = packed_weight_bytes(h);
-    if (!bytes) return LK_OK;
-    LK_HIP(hipMalloc(&h->pk_buf, bytes));
-    h->pk_bytes = bytes;
+// Pack the layer projections into buf (at least packed_weight_bytes(h)) on st.
+int pack_decode_weights(lk_handle* h, void* buf, hipStream_t st) {
     const lk_model_cfg& c = h->c;
     const int d = c.d_model, Hhd = c.n_heads * c.head_dim, F = c.ffn_dim;
     const int fin = c.ffn_act == LK_ACT_SWIGLU ? 2 : 1;
-    u16* p = (u16*)h->pk_buf;
+    u16* p = (u16*)buf;
     h->PL.resize(h->L.size());
     for (size_t i = 0; i < h->L.size(); ++i) {
         const lk_layer_weights& W = h->L[i];
@@ -958,6 +951,7 @@ int prepare_packed(lk_handle* h, hipStream_t st) {
         LK_HIP(pack(W.w_in, (long long)fin * F, d, &P.w_in));
         LK_HIP(pack(W.w_down, d, F, &P.w_down));
     }
+    h->pk_buf = buf;
     return LK_OK;
 }
 
@@ -1086,7 +1080,6 @@ int lk_looped_decode_step(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, fl
     if ((uintptr_t)d_ws % kAlign) return fail(LK_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     hipStream_t st = (hipStream_t)stream;
     const int d = h->c.d_model;
-    LK_TRY(prepare_packed(h, st));
     LK_HIP(hipMemcpyAsync(w.ids, d_ids, (size_t)B * 4, hipMemcpyDeviceToDevice, st));
     if (st && h->use_graphs) {
         DecodeGraph& g = h->graph;
@@ -1122,6 +1115,21 @@ int lk_decode_weight_bytes(const lk_handle* h, size_t* bytes) {
     if (!h || !bytes) return fail(LK_ERR_INVALID_ARG, "null argument");
     *bytes = packed_weight_bytes(h);
     return LK_OK;
+}
+
+int lk_set_decode_weights(lk_handle* h, void* d_buf, size_t buf_bytes, void* stream) {
+    if (!h) return fail(LK_ERR_INVALID_ARG, "null handle");
+    h->graph.reset();
+    if (!d_buf) {
+        h->pk_buf = nullptr;
+        h->PL.clear();
+        return LK_OK;
+    }
+    const size_t need = packed_weight_bytes(h);
+    if (!need) return fail(LK_ERR_UNSUPPORTED, "these shapes have no packed decode layout");
+    if (buf_bytes < need) return fail(LK_ERR_CAPACITY, "decode weight buffer too small");
+    if ((uintptr_t)d_buf % 16) return fail(LK_ERR_INVALID_ARG, "decode weight buffer must be 16-byte aligned");
+    return pack_decode_weights(h, d_buf, (hipStream_t)stream);
 }
 
 int lk_set_decode_graphs(lk_handle* h, int32_t enable) {

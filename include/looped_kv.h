@@ -169,11 +169,18 @@ int lk_set_decode_graphs(lk_handle *h, int32_t enable);
 /* Device bytes of the decode copy of the layer projections (0 if the shapes do
  * not take it: it needs d_model, heads*head_dim and ffn_dim multiples of 64).
  * Decode steps with at most 8 sequences multiply by the weights in an operand
- * order packed for the MFMA lanes (every wave load reads 1 KB contiguous); the
- * first decode step allocates this copy (hipMalloc) and fills it from the
- * caller's weights on the step's stream.  lk_destroy frees it.  The caller's
- * weights must not change afterwards. */
+ * order packed for the MFMA lanes (every wave load reads 1 KB contiguous). */
 int lk_decode_weight_bytes(const lk_handle *h, size_t *bytes);
+
+/* Give the handle a caller-owned device buffer of at least lk_decode_weight_bytes
+ * bytes (16-byte aligned) and fill it with the packed copy of the caller's weights
+ * on `stream`.  The buffer must stay allocated, and the weights unchanged, while
+ * the handle decodes; several handles over the same weights may share one buffer
+ * (each call rewrites the same contents).  d_buf == NULL detaches the buffer:
+ * decode then multiplies by the row-major weights.  Either way the captured decode
+ * step is dropped.  LK_ERR_UNSUPPORTED when the size query gives 0, LK_ERR_CAPACITY
+ * when buf_bytes is too small.  The library allocates no device memory for this. */
+int lk_set_decode_weights(lk_handle *h, void *d_buf, size_t buf_bytes, void *stream);
 
 /* Layer applications one prefill/decode pass runs per token: P + R*K + Q. */
 int lk_effective_depth(const lk_handle *h, int32_t *depth);

@@ -214,6 +214,45 @@ def test_decode_graph_replay_matches_eager_launches(mode, timed):
     assert sa.length() == sb.length() == T + steps
 
 
+def test_decode_packed_weights_match_row_major_weights():
+    """Decode with the packed decode copy of the weights (caller-owned buffer) against
+    decode with the buffer detached (row-major weights, other GEMM kernels): the same
+    products up to summation order.  Detaching and re-attaching the buffer drops the
+    captured step; the size query and the capacity check hold."""
+    s = _small()
+    # 16-bit KV: no quantizer decision can flip between the two summation orders
+    lz = I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=16, res_bits=16)
+    T, steps, Bsz = 150, 4, 3
+    W = I.gen_weights(s, seed=5)
+    ids = torch.from_numpy(I.gen_prompt_ids(s, Bsz, T))
+    dec = torch.from_numpy(I.gen_decode_ids(s, Bsz, steps)).cuda()
+    model = B.LoopedModel(s, lz, W)
+    nbytes = B.lk_decode_weight_bytes(model.h)
+    assert nbytes == 2 * sum(L["wqkv"].numel() + L["wo"].numel() + L["w_in"].numel() + L["w_down"].numel()
+                             for L in model.layers)
+    with pytest.raises(B.LKError):
+        B.lk_set_decode_weights(model.h, model._pk[1].data_ptr(), nbytes - 2)
+    model.pack_decode_weights(True)
+    side = torch.cuda.Stream()
+    sa, sb = model.store(Bsz, T, T + steps), model.store(Bsz, T, T + steps)
+    model.prefill(sa, ids)
+    model.prefill(sb, ids)
+    # the prefills ran on the null stream; torch's side stream does not wait for it, and
+    # the model's calls share one workspace
+    torch.cuda.synchronize()
+    outs = []
+    for st in (sa, sb):
+        o = []
+        for i in range(steps):
+            with torch.cuda.stream(side):
+                o.append(model.decode(st, dec[i]).clone())
+        side.synchronize()
+        outs.append(torch.stack(o))
+        model.pack_decode_weights(False)
+    log(f"packed vs row-major decode: max-abs-rel {max_abs_rel(outs[0].cpu().numpy(), outs[1].cpu().numpy()):.2e}")
+    assert max_abs_rel(outs[0].cpu().numpy(), outs[1].cpu().numpy()) < 1e-3
+
+
 def test_decode_window_ring_wraps_during_decode():
     """Decode positions cross the end of the float16 window ring (window 16 -> 128 rows):
     prompt 100, 40 steps, positions 100..139."""
