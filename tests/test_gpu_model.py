@@ -86,6 +86,18 @@ def test_small_shapes_ragged_prompt(name, kw, lz):
     check(r, name)
 
 
+@pytest.mark.parametrize("mode", ["lazy", "per_loop"])
+def test_decode_batch_above_eight_rows(mode):
+    """More than 8 sequences: decode takes the 16-row projection kernels (RMSNorm fused
+    from the float32 residual rows) instead of the folded packed-weight ones."""
+    s = _small()
+    lz = (I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4)
+          if mode == "lazy" else I.Lazy(mode="per_loop"))
+    log(f"batch 10 decode, {mode}")
+    r = run_pair(s, lz, batch=10, prompt=100, steps=2, seed=12)
+    check(r, f"batch 10 {mode}")
+
+
 def test_int4_natural_codes_drift_is_bounded():
     """Without injected codes the int4 path differs from the oracle by code flips only."""
     s = _small()
@@ -175,8 +187,9 @@ def test_full_width_shapes_short_prompt(name, batch, prompt, steps):
     check(r, name)
 
 
-@pytest.mark.parametrize("mode,timed", [("lazy", True), ("lazy", False), ("per_loop", True)])
-def test_decode_graph_replay_matches_eager_launches(mode, timed):
+@pytest.mark.parametrize("mode,timed,Bsz", [("lazy", True, 2), ("lazy", False, 2), ("per_loop", True, 2),
+                                           ("lazy", False, 10)])
+def test_decode_graph_replay_matches_eager_launches(mode, timed, Bsz):
     """Decode steps replayed from a captured HIP graph (non-null stream) equal the
     same steps launched kernel by kernel (null stream) bit for bit, replay after
     replay, with unrelated eager work and host synchronisation in between; the
@@ -184,7 +197,7 @@ def test_decode_graph_replay_matches_eager_launches(mode, timed):
     s = _small()
     lz = (I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4)
           if mode == "lazy" else I.Lazy(mode="per_loop"))
-    T, steps, Bsz = 150, 6, 2
+    T, steps = 150, 6
     W = I.gen_weights(s, seed=9)
     ids = torch.from_numpy(I.gen_prompt_ids(s, Bsz, T))
     dec = torch.from_numpy(I.gen_decode_ids(s, Bsz, steps)).cuda()
