@@ -52,6 +52,13 @@ def parse():
     ap.add_argument("--drift-batch", type=int, default=2,
                     help="sequences of the prompt compared lazy versus dense (full context)")
     ap.add_argument("--drift-steps", type=int, default=8)
+    ap.add_argument("--gemm-shapes", action="store_true",
+                    help="only time the prefill projection GEMMs of the workload, per shape, next to "
+                         "torch.matmul (hipBLASLt, bf16 output) as a reference; one JSON line per shape")
+    ap.add_argument("--gemm-filter", default=None, help="with --gemm-shapes: only shapes whose name contains this")
+    ap.add_argument("--gemm-reps", type=int, default=10)
+    ap.add_argument("--gemm-rows", default="all", choices=["all", "loop1", "lazy"],
+                    help="with --gemm-shapes: the loop-1 row count B*T, the lazy-loop one B*n, or both")
     return ap.parse_args()
 
 
@@ -79,6 +86,60 @@ def prefill_gemm_flops(shape, lazy, batch, T):
         dense_apps = s.n_prelude + s.n_coda + s.n_shared * s.n_loops
         sparse_rows = 0
     return per_row * (batch * T * dense_apps + sparse_rows)
+
+
+def gemm_shapes(args):
+    """Per-shape timing of the prefill projection GEMMs (library kernel with its fused
+    epilogue) at the workload's loop-1 rows (B*T) and lazy-loop rows (B*n)."""
+    import torch
+    from cross_loop_kv_amd import binding as B
+    from cross_loop_kv_amd import inputs as I
+    wl = I.workload(args.workload)
+    s, lz = wl.shape, wl.lazy
+    qkv_w = (s.n_heads + 2 * s.n_kv_heads) * s.head_dim
+    hhd = s.n_heads * s.head_dim
+    act = 2 if s.ffn_act == "swiglu" else 3
+    fin = 2 if s.ffn_act == "swiglu" else 1
+    rows = [wl.batch * wl.prompt] if args.gemm_rows != "lazy" else []
+    if lz.mode == "lazy" and s.n_loops > 1 and args.gemm_rows != "loop1":
+        rows.append(wl.batch * kept_rows(lz.rho, wl.prompt))
+    projs = [("qkv", qkv_w, s.d_model, 0), ("o", s.d_model, hhd, 1), ("ffn_in", s.ffn_dim, s.d_model, act),
+             ("down", s.d_model, s.ffn_dim, 1)]
+
+    def timeit(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for M in rows:
+        for name, N, K, epi in projs:
+            if args.gemm_filter and args.gemm_filter not in name:
+                continue
+            wrows = fin * N if name == "ffn_in" else N
+            gen = torch.Generator(device="cuda").manual_seed(M + N)
+            a = torch.randn(M, K, device="cuda", generator=gen).to(torch.bfloat16)
+            w = (torch.randn(wrows, K, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+            c = torch.zeros(M, N, device="cuda", dtype=torch.float32)
+            o = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+            flops = 2.0 * M * wrows * K
+            t_lib = timeit(lambda: B.lk_dbg_gemm_epi(a.data_ptr(), w.data_ptr(), epi, c.data_ptr(), o.data_ptr(),
+                                                     M, N, K), args.gemm_reps)
+            wt = w.t()
+            t_ref = timeit(lambda: torch.matmul(a, wt), args.gemm_reps)
+            print(json.dumps({"gemm": name, "M": M, "N": wrows, "K": K, "epilogue": ["store", "add", "swiglu", "gelu"][epi],
+                              "ms": round(t_lib, 4), "tflops": round(flops / t_lib / 1e9, 1),
+                              "frac": round(flops / t_lib / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "ref_hipblaslt_ms": round(t_ref, 4),
+                              "ref_frac": round(flops / t_ref / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}), flush=True)
+            del a, w, c, o, wt
+            torch.cuda.empty_cache()
 
 
 def drift_stats(a, b):
@@ -233,6 +294,9 @@ def main():
 
     assert torch.cuda.is_available(), "needs a GPU"
     torch.cuda.set_device(0)
+    if args.gemm_shapes:
+        gemm_shapes(args)
+        return
     wl = I.workload(args.workload)
     if args.prompt:
         wl.prompt = args.prompt
