@@ -195,15 +195,19 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_dense_i8_deep_48x4_b8
 
 def kernel_source_hash():
     """Hash of the source the loop-1 decode-attention kernel is built from: the
-    attention file up to the sparse-gather section (helpers, prefill and dense decode
-    kernels) and the KV-store address arithmetic of the common header."""
+    attention file's helpers (up to the flash prefill section) and its dense decode
+    section (up to the sparse-gather section), and the KV-store address arithmetic of
+    the common header."""
     import hashlib
     att = open(os.path.join(ROOT, "cross_loop_kv_amd", "csrc", "k_attn.hip")).read()
     com = open(os.path.join(ROOT, "cross_loop_kv_amd", "csrc", "lk_common.h")).read()
+    mark = "// ---------------------------------------------------------------- "
     a = att.index("typedef _Float16 half8")
-    b = att.index("// ---------------------------------------------------------------- sparse decode: gather")
-    c = com.index("// ---------------------------------------------------------------- KV store views")
-    return hashlib.sha256((att[a:b] + com[c:]).encode()).hexdigest()[:16]
+    a2 = att.index(mark + "flash prefill")
+    d = att.index(mark + "dense decode (MFMA)")
+    b = att.index(mark + "sparse decode: gather")
+    c = com.index(mark + "KV store views")
+    return hashlib.sha256((att[a:a2] + att[d:b] + com[c:]).encode()).hexdigest()[:16]
 
 
 def measured_traffic(workload):

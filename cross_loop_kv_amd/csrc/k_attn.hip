@@ -270,6 +270,183 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const u16* __restrict
     }
 }
 
+// ---------------------------------------------------------------- flash prefill, hd 128
+// 64-key tiles, one head and 128 queries per workgroup (4 waves x 32 queries), K/V staged
+// through registers into double-buffered LDS.  S^T = K Q^T for each 32-key half (LDS rows
+// permuted by flash_key_of_row so the score accumulator is already the B operand of
+// O^T += V^T P^T).  Per tile and lane: one FMA and one v_exp_f32 per score; the output is
+// rescaled only when some query's running max grows (a wave-uniform branch); tiles below
+// the diagonal skip the causal mask.  Workgroups take query blocks from the last one
+// down, so the longest causal spans start first.
+template <bool I8>
+__global__ __launch_bounds__(256, 2) void attn_prefill_fa_kernel(const u16* __restrict__ Q, KVLayer kv, int T,
+                                                                 int H, u16* __restrict__ O,
+                                                                 float* __restrict__ LSE, float sl2) {
+    constexpr int HD = 128, KT = 64;
+    constexpr int LDK = HD + 8;
+    constexpr int LDV = KT + 8;
+    constexpr int CPR = HD / 8;             // 16-byte chunks per K row
+    constexpr int NKC = KT * CPR;           // 1024 K chunks per tile
+    constexpr int NVC = (KT / 8) * HD;      // 1024 V chunks per tile
+    constexpr int PER = (NKC + NVC) / 256;  // 8 per thread
+    __shared__ __attribute__((aligned(16))) u16 Ks[2][KT * LDK];
+    __shared__ __attribute__((aligned(16))) u16 Vt[2][HD * LDV];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int kg = lane >> 5, l32 = lane & 31;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int G = H / kv.Hkv, g = h / G;
+    const int qblk = (gridDim.x - 1 - blockIdx.x) * 128;
+    const int q0 = qblk + w * 32;
+    const int qi = q0 + l32;
+    const long long ldq = (long long)H * HD;
+
+    bf16x8 qf[HD / 16];
+#pragma unroll
+    for (int ks = 0; ks < HD / 16; ++ks) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (qi < T) v = *(const uint4*)(Q + ((long long)b * T + qi) * ldq + h * HD + ks * 16 + kg * 8);
+        qf[ks] = as_bf16x8(v);
+    }
+    f32x16 oacc[HD / 32];
+#pragma unroll
+    for (int c = 0; c < HD / 32; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[c][i] = 0.f;
+    float m_i = -INFINITY, l_i = 0.f;
+
+    const int kend = min(T, qblk + 128);
+    const int ntiles = (kend + KT - 1) / KT;
+    uint4 regs[PER];
+    auto load_tile = [&](int t) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int c = tid + p * 256;
+            regs[p] = make_uint4(0, 0, 0, 0);
+            if (c < NKC) {
+                const int r = c / CPR;
+                const int key = t * KT + (r & 32) + flash_key_of_row(r & 31);
+                if (key < T) regs[p] = load_k8_bf16<HD, I8>(kv, b, g, key, (c % CPR) * 8);
+            } else {
+                const int cc = c - NKC;
+                const int blk = cc / HD, e = cc % HD;
+                const int pos0 = t * KT + blk * 8;
+                if (pos0 < T) regs[p] = load_v8_bf16<HD, I8>(kv, b, g, pos0, e, T - pos0);
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int c = tid + p * 256;
+            if (c < NKC) {
+                *(uint4*)&Ks[buf][(c / CPR) * LDK + (c % CPR) * 8] = regs[p];
+            } else {
+                const int cc = c - NKC;
+                *(uint4*)&Vt[buf][(cc % HD) * LDV + (cc / HD) * 8] = regs[p];
+            }
+        }
+    };
+    load_tile(0);
+    store_tile(0);
+    for (int t = 0; t < ntiles; ++t) {
+        const int cur = t & 1;
+        __syncthreads();
+        if (t + 1 < ntiles) load_tile(t + 1);
+        const int kbase = t * KT;
+        if (kbase <= q0 + 31) {
+            f32x16 sc[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sc[hh][i] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < HD / 16; ++ks) {
+                    const bf16x8 a = as_bf16x8(*(const uint4*)&Ks[cur][(32 * hh + l32) * LDK + ks * 16 + kg * 8]);
+                    sc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sc[hh], 0, 0, 0);
+                }
+            }
+            // causal / length mask only where the tile reaches the diagonal or the end
+            const bool full = kbase + KT - 1 <= q0 && kbase + KT <= T;
+            if (!full) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = kbase + 32 * hh + ((i < 8) ? 8 * kg + i : 16 + 8 * kg + (i - 8));
+                        if (key > qi || key >= T) sc[hh][i] = -INFINITY;
+                    }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[hh][i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_i, mx * sl2);
+            if (__builtin_amdgcn_ballot_w64(m_new > m_i)) {
+                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_i - m_new);
+                l_i *= alpha;
+#pragma unroll
+                for (int c = 0; c < HD / 32; ++c)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[c][i] *= alpha;
+            }
+            m_i = m_new;
+            const float nm = -m_new;
+            float rs = 0.f;
+            bf16x8 pb[2][2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                float p[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    p[i] = __builtin_amdgcn_exp2f(fmaf(sc[hh][i], sl2, nm));
+                    rs += p[i];
+                }
+                uint4 pu0, pu1;
+                pu0.x = pack_bf2(p[0], p[1]);
+                pu0.y = pack_bf2(p[2], p[3]);
+                pu0.z = pack_bf2(p[4], p[5]);
+                pu0.w = pack_bf2(p[6], p[7]);
+                pu1.x = pack_bf2(p[8], p[9]);
+                pu1.y = pack_bf2(p[10], p[11]);
+                pu1.z = pack_bf2(p[12], p[13]);
+                pu1.w = pack_bf2(p[14], p[15]);
+                pb[hh][0] = as_bf16x8(pu0);
+                pb[hh][1] = as_bf16x8(pu1);
+            }
+            rs += __shfl_xor(rs, 32);
+            l_i += rs;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int c = 0; c < HD / 32; ++c) {
+                    const u16* vrow = &Vt[cur][(c * 32 + l32) * LDV + 32 * hh];
+                    const bf16x8 va0 = as_bf16x8(*(const uint4*)(vrow + 8 * kg));
+                    const bf16x8 va1 = as_bf16x8(*(const uint4*)(vrow + 16 + 8 * kg));
+                    oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pb[hh][0], oacc[c], 0, 0, 0);
+                    oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pb[hh][1], oacc[c], 0, 0, 0);
+                }
+        }
+        if (t + 1 < ntiles) store_tile(cur ^ 1);
+    }
+    if (qi < T) {
+        const float inv = 1.f / l_i;
+        u16* orow = O + ((long long)b * T + qi) * ldq + h * HD;
+#pragma unroll
+        for (int c = 0; c < HD / 32; ++c)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int e0 = c * 32 + 8 * i4 + 4 * kg;
+                uint2 v;
+                v.x = pack_bf2(oacc[c][i4 * 4 + 0] * inv, oacc[c][i4 * 4 + 1] * inv);
+                v.y = pack_bf2(oacc[c][i4 * 4 + 2] * inv, oacc[c][i4 * 4 + 3] * inv);
+                *(uint2*)(orow + e0) = v;
+            }
+        if (kg == 0) LSE[((long long)b * H + h) * T + qi] = m_i + log2f(l_i);
+    }
+}
+
 // ---------------------------------------------------------------- column mass
 template <int HD, bool I8>
 __global__ __launch_bounds__(256) void column_mass_kernel(const u16* __restrict__ Q, KVLayer kv,
@@ -1056,6 +1233,13 @@ hipError_t prefill_hd(const u16* q, const KVLayer& kv, int B, int T, int H, u16*
                       hipStream_t st) {
     dim3 grid((T + 127) / 128, H, B);
     const float sl2 = kLog2e / sqrtf((float)HD);
+    if (HD == 128) {
+        if (kv.lazy && kv.base_bits == 8)
+            hipLaunchKernelGGL((attn_prefill_fa_kernel<true>), grid, dim3(256), 0, st, q, kv, T, H, out, lse, sl2);
+        else
+            hipLaunchKernelGGL((attn_prefill_fa_kernel<false>), grid, dim3(256), 0, st, q, kv, T, H, out, lse, sl2);
+        return hipGetLastError();
+    }
     if (kv.lazy && kv.base_bits == 8)
         hipLaunchKernelGGL((attn_prefill_kernel<HD, true>), grid, dim3(256), 0, st, q, kv, T, H, out, lse, sl2);
     else
