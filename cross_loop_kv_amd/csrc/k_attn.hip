@@ -954,6 +954,206 @@ __global__ __launch_bounds__(256) void gather_recon_kernel(RowsAttn a, int mode,
     }
 }
 
+// ---------------------------------------------------------------- sparse prefill rows (MFMA)
+// Token-sparse prefill at loop k >= 2 for hd 128: kept query i attends over
+// (S ∩ [0, i-w]) ∪ [i-w+1, i], the first part read from the float16 stable-column cache
+// sc (row r = column cols[r]), the second from a float16 copy fr of the loop-k
+// reconstruction at every prompt position.  A workgroup takes RB consecutive kept rows of
+// one sequence for all G query heads of KV head g (wave w: head w % G, rows 32 (w / G) ..),
+// so every K/V tile is read once for the G heads.  Tiles: first the cache rows with a
+// column at or below (last row's position - w), then the positions from the first row's
+// window start to the last row's position; per query both are masked exactly.  f16 MFMAs
+// (q converted from bf16 exactly), online softmax as in the flash prefill, output written
+// directly (no split partials).
+template <int G>
+__global__ __launch_bounds__(G > 4 ? 64 * G : 256) void attn_rows_pf_kernel(RowsAttn a, KVLayer sc, KVLayer fr,
+                                                                            float sl2) {
+    constexpr int HD = 128, KT = 64, LDK = HD + 8, LDV = KT + 8, CPR = HD / 8;
+    constexpr int NW = G > 4 ? G : 4, NT = NW * 64;
+    constexpr int RB = 32 * NW / G;
+    constexpr int NKC = KT * CPR, NVC = (KT / 8) * HD;
+    constexpr int PER = (NKC + NVC) / NT;
+    __shared__ __attribute__((aligned(16))) u16 Ks[2][KT * LDK];
+    __shared__ __attribute__((aligned(16))) u16 Vt[2][HD * LDV];
+    __shared__ int s_col[2][KT];
+    __shared__ int s_pos[RB];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int kg = lane >> 5, l32 = lane & 31;
+    const int g = blockIdx.y, b = blockIdx.z, Hkv = a.kv.Hkv, H = a.H;
+    const int bg = b * Hkv + g, n = a.n_rows, W = a.window;
+    const int j0 = (gridDim.x - 1 - blockIdx.x) * RB;
+    const int hh = w % G, rs = w / G, h = g * G + hh;
+    for (int i = tid; i < RB; i += NT) s_pos[i] = j0 + i < n ? a.qpos[(long long)b * n + j0 + i] : -1;
+    __syncthreads();
+    const int jl = min(j0 + RB, n) - 1;
+    const int Pf = s_pos[0], Pl = s_pos[jl - j0];
+    const int32_t* S = a.cols + (long long)bg * a.n_cols;
+    int lo = 0, hi = a.n_cols;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (S[mid] <= Pl - W) lo = mid + 1;
+        else hi = mid;
+    }
+    const int cnt1 = lo, nt1 = (cnt1 + KT - 1) / KT;
+    const int lo2 = max(0, Pf - W + 1) & ~7;
+    const int ntiles = nt1 + (Pl - lo2) / KT + 1;
+    const int jr = j0 + rs * 32 + l32;
+    const int P = jr < n ? s_pos[rs * 32 + l32] : -1;
+    const bool wave_rows = j0 + rs * 32 < n;
+    const int wPf = wave_rows ? s_pos[rs * 32] : 0;
+    const int wPl = wave_rows ? s_pos[min(j0 + rs * 32 + 31, n - 1) - j0] : -1;
+    const long long ldq = (long long)H * HD;
+
+    half8 qf[HD / 16];
+#pragma unroll
+    for (int ks = 0; ks < HD / 16; ++ks) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (jr < n) v = *(const uint4*)(a.q + ((long long)b * n + jr) * ldq + h * HD + ks * 16 + kg * 8);
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+        half8 hq;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            hq[2 * q] = (_Float16)__uint_as_float(wv[q] << 16);
+            hq[2 * q + 1] = (_Float16)__uint_as_float(wv[q] & 0xFFFF0000u);
+        }
+        qf[ks] = hq;
+    }
+    f32x16 oacc[HD / 32];
+#pragma unroll
+    for (int c = 0; c < HD / 32; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[c][i] = 0.f;
+    float m_i = -INFINITY, l_i = 0.f;
+
+    uint4 regs[PER];
+    int colr = INT_MAX;  // tile column of key tid (seg 1), staged like the operands
+    auto load_tile = [&](int t) {
+        const bool seg1 = t < nt1;
+        const int base = seg1 ? t * KT : lo2 + (t - nt1) * KT;
+        const int lim = seg1 ? cnt1 : Pl + 1;  // keys (rows or positions) below lim exist
+        const KVLayer& L = seg1 ? sc : fr;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int c = tid + p * NT;
+            regs[p] = make_uint4(0, 0, 0, 0);
+            if (c < NKC) {
+                const int r = c / CPR;
+                const int key = base + (r & 32) + flash_key_of_row(r & 31);
+                if (key < lim)
+                    regs[p] = *(const uint4*)((const u16*)L.base[0] + kv_row(L, b, g, key) * HD + (c % CPR) * 8);
+            } else {
+                const int cc = c - NKC;
+                const int blk = cc / HD, e = cc % HD;
+                const int k0 = base + blk * 8;
+                if (k0 < lim) regs[p] = mask_tail8(*(const uint4*)((const u16*)L.base[1] + v_elem(L, b, g, k0, e)), lim - k0);
+            }
+        }
+        if (tid < KT) colr = (seg1 && base + tid < cnt1) ? S[base + tid] : INT_MAX;
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int c = tid + p * NT;
+            if (c < NKC) {
+                *(uint4*)&Ks[buf][(c / CPR) * LDK + (c % CPR) * 8] = regs[p];
+            } else {
+                const int cc = c - NKC;
+                *(uint4*)&Vt[buf][(cc % HD) * LDV + (cc / HD) * 8] = regs[p];
+            }
+        }
+        if (tid < KT) s_col[buf][tid] = colr;
+    };
+    load_tile(0);
+    store_tile(0);
+    for (int t = 0; t < ntiles; ++t) {
+        const int cur = t & 1;
+        __syncthreads();
+        if (t + 1 < ntiles) load_tile(t + 1);
+        const bool seg1 = t < nt1;
+        const int pb = seg1 ? 0 : lo2 + (t - nt1) * KT;
+        // does any query of this wave see a key of the tile?
+        const bool live = wave_rows && (seg1 ? s_col[cur][0] <= wPl - W : (pb <= wPl && pb + KT - 1 > wPf - W));
+        if (live) {
+            f32x16 sv[2];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sv[hf][i] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < HD / 16; ++ks) {
+                    const half8 k8 = as_half8(*(const uint4*)&Ks[cur][(32 * hf + l32) * LDK + ks * 16 + kg * 8]);
+                    sv[hf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k8, qf[ks], sv[hf], 0, 0, 0);
+                }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int kx = 32 * hf + ((i < 8) ? 8 * kg + i : 16 + 8 * kg + (i - 8));
+                    const bool ok = seg1 ? s_col[cur][kx] <= P - W : (pb + kx <= P && pb + kx > P - W);
+                    if (!ok) sv[hf][i] = -INFINITY;
+                    mx = fmaxf(mx, sv[hf][i]);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_i, mx * sl2);
+            if (__builtin_amdgcn_ballot_w64(m_new > m_i)) {
+                const float alpha = (m_i == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_i - m_new);
+                l_i *= alpha;
+#pragma unroll
+                for (int c = 0; c < HD / 32; ++c)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[c][i] *= alpha;
+            }
+            m_i = m_new;
+            const float nm = (m_new == -INFINITY) ? 0.f : -m_new;
+            float rs_ = 0.f;
+            half8 pf[2][2];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+                for (int hq = 0; hq < 2; ++hq) {
+                    half8 pv;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float x = __builtin_amdgcn_exp2f(fmaf(sv[hf][8 * hq + i], sl2, nm));
+                        rs_ += x;
+                        pv[i] = (_Float16)x;
+                    }
+                    pf[hf][hq] = pv;
+                }
+            }
+            rs_ += __shfl_xor(rs_, 32);
+            l_i += rs_;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int c = 0; c < HD / 32; ++c) {
+                    const u16* vrow = &Vt[cur][(c * 32 + l32) * LDV + 32 * hf];
+                    const half8 va0 = as_half8(*(const uint4*)(vrow + 8 * kg));
+                    const half8 va1 = as_half8(*(const uint4*)(vrow + 16 + 8 * kg));
+                    oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va0, pf[hf][0], oacc[c], 0, 0, 0);
+                    oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va1, pf[hf][1], oacc[c], 0, 0, 0);
+                }
+        }
+        if (t + 1 < ntiles) store_tile(cur ^ 1);
+    }
+    if (jr < n && l_i > 0.f) {
+        const float inv = 1.f / l_i;
+        u16* orow = a.out + ((long long)b * n + jr) * ldq + h * HD;
+#pragma unroll
+        for (int c = 0; c < HD / 32; ++c)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int e0 = c * 32 + 8 * i4 + 4 * kg;
+                uint2 v;
+                v.x = pack_bf2(oacc[c][i4 * 4 + 0] * inv, oacc[c][i4 * 4 + 1] * inv);
+                v.y = pack_bf2(oacc[c][i4 * 4 + 2] * inv, oacc[c][i4 * 4 + 3] * inv);
+                *(uint2*)(orow + e0) = v;
+            }
+    }
+}
+
 // ---------------------------------------------------------------- sparse rows (VALU)
 // 32 consecutive K elements [e0, e0+32) of row (b, g, pos) reconstructed at loop k,
 // given that row's loop-2..k slots.
@@ -1332,6 +1532,23 @@ hipError_t attn_rows_main(const RowsAttn& a, hipStream_t st) {
             case 64: dense_hd<64>(a, G, st); break;
             default: dense_hd<128>(a, G, st); break;
         }
+    }
+    return hipGetLastError();
+}
+
+hipError_t attn_rows_prefill(const RowsAttn& a, const KVLayer& sc, const KVLayer& fr, hipStream_t st) {
+    const int G = a.H / a.kv.Hkv;
+    if (a.kv.hd != 128 || !a.cols || !a.qpos || a.n_rows < 1 || sc.Tmax % 8 || fr.Tmax % 8)
+        return hipErrorInvalidValue;
+    const int NW = G > 4 ? G : 4, RB = 32 * NW / G;
+    dim3 grid((a.n_rows + RB - 1) / RB, a.kv.Hkv, a.B);
+    const float sl2 = kLog2e / sqrtf(128.f);
+    switch (G) {
+        case 1: hipLaunchKernelGGL((attn_rows_pf_kernel<1>), grid, dim3(256), 0, st, a, sc, fr, sl2); break;
+        case 2: hipLaunchKernelGGL((attn_rows_pf_kernel<2>), grid, dim3(256), 0, st, a, sc, fr, sl2); break;
+        case 4: hipLaunchKernelGGL((attn_rows_pf_kernel<4>), grid, dim3(256), 0, st, a, sc, fr, sl2); break;
+        case 8: hipLaunchKernelGGL((attn_rows_pf_kernel<8>), grid, dim3(512), 0, st, a, sc, fr, sl2); break;
+        default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

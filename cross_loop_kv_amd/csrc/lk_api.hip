@@ -351,6 +351,8 @@ struct WS {
     float* out;        // decode: the step's output rows
     float* ps;         // decode: per-workgroup row sums of x^2 for the next RMSNorm ([d/8][8])
     float* tokrec;     // decode, lazy: float32 K/V reconstruction of the step's rows [R][B][2][Hkv][hd]
+    u16 *frk, *frv;    // prefill, lazy loops >= 2 (hd 128): float16 loop-k K/V at every prompt position
+    int fr_cap;        // rows per (b, g) of frk / frv (T rounded up to 64; 0: none)
     size_t total;
     long long part_floats;
 };
@@ -395,6 +397,10 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
     w.ids = (int32_t*)take((long long)B * 4);
     w.ps = (float*)take((d / 8 + 1) * 8 * 4);
     w.tokrec = (float*)take(hd_->lazy() && T == 1 ? (long long)c.n_shared * B * 2 * c.n_kv_heads * c.head_dim * 4 : 0);
+    w.fr_cap = (hd_->lazy() && T > 1 && c.n_loops >= 2 && c.head_dim == 128) ? (T + 63) / 64 * 64 : 0;
+    const long long fr_elems = (long long)B * c.n_kv_heads * w.fr_cap * c.head_dim;
+    w.frk = (u16*)take(fr_elems * 2);
+    w.frv = (u16*)take(fr_elems * 2);
     w.out = (float*)take((long long)B * d * 4);
     w.total = off;
     return w;
@@ -463,6 +469,8 @@ struct AttnPlan {
     float* mass;             // lazy loop 1: column mass output
     KVLayer scache;          // decode, loops >= 2: float16 reconstruction of the stable columns
     KVLayer ring;            // decode, loops >= 2: float16 window ring
+    KVLayer full;            // prefill, loops >= 2: float16 loop-k K/V of every prompt position
+                             // (full.base[0] == nullptr: the split row kernels instead)
 };
 
 // End the capture running on `st` and append what it recorded (if anything) as a
@@ -588,6 +596,22 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
                 return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
             LK_TRY(timed(h, TC_ATTN_DECODE_SPARSE, st, [=] { return lk::attn_rows_main(d, st); }));
             LK_HIP(lk::attn_rows_combine(d, st, io.fold));
+        } else if (ap.kind == ATTN_ROWS_SPARSE && io.rows_per_seq > 1 && ap.full.base[0]) {
+            // token-sparse prefill rows: the loop-k reconstruction is final for the stable
+            // columns (cached for decode too) and for every prompt position (workspace)
+            lk::RowsAttn gr{};
+            gr.B = a.B;
+            gr.kv = ap.read;
+            gr.k_loop = ap.k_loop;
+            gr.cols = ap.cols;
+            gr.n_cols = ap.n_cols;
+            gr.pos = ap.T - 1;
+            LK_HIP(lk::gather_recon(gr, lk::GATHER_ALL_S, ap.scache.Tmax, (u16*)ap.scache.base[0],
+                                    (u16*)ap.scache.base[1], st));
+            LK_HIP(lk::gather_recon(gr, lk::GATHER_RING, ap.full.Tmax, (u16*)ap.full.base[0], (u16*)ap.full.base[1],
+                                    st));
+            LK_TRY(timed(h, TC_ATTN_PREFILL_SPARSE, st,
+                         [=] { return lk::attn_rows_prefill(a, ap.scache, ap.full, st); }));
         } else {
             int chunk = kRowChunk;
             if (ap.kind == ATTN_ROWS_DENSE) chunk = dense_chunk(ncol_max);
@@ -851,6 +875,16 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
         }
         io.add = nullptr;
         if (K >= 2) LK_HIP(lk::delta_keys(w.h, w.h0, M, d, w.keys, st));
+        // decode caches: rows not written below stay zero
+        if (K >= 2)
+            LK_HIP(lk::fill_i32((int32_t*)(s->buf + s->lay.scache), 0, (long long)(s->lay.scache_bytes / 4), st));
+        KVLayer full{};
+        if (w.fr_cap) {
+            full = scache_layer(s, 2, 0);  // a float16 plain layer, re-pointed at the workspace
+            full.Tmax = w.fr_cap;
+            full.base[0] = w.frk;
+            full.base[1] = w.frv;
+        }
         for (int k = 2; k <= K; ++k) {
             if (s->f_tok) {
                 LK_HIP(hipMemcpyAsync(w.sel, s->f_tok + (long long)(k - 2) * B * n, (size_t)B * n * 4,
@@ -870,6 +904,8 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
                 ap.n_cols = s->lay.n_cols;
                 ap.window = h->z.window;
                 ap.T = T;
+                ap.scache = scache_layer(s, k, r);
+                ap.full = full;
                 lk::KVWrite kw{};
                 kw.kind = 2;
                 kw.layer = ap.read;
@@ -886,8 +922,8 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
             }
         }
         // The stable columns' and the prompt tail's loop-k reconstructions are final
-        // now: cache them (float16) for decode.  Rows not written here stay zero.
-        LK_HIP(lk::fill_i32((int32_t*)(s->buf + s->lay.scache), 0, (long long)(s->lay.scache_bytes / 4), st));
+        // now: cache them (float16) for decode (the stable columns already are when the
+        // loop used them through the cache).
         for (int k = 2; k <= K; ++k)
             for (int r = 0; r < R; ++r) {
                 lk::RowsAttn g{};
@@ -898,7 +934,8 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
                 g.n_cols = s->lay.n_cols;
                 g.pos = T - 1;
                 const KVLayer L = scache_layer(s, k, r);
-                LK_HIP(lk::gather_recon(g, lk::GATHER_ALL_S, s->lay.ncs, (u16*)L.base[0], (u16*)L.base[1], st));
+                if (!w.fr_cap)
+                    LK_HIP(lk::gather_recon(g, lk::GATHER_ALL_S, s->lay.ncs, (u16*)L.base[0], (u16*)L.base[1], st));
                 const KVLayer Rg = scache_layer(s, k, r, true);
                 LK_HIP(lk::gather_recon(g, lk::GATHER_RING, s->lay.wr, (u16*)Rg.base[0], (u16*)Rg.base[1], st));
             }

@@ -138,6 +138,12 @@ struct RowsAttn {
 //                 rows are left as they are).
 enum { GATHER_ALL_S = 1, GATHER_RING = 3 };
 hipError_t gather_recon(const RowsAttn& a, int mode, int ncap, u16* kc, u16* vc, hipStream_t st);
+// Token-sparse prefill rows (rows_per_seq > 1, hd 128): every kept row q of sequence b
+// (position qpos) attends over the cache rows of sc whose column cols[r] <= qpos - window
+// and over the positions (qpos - window, qpos] of fr (float16 plain layers: K rows, V
+// 8-key interleaved); writes `out` directly.  hipErrorInvalidValue if the shape is not
+// taken.
+hipError_t attn_rows_prefill(const RowsAttn& a, const KVLayer& sc, const KVLayer& fr, hipStream_t st);
 // attn_rows_main writes the per-split partials; attn_rows_combine merges them into `out`.
 hipError_t attn_rows_main(const RowsAttn& a, hipStream_t st);
 // packed_out: out in the lane-packed order of the decode products (at most 8 rows).
