@@ -49,6 +49,7 @@ class Shape:
     n_coda: int
     rms_eps: float = 1e-5
     rope_theta: float = 10000.0
+    input_reinject: bool = False  # the prelude output is fed into every loop k >= 2
 
     @property
     def n_layers_stored(self) -> int:

@@ -34,6 +34,14 @@ not given on any page):
   carried rows have key 0); the n largest keys are recomputed, the rest carry
   forward unchanged.  A recomputed query i attends over
   (S intersect [0, i]) union [max(0, i-w+1), i] of the loop-k reconstruction.
+* input re-injection (aiboss88.com tutorial, step 3: a structure that passes the
+  input representation into every loop): with ``shape.input_reinject`` the prelude
+  output e is added to the state before every loop k >= 2 (loop 1 starts from e), as
+  (state + e) + loop_emb[k-1]; in lazy mode only the recomputed rows receive it, like
+  the loop embedding.
+* loop count (aiboss88.com tutorial, step 3: n_recurrent_loops picked by the caller
+  with the same checkpoint): ``n_loops`` (default shape.n_loops) runs loops 1..n_loops
+  of a store laid out for shape.n_loops loops; prefill and decode use the same count.
 * KV store: loop 1 is the base (working precision, or int8 groups with a zero
   previous reconstruction); loop k >= 2 stores, for recomputed rows only,
   r = KV_k - recon_{k-1} quantized (16 bits: the full KV_k row instead), so
@@ -154,9 +162,13 @@ class LoopedOracle:
     """
 
     def __init__(self, shape, lazy, weights, batch: int, max_tokens: int,
-                 operand_precision: str = "fp32"):
+                 operand_precision: str = "fp32", n_loops=None):
         if operand_precision not in ("fp32", "bf16"):
             raise ValueError("operand_precision must be fp32 or bf16")
+        self.K = shape.n_loops if n_loops is None else int(n_loops)
+        if not 1 <= self.K <= shape.n_loops:
+            raise ValueError("n_loops must be in [1, shape.n_loops]")
+        self.inject = bool(getattr(shape, "input_reinject", False))
         self.bf16 = operand_precision == "bf16"
         self.s = shape
         self.lz = lazy
@@ -345,21 +357,28 @@ class LoopedOracle:
         pos = np.arange(T)
         h = self.w["tok_emb"][ids_b].astype(F32)
         h = self._prelude_idx(b, h, pos)
+        e = h.copy()
         P = s.n_prelude
         if self.lz.mode == "per_loop":
-            for k in range(1, s.n_loops + 1):
-                h = (h + self.w["loop_emb"][k - 1]).astype(F32)
+            for k in range(1, self.K + 1):
+                h = self._loop_input(h, e, k)
                 for r in range(s.n_shared):
                     h = self._shared_dense(P + r, h, pos, self.loop_k[k - 1][r],
                                            self.loop_v[k - 1][r], b)
         elif self.lz.mode == "last_loop":
-            for k in range(1, s.n_loops + 1):
-                h = (h + self.w["loop_emb"][k - 1]).astype(F32)
+            for k in range(1, self.K + 1):
+                h = self._loop_input(h, e, k)
                 for r in range(s.n_shared):
                     h = self._shared_dense(P + r, h, pos, self.last_k[r], self.last_v[r], b)
         else:
             h = self._lazy_prefill_loops(b, h, pos)
         return self._coda(b, h, pos)
+
+    def _loop_input(self, h, e, k):
+        """State entering loop k: (h + e if re-injecting and k >= 2) + loop_emb[k-1]."""
+        if self.inject and k >= 2:
+            h = (h + e).astype(F32)
+        return (h + self.w["loop_emb"][k - 1]).astype(F32)
 
     def _shared_dense(self, li, h, pos, kc, vc, b):
         q, k, v = self._qkv(li, h, pos)
@@ -372,7 +391,7 @@ class LoopedOracle:
 
     def _lazy_prefill_loops(self, b, h0, pos):
         s, lz = self.s, self.lz
-        P, R, K, T = s.n_prelude, s.n_shared, s.n_loops, pos.shape[0]
+        P, R, K, T = s.n_prelude, s.n_shared, self.K, pos.shape[0]
         allc = np.arange(T)
         # loop 1: dense, writes the base, accumulates the column mass, picks S.
         x = (h0 + self.w["loop_emb"][0]).astype(F32)
@@ -404,7 +423,7 @@ class LoopedOracle:
             I = np.asarray(I, dtype=np.int64)
             self.sel[(k, b)] = I.astype(np.int32)
             self.slot[k - 1, b, I] = np.arange(n, dtype=np.int32)
-            xs = (h_prev[I] + self.w["loop_emb"][k - 1]).astype(F32)
+            xs = self._loop_input(h_prev[I], h0[I], k)
             for r in range(R):
                 q, kk, vv = self._qkv(P + r, xs, I)
                 self._res_write(k, r, b, I, np.arange(n), kk.transpose(1, 0, 2),
@@ -444,13 +463,14 @@ class LoopedOracle:
 
     def _decode_one(self, b, tok, t):
         s, lz = self.s, self.lz
-        P, R, K = s.n_prelude, s.n_shared, s.n_loops
+        P, R, K = s.n_prelude, s.n_shared, self.K
         pos = np.array([t])
         h = self.w["tok_emb"][tok][None, :].astype(F32)
         h = self._prelude_idx(b, h, pos)
+        e = h.copy()
         if lz.mode in ("per_loop", "last_loop"):
             for k in range(1, K + 1):
-                h = (h + self.w["loop_emb"][k - 1]).astype(F32)
+                h = self._loop_input(h, e, k)
                 for r in range(R):
                     if lz.mode == "per_loop":
                         kc, vc = self.loop_k[k - 1][r], self.loop_v[k - 1][r]
@@ -461,7 +481,7 @@ class LoopedOracle:
             allc = np.arange(t + 1)
             slot = self.n_sel + (t - self.T)
             for k in range(1, K + 1):
-                h = (h + self.w["loop_emb"][k - 1]).astype(F32)
+                h = self._loop_input(h, e, k)
                 if k >= 2:
                     self.slot[k - 1, b, t] = slot
                 for r in range(R):

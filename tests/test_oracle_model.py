@@ -88,6 +88,69 @@ def test_dense_looped_equals_unrolled_stack(mk, K):
     assert max_abs_rel(out[0], ref0) > 1e-3
 
 
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_input_reinjection_equals_unrolled_stack(mode):
+    """The re-injection variant (aiboss88.com tutorial, step 3: the input representation
+    passed into every loop) against an independently written float64 torch stack that
+    adds the prelude output back before loops 2..K; it must differ from no re-injection."""
+    s = small_shape(n_loops=3, input_reinject=True)
+    W = I.gen_weights(s, seed=13)
+    ids = I.gen_prompt_ids(s, 2, 20, seed=14)
+    dec = I.gen_decode_ids(s, 2, 3, seed=15)
+    _, out, dout, depth = run_oracle(s, I.Lazy(mode=mode), W, ids, dec)
+    assert depth == accounting.effective_depth(s)
+    for b in range(2):
+        full = np.concatenate([ids[b], dec[:, b]])
+        ref = torch_ref.unrolled_forward(W, s, full, reinject=True).numpy()
+        assert max_abs_rel(out[b], ref[:20]) < 2e-5
+        if mode == "per_loop":   # last_loop decode reads the last pass's KV only
+            assert max_abs_rel(dout[:, b], ref[20:]) < 2e-5
+    ref0 = torch_ref.unrolled_forward(W, s, ids[0], reinject=False).numpy()
+    assert max_abs_rel(out[0], ref0) > 1e-3
+
+
+def test_input_reinjection_is_inert_at_one_loop():
+    """Loop 1 starts from the prelude output: with K = 1 re-injection changes nothing."""
+    s = small_shape(n_loops=1)
+    W = I.gen_weights(s, seed=16)
+    ids = I.gen_prompt_ids(s, 1, 18, seed=17)
+    dec = I.gen_decode_ids(s, 1, 2, seed=18)
+    s1 = small_shape(n_loops=1, input_reinject=True)
+    for lz in (I.Lazy(mode="per_loop"), I.Lazy(mode="lazy", rho=0.5, top_s=6, window=4, base_bits=8, res_bits=4)):
+        _, a, ad, _ = run_oracle(s, lz, W, ids, dec)
+        _, c, cd, _ = run_oracle(s1, lz, W, ids, dec)
+        np.testing.assert_array_equal(a, c)
+        np.testing.assert_array_equal(ad, cd)
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "lazy"])
+@pytest.mark.parametrize("reinject", [False, True])
+def test_call_loop_count_equals_model_with_that_many_loops(mode, reinject):
+    """n_recurrent_loops chosen per call (aiboss88.com tutorial, step 3): running 2 of
+    the 4 loops of a store laid out for 4 equals a model built with 2 loops (same
+    weights, loop-embedding rows 0..1), bit for bit, prefill and decode; the depth is
+    P + R*2 + Q."""
+    s4 = small_shape(n_loops=4, input_reinject=reinject)
+    s2 = small_shape(n_loops=2, input_reinject=reinject)
+    W = I.gen_weights(s4, seed=19)
+    W2 = dict(W)
+    W2["loop_emb"] = W["loop_emb"][:2].copy()
+    T, steps = 22, 3
+    ids = I.gen_prompt_ids(s4, 2, T, seed=20)
+    dec = I.gen_decode_ids(s4, 2, steps, seed=21)
+    lz = (I.Lazy(mode="lazy", rho=0.4, top_s=8, window=5, base_bits=8, res_bits=4) if mode == "lazy"
+          else I.Lazy(mode="per_loop"))
+    m4 = LoopedOracle(s4, lz, W, 2, T + steps, n_loops=2)
+    a = m4.prefill(ids)
+    assert m4.depth == accounting.effective_depth(s2)
+    ad = np.stack([m4.decode(d) for d in dec])
+    _, c, cd, _ = run_oracle(s2, lz, W2, ids, dec)
+    np.testing.assert_array_equal(a, c)
+    np.testing.assert_array_equal(ad, cd)
+    with pytest.raises(ValueError):
+        LoopedOracle(s4, lz, W, 2, T + steps, n_loops=5)
+
+
 def test_effective_depth_page_instances():
     mk = lambda p, r, k, q: I.Shape(1, 1, 1, 1, 32, 1, "gelu", p, r, k, q)
     # discosf.com section 3.1: 6 independent + 6 looped x3 + 6 independent -> depth 30, 18 stored
@@ -103,9 +166,9 @@ def test_effective_depth_page_instances():
     assert [accounting.effective_depth(mk(8, 9, k, 7)) for k in (1, 2, 3, 4)] == [24, 33, 42, 51]
 
 
-@pytest.mark.parametrize("mk", [tiny_shape, small_shape])
-def test_lazy_rho1_all_columns_is_bit_identical_to_dense(mk):
-    s = mk()
+@pytest.mark.parametrize("mk,reinject", [(tiny_shape, False), (small_shape, False), (small_shape, True)])
+def test_lazy_rho1_all_columns_is_bit_identical_to_dense(mk, reinject):
+    s = mk(input_reinject=reinject)
     W = I.gen_weights(s, seed=9)
     T, steps = 24, 4
     ids = I.gen_prompt_ids(s, 2, T, seed=10)

@@ -58,12 +58,13 @@ def layer(W, x, shape, mask=None):
     return x + f @ _t(W["w_down"]).T
 
 
-def unrolled_forward(weights, shape, ids, loops=None, loop_emb=True):
+def unrolled_forward(weights, shape, ids, loops=None, loop_emb=True, reinject=False):
     """Standard Transformer over the unrolled weight-tied stack.
 
-    Layer sequence: prelude layers, then for each loop k the loop embedding row
-    k-1 is added and the shared layers are applied, then the coda layers, then the
-    final RMSNorm.  ``ids`` is one sequence [T]; returns float64 [T, d].
+    Layer sequence: prelude layers, then for each loop k (with ``reinject``, the
+    prelude output is first added back to the state for k >= 2) the loop embedding
+    row k-1 is added and the shared layers are applied, then the coda layers, then
+    the final RMSNorm.  ``ids`` is one sequence [T]; returns float64 [T, d].
     """
     K = shape.n_loops if loops is None else loops
     L = weights["layers"]
@@ -71,7 +72,10 @@ def unrolled_forward(weights, shape, ids, loops=None, loop_emb=True):
     P, R = shape.n_prelude, shape.n_shared
     for li in range(P):
         x = layer(L[li], x, shape)
+    e = x
     for k in range(K):
+        if reinject and k >= 1:
+            x = x + e
         if loop_emb:
             x = x + _t(weights["loop_emb"][k])
         for r in range(R):
