@@ -33,7 +33,7 @@ class lk_model_cfg(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn_dim", C.c_int32),
                 ("ffn_act", C.c_int32), ("n_prelude", C.c_int32), ("n_shared", C.c_int32),
                 ("n_loops", C.c_int32), ("n_coda", C.c_int32), ("rms_eps", C.c_float),
-                ("rope_theta", C.c_float)]
+                ("rope_theta", C.c_float), ("input_reinject", C.c_int32)]
 
 
 class lk_lazy_cfg(C.Structure):
@@ -71,6 +71,7 @@ _SIGS = {
     "lk_kv_store_bytes_used": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
     "lk_kv_store_cache_bytes": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t)]),
     "lk_kv_store_length": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32)]),
+    "lk_kv_store_set_loops": (C.c_int, [C.c_void_p, C.c_int32]),
     "lk_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.POINTER(C.c_size_t)]),
     "lk_looped_prefill": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                     C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
@@ -173,6 +174,10 @@ def lk_kv_store_length(s: int) -> int:
     return t.value
 
 
+def lk_kv_store_set_loops(s: int, n: int) -> None:
+    _check(lib().lk_kv_store_set_loops(s, n))
+
+
 def lk_workspace_bytes(h: int, batch: int, tokens: int) -> int:
     n = C.c_size_t()
     _check(lib().lk_workspace_bytes(h, batch, tokens, C.byref(n)))
@@ -259,7 +264,8 @@ def lk_dbg_gemm_epi(d_a, d_w, epi, d_c, d_out, M, N, K, stream=None) -> None:
 def model_cfg(shape) -> lk_model_cfg:
     return lk_model_cfg(shape.vocab, shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim,
                         shape.ffn_dim, ACTS[shape.ffn_act], shape.n_prelude, shape.n_shared,
-                        shape.n_loops, shape.n_coda, shape.rms_eps, shape.rope_theta)
+                        shape.n_loops, shape.n_coda, shape.rms_eps, shape.rope_theta,
+                        int(getattr(shape, "input_reinject", False)))
 
 
 def lazy_cfg(lz) -> lk_lazy_cfg:
@@ -292,6 +298,11 @@ class Store:
 
     def length(self) -> int:
         return lk_kv_store_length(self.s)
+
+    def set_loops(self, n: int):
+        """Loop count for the next prefill and its decode steps (1..the model's K)."""
+        lk_kv_store_set_loops(self.s, n)
+        self.loops = n
 
     def cache_bytes(self) -> int:
         return lk_kv_store_cache_bytes(self.s)
@@ -427,8 +438,11 @@ class LoopedModel:
             self._ws_bytes = need
         return self._ws, need
 
-    def store(self, batch: int, prompt: int, max_tokens: int) -> Store:
-        return Store(self, batch, prompt, max_tokens)
+    def store(self, batch: int, prompt: int, max_tokens: int, loops: Optional[int] = None) -> Store:
+        st = Store(self, batch, prompt, max_tokens)
+        if loops is not None:
+            st.set_loops(loops)
+        return st
 
     def prefill(self, store: Store, ids, out=None):
         import torch

@@ -70,6 +70,12 @@ __global__ __launch_bounds__(kThreads) void add_rows_kernel(float* x, const u16*
     for (int j = threadIdx.x; j < d; j += kThreads) row[j] = row[j] + bf2f(add[j]);
 }
 
+__global__ void add_f32_kernel(float* x, const float* y, long long n) {
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+         i += (long long)gridDim.x * blockDim.x)
+        x[i] = x[i] + y[i];
+}
+
 __global__ void copy_f32_kernel(const float* s, float* d, long long n) {
     for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
          i += (long long)gridDim.x * blockDim.x)
@@ -104,13 +110,18 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(const float* a, const f
 
 __global__ __launch_bounds__(kThreads) void gather_kernel(const float* h, const int32_t* idx, int n,
                                                           int T, int d, const u16* add, float* xc,
-                                                          int32_t* slot_map, int Tmax) {
+                                                          int32_t* slot_map, int Tmax, const float* add_src) {
     const int r = blockIdx.x;  // compact row b*n + j
     const int b = r / n, j = r % n;
     const int i = idx[r];
     const float* src = h + ((long long)b * T + i) * d;
+    const float* src2 = add_src ? add_src + ((long long)b * T + i) * d : nullptr;
     float* dst = xc + (long long)r * d;
-    for (int c = threadIdx.x; c < d; c += kThreads) dst[c] = src[c] + (add ? bf2f(add[c]) : 0.f);
+    for (int c = threadIdx.x; c < d; c += kThreads) {
+        float v = src[c];
+        if (src2) v = v + src2[c];
+        dst[c] = v + (add ? bf2f(add[c]) : 0.f);
+    }
     if (slot_map && threadIdx.x == 0) slot_map[(long long)b * Tmax + i] = j;
 }
 
@@ -394,6 +405,10 @@ hipError_t add_rows(float* x, const u16* add, int rows, int d, hipStream_t st) {
     return hipGetLastError();
 }
 
+hipError_t add_f32(float* x, const float* y, long long n, hipStream_t st) {
+    hipLaunchKernelGGL(add_f32_kernel, dim3(grid_for(n)), dim3(kThreads), 0, st, x, y, n);
+    return hipGetLastError();
+}
 hipError_t copy_f32(const float* src, float* dst, long long n, hipStream_t st) {
     hipLaunchKernelGGL(copy_f32_kernel, dim3(grid_for(n)), dim3(kThreads), 0, st, src, dst, n);
     return hipGetLastError();
@@ -417,9 +432,9 @@ hipError_t delta_keys(const float* a, const float* b, int rows, int d, float* ke
 }
 
 hipError_t gather_rows(const float* h, const int32_t* idx, int B, int n, int T, int d, const u16* add,
-                       float* xc, int32_t* slot_map, int Tmax, hipStream_t st) {
+                       float* xc, int32_t* slot_map, int Tmax, hipStream_t st, const float* add_src) {
     hipLaunchKernelGGL(gather_kernel, dim3(B * n), dim3(kThreads), 0, st, h, idx, n, T, d, add, xc,
-                       slot_map, Tmax);
+                       slot_map, Tmax, add_src);
     return hipGetLastError();
 }
 

@@ -294,12 +294,14 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
     const bool out_lane = grp < 2 && c16 < 8;
     const int col = blockIdx.x * 8 + (c16 & 7);
     float c_pre[4] = {0.f, 0.f, 0.f, 0.f};
+    float r_pre[4] = {0.f, 0.f, 0.f, 0.f};
     float addv = 0.f, gainv = 0.f;
     if (EPI == EPI_ADD && w == 0 && out_lane) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = (grp & 1) * 4 + i;
             if (m < M) c_pre[i] = C[(long long)m * N + col];
+            if (PREP && io.add_rows && m < M) r_pre[i] = io.add_rows[(long long)m * N + col];
         }
         if (PREP && io.add_vec) addv = bf2f(io.add_vec[col]);
         if (PREP) gainv = bf2f(io.next_gain[col]);
@@ -364,6 +366,8 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
             C[o] = v0;
         } else if (EPI == EPI_ADD) {
             float x = c_pre[i] + v0;
+            if (PREP && io.x_save) io.x_save[o] = x;
+            if (PREP && io.add_rows) x = x + r_pre[i];
             if (PREP && io.add_vec) x = x + addv;
             C[o] = x;
             if (PREP) {
@@ -715,10 +719,14 @@ hipError_t gemm_fold_norm(const u16* xg, const float* ps, int nparts, float eps,
 }
 
 hipError_t gemm_fold_add(const u16* A, const u16* Wp, int M, int N, int K, float* x, const u16* add_vec,
-                         const u16* next_gain, u16* xg_out, float* ps_out, hipStream_t st) {
+                         const u16* next_gain, u16* xg_out, float* ps_out, hipStream_t st, const float* add_rows,
+                         float* x_save) {
     if (!fold_ok(M, N, K)) return hipErrorInvalidValue;
+    if ((add_rows || x_save) && !next_gain) return hipErrorInvalidValue;
     FoldIO io{};
     io.add_vec = add_vec;
+    io.add_rows = add_rows;
+    io.x_save = x_save;
     io.next_gain = next_gain;
     io.xg_out = xg_out;
     io.ps_out = ps_out;

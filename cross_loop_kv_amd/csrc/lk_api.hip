@@ -153,6 +153,7 @@ struct lk_kv_store {
     const int32_t* f_tok;
     const int32_t* f_cols;
     int keep_codes;
+    int K;  // loops the store runs (<= the model's n_loops)
 };
 
 namespace {
@@ -230,14 +231,14 @@ void store_bytes(const lk_kv_store* s, size_t* shared, size_t* total) {
         return bits == 16 ? 2 * n : n * bits / 8 + (n / 32) * 2;
     };
     if (h->z.mode == LK_MODE_PER_LOOP) {
-        sh = (long long)c.n_shared * c.n_loops * B * t * E * 2;
+        sh = (long long)c.n_shared * s->K * B * t * E * 2;
     } else if (h->z.mode == LK_MODE_LAST_LOOP) {
         sh = (long long)c.n_shared * B * t * E * 2;
     } else if (t > 0) {
         const long long stored = (long long)s->lay.n_sel + (t - s->Tp);
         sh = (long long)c.n_shared * B * t * rowb(E, h->z.base_bits) +
-             (long long)(c.n_loops - 1) * c.n_shared * B * stored * rowb(E, h->z.res_bits) +
-             (long long)(c.n_loops - 1) * B * t * 4 + (long long)c.n_shared * B * c.n_kv_heads * s->lay.n_cols * 4;
+             (long long)(s->K - 1) * c.n_shared * B * stored * rowb(E, h->z.res_bits) +
+             (long long)(s->K - 1) * B * t * 4 + (long long)c.n_shared * B * c.n_kv_heads * s->lay.n_cols * 4;
     }
     *shared = (size_t)sh;
     *total = (size_t)(sh + dense);
@@ -371,7 +372,7 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
         return base ? (void*)(base + o) : nullptr;
     };
     w.h = (float*)take(M * d * 4);
-    w.h0 = (float*)take(hd_->lazy() ? M * d * 4 : 0);
+    w.h0 = (float*)take(hd_->lazy() || c.input_reinject ? M * d * 4 : 0);
     w.xc = (float*)take(hd_->lazy() ? (long long)B * n * d * 4 : 0);
     // bf16 operands of the decode products are lane-packed over 8 rows: at least 8 rows
     const long long M8 = M < 8 ? 8 : M;
@@ -422,6 +423,7 @@ int check_cfg(const lk_model_cfg* c, const lk_lazy_cfg* z) {
     if ((c->n_heads * c->head_dim) % 64) return fail(LK_ERR_UNSUPPORTED, "n_heads * head_dim must be a multiple of 64");
     if (c->n_kv_heads * c->head_dim > 4096) return fail(LK_ERR_UNSUPPORTED, "n_kv_heads * head_dim > 4096");
     if (c->ffn_act != LK_ACT_GELU && c->ffn_act != LK_ACT_SWIGLU) return fail(LK_ERR_INVALID_ARG, "bad ffn_act");
+    if (c->input_reinject != 0 && c->input_reinject != 1) return fail(LK_ERR_INVALID_ARG, "input_reinject must be 0 or 1");
     if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(LK_ERR_INVALID_ARG, "bad eps / theta");
     if (z->mode != LK_MODE_PER_LOOP && z->mode != LK_MODE_LAST_LOOP && z->mode != LK_MODE_LAZY)
         return fail(LK_ERR_INVALID_ARG, "bad mode");
@@ -453,6 +455,12 @@ struct LayerIO {
     int nparts;
     const u16* next_gain;
     const u16* next_add;
+    // Input re-injection (decode): inj = rows added to x before this layer (row-major
+    // float32, added before `add`); with folded norms next_inj is added by this layer's
+    // down projection before next_add, and save_x receives x before those adds.
+    const float* inj;
+    const float* next_inj;
+    float* save_x;
 };
 
 enum AttnKind { ATTN_PREFILL_DENSE, ATTN_ROWS_DENSE, ATTN_ROWS_SPARSE };
@@ -518,6 +526,7 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
     // decode-sized row counts fold the RMSNorm into the skinny GEMMs
     const bool fused_norm = io.M <= 16;
     const lk_handle::Packed PW = io.fold ? h->PL[li] : lk_handle::Packed{};
+    if (io.inj) LK_HIP(lk::add_f32(io.x, io.inj, (long long)io.M * d, st));
     if (io.fold) {
         LK_TRY(timed(h, gcls, st, [=] {
             return lk::gemm_fold_norm(w.xn, w.ps, io.nparts, c.rms_eps, PW.wqkv, io.M, h->qkv_w(), d,
@@ -638,7 +647,7 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
         }));
         LK_TRY(timed(h, gcls, st, [=] {
             return lk::gemm_fold_add(w.act, PW.w_down, io.M, d, c.ffn_dim, io.x, io.next_add, io.next_gain, w.xn,
-                                     w.ps, st);
+                                     w.ps, st, io.next_inj, io.save_x);
         }));
         return LK_OK;
     }
@@ -725,6 +734,7 @@ int lk_kv_store_alloc(lk_handle* h, int32_t batch, int32_t prompt_tokens, int32_
     s->Tmax = max_tokens;
     s->Tpad = pad8(max_tokens);
     s->t = 0;
+    s->K = h->c.n_loops;
     s->prefilled = false;
     s->lay = lay;
     s->buf = (char*)dev_buf;
@@ -760,6 +770,14 @@ int lk_kv_store_bytes_used(const lk_kv_store* s, size_t* shared, size_t* total) 
 int lk_kv_store_cache_bytes(const lk_kv_store* s, size_t* bytes) {
     if (!s || !bytes) return fail(LK_ERR_INVALID_ARG, "null argument");
     *bytes = s->lay.scache_bytes;
+    return LK_OK;
+}
+
+int lk_kv_store_set_loops(lk_kv_store* s, int32_t n_loops) {
+    if (!s) return fail(LK_ERR_INVALID_ARG, "null store");
+    if (s->prefilled || s->t > 0) return fail(LK_ERR_STATE, "the loop count is set before prefill");
+    if (n_loops < 1 || n_loops > s->h->c.n_loops) return fail(LK_ERR_INVALID_ARG, "n_loops outside [1, model n_loops]");
+    s->K = n_loops;
     return LK_OK;
 }
 
@@ -824,8 +842,9 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
     if ((uintptr_t)d_ws % kAlign) return fail(LK_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     hipStream_t st = (hipStream_t)stream;
     const lk_model_cfg& c = h->c;
-    const int P = c.n_prelude, R = c.n_shared, K = c.n_loops, Q = c.n_coda, d = c.d_model;
+    const int P = c.n_prelude, R = c.n_shared, K = s->K, Q = c.n_coda, d = c.d_model;
     const int M = B * T;
+    const bool inject = c.input_reinject != 0;
     h->timer.in_call = 0;
     if (h->lazy())
         LK_HIP(lk::fill_i32(slot_map(s, 2), -1, (long long)(K - 1) * B * s->Tpad, st));
@@ -843,8 +862,10 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
         LK_TRY(run_layer(h, li, io, plain_write(dense_plan.read), dense_plan, w, st));
     }
     if (!h->lazy()) {
+        if (inject) LK_HIP(lk::copy_f32(w.h, w.h0, (long long)M * d, st));  // e = prelude output
         for (int k = 1; k <= K; ++k)
             for (int r = 0; r < R; ++r) {
+                if (inject && k >= 2 && r == 0) LK_HIP(lk::add_f32(w.h, w.h0, (long long)M * d, st));
                 io.add = (r == 0) ? h->lemb + (long long)(k - 1) * d : nullptr;
                 dense_plan.read = loop_layer(s, k, r);
                 LK_TRY(run_layer(h, P + r, io, plain_write(dense_plan.read), dense_plan, w, st));
@@ -893,7 +914,7 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
                 LK_HIP(lk::topk_rows(w.keys, B, T, n, w.sel, st));
             }
             LK_HIP(lk::gather_rows(w.h, w.sel, B, n, T, d, h->lemb + (long long)(k - 1) * d, w.xc,
-                                   slot_map(s, k), s->Tpad, st));
+                                   slot_map(s, k), s->Tpad, st, inject ? w.h0 : nullptr));
             LayerIO cio{w.xc, B * n, n, w.sel, 0, nullptr};
             for (int r = 0; r < R; ++r) {
                 AttnPlan ap{};
@@ -997,8 +1018,9 @@ int pack_decode_weights(lk_handle* h, void* buf, hipStream_t st) {
 // host's copy of the position, so the same launches serve every step.
 int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
     const lk_model_cfg& c = h->c;
-    const int P = c.n_prelude, R = c.n_shared, K = c.n_loops, Q = c.n_coda, d = c.d_model;
+    const int P = c.n_prelude, R = c.n_shared, K = s->K, Q = c.n_coda, d = c.d_model;
     const int B = s->B;
+    const bool inject = c.input_reinject != 0;
     const int32_t* dpos = dev_pos(s);
     h->timer.in_call = 0;
     // The layer applications of one step, in order.
@@ -1007,6 +1029,7 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
         const u16* add;
         lk::KVWrite kw;
         AttnPlan ap;
+        bool inj;  // re-injection before this layer (first shared layer of loops >= 2)
     };
     std::vector<App> apps;
     apps.reserve((size_t)P + (size_t)R * K + Q);
@@ -1017,14 +1040,15 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
     dense.dpos = dpos;
     for (int li = 0; li < P; ++li) {
         dense.read = dense_layer(s, li);
-        apps.push_back({li, nullptr, plain_write(dense.read), dense});
+        apps.push_back({li, nullptr, plain_write(dense.read), dense, false});
     }
     for (int k = 1; k <= K; ++k) {
         for (int r = 0; r < R; ++r) {
             const u16* add = (r == 0) ? h->lemb + (long long)(k - 1) * d : nullptr;
+            const bool inj = inject && k >= 2 && r == 0;
             if (!h->lazy()) {
                 dense.read = loop_layer(s, k, r);
-                apps.push_back({P + r, add, plain_write(dense.read), dense});
+                apps.push_back({P + r, add, plain_write(dense.read), dense, inj});
                 continue;
             }
             AttnPlan ap{};
@@ -1054,16 +1078,18 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
                 kw.slot_base = (long long)s->lay.n_sel - s->Tp;  // slot = n_sel + (t - T)
                 kw.slot_map_k = slot_map(s, k);
             }
-            apps.push_back({P + r, add, kw, ap});
+            apps.push_back({P + r, add, kw, ap, inj});
         }
     }
     for (int j = 0; j < Q; ++j) {
         dense.read = dense_layer(s, P + j);
-        apps.push_back({P + R + j, nullptr, plain_write(dense.read), dense});
+        apps.push_back({P + R + j, nullptr, plain_write(dense.read), dense, false});
     }
     // Folded norms: every projection input is prepared by the kernel that produced x.
     const bool fold = B <= 8 && h->pk_buf != nullptr;
     LK_HIP(lk::embed(w.ids, h->tok, w.h, B, d, c.vocab, st));
+    // re-injection: e = the prelude output (the embedding when there is no prelude)
+    if (inject && K >= 2 && P == 0) LK_HIP(lk::copy_f32(w.h, w.h0, (long long)B * d, st));
     if (fold)
         LK_HIP(lk::norm_prep(w.h, apps[0].add, (const u16*)h->L[apps[0].li].attn_norm, B, d, w.xn, w.ps, st));
     for (size_t i = 0; i < apps.size(); ++i) {
@@ -1074,7 +1100,13 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
         if (i + 1 < apps.size()) {
             io.next_gain = (const u16*)h->L[apps[i + 1].li].attn_norm;
             io.next_add = apps[i + 1].add;
+            if (fold && apps[i + 1].inj) io.next_inj = w.h0;
         }
+        if (inject && K >= 2 && P > 0) {
+            if (fold && i + 1 == (size_t)P) io.save_x = w.h0;  // x after the last prelude layer
+            if (!fold && i == (size_t)P) LK_HIP(lk::copy_f32(w.h, w.h0, (long long)B * d, st));
+        }
+        if (!fold && a.inj) io.inj = w.h0;
         LK_TRY(run_layer(h, a.li, io, a.kw, a.ap, w, st));
     }
     LK_HIP(lk::rmsnorm(w.h, nullptr, h->fnorm, c.rms_eps, B, d, nullptr, w.out, st));

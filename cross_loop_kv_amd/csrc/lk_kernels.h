@@ -19,13 +19,15 @@ hipError_t rmsnorm(float* x, const u16* add, const u16* gain, float eps, int row
                    u16* out_bf, float* out_f32, hipStream_t st);
 hipError_t add_rows(float* x, const u16* add, int rows, int d, hipStream_t st);
 hipError_t copy_f32(const float* src, float* dst, long long n, hipStream_t st);
+hipError_t add_f32(float* x, const float* y, long long n, hipStream_t st);  // x += y
 hipError_t fill_i32(int32_t* p, int32_t v, long long n, hipStream_t st);
 hipError_t fill_f32(float* p, float v, long long n, hipStream_t st);
 hipError_t add_i32(int32_t* p, int32_t v, hipStream_t st);  // *p += v (one thread)
 hipError_t delta_keys(const float* a, const float* b, int rows, int d, float* key, hipStream_t st);
-// xc[b*n + j] = h[b*T + idx[b*n + j]] + add; slot_map[b*Tmax + idx] = j when slot_map != nullptr.
+// xc[b*n + j] = (h[b*T + idx[b*n + j]] (+ add_src[same row])) + add; slot_map[b*Tmax + idx] = j
+// when slot_map != nullptr.
 hipError_t gather_rows(const float* h, const int32_t* idx, int B, int n, int T, int d, const u16* add,
-                       float* xc, int32_t* slot_map, int Tmax, hipStream_t st);
+                       float* xc, int32_t* slot_map, int Tmax, hipStream_t st, const float* add_src = nullptr);
 // key[b*T + idx] = ||xc - h[idx]||^2 (when key != nullptr), then h[b*T + idx] = xc.
 hipError_t scatter_rows(const float* xc, const int32_t* idx, int B, int n, int T, int d, float* h,
                         float* key, hipStream_t st);
@@ -82,6 +84,8 @@ struct FoldIO {
     int nparts;
     float eps;
     const u16* add_vec;    // PREP: bf16 [N] added to x after the product (nullptr: none)
+    const float* add_rows; // PREP: float32 [M, N] added to x after the product, before add_vec
+    float* x_save;         // PREP: float32 [M, N] receives x after the product, before the adds
     const u16* next_gain;  // PREP: bf16 [N] gain of the next RMSNorm
     u16* xg_out;           // PREP: bf16 [M, N]
     float* ps_out;         // PREP: [N / 8][8]
@@ -89,9 +93,11 @@ struct FoldIO {
 bool gemm_fold_supported(int M, int N, int K);
 hipError_t gemm_fold_norm(const u16* xg, const float* ps, int nparts, float eps, const u16* Wp, int M, int N, int K,
                           int epi, float* c, u16* out_bf, hipStream_t st);
-// x[M, N] += A W^T (+ add_vec); with next_gain also writes xg_out and ps_out (N / 8 parts).
+// x[M, N] += A W^T (then + add_rows, then + add_vec); with next_gain also writes xg_out and
+// ps_out (N / 8 parts); x_save (with next_gain) receives x before add_rows and add_vec.
 hipError_t gemm_fold_add(const u16* A, const u16* Wp, int M, int N, int K, float* x, const u16* add_vec,
-                         const u16* next_gain, u16* xg_out, float* ps_out, hipStream_t st);
+                         const u16* next_gain, u16* xg_out, float* ps_out, hipStream_t st,
+                         const float* add_rows = nullptr, float* x_save = nullptr);
 // Row-major W [rows, K] -> lane-packed Wp (rows % 8 == 0, K % 64 == 0).
 hipError_t pack_weights(const u16* W, long long rows, int K, u16* Wp, hipStream_t st);
 // x += add (optional); xg = bf16(x * gain) (lane-packed); ps[0][r] = sum of x^2 of row r.

@@ -67,6 +67,11 @@ typedef struct {
     int32_t vocab, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, ffn_act;
     int32_t n_prelude, n_shared, n_loops, n_coda;
     float rms_eps, rope_theta;
+    /* 1: input re-injection variant (aiboss88.com tutorial, step 3: the input
+     * representation is passed into every loop): the prelude output e is added to
+     * the state before every loop k >= 2, as (state + e) + loop_emb[k-1]; in lazy
+     * mode only the recomputed rows receive it.  0: no re-injection. */
+    int32_t input_reinject;
 } lk_model_cfg;
 
 /* Cache/update policy.  mode LK_MODE_*; rho in (0, 1] (kept-token fraction at
@@ -182,6 +187,14 @@ int lk_decode_weight_bytes(const lk_handle *h, size_t *bytes);
  * when buf_bytes is too small.  The library allocates no device memory for this. */
 int lk_set_decode_weights(lk_handle *h, void *d_buf, size_t buf_bytes, void *stream);
 
+/* Loops the store runs (the tutorial's n_recurrent_loops, picked by the caller with
+ * the same weights; default: the model's n_loops).  Set between allocation and
+ * prefill: the prefill and every decode step of the store then run loops
+ * 1..n_loops, and the byte counts cover those loops; the layout stays the one for
+ * the model's n_loops.  LK_ERR_STATE after prefill, LK_ERR_INVALID_ARG outside
+ * [1, model n_loops]. */
+int lk_kv_store_set_loops(lk_kv_store *s, int32_t n_loops);
+
 /* Layer applications one prefill/decode pass runs per token: P + R*K + Q. */
 int lk_effective_depth(const lk_handle *h, int32_t *depth);
 
@@ -227,7 +240,8 @@ int lk_kv_store_view(const lk_kv_store *s, lk_store_view *v);
 
 /* Override the selections of the next prefill with caller data (device
  * pointers read during lk_looped_prefill; NULL restores natural selection):
- * tokens int32 [n_loops-1][batch][n_selected] ascending per row;
+ * tokens int32 [L-1][batch][n_selected] ascending per row, L the store's loop
+ * count (lk_kv_store_set_loops);
  * columns int32 [R][batch][Hkv][n_columns] ascending per row. */
 int lk_kv_store_force_selection(lk_kv_store *s, const int32_t *d_tokens, const int32_t *d_columns);
 

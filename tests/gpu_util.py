@@ -24,7 +24,7 @@ def max_abs_rel(a, b):
 
 def oracle_selection(m, shape, batch):
     """Oracle's kept tokens [K-1, B, n] and column sets [R, B, Hkv, n_cols] as int32 arrays."""
-    K, R, Hkv = shape.n_loops, shape.n_shared, shape.n_kv_heads
+    K, R, Hkv = m.K, shape.n_shared, shape.n_kv_heads
     tok = np.stack([np.stack([m.sel[(k, b)] for b in range(batch)]) for k in range(2, K + 1)]) \
         if K >= 2 else np.zeros((0, batch, 1), np.int32)
     cols = np.stack([np.stack([np.stack(m.S[r][b]) for b in range(batch)]) for r in range(R)])
@@ -75,7 +75,7 @@ def inject_oracle_codes(store, m, shape, lazy):
     from oracle import quant
     v = store.view()
     B_, Hkv, hd = m.B, shape.n_kv_heads, shape.head_dim
-    R, K, Tp = shape.n_shared, shape.n_loops, v.row_stride
+    R, K, Tp = shape.n_shared, m.K, v.row_stride
     ng = hd // lazy.group
     if lazy.base_bits == 8:
         reg = B_ * Hkv * Tp * hd               # int8 elements of one (layer, K|V) region
@@ -102,21 +102,23 @@ def inject_oracle_codes(store, m, shape, lazy):
     store.keep_codes(True)
 
 
-def run_pair(shape, lazy, batch, prompt, steps, seed=0, force=True, weights=None, force_codes=None):
+def run_pair(shape, lazy, batch, prompt, steps, seed=0, force=True, weights=None, force_codes=None,
+             loops=None):
     """Prefill + `steps` decode steps on the oracle and the GPU; returns a result dict.
 
     force: inject the oracle's token and column selections.  force_codes (default:
-    when the residuals are 4-bit): also inject the oracle's quantized codes."""
+    when the residuals are 4-bit): also inject the oracle's quantized codes.
+    loops: run the shared block this many times (default: the shape's n_loops)."""
     W = weights if weights is not None else I.gen_weights(shape, seed=seed)
     ids = I.gen_prompt_ids(shape, batch, prompt)
     dec = I.gen_decode_ids(shape, batch, steps)
     t0 = time.time()
-    m = LoopedOracle(shape, lazy, W, batch, prompt + steps)
+    m = LoopedOracle(shape, lazy, W, batch, prompt + steps, n_loops=loops)
     o_out = m.prefill(ids)
     o_dec = [m.decode(d) for d in dec]
     t_oracle = time.time() - t0
     model = B.LoopedModel(shape, lazy, W)
-    store = model.store(batch, prompt, prompt + steps)
+    store = model.store(batch, prompt, prompt + steps, loops=loops)
     if lazy.mode == "lazy" and force:
         tok, cols = oracle_selection(m, shape, batch)
         store.force_selection(torch.from_numpy(tok).cuda() if tok.size else None,
@@ -129,7 +131,7 @@ def run_pair(shape, lazy, batch, prompt, steps, seed=0, force=True, weights=None
     g_dec = [model.decode(store, torch.from_numpy(d)).cpu().numpy() for d in dec]
     torch.cuda.synchronize()
     # the same computation with bf16 operands, on the same integer decisions as the GPU run
-    m16 = LoopedOracle(shape, lazy, W, batch, prompt + steps, operand_precision="bf16")
+    m16 = LoopedOracle(shape, lazy, W, batch, prompt + steps, operand_precision="bf16", n_loops=loops)
     if lazy.mode == "lazy" and force:
         m16.forced_tokens = dict(m.sel)
         m16.forced_S = m.S

@@ -19,6 +19,7 @@ import torch
 from cross_loop_kv_amd import binding as B
 from cross_loop_kv_amd import inputs as I
 from oracle import accounting
+from oracle.model import LoopedOracle
 from tests.gpu_util import gpu_selection, log, max_abs_rel, run_pair
 
 pytestmark = pytest.mark.gpu
@@ -274,3 +275,83 @@ def test_decode_window_ring_wraps_during_decode():
     log("ring wrap: prompt 100, 40 decode steps")
     r = run_pair(s, lz, batch=2, prompt=100, steps=40, seed=11)
     check(r, "ring wrap")
+
+
+REINJECT = [
+    ("lazy_gqa_int8_int4", dict(), I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4), 2),
+    ("lazy_mha_hd128_int8res", dict(n_heads=4, n_kv_heads=4, head_dim=128, d_model=512),
+     I.Lazy(mode="lazy", rho=0.25, top_s=40, window=8, base_bits=16, res_bits=8), 2),
+    ("lazy_batch10", dict(), I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4), 10),
+    ("per_loop", dict(), I.Lazy(mode="per_loop"), 2),
+    ("per_loop_no_prelude", dict(n_prelude=0), I.Lazy(mode="per_loop"), 2),
+    ("lazy_no_prelude_batch10", dict(n_prelude=0),
+     I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4), 10),
+]
+
+
+@pytest.mark.parametrize("name,kw,lz,batch", REINJECT, ids=[c[0] for c in REINJECT])
+def test_input_reinjection_matches_oracle(name, kw, lz, batch):
+    """Loops >= 2 take the prelude output added back to their input (the re-injection
+    variant of the looped block).  Covers the folded decode (batch 2: the saved prelude
+    output rides in the down projection's epilogue), the unfolded one (batch 10), no
+    prelude (the embedding is re-injected) and the head-dim-128 prefill kernels."""
+    s = _small(input_reinject=True, **kw)
+    log(f"re-injection {name}")
+    r = run_pair(s, lz, batch=batch, prompt=150, steps=4, seed=21)
+    check(r, f"re-injection {name}")
+
+
+LOOPS = [("lazy", 2), ("lazy", 3), ("lazy", 1), ("per_loop", 2), ("last_loop", 3), ("per_loop", 1)]
+
+
+@pytest.mark.parametrize("mode,loops", LOOPS, ids=[f"{m}_K{k}" for m, k in LOOPS])
+def test_store_loop_count_matches_oracle(mode, loops):
+    """A store set to fewer loops than the model's 4 runs the shared block that many
+    times in prefill and decode (the oracle built with the same count), and its KV
+    byte count is the closed form at that count."""
+    import copy
+    s = _small(n_loops=4)
+    lz = (I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4)
+          if mode == "lazy" else I.Lazy(mode=mode))
+    log(f"store loops {loops} of 4, {mode}")
+    T, steps, Bsz = 140, 3, 2
+    r = run_pair(s, lz, batch=Bsz, prompt=T, steps=steps, seed=17, loops=loops)
+    check(r, f"K={loops} {mode}")
+    sk = copy.copy(s)
+    sk.n_loops = loops
+    exp = accounting.kv_bytes(sk, lz, Bsz, T, T + steps)
+    assert r["store"].bytes_used() == (exp["shared"], exp["total"])
+
+
+def test_stores_with_different_loop_counts_share_a_model():
+    """Two stores of one model, at 4 and 2 loops, decoded in turn on a side stream
+    (each step replays or recaptures the graph of its own store) against the oracle
+    at each count.  The count is fixed once a store has been prefilled."""
+    s = _small(n_loops=4, input_reinject=True)
+    lz = I.Lazy(mode="per_loop")
+    T, steps, Bsz = 120, 4, 2
+    W = I.gen_weights(s, seed=23)
+    ids = I.gen_prompt_ids(s, Bsz, T)
+    dec = I.gen_decode_ids(s, Bsz, steps)
+    model = B.LoopedModel(s, lz, W)
+    stores = {4: model.store(Bsz, T, T + steps), 2: model.store(Bsz, T, T + steps, loops=2)}
+    oracles = {k: LoopedOracle(s, lz, W, Bsz, T + steps, n_loops=k) for k in stores}
+    for k, st in stores.items():
+        g = model.prefill(st, torch.from_numpy(ids)).cpu().numpy()
+        o = oracles[k].prefill(ids)
+        log(f"  K={k} prefill {max_abs_rel(g, o):.3e}")
+        assert max_abs_rel(g, o) < TOL
+    with pytest.raises(B.LKError):
+        stores[2].set_loops(3)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    dd = torch.from_numpy(dec).cuda()
+    for i in range(steps):
+        for k, st in stores.items():
+            with torch.cuda.stream(side):
+                g = model.decode(st, dd[i])
+            side.synchronize()
+            o = oracles[k].decode(dec[i])
+            e = max_abs_rel(g.cpu().numpy(), o)
+            log(f"  step {i} K={k} decode {e:.3e}")
+            assert e < TOL
