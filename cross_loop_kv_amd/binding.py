@@ -60,6 +60,19 @@ class lk_store_view(C.Structure):
                 ("row_stride", C.c_int32)]
 
 
+SNAPSHOT_MAGIC = 0x313050414E534B4C   # bytes "LKSNAP01"
+SNAPSHOT_VERSION = 1
+
+
+class lk_store_snapshot(C.Structure):
+    """Header of a store snapshot; the body (the start of the store buffer) follows."""
+    _fields_ = [("magic", C.c_uint64), ("header_bytes", C.c_uint32), ("version", C.c_uint32),
+                ("cfg", lk_model_cfg), ("lazy", lk_lazy_cfg),
+                ("batch", C.c_int32), ("prompt_tokens", C.c_int32), ("max_tokens", C.c_int32),
+                ("loops", C.c_int32), ("tokens", C.c_int32), ("prefilled", C.c_int32),
+                ("body_bytes", C.c_uint64)]
+
+
 _SIGS = {
     "lk_create": (C.c_int, [C.POINTER(lk_model_cfg), C.POINTER(lk_lazy_cfg), C.POINTER(lk_weights),
                             C.POINTER(C.c_void_p)]),
@@ -72,6 +85,8 @@ _SIGS = {
     "lk_kv_store_cache_bytes": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t)]),
     "lk_kv_store_length": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32)]),
     "lk_kv_store_set_loops": (C.c_int, [C.c_void_p, C.c_int32]),
+    "lk_kv_store_export": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.POINTER(C.c_size_t), C.c_void_p]),
+    "lk_kv_store_import": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "lk_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.POINTER(C.c_size_t)]),
     "lk_looped_prefill": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                     C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
@@ -176,6 +191,20 @@ def lk_kv_store_length(s: int) -> int:
 
 def lk_kv_store_set_loops(s: int, n: int) -> None:
     _check(lib().lk_kv_store_set_loops(s, n))
+
+
+def lk_kv_store_export(s: int, stream=None) -> np.ndarray:
+    """The store's snapshot as a host uint8 array (header, then body)."""
+    need = C.c_size_t()
+    _check(lib().lk_kv_store_export(s, None, 0, C.byref(need), None))
+    buf = np.empty(need.value, np.uint8)
+    _check(lib().lk_kv_store_export(s, buf.ctypes.data, buf.size, C.byref(need), _stream(stream)))
+    return buf
+
+
+def lk_kv_store_import(s: int, snap: np.ndarray, stream=None) -> None:
+    snap = np.ascontiguousarray(snap, dtype=np.uint8)
+    _check(lib().lk_kv_store_import(s, snap.ctypes.data, snap.size, _stream(stream)))
 
 
 def lk_workspace_bytes(h: int, batch: int, tokens: int) -> int:
@@ -298,6 +327,15 @@ class Store:
 
     def length(self) -> int:
         return lk_kv_store_length(self.s)
+
+    def export(self) -> np.ndarray:
+        """Snapshot of the store's state (host uint8 array)."""
+        return lk_kv_store_export(self.s)
+
+    def import_(self, snap: np.ndarray):
+        """Replace the store's state with a snapshot (see lk_kv_store_import)."""
+        lk_kv_store_import(self.s, snap)
+        self.loops = lk_store_snapshot.from_buffer_copy(bytes(snap[:C.sizeof(lk_store_snapshot)])).loops
 
     def set_loops(self, n: int):
         """Loop count for the next prefill and its decode steps (1..the model's K)."""

@@ -676,6 +676,42 @@ lk::KVWrite plain_write(const KVLayer& L) {
     return k;
 }
 
+// Fill the float16 decode caches of loops 2..K from the base and residuals: the
+// stable-column reconstructions (when with_s) and the window rings ending at
+// position `last` (the rows of positions up to `last` that decode can read).
+int fill_decode_caches(lk_kv_store* s, bool with_s, int last, hipStream_t st) {
+    for (int k = 2; k <= s->K; ++k)
+        for (int r = 0; r < s->h->c.n_shared; ++r) {
+            lk::RowsAttn g{};
+            g.B = s->B;
+            g.kv = lazy_layer(s, r);
+            g.k_loop = k;
+            g.cols = col_sets(s, r);
+            g.n_cols = s->lay.n_cols;
+            g.pos = last;
+            if (with_s) {
+                const KVLayer L = scache_layer(s, k, r);
+                LK_HIP(lk::gather_recon(g, lk::GATHER_ALL_S, s->lay.ncs, (u16*)L.base[0], (u16*)L.base[1], st));
+            }
+            const KVLayer Rg = scache_layer(s, k, r, true);
+            LK_HIP(lk::gather_recon(g, lk::GATHER_RING, s->lay.wr, (u16*)Rg.base[0], (u16*)Rg.base[1], st));
+        }
+    return LK_OK;
+}
+
+bool same_cfg(const lk_model_cfg& a, const lk_model_cfg& b) {
+    return a.vocab == b.vocab && a.d_model == b.d_model && a.n_heads == b.n_heads && a.n_kv_heads == b.n_kv_heads &&
+           a.head_dim == b.head_dim && a.ffn_dim == b.ffn_dim && a.ffn_act == b.ffn_act &&
+           a.n_prelude == b.n_prelude && a.n_shared == b.n_shared && a.n_loops == b.n_loops &&
+           a.n_coda == b.n_coda && a.rms_eps == b.rms_eps && a.rope_theta == b.rope_theta &&
+           a.input_reinject == b.input_reinject;
+}
+
+bool same_lazy(const lk_lazy_cfg& a, const lk_lazy_cfg& b) {
+    return a.mode == b.mode && a.rho == b.rho && a.top_s == b.top_s && a.window == b.window &&
+           a.base_bits == b.base_bits && a.res_bits == b.res_bits && a.group == b.group;
+}
+
 }  // namespace
 
 // =============================================================================
@@ -818,6 +854,69 @@ int lk_kv_store_force_selection(lk_kv_store* s, const int32_t* d_tokens, const i
     return LK_OK;
 }
 
+int lk_kv_store_export(const lk_kv_store* s, void* host_buf, size_t buf_bytes, size_t* need_bytes, void* stream) {
+    if (!s || !need_bytes) return fail(LK_ERR_INVALID_ARG, "null argument");
+    const size_t body = s->lay.scache;  // everything before the derived decode caches
+    *need_bytes = sizeof(lk_store_snapshot) + body;
+    if (!host_buf) return LK_OK;
+    if (buf_bytes < *need_bytes) return fail(LK_ERR_CAPACITY, "snapshot buffer too small");
+    lk_store_snapshot hd;
+    std::memset(&hd, 0, sizeof(hd));
+    hd.magic = LK_SNAPSHOT_MAGIC;
+    hd.header_bytes = sizeof(lk_store_snapshot);
+    hd.version = LK_SNAPSHOT_VERSION;
+    hd.cfg = s->h->c;
+    hd.lazy = s->h->z;
+    hd.batch = s->B;
+    hd.prompt_tokens = s->Tp;
+    hd.max_tokens = s->Tmax;
+    hd.loops = s->K;
+    hd.tokens = s->t;
+    hd.prefilled = s->prefilled ? 1 : 0;
+    hd.body_bytes = body;
+    std::memcpy(host_buf, &hd, sizeof(hd));
+    hipStream_t st = (hipStream_t)stream;
+    LK_HIP(hipMemcpyAsync((char*)host_buf + sizeof(hd), s->buf, body, hipMemcpyDeviceToHost, st));
+    LK_HIP(hipStreamSynchronize(st));
+    return LK_OK;
+}
+
+int lk_kv_store_import(lk_kv_store* s, const void* host_buf, size_t bytes, void* stream) {
+    if (!s || !host_buf) return fail(LK_ERR_INVALID_ARG, "null argument");
+    if (bytes < sizeof(lk_store_snapshot)) return fail(LK_ERR_INVALID_ARG, "snapshot shorter than its header");
+    lk_store_snapshot hd;
+    std::memcpy(&hd, host_buf, sizeof(hd));
+    const lk_handle* h = s->h;
+    if (hd.magic != LK_SNAPSHOT_MAGIC || hd.header_bytes != sizeof(lk_store_snapshot) ||
+        hd.version != LK_SNAPSHOT_VERSION)
+        return fail(LK_ERR_INVALID_ARG, "not a store snapshot of this version");
+    if (!same_cfg(hd.cfg, h->c) || !same_lazy(hd.lazy, h->z))
+        return fail(LK_ERR_INVALID_ARG, "snapshot written under another model config or cache policy");
+    if (hd.batch != s->B || hd.prompt_tokens != s->Tp || hd.max_tokens != s->Tmax)
+        return fail(LK_ERR_INVALID_ARG, "snapshot of a store with another batch, prompt or capacity");
+    if (hd.loops < 1 || hd.loops > h->c.n_loops) return fail(LK_ERR_INVALID_ARG, "snapshot loop count out of range");
+    if (hd.prefilled ? (hd.tokens < s->Tp || hd.tokens > s->Tmax) : hd.tokens != 0)
+        return fail(LK_ERR_INVALID_ARG, "snapshot length inconsistent with its prefill flag");
+    if (hd.body_bytes != s->lay.scache) return fail(LK_ERR_INVALID_ARG, "snapshot body size differs from the store's");
+    if (bytes - sizeof(hd) < hd.body_bytes) return fail(LK_ERR_INVALID_ARG, "snapshot truncated");
+    if (h->graph.store == s) {  // its captured decode step may be in flight
+        LK_HIP(hipDeviceSynchronize());
+        s->h->graph.reset();
+    }
+    hipStream_t st = (hipStream_t)stream;
+    LK_HIP(hipMemcpyAsync(s->buf, (const char*)host_buf + sizeof(hd), hd.body_bytes, hipMemcpyHostToDevice, st));
+    s->t = hd.tokens;
+    s->K = hd.loops;
+    s->prefilled = hd.prefilled != 0;
+    LK_HIP(lk::fill_i32(dev_pos(s), hd.tokens, 1, st));
+    if (s->lay.scache_bytes) {
+        LK_HIP(lk::fill_i32((int32_t*)(s->buf + s->lay.scache), 0, (long long)(s->lay.scache_bytes / 4), st));
+        if (s->prefilled && s->K >= 2) LK_TRY(fill_decode_caches(s, true, s->t - 1, st));
+    }
+    LK_HIP(hipStreamSynchronize(st));
+    return LK_OK;
+}
+
 int lk_kv_store_keep_codes(lk_kv_store* s, int32_t enable) {
     if (!s) return fail(LK_ERR_INVALID_ARG, "null store");
     if (!s->h->lazy()) return fail(LK_ERR_STATE, "codes exist only in lazy mode");
@@ -945,21 +1044,7 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
         // The stable columns' and the prompt tail's loop-k reconstructions are final
         // now: cache them (float16) for decode (the stable columns already are when the
         // loop used them through the cache).
-        for (int k = 2; k <= K; ++k)
-            for (int r = 0; r < R; ++r) {
-                lk::RowsAttn g{};
-                g.B = B;
-                g.kv = lazy_layer(s, r);
-                g.k_loop = k;
-                g.cols = col_sets(s, r);
-                g.n_cols = s->lay.n_cols;
-                g.pos = T - 1;
-                const KVLayer L = scache_layer(s, k, r);
-                if (!w.fr_cap)
-                    LK_HIP(lk::gather_recon(g, lk::GATHER_ALL_S, s->lay.ncs, (u16*)L.base[0], (u16*)L.base[1], st));
-                const KVLayer Rg = scache_layer(s, k, r, true);
-                LK_HIP(lk::gather_recon(g, lk::GATHER_RING, s->lay.wr, (u16*)Rg.base[0], (u16*)Rg.base[1], st));
-            }
+        LK_TRY(fill_decode_caches(s, !w.fr_cap, T - 1, st));
     }
     for (int j = 0; j < Q; ++j) {
         dense_plan.read = dense_layer(s, P + j);

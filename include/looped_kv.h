@@ -31,7 +31,8 @@
  * Memory: the caller owns all device memory (weights, ids, outputs, the KV-store
  * buffer and the workspace); the library never allocates device memory.  All
  * work is enqueued on the caller's HIP stream (passed as void*; NULL means the
- * default stream) with no host synchronisation.  Every call returns LK_OK (0) or
+ * default stream) with no host synchronisation (except the snapshot copies,
+ * which wait for their stream).  Every call returns LK_OK (0) or
  * a negative LK_ERR_* code and leaves a message for lk_last_error() (thread
  * local); errors detected on the host are reported before anything is launched.
  * Calls that share a store or workspace must be ordered on one stream.
@@ -194,6 +195,50 @@ int lk_set_decode_weights(lk_handle *h, void *d_buf, size_t buf_bytes, void *str
  * the model's n_loops.  LK_ERR_STATE after prefill, LK_ERR_INVALID_ARG outside
  * [1, model n_loops]. */
 int lk_kv_store_set_loops(lk_kv_store *s, int32_t n_loops);
+
+/* Decode-state snapshots: checkpoint and resume of a decode session, and a way to
+ * start decode from a store filled on the host.  The pages define no snapshot;
+ * this one holds exactly the method's stored state: a header, then `body_bytes`
+ * bytes that are the start of the store buffer, laid out as lk_kv_store_alloc
+ * describes (offsets from the buffer start as lk_kv_store_view reports them):
+ * the dense prelude/coda rows, the per-loop / last-loop rows or the lazy base,
+ * residuals, slot maps and column sets, and the device copy of the length.  The
+ * lazy decode caches (lk_kv_store_cache_bytes) are derived data and are not in
+ * it: import rebuilds them from the base and residuals, with the same values the
+ * prefill and decode steps wrote. */
+#define LK_SNAPSHOT_MAGIC 0x313050414e534b4cull /* bytes "LKSNAP01" */
+#define LK_SNAPSHOT_VERSION 1
+typedef struct {
+    uint64_t magic;          /* LK_SNAPSHOT_MAGIC */
+    uint32_t header_bytes;   /* sizeof(lk_store_snapshot); the body follows */
+    uint32_t version;        /* LK_SNAPSHOT_VERSION */
+    lk_model_cfg cfg;        /* model config of the handle that wrote it */
+    lk_lazy_cfg lazy;        /* cache policy of that handle */
+    int32_t batch, prompt_tokens, max_tokens;  /* the store's allocation */
+    int32_t loops;           /* the store's loop count (lk_kv_store_set_loops) */
+    int32_t tokens;          /* tokens held per sequence */
+    int32_t prefilled;       /* 1 after prefill (then prompt_tokens <= tokens) */
+    uint64_t body_bytes;     /* bytes of the store buffer that follow */
+} lk_store_snapshot;
+
+/* Copy the store's state into host memory: header, then body.  host_buf == NULL
+ * is a size query (*need_bytes only).  Enqueues the copy on `stream` and waits
+ * for that stream; work on other streams that writes the store must be finished
+ * by the caller.  LK_ERR_CAPACITY if buf_bytes < *need_bytes. */
+int lk_kv_store_export(const lk_kv_store *s, void *host_buf, size_t buf_bytes, size_t *need_bytes,
+                       void *stream);
+
+/* Replace the store's state with a snapshot (host memory, `bytes` long).  The
+ * model config, cache policy, batch, prompt_tokens and max_tokens must equal the
+ * store's (any handle with the same config may have written it), loops must be
+ * in [1, model n_loops], tokens in [prompt_tokens, max_tokens] when prefilled and
+ * 0 otherwise, body_bytes the store's state size.  Uploads the body on `stream`,
+ * rebuilds the lazy decode caches there (positions up to tokens - 1), sets the
+ * length and loop count, drops a captured decode step of this store, and waits
+ * for the stream, so host_buf may be freed on return.  Errors other than
+ * LK_ERR_HIP leave the store unchanged.  The store's selection overrides and
+ * keep-codes setting are not part of the state and are kept. */
+int lk_kv_store_import(lk_kv_store *s, const void *host_buf, size_t bytes, void *stream);
 
 /* Layer applications one prefill/decode pass runs per token: P + R*K + Q. */
 int lk_effective_depth(const lk_handle *h, int32_t *depth);

@@ -444,6 +444,41 @@ class LoopedOracle:
         S, w = self.S[r][b], self.lz.window
         return attend(q, kr, vr, lambda i, g: sparse_cols(int(rows[i]), S[g], w))
 
+    def start_from_state(self, T: int, base, res, slot, S, dense_kv=None):
+        """Take a lazy store state as a prefill of T tokens would leave it, built
+        elsewhere, and continue with decode from there.
+
+        base[r][kv]: (int8 codes [B, Hkv, Tmax, hd], float16 scales [B, Hkv, Tmax,
+        hd/group]) for 8-bit bases, else float32 rows [B, Hkv, Tmax, hd];
+        res[(k, r, kv)] for k = 2..shape.n_loops: the same forms over
+        n_selected(rho, T) + Tmax - T slots (int8 codes hold the int4 values too);
+        slot [shape.n_loops, B, Tmax] int32, row k-1 the slot of each position at
+        loop k (-1: not stored); S[r][b][g] ascending int32 column arrays;
+        dense_kv[i] = (K rows, V rows) float32 [B, Hkv, Tmax, hd] of prelude/coda
+        layer i when there are any.  The arrays are used as given, not copied."""
+        s, lz = self.s, self.lz
+        if lz.mode != "lazy":
+            raise ValueError("a store state exists in lazy mode only")
+        if not 1 <= T <= self.Tmax:
+            raise ValueError("bad prompt length")
+        n_dense = s.n_prelude + s.n_coda
+        if n_dense and (dense_kv is None or len(dense_kv) != n_dense):
+            raise ValueError("prelude/coda rows are needed")
+        n = n_selected(lz.rho, T)
+        if slot.shape != (s.n_loops, self.B, self.Tmax):
+            raise ValueError("slot map shape")
+        for (k, r, kv), x in res.items():
+            a = x if lz.res_bits == 16 else x[0]
+            if a.shape[2] != n + self.Tmax - T:
+                raise ValueError("residual slot count")
+        self.T, self.t, self.n_sel = T, T, n
+        self.n_slots = n + self.Tmax - T
+        self.base, self.res, self.slot, self.S = base, res, slot, S
+        for i in range(n_dense):
+            self.dense_k[i], self.dense_v[i] = dense_kv[i]
+        self.sel = {(k, b): np.nonzero(slot[k - 1, b, :T] >= 0)[0].astype(np.int32)
+                    for k in range(2, self.K + 1) for b in range(self.B)}
+
     # --------------------------------------------------------------- decode
     def decode(self, ids: np.ndarray) -> np.ndarray:
         ids = np.asarray(ids).reshape(-1)

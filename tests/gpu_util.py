@@ -102,6 +102,19 @@ def inject_oracle_codes(store, m, shape, lazy):
     store.keep_codes(True)
 
 
+_WEIGHTS = {}
+
+
+def cached_weights(shape, seed):
+    """I.gen_weights(shape, seed), kept for the next call with the same arguments (the
+    full-width shapes take tens of seconds to draw); one entry is kept."""
+    key = (repr(shape), seed)
+    if key not in _WEIGHTS:
+        _WEIGHTS.clear()
+        _WEIGHTS[key] = I.gen_weights(shape, seed=seed)
+    return _WEIGHTS[key]
+
+
 def run_pair(shape, lazy, batch, prompt, steps, seed=0, force=True, weights=None, force_codes=None,
              loops=None):
     """Prefill + `steps` decode steps on the oracle and the GPU; returns a result dict.
@@ -109,7 +122,7 @@ def run_pair(shape, lazy, batch, prompt, steps, seed=0, force=True, weights=None
     force: inject the oracle's token and column selections.  force_codes (default:
     when the residuals are 4-bit): also inject the oracle's quantized codes.
     loops: run the shared block this many times (default: the shape's n_loops)."""
-    W = weights if weights is not None else I.gen_weights(shape, seed=seed)
+    W = weights if weights is not None else cached_weights(shape, seed)
     ids = I.gen_prompt_ids(shape, batch, prompt)
     dec = I.gen_decode_ids(shape, batch, steps)
     t0 = time.time()

@@ -39,9 +39,13 @@ def test_struct_layouts_match_the_header():
 #include "looped_kv.h"
 #define P(T, f) printf("%s.%s %zu\n", #T, #f, offsetof(T, f));
 int main(void) {
-  printf("lk_model_cfg %zu\nlk_lazy_cfg %zu\nlk_layer_weights %zu\nlk_weights %zu\nlk_store_view %zu\n",
+  printf("lk_model_cfg %zu\nlk_lazy_cfg %zu\nlk_layer_weights %zu\nlk_weights %zu\nlk_store_view %zu\n"
+         "lk_store_snapshot %zu\n",
          sizeof(lk_model_cfg), sizeof(lk_lazy_cfg), sizeof(lk_layer_weights), sizeof(lk_weights),
-         sizeof(lk_store_view));
+         sizeof(lk_store_view), sizeof(lk_store_snapshot));
+  P(lk_store_snapshot, cfg) P(lk_store_snapshot, lazy) P(lk_store_snapshot, batch)
+  P(lk_store_snapshot, prefilled) P(lk_store_snapshot, body_bytes)
+  printf("magic %llu\n", (unsigned long long)LK_SNAPSHOT_MAGIC);
   P(lk_model_cfg, ffn_act) P(lk_model_cfg, rms_eps) P(lk_model_cfg, rope_theta)
   P(lk_lazy_cfg, rho) P(lk_lazy_cfg, top_s) P(lk_lazy_cfg, group)
   P(lk_weights, layers) P(lk_layer_weights, w_down)
@@ -56,7 +60,10 @@ int main(void) {
         subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
         out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
     got = dict(line.rsplit(" ", 1) for line in out.strip().splitlines())
-    for name in ("lk_model_cfg", "lk_lazy_cfg", "lk_layer_weights", "lk_weights", "lk_store_view"):
+    assert int(got.pop("magic")) == B.SNAPSHOT_MAGIC
+    assert B.SNAPSHOT_MAGIC.to_bytes(8, "little") == b"LKSNAP01"
+    for name in ("lk_model_cfg", "lk_lazy_cfg", "lk_layer_weights", "lk_weights", "lk_store_view",
+                 "lk_store_snapshot"):
         assert int(got[name]) == ctypes.sizeof(getattr(B, name)), name
     for key, val in got.items():
         if "." in key:
@@ -154,3 +161,61 @@ def test_null_arguments_are_errors():
     assert lib.lk_looped_decode_step(None, None, None, None, None, 0, None) == -1
     assert lib.lk_dbg_topk(None, 1, 1, 1, None, None) == -1
     assert b"null" in lib.lk_last_error()
+
+
+def test_snapshot_size_query_and_import_validation():
+    """Snapshot header checks, all made on the host before any copy (a per_loop store
+    is allocated without a launch, so a dummy device address serves)."""
+    wl = I.workload("tiny_1p2x2c1_t32")
+    lz = I.Lazy(mode="per_loop")
+    h = _handle(wl.shape, lz)
+    other = _handle(I.Shape(**{**wl.shape.__dict__, "input_reinject": True}), lz)
+    try:
+        _, need = B.lk_kv_store_alloc(h, 1, 8, 12)
+        s, _ = B.lk_kv_store_alloc(h, 1, 8, 12, dev_buf=256, buf_bytes=need)
+        hdr_bytes = ctypes.sizeof(B.lk_store_snapshot)
+        n = ctypes.c_size_t()
+        assert B.lib().lk_kv_store_export(s, None, 0, ctypes.byref(n), None) == 0
+        body = n.value - hdr_bytes
+        assert 0 < body <= need
+
+        def header(**kw):
+            hd = B.lk_store_snapshot(B.SNAPSHOT_MAGIC, hdr_bytes, B.SNAPSHOT_VERSION, B.model_cfg(wl.shape),
+                                     B.lazy_cfg(lz), 1, 8, 12, wl.shape.n_loops, 10, 1, body)
+            for k, v in kw.items():
+                setattr(hd, k, v)
+            return bytearray(bytes(hd)) + bytearray(body)
+
+        import numpy as np
+        cases = [
+            ("short", header()[:hdr_bytes - 1]),
+            ("magic", header(magic=B.SNAPSHOT_MAGIC + 1)),
+            ("version", header(version=2)),
+            ("config", header(cfg=B.model_cfg(I.Shape(**{**wl.shape.__dict__, "input_reinject": True})))),
+            ("policy", header(lazy=B.lazy_cfg(I.Lazy(mode="last_loop")))),
+            ("batch", header(batch=2)),
+            ("capacity", header(max_tokens=13)),
+            ("loops", header(loops=0)),
+            ("loops", header(loops=wl.shape.n_loops + 1)),
+            ("length", header(tokens=7)),
+            ("length", header(tokens=13)),
+            ("length", header(prefilled=0)),
+            ("body", header(body_bytes=body + 256)),
+            ("truncated", header()[:-1]),
+        ]
+        for what, buf in cases:
+            a = np.frombuffer(bytes(buf), np.uint8)
+            with pytest.raises(B.LKError) as e:
+                B.lk_kv_store_import(s, a)
+            assert e.value.code == -1, what
+        assert B.lk_kv_store_length(s) == 0
+        small = np.zeros(8, np.uint8)   # the snapshot buffer must hold header and body
+        assert B.lib().lk_kv_store_export(s, small.ctypes.data, small.size, ctypes.byref(n), None) == -3
+        for bad in (0, wl.shape.n_loops + 1):
+            with pytest.raises(B.LKError):
+                B.lk_kv_store_set_loops(s, bad)
+        B.lk_kv_store_set_loops(s, 1)
+        B.lk_kv_store_release(s)
+    finally:
+        B.lk_destroy(other)
+        B.lk_destroy(h)

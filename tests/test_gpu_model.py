@@ -188,93 +188,122 @@ def test_full_width_shapes_short_prompt(name, batch, prompt, steps):
     check(r, name)
 
 
-@pytest.mark.parametrize("mode,timed,Bsz", [("lazy", True, 2), ("lazy", False, 2), ("per_loop", True, 2),
-                                           ("lazy", False, 10)])
-def test_decode_graph_replay_matches_eager_launches(mode, timed, Bsz):
-    """Decode steps replayed from a captured HIP graph (non-null stream) equal the
-    same steps launched kernel by kernel (null stream) bit for bit, replay after
-    replay, with unrelated eager work and host synchronisation in between; the
-    timer sees every replayed launch of its class."""
-    s = _small()
-    lz = (I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4)
-          if mode == "lazy" else I.Lazy(mode="per_loop"))
-    T, steps = 150, 6
-    W = I.gen_weights(s, seed=9)
-    ids = torch.from_numpy(I.gen_prompt_ids(s, Bsz, T))
-    dec = torch.from_numpy(I.gen_decode_ids(s, Bsz, steps)).cuda()
-    model = B.LoopedModel(s, lz, W)
-    sa, sb = model.store(Bsz, T, T + steps), model.store(Bsz, T, T + steps)
-    pa, pb = model.prefill(sa, ids), model.prefill(sb, ids)
-    assert torch.equal(pa, pb)
-    side = torch.cuda.Stream()
-    B.lk_timing_enable(model.h, "attn_decode_dense" if timed else None)
-    junk = torch.randn(512, 512, device="cuda")
-    for i in range(steps):
-        with torch.cuda.stream(side):
-            og = model.decode(sa, dec[i])
-        side.synchronize()
-        junk = (junk @ junk).clamp_(-1, 1)
-        oe = model.decode(sb, dec[i])
-        torch.cuda.synchronize()
-        assert torch.equal(og, oe), f"step {i}"
-    n, ms = B.lk_timing_read(model.h)
-    B.lk_timing_enable(model.h, None)
-    P, R, K, Q = s.n_prelude, s.n_shared, s.n_loops, s.n_coda
-    per_step = P + Q + (R if mode == "lazy" else R * K)
-    if timed:
-        assert n == 2 * steps * per_step and ms > 0   # replayed steps + eager steps
-    else:
-        assert n == 0
-    assert sa.length() == sb.length() == T + steps
+def _bound_check(what, err, oracle_bf16_run):
+    """err against 2e-2, or against twice the oracle's own bf16-operand sensitivity
+    when 2e-2 is exceeded (as in check(); the bf16-operand run is made only then)."""
+    log(f"  {what}: GPU vs fp32 oracle {err:.3e}")
+    if err < TOL:
+        return
+    err16, drift = oracle_bf16_run()
+    log(f"  {what}: vs bf16-operand oracle {err16:.3e}; oracle bf16 sensitivity {drift:.3e}")
+    assert err < 2 * drift and err16 < 2 * drift
 
 
-def test_decode_packed_weights_match_row_major_weights():
-    """Decode with the packed decode copy of the weights (caller-owned buffer) against
-    decode with the buffer detached (row-major weights, other GEMM kernels): the same
-    products up to summation order.  Detaching and re-attaching the buffer drops the
-    captured step; the size query and the capacity check hold."""
-    s = _small()
-    # 16-bit KV: no quantizer decision can flip between the two summation orders
-    lz = I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=16, res_bits=16)
-    T, steps, Bsz = 150, 4, 3
-    W = I.gen_weights(s, seed=5)
-    ids = torch.from_numpy(I.gen_prompt_ids(s, Bsz, T))
-    dec = torch.from_numpy(I.gen_decode_ids(s, Bsz, steps)).cuda()
-    model = B.LoopedModel(s, lz, W)
-    nbytes = B.lk_decode_weight_bytes(model.h)
-    assert nbytes == 2 * sum(L["wqkv"].numel() + L["wo"].numel() + L["w_in"].numel() + L["w_down"].numel()
-                             for L in model.layers)
-    with pytest.raises(B.LKError):
-        B.lk_set_decode_weights(model.h, model._pk[1].data_ptr(), nbytes - 2)
-    model.pack_decode_weights(True)
-    side = torch.cuda.Stream()
-    sa, sb = model.store(Bsz, T, T + steps), model.store(Bsz, T, T + steps)
-    model.prefill(sa, ids)
-    model.prefill(sb, ids)
-    # the prefills ran on the null stream; torch's side stream does not wait for it, and
-    # the model's calls share one workspace
+def _full_context_case(s, lz, Bn, T, samples, W, k_std):
+    """Synthetic prefill states for the sampled sequences, the oracle's decode of each
+    (it writes its codes of the new token into the state), and a snapshot holding them."""
+    import time
+    from tests.synth_state import synthetic_lazy_state
+    ids = I.gen_decode_ids(s, Bn, 1)[0]
+    states, oracles, outs = {}, {}, {}
+    for seq, seed in samples.items():
+        st = synthetic_lazy_state(s, lz, T, T + 1, seed=seed, k_std=k_std)
+        t0 = time.time()
+        m = LoopedOracle(s, lz, W, 1, T + 1)
+        m.start_from_state(T, st["base"], st["res"], st["slot"], st["S"])
+        outs[seq] = m.decode(ids[seq:seq + 1])[0]
+        log(f"  oracle decode of sequence {seq}: {time.time() - t0:.1f}s")
+        states[seq], oracles[seq] = st, m
+    return ids, states, oracles, outs
+
+
+def _bf16_rerun(s, lz, W, T, st, m, tok, out, gpu_out):
+    """The bf16-operand oracle on the same state and codes: (GPU vs it, it vs fp32)."""
+    def run():
+        m16 = LoopedOracle(s, lz, W, 1, T + 1, operand_precision="bf16")
+        m16.start_from_state(T, st["base"], st["res"], st["slot"], st["S"])
+        m16.forced_codes_from = m
+        o16 = m16.decode(np.array([tok]))[0]
+        return max_abs_rel(gpu_out, o16), max_abs_rel(o16, out)
+    return run
+
+
+def _gpu_decode(model, store, ids):
     torch.cuda.synchronize()
-    outs = []
-    for st in (sa, sb):
-        o = []
-        for i in range(steps):
-            with torch.cuda.stream(side):
-                o.append(model.decode(st, dec[i]).clone())
-        side.synchronize()
-        outs.append(torch.stack(o))
-        model.pack_decode_weights(False)
-    log(f"packed vs row-major decode: max-abs-rel {max_abs_rel(outs[0].cpu().numpy(), outs[1].cpu().numpy()):.2e}")
-    assert max_abs_rel(outs[0].cpu().numpy(), outs[1].cpu().numpy()) < 1e-3
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        g = model.decode(store, torch.from_numpy(ids).cuda())
+    side.synchronize()
+    return g.cpu().numpy()
 
 
-def test_decode_window_ring_wraps_during_decode():
-    """Decode positions cross the end of the float16 window ring (window 16 -> 128 rows):
-    prompt 100, 40 steps, positions 100..139."""
-    s = _small()
-    lz = I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4)
-    log("ring wrap: prompt 100, 40 decode steps")
-    r = run_pair(s, lz, batch=2, prompt=100, steps=40, seed=11)
-    check(r, "ring wrap")
+@pytest.mark.timeout(900)
+def test_full_context_decode_sampled_sequences():
+    """Every launch of the decode step the throughput figure times, at its full size
+    (batch 8, a 32768-token context, d 2048, 16 query / 4 KV heads of 128, FFN 5632,
+    4 loops, int8 base, int4 residuals, rho 0.1, top-s 1024, window 512; packed
+    weights, replayed from a captured graph), with 2 shared layers in place of 48:
+    depth only repeats the same launches, while a deep random stack amplifies bf16
+    rounding (the 48-layer case is the next test).  A CPU prefill of that context
+    is out of reach, so the store starts from synthetic prefill states imported
+    through a snapshot (the import rebuilds the decode caches).  Sequences 0 and 7
+    (the samples) are decoded by the oracle holding the same states; the GPU keeps
+    the oracle's codes for the new token.  Then sequences 1-6 are given other states
+    and the samples' outputs must not change by a bit."""
+    import copy
+    from tests.synth_state import snapshot_with_states
+    wl = I.workload("deep_48x4_b8_ctx32k")
+    s = copy.copy(wl.shape)
+    s.n_shared = 2
+    lz, Bn, T = wl.lazy, wl.batch, wl.prompt
+    log(f"full context decode: B={Bn} T={T} R={s.n_shared} K={s.n_loops}")
+    W = I.gen_weights(s, seed=3)
+    ids, states, oracles, outs = _full_context_case(s, lz, Bn, T, {0: 31, 7: 37}, W, k_std=2.0)
+    model = B.LoopedModel(s, lz, W)
+    store = model.store(Bn, T, T + 1)
+    store.keep_codes(True)
+    store.import_(snapshot_with_states(store, s, lz, states))
+    assert store.length() == T
+    g = _gpu_decode(model, store, ids)
+    assert np.isfinite(g).all()
+    for seq in states:
+        run = _bf16_rerun(s, lz, W, T, states[seq], oracles[seq], ids[seq], outs[seq], g[seq])
+        _bound_check(f"sequence {seq}", max_abs_rel(g[seq], outs[seq]), run)
+    # the other sequences take copies of sequence 0's state: samples unchanged
+    more = dict(states)
+    for b in range(1, Bn - 1):
+        more[b] = states[0]
+    store.import_(snapshot_with_states(store, s, lz, more))
+    g2 = _gpu_decode(model, store, ids)
+    for seq in states:
+        assert np.array_equal(g2[seq], g[seq]), f"sequence {seq} depends on the others"
+
+
+@pytest.mark.timeout(900)
+def test_full_depth_decode_at_full_context():
+    """The decode step the throughput figure times, whole: 48 shared layers x 4 loops
+    at batch 8 and a 32768-token context, from a synthetic prefill state (K/V spread
+    about 1) imported through a snapshot; the last sequence (the sample) against the
+    oracle holding the same state.  192 layer applications of random weights over a
+    random context amplify rounding: the oracle's own bf16-operand sensitivity is
+    measured and the bound is as in check()."""
+    from tests.gpu_util import cached_weights
+    from tests.synth_state import snapshot_with_states
+    wl = I.workload("deep_48x4_b8_ctx32k")
+    s, lz, Bn, T = wl.shape, wl.lazy, wl.batch, wl.prompt
+    log(f"full depth decode: B={Bn} T={T} R={s.n_shared} K={s.n_loops}")
+    W = cached_weights(s, 0)
+    ids, states, oracles, outs = _full_context_case(s, lz, Bn, T, {Bn - 1: 41}, W, k_std=1.0)
+    model = B.LoopedModel(s, lz, W)
+    store = model.store(Bn, T, T + 1)
+    store.keep_codes(True)
+    store.import_(snapshot_with_states(store, s, lz, states))
+    g = _gpu_decode(model, store, ids)
+    assert np.isfinite(g).all()
+    seq = Bn - 1
+    run = _bf16_rerun(s, lz, W, T, states[seq], oracles[seq], ids[seq], outs[seq], g[seq])
+    _bound_check(f"sequence {seq}", max_abs_rel(g[seq], outs[seq]), run)
+
 
 
 REINJECT = [
@@ -355,3 +384,63 @@ def test_stores_with_different_loop_counts_share_a_model():
             e = max_abs_rel(g.cpu().numpy(), o)
             log(f"  step {i} K={k} decode {e:.3e}")
             assert e < TOL
+
+
+SNAP = [
+    ("lazy_int8_int4", dict(), I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4), None),
+    ("lazy_hd128_loops2", dict(n_heads=4, n_kv_heads=4, head_dim=128, d_model=512, n_loops=3),
+     I.Lazy(mode="lazy", rho=0.25, top_s=40, window=8, base_bits=16, res_bits=8), 2),
+    ("per_loop", dict(), I.Lazy(mode="per_loop"), None),
+    ("last_loop", dict(), I.Lazy(mode="last_loop"), None),
+]
+
+
+@pytest.mark.parametrize("name,kw,lz,loops", SNAP, ids=[c[0] for c in SNAP])
+def test_snapshot_resume_is_bit_exact(name, kw, lz, loops):
+    """Snapshots taken after prefill and after two decode steps, imported into a
+    fresh store of the same model and back into the original one (rewinding it):
+    the resumed decode steps equal the uninterrupted ones bit for bit, launched
+    eagerly and replayed from a captured graph (the import rebuilds the float16
+    decode caches, which the snapshot does not hold), and a store's snapshot
+    survives import and export unchanged."""
+    s = _small(**kw)
+    T, steps, Bsz = 150, 6, 2
+    W = I.gen_weights(s, seed=29)
+    ids = torch.from_numpy(I.gen_prompt_ids(s, Bsz, T))
+    dec = torch.from_numpy(I.gen_decode_ids(s, Bsz, steps)).cuda()
+    model = B.LoopedModel(s, lz, W)
+    log(f"snapshot {name}")
+    a = model.store(Bsz, T, T + steps, loops=loops)
+    model.prefill(a, ids)
+    snap0 = a.export()
+    ref = [model.decode(a, dec[i]).clone() for i in range(steps)]
+    torch.cuda.synchronize()
+    # rewind a to the end of prefill and decode again from a graph on a side stream
+    a.import_(snap0)
+    assert a.length() == T
+    side = torch.cuda.Stream()
+    for i in range(2):
+        with torch.cuda.stream(side):
+            o = model.decode(a, dec[i]).clone()
+        side.synchronize()
+        assert torch.equal(o, ref[i]), f"rewound step {i}"
+    snap2, used2 = a.export(), a.bytes_used()
+    # a fresh store resumes from either snapshot
+    b = model.store(Bsz, T, T + steps)
+    for snap, first in ((snap2, 2), (snap0, 0)):
+        b.import_(snap)
+        assert b.length() == T + first
+        if first == 2:
+            assert b.bytes_used() == used2
+        else:
+            assert np.array_equal(b.export(), snap0)
+        for i in range(first, steps):
+            with torch.cuda.stream(side):
+                o = model.decode(b, dec[i]).clone()
+            side.synchronize()
+            assert torch.equal(o, ref[i]), f"resumed from {first}, step {i}"
+    # another batch size is refused, and the refused store is left as it was
+    c = model.store(Bsz + 1, T, T + steps)
+    with pytest.raises(B.LKError):
+        c.import_(snap2)
+    assert c.length() == 0

@@ -230,3 +230,33 @@ def test_lazy_oracle_matches_brute_force(name, kw, lz):
             stored = np.nonzero(m.slot[k_ - 1, b] >= 0)[0]
             exp = sorted(list(m.sel[(k_, b)]) + list(range(T, T + steps)))
             assert list(stored) == exp
+
+
+@pytest.mark.parametrize("name,kw,lz", CASES, ids=[c[0] for c in CASES])
+def test_decode_from_a_given_state_matches_brute_force(name, kw, lz):
+    """An oracle started from another one's post-prefill store state (copies of its
+    base, residuals, slot maps, column sets and prelude/coda rows) decodes as the
+    brute-force whole-matrix reference does, and exactly as the oracle that ran the
+    prefill."""
+    import copy
+    s = I.workload("tiny_1p2x2c1_t32").shape
+    for k, v in kw.items():
+        setattr(s, k, v)
+    W = I.gen_weights(s, seed=21)
+    W["loop_emb"] *= np.float32(20.0)
+    T, steps, B = 28, 3, 2
+    ids = I.gen_prompt_ids(s, B, T, seed=22)
+    dec = I.gen_decode_ids(s, B, steps, seed=23)
+    a = LoopedOracle(s, lz, W, B, T + steps)
+    a.prefill(ids)
+    m = LoopedOracle(s, lz, W, B, T + steps)
+    m.start_from_state(T, copy.deepcopy(a.base), copy.deepcopy(a.res), a.slot.copy(), copy.deepcopy(a.S),
+                       dense_kv=[(a.dense_k[i].copy(), a.dense_v[i].copy())
+                                 for i in range(s.n_prelude + s.n_coda)])
+    assert all(np.array_equal(m.sel[key], a.sel[key]) for key in a.sel)
+    got = np.stack([m.decode(d) for d in dec], 1)
+    cont = np.stack([a.decode(d) for d in dec], 1)
+    assert np.array_equal(got, cont)
+    for b in range(B):
+        _, dref, _, _ = brute_lazy(s, lz, W, ids[b], dec[:, b])
+        assert np.max(np.abs(got[b] - dref)) / np.max(np.abs(dref)) < 1e-4
