@@ -24,6 +24,7 @@
 //   In both, 8 waves split K and meet in LDS; every load of a wave covers 64
 //   contiguous bytes of each of its rows.
 #include <algorithm>
+#include <atomic>
 
 #include "lk_kernels.h"
 
@@ -449,6 +450,18 @@ void launch_skinny(const u16* A, const float* X, const u16* gain, float eps, con
 // output columns, so each wave holds gate and up of its 64 output columns.
 // Requires K % 128 == 0 and N % 256 == 0 (SwiGLU: N % 128 == 0).
 constexpr int GB_M = 256, GB_N = 256, GB_K = 64, GB_STAGE = (GB_M + GB_N) * GB_K;
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+    static std::atomic<int> n[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!n[dev]) {
+        int c = 0;
+        n[dev] = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c >= 8 ? c : 256;
+    }
+    return n[dev];
+}
 __shared__ __attribute__((aligned(1024))) u16 gb_s0[GB_STAGE];
 __shared__ __attribute__((aligned(1024))) u16 gb_s1[GB_STAGE];
 typedef __attribute__((address_space(3))) void lds_void;
@@ -502,14 +515,13 @@ __device__ __forceinline__ void gb_mma(f32x16 (&acc)[4][4], const bf16x8 (&fa)[4
         for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
-// scheduling: one LDS read after each of the first eight MFMAs of a group
+// scheduling: the eight LDS reads of the next k-slice spread over the 16 MFMAs of a group
 __device__ __forceinline__ void gb_sched_reads() {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 }
 
 // One slab in stage U.  On entry x holds k-slice 0 of the slab.  NEXT: another slab
@@ -536,39 +548,29 @@ __device__ __forceinline__ void gb_slab(f32x16 (&acc)[4][4], bf16x8 (&xa)[4], bf
     }
     gb_mma(acc, ya, yb);
     if (NEXT) {
-        if (DMA) {
+        if (DMA) {  // the 16 slab loads one per MFMA, the 8 LDS reads one per two
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // buffer loads
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         } else {
             gb_sched_reads();
         }
     }
 }
 
+// One 256 x 256 output tile (tm, tn).
 template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_big_kernel(const u16* __restrict__ A, const u16* __restrict__ W,
-                                                          int M, int N, int K, float* __restrict__ C,
-                                                          u16* __restrict__ Obf, int tiles_m, int tiles_n) {
+__device__ __forceinline__ void gb_tile(const u16* __restrict__ A, const u16* __restrict__ W, int M, int N, int K,
+                                        float* __restrict__ C, u16* __restrict__ Obf, int tm, int tn) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
     const int tid = threadIdx.x, lane = tid & 63;
     const int ws = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = ws >> 1, wn = ws & 1, l32 = lane & 31, kg = lane >> 5;
-    // tile order: XCD-major (grid is a multiple of 8), then groups of 8 M-tiles
-    const int ntiles = tiles_m * tiles_n;
-    const int per_xcd = gridDim.x / 8;
-    const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (t >= ntiles) return;
-    constexpr int GROUP = 8;
-    const int group_size = GROUP * tiles_n;
-    const int gid = t / group_size, first_m = gid * GROUP;
-    const int gm = min(tiles_m - first_m, GROUP);
-    const int tm = first_m + (t % group_size) % gm;
-    const int tn = (t % group_size) / gm;
     const int row0 = tm * GB_M;
     GbSrc src;
     src.ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long long)row0 * K), (short)0,
@@ -611,51 +613,79 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const u16* __restrict_
     gb_slab<1, false, false>(acc, xa, xb, ya, yb, src, s + 1, ws, wm, wn, l32, kg);
     // epilogue: acc[i][j][e] = C[row0 + wm*128 + 32 i + 8 (e/4) + 4 kg + e%4][col(j) + l32]
     if (EPI == EPI_ADD) {
-        // residual add: all 64 loads of a 32-row group are in flight before the first store
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float cv[16][4];
+        // residual add, software-pipelined over the four 32-row groups: the 64 loads of
+        // group i + 1 are issued before the stores of group i, so only the first group's
+        // loads cost a full memory round trip
+        float cv[2][16][4];
+        auto load_group = [&](int i, float (&dst)[16][4]) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int r = row0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * kg + (e & 3);
                 const float* crow = C + (long long)min(r, M - 1) * N + tn * GB_N + wn * 128 + l32;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) cv[e][j] = crow[32 * j];
+                for (int j = 0; j < 4; ++j) dst[e][j] = crow[32 * j];
             }
+        };
+        load_group(0, cv[0]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i + 1 < 4) load_group(i + 1, cv[(i + 1) & 1]);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int r = row0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * kg + (e & 3);
                 if (r >= M) continue;
                 float* crow = C + (long long)r * N + tn * GB_N + wn * 128 + l32;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) crow[32 * j] = cv[e][j] + acc[i][j][e];
+                for (int j = 0; j < 4; ++j) crow[32 * j] = cv[i & 1][e][j] + acc[i][j][e];
             }
         }
-        return;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = row0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * kg + (e & 3);
+                if (r >= M) continue;
+                if (DUAL) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int col = tn * 128 + wn * 64 + 32 * j + l32;
+                        Obf[(long long)r * N + col] = f2bf(silu_f(acc[i][j][e]) * acc[i][j + 2][e]);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int col = tn * GB_N + wn * 128 + 32 * j + l32;
+                        const long long o = (long long)r * N + col;
+                        if (EPI == EPI_STORE) C[o] = acc[i][j][e];
+                        else Obf[o] = f2bf(gelu_f(acc[i][j][e]));
+                    }
+                }
+            }
+        }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int r = row0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * kg + (e & 3);
-            if (r >= M) continue;
-            if (DUAL) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int col = tn * 128 + wn * 64 + 32 * j + l32;
-                    Obf[(long long)r * N + col] = f2bf(silu_f(acc[i][j][e]) * acc[i][j + 2][e]);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int col = tn * GB_N + wn * 128 + 32 * j + l32;
-                    const long long o = (long long)r * N + col;
-                    if (EPI == EPI_STORE) C[o] = acc[i][j][e];
-                    else if (EPI == EPI_ADD) C[o] = C[o] + acc[i][j][e];
-                    else Obf[o] = f2bf(gelu_f(acc[i][j][e]));
-                }
-            }
-        }
+}
+
+// Persistent over tiles: workgroup b stays on XCD b % 8 and takes that XCD's share of
+// the tiles (a contiguous range of the tile order) in turn, so a CU goes from one tile's
+// epilogue straight to the next tile's loads, and CUs drift out of step instead of all
+// storing at once.  Tile order within the range: groups of 8 M-tiles, N-tiles inside.
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_big_kernel(const u16* __restrict__ A, const u16* __restrict__ W,
+                                                          int M, int N, int K, float* __restrict__ C,
+                                                          u16* __restrict__ Obf, int tiles_m, int tiles_n) {
+    const int ntiles = tiles_m * tiles_n;
+    const int per_xcd = (ntiles + 7) / 8;
+    const int xcd = blockIdx.x % 8, slots = gridDim.x / 8;
+    constexpr int GROUP = 8;
+    const int group_size = GROUP * tiles_n;
+    for (int local = blockIdx.x / 8; local < per_xcd; local += slots) {
+        const int t = xcd * per_xcd + local;
+        if (t >= ntiles) break;
+        if (local != (int)blockIdx.x / 8) bare_barrier();  // every wave is done with the LDS stages
+        const int gid = t / group_size, first_m = gid * GROUP;
+        const int gm = min(tiles_m - first_m, GROUP);
+        gb_tile<EPI>(A, W, M, N, K, C, Obf, first_m + (t % group_size) % gm, (t % group_size) / gm);
     }
 }
 
@@ -667,8 +697,9 @@ bool launch_big(const u16* A, const u16* W, int M, int N, int K, float* c, u16* 
     const long long wspan = (EPI == EPI_SWIGLU) ? (long long)N + 128 : GB_N;
     if (wspan * K * 2 >= (1LL << 31) || (long long)GB_M * K * 2 >= (1LL << 31)) return false;
     const int tiles_m = (M + GB_M - 1) / GB_M, tiles_n = N / nspan;
-    // grid: a multiple of 8 so that tile t = (pid % 8) * (grid / 8) + pid / 8 covers every tile once
-    const int grid = (tiles_m * tiles_n + 7) / 8 * 8;
+    // grid: a multiple of 8 (workgroups per XCD), at most one workgroup per CU
+    const int per_xcd = (tiles_m * tiles_n + 7) / 8;
+    const int grid = 8 * std::min(per_xcd, cu_count() / 8);
     hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(grid), dim3(256), 0, st, A, W, M, N, K, c, out_bf, tiles_m,
                        tiles_n);
     return true;
