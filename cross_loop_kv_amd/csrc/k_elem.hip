@@ -288,9 +288,16 @@ __global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, in
     if (u < nq) {
         const int hh = u * qpb + t / half, i = t % half;
         if (hh >= H) return;
-        double sd, cd;
-        sincos((double)pos * inv.v[i], &sd, &cd);
-        const float c = (float)cd, sn = (float)sd;
+        float c, sn;
+        if (w.rope_cs) {
+            c = w.rope_cs[2 * i];
+            sn = w.rope_cs[2 * i + 1];
+        } else {
+            double sd, cd;
+            sincos((double)pos * inv.v[i], &sd, &cd);
+            c = (float)cd;
+            sn = (float)sd;
+        }
         const float x1 = src[hh * hd + i], x2 = src[hh * hd + i + half];
         u16* dq = q_out + (long long)r * H * hd + hh * hd;
         dq[i] = f2bf(x1 * c - x2 * sn);
@@ -303,9 +310,16 @@ __global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, in
     float x;
     if (kv == 0) {
         const int i = e % half;
-        double sd, cd;
-        sincos((double)pos * inv.v[i], &sd, &cd);
-        const float c = (float)cd, sn = (float)sd;
+        float c, sn;
+        if (w.rope_cs) {
+            c = w.rope_cs[2 * i];
+            sn = w.rope_cs[2 * i + 1];
+        } else {
+            double sd, cd;
+            sincos((double)pos * inv.v[i], &sd, &cd);
+            c = (float)cd;
+            sn = (float)sd;
+        }
         const float x1 = src[(H + g) * hd + i], x2 = src[(H + g) * hd + i + half];
         x = e < half ? x1 * c - x2 * sn : x2 * c + x1 * sn;
     } else {
@@ -456,6 +470,22 @@ hipError_t quantize_rows(const float* x, int rows, int hd, int bits, uint8_t* co
     const long long blocks = (groups + per_block - 1) / per_block;
     hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, x, groups,
                        hd, bits, codes, scales);
+    return hipGetLastError();
+}
+
+__global__ void rope_angles_kernel(const int32_t* dpos, InvFreq inv, int half, float* cs) {
+    const int i = threadIdx.x;
+    if (i >= half) return;
+    double sd, cd;
+    sincos((double)*dpos * inv.v[i], &sd, &cd);
+    cs[2 * i] = (float)cd;
+    cs[2 * i + 1] = (float)sd;
+}
+
+hipError_t rope_angles(const int32_t* dpos, const double* inv_freq, int hd, float* cs, hipStream_t st) {
+    InvFreq inv;
+    for (int i = 0; i < hd / 2; ++i) inv.v[i] = inv_freq[i];
+    hipLaunchKernelGGL(rope_angles_kernel, dim3(1), dim3(64), 0, st, dpos, inv, hd / 2, cs);
     return hipGetLastError();
 }
 

@@ -352,6 +352,7 @@ struct WS {
     float* out;        // decode: the step's output rows
     float* ps;         // decode: per-workgroup row sums of x^2 for the next RMSNorm ([d/8][8])
     float* tokrec;     // decode, lazy: float32 K/V reconstruction of the step's rows [R][B][2][Hkv][hd]
+    float* rope;       // decode: cos and sin of the step's position, [hd/2][2]
     u16 *frk, *frv;    // prefill, lazy loops >= 2 (hd 128): float16 loop-k K/V at every prompt position
     int fr_cap;        // rows per (b, g) of frk / frv (T rounded up to 64; 0: none)
     size_t total;
@@ -403,6 +404,7 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
     w.frk = (u16*)take(fr_elems * 2);
     w.frv = (u16*)take(fr_elems * 2);
     w.out = (float*)take((long long)B * d * 4);
+    w.rope = (float*)take(T == 1 ? (long long)c.head_dim * 4 : 0);
     w.total = off;
     return w;
 }
@@ -434,6 +436,7 @@ int check_cfg(const lk_model_cfg* c, const lk_lazy_cfg* z) {
         if (z->res_bits != 16 && z->res_bits != 8 && z->res_bits != 4)
             return fail(LK_ERR_INVALID_ARG, "res_bits must be 16, 8 or 4");
         if (z->group != 32) return fail(LK_ERR_UNSUPPORTED, "group must be 32");
+        if (z->stale_keys != 0 && z->stale_keys != 1) return fail(LK_ERR_INVALID_ARG, "stale_keys must be 0 or 1");
     }
     return LK_OK;
 }
@@ -548,6 +551,7 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
     const int32_t* pos = io.pos;
     lk::KVWrite kw = kvw;
     kw.dpos = io.dpos;
+    if (io.dpos && !io.pos && io.rows_per_seq == 1) kw.rope_cs = w.rope;  // decode: one position
     LK_HIP(lk::rope_kv_write(w.qkv, io.M, io.rows_per_seq, pos, io.pos_offset, H, c.n_kv_heads, hd,
                              h->inv_freq, w.q, kw, st));
     if (ap.kind == ATTN_PREFILL_DENSE) {
@@ -709,7 +713,8 @@ bool same_cfg(const lk_model_cfg& a, const lk_model_cfg& b) {
 
 bool same_lazy(const lk_lazy_cfg& a, const lk_lazy_cfg& b) {
     return a.mode == b.mode && a.rho == b.rho && a.top_s == b.top_s && a.window == b.window &&
-           a.base_bits == b.base_bits && a.res_bits == b.res_bits && a.group == b.group;
+           a.base_bits == b.base_bits && a.res_bits == b.res_bits && a.group == b.group &&
+           a.stale_keys == b.stale_keys;
 }
 
 }  // namespace
@@ -1035,7 +1040,9 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
                 LK_TRY(run_layer(h, P + r, cio, kw, ap, w, st));
             }
             if (k < K) {
-                LK_HIP(lk::fill_f32(w.keys, 0.f, (long long)M, st));
+                // the next loop's keys: the change of every recomputed token; a carried
+                // token's is zero, or (stale_keys) stays the one it has
+                if (!h->z.stale_keys) LK_HIP(lk::fill_f32(w.keys, 0.f, (long long)M, st));
                 LK_HIP(lk::scatter_rows(w.xc, w.sel, B, n, T, d, w.h, w.keys, st));
             } else {
                 LK_HIP(lk::scatter_rows(w.xc, w.sel, B, n, T, d, w.h, nullptr, st));
@@ -1173,6 +1180,7 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
     // Folded norms: every projection input is prepared by the kernel that produced x.
     const bool fold = B <= 8 && h->pk_buf != nullptr;
     LK_HIP(lk::embed(w.ids, h->tok, w.h, B, d, c.vocab, st));
+    LK_HIP(lk::rope_angles(dpos, h->inv_freq, c.head_dim, w.rope, st));
     // re-injection: e = the prelude output (the embedding when there is no prelude)
     if (inject && K >= 2 && P == 0) LK_HIP(lk::copy_f32(w.h, w.h0, (long long)B * d, st));
     if (fold)

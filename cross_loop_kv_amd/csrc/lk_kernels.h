@@ -57,7 +57,13 @@ struct KVWrite {
     // previous loop of this layer (read by kind 2) and at this loop (written), in place
     // of re-reading base + residuals through the slot maps.
     float* tok_recon;
+    // decode (every row at position *dpos): cos and sin of the rotation angles of that
+    // position, [hd/2][2] (rope_angles), in place of evaluating them per element
+    const float* rope_cs;
 };
+// cos and sin (float64 evaluation, rounded to float32) of position *dpos times each
+// inverse frequency into cs [hd/2][2].
+hipError_t rope_angles(const int32_t* dpos, const double* inv_freq, int hd, float* cs, hipStream_t st);
 hipError_t rope_kv_write(const float* qkv, int rows, int rows_per_seq, const int32_t* pos,
                          int pos_offset, int H, int Hkv, int hd, const double* inv_freq, u16* q_out,
                          const KVWrite& kvw, hipStream_t st);

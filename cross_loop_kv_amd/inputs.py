@@ -66,6 +66,7 @@ class Lazy:
     base_bits: int = 16     # loop-1 KV: 16 (working precision) or 8 (int8, group 32)
     res_bits: int = 16      # loop-k residual: 16, 8 or 4
     group: int = 32
+    stale_keys: bool = False  # carried tokens keep their last measured change (else 0)
 
 
 @dataclass

@@ -78,11 +78,17 @@ typedef struct {
 /* Cache/update policy.  mode LK_MODE_*; rho in (0, 1] (kept-token fraction at
  * loops >= 2), top_s >= 1 stable columns, window >= 1, base_bits 16 | 8,
  * res_bits 16 | 8 | 4, group must be 32.  Only mode LK_MODE_LAZY reads the
- * other fields. */
+ * other fields.  stale_keys (0 | 1): 0 ranks a token carried through loop k-1 by
+ * its change there, which is zero, so loop k >= 3 picks within the tokens loop
+ * k-1 recomputed; 1 lets a carried token keep the change measured when it was
+ * last recomputed (loop 2 measures every token), so tokens left out by one loop
+ * can be picked again later (the FlashLoop abstract, arxivdaily.com: state
+ * changes concentrate on a small subset of tokens as the loops proceed). */
 typedef struct {
     int32_t mode;
     double rho;
     int32_t top_s, window, base_bits, res_bits, group;
+    int32_t stale_keys;
 } lk_lazy_cfg;
 
 /* Device pointers of one layer, all bfloat16 row-major:

@@ -31,8 +31,9 @@ not given on any page):
   softmax probabilities; S = the top_s columns by mass (all columns if
   T <= top_s), reused at every later loop and decode step.
 * lazy loop k >= 2: key_i = ||h_{k-1,i} - h_{k-2,i}||^2 (h_0 = prelude output;
-  carried rows have key 0); the n largest keys are recomputed, the rest carry
-  forward unchanged.  A recomputed query i attends over
+  carried rows have key 0, or with ``lazy.stale_keys`` keep the key they had at
+  loop k-1, i.e. the change measured when they were last recomputed); the n
+  largest keys are recomputed, the rest carry forward unchanged.  A recomputed query i attends over
   (S intersect [0, i]) union [max(0, i-w+1), i] of the loop-k reconstruction.
 * input re-injection (aiboss88.com tutorial, step 3: a structure that passes the
   input representation into every loop): with ``shape.input_reinject`` the prelude
@@ -413,8 +414,15 @@ class LoopedOracle:
             x = self._out_ffn(P + r, x, o)
         h_prev2, h_prev = h0, x
         n = self.n_sel
+        stale = bool(getattr(lz, "stale_keys", False))
         for k in range(2, K + 1):
             key = np.sum((h_prev - h_prev2) ** 2, axis=-1, dtype=F32)
+            if stale and k >= 3:
+                # a token carried through loop k-1 keeps the change measured when it
+                # was last recomputed
+                carried = np.ones(key.shape[0], bool)
+                carried[self.sel[(k - 1, b)]] = False
+                key = np.where(carried, self.keys[(k - 1, b)], key).astype(F32)
             self.keys[(k, b)] = key
             if self.forced_tokens is not None:
                 I = self.forced_tokens[(k, b)]

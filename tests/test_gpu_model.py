@@ -128,6 +128,44 @@ def test_lazy_natural_selection_agrees_with_oracle():
     assert r["err_prefill"] < 0.1
 
 
+def test_stale_keys_natural_selection_agrees_with_oracle():
+    """Stale keys (a carried token keeps the change measured when it was last
+    recomputed) with natural selection over 4 loops: the GPU's kept-token sets agree
+    with the oracle's (Jaccard > 0.8: keys are float32 sums taken in another order, so
+    near-ties can fall either way), and loops 3 and 4 pick tokens that the previous loop
+    carried, which plain keys never do."""
+    s = _small(n_loops=4)
+    lz = I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4, stale_keys=True)
+    r = run_pair(s, lz, batch=2, prompt=150, steps=2, seed=7, force=False)
+    sel, _ = gpu_selection(r["store"], s, 2, 150)
+    m = r["oracle"]
+    jac, left_out = [], 0
+    for (k, b), idx in sel.items():
+        a, o = set(idx.tolist()), set(m.sel[(k, b)].tolist())
+        jac.append(len(a & o) / len(a | o))
+        if k >= 3:
+            left_out += len(a - set(sel[(k - 1, b)].tolist()))
+    log(f"  stale keys: token-set Jaccard min {min(jac):.3f} mean {np.mean(jac):.3f}; "
+        f"tokens picked after being carried {left_out}; prefill drift vs oracle {r['err_prefill']:.3e}")
+    assert min(jac) > 0.8 and left_out > 0
+    # a token recomputed on one side and carried on the other moves its row by far more
+    # than rounding, so the outputs are compared only when every set agrees (the
+    # computation on equal sets is checked with forced selection below)
+    if min(jac) == 1.0:
+        assert r["err_prefill"] < 0.1
+
+
+def test_stale_keys_forced_selection_matches_oracle():
+    """With the oracle's stale-key selections injected, prefill and decode agree with
+    the oracle to the usual bound (the kept sets now leave the previous loop's)."""
+    s = _small(n_loops=4)
+    lz = I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4, stale_keys=True)
+    r = run_pair(s, lz, batch=2, prompt=150, steps=3, seed=7)
+    m = r["oracle"]
+    assert sum(len(set(m.sel[(k, b)]) - set(m.sel[(k - 1, b)])) for k in (3, 4) for b in range(2)) > 0
+    check(r, "stale keys")
+
+
 def test_lazy_rho1_all_columns_matches_gpu_dense():
     """rho = 1, every column, 16-bit rows: the lazy path computes the dense function."""
     s = _small()

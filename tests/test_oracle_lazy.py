@@ -130,8 +130,14 @@ def brute_lazy(shape, lz, W, ids, dec):
     hist = [h0[:T], x]
     n = n_selected(lz.rho, T)
     sel = {}
+    last_change = None   # per token: the change measured when it was last recomputed
     for kk in range(2, K + 1):
         key = ((hist[-1].astype(np.float64) - hist[-2]) ** 2).sum(-1)
+        if getattr(lz, "stale_keys", False) and last_change is not None:
+            for i in range(T):
+                if i not in sel[kk - 1]:
+                    key[i] = last_change[i]
+        last_change = key.copy()
         Ik = sorted(sorted(range(T), key=lambda i: (-key[i], i))[:n])
         sel[kk] = Ik
         xs = hist[-1][Ik] + W["loop_emb"][kk - 1]
@@ -196,6 +202,8 @@ CASES = [
      I.Lazy(mode="lazy", rho=0.3, top_s=6, window=3, base_bits=8, res_bits=4)),
     ("gqa_res16", dict(n_heads=4, n_kv_heads=1, ffn_act="swiglu", n_loops=3, n_prelude=0),
      I.Lazy(mode="lazy", rho=0.25, top_s=5, window=2, base_bits=16, res_bits=16)),
+    ("stale_keys_k4", dict(n_heads=4, n_kv_heads=2, ffn_act="swiglu", n_loops=4),
+     I.Lazy(mode="lazy", rho=0.3, top_s=6, window=3, base_bits=8, res_bits=8, stale_keys=True)),
 ]
 
 
@@ -260,3 +268,43 @@ def test_decode_from_a_given_state_matches_brute_force(name, kw, lz):
     for b in range(B):
         _, dref, _, _ = brute_lazy(s, lz, W, ids[b], dec[:, b])
         assert np.max(np.abs(got[b] - dref)) / np.max(np.abs(dref)) < 1e-4
+
+
+def test_stale_keys_reselect_tokens_outside_the_previous_set():
+    """Without stale keys, loop k >= 3 picks within the tokens loop k-1 recomputed (the
+    others changed by zero); with them, a token left out at loop k-1 competes with the
+    change it showed when last recomputed, so later sets leave the previous one.  At
+    K = 2 the switch changes nothing (loop 2 measures every token)."""
+    s = I.workload("tiny_1p2x2c1_t32").shape
+    s.n_loops = 4
+    W = I.gen_weights(s, seed=31)
+    T, B, steps = 30, 2, 2
+    ids = I.gen_prompt_ids(s, B, T, seed=32)
+    dec = I.gen_decode_ids(s, B, steps, seed=33)
+    base = dict(mode="lazy", rho=0.3, top_s=6, window=3, base_bits=16, res_bits=16)
+    plain = LoopedOracle(s, I.Lazy(**base), W, B, T)
+    plain.prefill(ids)
+    stale = LoopedOracle(s, I.Lazy(**base, stale_keys=True), W, B, T + steps)
+    out = stale.prefill(ids)
+    douts = np.stack([stale.decode(d) for d in dec], 1)
+    for b in range(B):   # the brute-force reference with stale keys agrees
+        ref, dref, sel, _ = brute_lazy(s, I.Lazy(**base, stale_keys=True), W, ids[b], dec[:, b])
+        for k_, Ik in sel.items():
+            assert list(stale.sel[(k_, b)]) == Ik
+        assert np.max(np.abs(out[b] - ref)) / np.max(np.abs(ref)) < 1e-4
+        assert np.max(np.abs(douts[b] - dref)) / np.max(np.abs(dref)) < 1e-4
+    left_out = 0
+    for b in range(B):
+        assert np.array_equal(plain.sel[(2, b)], stale.sel[(2, b)])
+        for k in (3, 4):
+            assert set(plain.sel[(k, b)]) <= set(plain.sel[(k - 1, b)])
+            left_out += len(set(stale.sel[(k, b)]) - set(stale.sel[(k - 1, b)]))
+            # a carried token's key is its key of the previous loop
+            carried = np.setdiff1d(np.arange(T), stale.sel[(k - 1, b)])
+            assert np.array_equal(stale.keys[(k, b)][carried], stale.keys[(k - 1, b)][carried])
+    assert left_out > 0
+    s.n_loops = 2
+    W2 = I.gen_weights(s, seed=31)
+    o1 = LoopedOracle(s, I.Lazy(**base), W2, B, T).prefill(ids)
+    o2 = LoopedOracle(s, I.Lazy(**base, stale_keys=True), W2, B, T).prefill(ids)
+    assert np.array_equal(o1, o2)
