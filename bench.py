@@ -242,34 +242,34 @@ def cpu_baseline(wl, n_steps=8, rng_seed=3):
     R_full = wl.shape.n_shared
     W = I.gen_weights(s1)
     B, T, lz = wl.batch, wl.prompt, wl.lazy
-    m = LoopedOracle(s1, lz, W, B, T + n_steps)
+    Tm = T + n_steps
+    m = LoopedOracle(s1, lz, W, B, Tm)
     rng = np.random.default_rng(rng_seed)
-    Hkv, hd = s1.n_kv_heads, s1.head_dim
-    m.T, m.t = T, T
+    Hkv, hd, K = s1.n_kv_heads, s1.head_dim, s1.n_loops
     if lz.mode == "lazy":
-        m.n_sel = n_selected(lz.rho, T)
-        m._alloc_residuals(m.n_sel + n_steps)
-        for kv in range(2):
-            if lz.base_bits == 16:
-                m.base[0][kv][:] = rng.standard_normal(m.base[0][kv].shape, np.float32)
-            else:
-                m.base[0][kv][0][:] = rng.integers(-127, 128, m.base[0][kv][0].shape, dtype=np.int8)
-                m.base[0][kv][1][:] = np.float16(0.01)
-        for k in range(2, s1.n_loops + 1):
+        # a synthetic prefill state: base rows, kept-row residuals, slot maps, column sets
+        n = n_selected(lz.rho, T)
+        ng = hd // lz.group
+
+        def rows(n_rows, qmax, scale):
+            if qmax is None:
+                return rng.standard_normal((B, Hkv, n_rows, hd), np.float32)
+            return (rng.integers(-qmax, qmax + 1, (B, Hkv, n_rows, hd), dtype=np.int8),
+                    np.full((B, Hkv, n_rows, ng), scale, np.float16))
+
+        base = [[rows(Tm, None if lz.base_bits == 16 else 127, 0.01) for _ in range(2)]]
+        qres = None if lz.res_bits == 16 else 2 ** (lz.res_bits - 1) - 1
+        res = {(k, 0, kv): rows(n + n_steps, qres, 0.001) for k in range(2, K + 1) for kv in range(2)}
+        slot = np.full((K, B, Tm), -1, np.int32)
+        for k in range(2, K + 1):
             for b in range(B):
-                idx = np.sort(rng.choice(T, m.n_sel, replace=False))
-                m.slot[k - 1, b, idx] = np.arange(m.n_sel, dtype=np.int32)
-            for kv in range(2):
-                st = m.res[(k, 0, kv)]
-                if lz.res_bits == 16:
-                    st[:] = rng.standard_normal(st.shape, np.float32)
-                else:
-                    q = 2 ** (lz.res_bits - 1) - 1
-                    st[0][:] = rng.integers(-q, q + 1, st[0].shape, dtype=np.int8)
-                    st[1][:] = np.float16(0.001)
+                slot[k - 1, b, np.sort(rng.choice(T, n, replace=False))] = np.arange(n, dtype=np.int32)
         ncols = min(lz.top_s, T)
-        m.S = [[[np.sort(rng.choice(T, ncols, replace=False)).astype(np.int32) for _ in range(Hkv)]
-                for _ in range(B)]]
+        S = [[[np.sort(rng.choice(T, ncols, replace=False)).astype(np.int32) for _ in range(Hkv)]
+              for _ in range(B)]]
+        m.start_from_state(T, base, res, slot, S)
+    else:
+        m.T = m.t = T   # dense rows of a T-token prompt, left at zero
     ids = I.gen_decode_ids(s1, B, n_steps)
     t0 = time.time()
     for i in range(n_steps):
