@@ -568,6 +568,21 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
     // row of key `key` in kv (window ring: position ring0 + key at row % Tmax)
     auto row_of = [&](int key) { return seg2 ? (ring0 + key) % kv.Tmax : key; };
     const float sl2 = kLog2e / sqrtf((float)HD);
+    if (a.fuse_kv) {
+        // the new token's K/V row goes to the store first when this workgroup reads it
+        const int pos = *a.dpos;
+        const int key = SEG ? pos - ring0 : pos;
+        if ((!SEG || seg2) && key >= c_begin && key < c_begin + a.chunk) {
+            const int kvh = threadIdx.x >> 7, e = threadIdx.x & 127;
+            if (e < HD) {
+                const float c = kvh == 0 ? a.rope_cs[2 * (e % (HD / 2))] : 1.f;
+                const float sn = kvh == 0 ? a.rope_cs[2 * (e % (HD / 2)) + 1] : 0.f;
+                kv_write_elem(a.qkv + (long long)b * (a.H + 2 * Hkv) * HD, a.H, Hkv, HD, b, g, kvh, e, pos, 0, c, sn,
+                              a.kvw, kvh == 0 && g == 0 && e == 0);
+            }
+            __syncthreads();
+        }
+    }
 
     // int8 rows (hd >= 64): lane (key, kgrp) reads 16 bytes at 64h + 16 kgrp of its K row
     // for h < NQ / 2, so every load covers 64 contiguous bytes of each key; k-step j
@@ -580,7 +595,35 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (hvalid) v = *(const uint4*)(a.q + (long long)b * a.H * HD + (g * G + c16) * HD + kslice(j));
+        if (hvalid && a.fuse_kv) {  // rotate the float32 projection here (bf16 result)
+            // the 8 elements e0.. are pairs i0.. (one half of the head): 16-byte loads
+            const int e0 = kslice(j), i0 = e0 % (HD / 2);
+            const float* qh = a.qkv + (long long)b * (a.H + 2 * Hkv) * HD + (g * G + c16) * HD;
+            float x1[8], x2[8], cs[16];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                *(float4*)&x1[4 * t] = *(const float4*)(qh + i0 + 4 * t);
+                *(float4*)&x2[4 * t] = *(const float4*)(qh + i0 + HD / 2 + 4 * t);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) *(float4*)&cs[4 * t] = *(const float4*)(a.rope_cs + 2 * i0 + 4 * t);
+            const bool lo = e0 < HD / 2;
+            uint32_t o[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                float r2[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int m = 2 * t + u;
+                    const float c = cs[2 * m], sn = cs[2 * m + 1];
+                    r2[u] = lo ? x1[m] * c - x2[m] * sn : x2[m] * c + x1[m] * sn;
+                }
+                o[t] = pack_bf2(r2[0], r2[1]);
+            }
+            v = make_uint4(o[0], o[1], o[2], o[3]);
+        } else if (hvalid) {
+            v = *(const uint4*)(a.q + (long long)b * a.H * HD + (g * G + c16) * HD + kslice(j));
+        }
         if (HALF) {  // bf16 -> f16
             const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
             uint32_t o[4];

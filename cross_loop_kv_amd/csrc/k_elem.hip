@@ -307,10 +307,9 @@ __global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, in
     const int kv = (u - nq) / Hkv, g = (u - nq) % Hkv;
     const int e = t;
     if (e >= hd) return;  // whole 32-lane groups (hd is a multiple of 32)
-    float x;
+    float c = 1.f, sn = 0.f;
     if (kv == 0) {
         const int i = e % half;
-        float c, sn;
         if (w.rope_cs) {
             c = w.rope_cs[2 * i];
             sn = w.rope_cs[2 * i + 1];
@@ -320,71 +319,8 @@ __global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, in
             c = (float)cd;
             sn = (float)sd;
         }
-        const float x1 = src[(H + g) * hd + i], x2 = src[(H + g) * hd + i + half];
-        x = e < half ? x1 * c - x2 * sn : x2 * c + x1 * sn;
-    } else {
-        x = src[(H + Hkv + g) * hd + e];
     }
-    const KVLayer& L = w.layer;
-    const long long slot = w.slot_base + (w.dpos ? *w.dpos : 0) + iseq;
-    const long long row = kv_row(L, b, g, pos);
-    const long long idx = kv == 0 ? row * hd + e : v_elem(L, b, g, pos, e);
-    // decode: this row's reconstruction at the current loop, carried to the next loop
-    float* tr = w.tok_recon ? w.tok_recon + (((long long)b * 2 + kv) * Hkv + g) * hd + e : nullptr;
-    if (w.kind == 0 || (w.kind == 1 && L.base_bits == 16)) {
-        const u16 xb = f2bf(x);
-        ((u16*)L.base[kv])[idx] = xb;
-        if (tr) *tr = bf2f(xb);
-    } else if (w.kind == 1) {  // int8 base: residual against a zero reconstruction
-        float recon;
-        if (!w.keep_codes) {
-            u16 sb;
-            const int c = quant_group32(x, 127, &sb);
-            ((int8_t*)L.base[kv])[idx] = (int8_t)c;
-            if ((t & 31) == 0) {
-                const long long si = kv == 0 ? row * (hd / 32) + e / 32 : v_scale_idx(L, b, g, pos, e / 32);
-                ((u16*)L.base_scale[kv])[si] = sb;
-            }
-            recon = (float)c * h2f(sb);
-        } else {
-            recon = tr ? kv_base_elem(L, kv, b, g, pos, e) : 0.f;
-        }
-        if (tr) *tr = recon;
-    } else {
-        const long long rr = res_row(L, b, g, slot);
-        float recon;  // the row's loop-k reconstruction
-        if (L.res_bits == 16) {
-            const u16 xb = f2bf(x);
-            ((u16*)L.res[w.loop - 2][kv])[rr * hd + e] = xb;
-            recon = bf2f(xb);
-        } else {
-            const float prev = tr ? *tr : kv_recon_elem(L, kv, b, g, pos, e, w.loop - 1);
-            if (!w.keep_codes) {
-                u16 sb;
-                const int qmax = (1 << (L.res_bits - 1)) - 1;
-                const int c = quant_group32(x - prev, qmax, &sb);
-                if ((t & 31) == 0) ((u16*)L.res_scale[w.loop - 2][kv])[rr * (hd / 32) + e / 32] = sb;
-                if (L.res_bits == 8) {
-                    ((int8_t*)L.res[w.loop - 2][kv])[rr * hd + e] = (int8_t)c;
-                } else {
-                    const int other = __shfl_xor(c, 1);
-                    if ((t & 1) == 0)
-                        ((uint8_t*)L.res[w.loop - 2][kv])[rr * (hd / 2) + e / 2] = (uint8_t)((c & 0xF) | ((other & 0xF) << 4));
-                }
-                recon = prev + (float)c * h2f(sb);
-            } else {  // codes already in the store
-                recon = kv_apply_res(L, kv, b, g, w.loop, (int)slot, e, prev);
-            }
-        }
-        if (tr) *tr = recon;
-        if (w.ring_on) {
-            const KVLayer& Rg = w.ring;
-            const int rp = pos % Rg.Tmax;
-            const long long ri = kv == 0 ? kv_row(Rg, b, g, rp) * hd + e : v_elem(Rg, b, g, rp, e);
-            ((u16*)Rg.base[kv])[ri] = f2h_bits(recon);
-        }
-        if (w.slot_map_k && u == nq && t == 0) w.slot_map_k[(long long)b * L.Tmax + pos] = (int32_t)slot;
-    }
+    kv_write_elem(src, H, Hkv, hd, b, g, kv, e, pos, iseq, c, sn, w, u == nq && t == 0);
 }
 
 inline int grid_for(long long n) {

@@ -552,8 +552,11 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
     lk::KVWrite kw = kvw;
     kw.dpos = io.dpos;
     if (io.dpos && !io.pos && io.rows_per_seq == 1) kw.rope_cs = w.rope;  // decode: one position
-    LK_HIP(lk::rope_kv_write(w.qkv, io.M, io.rows_per_seq, pos, io.pos_offset, H, c.n_kv_heads, hd,
-                             h->inv_freq, w.q, kw, st));
+    // decode: the attention launch rotates q and writes the new token's K/V itself
+    const bool fuse_kv = kw.rope_cs && (ap.kind == ATTN_ROWS_DENSE || ap.kind == ATTN_ROWS_SPARSE);
+    if (!fuse_kv)
+        LK_HIP(lk::rope_kv_write(w.qkv, io.M, io.rows_per_seq, pos, io.pos_offset, H, c.n_kv_heads, hd,
+                                 h->inv_freq, w.q, kw, st));
     if (ap.kind == ATTN_PREFILL_DENSE) {
         LK_TRY(timed(h, TC_ATTN_PREFILL, st,
                      [=] { return lk::attn_prefill(w.q, ap.read, ap.B, ap.T, H, w.att, w.lse, st); }));
@@ -563,6 +566,10 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
     } else {
         lk::RowsAttn a{};
         a.q = w.q;
+        a.qkv = w.qkv;
+        a.rope_cs = w.rope;
+        a.kvw = kw;
+        a.fuse_kv = fuse_kv;
         a.qpos = io.pos;
         a.pos = ap.pos;
         a.dpos = ap.dpos;

@@ -68,6 +68,86 @@ hipError_t rope_kv_write(const float* qkv, int rows, int rows_per_seq, const int
                          int pos_offset, int H, int Hkv, int hd, const double* inv_freq, u16* q_out,
                          const KVWrite& kvw, hipStream_t st);
 
+// Element e of one token's K (kv = 0, rotated by the angle of pair e % (hd/2), cosine c,
+// sine sn) or V (kv = 1) row of KV head g into the store as w describes.  src: the
+// token's float32 projections [(H + 2 Hkv) hd]; b: its sequence, pos: its position,
+// iseq: its row within the sequence's rows of this call.  Threads e = 0..hd-1 of a
+// (token, kv, g) must be consecutive lanes of one wave from a 32-lane boundary: groups
+// of 32 quantize together.  `lead` (one thread per call) writes the slot map entry.
+__device__ __forceinline__ void kv_write_elem(const float* __restrict__ src, int H, int Hkv, int hd, int b, int g,
+                                              int kv, int e, int pos, int iseq, float c, float sn, const KVWrite& w,
+                                              bool lead) {
+    const int half = hd / 2;
+    float x;
+    if (kv == 0) {
+        const int i = e % half;
+        const float x1 = src[(H + g) * hd + i], x2 = src[(H + g) * hd + i + half];
+        x = e < half ? x1 * c - x2 * sn : x2 * c + x1 * sn;
+    } else {
+        x = src[(H + Hkv + g) * hd + e];
+    }
+    const KVLayer& L = w.layer;
+    const long long slot = w.slot_base + (w.dpos ? *w.dpos : 0) + iseq;
+    const long long row = kv_row(L, b, g, pos);
+    const long long idx = kv == 0 ? row * hd + e : v_elem(L, b, g, pos, e);
+    // decode: this row's reconstruction at the current loop, carried to the next loop
+    float* tr = w.tok_recon ? w.tok_recon + (((long long)b * 2 + kv) * Hkv + g) * hd + e : nullptr;
+    if (w.kind == 0 || (w.kind == 1 && L.base_bits == 16)) {
+        const u16 xb = f2bf(x);
+        ((u16*)L.base[kv])[idx] = xb;
+        if (tr) *tr = bf2f(xb);
+    } else if (w.kind == 1) {  // int8 base: residual against a zero reconstruction
+        float recon;
+        if (!w.keep_codes) {
+            u16 sb;
+            const int q = quant_group32(x, 127, &sb);
+            ((int8_t*)L.base[kv])[idx] = (int8_t)q;
+            if ((e & 31) == 0) {
+                const long long si = kv == 0 ? row * (hd / 32) + e / 32 : v_scale_idx(L, b, g, pos, e / 32);
+                ((u16*)L.base_scale[kv])[si] = sb;
+            }
+            recon = (float)q * h2f(sb);
+        } else {
+            recon = tr ? kv_base_elem(L, kv, b, g, pos, e) : 0.f;
+        }
+        if (tr) *tr = recon;
+    } else {
+        const long long rr = res_row(L, b, g, slot);
+        float recon;  // the row's loop-k reconstruction
+        if (L.res_bits == 16) {
+            const u16 xb = f2bf(x);
+            ((u16*)L.res[w.loop - 2][kv])[rr * hd + e] = xb;
+            recon = bf2f(xb);
+        } else {
+            const float prev = tr ? *tr : kv_recon_elem(L, kv, b, g, pos, e, w.loop - 1);
+            if (!w.keep_codes) {
+                u16 sb;
+                const int qmax = (1 << (L.res_bits - 1)) - 1;
+                const int q = quant_group32(x - prev, qmax, &sb);
+                if ((e & 31) == 0) ((u16*)L.res_scale[w.loop - 2][kv])[rr * (hd / 32) + e / 32] = sb;
+                if (L.res_bits == 8) {
+                    ((int8_t*)L.res[w.loop - 2][kv])[rr * hd + e] = (int8_t)q;
+                } else {
+                    const int other = __shfl_xor(q, 1);
+                    if ((e & 1) == 0)
+                        ((uint8_t*)L.res[w.loop - 2][kv])[rr * (hd / 2) + e / 2] = (uint8_t)((q & 0xF) | ((other & 0xF) << 4));
+                }
+                recon = prev + (float)q * h2f(sb);
+            } else {  // codes already in the store
+                recon = kv_apply_res(L, kv, b, g, w.loop, (int)slot, e, prev);
+            }
+        }
+        if (tr) *tr = recon;
+        if (w.ring_on) {
+            const KVLayer& Rg = w.ring;
+            const int rp = pos % Rg.Tmax;
+            const long long ri = kv == 0 ? kv_row(Rg, b, g, rp) * hd + e : v_elem(Rg, b, g, rp, e);
+            ((u16*)Rg.base[kv])[ri] = f2h_bits(recon);
+        }
+        if (w.slot_map_k && lead) w.slot_map_k[(long long)b * L.Tmax + pos] = (int32_t)slot;
+    }
+}
+
 // ---- GEMM (k_gemm.hip).  C = A[M,K] * W[N,K]^T, bf16 inputs, fp32 accumulation.
 enum Epi { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2, EPI_GELU = 3 };
 // STORE/ADD: c float32 [M, N] (ldc = N).  SWIGLU: W = [gate (N rows); up (N rows)],
@@ -141,6 +221,15 @@ struct RowsAttn {
     // position (max(0, pos-window+1) & ~7) with those below the window masked.
     KVLayer kv2;
     int seg_split;
+    // Decode (one row per sequence at position *dpos) with fuse_kv: q comes from the
+    // float32 projections qkv [B][(H + 2 Hkv) hd], rotated here with rope_cs
+    // ([hd/2][cos, sin] of the position), and the workgroup whose keys include the new
+    // position first writes that token's K/V row as kvw describes (the work a separate
+    // rope_kv_write launch does otherwise).
+    const float* qkv;
+    const float* rope_cs;
+    KVWrite kvw;
+    int fuse_kv;
 };
 // Write loop-k reconstructions as float16 rows into kc [B*Hkv][ncap][hd] and
 // 8-key-interleaved vc [B*Hkv][ncap/8][hd][8] (rows past the count are zero):
