@@ -196,18 +196,21 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_dense_i8_deep_48x4_b8
 def kernel_source_hash():
     """Hash of the source the loop-1 decode-attention kernel is built from: the
     attention file's helpers (up to the flash prefill section) and its dense decode
-    section (up to the sparse-gather section), and the KV-store address arithmetic of
-    the common header."""
+    section (up to the sparse-gather section), the KV-store address arithmetic of
+    the common header, and the new token's K/V writer of the kernel header."""
     import hashlib
     att = open(os.path.join(ROOT, "cross_loop_kv_amd", "csrc", "k_attn.hip")).read()
     com = open(os.path.join(ROOT, "cross_loop_kv_amd", "csrc", "lk_common.h")).read()
+    ker = open(os.path.join(ROOT, "cross_loop_kv_amd", "csrc", "lk_kernels.h")).read()
     mark = "// ---------------------------------------------------------------- "
     a = att.index("typedef _Float16 half8")
     a2 = att.index(mark + "flash prefill")
     d = att.index(mark + "dense decode (MFMA)")
     b = att.index(mark + "sparse decode: gather")
     c = com.index(mark + "KV store views")
-    return hashlib.sha256((att[a:a2] + att[d:b] + com[c:]).encode()).hexdigest()[:16]
+    k0 = ker.index("// Element e of one token's K")
+    k1 = ker.index("// ---- GEMM")
+    return hashlib.sha256((att[a:a2] + att[d:b] + com[c:] + ker[k0:k1]).encode()).hexdigest()[:16]
 
 
 def measured_traffic(workload):

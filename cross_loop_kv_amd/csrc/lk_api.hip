@@ -552,8 +552,11 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
     lk::KVWrite kw = kvw;
     kw.dpos = io.dpos;
     if (io.dpos && !io.pos && io.rows_per_seq == 1) kw.rope_cs = w.rope;  // decode: one position
-    // decode: the attention launch rotates q and writes the new token's K/V itself
-    const bool fuse_kv = kw.rope_cs && (ap.kind == ATTN_ROWS_DENSE || ap.kind == ATTN_ROWS_SPARSE);
+    // decode, loops >= 2: the sparse attention launch rotates q and writes the new
+    // token's K/V itself.  (The dense launches could too, and the step time would be
+    // the same: their writing workgroup gets longer by about what the separate launch
+    // costs, so they keep the separate launch and measure the attention alone.)
+    const bool fuse_kv = kw.rope_cs && ap.kind == ATTN_ROWS_SPARSE;
     if (!fuse_kv)
         LK_HIP(lk::rope_kv_write(w.qkv, io.M, io.rows_per_seq, pos, io.pos_offset, H, c.n_kv_heads, hd,
                                  h->inv_freq, w.q, kw, st));
