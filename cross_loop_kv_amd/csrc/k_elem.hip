@@ -371,6 +371,15 @@ hipError_t add_i32(int32_t* p, int32_t v, hipStream_t st) {
     hipLaunchKernelGGL(add_i32_kernel, dim3(1), dim3(64), 0, st, p, v);
     return hipGetLastError();
 }
+__global__ void iota_rows_kernel(int32_t* p, int n, long long total) {
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total; i += (long long)gridDim.x * blockDim.x)
+        p[i] = (int32_t)(i % n);
+}
+hipError_t iota_rows(int32_t* p, int rows, int n, hipStream_t st) {
+    const long long total = (long long)rows * n;
+    hipLaunchKernelGGL(iota_rows_kernel, dim3(grid_for(total)), dim3(kThreads), 0, st, p, n, total);
+    return hipGetLastError();
+}
 hipError_t fill_f32(float* p, float v, long long n, hipStream_t st) {
     hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n)), dim3(kThreads), 0, st, p, v, n);
     return hipGetLastError();

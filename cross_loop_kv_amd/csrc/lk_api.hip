@@ -42,6 +42,9 @@ int fail(int code, const std::string& msg) {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Loop k >= 2 recomputes every token when the refresh period divides k - 1.
+bool refresh_loop(const lk_lazy_cfg& z, int k) { return z.refresh_every > 0 && (k - 1) % z.refresh_every == 0; }
+
 int n_selected(double rho, int T) {
     if (T <= 0) return 0;
     long long n = (long long)std::ceil(rho * (double)T - 1e-9);
@@ -189,7 +192,10 @@ StoreLayout store_layout(const lk_handle* h, int B, int Tp, int Tmax) {
         s.base = take((size_t)c.n_shared * 2 * kvrows * hd * bb);
         s.base_sc = take(h->z.base_bits == 16 ? 0 : (size_t)c.n_shared * 2 * kvrows * (hd / 32) * 2);
         s.n_sel = n_selected(h->z.rho, Tp);
-        s.slots = (long long)s.n_sel + (Tmax - Tp);
+        int most = s.n_sel;  // the most prompt rows a loop stores
+        for (int k = 2; k <= c.n_loops; ++k)
+            if (refresh_loop(h->z, k)) most = Tp;
+        s.slots = (long long)most + (Tmax - Tp);
         s.res_row_b = h->z.res_bits == 16 ? hd * 2 : hd * h->z.res_bits / 8;
         const long long res_rows = (long long)(c.n_loops - 1) * c.n_shared * 2 * B * Hkv * s.slots;
         s.res = take((size_t)res_rows * s.res_row_b);
@@ -218,6 +224,9 @@ StoreLayout store_layout(const lk_handle* h, int B, int Tp, int Tmax) {
     return s;
 }
 
+// Prompt rows loop k >= 2 recomputes and stores: every one at a refresh loop, else n.
+int loop_rows(const lk_kv_store* s, int k) { return refresh_loop(s->h->z, k) ? s->Tp : s->lay.n_sel; }
+
 // Bytes of stored data at length t (closed form, no alignment padding).
 void store_bytes(const lk_kv_store* s, size_t* shared, size_t* total) {
     const lk_handle* h = s->h;
@@ -235,9 +244,10 @@ void store_bytes(const lk_kv_store* s, size_t* shared, size_t* total) {
     } else if (h->z.mode == LK_MODE_LAST_LOOP) {
         sh = (long long)c.n_shared * B * t * E * 2;
     } else if (t > 0) {
-        const long long stored = (long long)s->lay.n_sel + (t - s->Tp);
+        long long stored = 0;  // rows per sequence over loops 2..K: recomputed prompt rows + decoded
+        for (int k = 2; k <= s->K; ++k) stored += loop_rows(s, k) + (t - s->Tp);
         sh = (long long)c.n_shared * B * t * rowb(E, h->z.base_bits) +
-             (long long)(s->K - 1) * c.n_shared * B * stored * rowb(E, h->z.res_bits) +
+             (long long)c.n_shared * B * stored * rowb(E, h->z.res_bits) +
              (long long)(s->K - 1) * B * t * 4 + (long long)c.n_shared * B * c.n_kv_heads * s->lay.n_cols * 4;
     }
     *shared = (size_t)sh;
@@ -363,7 +373,12 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
     const lk_model_cfg& c = hd_->c;
     const long long M = (long long)B * T;
     const long long d = c.d_model;
-    const long long n = hd_->lazy() ? n_selected(hd_->z.rho, T) : T;
+    long long n = T;  // rows a loop >= 2 recomputes (the most over the loops)
+    if (hd_->lazy()) {
+        n = n_selected(hd_->z.rho, T);
+        for (int k = 2; k <= c.n_loops; ++k)
+            if (refresh_loop(hd_->z, k)) n = T;
+    }
     const long long Hhd = (long long)c.n_heads * c.head_dim;
     WS w{};
     size_t off = 0;
@@ -437,6 +452,7 @@ int check_cfg(const lk_model_cfg* c, const lk_lazy_cfg* z) {
             return fail(LK_ERR_INVALID_ARG, "res_bits must be 16, 8 or 4");
         if (z->group != 32) return fail(LK_ERR_UNSUPPORTED, "group must be 32");
         if (z->stale_keys != 0 && z->stale_keys != 1) return fail(LK_ERR_INVALID_ARG, "stale_keys must be 0 or 1");
+        if (z->refresh_every < 0) return fail(LK_ERR_INVALID_ARG, "refresh_every must be >= 0");
     }
     return LK_OK;
 }
@@ -724,7 +740,7 @@ bool same_cfg(const lk_model_cfg& a, const lk_model_cfg& b) {
 bool same_lazy(const lk_lazy_cfg& a, const lk_lazy_cfg& b) {
     return a.mode == b.mode && a.rho == b.rho && a.top_s == b.top_s && a.window == b.window &&
            a.base_bits == b.base_bits && a.res_bits == b.res_bits && a.group == b.group &&
-           a.stale_keys == b.stale_keys;
+           a.stale_keys == b.stale_keys && a.refresh_every == b.refresh_every;
 }
 
 }  // namespace
@@ -986,7 +1002,6 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
             }
         io.add = nullptr;
     } else {
-        const int n = s->lay.n_sel;
         LK_HIP(lk::copy_f32(w.h, w.h0, (long long)M * d, st));
         // loop 1: dense over every token; writes the base and picks the column sets
         for (int r = 0; r < R; ++r) {
@@ -1021,7 +1036,10 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
             full.base[1] = w.frv;
         }
         for (int k = 2; k <= K; ++k) {
-            if (s->f_tok) {
+            const int n = loop_rows(s, k);
+            if (refresh_loop(h->z, k)) {  // every token
+                LK_HIP(lk::iota_rows(w.sel, B, n, st));
+            } else if (s->f_tok) {
                 LK_HIP(hipMemcpyAsync(w.sel, s->f_tok + (long long)(k - 2) * B * n, (size_t)B * n * 4,
                                       hipMemcpyDeviceToDevice, st));
             } else {
@@ -1177,7 +1195,7 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
                 kw.ring_on = 1;
                 kw.kind = 2;
                 kw.loop = k;
-                kw.slot_base = (long long)s->lay.n_sel - s->Tp;  // slot = n_sel + (t - T)
+                kw.slot_base = (long long)loop_rows(s, k) - s->Tp;  // slot = n_k + (t - T)
                 kw.slot_map_k = slot_map(s, k);
             }
             apps.push_back({P + r, add, kw, ap, inj});

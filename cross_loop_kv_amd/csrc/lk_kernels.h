@@ -22,6 +22,7 @@ hipError_t copy_f32(const float* src, float* dst, long long n, hipStream_t st);
 hipError_t add_f32(float* x, const float* y, long long n, hipStream_t st);  // x += y
 hipError_t fill_i32(int32_t* p, int32_t v, long long n, hipStream_t st);
 hipError_t fill_f32(float* p, float v, long long n, hipStream_t st);
+hipError_t iota_rows(int32_t* p, int rows, int n, hipStream_t st);  // p[r * n + j] = j
 hipError_t add_i32(int32_t* p, int32_t v, hipStream_t st);  // *p += v (one thread)
 hipError_t delta_keys(const float* a, const float* b, int rows, int d, float* key, hipStream_t st);
 // xc[b*n + j] = (h[b*T + idx[b*n + j]] (+ add_src[same row])) + add; slot_map[b*Tmax + idx] = j

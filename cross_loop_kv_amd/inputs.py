@@ -67,6 +67,7 @@ class Lazy:
     res_bits: int = 16      # loop-k residual: 16, 8 or 4
     group: int = 32
     stale_keys: bool = False  # carried tokens keep their last measured change (else 0)
+    refresh_every: int = 0    # p > 0: loops k >= 2 with (k - 1) % p == 0 recompute every token
 
 
 @dataclass

@@ -89,6 +89,10 @@ typedef struct {
     double rho;
     int32_t top_s, window, base_bits, res_bits, group;
     int32_t stale_keys;
+    /* refresh_every = p > 0: every loop k >= 2 with (k - 1) % p == 0 recomputes every
+     * token instead of the top n (the token set is refreshed periodically; attention
+     * stays sparse and the residual rows of all tokens are stored); 0: never. */
+    int32_t refresh_every;
 } lk_lazy_cfg;
 
 /* Device pointers of one layer, all bfloat16 row-major:
@@ -128,7 +132,8 @@ void lk_destroy(lk_handle *h);
  *   rows (int4 packed two per byte low nibble first, int8, or bf16) plus float16
  *   scales; slot maps int32 [n_loops-1][batch][max_tokens] (-1 = not stored);
  *   column sets int32 [R][batch][Hkv][min(top_s, prompt_tokens)];
- *   slots = n_selected(prompt_tokens) + max_tokens - prompt_tokens.
+ *   slots = the most prompt tokens a loop stores (n_selected(prompt_tokens), or
+ *   prompt_tokens when some loop k <= n_loops refreshes) + max_tokens - prompt_tokens.
  * With dev_buf == NULL only *need_bytes is written (size query).  Otherwise
  * buf_bytes must be >= *need_bytes; the slot maps are cleared on `stream`
  * (void*, may be NULL) and *out receives a host handle. */
@@ -292,7 +297,7 @@ int lk_kv_store_view(const lk_kv_store *s, lk_store_view *v);
 /* Override the selections of the next prefill with caller data (device
  * pointers read during lk_looped_prefill; NULL restores natural selection):
  * tokens int32 [L-1][batch][n_selected] ascending per row, L the store's loop
- * count (lk_kv_store_set_loops);
+ * count (lk_kv_store_set_loops; refresh loops take every token and ignore theirs);
  * columns int32 [R][batch][Hkv][n_columns] ascending per row. */
 int lk_kv_store_force_selection(lk_kv_store *s, const int32_t *d_tokens, const int32_t *d_columns);
 

@@ -15,7 +15,8 @@ with one float16 scale per group of 32):
 * per_loop shared block: R * K * E * 2 per token;
 * last_loop shared block: R * E * 2 per token;
 * lazy shared block: base R * E * b_base per token, plus per loop k >= 2 one
-  residual row (R * E * b_res) per stored token, plus a 4-byte slot-map entry
+  residual row (R * E * b_res) per stored token (the n recomputed prompt tokens,
+  all prompt tokens at a refresh loop, and every decoded token), plus a 4-byte slot-map entry
   per (loop k >= 2, token), plus the column sets (4 bytes per column per
   (shared layer, KV head, sequence)).  b(16) = 2, b(8) = 1 + 2/32,
   b(4) = 1/2 + 2/32 bytes per element.
@@ -50,8 +51,12 @@ def kv_bytes(shape, lazy, batch: int, prompt: int, tokens: int) -> dict:
     elif lazy.mode == "lazy":
         g = lazy.group
         base = R * batch * tokens * row_bytes(E, lazy.base_bits, g)
-        slots = n_selected(lazy.rho, prompt) + (tokens - prompt)
-        res = (K - 1) * R * batch * slots * row_bytes(E, lazy.res_bits, g)
+        n = n_selected(lazy.rho, prompt)
+        p = int(getattr(lazy, "refresh_every", 0))
+        # rows stored per loop k >= 2: the recomputed prompt tokens (all of them at a
+        # refresh loop) and every decoded token
+        stored = sum((prompt if p > 0 and (k - 1) % p == 0 else n) + (tokens - prompt) for k in range(2, K + 1))
+        res = R * batch * stored * row_bytes(E, lazy.res_bits, g)
         slot_maps = (K - 1) * batch * tokens * 4
         cols = R * batch * shape.n_kv_heads * min(lazy.top_s, prompt) * 4
         shared = base + res + slot_maps + cols

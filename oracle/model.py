@@ -35,6 +35,9 @@ not given on any page):
   loop k-1, i.e. the change measured when they were last recomputed); the n
   largest keys are recomputed, the rest carry forward unchanged.  A recomputed query i attends over
   (S intersect [0, i]) union [max(0, i-w+1), i] of the loop-k reconstruction.
+* periodic refresh (``lazy.refresh_every`` = p > 0): a loop k >= 2 with (k - 1) % p
+  == 0 recomputes every token instead of the top n (the token set is refreshed; the
+  attention stays the sparse one and the residual rows are stored for every token).
 * input re-injection (aiboss88.com tutorial, step 3: a structure that passes the
   input representation into every loop): with ``shape.input_reinject`` the prelude
   output e is added to the state before every loop k >= 2 (loop 1 starts from e), as
@@ -187,6 +190,8 @@ class LoopedOracle:
                 raise ValueError("unsupported bit width")
             if shape.head_dim % lazy.group:
                 raise ValueError("head_dim must be a multiple of the group")
+            if int(getattr(lazy, "refresh_every", 0)) < 0:
+                raise ValueError("refresh_every must be >= 0")
         self.depth = 0           # layer applications in the last call
         self.forced_codes_from = None  # another LoopedOracle whose quantized codes are reused
         self.forced_tokens = None    # {(k, b): kept indices} overrides selection
@@ -319,6 +324,16 @@ class LoopedOracle:
             f = gelu_erf(b @ W["w_up"].T)
         return (x + self._rb(f.astype(F32)) @ W["w_down"].T).astype(F32)
 
+    def _refresh(self, k: int) -> bool:
+        """Loop k >= 2 recomputes every token (the refresh period divides k - 1)."""
+        p = int(getattr(self.lz, "refresh_every", 0))
+        return p > 0 and (k - 1) % p == 0
+
+    def _loop_rows(self, T: int) -> dict:
+        """Tokens each loop k >= 2 of the model recomputes: all at refresh loops, else n."""
+        n = n_selected(self.lz.rho, T)
+        return {k: (T if self._refresh(k) else n) for k in range(2, self.s.n_loops + 1)}
+
     # -------------------------------------------------------------- prefill
     def prefill(self, ids: np.ndarray) -> np.ndarray:
         ids = np.asarray(ids)
@@ -328,7 +343,8 @@ class LoopedOracle:
         self.T, self.t = T, T
         if self.lz.mode == "lazy":
             self.n_sel = n_selected(self.lz.rho, T)
-            self._alloc_residuals(self.n_sel + (self.Tmax - T))
+            self.n_k = self._loop_rows(T)
+            self._alloc_residuals(max(self.n_k.values(), default=0) + (self.Tmax - T))
             self.S = [[None] * B for _ in range(self.s.n_shared)]
         out = np.empty((B, T, self.s.d_model), F32)
         self.depth = 0
@@ -413,9 +429,9 @@ class LoopedOracle:
             self.depth += 1
             x = self._out_ffn(P + r, x, o)
         h_prev2, h_prev = h0, x
-        n = self.n_sel
         stale = bool(getattr(lz, "stale_keys", False))
         for k in range(2, K + 1):
+            n = self.n_k[k]
             key = np.sum((h_prev - h_prev2) ** 2, axis=-1, dtype=F32)
             if stale and k >= 3:
                 # a token carried through loop k-1 keeps the change measured when it
@@ -424,7 +440,9 @@ class LoopedOracle:
                 carried[self.sel[(k - 1, b)]] = False
                 key = np.where(carried, self.keys[(k - 1, b)], key).astype(F32)
             self.keys[(k, b)] = key
-            if self.forced_tokens is not None:
+            if self._refresh(k):
+                I = np.arange(T)
+            elif self.forced_tokens is not None:
                 I = self.forced_tokens[(k, b)]
             else:
                 I = top_n_ascending(key, n)
@@ -459,7 +477,8 @@ class LoopedOracle:
         base[r][kv]: (int8 codes [B, Hkv, Tmax, hd], float16 scales [B, Hkv, Tmax,
         hd/group]) for 8-bit bases, else float32 rows [B, Hkv, Tmax, hd];
         res[(k, r, kv)] for k = 2..shape.n_loops: the same forms over
-        n_selected(rho, T) + Tmax - T slots (int8 codes hold the int4 values too);
+        the most tokens a loop recomputes (n_selected(rho, T), or T with refresh loops)
+        + Tmax - T slots (int8 codes hold the int4 values too);
         slot [shape.n_loops, B, Tmax] int32, row k-1 the slot of each position at
         loop k (-1: not stored); S[r][b][g] ascending int32 column arrays;
         dense_kv[i] = (K rows, V rows) float32 [B, Hkv, Tmax, hd] of prelude/coda
@@ -473,14 +492,16 @@ class LoopedOracle:
         if n_dense and (dense_kv is None or len(dense_kv) != n_dense):
             raise ValueError("prelude/coda rows are needed")
         n = n_selected(lz.rho, T)
+        n_k = self._loop_rows(T)
+        n_max = max(n_k.values(), default=0)
         if slot.shape != (s.n_loops, self.B, self.Tmax):
             raise ValueError("slot map shape")
         for (k, r, kv), x in res.items():
             a = x if lz.res_bits == 16 else x[0]
-            if a.shape[2] != n + self.Tmax - T:
+            if a.shape[2] != n_max + self.Tmax - T:
                 raise ValueError("residual slot count")
-        self.T, self.t, self.n_sel = T, T, n
-        self.n_slots = n + self.Tmax - T
+        self.T, self.t, self.n_sel, self.n_k = T, T, n, n_k
+        self.n_slots = n_max + self.Tmax - T
         self.base, self.res, self.slot, self.S = base, res, slot, S
         for i in range(n_dense):
             self.dense_k[i], self.dense_v[i] = dense_kv[i]
@@ -522,10 +543,10 @@ class LoopedOracle:
                     h = self._shared_dense(P + r, h, pos, kc, vc, b)
         else:
             allc = np.arange(t + 1)
-            slot = self.n_sel + (t - self.T)
             for k in range(1, K + 1):
                 h = self._loop_input(h, e, k)
                 if k >= 2:
+                    slot = self.n_k[k] + (t - self.T)
                     self.slot[k - 1, b, t] = slot
                 for r in range(R):
                     q, kk, vv = self._qkv(P + r, h, pos)

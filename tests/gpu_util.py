@@ -25,7 +25,8 @@ def max_abs_rel(a, b):
 def oracle_selection(m, shape, batch):
     """Oracle's kept tokens [K-1, B, n] and column sets [R, B, Hkv, n_cols] as int32 arrays."""
     K, R, Hkv = m.K, shape.n_shared, shape.n_kv_heads
-    tok = np.stack([np.stack([m.sel[(k, b)] for b in range(batch)]) for k in range(2, K + 1)]) \
+    # refresh loops keep every token and ignore their rows here: the first n stand in
+    tok = np.stack([np.stack([m.sel[(k, b)][:m.n_sel] for b in range(batch)]) for k in range(2, K + 1)]) \
         if K >= 2 else np.zeros((0, batch, 1), np.int32)
     cols = np.stack([np.stack([np.stack(m.S[r][b]) for b in range(batch)]) for r in range(R)])
     return tok.astype(np.int32), cols.astype(np.int32)

@@ -166,6 +166,43 @@ def test_stale_keys_forced_selection_matches_oracle():
     check(r, "stale keys")
 
 
+@pytest.mark.parametrize("period,stale", [(2, False), (3, True)])
+def test_refresh_loops_match_oracle(period, stale):
+    """Periodic refresh over 4 loops (period 2: loop 3 recomputes every token; period 3:
+    loop 4 does, with stale keys): prefill and decode against the oracle with its
+    selections forced, and the store's byte count against the closed form."""
+    s = _small(n_loops=4)
+    lz = I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4, stale_keys=stale,
+                refresh_every=period)
+    T, steps, Bsz = 150, 3, 2
+    r = run_pair(s, lz, batch=Bsz, prompt=T, steps=steps, seed=7)
+    m = r["oracle"]
+    assert all(len(m.sel[(k, b)]) == T for b in range(Bsz) for k in range(2, 5) if (k - 1) % period == 0)
+    check(r, f"refresh every {period}")
+    exp = accounting.kv_bytes(s, lz, Bsz, T, T + steps)
+    assert r["store"].bytes_used() == (exp["shared"], exp["total"])
+
+
+def test_refresh_every_loop_is_rho_one():
+    """Refresh at every loop computes what rho = 1 computes: same selections (every
+    token, ascending), same store layout; the outputs agree bit for bit."""
+    s = _small(n_loops=3)
+    T, steps, Bsz = 120, 3, 2
+    W = I.gen_weights(s, seed=19)
+    ids = torch.from_numpy(I.gen_prompt_ids(s, Bsz, T))
+    dec = torch.from_numpy(I.gen_decode_ids(s, Bsz, steps)).cuda()
+    outs = []
+    for kw in (dict(rho=0.25, refresh_every=1), dict(rho=1.0)):
+        lz = I.Lazy(mode="lazy", top_s=24, window=16, base_bits=8, res_bits=8, **kw)
+        model = B.LoopedModel(s, lz, W)
+        st = model.store(Bsz, T, T + steps)
+        o = [model.prefill(st, ids).clone()] + [model.decode(st, dec[i]).clone() for i in range(steps)]
+        torch.cuda.synchronize()
+        outs.append(o)
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 def test_lazy_rho1_all_columns_matches_gpu_dense():
     """rho = 1, every column, 16-bit rows: the lazy path computes the dense function."""
     s = _small()

@@ -138,7 +138,11 @@ def brute_lazy(shape, lz, W, ids, dec):
                 if i not in sel[kk - 1]:
                     key[i] = last_change[i]
         last_change = key.copy()
-        Ik = sorted(sorted(range(T), key=lambda i: (-key[i], i))[:n])
+        p = getattr(lz, "refresh_every", 0)
+        if p > 0 and (kk - 1) % p == 0:   # a refresh loop recomputes every token
+            Ik = list(range(T))
+        else:
+            Ik = sorted(sorted(range(T), key=lambda i: (-key[i], i))[:n])
         sel[kk] = Ik
         xs = hist[-1][Ik] + W["loop_emb"][kk - 1]
         for r in range(R):
@@ -149,7 +153,7 @@ def brute_lazy(shape, lz, W, ids, dec):
             kr[Ik] = _store(k, kp[Ik], lz.res_bits)
             vr[Ik] = _store(v, vp[Ik], lz.res_bits)
             recon[(kk, r)] = (kr, vr)
-            mask = np.zeros((Hkv, n, T), bool)
+            mask = np.zeros((Hkv, len(Ik), T), bool)
             for g in range(Hkv):
                 for a, i in enumerate(Ik):
                     for j in range(T):
@@ -308,3 +312,46 @@ def test_stale_keys_reselect_tokens_outside_the_previous_set():
     o1 = LoopedOracle(s, I.Lazy(**base), W2, B, T).prefill(ids)
     o2 = LoopedOracle(s, I.Lazy(**base, stale_keys=True), W2, B, T).prefill(ids)
     assert np.array_equal(o1, o2)
+
+
+def test_refresh_loops_recompute_every_token():
+    """Periodic refresh: with period 1 every loop k >= 2 recomputes every token, which is
+    the rho = 1 computation bit for bit; with period 2 loop 3 is a refresh loop (all
+    tokens, brute-force reference agrees) while loops 2 and 4 keep the top n; the store
+    holds a residual row for every stored (loop, token) as the closed form counts."""
+    from oracle import accounting
+    s = I.workload("tiny_1p2x2c1_t32").shape
+    s.n_loops = 4
+    W = I.gen_weights(s, seed=41)
+    T, B, steps = 28, 2, 2
+    ids = I.gen_prompt_ids(s, B, T, seed=42)
+    dec = I.gen_decode_ids(s, B, steps, seed=43)
+    base = dict(mode="lazy", top_s=6, window=3, base_bits=8, res_bits=8)
+
+    def run(**kw):
+        m = LoopedOracle(s, I.Lazy(**base, **kw), W, B, T + steps)
+        out = m.prefill(ids)
+        return m, out, np.stack([m.decode(d) for d in dec], 1)
+
+    _, o1, d1 = run(rho=0.3, refresh_every=1)
+    _, o2, d2 = run(rho=1.0)
+    assert np.array_equal(o1, o2) and np.array_equal(d1, d2)
+    lz = I.Lazy(**base, rho=0.3, refresh_every=2)
+    m, out, douts = run(rho=0.3, refresh_every=2)
+    n = n_selected(0.3, T)
+    for b in range(B):
+        assert len(m.sel[(2, b)]) == n and len(m.sel[(4, b)]) == n
+        assert np.array_equal(m.sel[(3, b)], np.arange(T))
+        ref, dref, sel, _ = brute_lazy(s, lz, W, ids[b], dec[:, b])
+        for k_, Ik in sel.items():
+            assert list(m.sel[(k_, b)]) == Ik
+        assert np.max(np.abs(out[b] - ref)) / np.max(np.abs(ref)) < 1e-4
+        assert np.max(np.abs(douts[b] - dref)) / np.max(np.abs(dref)) < 1e-4
+    stored = int(sum((m.slot[k - 1] >= 0).sum() for k in range(2, s.n_loops + 1)))
+    assert stored == B * ((T + steps) + 2 * (n + steps))
+    E = 2 * s.n_kv_heads * s.head_dim
+    got = accounting.kv_bytes(s, lz, B, T, T + steps)["shared"]
+    rb = accounting.row_bytes
+    exp = (s.n_shared * B * (T + steps) * rb(E, 8) + s.n_shared * stored * rb(E, 8)
+           + (s.n_loops - 1) * B * (T + steps) * 4 + s.n_shared * B * s.n_kv_heads * min(6, T) * 4)
+    assert got == exp
