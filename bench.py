@@ -291,7 +291,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the path runs on a single MI355X and has no multi-GPU "
-              "mode (sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+              "mode; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
