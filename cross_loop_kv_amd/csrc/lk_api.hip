@@ -539,7 +539,10 @@ int timed(lk_handle* h, int cls, hipStream_t st, F fn) {
 int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, const AttnPlan& ap,
               const WS& w, hipStream_t st) {
     const lk_model_cfg& c = h->c;
-    const int gcls = ap.kind == ATTN_PREFILL_DENSE || io.rows_per_seq > 1 ? TC_GEMM_PREFILL : TC_GEMM_DECODE;
+    // a decode step carries the device position; a prefill loop may also hand over one
+    // row per sequence (one kept token), so the row count does not tell them apart
+    const bool decode = io.dpos != nullptr;
+    const int gcls = decode ? TC_GEMM_DECODE : TC_GEMM_PREFILL;
     const lk_layer_weights& W = h->L[li];
     const int d = c.d_model, H = c.n_heads, hd = c.head_dim, Hhd = H * hd;
     // decode-sized row counts fold the RMSNorm into the skinny GEMMs
@@ -567,7 +570,7 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
     const int32_t* pos = io.pos;
     lk::KVWrite kw = kvw;
     kw.dpos = io.dpos;
-    if (io.dpos && !io.pos && io.rows_per_seq == 1) kw.rope_cs = w.rope;  // decode: one position
+    if (decode && !io.pos && io.rows_per_seq == 1) kw.rope_cs = w.rope;  // decode: one position
     // decode, loops >= 2: the sparse attention launch rotates q and writes the new
     // token's K/V itself.  (The dense launches could too, and the step time would be
     // the same: their writing workgroup gets longer by about what the separate launch
@@ -619,7 +622,7 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
         };
         a.part = w.part;
         a.out = w.att;
-        if (ap.kind == ATTN_ROWS_SPARSE && io.rows_per_seq == 1) {
+        if (ap.kind == ATTN_ROWS_SPARSE && decode) {
             // decode, loops >= 2: the stable columns come from the float16 cache filled at
             // the end of prefill, the window from the float16 ring that prefill filled and
             // each decode step extends (rope_kv_write).  One launch runs over both
@@ -635,7 +638,7 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
                 return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
             LK_TRY(timed(h, TC_ATTN_DECODE_SPARSE, st, [=] { return lk::attn_rows_main(d, st); }));
             LK_HIP(lk::attn_rows_combine(d, st, io.fold));
-        } else if (ap.kind == ATTN_ROWS_SPARSE && io.rows_per_seq > 1 && ap.full.base[0]) {
+        } else if (ap.kind == ATTN_ROWS_SPARSE && !decode && ap.full.base[0]) {
             // token-sparse prefill rows: the loop-k reconstruction is final for the stable
             // columns (cached for decode too) and for every prompt position (workspace)
             lk::RowsAttn gr{};
@@ -659,7 +662,7 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
             a.n_splits = (int)((ncol_max + chunk - 1) / chunk);
             if ((long long)a.B * a.n_rows * H * a.n_splits * (hd + 2) > w.part_floats)
                 return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
-            const int acls = io.rows_per_seq > 1 ? TC_ATTN_PREFILL_SPARSE
+            const int acls = !decode ? TC_ATTN_PREFILL_SPARSE
                              : (ap.kind == ATTN_ROWS_SPARSE ? TC_ATTN_DECODE_SPARSE : TC_ATTN_DECODE_DENSE);
             LK_TRY(timed(h, acls, st, [=] { return lk::attn_rows_main(a, st); }));
             LK_HIP(lk::attn_rows_combine(a, st, io.fold));

@@ -223,6 +223,27 @@ def test_lazy_rho1_all_columns_matches_gpu_dense():
         assert max_abs_rel(a, b) < 1e-2
 
 
+DEGENERATE = [
+    ("lazy_T1", dict(), I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4), 1),
+    ("lazy_T5_window_past_prompt", dict(), I.Lazy(mode="lazy", rho=0.3, top_s=2, window=16, base_bits=8, res_bits=4), 5),
+    ("lazy_hd128_T3", dict(n_heads=4, n_kv_heads=4, head_dim=128, d_model=512),
+     I.Lazy(mode="lazy", rho=0.5, top_s=40, window=8, base_bits=16, res_bits=8), 3),
+    ("per_loop_T1", dict(), I.Lazy(mode="per_loop"), 1),
+    ("last_loop_T2", dict(n_loops=4), I.Lazy(mode="last_loop"), 2),
+]
+
+
+@pytest.mark.parametrize("name,kw,lz,T", DEGENERATE, ids=[c[0] for c in DEGENERATE])
+def test_degenerate_prompts_match_oracle(name, kw, lz, T):
+    """Prompts of 1-5 tokens: one kept token per loop, a window longer than the
+    prompt, a column set of all prompt columns, then decode steps that grow the
+    context past the window's start."""
+    s = _small(**kw)
+    log(f"degenerate {name}")
+    r = run_pair(s, lz, batch=2, prompt=T, steps=4, seed=33)
+    check(r, name)
+
+
 def test_decode_state_and_capacity_errors():
     wl = tiny()
     W = I.gen_weights(wl.shape)
