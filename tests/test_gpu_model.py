@@ -87,16 +87,17 @@ def test_small_shapes_ragged_prompt(name, kw, lz):
     check(r, name)
 
 
-@pytest.mark.parametrize("mode", ["lazy", "per_loop"])
-def test_decode_batch_above_eight_rows(mode):
+@pytest.mark.parametrize("mode,Bsz", [("lazy", 10), ("per_loop", 10), ("lazy", 20), ("per_loop", 20)])
+def test_decode_batch_above_eight_rows(mode, Bsz):
     """More than 8 sequences: decode takes the 16-row projection kernels (RMSNorm fused
-    from the float32 residual rows) instead of the folded packed-weight ones."""
+    from the float32 residual rows) instead of the folded packed-weight ones, and above
+    16 the separate RMSNorm and the tiled projections."""
     s = _small()
     lz = (I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4)
           if mode == "lazy" else I.Lazy(mode="per_loop"))
-    log(f"batch 10 decode, {mode}")
-    r = run_pair(s, lz, batch=10, prompt=100, steps=2, seed=12)
-    check(r, f"batch 10 {mode}")
+    log(f"batch {Bsz} decode, {mode}")
+    r = run_pair(s, lz, batch=Bsz, prompt=100, steps=2, seed=12)
+    check(r, f"batch {Bsz} {mode}")
 
 
 def test_int4_natural_codes_drift_is_bounded():
