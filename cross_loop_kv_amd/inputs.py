@@ -68,6 +68,7 @@ class Lazy:
     group: int = 32
     stale_keys: bool = False  # carried tokens keep their last measured change (else 0)
     refresh_every: int = 0    # p > 0: loops k >= 2 with (k - 1) % p == 0 recompute every token
+    diff_attn: bool = False   # loops k >= 2: sparse term plus the row's loop-1 (dense - sparse)
 
 
 @dataclass

@@ -35,6 +35,16 @@ not given on any page):
   loop k-1, i.e. the change measured when they were last recomputed); the n
   largest keys are recomputed, the rest carry forward unchanged.  A recomputed query i attends over
   (S intersect [0, i]) union [max(0, i-w+1), i] of the loop-k reconstruction.
+* difference-corrected sparse attention (``lazy.diff_attn``; the FlashLoop abstract,
+  arxivdaily.com: the attention-output *differences* between loops come from a sparse,
+  stable set of key columns): a recomputed row's attention output at loop k >= 2 is its
+  previous output plus the change of its sparse term, o_k = o_{k'} + (a_k - a_{k'}),
+  where a_j is the softmax over the row's sparse column set of loop j's query and
+  reconstruction and k' the loop that last computed the row.  Since loop 1 computes
+  every row densely, o_k = a_k + (o_1 - a_1) exactly: the oracle keeps D = o_1 - a_1
+  per (shared layer, token) from loop 1 and adds it to the sparse output.  A decode
+  token's D comes from its own loop 1 (dense output minus the sparse one over the
+  loop-1 reconstruction).  Off, o_k = a_k.
 * periodic refresh (``lazy.refresh_every`` = p > 0): a loop k >= 2 with (k - 1) % p
   == 0 recomputes every token instead of the top n (the token set is refreshed; the
   attention stays the sparse one and the residual rows are stored for every token).
@@ -192,6 +202,8 @@ class LoopedOracle:
                 raise ValueError("head_dim must be a multiple of the group")
             if int(getattr(lazy, "refresh_every", 0)) < 0:
                 raise ValueError("refresh_every must be >= 0")
+        self.diff = lazy.mode == "lazy" and bool(getattr(lazy, "diff_attn", False))
+        self.D = {}                  # diff_attn: (r, b) -> o_1 - a_1 [T, H, hd] of the prompt
         self.depth = 0           # layer applications in the last call
         self.forced_codes_from = None  # another LoopedOracle whose quantized codes are reused
         self.forced_tokens = None    # {(k, b): kept indices} overrides selection
@@ -426,6 +438,9 @@ class LoopedOracle:
                                 else top_n_ascending(mass[g], lz.top_s)
                                 for g in range(s.n_kv_heads)]
             self.mass[(r, b)] = mass
+            if self.diff and K >= 2:
+                # the loop-1 sparse term of every token over the loop-1 reconstruction
+                self.D[(r, b)] = (o - self._attend_sparse(q, kr, vr, pos, r, b)).astype(F32)
             self.depth += 1
             x = self._out_ffn(P + r, x, o)
         h_prev2, h_prev = h0, x
@@ -458,6 +473,8 @@ class LoopedOracle:
                 vr = self.recon(k, r, b, 1, allc)
                 # each KV head has its own S: attend head-group by head-group.
                 o = self._attend_sparse(q, kr, vr, I, r, b)
+                if self.diff:
+                    o = (o + self.D[(r, b)][I]).astype(F32)
                 self.depth += 1
                 xs = self._out_ffn(P + r, xs, o)
             h_new = h_prev.copy()
@@ -543,6 +560,7 @@ class LoopedOracle:
                     h = self._shared_dense(P + r, h, pos, kc, vc, b)
         else:
             allc = np.arange(t + 1)
+            D = {}           # diff_attn: shared layer -> this token's o_1 - a_1 [1, H, hd]
             for k in range(1, K + 1):
                 h = self._loop_input(h, e, k)
                 if k >= 2:
@@ -556,11 +574,15 @@ class LoopedOracle:
                         kr = self.recon(1, r, b, 0, allc)
                         vr = self.recon(1, r, b, 1, allc)
                         o = attend(q, kr, vr, lambda i, g: allc)
+                        if self.diff and K >= 2:
+                            D[r] = (o - self._attend_sparse(q, kr, vr, pos, r, b)).astype(F32)
                     else:
                         self._res_write(k, r, b, pos, np.array([slot]), kt, vt)
                         kr = self.recon(k, r, b, 0, allc)
                         vr = self.recon(k, r, b, 1, allc)
                         o = self._attend_sparse(q, kr, vr, pos, r, b)
+                        if self.diff:
+                            o = (o + D[r]).astype(F32)
                     self.depth += 1
                     h = self._out_ffn(P + r, h, o)
         # coda

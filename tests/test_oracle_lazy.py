@@ -103,6 +103,17 @@ def brute_lazy(shape, lz, W, ids, dec):
     x = h0[:T] + W["loop_emb"][0]
     recon = {}
     S = {}
+    diff = bool(getattr(lz, "diff_attn", False)) and K >= 2
+    last = {}
+
+    def sparse_mask(r, rows, ncol):
+        m_ = np.zeros((Hkv, len(rows), ncol), bool)
+        for g in range(Hkv):
+            for a, i in enumerate(rows):
+                for j in range(ncol):
+                    m_[g, a, j] = j <= i and (j in S[r][g] or j > i - lz.window)
+        return m_
+
     for r in range(R):
         li = P + r
         q, k, v = proj(li, x, np.arange(T))
@@ -126,6 +137,8 @@ def brute_lazy(shape, lz, W, ids, dec):
             else:
                 S[r].append(sorted(sorted(range(T), key=lambda j: (-tot[j], j))[: lz.top_s]))
         recon[(1, r)] = (kb, vb)
+        if diff:   # each token's last (output, sparse term) pair at this layer
+            last[r] = (o.copy(), _masked_attn(q, kb, vb, sparse_mask(r, range(T), T))[0])
         x = out_ffn(li, x, o)
     hist = [h0[:T], x]
     n = n_selected(lz.rho, T)
@@ -153,12 +166,12 @@ def brute_lazy(shape, lz, W, ids, dec):
             kr[Ik] = _store(k, kp[Ik], lz.res_bits)
             vr[Ik] = _store(v, vp[Ik], lz.res_bits)
             recon[(kk, r)] = (kr, vr)
-            mask = np.zeros((Hkv, len(Ik), T), bool)
-            for g in range(Hkv):
-                for a, i in enumerate(Ik):
-                    for j in range(T):
-                        mask[g, a, j] = j <= i and (j in S[r][g] or j > i - lz.window)
-            o, _ = _masked_attn(q, kr, vr, mask)
+            o, _ = _masked_attn(q, kr, vr, sparse_mask(r, Ik, T))
+            if diff:   # o_k = o_{k'} + (a_k - a_{k'}), k' the row's last computing loop
+                po, pa = last[r]
+                a_k = o
+                o = (po[Ik] + (a_k - pa[Ik])).astype(F32)
+                po[Ik], pa[Ik] = o, a_k
             xs = out_ffn(li, xs, o)
         hn = hist[-1].copy()
         hn[Ik] = xs
@@ -172,6 +185,7 @@ def brute_lazy(shape, lz, W, ids, dec):
     hdec = []
     for t in range(T, N):
         x = h0[t:t + 1]
+        dlast = {}
         for kk in range(1, K + 1):
             x = x + W["loop_emb"][kk - 1]
             for r in range(R):
@@ -190,6 +204,12 @@ def brute_lazy(shape, lz, W, ids, dec):
                     for j in range(t + 1):
                         mask[g, 0, j] = kk == 1 or (j in S[r][g] or j > t - lz.window)
                 o, _ = _masked_attn(q, kc, vc, mask)
+                if diff:
+                    a_k = _masked_attn(q, kc, vc, sparse_mask(r, [t], N))[0]
+                    if kk >= 2:
+                        po, pa = dlast[r]
+                        o = (po + (a_k - pa)).astype(F32)
+                    dlast[r] = (o, a_k)
                 x = out_ffn(li, x, o)
         hdec.append(x[0])
     # coda over [prompt rows after the loops ; decode rows] causally
@@ -208,6 +228,11 @@ CASES = [
      I.Lazy(mode="lazy", rho=0.25, top_s=5, window=2, base_bits=16, res_bits=16)),
     ("stale_keys_k4", dict(n_heads=4, n_kv_heads=2, ffn_act="swiglu", n_loops=4),
      I.Lazy(mode="lazy", rho=0.3, top_s=6, window=3, base_bits=8, res_bits=8, stale_keys=True)),
+    ("diff_attn_k3", dict(n_heads=4, n_kv_heads=2, ffn_act="swiglu", n_loops=3),
+     I.Lazy(mode="lazy", rho=0.3, top_s=6, window=3, base_bits=8, res_bits=4, diff_attn=True)),
+    ("diff_attn_stale_refresh_k4", dict(n_heads=4, n_kv_heads=2, ffn_act="swiglu", n_loops=4),
+     I.Lazy(mode="lazy", rho=0.3, top_s=5, window=2, base_bits=16, res_bits=8, diff_attn=True,
+            stale_keys=True, refresh_every=2)),
 ]
 
 
@@ -355,3 +380,35 @@ def test_refresh_loops_recompute_every_token():
     exp = (s.n_shared * B * (T + steps) * rb(E, 8) + s.n_shared * stored * rb(E, 8)
            + (s.n_loops - 1) * B * (T + steps) * 4 + s.n_shared * B * s.n_kv_heads * min(6, T) * 4)
     assert got == exp
+
+
+def test_diff_attn_reduces_to_plain_sparse_when_the_column_set_is_every_column():
+    """Difference-corrected attention adds o_1 - a_1 to the sparse output.  When the
+    sparse set of every row is its whole causal range (top_s >= T), a_1 = o_1 computed
+    over the same columns, so the correction is exactly zero and the outputs equal the
+    plain lazy ones bit for bit; with top_s < T the correction is not zero and changes
+    the prompt and decode outputs (so the switch is not a no-op)."""
+    s = I.workload("tiny_1p2x2c1_t32").shape
+    s.n_loops = 3
+    W = I.gen_weights(s, seed=51)
+    T, B, steps = 24, 2, 2
+    ids = I.gen_prompt_ids(s, B, T, seed=52)
+    dec = I.gen_decode_ids(s, B, steps, seed=53)
+
+    def run(**kw):
+        m = LoopedOracle(s, I.Lazy(mode="lazy", rho=0.4, window=3, base_bits=8, res_bits=4, **kw), W, B,
+                         T + steps)
+        out = m.prefill(ids)
+        return m, out, np.stack([m.decode(d) for d in dec], 1)
+
+    m1, o1, d1 = run(top_s=T + steps)
+    m2, o2, d2 = run(top_s=T + steps, diff_attn=True)
+    assert np.array_equal(o1, o2) and np.array_equal(d1, d2)
+    assert all(not np.any(D) for D in m2.D.values())
+    _, o3, d3 = run(top_s=4)
+    m4, o4, d4 = run(top_s=4, diff_attn=True)
+    assert max(float(np.max(np.abs(D))) for D in m4.D.values()) > 0
+    assert np.max(np.abs(o3 - o4)) > 1e-4 and np.max(np.abs(d3 - d4)) > 1e-4
+    # rows whose sparse set is their whole causal range (i < window) carry D = 0
+    for (r, b), D in m4.D.items():
+        assert not np.any(D[: 3])
