@@ -1184,16 +1184,48 @@ __global__ __launch_bounds__(G > 4 ? 64 * G : 256) void attn_rows_pf_kernel(Rows
     if (jr < n && l_i > 0.f) {
         const float inv = 1.f / l_i;
         u16* orow = a.out + ((long long)b * n + jr) * ldq + h * HD;
+        if (a.diff_mode == DIFF_NONE) {
 #pragma unroll
-        for (int c = 0; c < HD / 32; ++c)
+            for (int c = 0; c < HD / 32; ++c)
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const int e0 = c * 32 + 8 * i4 + 4 * kg;
-                uint2 v;
-                v.x = pack_bf2(oacc[c][i4 * 4 + 0] * inv, oacc[c][i4 * 4 + 1] * inv);
-                v.y = pack_bf2(oacc[c][i4 * 4 + 2] * inv, oacc[c][i4 * 4 + 3] * inv);
-                *(uint2*)(orow + e0) = v;
-            }
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int e0 = c * 32 + 8 * i4 + 4 * kg;
+                    uint2 v;
+                    v.x = pack_bf2(oacc[c][i4 * 4 + 0] * inv, oacc[c][i4 * 4 + 1] * inv);
+                    v.y = pack_bf2(oacc[c][i4 * 4 + 2] * inv, oacc[c][i4 * 4 + 3] * inv);
+                    *(uint2*)(orow + e0) = v;
+                }
+        } else {
+            // difference correction: the row's float16 D at its position P
+            u16* drow = a.d16 + ((long long)b * a.d_rows + P) * ldq + h * HD;
+            const bool add = a.diff_mode == DIFF_ADD16;
+#pragma unroll
+            for (int c = 0; c < HD / 32; ++c)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int e0 = c * 32 + 8 * i4 + 4 * kg;
+                    const uint2 dv = *(const uint2*)(drow + e0);
+                    const uint2 ov = add ? dv : *(const uint2*)(orow + e0);
+                    float x[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t wd = j < 2 ? dv.x : dv.y, wo = j < 2 ? ov.x : ov.y;
+                        const float o = oacc[c][i4 * 4 + j] * inv;
+                        x[j] = add ? o + h2f((u16)(wd >> (16 * (j & 1))))
+                                   : __uint_as_float((j & 1) ? (wo & 0xFFFF0000u) : (wo << 16)) - o;
+                    }
+                    uint2 v;
+                    if (add) {
+                        v.x = pack_bf2(x[0], x[1]);
+                        v.y = pack_bf2(x[2], x[3]);
+                        *(uint2*)(orow + e0) = v;
+                    } else {
+                        v.x = (uint32_t)f2h_bits(x[0]) | ((uint32_t)f2h_bits(x[1]) << 16);
+                        v.y = (uint32_t)f2h_bits(x[2]) | ((uint32_t)f2h_bits(x[3]) << 16);
+                        *(uint2*)(drow + e0) = v;
+                    }
+                }
+        }
     }
 }
 
@@ -1296,7 +1328,7 @@ __global__ __launch_bounds__(64) void attn_rows_kernel(RowsAttn a) {
     const int b = bg / Hkv, g = bg % Hkv;
     const int lane = threadIdx.x;
     const long long qrow = (long long)b * a.n_rows + row;
-    const int pos = a.qpos ? a.qpos[qrow] : a.pos;
+    const int pos = a.qpos ? a.qpos[qrow] : (a.dpos ? *a.dpos : a.pos);
     const int nres = a.kv.lazy ? a.k_loop - 1 : 0;
     __shared__ float qs[G][HD];
     __shared__ float ps[G][64];
@@ -1412,9 +1444,17 @@ constexpr int kCombineMaxSplits = 256, kCombineMaxG = 8;
 // m_s and l_s per thread and split) is issued before the block reductions, so a launch
 // with up to 32 splits waits on one memory round trip.
 constexpr int kCombinePre = 32;
+// The difference correction of the merged rows (RowsAttn's diff_* fields).
+struct DiffOut {
+    int mode;
+    float* d32;
+    u16* d16;
+    int d_rows, n_rows;
+    const int32_t* qpos;
+};
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part, int n_splits, int G,
                                                            int HD, int H, int Hkv, u16* __restrict__ out,
-                                                           bool packed) {
+                                                           bool packed, DiffOut df) {
     __shared__ float wts[kCombineMaxSplits];
     __shared__ float red[2];
     const long long qrow = blockIdx.x;
@@ -1467,7 +1507,25 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
         }
         const float o = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * inv;
         const int k = head * HD + e;
-        out[packed ? pk_index((int)qrow, k, H * HD) : qrow * H * HD + k] = f2bf(o);
+        const long long oi = packed ? pk_index((int)qrow, k, H * HD) : qrow * H * HD + k;
+        const long long di = qrow * H * HD + k;
+        switch (df.mode) {
+            case DIFF_ADD32: out[oi] = f2bf(o + df.d32[di]); break;
+            case DIFF_SET32:
+                df.d32[di] = o;
+                out[oi] = f2bf(o);
+                break;
+            case DIFF_SUB32: df.d32[di] -= o; break;
+            case DIFF_ADD16:
+            case DIFF_OUT16: {
+                const long long b = qrow / df.n_rows;
+                const long long ri = (b * df.d_rows + df.qpos[qrow]) * H * HD + k;
+                if (df.mode == DIFF_ADD16) out[oi] = f2bf(o + h2f(df.d16[ri]));
+                else df.d16[ri] = f2h_bits(bf2f(out[oi]) - o);
+                break;
+            }
+            default: out[oi] = f2bf(o); break;
+        }
     }
 }
 
@@ -1583,6 +1641,8 @@ hipError_t attn_rows_prefill(const RowsAttn& a, const KVLayer& sc, const KVLayer
     const int G = a.H / a.kv.Hkv;
     if (a.kv.hd != 128 || !a.cols || !a.qpos || a.n_rows < 1 || sc.Tmax % 8 || fr.Tmax % 8)
         return hipErrorInvalidValue;
+    if (a.diff_mode != DIFF_NONE && ((a.diff_mode != DIFF_ADD16 && a.diff_mode != DIFF_OUT16) || !a.d16))
+        return hipErrorInvalidValue;
     const int NW = G > 4 ? G : 4, RB = 32 * NW / G;
     dim3 grid((a.n_rows + RB - 1) / RB, a.kv.Hkv, a.B);
     const float sl2 = kLog2e / sqrtf(128.f);
@@ -1611,9 +1671,14 @@ hipError_t attn_rows_combine(const RowsAttn& a, hipStream_t st, bool packed_out)
     const int G = a.H / a.kv.Hkv;
     if (a.n_splits > kCombineMaxSplits || G > kCombineMaxG) return hipErrorInvalidValue;
     if (packed_out && (a.B * a.n_rows > 8 || (a.H * a.kv.hd) % 64)) return hipErrorInvalidValue;
+    if ((a.diff_mode == DIFF_ADD32 || a.diff_mode == DIFF_SET32 || a.diff_mode == DIFF_SUB32) && !a.d32)
+        return hipErrorInvalidValue;
+    if ((a.diff_mode == DIFF_ADD16 || a.diff_mode == DIFF_OUT16) && (!a.d16 || !a.qpos || packed_out))
+        return hipErrorInvalidValue;
+    const DiffOut df{a.diff_mode, a.d32, a.d16, a.d_rows, a.n_rows, a.qpos};
     dim3 grid(a.B * a.n_rows, a.H);
     hipLaunchKernelGGL(attn_combine_kernel, grid, dim3(128), 0, st, a.part, a.n_splits, G, a.kv.hd, a.H,
-                       a.kv.Hkv, a.out, packed_out);
+                       a.kv.Hkv, a.out, packed_out, df);
     return hipGetLastError();
 }
 

@@ -365,6 +365,10 @@ struct WS {
     float* rope;       // decode: cos and sin of the step's position, [hd/2][2]
     u16 *frk, *frv;    // prefill, lazy loops >= 2 (hd 128): float16 loop-k K/V at every prompt position
     int fr_cap;        // rows per (b, g) of frk / frv (T rounded up to 64; 0: none)
+    // difference-corrected sparse attention: each row's loop-1 dense minus sparse output
+    // per shared layer; prefill float16 [R][B][T][H hd], decode float32 [R][B][H hd]
+    u16* dprompt;
+    float* dstep;
     size_t total;
     long long part_floats;
 };
@@ -400,26 +404,34 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
     w.lse = (float*)take(M * c.n_heads * 4);
     w.mass = (float*)take(hd_->lazy() ? M * c.n_kv_heads * 4 : 0);
     w.keys = (float*)take(hd_->lazy() ? M * 4 : 0);
-    w.sel = (int32_t*)take(hd_->lazy() ? (long long)B * n * 4 : 0);
+    const bool diff = hd_->lazy() && hd_->z.diff_attn && c.n_loops >= 2;
+    // the loop-1 sparse term of the difference correction runs over every prompt row
+    const long long n_att = diff ? std::max(n, (long long)T) : n;
+    w.sel = (int32_t*)take(hd_->lazy() ? (long long)B * n_att * 4 : 0);
     // row-attention partials: decode rows use up to kMaxSplits splits; token-sparse
     // prefill rows need ceil((columns + window) / chunk) splits.
     long long pf = (long long)B * c.n_heads * kMaxSplits * (c.head_dim + 2);
+    const bool fr_path = hd_->lazy() && T > 1 && c.n_loops >= 2 && c.head_dim == 128;
     if (hd_->lazy() && T > 1) {
         const long long ncol = std::min((long long)std::min(hd_->z.top_s, T) + hd_->z.window, (long long)T);
         const long long sp = (ncol + kRowChunk - 1) / kRowChunk;
-        pf = std::max(pf, (long long)B * n * c.n_heads * sp * (c.head_dim + 2));
+        // the split-row kernels take the loop-1 sparse term when the float16 path does not
+        const long long rows = fr_path ? n : n_att;
+        pf = std::max(pf, (long long)B * rows * c.n_heads * sp * (c.head_dim + 2));
     }
     w.part_floats = pf;
     w.part = (float*)take(pf * 4);
     w.ids = (int32_t*)take((long long)B * 4);
     w.ps = (float*)take((d / 8 + 1) * 8 * 4);
     w.tokrec = (float*)take(hd_->lazy() && T == 1 ? (long long)c.n_shared * B * 2 * c.n_kv_heads * c.head_dim * 4 : 0);
-    w.fr_cap = (hd_->lazy() && T > 1 && c.n_loops >= 2 && c.head_dim == 128) ? (T + 63) / 64 * 64 : 0;
+    w.fr_cap = fr_path ? (T + 63) / 64 * 64 : 0;
     const long long fr_elems = (long long)B * c.n_kv_heads * w.fr_cap * c.head_dim;
     w.frk = (u16*)take(fr_elems * 2);
     w.frv = (u16*)take(fr_elems * 2);
     w.out = (float*)take((long long)B * d * 4);
     w.rope = (float*)take(T == 1 ? (long long)c.head_dim * 4 : 0);
+    w.dprompt = (u16*)take(diff ? (long long)c.n_shared * M * Hhd * 2 : 0);
+    w.dstep = (float*)take(diff && T == 1 ? (long long)c.n_shared * B * Hhd * 4 : 0);
     w.total = off;
     return w;
 }
@@ -452,6 +464,7 @@ int check_cfg(const lk_model_cfg* c, const lk_lazy_cfg* z) {
             return fail(LK_ERR_INVALID_ARG, "res_bits must be 16, 8 or 4");
         if (z->group != 32) return fail(LK_ERR_UNSUPPORTED, "group must be 32");
         if (z->stale_keys != 0 && z->stale_keys != 1) return fail(LK_ERR_INVALID_ARG, "stale_keys must be 0 or 1");
+        if (z->diff_attn != 0 && z->diff_attn != 1) return fail(LK_ERR_INVALID_ARG, "diff_attn must be 0 or 1");
         if (z->refresh_every < 0) return fail(LK_ERR_INVALID_ARG, "refresh_every must be >= 0");
     }
     return LK_OK;
@@ -498,6 +511,12 @@ struct AttnPlan {
     KVLayer ring;            // decode, loops >= 2: float16 window ring
     KVLayer full;            // prefill, loops >= 2: float16 loop-k K/V of every prompt position
                              // (full.base[0] == nullptr: the split row kernels instead)
+    // difference-corrected sparse attention of a shared layer (nullptr: off).  Decode:
+    // d32 [B][H hd] is set to the dense output minus the sparse one at loop 1 (cols,
+    // n_cols and window given) and added at loops >= 2.  Prefill loops >= 2: d16
+    // [B][T][H hd] is added, row by position.
+    float* d32;
+    u16* d16;
 };
 
 // End the capture running on `st` and append what it recorded (if anything) as a
@@ -636,6 +655,10 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
             d.n_splits = d.seg_split + ap.ring.Tmax / kSegChunk;
             if ((long long)a.B * H * d.n_splits * (hd + 2) > w.part_floats)
                 return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
+            if (ap.d32) {
+                d.diff_mode = lk::DIFF_ADD32;
+                d.d32 = ap.d32;
+            }
             LK_TRY(timed(h, TC_ATTN_DECODE_SPARSE, st, [=] { return lk::attn_rows_main(d, st); }));
             LK_HIP(lk::attn_rows_combine(d, st, io.fold));
         } else if (ap.kind == ATTN_ROWS_SPARSE && !decode && ap.full.base[0]) {
@@ -652,9 +675,23 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
                                     (u16*)ap.scache.base[1], st));
             LK_HIP(lk::gather_recon(gr, lk::GATHER_RING, ap.full.Tmax, (u16*)ap.full.base[0], (u16*)ap.full.base[1],
                                     st));
+            if (ap.d16) {
+                a.diff_mode = lk::DIFF_ADD16;
+                a.d16 = ap.d16;
+                a.d_rows = ap.T;
+            }
             LK_TRY(timed(h, TC_ATTN_PREFILL_SPARSE, st,
                          [=] { return lk::attn_rows_prefill(a, ap.scache, ap.full, st); }));
         } else {
+            if (ap.kind == ATTN_ROWS_SPARSE && ap.d16) {
+                a.diff_mode = lk::DIFF_ADD16;
+                a.d16 = ap.d16;
+                a.d_rows = ap.T;
+            }
+            if (ap.kind == ATTN_ROWS_DENSE && ap.d32) {
+                a.diff_mode = lk::DIFF_SET32;
+                a.d32 = ap.d32;
+            }
             int chunk = kRowChunk;
             if (ap.kind == ATTN_ROWS_DENSE) chunk = dense_chunk(ncol_max);
             while ((ncol_max + chunk - 1) / chunk > kMaxSplits) chunk *= 2;
@@ -666,6 +703,23 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
                              : (ap.kind == ATTN_ROWS_SPARSE ? TC_ATTN_DECODE_SPARSE : TC_ATTN_DECODE_DENSE);
             LK_TRY(timed(h, acls, st, [=] { return lk::attn_rows_main(a, st); }));
             LK_HIP(lk::attn_rows_combine(a, st, io.fold));
+            if (ap.kind == ATTN_ROWS_DENSE && ap.d32) {
+                // the token's loop-1 sparse term over the same reconstruction, taken
+                // off the dense output just stored in d32
+                lk::RowsAttn sp = a;
+                sp.cols = ap.cols;
+                sp.n_cols = ap.n_cols;
+                sp.window = ap.window;
+                sp.chunk = kRowChunk;
+                const long long nsp = std::min((long long)ap.n_cols + ap.window, (long long)ap.pos + 1);
+                sp.n_splits = (int)((nsp + kRowChunk - 1) / kRowChunk);
+                sp.diff_mode = lk::DIFF_SUB32;
+                if (!sp.cols || sp.n_splits > kMaxSplits ||
+                    (long long)a.B * a.n_rows * H * sp.n_splits * (hd + 2) > w.part_floats)
+                    return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
+                LK_HIP(lk::attn_rows_main(sp, st));
+                LK_HIP(lk::attn_rows_combine(sp, st, false));
+            }
         }
     }
     const int act = c.ffn_act == LK_ACT_SWIGLU ? lk::EPI_SWIGLU : lk::EPI_GELU;
@@ -699,6 +753,60 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
     LK_TRY(timed(h, gcls, st, [=] {
         return lk::gemm(w.act, (const u16*)W.w_down, io.M, d, c.ffn_dim, lk::EPI_ADD, io.x, nullptr, st);
     }));
+    return LK_OK;
+}
+
+// Difference-corrected attention at prefill loop 1 of shared layer r: the sparse term
+// of every prompt row (its column set over the loop-1 reconstruction), taken off the
+// dense output the layer left in w.att, into the float16 rows of layer r in w.dprompt.
+// Runs after the layer picked its column sets; w.q still holds the rotated queries.
+int diff_prompt_rows(lk_handle* h, lk_kv_store* s, int r, const WS& w, int B, int T, hipStream_t st) {
+    const lk_model_cfg& c = h->c;
+    const long long Hhd = (long long)c.n_heads * c.head_dim;
+    lk::RowsAttn a{};
+    a.q = w.q;
+    a.qpos = w.sel;
+    a.B = B;
+    a.n_rows = T;
+    a.H = c.n_heads;
+    a.kv = lazy_layer(s, r);
+    a.k_loop = 1;
+    a.cols = col_sets(s, r);
+    a.n_cols = s->lay.n_cols;
+    a.window = h->z.window;
+    a.out = w.att;
+    a.part = w.part;
+    a.diff_mode = lk::DIFF_OUT16;
+    a.d16 = w.dprompt + (long long)r * B * T * Hhd;
+    a.d_rows = T;
+    LK_HIP(lk::iota_rows(w.sel, B, T, st));
+    if (w.fr_cap) {
+        // loop 2's stable-column cache of layer r is free until loop 2 fills it (and is
+        // cleared after loop 1): it holds the loop-1 rows here
+        const KVLayer sc = scache_layer(s, 2, r);
+        KVLayer fr = sc;
+        fr.Tmax = w.fr_cap;
+        fr.base[0] = w.frk;
+        fr.base[1] = w.frv;
+        lk::RowsAttn gr{};
+        gr.B = B;
+        gr.kv = a.kv;
+        gr.k_loop = 1;
+        gr.cols = a.cols;
+        gr.n_cols = a.n_cols;
+        gr.pos = T - 1;
+        LK_HIP(lk::gather_recon(gr, lk::GATHER_ALL_S, sc.Tmax, (u16*)sc.base[0], (u16*)sc.base[1], st));
+        LK_HIP(lk::gather_recon(gr, lk::GATHER_RING, fr.Tmax, w.frk, w.frv, st));
+        LK_HIP(lk::attn_rows_prefill(a, sc, fr, st));
+        return LK_OK;
+    }
+    const long long ncol = std::min((long long)a.n_cols + a.window, (long long)T);
+    a.chunk = kRowChunk;
+    a.n_splits = (int)((ncol + kRowChunk - 1) / kRowChunk);
+    if ((long long)B * T * c.n_heads * a.n_splits * (c.head_dim + 2) > w.part_floats)
+        return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
+    LK_HIP(lk::attn_rows_main(a, st));
+    LK_HIP(lk::attn_rows_combine(a, st, false));
     return LK_OK;
 }
 
@@ -743,7 +851,7 @@ bool same_cfg(const lk_model_cfg& a, const lk_model_cfg& b) {
 bool same_lazy(const lk_lazy_cfg& a, const lk_lazy_cfg& b) {
     return a.mode == b.mode && a.rho == b.rho && a.top_s == b.top_s && a.window == b.window &&
            a.base_bits == b.base_bits && a.res_bits == b.res_bits && a.group == b.group &&
-           a.stale_keys == b.stale_keys && a.refresh_every == b.refresh_every;
+           a.stale_keys == b.stale_keys && a.refresh_every == b.refresh_every && a.diff_attn == b.diff_attn;
 }
 
 }  // namespace
@@ -1005,6 +1113,7 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
             }
         io.add = nullptr;
     } else {
+        const bool diff = h->z.diff_attn && K >= 2;
         LK_HIP(lk::copy_f32(w.h, w.h0, (long long)M * d, st));
         // loop 1: dense over every token; writes the base and picks the column sets
         for (int r = 0; r < R; ++r) {
@@ -1025,6 +1134,7 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
             } else {
                 LK_HIP(lk::topk_rows(w.mass, B * c.n_kv_heads, T, nc, cols, st));
             }
+            if (diff) LK_TRY(diff_prompt_rows(h, s, r, w, B, T, st));
         }
         io.add = nullptr;
         if (K >= 2) LK_HIP(lk::delta_keys(w.h, w.h0, M, d, w.keys, st));
@@ -1062,6 +1172,7 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
                 ap.T = T;
                 ap.scache = scache_layer(s, k, r);
                 ap.full = full;
+                if (diff) ap.d16 = w.dprompt + (long long)r * M * c.n_heads * c.head_dim;
                 lk::KVWrite kw{};
                 kw.kind = 2;
                 kw.layer = ap.read;
@@ -1182,6 +1293,12 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
             kw.layer = ap.read;
             kw.keep_codes = s->keep_codes;
             kw.tok_recon = w.tokrec + (long long)r * B * 2 * c.n_kv_heads * c.head_dim;
+            if (h->z.diff_attn && K >= 2) {
+                ap.d32 = w.dstep + (long long)r * B * c.n_heads * c.head_dim;
+                ap.cols = col_sets(s, r);
+                ap.n_cols = s->lay.n_cols;
+                ap.window = h->z.window;
+            }
             if (k == 1) {
                 ap.kind = ATTN_ROWS_DENSE;
                 ap.k_loop = 1;

@@ -231,7 +231,21 @@ struct RowsAttn {
     const float* rope_cs;
     KVWrite kvw;
     int fuse_kv;
+    // Difference-corrected sparse attention: the normalized output o of query row
+    // (b, i), heads h, meets a correction row (DIFF_NONE: out = o).
+    //   DIFF_ADD32  out = o + d32[b * n_rows + i]
+    //   DIFF_SET32  d32[b * n_rows + i] = o, and out = o
+    //   DIFF_SUB32  d32[b * n_rows + i] -= o; out is not written
+    //   DIFF_ADD16  out = o + d16[b][qpos]
+    //   DIFF_OUT16  d16[b][qpos] = out - o; out is read, not written
+    // d32 is float32 [B * n_rows][H * hd]; d16 float16 [B][d_rows][H * hd].  The
+    // combine takes every mode; attn_rows_prefill takes ADD16 and OUT16.
+    int diff_mode;
+    float* d32;
+    u16* d16;
+    int d_rows;
 };
+enum { DIFF_NONE = 0, DIFF_ADD32, DIFF_SET32, DIFF_SUB32, DIFF_ADD16, DIFF_OUT16 };
 // Write loop-k reconstructions as float16 rows into kc [B*Hkv][ncap][hd] and
 // 8-key-interleaved vc [B*Hkv][ncap/8][hd][8] (rows past the count are zero):
 //  GATHER_ALL_S:  row i = column cols[i] of the (b, g) column set, i < n_cols;

@@ -93,6 +93,16 @@ typedef struct {
      * token instead of the top n (the token set is refreshed periodically; attention
      * stays sparse and the residual rows of all tokens are stored); 0: never. */
     int32_t refresh_every;
+    /* diff_attn (0 | 1): 1 takes the difference reading of sparse attention (the
+     * FlashLoop abstract, arxivdaily.com: the attention-output differences between
+     * loops come from a sparse, stable set of key columns).  A row recomputed at loop
+     * k >= 2 outputs its previous output plus the change of its sparse term, which is
+     * its sparse output a_k plus o_1 - a_1, o_1 its dense loop-1 output and a_1 its
+     * loop-1 sparse output (same column set, loop-1 reconstruction).  Prefill keeps
+     * o_1 - a_1 for every prompt row and shared layer in the workspace (float16,
+     * R * batch * tokens * n_heads * head_dim * 2 bytes); a decode token computes its
+     * own at its loop 1 (float32).  The store is unchanged.  0: a_k alone. */
+    int32_t diff_attn;
 } lk_lazy_cfg;
 
 /* Device pointers of one layer, all bfloat16 row-major:

@@ -48,7 +48,7 @@ int main(void) {
   printf("magic %llu\n", (unsigned long long)LK_SNAPSHOT_MAGIC);
   P(lk_model_cfg, ffn_act) P(lk_model_cfg, rms_eps) P(lk_model_cfg, rope_theta)
   P(lk_lazy_cfg, rho) P(lk_lazy_cfg, top_s) P(lk_lazy_cfg, group) P(lk_lazy_cfg, stale_keys)
-  P(lk_lazy_cfg, refresh_every)
+  P(lk_lazy_cfg, refresh_every) P(lk_lazy_cfg, diff_attn)
   P(lk_weights, layers) P(lk_layer_weights, w_down)
   P(lk_store_view, slots) P(lk_store_view, n_selected) P(lk_store_view, res_row_bytes) P(lk_store_view, row_stride)
   return 0;
@@ -128,7 +128,7 @@ def test_create_rejects_bad_model_configs(field, value, code):
 
 @pytest.mark.parametrize("kw", [dict(rho=0.0), dict(rho=1.5), dict(window=0), dict(top_s=0),
                                 dict(base_bits=4), dict(res_bits=2), dict(group=16), dict(stale_keys=2),
-                                dict(refresh_every=-1)])
+                                dict(refresh_every=-1), dict(diff_attn=2)])
 def test_create_rejects_bad_lazy_configs(kw):
     s = I.workload("tiny_1p2x2c1_t32").shape
     lz = I.Lazy(mode="lazy", rho=0.5, top_s=8, window=4, base_bits=16, res_bits=8)

@@ -184,6 +184,34 @@ def test_refresh_loops_match_oracle(period, stale):
     assert r["store"].bytes_used() == (exp["shared"], exp["total"])
 
 
+DIFF = [
+    ("gqa_hd64_int8_int4", dict(), I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4,
+                                          diff_attn=True), 2),
+    ("g4_hd128_int8_int4", dict(n_heads=8, n_kv_heads=2, head_dim=128, d_model=512),
+     I.Lazy(mode="lazy", rho=0.25, top_s=40, window=24, base_bits=8, res_bits=4, diff_attn=True), 2),
+    ("g4_hd128_batch10", dict(n_heads=8, n_kv_heads=2, head_dim=128, d_model=512),
+     I.Lazy(mode="lazy", rho=0.25, top_s=40, window=24, base_bits=8, res_bits=4, diff_attn=True), 10),
+    ("hd64_stale_refresh_k4", dict(n_loops=4),
+     I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4, diff_attn=True, stale_keys=True,
+            refresh_every=2), 2),
+]
+
+
+@pytest.mark.parametrize("name,kw,lz,batch", DIFF, ids=[c[0] for c in DIFF])
+def test_diff_attention_matches_oracle(name, kw, lz, batch):
+    """Difference-corrected sparse attention (each recomputed row adds its loop-1 dense
+    minus sparse output to its sparse output): prefill over a ragged 150-token prompt
+    and decode against the oracle, through the split-row kernels (hd 64) and the
+    float16 sparse-row kernel (hd 128), with stale keys and refresh loops, and at a
+    batch past the 8-row folded decode products.  The oracle's correction is not zero
+    here, so the path is exercised."""
+    s = _small(**kw)
+    r = run_pair(s, lz, batch=batch, prompt=150, steps=3, seed=7)
+    m = r["oracle"]
+    assert max(float(np.max(np.abs(D))) for D in m.D.values()) > 1e-3
+    check(r, f"diff attention {name}")
+
+
 def test_refresh_every_loop_is_rho_one():
     """Refresh at every loop computes what rho = 1 computes: same selections (every
     token, ascending), same store layout; the outputs agree bit for bit."""
