@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--mode", default=None, choices=["per_loop", "last_loop", "lazy"])
     ap.add_argument("--prompt", type=int, default=None, help="override the prompt length")
     ap.add_argument("--base-bits", type=int, default=None)
+    ap.add_argument("--diff-attn", action="store_true",
+                    help="difference-corrected sparse attention (lazy mode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timer", action="store_true",
                     help="replay the decode step as one graph with no timed kernel class")
@@ -311,6 +313,8 @@ def main():
         wl.lazy.mode = args.mode
     if args.base_bits:
         wl.lazy.base_bits = args.base_bits
+    if args.diff_attn:
+        wl.lazy.diff_attn = True
     s, lz = wl.shape, wl.lazy
     Bsz, T = wl.batch, wl.prompt
     total_tokens = T + args.warmup + args.steps
@@ -401,7 +405,8 @@ def main():
                    "coda": s.n_coda, "d_model": s.d_model, "heads": s.n_heads,
                    "kv_heads": s.n_kv_heads, "ffn": s.ffn_dim, "mode": lz.mode, "rho": lz.rho,
                    "top_s": lz.top_s, "window": lz.window, "base_bits": lz.base_bits,
-                   "res_bits": lz.res_bits, "layer_applications": model.effective_depth()},
+                   "res_bits": lz.res_bits, "layer_applications": model.effective_depth(),
+                   **({"diff_attn": True} if getattr(lz, "diff_attn", False) else {})},
         "kv_bytes_per_token": round(kv_tok_resident, 1),
         "kv_bytes_per_token_dense_per_loop": dense_per_loop,
         "kv_reduction_vs_dense_per_loop": round(dense_per_loop / kv_tok_resident, 3),

@@ -142,6 +142,7 @@ struct StoreLayout {
     int n_sel, n_cols;
     int ncs;                 // rows per (b, g) of the stable-column cache (n_cols rounded up to 128)
     int wr;                  // rows per (b, g) of the window ring (window + 16 rounded up to 128)
+    int ck0;                 // first cached loop: 2, or 1 with difference-corrected attention
     size_t scache_bytes;     // stable-column cache and window rings together
     long long res_row_b;
 };
@@ -205,19 +206,21 @@ StoreLayout store_layout(const lk_handle* h, int B, int Tp, int Tmax) {
         s.cols = take((size_t)c.n_shared * B * Hkv * s.n_cols * 4);
     }
     s.state = take(64);  // int32 decode position t (device copy of the store length)
-    // Decode cache: for every loop k >= 2 and shared layer r, the float16 loop-k
+    // Decode cache: for every loop k >= ck0 and shared layer r, the float16 loop-k
     // reconstruction of the stable columns S (fixed once prefill has run), K rows
     // [B][Hkv][ncs][hd] then 8-key-interleaved V [B][Hkv][ncs/8][hd][8].
-    // Then the window rings: per loop k >= 2 and shared layer r, the float16 loop-k
+    // Then the window rings: per loop k >= ck0 and shared layer r, the float16 loop-k
     // reconstruction of the last wr positions (position p at row p % wr), K then V as
-    // above; prefill fills them, every decode step writes its own row.
+    // above; prefill fills them, every decode step writes its own row.  ck0 = 2, or 1
+    // when difference-corrected attention also takes a sparse term at loop 1.
     s.ncs = s.wr = 0;
+    s.ck0 = h->z.diff_attn ? 1 : 2;
     s.scache_bytes = 0;
     s.scache = off;
     if (h->z.mode == LK_MODE_LAZY && c.n_loops >= 2) {
         s.ncs = (s.n_cols + 127) / 128 * 128;
         s.wr = (h->z.window + 16 + 127) / 128 * 128;
-        s.scache_bytes = (size_t)(c.n_loops - 1) * c.n_shared * 2 * B * Hkv * ((size_t)s.ncs + s.wr) * hd * 2;
+        s.scache_bytes = (size_t)(c.n_loops + 1 - s.ck0) * c.n_shared * 2 * B * Hkv * ((size_t)s.ncs + s.wr) * hd * 2;
         s.scache = take(s.scache_bytes);
     }
     s.total = off;
@@ -325,14 +328,16 @@ int32_t* slot_map(const lk_kv_store* s, int k) {
 }
 int32_t* dev_pos(const lk_kv_store* s) { return (int32_t*)(s->buf + s->lay.state); }
 
-// Stable-column cache (ring == false) or window ring (ring == true) of loop k >= 2,
+// Stable-column cache (ring == false) or window ring (ring == true) of loop k >= ck0,
 // shared layer r, as float16 plain rows.
 KVLayer scache_layer(const lk_kv_store* s, int k, int r, bool ring = false) {
     const lk_model_cfg& c = s->h->c;
     const int rows = ring ? s->lay.wr : s->lay.ncs;
+    const int k0 = s->lay.ck0;
     const size_t one = (size_t)s->B * c.n_kv_heads * rows * c.head_dim * 2;  // K or V of one (k, r)
-    size_t off = s->lay.scache + ((size_t)(k - 2) * c.n_shared + r) * 2 * one;
-    if (ring) off += (size_t)(c.n_loops - 1) * c.n_shared * 2 * s->B * c.n_kv_heads * s->lay.ncs * c.head_dim * 2;
+    size_t off = s->lay.scache + ((size_t)(k - k0) * c.n_shared + r) * 2 * one;
+    if (ring)
+        off += (size_t)(c.n_loops + 1 - k0) * c.n_shared * 2 * s->B * c.n_kv_heads * s->lay.ncs * c.head_dim * 2;
     char* base = s->buf + off;
     KVLayer L{};
     L.lazy = 0;
@@ -704,18 +709,23 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
             LK_TRY(timed(h, acls, st, [=] { return lk::attn_rows_main(a, st); }));
             LK_HIP(lk::attn_rows_combine(a, st, io.fold));
             if (ap.kind == ATTN_ROWS_DENSE && ap.d32) {
-                // the token's loop-1 sparse term over the same reconstruction, taken
+                // the token's loop-1 sparse term, over the float16 loop-1 caches of the
+                // stable columns and the window (as the later loops read theirs), taken
                 // off the dense output just stored in d32
+                constexpr int kSegChunk = 128;
                 lk::RowsAttn sp = a;
                 sp.cols = ap.cols;
                 sp.n_cols = ap.n_cols;
                 sp.window = ap.window;
-                sp.chunk = kRowChunk;
-                const long long nsp = std::min((long long)ap.n_cols + ap.window, (long long)ap.pos + 1);
-                sp.n_splits = (int)((nsp + kRowChunk - 1) / kRowChunk);
+                sp.kv = ap.scache;
+                sp.kv2 = ap.ring;
+                sp.chunk = kSegChunk;
+                sp.seg_split = ap.scache.Tmax / kSegChunk;
+                sp.n_splits = sp.seg_split + ap.ring.Tmax / kSegChunk;
+                sp.fuse_kv = 0;
                 sp.diff_mode = lk::DIFF_SUB32;
-                if (!sp.cols || sp.n_splits > kMaxSplits ||
-                    (long long)a.B * a.n_rows * H * sp.n_splits * (hd + 2) > w.part_floats)
+                if (!sp.cols || !ap.scache.base[0] || !ap.ring.base[0] ||
+                    (long long)a.B * H * sp.n_splits * (hd + 2) > w.part_floats)
                     return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
                 LK_HIP(lk::attn_rows_main(sp, st));
                 LK_HIP(lk::attn_rows_combine(sp, st, false));
@@ -781,9 +791,9 @@ int diff_prompt_rows(lk_handle* h, lk_kv_store* s, int r, const WS& w, int B, in
     a.d_rows = T;
     LK_HIP(lk::iota_rows(w.sel, B, T, st));
     if (w.fr_cap) {
-        // loop 2's stable-column cache of layer r is free until loop 2 fills it (and is
-        // cleared after loop 1): it holds the loop-1 rows here
-        const KVLayer sc = scache_layer(s, 2, r);
+        // the loop-1 stable-column cache of layer r (filled again for decode once the
+        // loops are done)
+        const KVLayer sc = scache_layer(s, 1, r);
         KVLayer fr = sc;
         fr.Tmax = w.fr_cap;
         fr.base[0] = w.frk;
@@ -817,11 +827,13 @@ lk::KVWrite plain_write(const KVLayer& L) {
     return k;
 }
 
-// Fill the float16 decode caches of loops 2..K from the base and residuals: the
-// stable-column reconstructions (when with_s) and the window rings ending at
-// position `last` (the rows of positions up to `last` that decode can read).
+// Fill the float16 decode caches of loops ck0..K from the base and residuals: the
+// stable-column reconstructions (when with_s; always for loop 1, which prefill does
+// not cache as it goes) and the window rings ending at position `last` (the rows of
+// positions up to `last` that decode can read).
 int fill_decode_caches(lk_kv_store* s, bool with_s, int last, hipStream_t st) {
-    for (int k = 2; k <= s->K; ++k)
+    if (s->K < 2) return LK_OK;
+    for (int k = s->lay.ck0; k <= s->K; ++k)
         for (int r = 0; r < s->h->c.n_shared; ++r) {
             lk::RowsAttn g{};
             g.B = s->B;
@@ -830,7 +842,7 @@ int fill_decode_caches(lk_kv_store* s, bool with_s, int last, hipStream_t st) {
             g.cols = col_sets(s, r);
             g.n_cols = s->lay.n_cols;
             g.pos = last;
-            if (with_s) {
+            if (with_s || k == 1) {
                 const KVLayer L = scache_layer(s, k, r);
                 LK_HIP(lk::gather_recon(g, lk::GATHER_ALL_S, s->lay.ncs, (u16*)L.base[0], (u16*)L.base[1], st));
             }
@@ -1298,6 +1310,12 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
                 ap.cols = col_sets(s, r);
                 ap.n_cols = s->lay.n_cols;
                 ap.window = h->z.window;
+                if (k == 1) {  // the loop-1 sparse term reads the loop-1 caches
+                    ap.scache = scache_layer(s, 1, r);
+                    ap.ring = scache_layer(s, 1, r, true);
+                    kw.ring = ap.ring;
+                    kw.ring_on = 1;
+                }
             }
             if (k == 1) {
                 ap.kind = ATTN_ROWS_DENSE;

@@ -50,8 +50,9 @@ struct KVWrite {
     int32_t* slot_map_k;  // kind 2 decode: slot map of loop k to write (nullptr: already written)
     int keep_codes;       // leave int8/int4 codes and their scales in the store untouched
     const int32_t* dpos;  // decode: device position t (replaces pos_offset; slot = slot_base + t + row)
-    // kind 2 decode: also write the row's float16 loop-k reconstruction into this
-    // window ring (plain rows, position p at row p % ring.Tmax), when ring_on != 0.
+    // kinds 1 and 2, decode: also write the row's float16 reconstruction (the base's at
+    // loop 1, loop k's for kind 2) into this window ring (plain rows, position p at row
+    // p % ring.Tmax), when ring_on != 0.
     KVLayer ring;
     int ring_on;
     // decode (kinds 1 and 2): float32 [B][2][Hkv][hd] reconstruction of the row at the
@@ -93,10 +94,17 @@ __device__ __forceinline__ void kv_write_elem(const float* __restrict__ src, int
     const long long idx = kv == 0 ? row * hd + e : v_elem(L, b, g, pos, e);
     // decode: this row's reconstruction at the current loop, carried to the next loop
     float* tr = w.tok_recon ? w.tok_recon + (((long long)b * 2 + kv) * Hkv + g) * hd + e : nullptr;
+    auto ring_write = [&](float recon) {
+        const KVLayer& Rg = w.ring;
+        const int rp = pos % Rg.Tmax;
+        const long long ri = kv == 0 ? kv_row(Rg, b, g, rp) * hd + e : v_elem(Rg, b, g, rp, e);
+        ((u16*)Rg.base[kv])[ri] = f2h_bits(recon);
+    };
     if (w.kind == 0 || (w.kind == 1 && L.base_bits == 16)) {
         const u16 xb = f2bf(x);
         ((u16*)L.base[kv])[idx] = xb;
         if (tr) *tr = bf2f(xb);
+        if (w.kind == 1 && w.ring_on) ring_write(bf2f(xb));
     } else if (w.kind == 1) {  // int8 base: residual against a zero reconstruction
         float recon;
         if (!w.keep_codes) {
@@ -109,9 +117,10 @@ __device__ __forceinline__ void kv_write_elem(const float* __restrict__ src, int
             }
             recon = (float)q * h2f(sb);
         } else {
-            recon = tr ? kv_base_elem(L, kv, b, g, pos, e) : 0.f;
+            recon = (tr || w.ring_on) ? kv_base_elem(L, kv, b, g, pos, e) : 0.f;
         }
         if (tr) *tr = recon;
+        if (w.ring_on) ring_write(recon);
     } else {
         const long long rr = res_row(L, b, g, slot);
         float recon;  // the row's loop-k reconstruction
@@ -139,12 +148,7 @@ __device__ __forceinline__ void kv_write_elem(const float* __restrict__ src, int
             }
         }
         if (tr) *tr = recon;
-        if (w.ring_on) {
-            const KVLayer& Rg = w.ring;
-            const int rp = pos % Rg.Tmax;
-            const long long ri = kv == 0 ? kv_row(Rg, b, g, rp) * hd + e : v_elem(Rg, b, g, rp, e);
-            ((u16*)Rg.base[kv])[ri] = f2h_bits(recon);
-        }
+        if (w.ring_on) ring_write(recon);
         if (w.slot_map_k && lead) w.slot_map_k[(long long)b * L.Tmax + pos] = (int32_t)slot;
     }
 }

@@ -158,7 +158,8 @@ void lk_kv_store_release(lk_kv_store *s);
  * Per-token figures divide by batch * t. */
 int lk_kv_store_bytes_used(const lk_kv_store *s, size_t *shared, size_t *total);
 /* Bytes of the lazy store's decode cache (0 in the other modes): for every loop
- * k >= 2 and shared layer, the float16 loop-k reconstruction of (1) the stable
+ * k >= 2 (k >= 1 with diff_attn) and shared layer, the float16 loop-k
+ * reconstruction of (1) the stable
  * columns S, written at the end of prefill (S and those reconstructions do not
  * change afterwards), and (2) a ring of the last window + 16 positions (rounded up
  * to 128), filled at the end of prefill and extended by every decode step.  The

@@ -363,7 +363,8 @@ def _gpu_decode(model, store, ids):
 
 
 @pytest.mark.timeout(900)
-def test_full_context_decode_sampled_sequences():
+@pytest.mark.parametrize("diff", [False, True], ids=["sparse", "diff_attn"])
+def test_full_context_decode_sampled_sequences(diff):
     """Every launch of the decode step the throughput figure times, at its full size
     (batch 8, a 32768-token context, d 2048, 16 query / 4 KV heads of 128, FFN 5632,
     4 loops, int8 base, int4 residuals, rho 0.1, top-s 1024, window 512; packed
@@ -374,14 +375,17 @@ def test_full_context_decode_sampled_sequences():
     through a snapshot (the import rebuilds the decode caches).  Sequences 0 and 7
     (the samples) are decoded by the oracle holding the same states; the GPU keeps
     the oracle's codes for the new token.  Then sequences 1-6 are given other states
-    and the samples' outputs must not change by a bit."""
+    and the samples' outputs must not change by a bit.  With diff_attn the same step
+    takes the difference-corrected sparse attention (each token's loop-1 dense minus
+    sparse output added at loops >= 2)."""
     import copy
     from tests.synth_state import snapshot_with_states
     wl = I.workload("deep_48x4_b8_ctx32k")
     s = copy.copy(wl.shape)
     s.n_shared = 2
-    lz, Bn, T = wl.lazy, wl.batch, wl.prompt
-    log(f"full context decode: B={Bn} T={T} R={s.n_shared} K={s.n_loops}")
+    lz, Bn, T = copy.copy(wl.lazy), wl.batch, wl.prompt
+    lz.diff_attn = diff
+    log(f"full context decode: B={Bn} T={T} R={s.n_shared} K={s.n_loops} diff_attn={diff}")
     W = I.gen_weights(s, seed=3)
     ids, states, oracles, outs = _full_context_case(s, lz, Bn, T, {0: 31, 7: 37}, W, k_std=2.0)
     model = B.LoopedModel(s, lz, W)
