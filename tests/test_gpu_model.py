@@ -259,6 +259,10 @@ DEGENERATE = [
      I.Lazy(mode="lazy", rho=0.5, top_s=40, window=8, base_bits=16, res_bits=8), 3),
     ("per_loop_T1", dict(), I.Lazy(mode="per_loop"), 1),
     ("last_loop_T2", dict(n_loops=4), I.Lazy(mode="last_loop"), 2),
+    ("diff_attn_T1", dict(), I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4,
+                                    diff_attn=True), 1),
+    ("diff_attn_hd128_T4", dict(n_heads=8, n_kv_heads=2, head_dim=128, d_model=512),
+     I.Lazy(mode="lazy", rho=0.5, top_s=2, window=2, base_bits=8, res_bits=4, diff_attn=True), 4),
 ]
 
 
@@ -521,6 +525,8 @@ SNAP = [
      I.Lazy(mode="lazy", rho=0.25, top_s=40, window=8, base_bits=16, res_bits=8), 2),
     ("per_loop", dict(), I.Lazy(mode="per_loop"), None),
     ("last_loop", dict(), I.Lazy(mode="last_loop"), None),
+    ("lazy_diff_attn_hd128", dict(n_heads=8, n_kv_heads=2, head_dim=128, d_model=512),
+     I.Lazy(mode="lazy", rho=0.25, top_s=40, window=24, base_bits=8, res_bits=4, diff_attn=True), None),
 ]
 
 
