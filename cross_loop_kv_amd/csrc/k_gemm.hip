@@ -495,18 +495,21 @@ __device__ __forceinline__ void gb_issue(u16* st, const GbSrc& d, int k0, int ws
                                                  k0 * 2, 0, 0);
 }
 // Operands of k-slice c (chunk index 0..7 = 16-element group incl. the lane's k half).
+// Read order fa[0], fb[0..3], fa[1..3]: the order the MFMAs of the slice consume them.
 __device__ __forceinline__ void gb_read(const u16* st, bf16x8 (&fa)[4], bf16x8 (&fb)[4], int wm, int wn, int l32,
                                         int c) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    auto ra = [&](int i) {
         const int r = wm * 128 + 32 * i + l32;
         fa[i] = as_bf16x8(*(const uint4*)(st + r * GB_K + ((c ^ (r & 7)) * 8)));
-    }
+    };
+    ra(0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = wn * 128 + 32 * j + l32;
         fb[j] = as_bf16x8(*(const uint4*)(st + GB_M * GB_K + r * GB_K + ((c ^ (r & 7)) * 8)));
     }
+#pragma unroll
+    for (int i = 1; i < 4; ++i) ra(i);
 }
 __device__ __forceinline__ void gb_mma(f32x16 (&acc)[4][4], const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
 #pragma unroll
@@ -515,13 +518,16 @@ __device__ __forceinline__ void gb_mma(f32x16 (&acc)[4][4], const bf16x8 (&fa)[4
         for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
-// scheduling: the eight LDS reads of the next k-slice spread over the 16 MFMAs of a group
+// scheduling: the eight LDS reads of the next k-slice go out one per MFMA over the
+// first half of the 16 MFMAs of a group, so each has at least eight MFMAs (about 256
+// cycles) to land before the next group needs it
 __device__ __forceinline__ void gb_sched_reads() {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // MFMA
 }
 
 // One slab in stage U.  On entry x holds k-slice 0 of the slab.  NEXT: another slab
