@@ -69,6 +69,7 @@ class Lazy:
     stale_keys: bool = False  # carried tokens keep their last measured change (else 0)
     refresh_every: int = 0    # p > 0: loops k >= 2 with (k - 1) % p == 0 recompute every token
     diff_attn: bool = False   # loops k >= 2: sparse term plus the row's loop-1 (dense - sparse)
+    skip_tau: float = 0.0     # decode: a token leaves the loops once its state change is below this
 
 
 @dataclass

@@ -45,6 +45,13 @@ not given on any page):
   per (shared layer, token) from loop 1 and adds it to the sparse output.  A decode
   token's D comes from its own loop 1 (dense output minus the sparse one over the
   loop-1 reconstruction).  Off, o_k = a_k.
+* decode-time loop skipping (``lazy.skip_tau`` = tau > 0; the FlashLoop abstract: state
+  changes concentrate on fewer tokens as the loops proceed, carried into decode): a
+  decode token enters loop k >= 2 only if the squared change of its state over loop
+  k-1, ||h_{k-1} - h_{k-2}||^2 (the selection key; h_0 = the prelude output), is at
+  least tau.  Otherwise it leaves the loops with the state h_{k-1}, which goes to the
+  coda; it stores no row for loops k..K, so its loop-j reconstruction stays its
+  loop-(k-1) one (the lazy store's rule for carried rows).  tau = 0: never skipped.
 * periodic refresh (``lazy.refresh_every`` = p > 0): a loop k >= 2 with (k - 1) % p
   == 0 recomputes every token instead of the top n (the token set is refreshed; the
   attention stays the sparse one and the residual rows are stored for every token).
@@ -203,6 +210,11 @@ class LoopedOracle:
             if int(getattr(lazy, "refresh_every", 0)) < 0:
                 raise ValueError("refresh_every must be >= 0")
         self.diff = lazy.mode == "lazy" and bool(getattr(lazy, "diff_attn", False))
+        self.tau = F32(getattr(lazy, "skip_tau", 0.0)) if lazy.mode == "lazy" else F32(0)
+        if self.tau < 0:
+            raise ValueError("skip_tau must be >= 0")
+        self.decode_keys = {}        # (k, b, t) -> a decode token's key at loop k >= 2
+        self.decode_loops = {}       # (b, t) -> loops a decode token ran
         self.D = {}                  # diff_attn: (r, b) -> o_1 - a_1 [T, H, hd] of the prompt
         self.depth = 0           # layer applications in the last call
         self.forced_codes_from = None  # another LoopedOracle whose quantized codes are reused
@@ -561,7 +573,16 @@ class LoopedOracle:
         else:
             allc = np.arange(t + 1)
             D = {}           # diff_attn: shared layer -> this token's o_1 - a_1 [1, H, hd]
+            h_prev2 = e      # h_{k-2} at loop k (h_0: the prelude output)
+            ran = K
             for k in range(1, K + 1):
+                if k >= 2 and self.tau > 0:
+                    key = np.sum((h - h_prev2) ** 2, axis=-1, dtype=F32)[0]
+                    self.decode_keys[(k, b, t)] = key
+                    if key < self.tau:   # leaves the loops with h_{k-1}
+                        ran = k - 1
+                        break
+                    h_prev2 = h
                 h = self._loop_input(h, e, k)
                 if k >= 2:
                     slot = self.n_k[k] + (t - self.T)
@@ -585,6 +606,7 @@ class LoopedOracle:
                             o = (o + D[r]).astype(F32)
                     self.depth += 1
                     h = self._out_ffn(P + r, h, o)
+            self.decode_loops[(b, t)] = ran
         # coda
         for j in range(s.n_coda):
             h = self._dense_layer_idx(P + R + j, P + j, h, pos, b)

@@ -183,10 +183,21 @@ def brute_lazy(shape, lz, W, ids, dec):
                          np.concatenate([b, np.zeros((N - T,) + b.shape[1:], F32)]))
                   for key_, (a, b) in recon.items()}
     hdec = []
+    tau = float(getattr(lz, "skip_tau", 0.0))
     for t in range(T, N):
         x = h0[t:t + 1]
         dlast = {}
+        x_prev2 = x
         for kk in range(1, K + 1):
+            if kk >= 2 and tau > 0:
+                if float(((x.astype(np.float64) - x_prev2) ** 2).sum()) < tau:
+                    # the token leaves the loops: its rows of loops kk..K are its loop-(kk-1) rows
+                    for k2 in range(kk, K + 1):
+                        for r in range(R):
+                            for a_ in (0, 1):
+                                full_recon[(k2, r)][a_][t] = full_recon[(k2 - 1, r)][a_][t]
+                    break
+                x_prev2 = x
             x = x + W["loop_emb"][kk - 1]
             for r in range(R):
                 li = P + r
@@ -412,3 +423,56 @@ def test_diff_attn_reduces_to_plain_sparse_when_the_column_set_is_every_column()
     # rows whose sparse set is their whole causal range (i < window) carry D = 0
     for (r, b), D in m4.D.items():
         assert not np.any(D[: 3])
+
+
+def _skip_case():
+    s = I.workload("tiny_1p2x2c1_t32").shape
+    s.n_loops = 4
+    s.n_heads, s.n_kv_heads, s.ffn_act = 4, 2, "swiglu"
+    W = I.gen_weights(s, seed=61)
+    T, B, steps = 20, 2, 6
+    return s, W, T, B, steps, I.gen_prompt_ids(s, B, T, seed=62), I.gen_decode_ids(s, B, steps, seed=63)
+
+
+def _gap_tau(keys):
+    """A threshold in the widest relative gap of the keys' middle half."""
+    v = np.sort(np.asarray(keys, np.float64))
+    lo, hi = len(v) // 4, 3 * len(v) // 4
+    i = max(range(lo, hi), key=lambda j: v[j + 1] / v[j])
+    return float(np.sqrt(v[i] * v[i + 1])), v[i + 1] / v[i]
+
+
+def test_decode_loop_skipping_matches_brute_force():
+    """Decode-time loop skipping: a decode token whose state changed by less than tau
+    over the last loop leaves the loops.  The brute-force reference (whole K/V arrays,
+    a skipped token's rows copied from its last loop) gives the same outputs; some
+    tokens leave early and some run every loop; a carried token stores no row for the
+    loops it skipped; tau = 0 is the plain decode bit for bit."""
+    s, W, T, B, steps, ids, dec = _skip_case()
+    base = dict(mode="lazy", rho=0.4, top_s=6, window=3, base_bits=8, res_bits=8)
+    probe = LoopedOracle(s, I.Lazy(**base, skip_tau=1e-30), W, B, T + steps)
+    probe.prefill(ids)
+    for d in dec:
+        probe.decode(d)
+    tau, ratio = _gap_tau([v for (k, b, t), v in probe.decode_keys.items() if k == 2])
+    assert ratio > 1.05
+    lz = I.Lazy(**base, skip_tau=tau)
+    m = LoopedOracle(s, lz, W, B, T + steps)
+    out = m.prefill(ids)
+    douts = np.stack([m.decode(d) for d in dec], 1)
+    loops = np.array([[m.decode_loops[(b, t)] for t in range(T, T + steps)] for b in range(B)])
+    assert (loops < s.n_loops).any() and (loops == s.n_loops).any()
+    for b in range(B):
+        for i, t in enumerate(range(T, T + steps)):
+            for k in range(2, s.n_loops + 1):
+                assert (m.slot[k - 1, b, t] >= 0) == (k <= loops[b, i])
+        ref, dref, _, _ = brute_lazy(s, lz, W, ids[b], dec[:, b])
+        assert np.max(np.abs(out[b] - ref)) / np.max(np.abs(ref)) < 1e-4
+        assert np.max(np.abs(douts[b] - dref)) / np.max(np.abs(dref)) < 1e-4
+    plain = LoopedOracle(s, I.Lazy(**base), W, B, T + steps)
+    plain.prefill(ids)
+    p_out = np.stack([plain.decode(d) for d in dec], 1)
+    zero = LoopedOracle(s, I.Lazy(**base, skip_tau=0.0), W, B, T + steps)
+    zero.prefill(ids)
+    assert np.array_equal(np.stack([zero.decode(d) for d in dec], 1), p_out)
+    assert not np.array_equal(douts, p_out)
