@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--base-bits", type=int, default=None)
     ap.add_argument("--diff-attn", action="store_true",
                     help="difference-corrected sparse attention (lazy mode)")
+    ap.add_argument("--skip-tau", type=float, default=0.0,
+                    help="decode-time loop skipping threshold (lazy mode; 0: off)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timer", action="store_true",
                     help="replay the decode step as one graph with no timed kernel class")
@@ -315,6 +317,8 @@ def main():
         wl.lazy.base_bits = args.base_bits
     if args.diff_attn:
         wl.lazy.diff_attn = True
+    if args.skip_tau:
+        wl.lazy.skip_tau = args.skip_tau
     s, lz = wl.shape, wl.lazy
     Bsz, T = wl.batch, wl.prompt
     total_tokens = T + args.warmup + args.steps
@@ -406,7 +410,8 @@ def main():
                    "kv_heads": s.n_kv_heads, "ffn": s.ffn_dim, "mode": lz.mode, "rho": lz.rho,
                    "top_s": lz.top_s, "window": lz.window, "base_bits": lz.base_bits,
                    "res_bits": lz.res_bits, "layer_applications": model.effective_depth(),
-                   **({"diff_attn": True} if getattr(lz, "diff_attn", False) else {})},
+                   **({"diff_attn": True} if getattr(lz, "diff_attn", False) else {}),
+                   **({"skip_tau": lz.skip_tau} if getattr(lz, "skip_tau", 0.0) else {})},
         "kv_bytes_per_token": round(kv_tok_resident, 1),
         "kv_bytes_per_token_dense_per_loop": dense_per_loop,
         "kv_reduction_vs_dense_per_loop": round(dense_per_loop / kv_tok_resident, 3),
@@ -437,6 +442,13 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)...")
         res["cpu_baseline"] = cpu_baseline(wl)
+    if getattr(lz, "skip_tau", 0.0) and lz.mode == "lazy" and s.n_loops > 1:
+        # share of the decode tokens' loop-k rows (k >= 2) that were stored, from the slot maps
+        v = store.view()
+        off = int(v.slot_maps) - store.buf.data_ptr()
+        sm = store.buf[off:off + (s.n_loops - 1) * Bsz * v.row_stride * 4].view(torch.int32)
+        sm = sm.view(s.n_loops - 1, Bsz, v.row_stride)[:, :, T:t_now]
+        res["skip"] = {"tau": lz.skip_tau, "decode_loop_rows_stored_frac": round(float((sm >= 0).float().mean()), 4)}
     print(json.dumps(res), flush=True)
 
 

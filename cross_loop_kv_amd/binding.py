@@ -40,7 +40,7 @@ class lk_lazy_cfg(C.Structure):
     _fields_ = [("mode", C.c_int32), ("rho", C.c_double), ("top_s", C.c_int32),
                 ("window", C.c_int32), ("base_bits", C.c_int32), ("res_bits", C.c_int32),
                 ("group", C.c_int32), ("stale_keys", C.c_int32), ("refresh_every", C.c_int32),
-                ("diff_attn", C.c_int32)]
+                ("diff_attn", C.c_int32), ("skip_tau", C.c_float)]
 
 
 class lk_layer_weights(C.Structure):
@@ -62,7 +62,7 @@ class lk_store_view(C.Structure):
 
 
 SNAPSHOT_MAGIC = 0x313050414E534B4C   # bytes "LKSNAP01"
-SNAPSHOT_VERSION = 1
+SNAPSHOT_VERSION = 2
 
 
 class lk_store_snapshot(C.Structure):
@@ -301,7 +301,8 @@ def model_cfg(shape) -> lk_model_cfg:
 def lazy_cfg(lz) -> lk_lazy_cfg:
     return lk_lazy_cfg(MODES[lz.mode], float(lz.rho), int(lz.top_s), int(lz.window),
                        int(lz.base_bits), int(lz.res_bits), int(lz.group), int(getattr(lz, "stale_keys", False)),
-                       int(getattr(lz, "refresh_every", 0)), int(getattr(lz, "diff_attn", False)))
+                       int(getattr(lz, "refresh_every", 0)), int(getattr(lz, "diff_attn", False)),
+                       float(getattr(lz, "skip_tau", 0.0)))
 
 
 def _aligned_bytes(nbytes: int, device):

@@ -81,6 +81,33 @@ __global__ void copy_f32_kernel(const float* s, float* d, long long n) {
          i += (long long)gridDim.x * blockDim.x)
         d[i] = s[i];
 }
+// Decode-time loop skipping, at the start of a loop k >= 2: row b (one block) still in
+// the loops computes key = sum_e (src - prev)^2, its state change over loop k-1, leaves
+// the loops when key < tau, and sets prev = src (h_{k-1}: the next loop's h_{k-2}, and
+// the final state of a row that left).  Rows already out are not touched.
+__global__ __launch_bounds__(256) void skip_gate_kernel(const float* __restrict__ src, float* __restrict__ prev,
+                                                        int32_t* __restrict__ act, float tau, int d) {
+    __shared__ float red[16];
+    const int b = blockIdx.x;
+    if (!act[b]) return;
+    const float* x = src + (long long)b * d;
+    float* y = prev + (long long)b * d;
+    float v = 0.f;
+    for (int e = threadIdx.x; e < d; e += blockDim.x) {
+        const float t = x[e] - y[e];
+        v += t * t;
+    }
+    const float key = block_sum(v, red);
+    for (int e = threadIdx.x; e < d; e += blockDim.x) y[e] = x[e];
+    if (threadIdx.x == 0 && key < tau) act[b] = 0;
+}
+// After the last loop: rows that left take back their final state.
+__global__ void skip_restore_kernel(float* __restrict__ h, const float* __restrict__ prev,
+                                    const int32_t* __restrict__ act, int d) {
+    const int b = blockIdx.x;
+    if (act[b]) return;
+    for (int e = threadIdx.x; e < d; e += blockDim.x) h[(long long)b * d + e] = prev[(long long)b * d + e];
+}
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, long long n) {
     for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
          i += (long long)gridDim.x * blockDim.x)
@@ -361,6 +388,14 @@ hipError_t add_f32(float* x, const float* y, long long n, hipStream_t st) {
 }
 hipError_t copy_f32(const float* src, float* dst, long long n, hipStream_t st) {
     hipLaunchKernelGGL(copy_f32_kernel, dim3(grid_for(n)), dim3(kThreads), 0, st, src, dst, n);
+    return hipGetLastError();
+}
+hipError_t skip_gate(const float* src, float* prev, int32_t* act, float tau, int B, int d, hipStream_t st) {
+    hipLaunchKernelGGL(skip_gate_kernel, dim3(B), dim3(256), 0, st, src, prev, act, tau, d);
+    return hipGetLastError();
+}
+hipError_t skip_restore(float* h, const float* prev, const int32_t* act, int B, int d, hipStream_t st) {
+    hipLaunchKernelGGL(skip_restore_kernel, dim3(B), dim3(256), 0, st, h, prev, act, d);
     return hipGetLastError();
 }
 hipError_t fill_i32(int32_t* p, int32_t v, long long n, hipStream_t st) {

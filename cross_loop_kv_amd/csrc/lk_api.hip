@@ -374,6 +374,10 @@ struct WS {
     // per shared layer; prefill float16 [R][B][T][H hd], decode float32 [R][B][H hd]
     u16* dprompt;
     float* dstep;
+    // decode-time loop skipping: h_{k-2} per sequence (the final state of a token that
+    // left), h_{k-1} saved by the last layer of a loop, and the still-in-the-loops flags
+    float *sk_prev, *sk_save;
+    int32_t* sk_act;
     size_t total;
     long long part_floats;
 };
@@ -437,6 +441,10 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
     w.rope = (float*)take(T == 1 ? (long long)c.head_dim * 4 : 0);
     w.dprompt = (u16*)take(diff ? (long long)c.n_shared * M * Hhd * 2 : 0);
     w.dstep = (float*)take(diff && T == 1 ? (long long)c.n_shared * B * Hhd * 4 : 0);
+    const bool skip = hd_->lazy() && hd_->z.skip_tau > 0.f && c.n_loops >= 2 && T == 1;
+    w.sk_prev = (float*)take(skip ? (long long)B * d * 4 : 0);
+    w.sk_save = (float*)take(skip ? (long long)B * d * 4 : 0);
+    w.sk_act = (int32_t*)take(skip ? (long long)B * 4 : 0);
     w.total = off;
     return w;
 }
@@ -470,6 +478,8 @@ int check_cfg(const lk_model_cfg* c, const lk_lazy_cfg* z) {
         if (z->group != 32) return fail(LK_ERR_UNSUPPORTED, "group must be 32");
         if (z->stale_keys != 0 && z->stale_keys != 1) return fail(LK_ERR_INVALID_ARG, "stale_keys must be 0 or 1");
         if (z->diff_attn != 0 && z->diff_attn != 1) return fail(LK_ERR_INVALID_ARG, "diff_attn must be 0 or 1");
+        if (!(z->skip_tau >= 0.f) || !std::isfinite(z->skip_tau))
+            return fail(LK_ERR_INVALID_ARG, "skip_tau must be finite and >= 0");
         if (z->refresh_every < 0) return fail(LK_ERR_INVALID_ARG, "refresh_every must be >= 0");
     }
     return LK_OK;
@@ -863,7 +873,8 @@ bool same_cfg(const lk_model_cfg& a, const lk_model_cfg& b) {
 bool same_lazy(const lk_lazy_cfg& a, const lk_lazy_cfg& b) {
     return a.mode == b.mode && a.rho == b.rho && a.top_s == b.top_s && a.window == b.window &&
            a.base_bits == b.base_bits && a.res_bits == b.res_bits && a.group == b.group &&
-           a.stale_keys == b.stale_keys && a.refresh_every == b.refresh_every && a.diff_attn == b.diff_attn;
+           a.stale_keys == b.stale_keys && a.refresh_every == b.refresh_every && a.diff_attn == b.diff_attn &&
+           a.skip_tau == b.skip_tau;
 }
 
 }  // namespace
@@ -1268,6 +1279,7 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
     const int B = s->B;
     const bool inject = c.input_reinject != 0;
     const int32_t* dpos = dev_pos(s);
+    const bool skip = h->lazy() && h->z.skip_tau > 0.f && K >= 2;
     h->timer.in_call = 0;
     // The layer applications of one step, in order.
     struct App {
@@ -1304,6 +1316,7 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
             lk::KVWrite kw{};
             kw.layer = ap.read;
             kw.keep_codes = s->keep_codes;
+            if (skip) kw.active = w.sk_act;
             kw.tok_recon = w.tokrec + (long long)r * B * 2 * c.n_kv_heads * c.head_dim;
             if (h->z.diff_attn && K >= 2) {
                 ap.d32 = w.dstep + (long long)r * B * c.n_heads * c.head_dim;
@@ -1347,15 +1360,25 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
     const bool fold = B <= 8 && h->pk_buf != nullptr;
     LK_HIP(lk::embed(w.ids, h->tok, w.h, B, d, c.vocab, st));
     LK_HIP(lk::rope_angles(dpos, h->inv_freq, c.head_dim, w.rope, st));
+    if (skip) {  // every token enters the loops; h_0 is the prelude output
+        LK_HIP(lk::fill_i32(w.sk_act, 1, B, st));
+        if (P == 0) LK_HIP(lk::copy_f32(w.h, w.sk_prev, (long long)B * d, st));
+    }
     // re-injection: e = the prelude output (the embedding when there is no prelude)
     if (inject && K >= 2 && P == 0) LK_HIP(lk::copy_f32(w.h, w.h0, (long long)B * d, st));
     if (fold)
         LK_HIP(lk::norm_prep(w.h, apps[0].add, (const u16*)h->L[apps[0].li].attn_norm, B, d, w.xn, w.ps, st));
+    int nparts_next = 0;  // the next layer's normed input was prepared by norm_prep
     for (size_t i = 0; i < apps.size(); ++i) {
         const App& a = apps[i];
         LayerIO io{w.h, B, 1, nullptr, 0, fold ? nullptr : a.add, dpos};
         io.fold = fold;
-        io.nparts = i == 0 ? 1 : d / 8;
+        io.nparts = i == 0 || nparts_next ? 1 : d / 8;
+        nparts_next = 0;
+        // position of a shared-layer application in the loops
+        const long long li_loop = (long long)i - P;
+        const int kk = li_loop >= 0 && li_loop < (long long)K * R ? (int)(li_loop / R) + 1 : 0;
+        const int rr = kk ? (int)(li_loop % R) : -1;
         if (i + 1 < apps.size()) {
             io.next_gain = (const u16*)h->L[apps[i + 1].li].attn_norm;
             io.next_add = apps[i + 1].add;
@@ -1366,7 +1389,27 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
             if (!fold && i == (size_t)P) LK_HIP(lk::copy_f32(w.h, w.h0, (long long)B * d, st));
         }
         if (!fold && a.inj) io.inj = w.h0;
+        bool copy_e = false;  // skipping: h_0 = the prelude output, saved by the layer
+        if (skip && P > 0) {
+            if (fold && i + 1 == (size_t)P) {
+                if (io.save_x) copy_e = true;
+                else io.save_x = w.sk_prev;
+            }
+            if (!fold && i == (size_t)P) LK_HIP(lk::copy_f32(w.h, w.sk_prev, (long long)B * d, st));
+        }
+        if (skip && kk >= 2 && rr == 0)  // h_{k-1}: saved by the last layer (folded) or in h
+            LK_HIP(lk::skip_gate(fold ? w.sk_save : w.h, w.sk_prev, w.sk_act, h->z.skip_tau, B, d, st));
+        if (skip && fold && kk >= 1 && kk < K && rr == R - 1) io.save_x = w.sk_save;
         LK_TRY(run_layer(h, a.li, io, a.kw, a.ap, w, st));
+        if (copy_e) LK_HIP(lk::copy_f32(io.save_x, w.sk_prev, (long long)B * d, st));
+        if (skip && kk == K && rr == R - 1) {
+            LK_HIP(lk::skip_restore(w.h, w.sk_prev, w.sk_act, B, d, st));
+            if (fold && i + 1 < apps.size()) {  // the coda's first normed input, again
+                LK_HIP(lk::norm_prep(w.h, nullptr, (const u16*)h->L[apps[i + 1].li].attn_norm, B, d, w.xn, w.ps,
+                                     st));
+                nparts_next = 1;
+            }
+        }
     }
     LK_HIP(lk::rmsnorm(w.h, nullptr, h->fnorm, c.rms_eps, B, d, nullptr, w.out, st));
     LK_HIP(lk::add_i32(dev_pos(s), 1, st));

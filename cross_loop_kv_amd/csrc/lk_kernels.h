@@ -24,6 +24,12 @@ hipError_t fill_i32(int32_t* p, int32_t v, long long n, hipStream_t st);
 hipError_t fill_f32(float* p, float v, long long n, hipStream_t st);
 hipError_t iota_rows(int32_t* p, int rows, int n, hipStream_t st);  // p[r * n + j] = j
 hipError_t add_i32(int32_t* p, int32_t v, hipStream_t st);  // *p += v (one thread)
+// Decode-time loop skipping.  skip_gate, at the start of a loop k >= 2, for each of the B
+// rows still in the loops (act[b] != 0): key = ||src_b - prev_b||^2 (float32 [B, d]; src
+// = h_{k-1}, prev = h_{k-2}); act[b] = 0 when key < tau; prev_b = src_b.  skip_restore,
+// after the last loop: h_b = prev_b for the rows that left.
+hipError_t skip_gate(const float* src, float* prev, int32_t* act, float tau, int B, int d, hipStream_t st);
+hipError_t skip_restore(float* h, const float* prev, const int32_t* act, int B, int d, hipStream_t st);
 hipError_t delta_keys(const float* a, const float* b, int rows, int d, float* key, hipStream_t st);
 // xc[b*n + j] = (h[b*T + idx[b*n + j]] (+ add_src[same row])) + add; slot_map[b*Tmax + idx] = j
 // when slot_map != nullptr.
@@ -62,6 +68,10 @@ struct KVWrite {
     // decode (every row at position *dpos): cos and sin of the rotation angles of that
     // position, [hd/2][2] (rope_angles), in place of evaluating them per element
     const float* rope_cs;
+    // kind 2 decode with loop skipping: act[b] == 0 marks a sequence whose token left the
+    // loops; its row stores nothing (slot map entry -1), keeps the previous loop's
+    // reconstruction and puts that into the ring.  nullptr: every row stores.
+    const int32_t* active;
 };
 // cos and sin (float64 evaluation, rounded to float32) of position *dpos times each
 // inverse frequency into cs [hd/2][2].
@@ -121,6 +131,10 @@ __device__ __forceinline__ void kv_write_elem(const float* __restrict__ src, int
         }
         if (tr) *tr = recon;
         if (w.ring_on) ring_write(recon);
+    } else if (w.active && !w.active[b]) {  // the token left the loops: carried row
+        const float recon = tr ? *tr : kv_recon_elem(L, kv, b, g, pos, e, w.loop - 1);
+        if (w.ring_on) ring_write(recon);
+        if (w.slot_map_k && lead) w.slot_map_k[(long long)b * L.Tmax + pos] = -1;
     } else {
         const long long rr = res_row(L, b, g, slot);
         float recon;  // the row's loop-k reconstruction

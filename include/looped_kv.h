@@ -103,6 +103,14 @@ typedef struct {
      * R * batch * tokens * n_heads * head_dim * 2 bytes); a decode token computes its
      * own at its loop 1 (float32).  The store is unchanged.  0: a_k alone. */
     int32_t diff_attn;
+    /* skip_tau >= 0: decode-time loop skipping (the FlashLoop abstract: state changes
+     * concentrate on fewer tokens as the loops proceed, carried into decode).  A decode
+     * token enters loop k >= 2 only if ||h_{k-1} - h_{k-2}||^2 >= skip_tau (h_0 the
+     * prelude output); otherwise it leaves the loops with h_{k-1}, and for loops k..K
+     * stores no residual row (slot map entry -1: its reconstruction stays the
+     * previous loop's; its slot stays reserved).  In a batched step the sequences that
+     * left are masked: every launch still runs.  0: never skipped. */
+    float skip_tau;
 } lk_lazy_cfg;
 
 /* Device pointers of one layer, all bfloat16 row-major:
@@ -229,7 +237,7 @@ int lk_kv_store_set_loops(lk_kv_store *s, int32_t n_loops);
  * it: import rebuilds them from the base and residuals, with the same values the
  * prefill and decode steps wrote. */
 #define LK_SNAPSHOT_MAGIC 0x313050414e534b4cull /* bytes "LKSNAP01" */
-#define LK_SNAPSHOT_VERSION 1
+#define LK_SNAPSHOT_VERSION 2
 typedef struct {
     uint64_t magic;          /* LK_SNAPSHOT_MAGIC */
     uint32_t header_bytes;   /* sizeof(lk_store_snapshot); the body follows */

@@ -46,9 +46,10 @@ int main(void) {
   P(lk_store_snapshot, cfg) P(lk_store_snapshot, lazy) P(lk_store_snapshot, batch)
   P(lk_store_snapshot, prefilled) P(lk_store_snapshot, body_bytes)
   printf("magic %llu\n", (unsigned long long)LK_SNAPSHOT_MAGIC);
+  printf("snapshot_version %d\n", (int)LK_SNAPSHOT_VERSION);
   P(lk_model_cfg, ffn_act) P(lk_model_cfg, rms_eps) P(lk_model_cfg, rope_theta)
   P(lk_lazy_cfg, rho) P(lk_lazy_cfg, top_s) P(lk_lazy_cfg, group) P(lk_lazy_cfg, stale_keys)
-  P(lk_lazy_cfg, refresh_every) P(lk_lazy_cfg, diff_attn)
+  P(lk_lazy_cfg, refresh_every) P(lk_lazy_cfg, diff_attn) P(lk_lazy_cfg, skip_tau)
   P(lk_weights, layers) P(lk_layer_weights, w_down)
   P(lk_store_view, slots) P(lk_store_view, n_selected) P(lk_store_view, res_row_bytes) P(lk_store_view, row_stride)
   return 0;
@@ -62,6 +63,7 @@ int main(void) {
         out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
     got = dict(line.rsplit(" ", 1) for line in out.strip().splitlines())
     assert int(got.pop("magic")) == B.SNAPSHOT_MAGIC
+    assert int(got.pop("snapshot_version")) == B.SNAPSHOT_VERSION
     assert B.SNAPSHOT_MAGIC.to_bytes(8, "little") == b"LKSNAP01"
     for name in ("lk_model_cfg", "lk_lazy_cfg", "lk_layer_weights", "lk_weights", "lk_store_view",
                  "lk_store_snapshot"):
@@ -128,7 +130,8 @@ def test_create_rejects_bad_model_configs(field, value, code):
 
 @pytest.mark.parametrize("kw", [dict(rho=0.0), dict(rho=1.5), dict(window=0), dict(top_s=0),
                                 dict(base_bits=4), dict(res_bits=2), dict(group=16), dict(stale_keys=2),
-                                dict(refresh_every=-1), dict(diff_attn=2)])
+                                dict(refresh_every=-1), dict(diff_attn=2),
+                                dict(skip_tau=-1.0), dict(skip_tau=float("nan"))])
 def test_create_rejects_bad_lazy_configs(kw):
     s = I.workload("tiny_1p2x2c1_t32").shape
     lz = I.Lazy(mode="lazy", rho=0.5, top_s=8, window=4, base_bits=16, res_bits=8)
@@ -192,7 +195,7 @@ def test_snapshot_size_query_and_import_validation():
         cases = [
             ("short", header()[:hdr_bytes - 1]),
             ("magic", header(magic=B.SNAPSHOT_MAGIC + 1)),
-            ("version", header(version=2)),
+            ("version", header(version=99)),
             ("config", header(cfg=B.model_cfg(I.Shape(**{**wl.shape.__dict__, "input_reinject": True})))),
             ("policy", header(lazy=B.lazy_cfg(I.Lazy(mode="last_loop")))),
             ("batch", header(batch=2)),

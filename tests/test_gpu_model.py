@@ -20,7 +20,7 @@ from cross_loop_kv_amd import binding as B
 from cross_loop_kv_amd import inputs as I
 from oracle import accounting
 from oracle.model import LoopedOracle
-from tests.gpu_util import gpu_selection, log, max_abs_rel, run_pair
+from tests.gpu_util import gpu_selection, log, max_abs_rel, run_pair, store_region
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -210,6 +210,75 @@ def test_diff_attention_matches_oracle(name, kw, lz, batch):
     m = r["oracle"]
     assert max(float(np.max(np.abs(D))) for D in m.D.values()) > 1e-3
     check(r, f"diff attention {name}")
+
+
+SKIP = [
+    ("hd64_folded", dict(n_loops=4), dict(), 2),
+    ("hd64_no_prelude", dict(n_loops=4, n_prelude=0), dict(), 2),
+    ("hd64_batch10", dict(n_loops=4), dict(), 10),
+    ("hd128_diff_attn", dict(n_loops=4, n_heads=8, n_kv_heads=2, head_dim=128, d_model=512),
+     dict(diff_attn=True), 4),
+]
+
+
+def _skip_tau(s, lz_kw, W, batch, T, steps):
+    """A threshold that some decode tokens' keys fall below and others stay above, with
+    every key of the oracle's run at least 1 % away from it, and on which the oracle run
+    with bf16 operands (the GPU path's rounding) takes the same decisions."""
+    ids = I.gen_prompt_ids(s, batch, T)
+    dec = I.gen_decode_ids(s, batch, steps)
+    probe = LoopedOracle(s, I.Lazy(**lz_kw, skip_tau=1e-30), W, batch, T + steps)
+    probe.prefill(ids)
+    for d in dec:
+        probe.decode(d)
+    v = np.sort(np.array(list(probe.decode_keys.values()), np.float64))
+    gaps = sorted(range(len(v) - 1), key=lambda j: -v[j + 1] / v[j])
+    for j in gaps[:12]:
+        tau = float(np.sqrt(v[j] * v[j + 1]))
+        lz = I.Lazy(**lz_kw, skip_tau=tau)
+        m = LoopedOracle(s, lz, W, batch, T + steps)
+        m.prefill(ids)
+        for d in dec:
+            m.decode(d)
+        keys = np.array(list(m.decode_keys.values()), np.float64)
+        loops = np.array(list(m.decode_loops.values()))
+        if np.min(np.abs(keys / tau - 1)) < 0.01 or not (loops < s.n_loops).any() or (loops < s.n_loops).all():
+            continue
+        m16 = LoopedOracle(s, lz, W, batch, T + steps, operand_precision="bf16")
+        m16.forced_tokens, m16.forced_S = dict(m.sel), m.S
+        m16.prefill(ids)
+        for d in dec:
+            m16.decode(d)
+        if m16.decode_loops == m.decode_loops:
+            return tau
+    pytest.fail("no threshold with a 1 % margin")
+
+
+@pytest.mark.parametrize("name,kw,extra,batch", SKIP, ids=[c[0] for c in SKIP])
+def test_decode_loop_skipping_matches_oracle(name, kw, extra, batch):
+    """Decode-time loop skipping: the tokens that leave the loops early are the oracle's
+    (the decode slot maps agree bit for bit: -1 for every loop a token skipped), and the
+    outputs agree within the usual bound, with the folded decode products, without a
+    prelude (h_0 = the embedding), at 10 sequences (unfolded products) and together
+    with difference-corrected attention."""
+    s = _small(**kw)
+    T, steps = 60, 6
+    lz_kw = dict(mode="lazy", rho=0.3, top_s=12, window=8, base_bits=8, res_bits=4, **extra)
+    W = I.gen_weights(s, seed=7)
+    tau = _skip_tau(s, lz_kw, W, batch, T, steps)
+    lz = I.Lazy(**lz_kw, skip_tau=tau)
+    r = run_pair(s, lz, batch=batch, prompt=T, steps=steps, seed=7, weights=W)
+    m, store = r["oracle"], r["store"]
+    loops = np.array([[m.decode_loops[(b, t)] for t in range(T, T + steps)] for b in range(batch)])
+    log(f"  {name}: tau {tau:.4g}, loops run per decode token {loops.tolist()}")
+    assert (loops < s.n_loops).any() and (loops == s.n_loops).any()
+    v = store.view()
+    torch.cuda.synchronize()
+    sm = store_region(store, v.slot_maps, (s.n_loops - 1) * batch * v.row_stride * 4, torch.int32)
+    sm = sm.view(s.n_loops - 1, batch, v.row_stride)[:, :, T:T + steps].cpu().numpy()
+    for k in range(2, s.n_loops + 1):
+        assert np.array_equal(sm[k - 2] >= 0, k <= loops), f"loop {k}"
+    check(r, f"loop skipping {name}")
 
 
 def test_refresh_every_loop_is_rho_one():
