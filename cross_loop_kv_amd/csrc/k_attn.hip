@@ -526,13 +526,16 @@ __global__ __launch_bounds__(256) void column_mass_kernel(const u16* __restrict_
 
 // ---------------------------------------------------------------- dense decode (MFMA)
 // Row types of the dense decode kernel.
-enum { RT_BF16 = 0, RT_I8 = 1, RT_F16 = 2, RT_F16_2SEG = 3 };
+// RT_F16_2SEG_LIVE: two segments, and the launch stops after the new token's K/V write
+// when no sequence is left in the loops (*a.live == 0).
+enum { RT_BF16 = 0, RT_I8 = 1, RT_F16 = 2, RT_F16_2SEG = 3, RT_F16_2SEG_LIVE = 4 };
 
 template <int HD, int G, int RT>
 __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
     constexpr bool I8 = RT == RT_I8;
     constexpr bool HALF = RT != RT_BF16;  // f16 MFMA (int8 codes are converted to f16)
-    constexpr bool SEG = RT == RT_F16_2SEG;
+    constexpr bool SEG = RT == RT_F16_2SEG || RT == RT_F16_2SEG_LIVE;
+    constexpr bool LIVE = RT == RT_F16_2SEG_LIVE;
     constexpr int NQ = HD / 32;   // 32-wide k-steps over hd (= scale groups)
     constexpr int NE = HD / 16;   // 16-row tiles of O^T
     const int split = blockIdx.x, bg = blockIdx.y;
@@ -583,6 +586,7 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
             __syncthreads();
         }
     }
+    if (LIVE && *a.live == 0) return;  // no sequence left in the loops: the write only
 
     // int8 rows (hd >= 64): lane (key, kgrp) reads 16 bytes at 64h + 16 kgrp of its K row
     // for h < NQ / 2, so every load covers 64 contiguous bytes of each key; k-step j
@@ -1451,10 +1455,13 @@ struct DiffOut {
     u16* d16;
     int d_rows, n_rows;
     const int32_t* qpos;
+    const int32_t* live;
 };
+template <bool LIVE>
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part, int n_splits, int G,
                                                            int HD, int H, int Hkv, u16* __restrict__ out,
                                                            bool packed, DiffOut df) {
+    if (LIVE && *df.live == 0) return;  // no sequence left in the loops
     __shared__ float wts[kCombineMaxSplits];
     __shared__ float red[2];
     const long long qrow = blockIdx.x;
@@ -1563,7 +1570,9 @@ hipError_t mass_hd(const u16* q, const KVLayer& kv, const float* lse, int B, int
 template <int HD, int G>
 void dense_launch(const RowsAttn& a, hipStream_t st) {
     dim3 grid(a.n_splits, a.B * a.kv.Hkv);
-    if (a.seg_split > 0)
+    if (a.seg_split > 0 && a.live)
+        hipLaunchKernelGGL((attn_decode_dense_kernel<HD, G, RT_F16_2SEG_LIVE>), grid, dim3(256), 0, st, a);
+    else if (a.seg_split > 0)
         hipLaunchKernelGGL((attn_decode_dense_kernel<HD, G, RT_F16_2SEG>), grid, dim3(256), 0, st, a);
     else if (a.kv.lazy && a.kv.base_bits == 8)
         hipLaunchKernelGGL((attn_decode_dense_kernel<HD, G, RT_I8>), grid, dim3(256), 0, st, a);
@@ -1675,10 +1684,14 @@ hipError_t attn_rows_combine(const RowsAttn& a, hipStream_t st, bool packed_out)
         return hipErrorInvalidValue;
     if ((a.diff_mode == DIFF_ADD16 || a.diff_mode == DIFF_OUT16) && (!a.d16 || !a.qpos || packed_out))
         return hipErrorInvalidValue;
-    const DiffOut df{a.diff_mode, a.d32, a.d16, a.d_rows, a.n_rows, a.qpos};
+    const DiffOut df{a.diff_mode, a.d32, a.d16, a.d_rows, a.n_rows, a.qpos, a.live};
     dim3 grid(a.B * a.n_rows, a.H);
-    hipLaunchKernelGGL(attn_combine_kernel, grid, dim3(128), 0, st, a.part, a.n_splits, G, a.kv.hd, a.H,
-                       a.kv.Hkv, a.out, packed_out, df);
+    if (a.live)
+        hipLaunchKernelGGL(attn_combine_kernel<true>, grid, dim3(128), 0, st, a.part, a.n_splits, G, a.kv.hd, a.H,
+                           a.kv.Hkv, a.out, packed_out, df);
+    else
+        hipLaunchKernelGGL(attn_combine_kernel<false>, grid, dim3(128), 0, st, a.part, a.n_splits, G, a.kv.hd, a.H,
+                           a.kv.Hkv, a.out, packed_out, df);
     return hipGetLastError();
 }
 

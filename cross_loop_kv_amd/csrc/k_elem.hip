@@ -86,7 +86,8 @@ __global__ void copy_f32_kernel(const float* s, float* d, long long n) {
 // the loops when key < tau, and sets prev = src (h_{k-1}: the next loop's h_{k-2}, and
 // the final state of a row that left).  Rows already out are not touched.
 __global__ __launch_bounds__(256) void skip_gate_kernel(const float* __restrict__ src, float* __restrict__ prev,
-                                                        int32_t* __restrict__ act, float tau, int d) {
+                                                        int32_t* __restrict__ act, int32_t* __restrict__ live,
+                                                        float tau, int d) {
     __shared__ float red[16];
     const int b = blockIdx.x;
     if (!act[b]) return;
@@ -99,7 +100,10 @@ __global__ __launch_bounds__(256) void skip_gate_kernel(const float* __restrict_
     }
     const float key = block_sum(v, red);
     for (int e = threadIdx.x; e < d; e += blockDim.x) y[e] = x[e];
-    if (threadIdx.x == 0 && key < tau) act[b] = 0;
+    if (threadIdx.x == 0 && key < tau) {
+        act[b] = 0;
+        atomicSub(live, 1);
+    }
 }
 // After the last loop: rows that left take back their final state.
 __global__ void skip_restore_kernel(float* __restrict__ h, const float* __restrict__ prev,
@@ -390,8 +394,9 @@ hipError_t copy_f32(const float* src, float* dst, long long n, hipStream_t st) {
     hipLaunchKernelGGL(copy_f32_kernel, dim3(grid_for(n)), dim3(kThreads), 0, st, src, dst, n);
     return hipGetLastError();
 }
-hipError_t skip_gate(const float* src, float* prev, int32_t* act, float tau, int B, int d, hipStream_t st) {
-    hipLaunchKernelGGL(skip_gate_kernel, dim3(B), dim3(256), 0, st, src, prev, act, tau, d);
+hipError_t skip_gate(const float* src, float* prev, int32_t* act, int32_t* live, float tau, int B, int d,
+                     hipStream_t st) {
+    hipLaunchKernelGGL(skip_gate_kernel, dim3(B), dim3(256), 0, st, src, prev, act, live, tau, d);
     return hipGetLastError();
 }
 hipError_t skip_restore(float* h, const float* prev, const int32_t* act, int B, int d, hipStream_t st) {

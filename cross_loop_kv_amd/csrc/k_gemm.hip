@@ -259,10 +259,11 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(const u16* __restrict_
 // PREP (with EPI_ADD): besides x += A W^T (+ add_vec), write what the next NORM
 // product needs: xg_out = bf16(x * next_gain) and, per workgroup, the row sums of x^2
 // over its 8 columns into ps_out [N / 8][8].
-template <int EPI, int NL, bool NORM, bool PREP, bool PK>
+template <int EPI, int NL, bool NORM, bool PREP, bool PK, bool LIVE>
 __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ A, const u16* __restrict__ W,
                                                         int M, int N, int K, float* __restrict__ C,
                                                         u16* __restrict__ Obf, FoldIO io) {
+    if (LIVE && *io.live == 0) return;  // no sequence left in the loops
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
     constexpr int NWV = 8;
     __shared__ f32x4 red[NWV][64][DUAL ? 2 : 1];
@@ -399,10 +400,14 @@ void launch_fold(const u16* A, const u16* W, int M, int N, int K, float* c, u16*
     // one batch of loads per wave at K = 2048 (4 chunks) and K = 5632 (11 chunks)
     const int per_wave = (K / 64 + 7) / 8;
     dim3 grid(N / 8);
-    if (per_wave > 4)
-        hipLaunchKernelGGL((gemm_fold_kernel<EPI, 11, NORM, PREP, PK>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf, io);
+    if (io.live && per_wave > 4)
+        hipLaunchKernelGGL((gemm_fold_kernel<EPI, 11, NORM, PREP, PK, true>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf, io);
+    else if (io.live)
+        hipLaunchKernelGGL((gemm_fold_kernel<EPI, 4, NORM, PREP, PK, true>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf, io);
+    else if (per_wave > 4)
+        hipLaunchKernelGGL((gemm_fold_kernel<EPI, 11, NORM, PREP, PK, false>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf, io);
     else
-        hipLaunchKernelGGL((gemm_fold_kernel<EPI, 4, NORM, PREP, PK>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf, io);
+        hipLaunchKernelGGL((gemm_fold_kernel<EPI, 4, NORM, PREP, PK, false>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf, io);
 }
 
 __global__ void pack_rows_kernel(const u16* __restrict__ W, long long rows, int K, u16* __restrict__ Wp) {
@@ -740,9 +745,10 @@ hipError_t gemm_rmsnorm(const float* X, const u16* gain, float eps, const u16* W
 bool gemm_fold_supported(int M, int N, int K) { return fold_ok(M, N, K); }
 
 hipError_t gemm_fold_norm(const u16* xg, const float* ps, int nparts, float eps, const u16* Wp, int M, int N, int K,
-                          int epi, float* c, u16* out_bf, hipStream_t st) {
+                          int epi, float* c, u16* out_bf, hipStream_t st, const int32_t* live) {
     if (!fold_ok(M, N, K)) return hipErrorInvalidValue;
     FoldIO io{};
+    io.live = live;
     io.ps_in = ps;
     io.nparts = nparts;
     io.eps = eps;
@@ -757,10 +763,11 @@ hipError_t gemm_fold_norm(const u16* xg, const float* ps, int nparts, float eps,
 
 hipError_t gemm_fold_add(const u16* A, const u16* Wp, int M, int N, int K, float* x, const u16* add_vec,
                          const u16* next_gain, u16* xg_out, float* ps_out, hipStream_t st, const float* add_rows,
-                         float* x_save) {
+                         float* x_save, const int32_t* live) {
     if (!fold_ok(M, N, K)) return hipErrorInvalidValue;
     if ((add_rows || x_save) && !next_gain) return hipErrorInvalidValue;
     FoldIO io{};
+    io.live = live;
     io.add_vec = add_vec;
     io.add_rows = add_rows;
     io.x_save = x_save;

@@ -377,7 +377,7 @@ struct WS {
     // decode-time loop skipping: h_{k-2} per sequence (the final state of a token that
     // left), h_{k-1} saved by the last layer of a loop, and the still-in-the-loops flags
     float *sk_prev, *sk_save;
-    int32_t* sk_act;
+    int32_t *sk_act, *sk_live;  // flags per sequence; how many are still in the loops
     size_t total;
     long long part_floats;
 };
@@ -445,6 +445,7 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
     w.sk_prev = (float*)take(skip ? (long long)B * d * 4 : 0);
     w.sk_save = (float*)take(skip ? (long long)B * d * 4 : 0);
     w.sk_act = (int32_t*)take(skip ? (long long)B * 4 : 0);
+    w.sk_live = (int32_t*)take(skip ? 4 : 0);
     w.total = off;
     return w;
 }
@@ -508,6 +509,9 @@ struct LayerIO {
     const float* inj;
     const float* next_inj;
     float* save_x;
+    // decode-time loop skipping, folded decode: *live == 0 (no sequence left in the
+    // loops) lets the layer's launches return at once (the new token's K/V write stays)
+    const int32_t* live;
 };
 
 enum AttnKind { ATTN_PREFILL_DENSE, ATTN_ROWS_DENSE, ATTN_ROWS_SPARSE };
@@ -586,7 +590,7 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
     if (io.fold) {
         LK_TRY(timed(h, gcls, st, [=] {
             return lk::gemm_fold_norm(w.xn, w.ps, io.nparts, c.rms_eps, PW.wqkv, io.M, h->qkv_w(), d,
-                                      lk::EPI_STORE, w.qkv, nullptr, st);
+                                      lk::EPI_STORE, w.qkv, nullptr, st, io.live);
         }));
     } else if (fused_norm) {
         if (io.add) LK_HIP(lk::add_rows(io.x, io.add, io.M, d, st));
@@ -674,6 +678,7 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
                 d.diff_mode = lk::DIFF_ADD32;
                 d.d32 = ap.d32;
             }
+            d.live = io.live;
             LK_TRY(timed(h, TC_ATTN_DECODE_SPARSE, st, [=] { return lk::attn_rows_main(d, st); }));
             LK_HIP(lk::attn_rows_combine(d, st, io.fold));
         } else if (ap.kind == ATTN_ROWS_SPARSE && !decode && ap.full.base[0]) {
@@ -746,15 +751,15 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
     if (io.fold) {
         LK_TRY(timed(h, gcls, st, [=] {
             return lk::gemm_fold_add(w.att, PW.wo, io.M, d, Hhd, io.x, nullptr, (const u16*)W.ffn_norm, w.xn, w.ps,
-                                     st);
+                                     st, nullptr, nullptr, io.live);
         }));
         LK_TRY(timed(h, gcls, st, [=] {
             return lk::gemm_fold_norm(w.xn, w.ps, d / 8, c.rms_eps, PW.w_in, io.M, c.ffn_dim, d, act, nullptr,
-                                      w.act, st);
+                                      w.act, st, io.live);
         }));
         LK_TRY(timed(h, gcls, st, [=] {
             return lk::gemm_fold_add(w.act, PW.w_down, io.M, d, c.ffn_dim, io.x, io.next_add, io.next_gain, w.xn,
-                                     w.ps, st, io.next_inj, io.save_x);
+                                     w.ps, st, io.next_inj, io.save_x, io.live);
         }));
         return LK_OK;
     }
@@ -1362,6 +1367,7 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
     LK_HIP(lk::rope_angles(dpos, h->inv_freq, c.head_dim, w.rope, st));
     if (skip) {  // every token enters the loops; h_0 is the prelude output
         LK_HIP(lk::fill_i32(w.sk_act, 1, B, st));
+        LK_HIP(lk::fill_i32(w.sk_live, B, 1, st));
         if (P == 0) LK_HIP(lk::copy_f32(w.h, w.sk_prev, (long long)B * d, st));
     }
     // re-injection: e = the prelude output (the embedding when there is no prelude)
@@ -1398,7 +1404,9 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
             if (!fold && i == (size_t)P) LK_HIP(lk::copy_f32(w.h, w.sk_prev, (long long)B * d, st));
         }
         if (skip && kk >= 2 && rr == 0)  // h_{k-1}: saved by the last layer (folded) or in h
-            LK_HIP(lk::skip_gate(fold ? w.sk_save : w.h, w.sk_prev, w.sk_act, h->z.skip_tau, B, d, st));
+            LK_HIP(lk::skip_gate(fold ? w.sk_save : w.h, w.sk_prev, w.sk_act, w.sk_live, h->z.skip_tau, B, d, st));
+        // folded decode: the launches of loops >= 2 return at once when no sequence is left
+        if (skip && fold && kk >= 2) io.live = w.sk_live;
         if (skip && fold && kk >= 1 && kk < K && rr == R - 1) io.save_x = w.sk_save;
         LK_TRY(run_layer(h, a.li, io, a.kw, a.ap, w, st));
         if (copy_e) LK_HIP(lk::copy_f32(io.save_x, w.sk_prev, (long long)B * d, st));

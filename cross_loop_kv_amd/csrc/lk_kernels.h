@@ -26,9 +26,11 @@ hipError_t iota_rows(int32_t* p, int rows, int n, hipStream_t st);  // p[r * n +
 hipError_t add_i32(int32_t* p, int32_t v, hipStream_t st);  // *p += v (one thread)
 // Decode-time loop skipping.  skip_gate, at the start of a loop k >= 2, for each of the B
 // rows still in the loops (act[b] != 0): key = ||src_b - prev_b||^2 (float32 [B, d]; src
-// = h_{k-1}, prev = h_{k-2}); act[b] = 0 when key < tau; prev_b = src_b.  skip_restore,
+// = h_{k-1}, prev = h_{k-2}); act[b] = 0 and *live -= 1 when key < tau; prev_b = src_b
+// (*live counts the rows still in the loops).  skip_restore,
 // after the last loop: h_b = prev_b for the rows that left.
-hipError_t skip_gate(const float* src, float* prev, int32_t* act, float tau, int B, int d, hipStream_t st);
+hipError_t skip_gate(const float* src, float* prev, int32_t* act, int32_t* live, float tau, int B, int d,
+                     hipStream_t st);
 hipError_t skip_restore(float* h, const float* prev, const int32_t* act, int B, int d, hipStream_t st);
 hipError_t delta_keys(const float* a, const float* b, int rows, int d, float* key, hipStream_t st);
 // xc[b*n + j] = (h[b*T + idx[b*n + j]] (+ add_src[same row])) + add; slot_map[b*Tmax + idx] = j
@@ -194,15 +196,16 @@ struct FoldIO {
     const u16* next_gain;  // PREP: bf16 [N] gain of the next RMSNorm
     u16* xg_out;           // PREP: bf16 [M, N]
     float* ps_out;         // PREP: [N / 8][8]
+    const int32_t* live;   // nonzero *live or nullptr: run; *live == 0: return at once
 };
 bool gemm_fold_supported(int M, int N, int K);
 hipError_t gemm_fold_norm(const u16* xg, const float* ps, int nparts, float eps, const u16* Wp, int M, int N, int K,
-                          int epi, float* c, u16* out_bf, hipStream_t st);
+                          int epi, float* c, u16* out_bf, hipStream_t st, const int32_t* live = nullptr);
 // x[M, N] += A W^T (then + add_rows, then + add_vec); with next_gain also writes xg_out and
 // ps_out (N / 8 parts); x_save (with next_gain) receives x before add_rows and add_vec.
 hipError_t gemm_fold_add(const u16* A, const u16* Wp, int M, int N, int K, float* x, const u16* add_vec,
                          const u16* next_gain, u16* xg_out, float* ps_out, hipStream_t st,
-                         const float* add_rows = nullptr, float* x_save = nullptr);
+                         const float* add_rows = nullptr, float* x_save = nullptr, const int32_t* live = nullptr);
 // Row-major W [rows, K] -> lane-packed Wp (rows % 8 == 0, K % 64 == 0).
 hipError_t pack_weights(const u16* W, long long rows, int K, u16* Wp, hipStream_t st);
 // x += add (optional); xg = bf16(x * gain) (lane-packed); ps[0][r] = sum of x^2 of row r.
@@ -262,6 +265,10 @@ struct RowsAttn {
     float* d32;
     u16* d16;
     int d_rows;
+    // Decode-time loop skipping: *live == 0 (no sequence left in the loops) makes the
+    // two-segment sparse launch do only its new-token K/V write and the merge return at
+    // once.  nullptr: always run.
+    const int32_t* live;
 };
 enum { DIFF_NONE = 0, DIFF_ADD32, DIFF_SET32, DIFF_SUB32, DIFF_ADD16, DIFF_OUT16 };
 // Write loop-k reconstructions as float16 rows into kc [B*Hkv][ncap][hd] and

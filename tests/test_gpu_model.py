@@ -281,6 +281,29 @@ def test_decode_loop_skipping_matches_oracle(name, kw, extra, batch):
     check(r, f"loop skipping {name}")
 
 
+@pytest.mark.parametrize("kw,extra,batch", [(dict(n_loops=4), dict(), 2),
+                                             (dict(n_loops=3, n_heads=8, n_kv_heads=2, head_dim=128, d_model=512),
+                                              dict(diff_attn=True), 8)],
+                         ids=["hd64_b2", "hd128_diff_attn_b8"])
+def test_decode_every_sequence_leaves_the_loops(kw, extra, batch):
+    """A threshold above every key: each decode token leaves the loops after loop 1.
+    The folded decode's launches of loops >= 2 then return at once (only the new
+    token's carried K/V row is written, into the window ring and as -1 in the slot
+    map); outputs against the oracle, and no decode token holds a loop-k row."""
+    s = _small(**kw)
+    T, steps = 40, 4
+    lz = I.Lazy(mode="lazy", rho=0.3, top_s=12, window=8, base_bits=8, res_bits=4, skip_tau=1e30, **extra)
+    r = run_pair(s, lz, batch=batch, prompt=T, steps=steps, seed=7)
+    m, store = r["oracle"], r["store"]
+    assert set(m.decode_loops.values()) == {1}
+    v = store.view()
+    torch.cuda.synchronize()
+    sm = store_region(store, v.slot_maps, (s.n_loops - 1) * batch * v.row_stride * 4, torch.int32)
+    sm = sm.view(s.n_loops - 1, batch, v.row_stride)[:, :, T:T + steps].cpu().numpy()
+    assert (sm == -1).all()
+    check(r, "every sequence leaves")
+
+
 def test_refresh_every_loop_is_rho_one():
     """Refresh at every loop computes what rho = 1 computes: same selections (every
     token, ascending), same store layout; the outputs agree bit for bit."""
