@@ -114,7 +114,7 @@ def test_store_size_query_matches_closed_form(name):
 
 @pytest.mark.parametrize("field,value,code", [
     ("head_dim", 96, -2), ("n_kv_heads", 3, -1), ("n_shared", 0, -1), ("d_model", 100, -2),
-    ("n_loops", 0, -1), ("ffn_act", "relu", None),
+    ("n_loops", 0, -1), ("n_loops", 18, -2), ("ffn_act", "relu", None),
 ])
 def test_create_rejects_bad_model_configs(field, value, code):
     s = I.workload("tiny_1p2x2c1_t32").shape

@@ -304,6 +304,18 @@ def test_decode_every_sequence_leaves_the_loops(kw, extra, batch):
     check(r, "every sequence leaves")
 
 
+@pytest.mark.parametrize("extra", [dict(), dict(diff_attn=True, stale_keys=True)], ids=["lazy", "diff_stale"])
+def test_most_loops_matches_oracle(extra):
+    """The largest loop count a store takes (17 loops: 16 residual loops in the
+    per-row slot lists of the attention and gather kernels), prefill over a ragged
+    prompt and decode against the oracle; also with difference-corrected attention
+    and stale keys."""
+    s = _small(n_loops=17, n_shared=1)
+    lz = I.Lazy(mode="lazy", rho=0.3, top_s=12, window=8, base_bits=8, res_bits=4, **extra)
+    r = run_pair(s, lz, batch=2, prompt=70, steps=3, seed=7)
+    check(r, "17 loops")
+
+
 def test_refresh_every_loop_is_rho_one():
     """Refresh at every loop computes what rho = 1 computes: same selections (every
     token, ascending), same store layout; the outputs agree bit for bit."""
