@@ -70,13 +70,8 @@ not given on any page):
   Residual rows live in compact slots addressed by a per-(loop, sequence) slot
   map.  A decode token runs every loop and is always stored.
 
-Operand precision: by default every tensor is float32.  With
-``operand_precision="bf16"`` the oracle rounds (to nearest even) exactly the
-tensors that a bf16-operand implementation holds in bfloat16 -- the inputs of
-every projection GEMM (normed activations, attention output, FFN activation),
-the rotated queries and every K/V row kept at 16 bits -- and computes
-everything else in float32.  This measures how much of a bf16 implementation's
-distance from the float32 result is the rounding of its operands.
+Every tensor is float32; the GPU path's own roundings are its business and are
+held to the parity bound by the tests, not modelled here.
 """
 from __future__ import annotations
 
@@ -92,13 +87,6 @@ F32 = np.float32
 # ----------------------------------------------------------------------------
 # Building blocks
 # ----------------------------------------------------------------------------
-
-def round_bf16(x: np.ndarray) -> np.ndarray:
-    """Float32 values rounded to the nearest bfloat16 (ties to even), as float32."""
-    u = np.ascontiguousarray(x, dtype=F32).view(np.uint32).astype(np.uint64)
-    u = ((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
-    return u.view(F32).reshape(np.shape(x))
-
 
 def rmsnorm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
     x = np.asarray(x, dtype=F32)
@@ -161,6 +149,61 @@ def attend(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, cols_of, mass=None
     return out
 
 
+def attend_masked(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, pos: np.ndarray, allowed,
+                  mass=None, block: int = 256):
+    """``attend`` written as a masked softmax: query row i (at position pos[i], pos
+    ascending) over the key columns c <= max(pos) with ``allowed(p, c, g)`` true,
+    where p is a block of row positions [nb], c the column indices [nc] and the
+    result a boolean [nb, nc] (the row's column set as a mask; columns outside it
+    get score -inf, so probability 0).  Rows are taken ``block`` at a time as one
+    score matrix per KV head; per row this is the same softmax and products as
+    ``attend`` over the gathered columns, up to the summation order inside the
+    matrix products.  The block arithmetic runs as float32 PyTorch CPU operations
+    (multithreaded), which is what makes a 32k-token prompt affordable.  ``mass`` as
+    in ``attend``."""
+    import torch
+    n, H, hd = q.shape
+    Hkv = keys.shape[0]
+    G = H // Hkv
+    pos = np.asarray(pos, np.int64)
+    scale = float(F32(1.0 / np.sqrt(hd)))
+    out = np.empty((n, H, hd), dtype=F32)
+    qt = torch.from_numpy(np.ascontiguousarray(q, dtype=F32))
+    kt = torch.from_numpy(np.ascontiguousarray(keys, dtype=F32))
+    vt = torch.from_numpy(np.ascontiguousarray(vals, dtype=F32))
+    for g in range(Hkv):
+        for i0 in range(0, n, block):
+            i1 = min(n, i0 + block)
+            pb = pos[i0:i1]
+            nc = int(pb[-1]) + 1
+            ok = torch.from_numpy(np.ascontiguousarray(allowed(pb, np.arange(nc), g)))   # [nb, nc]
+            qb = qt[i0:i1, g * G:(g + 1) * G, :].reshape(-1, hd)                        # [nb*G, hd]
+            sc = (qb @ kt[g, :nc, :].T) * scale
+            sc = sc.view(i1 - i0, G, nc).masked_fill(~ok[:, None, :], float("-inf"))
+            m = sc.amax(dim=-1, keepdim=True)
+            p = torch.exp(sc - m)
+            p = p / p.sum(dim=-1, keepdim=True)
+            out[i0:i1, g * G:(g + 1) * G] = (p.view(-1, nc) @ vt[g, :nc, :]).view(i1 - i0, G, hd).numpy()
+            if mass is not None:
+                mass[g, :nc] += p.sum(dim=(0, 1)).numpy()
+    return out
+
+
+def causal_mask(p: np.ndarray, c: np.ndarray, g: int) -> np.ndarray:
+    """Column c is visible from position p when c <= p."""
+    return c[None, :] <= p[:, None]
+
+
+def sparse_mask(S: np.ndarray, window: int):
+    """Mask form of ``sparse_cols``: (S intersect [0, p]) union [p - window + 1, p]."""
+    def allowed(p, c, g):
+        inS = np.zeros(c.shape[0], bool)
+        s_g = S[g]
+        inS[s_g[s_g < c.shape[0]]] = True
+        return (c[None, :] <= p[:, None]) & (inS[None, :] | (c[None, :] > p[:, None] - window))
+    return allowed
+
+
 def causal_cols(i: int) -> np.ndarray:
     return np.arange(i + 1)
 
@@ -182,15 +225,11 @@ class LoopedOracle:
     ``decode(ids[B])`` appends one token per sequence and returns [B, d].
     """
 
-    def __init__(self, shape, lazy, weights, batch: int, max_tokens: int,
-                 operand_precision: str = "fp32", n_loops=None):
-        if operand_precision not in ("fp32", "bf16"):
-            raise ValueError("operand_precision must be fp32 or bf16")
+    def __init__(self, shape, lazy, weights, batch: int, max_tokens: int, n_loops=None):
         self.K = shape.n_loops if n_loops is None else int(n_loops)
         if not 1 <= self.K <= shape.n_loops:
             raise ValueError("n_loops must be in [1, shape.n_loops]")
         self.inject = bool(getattr(shape, "input_reinject", False))
-        self.bf16 = operand_precision == "bf16"
         self.s = shape
         self.lz = lazy
         self.w = weights
@@ -225,10 +264,6 @@ class LoopedOracle:
         self.T = None            # prompt length
         self.t = 0               # tokens held per sequence
         self._alloc()
-
-    def _rb(self, x):
-        """Round an operand to bf16 in bf16-operand mode (identity otherwise)."""
-        return round_bf16(x) if self.bf16 else x
 
     # ---------------------------------------------------------------- store
     def _alloc(self):
@@ -277,7 +312,7 @@ class LoopedOracle:
         """kvals/vvals [Hkv, n, hd] for positions ``rows``."""
         for kv, x in ((0, kvals), (1, vvals)):
             if self.lz.base_bits == 16:
-                self.base[r][kv][b][:, rows, :] = self._rb(x)
+                self.base[r][kv][b][:, rows, :] = x
             else:
                 if self.forced_codes_from is not None:
                     src = self.forced_codes_from.base[r][kv]
@@ -314,7 +349,7 @@ class LoopedOracle:
         for kv, x in ((0, kvals), (1, vvals)):
             store = self.res[(k, r, kv)]
             if self.lz.res_bits == 16:
-                store[b][:, slots, :] = self._rb(x)
+                store[b][:, slots, :] = x
             elif self.forced_codes_from is not None:
                 src = self.forced_codes_from.res[(k, r, kv)]
                 codes, sc = src[0][b][:, slots, :], src[1][b][:, slots, :]
@@ -330,23 +365,23 @@ class LoopedOracle:
     def _qkv(self, li, x, pos):
         s, W = self.s, self.w["layers"][li]
         n = x.shape[0]
-        a = self._rb(rmsnorm(x, W["attn_norm"], s.rms_eps))
+        a = rmsnorm(x, W["attn_norm"], s.rms_eps)
         q = (a @ W["wq"].T).reshape(n, s.n_heads, s.head_dim)
         k = (a @ W["wk"].T).reshape(n, s.n_kv_heads, s.head_dim)
         v = (a @ W["wv"].T).reshape(n, s.n_kv_heads, s.head_dim)
         cos, sin = rope_cos_sin(pos, s.head_dim, s.rope_theta)
-        return self._rb(apply_rope(q, cos, sin)), apply_rope(k, cos, sin), v.astype(F32)
+        return apply_rope(q, cos, sin), apply_rope(k, cos, sin), v.astype(F32)
 
     def _out_ffn(self, li, x, o):
         s, W = self.s, self.w["layers"][li]
         n = x.shape[0]
-        x = (x + self._rb(o.reshape(n, -1)) @ W["wo"].T).astype(F32)
-        b = self._rb(rmsnorm(x, W["ffn_norm"], s.rms_eps))
+        x = (x + o.reshape(n, -1) @ W["wo"].T).astype(F32)
+        b = rmsnorm(x, W["ffn_norm"], s.rms_eps)
         if s.ffn_act == "swiglu":
             f = silu(b @ W["w_gate"].T) * (b @ W["w_up"].T)
         else:
             f = gelu_erf(b @ W["w_up"].T)
-        return (x + self._rb(f.astype(F32)) @ W["w_down"].T).astype(F32)
+        return (x + f.astype(F32) @ W["w_down"].T).astype(F32)
 
     def _refresh(self, k: int) -> bool:
         """Loop k >= 2 recomputes every token (the refresh period divides k - 1)."""
@@ -423,10 +458,10 @@ class LoopedOracle:
 
     def _shared_dense(self, li, h, pos, kc, vc, b):
         q, k, v = self._qkv(li, h, pos)
-        kc[b][:, pos, :] = self._rb(k.transpose(1, 0, 2))
-        vc[b][:, pos, :] = self._rb(v.transpose(1, 0, 2))
+        kc[b][:, pos, :] = k.transpose(1, 0, 2)
+        vc[b][:, pos, :] = v.transpose(1, 0, 2)
         hi = int(pos.max()) + 1
-        o = attend(q, kc[b][:, :hi], vc[b][:, :hi], lambda i, g: causal_cols(int(pos[i])))
+        o = attend_masked(q, kc[b][:, :hi], vc[b][:, :hi], pos, causal_mask)
         self.depth += 1
         return self._out_ffn(li, h, o)
 
@@ -442,7 +477,7 @@ class LoopedOracle:
             kr = self.recon(1, r, b, 0, allc)
             vr = self.recon(1, r, b, 1, allc)
             mass = np.zeros((s.n_kv_heads, T), F32)
-            o = attend(q, kr, vr, lambda i, g: causal_cols(int(pos[i])), mass=mass)
+            o = attend_masked(q, kr, vr, pos, causal_mask, mass=mass)
             if self.forced_S is not None:
                 self.S[r][b] = [np.asarray(c, np.int32) for c in self.forced_S[r][b]]
             else:
@@ -497,7 +532,7 @@ class LoopedOracle:
     def _attend_sparse(self, q, kr, vr, rows, r, b):
         """Rows ``rows`` attend over their sparse column sets (each KV head has its own S)."""
         S, w = self.S[r][b], self.lz.window
-        return attend(q, kr, vr, lambda i, g: sparse_cols(int(rows[i]), S[g], w))
+        return attend_masked(q, kr, vr, rows, sparse_mask(S, w))
 
     def start_from_state(self, T: int, base, res, slot, S, dense_kv=None):
         """Take a lazy store state as a prefill of T tokens would leave it, built
@@ -594,7 +629,7 @@ class LoopedOracle:
                         self._base_write(r, b, pos, kt, vt)
                         kr = self.recon(1, r, b, 0, allc)
                         vr = self.recon(1, r, b, 1, allc)
-                        o = attend(q, kr, vr, lambda i, g: allc)
+                        o = attend_masked(q, kr, vr, pos, causal_mask)
                         if self.diff and K >= 2:
                             D[r] = (o - self._attend_sparse(q, kr, vr, pos, r, b)).astype(F32)
                     else:

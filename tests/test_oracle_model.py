@@ -19,7 +19,7 @@ import torch
 
 from cross_loop_kv_amd import inputs as I
 from oracle import accounting
-from oracle.model import LoopedOracle, apply_rope, attend, rope_cos_sin, round_bf16, sparse_cols
+from oracle.model import LoopedOracle, apply_rope, attend, rope_cos_sin, sparse_cols
 from tests import torch_ref
 
 
@@ -310,27 +310,6 @@ def test_column_mass_matches_library_softmax_sums():
     np.testing.assert_allclose(mass, ref, rtol=2e-5, atol=1e-6)
 
 
-def test_round_bf16_matches_library_conversion():
-    rng = np.random.default_rng(4)
-    x = (rng.standard_normal(100000) * 10 ** rng.uniform(-6, 6, 100000)).astype(np.float32)
-    # exact ties between bfloat16 neighbours, both parities
-    ties = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 3.0 * (1 + 2 ** -8)], np.float32)
-    x = np.concatenate([x, ties, np.zeros(1, np.float32)])
-    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
-    np.testing.assert_array_equal(round_bf16(x), ref)
-
-
-def test_bf16_operand_mode_is_a_small_perturbation():
-    s = small_shape()
-    W = I.gen_weights(s, seed=17)
-    ids = I.gen_prompt_ids(s, 1, 24, seed=18)
-    out = {}
-    for prec in ("fp32", "bf16"):
-        m = LoopedOracle(s, I.Lazy(mode="per_loop"), W, 1, 24, operand_precision=prec)
-        out[prec] = m.prefill(ids)
-    assert 1e-5 < max_abs_rel(out["bf16"], out["fp32"]) < 3e-2
-
-
 def test_forced_codes_reproduce_the_source_oracle():
     """An oracle that takes another oracle's selections and codes reproduces it exactly."""
     s = small_shape()
@@ -350,3 +329,35 @@ def test_forced_codes_reproduce_the_source_oracle():
     np.testing.assert_array_equal(oa, ob)
     for x, y in zip(da, db):
         np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("rows,sparse", [("all", False), ("all", True), ("subset", True)])
+def test_masked_attention_equals_row_by_row_attention(rows, sparse):
+    """The masked, block-at-a-time form the model uses (attend_masked) gives the
+    row-by-row gathered softmax (attend) for every row, several blocks and a ragged
+    last block, dense causal or sparse (stable columns plus a window), with the
+    column mass; only the summation order inside the products differs."""
+    from oracle.model import attend_masked, causal_mask, sparse_mask
+    rng = np.random.default_rng(23)
+    T, H, Hkv, hd, w = 300, 4, 2, 32, 7
+    q = rng.standard_normal((T, H, hd)).astype(np.float32)
+    K = (rng.standard_normal((Hkv, T, hd)) * 2).astype(np.float32)
+    V = rng.standard_normal((Hkv, T, hd)).astype(np.float32)
+    S = [np.sort(rng.choice(T, 40, replace=False)).astype(np.int32) for _ in range(Hkv)]
+    pos = np.arange(T) if rows == "all" else np.sort(rng.choice(T, 90, replace=False))
+    if sparse:
+        allowed = sparse_mask(S, w)
+        cols_of = lambda i, g: sparse_cols(int(pos[i]), S[g], w)
+    else:
+        allowed = causal_mask
+        cols_of = lambda i, g: np.arange(int(pos[i]) + 1)
+    m1, m2 = np.zeros((Hkv, T), np.float32), np.zeros((Hkv, T), np.float32)
+    a = attend_masked(q[pos], K, V, pos, allowed, mass=m1, block=64)
+    b = attend(q[pos], K, V, cols_of, mass=m2)
+    assert np.max(np.abs(a - b)) <= 1e-5 * np.max(np.abs(b))
+    assert np.max(np.abs(m1 - m2)) <= 1e-5 * np.max(np.abs(m2))
+    # the mask is exactly the gathered column set
+    for i in range(0, len(pos), 17):
+        for g in range(Hkv):
+            got = np.nonzero(allowed(pos[i:i + 1], np.arange(int(pos[i]) + 1), g)[0])[0]
+            assert np.array_equal(got, cols_of(i, g))
