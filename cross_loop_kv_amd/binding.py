@@ -58,8 +58,22 @@ class lk_store_view(C.Structure):
                 ("base_scales", C.c_void_p), ("res_codes", C.c_void_p), ("res_scales", C.c_void_p),
                 ("slot_maps", C.c_void_p), ("columns", C.c_void_p), ("slots", C.c_int64),
                 ("n_selected", C.c_int32), ("n_columns", C.c_int32), ("res_row_bytes", C.c_int64),
-                ("row_stride", C.c_int32)]
+                ("row_stride", C.c_int32), ("decode_cache", C.c_void_p), ("cache_rows", C.c_int32),
+                ("ring_rows", C.c_int32), ("first_cached_loop", C.c_int32)]
 
+
+class lk_dbg_attn_args(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("B", C.c_int32), ("H", C.c_int32), ("Hkv", C.c_int32), ("hd", C.c_int32),
+                ("kv_format", C.c_int32), ("t", C.c_int32), ("T", C.c_int32), ("tmax", C.c_int32),
+                ("q", C.c_void_p), ("q_half", C.c_int32), ("k", C.c_void_p), ("v", C.c_void_p),
+                ("k_scales", C.c_void_p), ("v_scales", C.c_void_p), ("cols", C.c_void_p),
+                ("n_cols", C.c_int32), ("window", C.c_int32), ("s_k", C.c_void_p), ("s_v", C.c_void_p),
+                ("s_cap", C.c_int32), ("r_k", C.c_void_p), ("r_v", C.c_void_p), ("r_cap", C.c_int32),
+                ("qpos", C.c_void_p), ("n_rows", C.c_int32), ("out", C.c_void_p), ("out32", C.c_void_p),
+                ("lse", C.c_void_p), ("mass", C.c_void_p), ("ws", C.c_void_p), ("ws_bytes", C.c_size_t)]
+
+
+DBG_ATTN = {"decode": 0, "decode_seg": 1, "prefill": 2, "mass": 3, "prefill_sparse": 4}
 
 SNAPSHOT_MAGIC = 0x313050414E534B4C   # bytes "LKSNAP01"
 SNAPSHOT_VERSION = 2
@@ -112,6 +126,9 @@ _SIGS = {
                               C.c_void_p]),
     "lk_dbg_gemm_epi": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32,
                                   C.c_int32, C.c_int32, C.c_void_p]),
+    "lk_dbg_attention": (C.c_int, [C.POINTER(lk_dbg_attn_args), C.POINTER(C.c_size_t), C.c_void_p]),
+    "lk_dbg_kv_write": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p,
+                                  C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -288,6 +305,20 @@ def lk_dbg_gemm(d_a, d_w, d_c, M, N, K, stream=None) -> None:
 
 def lk_dbg_gemm_epi(d_a, d_w, epi, d_c, d_out, M, N, K, stream=None) -> None:
     _check(lib().lk_dbg_gemm_epi(d_a, d_w, epi, d_c, d_out, M, N, K, _stream(stream)))
+
+
+def lk_dbg_attention(args: lk_dbg_attn_args, stream=None) -> int:
+    """Runs the kind's kernels (args.ws set) or returns the workspace bytes it needs
+    (args.ws None)."""
+    need = C.c_size_t()
+    _check(lib().lk_dbg_attention(C.byref(args), C.byref(need), _stream(stream)))
+    return need.value
+
+
+def lk_dbg_kv_write(s, layer, loop, d_qkv, rows_per_seq, d_pos, d_q_out, q_half, d_ws=None, ws_bytes=0,
+                    stream=None) -> None:
+    _check(lib().lk_dbg_kv_write(s, layer, loop, d_qkv, rows_per_seq, d_pos, d_q_out, 1 if q_half else 0,
+                                 d_ws, ws_bytes, _stream(stream)))
 
 
 # ---- model / store objects (device memory from torch) ----------------------------------

@@ -8,7 +8,8 @@
 // Scores are kept in log2 units (q.k * log2(e) / sqrt(hd)) everywhere, so that the
 // split partials (m, l, o) of every kernel combine the same way.
 //
-// * attn_prefill: causal flash attention with v_mfma_f32_32x32x16_bf16.  Scores
+// * attn_prefill: causal flash attention with v_mfma_f32_32x32x16 (bf16 operands over
+//   bf16 rows; float16 over int8 rows, whose codes times scales are rounded once).  Scores
 //   are formed transposed (S^T = K Q^T) so every lane owns one query column and
 //   the softmax statistics stay per lane (lanes l and l+32 share a query).  The
 //   K rows of a tile are staged in LDS in a permuted order chosen so that each
@@ -39,6 +40,29 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(half8, v); }
 
+// Operand type of the prefill kernels: float16 over int8 rows (code * scale rounded
+// once to float16; q converted from bf16, exact inside the float16 range) and bf16
+// over bf16 rows.  Eight operand elements travel as one uint4.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_op2(float a, float b) {
+    if constexpr (F16) return (uint32_t)f2h_bits(a) | ((uint32_t)f2h_bits(b) << 16);
+    else return pack_bf2(a, b);
+}
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
+    if constexpr (F16) return __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(a), as_half8(b), c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+// Eight bf16 values as float16 (exact for magnitudes in the float16 normal range).
+__device__ __forceinline__ uint4 bf8_to_h8(uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        o[t] = (uint32_t)f2h_bits(__uint_as_float(w[t] << 16)) | ((uint32_t)f2h_bits(__uint_as_float(w[t] & 0xFFFF0000u)) << 16);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // 8 signed bytes -> 8 float16 (exact), multiplied by per-pair scales (packed f16).
 // Byte j of the input becomes element j.  Each byte is biased to u = c + 128 and
 // placed under the float16 exponent of 1024 (bits 0x64uu = 1024 + u); subtracting
@@ -62,9 +86,10 @@ __device__ __forceinline__ uint4 i8x8_to_f16(uint2 c, uint4 scale_pairs) {
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// 8 consecutive K elements of row (b, g, pos) as bf16 (dequantized if int8).
+// 8 consecutive K elements of row (b, g, pos) as operands: bf16 rows as they are, int8
+// codes times their group scale as float16.
 template <int HD, bool I8>
-__device__ __forceinline__ uint4 load_k8_bf16(const KVLayer& kv, int b, int g, int pos, int e0) {
+__device__ __forceinline__ uint4 load_k8(const KVLayer& kv, int b, int g, int pos, int e0) {
     const long long row = kv_row(kv, b, g, pos);
     if (!I8) return *(const uint4*)((const u16*)kv.base[0] + row * HD + e0);
     const uint2 c = *(const uint2*)((const int8_t*)kv.base[0] + row * HD + e0);
@@ -75,7 +100,7 @@ __device__ __forceinline__ uint4 load_k8_bf16(const KVLayer& kv, int b, int g, i
     for (int q = 0; q < 4; ++q) {
         const uint32_t word = wv[q >> 1];
         const int sh = (q & 1) * 16;
-        o[q] = pack_bf2((float)(int8_t)((word >> sh) & 0xFF) * s, (float)(int8_t)((word >> (sh + 8)) & 0xFF) * s);
+        o[q] = pack_op2<true>((float)(int8_t)((word >> sh) & 0xFF) * s, (float)(int8_t)((word >> (sh + 8)) & 0xFF) * s);
     }
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
@@ -92,9 +117,10 @@ __device__ __forceinline__ uint4 mask_tail8(uint4 v, int valid) {
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Eight keys [pos0, pos0+8) of V at head dim e as bf16 (pos0 multiple of 8), keys >= valid zeroed.
+// Eight keys [pos0, pos0+8) of V at head dim e as operands (pos0 a multiple of 8; bf16
+// rows, or int8 codes times scales as float16), keys >= valid zeroed.
 template <int HD, bool I8>
-__device__ __forceinline__ uint4 load_v8_bf16(const KVLayer& kv, int b, int g, int pos0, int e, int valid) {
+__device__ __forceinline__ uint4 load_v8(const KVLayer& kv, int b, int g, int pos0, int e, int valid) {
     const long long idx = v_elem(kv, b, g, pos0, e);
     uint4 out;
     if (!I8) {
@@ -108,8 +134,8 @@ __device__ __forceinline__ uint4 load_v8_bf16(const KVLayer& kv, int b, int g, i
         for (int q = 0; q < 4; ++q) {
             const uint32_t word = wv[q >> 1];
             const int sh = (q & 1) * 16;
-            o[q] = pack_bf2((float)(int8_t)((word >> sh) & 0xFF) * h2f(sp[2 * q]),
-                            (float)(int8_t)((word >> (sh + 8)) & 0xFF) * h2f(sp[2 * q + 1]));
+            o[q] = pack_op2<true>((float)(int8_t)((word >> sh) & 0xFF) * h2f(sp[2 * q]),
+                                  (float)(int8_t)((word >> (sh + 8)) & 0xFF) * h2f(sp[2 * q + 1]));
         }
         out = make_uint4(o[0], o[1], o[2], o[3]);
     }
@@ -146,12 +172,12 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const u16* __restrict
     const int qi = q0 + l32;
     const long long ldq = (long long)H * HD;
 
-    bf16x8 qf[HD / 16];
+    uint4 qf[HD / 16];
 #pragma unroll
     for (int ks = 0; ks < HD / 16; ++ks) {
         uint4 v = make_uint4(0, 0, 0, 0);
         if (qi < T) v = *(const uint4*)(Q + ((long long)b * T + qi) * ldq + h * HD + ks * 16 + kg * 8);
-        qf[ks] = as_bf16x8(v);
+        qf[ks] = I8 ? bf8_to_h8(v) : v;
     }
     f32x16 oacc[HD / 32];
 #pragma unroll
@@ -170,12 +196,12 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const u16* __restrict
             regs[p] = make_uint4(0, 0, 0, 0);
             if (c < NKC) {
                 const int key = t * KT + flash_key_of_row(c / CPR);
-                if (key < T) regs[p] = load_k8_bf16<HD, I8>(kv, b, g, key, (c % CPR) * 8);
+                if (key < T) regs[p] = load_k8<HD, I8>(kv, b, g, key, (c % CPR) * 8);
             } else if (c < NKC + NVC) {
                 const int cc = c - NKC;
                 const int blk = cc / HD, e = cc % HD;
                 const int pos0 = t * KT + blk * 8;
-                if (pos0 < T) regs[p] = load_v8_bf16<HD, I8>(kv, b, g, pos0, e, T - pos0);
+                if (pos0 < T) regs[p] = load_v8<HD, I8>(kv, b, g, pos0, e, T - pos0);
             }
         }
     };
@@ -204,8 +230,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const u16* __restrict
             for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < HD / 16; ++ks) {
-                const bf16x8 a = as_bf16x8(*(const uint4*)&Ks[cur][l32 * LDK + ks * 16 + kg * 8]);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
+                s = mfma32<I8>(*(const uint4*)&Ks[cur][l32 * LDK + ks * 16 + kg * 8], qf[ks], s);
             }
             float mx = -INFINITY;
 #pragma unroll
@@ -232,23 +257,20 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const u16* __restrict
             for (int c = 0; c < HD / 32; ++c)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[c][i] *= alpha;
-            uint4 pu0, pu1;
-            pu0.x = pack_bf2(p[0], p[1]);
-            pu0.y = pack_bf2(p[2], p[3]);
-            pu0.z = pack_bf2(p[4], p[5]);
-            pu0.w = pack_bf2(p[6], p[7]);
-            pu1.x = pack_bf2(p[8], p[9]);
-            pu1.y = pack_bf2(p[10], p[11]);
-            pu1.z = pack_bf2(p[12], p[13]);
-            pu1.w = pack_bf2(p[14], p[15]);
-            const bf16x8 pb0 = as_bf16x8(pu0), pb1 = as_bf16x8(pu1);
+            uint4 pb0, pb1;
+            pb0.x = pack_op2<I8>(p[0], p[1]);
+            pb0.y = pack_op2<I8>(p[2], p[3]);
+            pb0.z = pack_op2<I8>(p[4], p[5]);
+            pb0.w = pack_op2<I8>(p[6], p[7]);
+            pb1.x = pack_op2<I8>(p[8], p[9]);
+            pb1.y = pack_op2<I8>(p[10], p[11]);
+            pb1.z = pack_op2<I8>(p[12], p[13]);
+            pb1.w = pack_op2<I8>(p[14], p[15]);
 #pragma unroll
             for (int c = 0; c < HD / 32; ++c) {
                 const u16* vrow = &Vt[cur][(c * 32 + l32) * LDV];
-                const bf16x8 va0 = as_bf16x8(*(const uint4*)(vrow + 8 * kg));
-                const bf16x8 va1 = as_bf16x8(*(const uint4*)(vrow + 16 + 8 * kg));
-                oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pb0, oacc[c], 0, 0, 0);
-                oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pb1, oacc[c], 0, 0, 0);
+                oacc[c] = mfma32<I8>(*(const uint4*)(vrow + 8 * kg), pb0, oacc[c]);
+                oacc[c] = mfma32<I8>(*(const uint4*)(vrow + 16 + 8 * kg), pb1, oacc[c]);
             }
         }
         if (t + 1 < ntiles) store_tile(cur ^ 1);
@@ -300,12 +322,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_fa_kernel(const u16* __re
     const int qi = q0 + l32;
     const long long ldq = (long long)H * HD;
 
-    bf16x8 qf[HD / 16];
+    uint4 qf[HD / 16];
 #pragma unroll
     for (int ks = 0; ks < HD / 16; ++ks) {
         uint4 v = make_uint4(0, 0, 0, 0);
         if (qi < T) v = *(const uint4*)(Q + ((long long)b * T + qi) * ldq + h * HD + ks * 16 + kg * 8);
-        qf[ks] = as_bf16x8(v);
+        qf[ks] = I8 ? bf8_to_h8(v) : v;
     }
     f32x16 oacc[HD / 32];
 #pragma unroll
@@ -325,12 +347,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_fa_kernel(const u16* __re
             if (c < NKC) {
                 const int r = c / CPR;
                 const int key = t * KT + (r & 32) + flash_key_of_row(r & 31);
-                if (key < T) regs[p] = load_k8_bf16<HD, I8>(kv, b, g, key, (c % CPR) * 8);
+                if (key < T) regs[p] = load_k8<HD, I8>(kv, b, g, key, (c % CPR) * 8);
             } else {
                 const int cc = c - NKC;
                 const int blk = cc / HD, e = cc % HD;
                 const int pos0 = t * KT + blk * 8;
-                if (pos0 < T) regs[p] = load_v8_bf16<HD, I8>(kv, b, g, pos0, e, T - pos0);
+                if (pos0 < T) regs[p] = load_v8<HD, I8>(kv, b, g, pos0, e, T - pos0);
             }
         }
     };
@@ -361,8 +383,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_fa_kernel(const u16* __re
                 for (int i = 0; i < 16; ++i) sc[hh][i] = 0.f;
 #pragma unroll
                 for (int ks = 0; ks < HD / 16; ++ks) {
-                    const bf16x8 a = as_bf16x8(*(const uint4*)&Ks[cur][(32 * hh + l32) * LDK + ks * 16 + kg * 8]);
-                    sc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sc[hh], 0, 0, 0);
+                    sc[hh] = mfma32<I8>(*(const uint4*)&Ks[cur][(32 * hh + l32) * LDK + ks * 16 + kg * 8], qf[ks], sc[hh]);
                 }
             }
             // causal / length mask only where the tile reaches the diagonal or the end
@@ -394,7 +415,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_fa_kernel(const u16* __re
             m_i = m_new;
             const float nm = -m_new;
             float rs = 0.f;
-            bf16x8 pb[2][2];
+            uint4 pb[2][2];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 float p[16];
@@ -404,16 +425,16 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_fa_kernel(const u16* __re
                     rs += p[i];
                 }
                 uint4 pu0, pu1;
-                pu0.x = pack_bf2(p[0], p[1]);
-                pu0.y = pack_bf2(p[2], p[3]);
-                pu0.z = pack_bf2(p[4], p[5]);
-                pu0.w = pack_bf2(p[6], p[7]);
-                pu1.x = pack_bf2(p[8], p[9]);
-                pu1.y = pack_bf2(p[10], p[11]);
-                pu1.z = pack_bf2(p[12], p[13]);
-                pu1.w = pack_bf2(p[14], p[15]);
-                pb[hh][0] = as_bf16x8(pu0);
-                pb[hh][1] = as_bf16x8(pu1);
+                pu0.x = pack_op2<I8>(p[0], p[1]);
+                pu0.y = pack_op2<I8>(p[2], p[3]);
+                pu0.z = pack_op2<I8>(p[4], p[5]);
+                pu0.w = pack_op2<I8>(p[6], p[7]);
+                pu1.x = pack_op2<I8>(p[8], p[9]);
+                pu1.y = pack_op2<I8>(p[10], p[11]);
+                pu1.z = pack_op2<I8>(p[12], p[13]);
+                pu1.w = pack_op2<I8>(p[14], p[15]);
+                pb[hh][0] = pu0;
+                pb[hh][1] = pu1;
             }
             rs += __shfl_xor(rs, 32);
             l_i += rs;
@@ -422,10 +443,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_fa_kernel(const u16* __re
 #pragma unroll
                 for (int c = 0; c < HD / 32; ++c) {
                     const u16* vrow = &Vt[cur][(c * 32 + l32) * LDV + 32 * hh];
-                    const bf16x8 va0 = as_bf16x8(*(const uint4*)(vrow + 8 * kg));
-                    const bf16x8 va1 = as_bf16x8(*(const uint4*)(vrow + 16 + 8 * kg));
-                    oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pb[hh][0], oacc[c], 0, 0, 0);
-                    oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pb[hh][1], oacc[c], 0, 0, 0);
+                    oacc[c] = mfma32<I8>(*(const uint4*)(vrow + 8 * kg), pb[hh][0], oacc[c]);
+                    oacc[c] = mfma32<I8>(*(const uint4*)(vrow + 16 + 8 * kg), pb[hh][1], oacc[c]);
                 }
         }
         if (t + 1 < ntiles) store_tile(cur ^ 1);
@@ -462,14 +481,14 @@ __global__ __launch_bounds__(256) void column_mass_kernel(const u16* __restrict_
     const int kblk = blockIdx.x * 128;
     const int j0 = kblk + w * 32;
     const long long ldq = (long long)H * HD;
-    bf16x8 kf[HD / 16];
+    uint4 kf[HD / 16];
     {
         const int key = j0 + l32;
 #pragma unroll
         for (int ks = 0; ks < HD / 16; ++ks) {
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (key < T) v = load_k8_bf16<HD, I8>(kv, b, g, key, ks * 16 + kg * 8);
-            kf[ks] = as_bf16x8(v);
+            if (key < T) v = load_k8<HD, I8>(kv, b, g, key, ks * 16 + kg * 8);
+            kf[ks] = v;
         }
     }
     float cs[16];
@@ -485,7 +504,7 @@ __global__ __launch_bounds__(256) void column_mass_kernel(const u16* __restrict_
                 const int q = qt * 32 + r;
                 uint4 v = make_uint4(0, 0, 0, 0);
                 if (q < T) v = *(const uint4*)(Q + ((long long)b * T + q) * ldq + h * HD + ch * 8);
-                *(uint4*)&Qs[r * LDQ + ch * 8] = v;
+                *(uint4*)&Qs[r * LDQ + ch * 8] = I8 ? bf8_to_h8(v) : v;
             }
             __syncthreads();
             if (qt * 32 + 31 < j0) continue;
@@ -494,8 +513,7 @@ __global__ __launch_bounds__(256) void column_mass_kernel(const u16* __restrict_
             for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < HD / 16; ++ks) {
-                const bf16x8 bq = as_bf16x8(*(const uint4*)&Qs[l32 * LDQ + ks * 16 + kg * 8]);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], bq, s, 0, 0, 0);
+                s = mfma32<I8>(kf[ks], *(const uint4*)&Qs[l32 * LDQ + ks * 16 + kg * 8], s);
             }
             const int q = qt * 32 + l32;
             if (q < T) {
@@ -599,7 +617,7 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (hvalid && a.fuse_kv) {  // rotate the float32 projection here (bf16 result)
+        if (hvalid && a.fuse_kv) {  // rotate the float32 projection here
             // the 8 elements e0.. are pairs i0.. (one half of the head): 16-byte loads
             const int e0 = kslice(j), i0 = e0 % (HD / 2);
             const float* qh = a.qkv + (long long)b * (a.H + 2 * Hkv) * HD + (g * G + c16) * HD;
@@ -620,15 +638,16 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
                 for (int u = 0; u < 2; ++u) {
                     const int m = 2 * t + u;
                     const float c = cs[2 * m], sn = cs[2 * m + 1];
-                    r2[u] = lo ? x1[m] * c - x2[m] * sn : x2[m] * c + x1[m] * sn;
+                    r2[u] = lo ? rope_lo(x1[m], x2[m], c, sn) : rope_hi(x1[m], x2[m], c, sn);
                 }
-                o[t] = pack_bf2(r2[0], r2[1]);
+                // the float16 kernels take the rotated float32 q with one rounding
+                o[t] = HALF ? ((uint32_t)f2h_bits(r2[0]) | ((uint32_t)f2h_bits(r2[1]) << 16)) : pack_bf2(r2[0], r2[1]);
             }
             v = make_uint4(o[0], o[1], o[2], o[3]);
         } else if (hvalid) {
             v = *(const uint4*)(a.q + (long long)b * a.H * HD + (g * G + c16) * HD + kslice(j));
         }
-        if (HALF) {  // bf16 -> f16
+        if (HALF && !a.fuse_kv && !a.q_half) {  // bf16 -> f16
             const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
             uint32_t o[4];
 #pragma unroll
@@ -1516,11 +1535,16 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
         const int k = head * HD + e;
         const long long oi = packed ? pk_index((int)qrow, k, H * HD) : qrow * H * HD + k;
         const long long di = qrow * H * HD + k;
+        // packed (decode products): a hi/lo bf16 pair, lo 8 H hd elements on
+        auto put = [&](float y) {
+            if (packed) split_bf2(y, &out[oi], &out[8LL * H * HD + oi]);
+            else out[oi] = f2bf(y);
+        };
         switch (df.mode) {
-            case DIFF_ADD32: out[oi] = f2bf(o + df.d32[di]); break;
+            case DIFF_ADD32: put(o + df.d32[di]); break;
             case DIFF_SET32:
                 df.d32[di] = o;
-                out[oi] = f2bf(o);
+                put(o);
                 break;
             case DIFF_SUB32: df.d32[di] -= o; break;
             case DIFF_ADD16:
@@ -1531,7 +1555,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
                 else df.d16[ri] = f2h_bits(bf2f(out[oi]) - o);
                 break;
             }
-            default: out[oi] = f2bf(o); break;
+            default: put(o); break;
         }
     }
 }

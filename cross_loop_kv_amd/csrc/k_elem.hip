@@ -21,7 +21,8 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(const int32_t* ids, con
     for (int j = threadIdx.x; j < d; j += kThreads) dst[j] = bf2f(tok[src + j]);
 }
 
-// x += add (optional); xg = bf16(x * gain); ps[r] = sum of x^2 over the row.
+// x += add (optional); xg = x * gain as a lane-packed hi/lo bf16 pair (hi at xg, lo at
+// xg + 8 d); ps[r] = sum of x^2 over the row.
 __global__ __launch_bounds__(kThreads) void norm_prep_kernel(float* x, const u16* add, const u16* gain, int d,
                                                              u16* xg, float* ps) {
     __shared__ float red[16];
@@ -34,7 +35,8 @@ __global__ __launch_bounds__(kThreads) void norm_prep_kernel(float* x, const u16
             v = v + bf2f(add[j]);
             row[j] = v;
         }
-        xg[pk_index(r, j, d)] = f2bf(v * bf2f(gain[j]));
+        const long long pi = pk_index(r, j, d);
+        split_bf2(v * bf2f(gain[j]), &xg[pi], &xg[8LL * d + pi]);
         ss += v * v;
     }
     ss = block_sum(ss, red);
@@ -306,7 +308,7 @@ namespace {
 __global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, int rows_per_seq,
                                                             const int32_t* pos_arr, int pos_offset,
                                                             int H, int Hkv, int hd, InvFreq inv,
-                                                            u16* q_out, KVWrite w) {
+                                                            u16* q_out, int q_half, KVWrite w) {
     const int r = blockIdx.x, u = blockIdx.y, t = threadIdx.x;
     const int b = r / rows_per_seq;
     const int iseq = r % rows_per_seq;
@@ -331,8 +333,9 @@ __global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, in
         }
         const float x1 = src[hh * hd + i], x2 = src[hh * hd + i + half];
         u16* dq = q_out + (long long)r * H * hd + hh * hd;
-        dq[i] = f2bf(x1 * c - x2 * sn);
-        dq[i + half] = f2bf(x2 * c + x1 * sn);
+        const float r1 = rope_lo(x1, x2, c, sn), r2 = rope_hi(x1, x2, c, sn);
+        dq[i] = q_half ? f2h_bits(r1) : f2bf(r1);
+        dq[i + half] = q_half ? f2h_bits(r2) : f2bf(r2);
         return;
     }
     const int kv = (u - nq) / Hkv, g = (u - nq) % Hkv;
@@ -476,13 +479,13 @@ hipError_t rope_angles(const int32_t* dpos, const double* inv_freq, int hd, floa
 
 hipError_t rope_kv_write(const float* qkv, int rows, int rows_per_seq, const int32_t* pos, int pos_offset,
                          int H, int Hkv, int hd, const double* inv_freq, u16* q_out, const KVWrite& kvw,
-                         hipStream_t st) {
+                         hipStream_t st, int q_half) {
     InvFreq inv;
     for (int i = 0; i < hd / 2; ++i) inv.v[i] = inv_freq[i];
     const int qpb = 256 / hd;
     const int units = (H + qpb - 1) / qpb + 2 * Hkv;
     hipLaunchKernelGGL(rope_kv_write_kernel, dim3(rows, units), dim3(128), 0, st, qkv, rows_per_seq, pos,
-                       pos_offset, H, Hkv, hd, inv, q_out, kvw);
+                       pos_offset, H, Hkv, hd, inv, q_out, q_half, kvw);
     return hipGetLastError();
 }
 

@@ -254,11 +254,14 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(const u16* __restrict_
 // Requires M <= 8 and K % 64 == 0.  Wave w takes the 32-element k chunks c = w, w + 8,
 // ... of each half, NL chunks per batch of loads.
 //
-// NORM (RMSNorm folded in): A holds bf16(x * gain) and ps_in [nparts][8] partial sums
-// of x^2 per row; the product is scaled by 1 / sqrt(sum / K + eps).
+// PK (lane-packed operands, the decode products): A is a hi/lo pair of bf16 operands,
+// hi at A and lo at A + 8 K (x = hi + lo to 2^-16), and the bf16 outputs (xg_out, Obf)
+// are written the same way; otherwise A and the outputs are plain bf16, row-major.
+// NORM (RMSNorm folded in): A holds x * gain and ps_in [nparts][8] partial sums of x^2
+// per row; the product is scaled by 1 / sqrt(sum / K + eps).
 // PREP (with EPI_ADD): besides x += A W^T (+ add_vec), write what the next NORM
-// product needs: xg_out = bf16(x * next_gain) and, per workgroup, the row sums of x^2
-// over its 8 columns into ps_out [N / 8][8].
+// product needs: xg_out = x * next_gain and, per workgroup, the row sums of x^2 over
+// its 8 columns into ps_out [N / 8][8].
 template <int EPI, int NL, bool NORM, bool PREP, bool PK, bool LIVE>
 __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ A, const u16* __restrict__ W,
                                                         int M, int N, int K, float* __restrict__ C,
@@ -308,9 +311,12 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
         if (PREP && io.add_vec) addv = bf2f(io.add_vec[col]);
         if (PREP) gainv = bf2f(io.next_gain[col]);
     }
+    // PK: the activation is a hi/lo bf16 pair (lo at A + 8 K); both halves meet the same
+    // weight operand, so the product carries the float32 activation to 2^-16.
+    const long long lo_off = 8LL * K;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = w; c0 < nch; c0 += NWV * NL) {
-        uint4 wv[NL], wv1[NL], av[NL];
+        uint4 wv[NL], wv1[NL], av[NL], al[NL];
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             const int c = c0 + j * NWV;
@@ -321,13 +327,19 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             const int c = c0 + j * NWV;
-            av[j] = (c < nch && mvalid) ? *(const uint4*)(ar + (long long)c * wstep) : make_uint4(0, 0, 0, 0);
+            const bool ok = c < nch && mvalid;
+            av[j] = ok ? *(const uint4*)(ar + (long long)c * wstep) : make_uint4(0, 0, 0, 0);
+            if (PK) al[j] = ok ? *(const uint4*)(ar + lo_off + (long long)c * wstep) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[j]), as_bf16x8(wv[j]), acc0, 0, 0, 0);
-            if (DUAL)
+            if (PK) acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al[j]), as_bf16x8(wv[j]), acc0, 0, 0, 0);
+            if (DUAL) {
                 acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[j]), as_bf16x8(wv1[j]), acc1, 0, 0, 0);
+                if (PK)
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al[j]), as_bf16x8(wv1[j]), acc1, 0, 0, 0);
+            }
         }
     }
     if (norm_wave) {  // wave w: row w's sum of squares, partials in a fixed order
@@ -373,13 +385,22 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
             if (PREP && io.add_vec) x = x + addv;
             C[o] = x;
             if (PREP) {
-                io.xg_out[PK ? pk_index(m, col, N) : o] = f2bf(x * gainv);
+                if (PK) {
+                    const long long pi = pk_index(m, col, N);
+                    split_bf2(x * gainv, &io.xg_out[pi], &io.xg_out[8LL * N + pi]);
+                } else {
+                    io.xg_out[o] = f2bf(x * gainv);
+                }
                 sq[i] = x * x;
             }
-        } else if (EPI == EPI_SWIGLU) {
-            Obf[PK ? pk_index(m, col, N) : o] = f2bf(silu_f(v0) * ((s1[i] + o1[i]) * inv));
         } else {
-            Obf[PK ? pk_index(m, col, N) : o] = f2bf(gelu_f(v0));
+            const float y = EPI == EPI_SWIGLU ? silu_f(v0) * ((s1[i] + o1[i]) * inv) : gelu_f(v0);
+            if (PK) {
+                const long long pi = pk_index(m, col, N);
+                split_bf2(y, &Obf[pi], &Obf[8LL * N + pi]);
+            } else {
+                Obf[o] = f2bf(y);
+            }
         }
     }
     if (PREP) {

@@ -56,6 +56,18 @@ int n_selected(double rho, int T) {
 // Columns per split and the split-count ceiling of the row-attention kernel.
 constexpr int kRowChunk = 256;
 constexpr int kMaxSplits = 256;
+// Rows per split of the two-segment decode attention (stable-column cache, window ring).
+constexpr int kSegChunk = 128;
+
+// Dense decode attention over ncol keys of `pairs` (sequence, KV head) pairs: one
+// workgroup per (pair, chunk), about 768 workgroups (three per CU; longer chunks keep
+// each wave streaming longer).
+int decode_dense_chunk(long long pairs, long long ncol) {
+    const long long want = (ncol * pairs + 767) / 768;
+    int ch = (int)std::max(128LL, (want + 127) / 128 * 128);
+    while ((ncol + ch - 1) / ch > kMaxSplits) ch *= 2;
+    return ch;
+}
 
 }  // namespace
 
@@ -403,13 +415,15 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
     w.h = (float*)take(M * d * 4);
     w.h0 = (float*)take(hd_->lazy() || c.input_reinject ? M * d * 4 : 0);
     w.xc = (float*)take(hd_->lazy() ? (long long)B * n * d * 4 : 0);
-    // bf16 operands of the decode products are lane-packed over 8 rows: at least 8 rows
+    // bf16 operands of the decode products are lane-packed over 8 rows (at least 8 rows)
+    // and held as hi/lo pairs (twice the elements)
     const long long M8 = M < 8 ? 8 : M;
-    w.xn = (u16*)take(M8 * d * 2);
+    const long long pair = T == 1 ? 2 : 1;
+    w.xn = (u16*)take(pair * M8 * d * 2);
     w.qkv = (float*)take(M * hd_->qkv_w() * 4);
     w.q = (u16*)take(M * Hhd * 2);
-    w.att = (u16*)take(M8 * Hhd * 2);
-    w.act = (u16*)take(M8 * (long long)c.ffn_dim * 2);
+    w.att = (u16*)take(pair * M8 * Hhd * 2);
+    w.act = (u16*)take(pair * M8 * (long long)c.ffn_dim * 2);
     w.lse = (float*)take(M * c.n_heads * 4);
     w.mass = (float*)take(hd_->lazy() ? M * c.n_kv_heads * 4 : 0);
     w.keys = (float*)take(hd_->lazy() ? M * 4 : 0);
@@ -614,9 +628,11 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
     // the same: their writing workgroup gets longer by about what the separate launch
     // costs, so they keep the separate launch and measure the attention alone.)
     const bool fuse_kv = kw.rope_cs && ap.kind == ATTN_ROWS_SPARSE;
+    // decode over an int8 base: the float16 MFMA kernel takes q as float16 (one rounding)
+    const int q_half = decode && ap.kind == ATTN_ROWS_DENSE && ap.read.lazy && ap.read.base_bits == 8;
     if (!fuse_kv)
         LK_HIP(lk::rope_kv_write(w.qkv, io.M, io.rows_per_seq, pos, io.pos_offset, H, c.n_kv_heads, hd,
-                                 h->inv_freq, w.q, kw, st));
+                                 h->inv_freq, w.q, kw, st, q_half));
     if (ap.kind == ATTN_PREFILL_DENSE) {
         LK_TRY(timed(h, TC_ATTN_PREFILL, st,
                      [=] { return lk::attn_prefill(w.q, ap.read, ap.B, ap.T, H, w.att, w.lse, st); }));
@@ -626,6 +642,7 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
     } else {
         lk::RowsAttn a{};
         a.q = w.q;
+        a.q_half = q_half;
         a.qkv = w.qkv;
         a.rope_cs = w.rope;
         a.kvw = kw;
@@ -649,15 +666,6 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
             a.cols = nullptr;
             ncol_max = (long long)ap.pos + 1;
         }
-        // dense decode: one workgroup per (sequence, KV head, chunk), about 768 workgroups
-        // (three per CU; longer chunks keep each wave streaming longer)
-        auto dense_chunk = [=](long long ncol) {
-            const long long pairs = (long long)a.B * c.n_kv_heads;
-            const long long want = (ncol * pairs + 767) / 768;
-            int ch = (int)std::max(128LL, (want + 127) / 128 * 128);
-            while ((ncol + ch - 1) / ch > kMaxSplits) ch *= 2;
-            return ch;
-        };
         a.part = w.part;
         a.out = w.att;
         if (ap.kind == ATTN_ROWS_SPARSE && decode) {
@@ -665,7 +673,6 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
             // the end of prefill, the window from the float16 ring that prefill filled and
             // each decode step extends (rope_kv_write).  One launch runs over both
             // segments and the combine merges their splits.
-            constexpr int kSegChunk = 128;
             lk::RowsAttn d = a;
             d.kv = ap.scache;
             d.kv2 = ap.ring;
@@ -713,7 +720,7 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
                 a.d32 = ap.d32;
             }
             int chunk = kRowChunk;
-            if (ap.kind == ATTN_ROWS_DENSE) chunk = dense_chunk(ncol_max);
+            if (ap.kind == ATTN_ROWS_DENSE) chunk = decode_dense_chunk(a.B * c.n_kv_heads, ncol_max);
             while ((ncol_max + chunk - 1) / chunk > kMaxSplits) chunk *= 2;
             a.chunk = chunk;
             a.n_splits = (int)((ncol_max + chunk - 1) / chunk);
@@ -727,7 +734,6 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
                 // the token's loop-1 sparse term, over the float16 loop-1 caches of the
                 // stable columns and the window (as the later loops read theirs), taken
                 // off the dense output just stored in d32
-                constexpr int kSegChunk = 128;
                 lk::RowsAttn sp = a;
                 sp.cols = ap.cols;
                 sp.n_cols = ap.n_cols;
@@ -1013,6 +1019,12 @@ int lk_kv_store_view(const lk_kv_store* s, lk_store_view* v) {
     v->n_selected = s->lay.n_sel;
     v->n_columns = s->lay.n_cols;
     v->res_row_bytes = s->lay.res_row_b;
+    if (s->lay.scache_bytes) {
+        v->decode_cache = s->buf + s->lay.scache;
+        v->cache_rows = s->lay.ncs;
+        v->ring_rows = s->lay.wr;
+        v->first_cached_loop = s->lay.ck0;
+    }
     return LK_OK;
 }
 
@@ -1593,6 +1605,177 @@ int lk_dbg_gemm_epi(const void* d_a, const void* d_w, int32_t epi, float* d_c, v
     if (M < 1 || N < 16 || N % 16 || K < 32 || K % 32)
         return fail(LK_ERR_INVALID_ARG, "need M >= 1, N a multiple of 16, K a multiple of 32");
     LK_HIP(lk::gemm((const u16*)d_a, (const u16*)d_w, M, N, K, epi, d_c, (u16*)d_out, (hipStream_t)stream));
+    return LK_OK;
+}
+
+
+int lk_dbg_attention(const lk_dbg_attn_args* x, size_t* ws_need, void* stream) {
+    if (!x) return fail(LK_ERR_INVALID_ARG, "null argument");
+    const int B = x->B, H = x->H, Hkv = x->Hkv, hd = x->hd;
+    if (B < 1 || H < 1 || Hkv < 1 || H % Hkv) return fail(LK_ERR_INVALID_ARG, "bad head counts");
+    const int G = H / Hkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return fail(LK_ERR_UNSUPPORTED, "H / Hkv must be 1, 2, 4 or 8");
+    if (hd != 32 && hd != 64 && hd != 128) return fail(LK_ERR_UNSUPPORTED, "head_dim must be 32, 64 or 128");
+    if (!x->q || !x->out) return fail(LK_ERR_INVALID_ARG, "null q or out");
+    hipStream_t st = (hipStream_t)stream;
+    auto rows_layer = [&](int fmt, const void* k, const void* v, const uint16_t* ks, const uint16_t* vs, int tmax) {
+        KVLayer L{};
+        L.B = B;
+        L.Hkv = Hkv;
+        L.hd = hd;
+        L.Tmax = tmax;
+        L.n_loops = 1;
+        L.base[0] = k;
+        L.base[1] = v;
+        L.base_bits = 16;
+        L.res_bits = 16;
+        if (fmt == 1) {
+            L.lazy = 1;
+            L.base_bits = 8;
+            L.base_scale[0] = ks;
+            L.base_scale[1] = vs;
+        } else if (fmt == 2) {
+            L.f16 = 1;
+        }
+        return L;
+    };
+    size_t need = 0;
+    switch (x->kind) {
+        case LK_DBG_ATTN_DECODE:
+        case LK_DBG_ATTN_DECODE_SEG: {
+            lk::RowsAttn a{};
+            a.q = (const u16*)x->q;
+            a.q_half = x->q_half != 0;
+            a.B = B;
+            a.n_rows = 1;
+            a.H = H;
+            a.pos = x->t;
+            a.k_loop = 1;
+            a.out = (u16*)x->out;
+            if (x->out32) {
+                a.diff_mode = lk::DIFF_SET32;
+                a.d32 = x->out32;
+            }
+            if (x->kind == LK_DBG_ATTN_DECODE) {
+                if (x->kv_format != 0 && x->kv_format != 1) return fail(LK_ERR_UNSUPPORTED, "decode rows are bf16 or int8");
+                if (!x->k || !x->v || (x->kv_format == 1 && (!x->k_scales || !x->v_scales)))
+                    return fail(LK_ERR_INVALID_ARG, "null K/V rows");
+                if (x->tmax < 8 || x->tmax % 8 || x->t < 0 || x->t >= x->tmax)
+                    return fail(LK_ERR_INVALID_ARG, "need tmax a multiple of 8 and 0 <= t < tmax");
+                a.kv = rows_layer(x->kv_format, x->k, x->v, x->k_scales, x->v_scales, x->tmax);
+                // as a decode step: splits sized for the capacity tmax
+                a.chunk = decode_dense_chunk((long long)B * Hkv, x->tmax);
+                a.n_splits = (x->tmax + a.chunk - 1) / a.chunk;
+            } else {
+                if (!x->cols || !x->s_k || !x->s_v || !x->r_k || !x->r_v) return fail(LK_ERR_INVALID_ARG, "null argument");
+                if (x->n_cols < 1 || x->s_cap < x->n_cols || x->s_cap % kSegChunk || x->r_cap % kSegChunk ||
+                    x->window < 1 || x->r_cap < x->window + 8 || x->t < 0)
+                    return fail(LK_ERR_INVALID_ARG, "need s_cap >= n_cols, s_cap and r_cap multiples of 128, "
+                                                    "r_cap >= window + 8");
+                a.kv = rows_layer(2, x->s_k, x->s_v, nullptr, nullptr, x->s_cap);
+                a.kv2 = rows_layer(2, x->r_k, x->r_v, nullptr, nullptr, x->r_cap);
+                a.cols = x->cols;
+                a.n_cols = x->n_cols;
+                a.window = x->window;
+                a.chunk = kSegChunk;
+                a.seg_split = x->s_cap / kSegChunk;
+                a.n_splits = a.seg_split + x->r_cap / kSegChunk;
+            }
+            need = (size_t)B * H * a.n_splits * (hd + 2) * 4;
+            if (!x->ws) {
+                if (!ws_need) return fail(LK_ERR_INVALID_ARG, "null workspace");
+                break;
+            }
+            if (x->ws_bytes < need) return fail(LK_ERR_CAPACITY, "workspace too small");
+            a.part = (float*)x->ws;
+            LK_HIP(lk::attn_rows_main(a, st));
+            LK_HIP(lk::attn_rows_combine(a, st, false));
+            break;
+        }
+        case LK_DBG_ATTN_PREFILL:
+        case LK_DBG_ATTN_MASS: {
+            if (x->kv_format != 0 && x->kv_format != 1) return fail(LK_ERR_UNSUPPORTED, "prefill rows are bf16 or int8");
+            if (!x->k || !x->v || (x->kv_format == 1 && (!x->k_scales || !x->v_scales)) || !x->lse)
+                return fail(LK_ERR_INVALID_ARG, "null argument");
+            if (x->kind == LK_DBG_ATTN_MASS && !x->mass) return fail(LK_ERR_INVALID_ARG, "null mass");
+            if (x->T < 1 || x->tmax < x->T || x->tmax % 8) return fail(LK_ERR_INVALID_ARG, "need 1 <= T <= tmax, tmax % 8 == 0");
+            if (!x->ws && ws_need) break;
+            const KVLayer L = rows_layer(x->kv_format, x->k, x->v, x->k_scales, x->v_scales, x->tmax);
+            if (x->kind == LK_DBG_ATTN_PREFILL)
+                LK_HIP(lk::attn_prefill((const u16*)x->q, L, B, x->T, H, (u16*)x->out, x->lse, st));
+            else
+                LK_HIP(lk::column_mass((const u16*)x->q, L, x->lse, B, x->T, H, x->mass, st));
+            break;
+        }
+        case LK_DBG_ATTN_PREFILL_SPARSE: {
+            if (hd != 128) return fail(LK_ERR_UNSUPPORTED, "the sparse prefill rows take head_dim 128");
+            if (!x->cols || !x->qpos || !x->s_k || !x->s_v || !x->r_k || !x->r_v) return fail(LK_ERR_INVALID_ARG, "null argument");
+            if (x->n_rows < 1 || x->n_cols < 1 || x->window < 1 || x->s_cap < x->n_cols || x->s_cap % 8 || x->r_cap % 8)
+                return fail(LK_ERR_INVALID_ARG, "bad sizes");
+            if (!x->ws && ws_need) break;
+            lk::RowsAttn a{};
+            a.q = (const u16*)x->q;
+            a.qpos = x->qpos;
+            a.B = B;
+            a.n_rows = x->n_rows;
+            a.H = H;
+            a.cols = x->cols;
+            a.n_cols = x->n_cols;
+            a.window = x->window;
+            a.out = (u16*)x->out;
+            a.kv = rows_layer(2, x->s_k, x->s_v, nullptr, nullptr, x->s_cap);
+            const KVLayer fr = rows_layer(2, x->r_k, x->r_v, nullptr, nullptr, x->r_cap);
+            LK_HIP(lk::attn_rows_prefill(a, a.kv, fr, st));
+            break;
+        }
+        default:
+            return fail(LK_ERR_INVALID_ARG, "unknown kind");
+    }
+    if (ws_need) *ws_need = need;
+    return LK_OK;
+}
+
+int lk_dbg_kv_write(lk_kv_store* s, int32_t layer, int32_t loop, const float* d_qkv, int32_t rows_per_seq,
+                    const int32_t* d_pos, void* d_q_out, int32_t q_half, void* d_ws, size_t ws_bytes, void* stream) {
+    if (!s || !d_qkv || !d_q_out) return fail(LK_ERR_INVALID_ARG, "null argument");
+    lk_handle* h = s->h;
+    if (!h->lazy()) return fail(LK_ERR_UNSUPPORTED, "the writer test entry takes lazy stores");
+    const lk_model_cfg& c = h->c;
+    if (layer < 0 || layer >= c.n_shared || loop < 1 || loop > s->K) return fail(LK_ERR_INVALID_ARG, "bad layer or loop");
+    hipStream_t st = (hipStream_t)stream;
+    const int B = s->B;
+    lk::KVWrite kw{};
+    kw.layer = lazy_layer(s, layer);
+    kw.loop = loop;
+    kw.kind = loop == 1 ? 1 : 2;
+    kw.keep_codes = 0;
+    if (d_pos) {
+        if (rows_per_seq < 1 || rows_per_seq > s->Tpad || (loop >= 2 && rows_per_seq > s->lay.slots))
+            return fail(LK_ERR_INVALID_ARG, "rows_per_seq out of range");
+        kw.slot_base = 0;
+        if (loop >= 2) kw.slot_map_k = slot_map(s, loop);
+        LK_HIP(lk::rope_kv_write(d_qkv, B * rows_per_seq, rows_per_seq, d_pos, 0, c.n_heads, c.n_kv_heads, c.head_dim,
+                                 h->inv_freq, (u16*)d_q_out, kw, st, q_half));
+        return LK_OK;
+    }
+    if (!s->prefilled) return fail(LK_ERR_STATE, "decode-mode write before prefill");
+    if (s->t >= s->Tmax) return fail(LK_ERR_CAPACITY, "store is full");
+    if (!d_ws) return fail(LK_ERR_INVALID_ARG, "decode mode needs the decode workspace");
+    const WS w = ws_layout(h, B, 1, (char*)d_ws);
+    if (ws_bytes < w.total) return fail(LK_ERR_CAPACITY, "workspace too small");
+    const int32_t* dpos = dev_pos(s);
+    LK_HIP(lk::rope_angles(dpos, h->inv_freq, c.head_dim, w.rope, st));
+    kw.dpos = dpos;
+    kw.rope_cs = w.rope;
+    kw.tok_recon = w.tokrec + (long long)layer * B * 2 * c.n_kv_heads * c.head_dim;
+    if (loop >= 2) {
+        kw.ring = scache_layer(s, loop, layer, true);
+        kw.ring_on = 1;
+        kw.slot_base = (long long)loop_rows(s, loop) - s->Tp;
+        kw.slot_map_k = slot_map(s, loop);
+    }
+    LK_HIP(lk::rope_kv_write(d_qkv, B, 1, nullptr, 0, c.n_heads, c.n_kv_heads, c.head_dim, h->inv_freq,
+                             (u16*)d_q_out, kw, st, q_half));
     return LK_OK;
 }
 

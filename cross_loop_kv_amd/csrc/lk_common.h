@@ -38,6 +38,30 @@ __device__ __forceinline__ float h2f(u16 bits) {
     return (float)__builtin_bit_cast(_Float16, bits);
 }
 
+// ---------------------------------------------------------------- rotary embedding
+// Rotate-half RoPE of the pair (x1, x2) = (x[i], x[i + hd/2]) by an angle with cosine c
+// and sine sn: x1' = x1 c - x2 sn, x2' = x2 c + x1 sn.  Each product is rounded before
+// the sum (no fused multiply-add), so the rotated value is the same float32 as the
+// plain elementwise evaluation of the formula.
+__device__ __forceinline__ float rope_lo(float x1, float x2, float c, float sn) {
+#pragma clang fp contract(off)
+    return x1 * c - x2 * sn;
+}
+__device__ __forceinline__ float rope_hi(float x1, float x2, float c, float sn) {
+#pragma clang fp contract(off)
+    return x2 * c + x1 * sn;
+}
+
+// ---------------------------------------------------------------- split operands
+// A float32 value as the sum of two bfloat16 values: hi = bf16(x), lo = bf16(x - hi)
+// (x - hi is exact).  hi + lo is within 2^-16 |x| of x, so a product that takes both
+// halves through bf16 MFMAs is as accurate as a float32 operand to that level.
+__device__ __forceinline__ void split_bf2(float x, u16* hi, u16* lo) {
+    const u16 h = f2bf(x);
+    *hi = h;
+    *lo = f2bf(x - bf2f(h));
+}
+
 // ---------------------------------------------------------------- reductions
 // Butterfly reductions: every lane ends with the same, run-to-run identical value.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -78,9 +78,11 @@ struct KVWrite {
 // cos and sin (float64 evaluation, rounded to float32) of position *dpos times each
 // inverse frequency into cs [hd/2][2].
 hipError_t rope_angles(const int32_t* dpos, const double* inv_freq, int hd, float* cs, hipStream_t st);
+// q_half: q_out receives float16 bits instead of bfloat16 (decode, for the float16 MFMA
+// attention kernels, which then take q with one rounding).
 hipError_t rope_kv_write(const float* qkv, int rows, int rows_per_seq, const int32_t* pos,
                          int pos_offset, int H, int Hkv, int hd, const double* inv_freq, u16* q_out,
-                         const KVWrite& kvw, hipStream_t st);
+                         const KVWrite& kvw, hipStream_t st, int q_half = 0);
 
 // Element e of one token's K (kv = 0, rotated by the angle of pair e % (hd/2), cosine c,
 // sine sn) or V (kv = 1) row of KV head g into the store as w describes.  src: the
@@ -96,7 +98,7 @@ __device__ __forceinline__ void kv_write_elem(const float* __restrict__ src, int
     if (kv == 0) {
         const int i = e % half;
         const float x1 = src[(H + g) * hd + i], x2 = src[(H + g) * hd + i + half];
-        x = e < half ? x1 * c - x2 * sn : x2 * c + x1 * sn;
+        x = e < half ? rope_lo(x1, x2, c, sn) : rope_hi(x1, x2, c, sn);
     } else {
         x = src[(H + Hkv + g) * hd + e];
     }
@@ -182,10 +184,13 @@ hipError_t gemm_rmsnorm(const float* X, const u16* gain, float eps, const u16* W
 
 // Decode-sized products (M <= 8 rows, K % 64 == 0, N % 8 == 0) with the RMSNorm
 // carried between kernels: a producer adds its product into the residual stream x
-// and leaves xg = bf16(x * next_gain) plus per-workgroup row sums of x^2 (ps, [nparts][8]);
+// and leaves xg = x * next_gain plus per-workgroup row sums of x^2 (ps, [nparts][8]);
 // the consumer multiplies xg by W and scales by 1 / sqrt(sum(ps) / K + eps).
-// Weights (Wp) and bf16 activations (xg, A, and the bf16 outputs) are in the
+// Weights (Wp) and activations (xg, A, and the activation outputs) are in the
 // lane-packed order of pk_index (weights: rows = N, or 2N for SwiGLU's [gate; up]).
+// Every activation operand of these products is a hi/lo pair of bf16 values
+// (split_bf2): hi in the first 8 K elements of the buffer, lo in the next 8 K, so the
+// decode projections see their float32 inputs to 2^-16 (the weights are bf16 as given).
 struct FoldIO {
     const float* ps_in;    // NORM: partial sums of x^2 [nparts][8]
     int nparts;
@@ -208,7 +213,8 @@ hipError_t gemm_fold_add(const u16* A, const u16* Wp, int M, int N, int K, float
                          const float* add_rows = nullptr, float* x_save = nullptr, const int32_t* live = nullptr);
 // Row-major W [rows, K] -> lane-packed Wp (rows % 8 == 0, K % 64 == 0).
 hipError_t pack_weights(const u16* W, long long rows, int K, u16* Wp, hipStream_t st);
-// x += add (optional); xg = bf16(x * gain) (lane-packed); ps[0][r] = sum of x^2 of row r.
+// x += add (optional); xg = x * gain as a lane-packed hi/lo bf16 pair (hi at xg, lo at
+// xg + 8 d); ps[0][r] = sum of x^2 of row r.
 hipError_t norm_prep(float* x, const u16* add, const u16* gain, int rows, int d, u16* xg, float* ps,
                      hipStream_t st);
 
@@ -223,7 +229,8 @@ hipError_t column_mass(const u16* q, const KVLayer& kv, const float* lse, int B,
 
 // Row attention over explicit column sets (decode and token-sparse prefill).
 struct RowsAttn {
-    const u16* q;          // bf16 [B * n_rows, H * hd]
+    const u16* q;          // bf16 [B * n_rows, H * hd] (float16 when q_half != 0)
+    int q_half;            // q holds float16 bits (decode: the float16 MFMA kernels take it as is)
     const int32_t* qpos;   // [B * n_rows] positions (nullptr: all rows at `pos`)
     int pos;
     int B, n_rows, H;
@@ -287,7 +294,8 @@ hipError_t gather_recon(const RowsAttn& a, int mode, int ncap, u16* kc, u16* vc,
 hipError_t attn_rows_prefill(const RowsAttn& a, const KVLayer& sc, const KVLayer& fr, hipStream_t st);
 // attn_rows_main writes the per-split partials; attn_rows_combine merges them into `out`.
 hipError_t attn_rows_main(const RowsAttn& a, hipStream_t st);
-// packed_out: out in the lane-packed order of the decode products (at most 8 rows).
+// packed_out: out in the lane-packed order of the decode products (at most 8 rows), as a
+// hi/lo bf16 pair (lo at out + 8 H hd).
 hipError_t attn_rows_combine(const RowsAttn& a, hipStream_t st, bool packed_out = false);
 
 }  // namespace lk

@@ -310,6 +310,15 @@ typedef struct {
     int32_t n_columns;      /* min(top_s, prompt_tokens) */
     int64_t res_row_bytes;  /* bytes of one residual row (hd elements) */
     int32_t row_stride;     /* Tp: positions per (sequence, KV head), max_tokens padded to 8 */
+    /* lazy decode caches (lk_kv_store_cache_bytes; NULL when there are none), float16:
+     * for loops k = first_cached_loop..n_loops and shared layers r (index (k -
+     * first_cached_loop) * R + r), the stable-column reconstruction, K rows
+     * [batch][Hkv][cache_rows][hd] then V rows 8-key interleaved
+     * [batch][Hkv][cache_rows/8][hd][8] (row i = column i of the column set); after all
+     * of those, in the same order, the window rings with ring_rows rows per (sequence,
+     * KV head) in the same two layouts (position p at row p % ring_rows). */
+    void *decode_cache;
+    int32_t cache_rows, ring_rows, first_cached_loop;
 } lk_store_view;
 int lk_kv_store_view(const lk_kv_store *s, lk_store_view *v);
 
@@ -356,6 +365,103 @@ int lk_dbg_gemm(const void *d_a, const void *d_w, float *d_c, int32_t M, int32_t
  * Same size rules as lk_dbg_gemm. */
 int lk_dbg_gemm_epi(const void *d_a, const void *d_w, int32_t epi, float *d_c, void *d_out,
                     int32_t M, int32_t N, int32_t K, void *stream);
+
+/* Attention kernels on caller data (test entry point): each kind runs the kernels,
+ * launch shapes and split counts that prefill or decode run for that step, on K/V
+ * rows the caller lays out as the store does.  Softmax of q.k / sqrt(hd) over each
+ * query's key set; query head h reads KV head h / (H / Hkv) (the FlashLoop abstract,
+ * arxivdaily.com: loops k >= 2 attend over a sparse, stable subset of key columns;
+ * the loop-1 attention that ranks those columns is the dense causal one).
+ *
+ * Row layouts (positions per (sequence, KV head) padded to `tmax`, a multiple of 8):
+ *   K rows [B][Hkv][tmax][hd]; V rows 8-key interleaved [B][Hkv][tmax/8][hd][8]
+ *   (element (pos, e) at ((b*Hkv + g)*tmax/8 + pos/8)*hd*8 + e*8 + pos%8);
+ *   kv_format 0: bfloat16 rows; 1: int8 codes with float16 scales per 32 elements,
+ *   K scales [B][Hkv][tmax][hd/32], V scales [B][Hkv][tmax/8][hd/32][8] (value =
+ *   code * scale); 2: float16 rows.
+ *
+ * Kinds:
+ *   LK_DBG_ATTN_DECODE: one query per sequence at position t over keys [0, t]
+ *     (kv_format 0 or 1; t < tmax), split over the context and merged, as a decode
+ *     step's loop-1 attention; q [B][H*hd] (float16 bits when q_half, which the
+ *     int8 kernel takes as is; else bf16).  out bf16 [B][H*hd], out32 float32 (same).
+ *   LK_DBG_ATTN_DECODE_SEG: one query per sequence at position t over
+ *     (S intersect [0, t - window]) union [max(0, t - window + 1), t], S = cols
+ *     [B][Hkv][n_cols] ascending, as a decode step's loop k >= 2: the stable
+ *     columns are read from a float16 cache (s_k / s_v: row i holds column cols[i],
+ *     s_cap rows per (b, g), a multiple of 128, >= n_cols) and the window from a
+ *     float16 ring (r_k / r_v: position p at row p % r_cap, r_cap a multiple of 128,
+ *     > window + 8).  q and outputs as LK_DBG_ATTN_DECODE.
+ *   LK_DBG_ATTN_PREFILL: causal attention of T prompt tokens (query i over keys
+ *     [0, i]; kv_format 0 or 1, T <= tmax); q bf16 [B][T][H*hd]; out bf16
+ *     [B][T][H*hd]; lse float32 [B][H][T], the log2 of each row's softmax
+ *     denominator in units of the log2-scaled scores (q.k * log2(e) / sqrt(hd)).
+ *   LK_DBG_ATTN_MASS: column mass of that attention, mass float32 [B][Hkv][T]:
+ *     mass[b][g][j] = sum over queries i >= j and the query heads of g of the
+ *     probability of key j, with lse (as LK_DBG_ATTN_PREFILL writes it) as input.
+ *   LK_DBG_ATTN_PREFILL_SPARSE: n_rows kept prompt rows per sequence (positions
+ *     qpos [B][n_rows], ascending), row at position i over (S intersect [0, i -
+ *     window]) union [max(0, i - window + 1), i], hd 128: stable columns from the
+ *     float16 cache s_k / s_v (as above, s_cap a multiple of 8), the window from
+ *     float16 rows at every position r_k / r_v (r_cap = positions, a multiple of 8);
+ *     q bf16 [B][n_rows][H*hd]; out bf16 [B][n_rows][H*hd].
+ * ws: device scratch of ws_bytes (split partials; lk_dbg_attention with ws == NULL
+ * writes the bytes a call needs to *ws_need and launches nothing).  head_dim 32, 64
+ * or 128 (128 only for PREFILL_SPARSE); H / Hkv in {1, 2, 4, 8}. */
+#define LK_DBG_ATTN_DECODE 0
+#define LK_DBG_ATTN_DECODE_SEG 1
+#define LK_DBG_ATTN_PREFILL 2
+#define LK_DBG_ATTN_MASS 3
+#define LK_DBG_ATTN_PREFILL_SPARSE 4
+typedef struct {
+    int32_t kind;
+    int32_t B, H, Hkv, hd;
+    int32_t kv_format;           /* 0 bf16, 1 int8 + float16 scales, 2 float16 */
+    int32_t t;                   /* DECODE*: the query position */
+    int32_t T;                   /* PREFILL, MASS, PREFILL_SPARSE: prompt tokens */
+    int32_t tmax;                /* positions per (sequence, KV head) of k / v */
+    const void *q;
+    int32_t q_half;              /* DECODE*: q holds float16 bits */
+    const void *k, *v;           /* rows (DECODE, PREFILL, MASS) */
+    const uint16_t *k_scales, *v_scales;  /* kv_format 1 */
+    const int32_t *cols;         /* DECODE_SEG, PREFILL_SPARSE: [B][Hkv][n_cols] */
+    int32_t n_cols, window;
+    const void *s_k, *s_v;       /* float16 stable-column cache */
+    int32_t s_cap;
+    const void *r_k, *r_v;       /* float16 window ring (DECODE_SEG) or rows (PREFILL_SPARSE) */
+    int32_t r_cap;
+    const int32_t *qpos;         /* PREFILL_SPARSE: [B][n_rows] */
+    int32_t n_rows;
+    void *out;                   /* bf16 outputs as above */
+    float *out32;                /* DECODE*: float32 [B][H*hd] (may be NULL) */
+    float *lse;                  /* PREFILL: output; MASS: input */
+    float *mass;                 /* MASS: output */
+    void *ws;
+    size_t ws_bytes;
+} lk_dbg_attn_args;
+int lk_dbg_attention(const lk_dbg_attn_args *a, size_t *ws_need, void *stream);
+
+/* Store writer on caller projections (test entry point).  d_qkv float32 [rows][(H +
+ * 2 Hkv) hd], the QKV projection of each row (q heads, k heads, v heads).  q and K are
+ * rotated at the row's position, q into d_q_out (bf16 [rows][H hd], float16 bits when
+ * q_half), and K/V go into shared layer `layer` of lazy store s as loop `loop` writes
+ * them (the FlashLoop abstract: loop-k KV kept as the loop-(k-1) KV plus a low-bit
+ * residual; the quantizer and layouts as lk_kv_store_alloc describes):
+ *   d_pos != NULL (prefill): rows = batch * rows_per_seq, row r of sequence r /
+ *     rows_per_seq at position d_pos[r]; loop 1 writes the base rows; loop k >= 2
+ *     quantizes the difference to the store's loop-(k-1) reconstruction of that
+ *     position into slot r % rows_per_seq and sets the loop-k slot-map entry;
+ *   d_pos == NULL (decode): one row per sequence at position t = the store length,
+ *     exactly as a decode step's loop `loop` writes it: the slot is the loop's first
+ *     decode slot plus t - prompt_tokens, the previous loop's reconstruction of the
+ *     row is the float32 one the step carries in the decode workspace d_ws (so a
+ *     token's loops are written in the order 1, 2, ..), and loops k >= 2 also write
+ *     the row's float16 reconstruction into the window ring.  The store length is
+ *     not changed.
+ * d_ws: a decode workspace (lk_workspace_bytes(batch, 1)) in decode mode, else unused. */
+int lk_dbg_kv_write(lk_kv_store *s, int32_t layer, int32_t loop, const float *d_qkv, int32_t rows_per_seq,
+                    const int32_t *d_pos, void *d_q_out, int32_t q_half, void *d_ws, size_t ws_bytes,
+                    void *stream);
 
 #ifdef __cplusplus
 }

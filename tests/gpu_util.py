@@ -121,7 +121,11 @@ def run_pair(shape, lazy, batch, prompt, steps, seed=0, force=True, weights=None
     """Prefill + `steps` decode steps on the oracle and the GPU; returns a result dict.
 
     force: inject the oracle's token and column selections.  force_codes (default:
-    when the residuals are 4-bit): also inject the oracle's quantized codes.
+    with int4 residuals): also inject the oracle's quantized codes (prefill and decode
+    rows), so that both sides make the same integer decisions on inputs that differ by
+    the GPU's bf16 products (an int4 step is amax/7 of a group, far more than that
+    rounding).  The writer itself is compared bit for bit on identical inputs in
+    test_gpu_writer, and the full-context decode tests run on the GPU's own codes.
     loops: run the shared block this many times (default: the shape's n_loops)."""
     W = weights if weights is not None else cached_weights(shape, seed)
     ids = I.gen_prompt_ids(shape, batch, prompt)
@@ -144,20 +148,8 @@ def run_pair(shape, lazy, batch, prompt, steps, seed=0, force=True, weights=None
     g_out = model.prefill(store, torch.from_numpy(ids)).cpu().numpy()
     g_dec = [model.decode(store, torch.from_numpy(d)).cpu().numpy() for d in dec]
     torch.cuda.synchronize()
-    # the same computation with bf16 operands, on the same integer decisions as the GPU run
-    m16 = LoopedOracle(shape, lazy, W, batch, prompt + steps, operand_precision="bf16", n_loops=loops)
-    if lazy.mode == "lazy" and force:
-        m16.forced_tokens = dict(m.sel)
-        m16.forced_S = m.S
-        if force_codes:
-            m16.forced_codes_from = m
-    o16_out = m16.prefill(ids)
-    o16_dec = [m16.decode(d) for d in dec]
     res = dict(oracle=m, model=model, store=store, o_out=o_out, g_out=g_out, o_dec=o_dec, g_dec=g_dec,
                t_oracle=t_oracle, ids=ids, dec=dec, forced_codes=bool(force and force_codes))
     res["err_prefill"] = max_abs_rel(g_out, o_out)
     res["err_decode"] = [max_abs_rel(g, o) for g, o in zip(g_dec, o_dec)]
-    res["err16_prefill"] = max_abs_rel(g_out, o16_out)
-    res["err16_decode"] = [max_abs_rel(g, o) for g, o in zip(g_dec, o16_dec)]
-    res["bf16_drift"] = max_abs_rel(o16_out, o_out)
     return res

@@ -40,9 +40,12 @@ def test_struct_layouts_match_the_header():
 #define P(T, f) printf("%s.%s %zu\n", #T, #f, offsetof(T, f));
 int main(void) {
   printf("lk_model_cfg %zu\nlk_lazy_cfg %zu\nlk_layer_weights %zu\nlk_weights %zu\nlk_store_view %zu\n"
-         "lk_store_snapshot %zu\n",
+         "lk_store_snapshot %zu\nlk_dbg_attn_args %zu\n",
          sizeof(lk_model_cfg), sizeof(lk_lazy_cfg), sizeof(lk_layer_weights), sizeof(lk_weights),
-         sizeof(lk_store_view), sizeof(lk_store_snapshot));
+         sizeof(lk_store_view), sizeof(lk_store_snapshot), sizeof(lk_dbg_attn_args));
+  P(lk_dbg_attn_args, q) P(lk_dbg_attn_args, q_half) P(lk_dbg_attn_args, cols) P(lk_dbg_attn_args, s_cap)
+  P(lk_dbg_attn_args, r_cap) P(lk_dbg_attn_args, qpos) P(lk_dbg_attn_args, n_rows) P(lk_dbg_attn_args, out32)
+  P(lk_dbg_attn_args, mass) P(lk_dbg_attn_args, ws_bytes)
   P(lk_store_snapshot, cfg) P(lk_store_snapshot, lazy) P(lk_store_snapshot, batch)
   P(lk_store_snapshot, prefilled) P(lk_store_snapshot, body_bytes)
   printf("magic %llu\n", (unsigned long long)LK_SNAPSHOT_MAGIC);
@@ -52,6 +55,7 @@ int main(void) {
   P(lk_lazy_cfg, refresh_every) P(lk_lazy_cfg, diff_attn) P(lk_lazy_cfg, skip_tau)
   P(lk_weights, layers) P(lk_layer_weights, w_down)
   P(lk_store_view, slots) P(lk_store_view, n_selected) P(lk_store_view, res_row_bytes) P(lk_store_view, row_stride)
+  P(lk_store_view, decode_cache) P(lk_store_view, ring_rows) P(lk_store_view, first_cached_loop)
   return 0;
 }
 """
@@ -66,7 +70,7 @@ int main(void) {
     assert int(got.pop("snapshot_version")) == B.SNAPSHOT_VERSION
     assert B.SNAPSHOT_MAGIC.to_bytes(8, "little") == b"LKSNAP01"
     for name in ("lk_model_cfg", "lk_lazy_cfg", "lk_layer_weights", "lk_weights", "lk_store_view",
-                 "lk_store_snapshot"):
+                 "lk_store_snapshot", "lk_dbg_attn_args"):
         assert int(got[name]) == ctypes.sizeof(getattr(B, name)), name
     for key, val in got.items():
         if "." in key:
@@ -224,3 +228,34 @@ def test_snapshot_size_query_and_import_validation():
     finally:
         B.lk_destroy(other)
         B.lk_destroy(h)
+
+
+def test_debug_attention_argument_errors_and_size_query():
+    """Host-side checks of lk_dbg_attention (nothing is launched): bad head counts and
+    shapes are refused, and with no workspace the decode kinds report the bytes of
+    their split partials (B * H * splits * (hd + 2) floats, splits as a decode step
+    sizes them for the capacity tmax)."""
+    a = B.lk_dbg_attn_args(kind=B.DBG_ATTN["decode"], B=8, H=16, Hkv=4, hd=128, kv_format=1, t=100,
+                           tmax=33088, q=16, k=16, v=16, k_scales=16, v_scales=16, out=16)
+    need = B.lk_dbg_attention(a)
+    assert need > 0 and need % (8 * 16 * 130 * 4) == 0
+    splits = need // (8 * 16 * 130 * 4)
+    assert 1 <= splits <= 256 and splits * 768 >= (8 * 4 * 33088) // 768   # chunks >= 128 keys
+    bad = B.lk_dbg_attn_args(kind=B.DBG_ATTN["decode"], B=8, H=12, Hkv=4, hd=128, kv_format=1, t=10, tmax=64,
+                             q=16, k=16, v=16, k_scales=16, v_scales=16, out=16)
+    with pytest.raises(B.LKError):
+        B.lk_dbg_attention(bad)
+    seg = B.lk_dbg_attn_args(kind=B.DBG_ATTN["decode_seg"], B=2, H=8, Hkv=2, hd=64, t=500, q=16, cols=16,
+                             n_cols=100, window=40, s_k=16, s_v=16, s_cap=128, r_k=16, r_v=16, r_cap=128, out=16)
+    assert B.lk_dbg_attention(seg) == 2 * 8 * 2 * 66 * 4      # 1 + 1 splits of 128 rows
+    seg.s_cap = 64                                            # below n_cols and not a multiple of 128
+    with pytest.raises(B.LKError):
+        B.lk_dbg_attention(seg)
+    sp = B.lk_dbg_attn_args(kind=B.DBG_ATTN["prefill_sparse"], B=1, H=8, Hkv=2, hd=64, T=100, q=16, cols=16,
+                            n_cols=10, window=4, s_k=16, s_v=16, s_cap=16, r_k=16, r_v=16, r_cap=104, qpos=16,
+                            n_rows=10, out=16)
+    with pytest.raises(B.LKError) as e:
+        B.lk_dbg_attention(sp)                                # head_dim 64 is not taken there
+    assert e.value.code == -2
+    with pytest.raises(B.LKError):
+        B.lk_dbg_attention(B.lk_dbg_attn_args(kind=9, B=1, H=1, Hkv=1, hd=32, q=16, out=16))

@@ -1,16 +1,12 @@
 """End-to-end GPU parity against the CPU oracle (prefill + decode), through the C ABI.
 
-With the oracle's token and column selections injected (forced selection), the
-final-normed hidden states must agree within max-abs-relative 2e-2 (bf16 GEMM
-operands and KV vs the float32 oracle).  With 4-bit residuals the oracle's
-quantized codes are injected as well: one int4 step is amax/7 of a group, so a
-code that flips between two implementations whose inputs differ by bf16
-rounding moves a K/V element by far more than that rounding, and the
-comparison of the floating-point path is made on equal integer decisions (the
-quantizer itself is compared bit for bit on identical inputs in
-test_gpu_kernels).  Natural selection and natural int4 codes are reported with
-a looser sanity bound.  The store's byte count must equal the oracle's closed
-form exactly.
+The final-normed hidden states must agree with the float32 oracle within
+max-abs-relative 2e-2 (bf16 GEMM operands and KV against float32).  Token and column
+selections are the oracle's (forced selection) unless a test checks natural
+selection, and then every GPU pick must be a valid top-n / top-s of the oracle's keys
+or masses up to a float32 margin.  Quantized codes are the GPU's own (the writer is
+compared bit for bit on identical inputs in test_gpu_writer).  The store's byte count
+must equal the oracle's closed form exactly.
 """
 import numpy as np
 import pytest
@@ -27,19 +23,26 @@ TOL = 2e-2
 
 
 def check(r, what=""):
-    """GPU vs the float32 oracle and vs the oracle run with bf16 operands.
+    """GPU vs the float32 oracle: prefill and every decode step within TOL."""
+    log(f"  {what} vs fp32 oracle: prefill {r['err_prefill']:.3e} decode {max(r['err_decode'] or [0]):.3e}")
+    assert r["err_prefill"] < TOL and max(r["err_decode"] or [0]) < TOL
 
-    Bound: TOL (2e-2), or twice the oracle's own sensitivity to bf16 operand
-    rounding (max-abs-rel between its float32 and bf16-operand runs on the same
-    integer decisions) when that is larger.  A stack that moves by that much
-    under a 2^-9 perturbation of its operands cannot be held closer than that by
-    any bf16 implementation; for all but the widest shape the bound is TOL."""
-    tol = max(TOL, 2 * r["bf16_drift"])
-    log(f"  {what} vs fp32 oracle: prefill {r['err_prefill']:.3e} decode {max(r['err_decode'] or [0]):.3e}; "
-        f"vs bf16-operand oracle: prefill {r['err16_prefill']:.3e} decode {max(r['err16_decode'] or [0]):.3e}; "
-        f"oracle bf16 sensitivity {r['bf16_drift']:.3e}; bound {tol:.2e}")
-    assert r["err16_prefill"] < tol and max(r["err16_decode"] or [0]) < tol
-    assert r["err_prefill"] < tol and max(r["err_decode"] or [0]) < tol
+
+def valid_top(picked, ref_keys, n, margin):
+    """picked (the GPU's n indices) is a top-n of ref_keys (the oracle's) up to a
+    relative margin: every picked index has a key of at least (1 - margin) * thr, every
+    left-out one at most (1 + margin) * thr, thr = the n-th largest oracle key.  Returns
+    the number of indices on which the two sets differ."""
+    picked = np.asarray(picked)
+    ref = np.asarray(ref_keys, np.float64)
+    assert len(np.unique(picked)) == len(picked) == n
+    thr = np.sort(ref)[::-1][n - 1]
+    lo, hi = thr * (1 - margin), thr * (1 + margin)
+    assert np.all(ref[picked] >= lo), "a picked index is well below the oracle's top-n"
+    out = np.setdiff1d(np.arange(ref.size), picked)
+    assert np.all(ref[out] <= hi), "a left-out index is well above the oracle's top-n"
+    from oracle.select import top_n_ascending
+    return int(np.setxor1d(picked, top_n_ascending(ref_keys, n)).size)
 
 
 def tiny():
@@ -100,60 +103,98 @@ def test_decode_batch_above_eight_rows(mode, Bsz):
     check(r, f"batch {Bsz} {mode}")
 
 
-def test_int4_natural_codes_drift_is_bounded():
-    """Without injected codes the int4 path differs from the oracle by code flips only."""
+def test_int4_codes_natural_and_injected():
+    """The same int4 run twice.  With the oracle's prefill codes injected (both sides
+    take the same integer decisions on the prompt; decode writes the GPU's own codes):
+    within the bound.  With the GPU's own codes throughout: its prefill codes are the
+    oracle's except for flips between adjacent codes of near-tie elements (the GPU's K/V
+    come from bf16 products, and a residual is a small difference of two such values),
+    and its scales within a few percent; the output difference that the flips cause is
+    reported (an int4 step is amax/7 of a group)."""
     s = _small()
     lz = I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4)
-    r = run_pair(s, lz, batch=2, prompt=150, steps=3, seed=5, force_codes=False)
     f = run_pair(s, lz, batch=2, prompt=150, steps=3, seed=5, force_codes=True)
-    log(f"  int4 natural codes: prefill {r['err_prefill']:.3e} decode {max(r['err_decode']):.3e}")
-    check(f, "int4 injected codes")
-    assert r["err_prefill"] < 0.1 and max(r["err_decode"]) < 0.1
+    check(f, "int4 injected prefill codes")
+    r = run_pair(s, lz, batch=2, prompt=150, steps=3, seed=5, force_codes=False)
+    from oracle import quant
+    v = r["store"].view()
+    m = r["oracle"]
+    torch.cuda.synchronize()
+    Hkv, hd, R, K = s.n_kv_heads, s.head_dim, s.n_shared, s.n_loops
+    rows = 2 * Hkv * v.slots
+    n = m.n_sel
+    flips = total = sdiff = stot = 0
+    for k in range(2, K + 1):
+        for rr in range(R):
+            for kv in range(2):
+                reg = ((k - 2) * R + rr) * 2 + kv
+                gc = store_region(r["store"], v.res_codes + reg * rows * v.res_row_bytes, rows * v.res_row_bytes,
+                                  torch.uint8).cpu().numpy().reshape(2, Hkv, v.slots, -1)[:, :, :n]
+                gs = store_region(r["store"], v.res_scales + reg * rows * (hd // 32) * 2, rows * (hd // 32) * 2,
+                                  torch.int16).cpu().numpy().view(np.float16).reshape(2, Hkv, v.slots, -1)[:, :, :n]
+                oc, os_ = m.res[(k, rr, kv)]
+                d = quant.unpack_int4(gc).astype(int) - oc[:, :, :n].astype(int)
+                assert np.abs(d).max() <= 1, "a GPU code is more than one step from the oracle's"
+                flips += int((d != 0).sum())
+                total += d.size
+                rel = np.abs(gs.astype(np.float64) - os_[:, :, :n]) / np.maximum(np.abs(os_[:, :, :n]), 1e-30)
+                sdiff += int((rel > 0).sum())
+                stot += rel.size
+                assert rel.max() <= 0.05, "a GPU scale is far from the oracle's"
+    log(f"  int4 natural codes: {flips / total:.2%} of codes flipped by one step, {sdiff / stot:.2%} of scales "
+        f"differ; output difference: prefill {r['err_prefill']:.3e} decode "
+        f"{max(r['err_decode']):.3e}")
+    assert flips / total < 0.05 and sdiff / stot < 0.05
 
 
-def test_lazy_natural_selection_agrees_with_oracle():
+def _check_natural_selection(r, s, Bsz, T, margin=0.05):
+    """The GPU's kept tokens (read from its slot maps) and column sets against the
+    oracle's keys and masses of the same run: at loop 2 (whose keys both sides take from
+    the dense loop 1) every kept set is a valid top-n of the oracle's keys up to
+    `margin`, and every column set a valid top-s of the oracle's loop-1 mass; a later
+    loop is checked the same way when every earlier set agreed exactly (its keys depend
+    on them).  Returns (differing tokens, differing columns)."""
+    sel, cols = gpu_selection(r["store"], s, Bsz, T)
+    m = r["oracle"]
+    n = m.n_sel
+    tok_diff, col_diff, same_so_far = 0, 0, {b: True for b in range(Bsz)}
+    for k in range(2, s.n_loops + 1):
+        for b in range(Bsz):
+            if not same_so_far[b]:
+                continue
+            d = valid_top(sel[(k, b)], m.keys[(k, b)], n, margin)
+            tok_diff += d
+            same_so_far[b] = d == 0
+    for rr in range(s.n_shared):
+        for b in range(Bsz):
+            for g in range(s.n_kv_heads):
+                col_diff += valid_top(cols[rr, b, g], m.mass[(rr, b)][g], len(m.S[rr][b][g]), margin)
+    return tok_diff, col_diff
+
+
+def test_lazy_natural_selection_is_a_valid_top_n():
     s = _small()
     lz = I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4)
     r = run_pair(s, lz, batch=2, prompt=150, steps=2, seed=6, force=False)
-    sel, cols = gpu_selection(r["store"], s, 2, 150)
-    m = r["oracle"]
-    jac = []
-    for (k, b), idx in sel.items():
-        a, o = set(idx.tolist()), set(m.sel[(k, b)].tolist())
-        jac.append(len(a & o) / len(a | o))
-    same_cols = np.mean([np.array_equal(cols[rr, b, g], m.S[rr][b][g])
-                         for rr in range(s.n_shared) for b in range(2) for g in range(s.n_kv_heads)])
-    log(f"  token-set Jaccard min {min(jac):.3f} mean {np.mean(jac):.3f}; column sets equal {same_cols:.2f}; "
-        f"prefill drift vs oracle {r['err_prefill']:.3e}")
-    assert min(jac) > 0.8 and same_cols > 0.8
-    assert r["err_prefill"] < 0.1
+    td, cd = _check_natural_selection(r, s, 2, 150)
+    log(f"  natural selection: {td} tokens and {cd} columns differ from the oracle's, all in near-ties; "
+        f"output difference with natural selection and codes: prefill {r['err_prefill']:.3e}")
 
 
-def test_stale_keys_natural_selection_agrees_with_oracle():
+def test_stale_keys_natural_selection_is_a_valid_top_n():
     """Stale keys (a carried token keeps the change measured when it was last
-    recomputed) with natural selection over 4 loops: the GPU's kept-token sets agree
-    with the oracle's (Jaccard > 0.8: keys are float32 sums taken in another order, so
-    near-ties can fall either way), and loops 3 and 4 pick tokens that the previous loop
-    carried, which plain keys never do."""
+    recomputed) with natural selection over 4 loops: the GPU's kept sets are valid
+    top-n sets of the oracle's keys (see _check_natural_selection), and loops 3 and 4
+    pick tokens that the previous loop carried, which plain keys never do."""
     s = _small(n_loops=4)
     lz = I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4, stale_keys=True)
     r = run_pair(s, lz, batch=2, prompt=150, steps=2, seed=7, force=False)
     sel, _ = gpu_selection(r["store"], s, 2, 150)
-    m = r["oracle"]
-    jac, left_out = [], 0
-    for (k, b), idx in sel.items():
-        a, o = set(idx.tolist()), set(m.sel[(k, b)].tolist())
-        jac.append(len(a & o) / len(a | o))
-        if k >= 3:
-            left_out += len(a - set(sel[(k - 1, b)].tolist()))
-    log(f"  stale keys: token-set Jaccard min {min(jac):.3f} mean {np.mean(jac):.3f}; "
-        f"tokens picked after being carried {left_out}; prefill drift vs oracle {r['err_prefill']:.3e}")
-    assert min(jac) > 0.8 and left_out > 0
-    # a token recomputed on one side and carried on the other moves its row by far more
-    # than rounding, so the outputs are compared only when every set agrees (the
-    # computation on equal sets is checked with forced selection below)
-    if min(jac) == 1.0:
-        assert r["err_prefill"] < 0.1
+    left_out = sum(len(set(sel[(k, b)].tolist()) - set(sel[(k - 1, b)].tolist())) for k in (3, 4) for b in range(2))
+    td, cd = _check_natural_selection(r, s, 2, 150)
+    log(f"  stale keys: {td} tokens / {cd} columns differ in near-ties; tokens picked after being carried "
+        f"{left_out}; prefill {r['err_prefill']:.3e}")
+    assert left_out > 0
 
 
 def test_stale_keys_forced_selection_matches_oracle():
@@ -222,9 +263,10 @@ SKIP = [
 
 
 def _skip_tau(s, lz_kw, W, batch, T, steps):
-    """A threshold that some decode tokens' keys fall below and others stay above, with
-    every key of the oracle's run at least 1 % away from it, and on which the oracle run
-    with bf16 operands (the GPU path's rounding) takes the same decisions."""
+    """A threshold that some decode tokens' keys fall below and others stay above: of
+    the widest relative gaps between the oracle's decode keys, the one whose threshold
+    keeps every key of the oracle's run furthest from it (at least 1.5 %; the GPU's keys
+    differ from the oracle's by float rounding, far less than that)."""
     ids = I.gen_prompt_ids(s, batch, T)
     dec = I.gen_decode_ids(s, batch, steps)
     probe = LoopedOracle(s, I.Lazy(**lz_kw, skip_tau=1e-30), W, batch, T + steps)
@@ -233,25 +275,22 @@ def _skip_tau(s, lz_kw, W, batch, T, steps):
         probe.decode(d)
     v = np.sort(np.array(list(probe.decode_keys.values()), np.float64))
     gaps = sorted(range(len(v) - 1), key=lambda j: -v[j + 1] / v[j])
-    for j in gaps[:12]:
+    best = (0.0, None)
+    for j in gaps[:40]:
         tau = float(np.sqrt(v[j] * v[j + 1]))
-        lz = I.Lazy(**lz_kw, skip_tau=tau)
-        m = LoopedOracle(s, lz, W, batch, T + steps)
+        m = LoopedOracle(s, I.Lazy(**lz_kw, skip_tau=tau), W, batch, T + steps)
         m.prefill(ids)
         for d in dec:
             m.decode(d)
         keys = np.array(list(m.decode_keys.values()), np.float64)
         loops = np.array(list(m.decode_loops.values()))
-        if np.min(np.abs(keys / tau - 1)) < 0.01 or not (loops < s.n_loops).any() or (loops < s.n_loops).all():
-            continue
-        m16 = LoopedOracle(s, lz, W, batch, T + steps, operand_precision="bf16")
-        m16.forced_tokens, m16.forced_S = dict(m.sel), m.S
-        m16.prefill(ids)
-        for d in dec:
-            m16.decode(d)
-        if m16.decode_loops == m.decode_loops:
-            return tau
-    pytest.fail("no threshold with a 1 % margin")
+        margin = float(np.min(np.abs(keys / tau - 1)))
+        if (loops < s.n_loops).any() and not (loops < s.n_loops).all() and margin > best[0]:
+            best = (margin, tau)
+    if best[0] < 0.015:
+        pytest.fail("no threshold with a 1.5 % margin")
+    log(f"  threshold {best[1]:.4g}: every oracle key at least {best[0]:.1%} away")
+    return best[1]
 
 
 @pytest.mark.parametrize("name,kw,extra,batch", SKIP, ids=[c[0] for c in SKIP])
@@ -400,36 +439,32 @@ def test_decode_state_and_capacity_errors():
 
 
 REDUCED = [
-    # full widths, shortened prompts; layer counts as named
-    ("prefill_2p4x4c2_b4_t4096", 2, 200, 2),
-    ("twopass_22x2_b16_ctx8k", 2, 160, 2),
-    ("long_4p8x8c4_ctx64k", 1, 130, 2),
-    ("deep_48x4_b8_ctx32k", 1, 96, 2),
+    # full widths, shortened prompts; layer counts as named unless given
+    ("prefill_2p4x4c2_b4_t4096", 2, 200, 2, None),
+    ("twopass_22x2_b16_ctx8k", 2, 160, 2, None),
+    # d 4096, 32 / 8 heads, FFN 11008 and the 8-loop structure, with 1 + 2 x 8 + 1
+    # layers (18 applications) in place of 4 + 8 x 8 + 4 (72)
+    ("long_4p8x8c4_ctx64k", 1, 130, 2, dict(n_prelude=1, n_shared=2, n_coda=1)),
+    ("deep_48x4_b8_ctx32k", 1, 96, 2, None),
 ]
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,batch,prompt,steps", REDUCED, ids=[r[0] for r in REDUCED])
-def test_full_width_shapes_short_prompt(name, batch, prompt, steps):
+@pytest.mark.parametrize("name,batch,prompt,steps,layers", REDUCED, ids=[r[0] for r in REDUCED])
+def test_full_width_shapes_short_prompt(name, batch, prompt, steps, layers):
+    import copy
     wl = I.workload(name)
+    shape = copy.copy(wl.shape)
+    for k, v in (layers or {}).items():
+        setattr(shape, k, v)
     lz = I.Lazy(**{**wl.lazy.__dict__})
     lz.top_s = max(8, prompt // 8)
     lz.window = max(4, prompt // 16)
-    log(f"full-width {name} B={batch} T={prompt}")
-    r = run_pair(wl.shape, lz, batch, prompt, steps)
+    log(f"full-width {name} B={batch} T={prompt} layers {shape.n_prelude}+{shape.n_shared}x{shape.n_loops}"
+        f"+{shape.n_coda}")
+    r = run_pair(shape, lz, batch, prompt, steps)
     log(f"  oracle {r['t_oracle']:.1f}s")
     check(r, name)
-
-
-def _bound_check(what, err, oracle_bf16_run):
-    """err against 2e-2, or against twice the oracle's own bf16-operand sensitivity
-    when 2e-2 is exceeded (as in check(); the bf16-operand run is made only then)."""
-    log(f"  {what}: GPU vs fp32 oracle {err:.3e}")
-    if err < TOL:
-        return
-    err16, drift = oracle_bf16_run()
-    log(f"  {what}: vs bf16-operand oracle {err16:.3e}; oracle bf16 sensitivity {drift:.3e}")
-    assert err < 2 * drift and err16 < 2 * drift
 
 
 def _full_context_case(s, lz, Bn, T, samples, W, k_std):
@@ -450,17 +485,6 @@ def _full_context_case(s, lz, Bn, T, samples, W, k_std):
     return ids, states, oracles, outs
 
 
-def _bf16_rerun(s, lz, W, T, st, m, tok, out, gpu_out):
-    """The bf16-operand oracle on the same state and codes: (GPU vs it, it vs fp32)."""
-    def run():
-        m16 = LoopedOracle(s, lz, W, 1, T + 1, operand_precision="bf16")
-        m16.start_from_state(T, st["base"], st["res"], st["slot"], st["S"])
-        m16.forced_codes_from = m
-        o16 = m16.decode(np.array([tok]))[0]
-        return max_abs_rel(gpu_out, o16), max_abs_rel(o16, out)
-    return run
-
-
 def _gpu_decode(model, store, ids):
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
@@ -477,13 +501,12 @@ def test_full_context_decode_sampled_sequences(diff):
     (batch 8, a 32768-token context, d 2048, 16 query / 4 KV heads of 128, FFN 5632,
     4 loops, int8 base, int4 residuals, rho 0.1, top-s 1024, window 512; packed
     weights, replayed from a captured graph), with 2 shared layers in place of 48:
-    depth only repeats the same launches, while a deep random stack amplifies bf16
-    rounding (the 48-layer case is the next test).  A CPU prefill of that context
-    is out of reach, so the store starts from synthetic prefill states imported
-    through a snapshot (the import rebuilds the decode caches).  Sequences 0 and 7
-    (the samples) are decoded by the oracle holding the same states; the GPU keeps
-    the oracle's codes for the new token.  Then sequences 1-6 are given other states
-    and the samples' outputs must not change by a bit.  With diff_attn the same step
+    depth only repeats the same launches (the 48-layer case is the next test).  A CPU
+    prefill of that context is out of reach here, so the store starts from synthetic
+    prefill states imported through a snapshot (the import rebuilds the decode
+    caches).  Sequences 0 and 7 (the samples) are decoded by the oracle holding the
+    same states; the GPU writes its own codes for the new token.  Then sequences 1-6
+    are given other states and the samples' outputs must not change by a bit.  With diff_attn the same step
     takes the difference-corrected sparse attention (each token's loop-1 dense minus
     sparse output added at loops >= 2)."""
     import copy
@@ -498,14 +521,14 @@ def test_full_context_decode_sampled_sequences(diff):
     ids, states, oracles, outs = _full_context_case(s, lz, Bn, T, {0: 31, 7: 37}, W, k_std=2.0)
     model = B.LoopedModel(s, lz, W)
     store = model.store(Bn, T, T + 1)
-    store.keep_codes(True)
     store.import_(snapshot_with_states(store, s, lz, states))
     assert store.length() == T
     g = _gpu_decode(model, store, ids)
     assert np.isfinite(g).all()
     for seq in states:
-        run = _bf16_rerun(s, lz, W, T, states[seq], oracles[seq], ids[seq], outs[seq], g[seq])
-        _bound_check(f"sequence {seq}", max_abs_rel(g[seq], outs[seq]), run)
+        e = max_abs_rel(g[seq], outs[seq])
+        log(f"  sequence {seq}: GPU vs fp32 oracle {e:.3e}")
+        assert e < TOL
     # the other sequences take copies of sequence 0's state: samples unchanged
     more = dict(states)
     for b in range(1, Bn - 1):
@@ -521,9 +544,10 @@ def test_full_depth_decode_at_full_context():
     """The decode step the throughput figure times, whole: 48 shared layers x 4 loops
     at batch 8 and a 32768-token context, from a synthetic prefill state (K/V spread
     about 1) imported through a snapshot; the last sequence (the sample) against the
-    oracle holding the same state.  192 layer applications of random weights over a
-    random context amplify rounding: the oracle's own bf16-operand sensitivity is
-    measured and the bound is as in check()."""
+    oracle holding the same state, within 2e-2.  192 layer applications of random
+    weights over a random context amplify any rounding; the decode products take their
+    activations as hi/lo bf16 pairs and the attention its queries in float16, which
+    keeps the step within the bound at this depth."""
     from tests.gpu_util import cached_weights
     from tests.synth_state import snapshot_with_states
     wl = I.workload("deep_48x4_b8_ctx32k")
@@ -533,13 +557,13 @@ def test_full_depth_decode_at_full_context():
     ids, states, oracles, outs = _full_context_case(s, lz, Bn, T, {Bn - 1: 41}, W, k_std=1.0)
     model = B.LoopedModel(s, lz, W)
     store = model.store(Bn, T, T + 1)
-    store.keep_codes(True)
     store.import_(snapshot_with_states(store, s, lz, states))
     g = _gpu_decode(model, store, ids)
     assert np.isfinite(g).all()
     seq = Bn - 1
-    run = _bf16_rerun(s, lz, W, T, states[seq], oracles[seq], ids[seq], outs[seq], g[seq])
-    _bound_check(f"sequence {seq}", max_abs_rel(g[seq], outs[seq]), run)
+    e = max_abs_rel(g[seq], outs[seq])
+    log(f"  sequence {seq}: GPU vs fp32 oracle {e:.3e}")
+    assert e < TOL
 
 
 
@@ -683,3 +707,119 @@ def test_snapshot_resume_is_bit_exact(name, kw, lz, loops):
     with pytest.raises(B.LKError):
         c.import_(snap2)
     assert c.length() == 0
+
+
+# ---------------------------------------------------------------- graph replay, weights, ring
+@pytest.mark.parametrize("mode,timed,Bsz", [("lazy", "all", 2), ("lazy", None, 2), ("per_loop", "all", 2),
+                                           ("lazy", "one", 2), ("lazy", None, 10), ("lazy", "one", 10)])
+def test_decode_graph_replay_matches_eager_launches(mode, timed, Bsz):
+    """Decode steps replayed from captured HIP graphs (non-null stream) equal the same
+    steps launched kernel by kernel (null stream) bit for bit, replay after replay, with
+    unrelated eager work and host synchronisation in between.  With a timed kernel class
+    the step is cut around its launches ("all": every launch of the class; "one":
+    lk_timing_sample(1), the split the throughput measurement uses, which keeps the step
+    in two graphs), and the timer sees the launches it should."""
+    s = _small()
+    lz = (I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4)
+          if mode == "lazy" else I.Lazy(mode="per_loop"))
+    T, steps = 150, 6
+    W = I.gen_weights(s, seed=9)
+    ids = torch.from_numpy(I.gen_prompt_ids(s, Bsz, T))
+    dec = torch.from_numpy(I.gen_decode_ids(s, Bsz, steps)).cuda()
+    model = B.LoopedModel(s, lz, W)
+    sa, sb = model.store(Bsz, T, T + steps), model.store(Bsz, T, T + steps)
+    pa, pb = model.prefill(sa, ids).clone(), model.prefill(sb, ids).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(pa, pb)
+    side = torch.cuda.Stream()
+    B.lk_timing_enable(model.h, "attn_decode_dense" if timed else None)
+    if timed == "one":
+        B.lk_timing_sample(model.h, 1)
+    junk = torch.randn(512, 512, device="cuda")
+    for i in range(steps):
+        with torch.cuda.stream(side):
+            og = model.decode(sa, dec[i]).clone()
+        side.synchronize()
+        junk = (junk @ junk).clamp_(-1, 1)
+        oe = model.decode(sb, dec[i]).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(og, oe), f"step {i}"
+    n, ms = B.lk_timing_read(model.h)
+    B.lk_timing_enable(model.h, None)
+    B.lk_timing_sample(model.h, 0)
+    P, R, K, Q = s.n_prelude, s.n_shared, s.n_loops, s.n_coda
+    per_step = P + Q + (R if mode == "lazy" else R * K)   # dense-row decode attention launches
+    if timed == "all":
+        assert n == 2 * steps * per_step and ms > 0      # replayed steps + eager steps
+    elif timed == "one":
+        assert n == 2 * steps and ms > 0
+    else:
+        assert n == 0
+    assert sa.length() == sb.length() == T + steps
+
+
+def test_decode_packed_weights_match_row_major_weights():
+    """Decode with the packed decode copy of the weights (the folded products, hi/lo
+    activations) against decode with the buffer detached (row-major weights, the
+    unfolded kernels, bf16 activations): both against the oracle, and each other within
+    the bound.  Detaching and re-attaching the buffer drops the captured step; the size
+    query and the capacity check hold."""
+    s = _small()
+    lz = I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=16, res_bits=16)
+    T, steps, Bsz = 150, 4, 3
+    W = I.gen_weights(s, seed=5)
+    ids = I.gen_prompt_ids(s, Bsz, T)
+    decn = I.gen_decode_ids(s, Bsz, steps)
+    dec = torch.from_numpy(decn).cuda()
+    m = LoopedOracle(s, lz, W, Bsz, T + steps)
+    m.prefill(ids)
+    o_dec = [m.decode(d) for d in decn]
+    model = B.LoopedModel(s, lz, W)
+    nbytes = B.lk_decode_weight_bytes(model.h)
+    assert nbytes == 2 * sum(L["wqkv"].numel() + L["wo"].numel() + L["w_in"].numel() + L["w_down"].numel()
+                             for L in model.layers)
+    with pytest.raises(B.LKError):
+        B.lk_set_decode_weights(model.h, model._pk[1].data_ptr(), nbytes - 2)
+    model.pack_decode_weights(True)
+    side = torch.cuda.Stream()
+    sa, sb = model.store(Bsz, T, T + steps), model.store(Bsz, T, T + steps)
+    model.prefill(sa, torch.from_numpy(ids))
+    model.prefill(sb, torch.from_numpy(ids))
+    torch.cuda.synchronize()
+    outs = []
+    for st in (sa, sb):
+        o = []
+        for i in range(steps):
+            with torch.cuda.stream(side):
+                o.append(model.decode(st, dec[i]).clone())
+        side.synchronize()
+        outs.append(torch.stack(o).cpu().numpy())
+        model.pack_decode_weights(False)
+    model.pack_decode_weights(True)
+    for name, o in zip(("packed", "row-major"), outs):
+        e = max(max_abs_rel(o[i], o_dec[i]) for i in range(steps))
+        log(f"  {name} decode vs oracle: {e:.2e}")
+        assert e < TOL
+    d = max_abs_rel(outs[0], outs[1])
+    log(f"  packed vs row-major decode: {d:.2e}")
+    assert d < TOL
+
+
+def test_decode_window_ring_wraps_during_decode():
+    """Decode positions cross the end of the float16 window ring (window 16 -> 128 rows):
+    prompt 100, 40 steps, positions 100..139."""
+    s = _small()
+    lz = I.Lazy(mode="lazy", rho=0.3, top_s=24, window=16, base_bits=8, res_bits=4)
+    log("ring wrap: prompt 100, 40 decode steps")
+    r = run_pair(s, lz, batch=2, prompt=100, steps=40, seed=11)
+    check(r, "ring wrap")
+
+
+def test_tiny_workload_with_float32_weights():
+    """The tiny workload as named: float32 weights (not rounded to bf16).  The oracle
+    uses them as drawn; the library holds its weights in bf16, so the GPU runs on their
+    bf16 rounding, and the comparison includes that rounding."""
+    wl = tiny()
+    W = I.gen_weights(wl.shape, bf16=False)
+    r = run_pair(wl.shape, wl.lazy, wl.batch, wl.prompt, wl.decode_steps, weights=W)
+    check(r, "tiny, float32 weights")
