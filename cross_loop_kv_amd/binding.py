@@ -107,6 +107,7 @@ _SIGS = {
                                     C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "lk_looped_decode_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_size_t, C.c_void_p]),
+    "lk_looped_decode_step_static": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "lk_effective_depth": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32)]),
     "lk_last_error": (C.c_char_p, []),
     "lk_kv_store_view": (C.c_int, [C.c_void_p, C.POINTER(lk_store_view)]),
@@ -237,6 +238,10 @@ def lk_looped_prefill(h, s, d_ids, B, T, d_out, d_ws, ws_bytes, stream=None) -> 
 
 def lk_looped_decode_step(h, s, d_ids, d_out, d_ws, ws_bytes, stream=None) -> None:
     _check(lib().lk_looped_decode_step(h, s, d_ids, d_out, d_ws, ws_bytes, _stream(stream)))
+
+
+def lk_looped_decode_step_static(h, s, d_ids, d_out, stream=None) -> None:
+    _check(lib().lk_looped_decode_step_static(h, s, d_ids, d_out, _stream(stream)))
 
 
 def lk_effective_depth(h: int) -> int:

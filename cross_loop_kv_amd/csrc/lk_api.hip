@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1455,6 +1456,33 @@ int capture_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
     return rc;
 }
 
+// Decode workspace for callers that cannot allocate (lk_looped_decode_step_static): a
+// file-scope device array, one copy per GPU, which every such call on that GPU shares.
+// Host code never passes `scratch` itself (on the host it is a stand-in, not a device
+// address): each device's address comes from hipGetSymbolAddress, taken once per device
+// with that device current, and the kernels receive that address.
+constexpr size_t kStaticScratchBytes = 64ull << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+    int dev = -1;
+    LK_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(LK_ERR_UNSUPPORTED, "device index beyond the static scratch table");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(LK_ERR_HIP, std::string("static scratch address: ") + hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return LK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1498,6 +1526,28 @@ int lk_looped_decode_step(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, fl
         LK_TRY(enqueue_decode(h, s, w, st));
     }
     LK_HIP(hipMemcpyAsync(d_out, w.out, (size_t)B * d * 4, hipMemcpyDeviceToDevice, st));
+    s->t += 1;
+    return LK_OK;
+}
+
+int lk_looped_decode_step_static(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, float* d_out, void* stream) {
+    if (!h || !s || !d_ids || !d_out) return fail(LK_ERR_INVALID_ARG, "null argument");
+    if (s->h != h) return fail(LK_ERR_INVALID_ARG, "store belongs to another handle");
+    if (!s->prefilled) return fail(LK_ERR_STATE, "decode before prefill");
+    if (s->t >= s->Tmax) return fail(LK_ERR_CAPACITY, "store is full (max_tokens reached)");
+    const int B = s->B;
+    const size_t need = ws_layout(h, B, 1, nullptr).total;
+    if (need > kStaticScratchBytes)
+        return fail(LK_ERR_CAPACITY, "the decode workspace of this model and batch (" + std::to_string(need) +
+                                         " bytes) exceeds the static scratch (" +
+                                         std::to_string(kStaticScratchBytes) + " bytes)");
+    void* ws = nullptr;
+    LK_TRY(static_scratch(&ws));
+    const WS w = ws_layout(h, B, 1, (char*)ws);
+    hipStream_t st = (hipStream_t)stream;
+    LK_HIP(hipMemcpyAsync(w.ids, d_ids, (size_t)B * 4, hipMemcpyDeviceToDevice, st));
+    LK_TRY(enqueue_decode(h, s, w, st));
+    LK_HIP(hipMemcpyAsync(d_out, w.out, (size_t)B * h->c.d_model * 4, hipMemcpyDeviceToDevice, st));
     s->t += 1;
     return LK_OK;
 }

@@ -198,6 +198,20 @@ int lk_looped_prefill(lk_handle *h, lk_kv_store *s, const int32_t *d_ids, int32_
 int lk_looped_decode_step(lk_handle *h, lk_kv_store *s, const int32_t *d_ids, float *d_out,
                           void *d_ws, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory or call allocating routines (code
+ * that a caller records into its own HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc): lk_looped_decode_step with the workspace taken from a static
+ * device array of 64 MiB per GPU that the library holds until the process ends, and
+ * with the step's kernels launched on `stream` one by one (no graph of its own, so a
+ * caller's capture records them).  Same arguments and results as
+ * lk_looped_decode_step otherwise.  LK_ERR_CAPACITY when the decode workspace of this
+ * model and batch (lk_workspace_bytes(batch, 1)) exceeds 64 MiB.  Every call on one
+ * GPU uses that GPU's one array: calls that overlap on a GPU (other streams, other
+ * threads, other handles) race and must be ordered by the caller; the array keeps
+ * the last call's contents, and a step writes every part of it that it reads. */
+int lk_looped_decode_step_static(lk_handle *h, lk_kv_store *s, const int32_t *d_ids, float *d_out,
+                                 void *stream);
+
 /* Graph replay of decode steps on (enable != 0, the default) or off (every
  * step launches its kernels one by one).  Drops any captured step. */
 int lk_set_decode_graphs(lk_handle *h, int32_t enable);
