@@ -56,6 +56,13 @@ def parse():
     ap.add_argument("--drift-batch", type=int, default=2,
                     help="sequences of the prompt compared lazy versus dense (full context)")
     ap.add_argument("--drift-steps", type=int, default=8)
+    ap.add_argument("--no-baselines", action="store_true",
+                    help="skip the dense per-loop, last-loop and bf16-base decode baselines")
+    ap.add_argument("--baseline-steps", type=int, default=32)
+    ap.add_argument("--sweep", action="store_true",
+                    help="only the rho x residual-bits frontier of the long-context workload: one JSON "
+                         "line per point (tokens/s, KV bytes/token, drift against dense per-loop)")
+    ap.add_argument("--sweep-steps", type=int, default=64)
     ap.add_argument("--gemm-shapes", action="store_true",
                     help="only time the prefill projection GEMMs of the workload, per shape, next to "
                          "torch.matmul (hipBLASLt, bf16 output) as a reference; one JSON line per shape")
@@ -90,6 +97,138 @@ def prefill_gemm_flops(shape, lazy, batch, T):
         dense_apps = s.n_prelude + s.n_coda + s.n_shared * s.n_loops
         sparse_rows = 0
     return per_row * (batch * T * dense_apps + sparse_rows)
+
+
+def prefill_attention_flops(shape, lazy, batch, T):
+    """Algorithmic flops of one prefill's dense causal attention launches (prelude, coda
+    and loop 1; every loop in the dense modes): Q K^T and P V over the causal half,
+    2 hd flops per (query, key <= query, head) each; and of its column-mass launches
+    (lazy loop 1): one more Q K^T over the causal half."""
+    s = shape
+    pairs = T * (T + 1) / 2.0
+    dense_layers = s.n_prelude + s.n_coda + (s.n_shared if lazy.mode == "lazy" else s.n_shared * s.n_loops)
+    attn = 4.0 * s.head_dim * s.n_heads * pairs * batch * dense_layers
+    mass = 2.0 * s.head_dim * s.n_heads * pairs * batch * (s.n_shared if lazy.mode == "lazy" else 0)
+    return attn, mass
+
+
+def decode_run(model, store, dec, warmup, steps, timer=None):
+    """Decode `warmup` then `steps` timed steps on a dedicated stream (graph replay);
+    returns (seconds of the timed steps, last output)."""
+    import torch
+    from cross_loop_kv_amd import binding as B
+    dout = torch.empty(store.batch, model.shape.d_model, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    B.lk_timing_enable(model.h, timer)
+    B.lk_timing_sample(model.h, 1)
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            model.decode(store, dec[i], out=dout)
+    torch.cuda.synchronize()
+    B.lk_timing_read(model.h)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            model.decode(store, dec[warmup + i], out=dout)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, dout
+
+
+def decode_baseline(model, wl, lazy, ids, dec, warmup, steps):
+    """Decode throughput of another cache policy over the same device weights (a sibling
+    handle): its own prefill of the same prompt (untimed), then timed decode steps."""
+    import torch
+    Bsz, T = ids.shape
+    sib = model.sibling(lazy)
+    st = sib.store(Bsz, T, T + warmup + steps)
+    t0 = time.time()
+    sib.prefill(st, ids)
+    torch.cuda.synchronize()
+    prefill_s = time.time() - t0
+    el, dout = decode_run(sib, st, dec, warmup, steps)
+    assert torch.isfinite(dout).all().item()
+    shared, _ = st.bytes_used()
+    cache = st.cache_bytes()
+    t_now = st.length()
+    res = {"mode": lazy.mode, "tokens_per_s": round(Bsz * steps / el, 2), "ms_per_step": round(el * 1e3 / steps, 3),
+           "steps": steps, "prefill_s": round(prefill_s, 2),
+           "kv_bytes_per_token_store_only": round(shared / (Bsz * t_now), 1),
+           "kv_bytes_per_token": round((shared + cache) / (Bsz * t_now), 1)}
+    if lazy.mode == "lazy":
+        res["base_bits"] = lazy.base_bits
+        res["res_bits"] = lazy.res_bits
+    del st
+    sib.close()
+    del sib
+    torch.cuda.empty_cache()
+    log(f"baseline {res}")
+    return res
+
+
+def frontier_sweep(args):
+    """The long-context workload's speed / KV-memory / drift frontier: for rho in
+    {1, .5, .25, .1} and residual bits in {16, 8, 4}, a lazy prefill of the 65536-token
+    prompt and timed decode steps, against dense per-loop inference over the same
+    weights, prompt and decode tokens (drift of the prefill outputs and of every
+    decode step's output).  One JSON line per point."""
+    import torch
+    from cross_loop_kv_amd import binding as B
+    from cross_loop_kv_amd import inputs as I
+    wl = I.workload("long_4p8x8c4_ctx64k")
+    s, Bsz, T = wl.shape, wl.batch, wl.prompt
+    warm, steps = 8, args.sweep_steps
+    ids = torch.from_numpy(I.gen_prompt_ids(s, Bsz, T)).cuda()
+    dec = torch.from_numpy(I.gen_decode_ids(s, Bsz, warm + steps)).cuda()
+    dense_lz = I.Lazy(mode="per_loop")
+    model = B.LoopedModel(s, dense_lz, I.iter_weights(s))
+
+    def run(m, lz):
+        st = m.store(Bsz, T, T + warm + steps)
+        t0 = time.time()
+        p = m.prefill(st, ids)
+        torch.cuda.synchronize()
+        pf = time.time() - t0
+        outs, t_dec = [], 0.0
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            for i in range(warm + steps):
+                if i == warm:
+                    stream.synchronize()
+                    t0 = time.perf_counter()
+                outs.append(m.decode(st, dec[i]).clone())
+        stream.synchronize()
+        t_dec = time.perf_counter() - t0
+        shared, _ = st.bytes_used()
+        cache = st.cache_bytes()
+        t_now = st.length()
+        info = {"prefill_s": round(pf, 2), "tokens_per_s": round(Bsz * steps / t_dec, 2),
+                "kv_bytes_per_token_store_only": round(shared / (Bsz * t_now), 1),
+                "kv_bytes_per_token": round((shared + cache) / (Bsz * t_now), 1)}
+        del st
+        torch.cuda.empty_cache()
+        return p, torch.stack(outs[warm:], 0), info
+
+    dp, dd, dinfo = run(model, dense_lz)
+    log(f"dense per-loop: {dinfo}")
+    E = 2 * s.n_kv_heads * s.head_dim
+    dense_tok = 2 * s.n_shared * s.n_loops * E
+    for rho in (1.0, 0.5, 0.25, 0.1):
+        for bits in (16, 8, 4):
+            lz = copy.deepcopy(wl.lazy)
+            lz.rho, lz.res_bits = rho, bits
+            sib = model.sibling(lz)
+            p, d, info = run(sib, lz)
+            sib.close()
+            del sib
+            point = {"sweep": "long_4p8x8c4_ctx64k", "rho": rho, "res_bits": bits, "base_bits": lz.base_bits,
+                     "top_s": lz.top_s, "window": lz.window, "decode_steps": steps, **info,
+                     "kv_reduction_store_only": round(dense_tok / info["kv_bytes_per_token_store_only"], 3),
+                     "dense_per_loop_tokens_per_s": dinfo["tokens_per_s"],
+                     "speedup_vs_dense": round(info["tokens_per_s"] / dinfo["tokens_per_s"], 3),
+                     "drift_prefill": drift_stats(p, dp), "drift_decode": drift_stats(d, dd)}
+            print(json.dumps(point), flush=True)
+            del p, d
+            torch.cuda.empty_cache()
 
 
 def gemm_shapes(args):
@@ -238,7 +377,8 @@ def cpu_baseline(wl, n_steps=8, rng_seed=3):
     (what a prefill leaves: base, kept-row residuals, slot maps, column sets),
     scaled to the R shared layers of the workload."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    import torch
+    from threadpoolctl import threadpool_limits
 
     from cross_loop_kv_amd import inputs as I
     from oracle.model import LoopedOracle
@@ -278,13 +418,15 @@ def cpu_baseline(wl, n_steps=8, rng_seed=3):
     else:
         m.T = m.t = T   # dense rows of a T-token prompt, left at zero
     ids = I.gen_decode_ids(s1, B, n_steps)
-    t0 = time.time()
-    for i in range(n_steps):
-        m.decode(ids[i])
-    dt = time.time() - t0
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    with threadpool_limits(limits=cores):
+        t0 = time.time()
+        for i in range(n_steps):
+            m.decode(ids[i])
+        dt = time.time() - t0
     step_s = dt / n_steps * R_full
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": B / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": B / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": (f"{n_steps} decode steps of batch {B} at context {T + 1}..{T + n_steps} through 1 shared "
                        f"layer x {s1.n_loops} loops ({s1.n_loops} layer applications each) on a synthetic store, "
                        f"{dt:.1f} s, scaled x{R_full} to the {R_full}-layer stack")}
@@ -307,6 +449,9 @@ def main():
     torch.cuda.set_device(0)
     if args.gemm_shapes:
         gemm_shapes(args)
+        return
+    if args.sweep:
+        frontier_sweep(args)
         return
     wl = I.workload(args.workload)
     if args.prompt:
@@ -332,14 +477,18 @@ def main():
     ids = torch.from_numpy(I.gen_prompt_ids(s, Bsz, T)).cuda()
     dec = torch.from_numpy(I.gen_decode_ids(s, Bsz, args.warmup + args.steps)).cuda()
     torch.cuda.synchronize()
-    # every projection GEMM of the prefill runs between two HIP events
-    B.lk_timing_enable(model.h, "gemm_prefill")
+    # every projection GEMM, dense attention and column-mass launch of the prefill runs
+    # between two HIP events
+    B.lk_timing_enable(model.h, "gemm_prefill,attn_prefill,column_mass")
     B.lk_timing_sample(model.h, 0)
     t0 = time.time()
     out = model.prefill(store, ids)
     torch.cuda.synchronize()
     prefill_s = time.time() - t0
-    g_launches, g_ms = B.lk_timing_read(model.h)
+    g_launches, g_ms = B.lk_timing_read_class(model.h, "gemm_prefill")
+    a_launches, a_ms = B.lk_timing_read_class(model.h, "attn_prefill")
+    m_launches, m_ms = B.lk_timing_read_class(model.h, "column_mass")
+    B.lk_timing_read(model.h)
     assert torch.isfinite(out).all().item(), "non-finite prefill output"
     del out
     log(f"prefill {Bsz}x{T}: {prefill_s:.2f}s (projection GEMMs {g_ms / 1e3:.2f}s over {g_launches} launches)")
@@ -435,13 +584,6 @@ def main():
         "achieved": round(g_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
         "frac": round(g_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "launches_timed": g_launches,
         "algorithmic_flops": int(g_flops), "time_ms": round(g_ms, 2)}
-    if not args.no_drift:
-        del store
-        log(f"drift: lazy vs dense per-loop, {args.drift_batch} sequences at context {T}...")
-        res["drift"] = measure_drift(model, wl, ids, dec, min(args.drift_batch, Bsz), args.drift_steps)
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle sample)...")
-        res["cpu_baseline"] = cpu_baseline(wl)
     if getattr(lz, "skip_tau", 0.0) and lz.mode == "lazy" and s.n_loops > 1:
         # share of the decode tokens' loop-k rows (k >= 2) that were stored, from the slot maps
         v = store.view()
@@ -449,6 +591,36 @@ def main():
         sm = store.buf[off:off + (s.n_loops - 1) * Bsz * v.row_stride * 4].view(torch.int32)
         sm = sm.view(s.n_loops - 1, Bsz, v.row_stride)[:, :, T:t_now]
         res["skip"] = {"tau": lz.skip_tau, "decode_loop_rows_stored_frac": round(float((sm >= 0).float().mean()), 4)}
+    a_flops, m_flops = prefill_attention_flops(s, lz, Bsz, T)
+    res["roofline_prefill_attention"] = {
+        "kernel": "attn_prefill_fa_kernel (loop-1 causal attention over the prompt)", "bound": "mfma",
+        "achieved": round(a_flops / (a_ms * 1e-3) / 1e12, 1) if a_ms > 0 else None,
+        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(a_flops / (a_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4) if a_ms > 0 else None,
+        "launches_timed": a_launches, "algorithmic_flops": int(a_flops), "time_ms": round(a_ms, 2),
+        "column_mass": {"achieved": round(m_flops / (m_ms * 1e-3) / 1e12, 1) if m_ms > 0 else None,
+                        "frac": round(m_flops / (m_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4) if m_ms > 0 else None,
+                        "launches_timed": m_launches, "algorithmic_flops": int(m_flops),
+                        "time_ms": round(m_ms, 2)}}
+    if not args.no_baselines and lz.mode == "lazy":
+        # the same workload under the dense per-loop cache, the last-loop-only cache and a
+        # bf16 loop-1 base, on the same weights, prompt and decode tokens
+        del store
+        torch.cuda.empty_cache()
+        base = []
+        for blz in (I.Lazy(mode="per_loop"), I.Lazy(mode="last_loop"),
+                    I.Lazy(**{**lz.__dict__, "base_bits": 16})):
+            base.append(decode_baseline(model, wl, blz, ids, dec, 8, args.baseline_steps))
+        res["baselines"] = {b["mode"] + ("_bf16_base" if b.get("base_bits") == 16 else ""): b for b in base}
+        res["baselines"]["lazy_speedup_vs_per_loop"] = round(value / base[0]["tokens_per_s"], 3)
+        store = None
+    if not args.no_drift:
+        del store
+        log(f"drift: lazy vs dense per-loop, {args.drift_batch} sequences at context {T}...")
+        res["drift"] = measure_drift(model, wl, ids, dec, min(args.drift_batch, Bsz), args.drift_steps)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle sample)...")
+        res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)
 
 

@@ -119,6 +119,7 @@ _SIGS = {
     "lk_decode_weight_bytes": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t)]),
     "lk_set_decode_weights": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "lk_timing_read": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
+    "lk_timing_read_class": (C.c_int, [C.c_void_p, C.c_char_p, C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
     "lk_dbg_topk": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
     "lk_dbg_quantize": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
                                   C.c_void_p, C.c_void_p]),
@@ -289,6 +290,12 @@ def lk_timing_enable(h: int, kernel_class: Optional[str]) -> None:
 def lk_timing_read(h: int) -> Tuple[int, float]:
     n, ms = C.c_int32(), C.c_double()
     _check(lib().lk_timing_read(h, C.byref(n), C.byref(ms)))
+    return n.value, ms.value
+
+
+def lk_timing_read_class(h: int, kernel_class: str) -> Tuple[int, float]:
+    n, ms = C.c_int32(), C.c_double()
+    _check(lib().lk_timing_read_class(h, kernel_class.encode(), C.byref(n), C.byref(ms)))
     return n.value, ms.value
 
 

@@ -548,6 +548,208 @@ __global__ __launch_bounds__(256) void column_mass_kernel(const u16* __restrict_
 // when no sequence is left in the loops (*a.live == 0).
 enum { RT_BF16 = 0, RT_I8 = 1, RT_F16 = 2, RT_F16_2SEG = 3, RT_F16_2SEG_LIVE = 4 };
 
+// One 32-key tile [kb, kb + 32) of the decode attention for the wave that calls it: keys
+// in [c_lo, c_end) take part, row_of(key) is the key's row in kv.  Lane (kgrp, head c16)
+// holds the Q^T operand qop and the wave's running max m, sum l and O^T tiles oacc.
+template <int HD, int G, int RT, class RowOf>
+__device__ __forceinline__ void decode_tile(const KVLayer& kv, int b, int g, int kb, int c_lo, int c_end,
+                                            RowOf row_of, const uint4 (&qop)[HD / 32], f32x4 (&oacc)[HD / 16],
+                                            float& m, float& l, float sl2, int c16, int kgrp) {
+    constexpr bool I8 = RT == RT_I8;
+    constexpr bool HALF = RT != RT_BF16;  // f16 MFMA (int8 codes are converted to f16)
+    constexpr int NQ = HD / 32;
+    constexpr int NE = HD / 16;
+    constexpr bool KPERM = I8 && NQ % 2 == 0;
+    // V operands of the tile are loaded first, so that K and V are in flight together.
+    // int8 V: one 16-byte load per pair of O^T tiles; tile et's row r is head dim
+    // vdim(et, r) = 32 (et/2) + 2 r + et%2 (the 8 keys of dims e and e + 1 are adjacent)
+    const int pos0 = row_of(min(kb + 8 * kgrp, ((c_end - 1) >> 3) << 3));
+    uint4 vraw[I8 ? NE / 2 : NE], vsc[I8 ? NE / 2 : 1];
+    if (I8) {
+#pragma unroll
+        for (int pp = 0; pp < NE / 2; ++pp) {
+            vraw[pp] = *(const uint4*)((const int8_t*)kv.base[1] + v_elem(kv, b, g, pos0, 32 * pp + 2 * c16));
+            vsc[pp] = *(const uint4*)(kv.base_scale[1] + v_scale_idx(kv, b, g, pos0, pp));
+        }
+    } else {
+#pragma unroll
+        for (int et = 0; et < NE; ++et) vraw[et] = *(const uint4*)((const u16*)kv.base[1] + v_elem(kv, b, g, pos0, 16 * et + c16));
+    }
+    // ---- S^T = K Q^T: n-tile nt covers keys kb + 8*(r/4) + 4*nt + r%4 for row r
+    f32x4 sacc[2];
+    long long krow[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+        krow[nt] = kv_row(kv, b, g, row_of(min(kb + 8 * (c16 >> 2) + 4 * nt + (c16 & 3), c_end - 1)));
+    uint4 kraw[2][KPERM ? NQ / 2 : 1];
+    uint32_t kscl[2][KPERM ? NQ / 2 : 1];
+    if (KPERM) {  // all K codes and scales of the tile first
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int hh = 0; hh < NQ / 2; ++hh) {
+                kraw[nt][hh] = *(const uint4*)((const int8_t*)kv.base[0] + krow[nt] * HD + 64 * hh + 16 * kgrp);
+                kscl[nt][hh] = kv.base_scale[0][krow[nt] * NQ + 2 * hh + (kgrp >> 1)];
+            }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const long long row = krow[nt];
+        sacc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (KPERM) {
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                const uint4 c4 = kraw[nt][j >> 1];
+                const uint2 c = (j & 1) ? make_uint2(c4.z, c4.w) : make_uint2(c4.x, c4.y);
+                const uint32_t sp = kscl[nt][j >> 1] | (kscl[nt][j >> 1] << 16);
+                const uint4 kf = i8x8_to_f16(c, make_uint4(sp, sp, sp, sp));
+                sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kf), as_half8(qop[j]), sacc[nt], 0, 0, 0);
+            }
+        } else if (I8) {
+            const u16* ks = kv.base_scale[0] + row * NQ;
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                const uint2 c = *(const uint2*)((const int8_t*)kv.base[0] + row * HD + 32 * j + 8 * kgrp);
+                const uint32_t s1 = ks[j];
+                const uint32_t sp = s1 | (s1 << 16);
+                const uint4 kf = i8x8_to_f16(c, make_uint4(sp, sp, sp, sp));
+                sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kf), as_half8(qop[j]), sacc[nt], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                const uint4 kf = *(const uint4*)((const u16*)kv.base[0] + row * HD + 32 * j + 8 * kgrp);
+                if (HALF)
+                    sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kf), as_half8(qop[j]), sacc[nt], 0, 0, 0);
+                else
+                    sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qop[j]), sacc[nt], 0, 0, 0);
+            }
+        }
+    }
+    // lane (kgrp, head c16) holds keys kb + 8kgrp + 4nt + i
+    float s[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = kb + 8 * kgrp + 4 * nt + i;
+            const float v = (key >= c_lo && key < c_end) ? sacc[nt][i] * sl2 : -INFINITY;
+            s[nt * 4 + i] = v;
+            mx = fmaxf(mx, v);
+        }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - m_new);
+    float p[8];
+    float rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        p[j] = (s[j] == -INFINITY) ? 0.f : exp2f(s[j] - m_new);
+        rs += p[j];
+    }
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    l = l * alpha + rs;
+    m = m_new;
+#pragma unroll
+    for (int et = 0; et < NE; ++et) oacc[et] *= alpha;
+    // ---- O^T += V^T P^T; lane (e, kgrp): V[keys kb+8kgrp .. +8][e] is one contiguous run
+    uint4 pu;
+    if (HALF) {
+        pu.x = (uint32_t)f2h_bits(p[0]) | ((uint32_t)f2h_bits(p[1]) << 16);
+        pu.y = (uint32_t)f2h_bits(p[2]) | ((uint32_t)f2h_bits(p[3]) << 16);
+        pu.z = (uint32_t)f2h_bits(p[4]) | ((uint32_t)f2h_bits(p[5]) << 16);
+        pu.w = (uint32_t)f2h_bits(p[6]) | ((uint32_t)f2h_bits(p[7]) << 16);
+    } else {
+        pu.x = pack_bf2(p[0], p[1]);
+        pu.y = pack_bf2(p[2], p[3]);
+        pu.z = pack_bf2(p[4], p[5]);
+        pu.w = pack_bf2(p[6], p[7]);
+    }
+    const int valid = c_end - (kb + 8 * kgrp);
+    // rows past the end of the context are unwritten: clamp the block address, zero the values
+#pragma unroll
+    for (int et = 0; et < NE; ++et) {
+        uint4 vf;
+        if (I8) {
+            const uint4 c4 = vraw[et >> 1];
+            const uint2 c = (et & 1) ? make_uint2(c4.z, c4.w) : make_uint2(c4.x, c4.y);
+            vf = i8x8_to_f16(c, vsc[et >> 1]);
+        } else {
+            vf = vraw[et];
+        }
+        vf = mask_tail8(vf, valid);
+        if (HALF)
+            oacc[et] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(vf), as_half8(pu), oacc[et], 0, 0, 0);
+        else
+            oacc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), as_bf16x8(pu), oacc[et], 0, 0, 0);
+    }
+}
+
+// Q^T operand of the decode attention for lane (kgrp, head c16) of KV head g of sequence
+// b: q rotated here from the float32 projections (fuse_kv; one rounding to the
+// operand type) or read from a.q (bf16, or float16 bits when q_half).
+template <int HD, int G, int RT>
+__device__ __forceinline__ void decode_q(const RowsAttn& a, int b, int g, int c16, int kgrp, uint4 (&qop)[HD / 32]) {
+    constexpr bool I8 = RT == RT_I8;
+    constexpr bool HALF = RT != RT_BF16;
+    constexpr int NQ = HD / 32;
+    const int Hkv = a.kv.Hkv;
+    // int8 rows (hd >= 64): lane (key, kgrp) reads 16 bytes at 64h + 16 kgrp of its K row
+    // for h < NQ / 2, so every load covers 64 contiguous bytes of each key; k-step j
+    // takes elements 64 (j/2) + 16 kgrp + 8 (j%2) .. +8.  Other rows: 32 j + 8 kgrp.
+    constexpr bool KPERM = I8 && NQ % 2 == 0;
+    auto kslice = [&](int j) { return KPERM ? 64 * (j >> 1) + 16 * kgrp + 8 * (j & 1) : 32 * j + 8 * kgrp; };
+    // Q^T operand: lane (head c16, kgrp) holds q[h][kslice(j) .. +8]
+    const bool hvalid = c16 < G;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (hvalid && a.fuse_kv) {  // rotate the float32 projection here
+            // the 8 elements e0.. are pairs i0.. (one half of the head): 16-byte loads
+            const int e0 = kslice(j), i0 = e0 % (HD / 2);
+            const float* qh = a.qkv + (long long)b * (a.H + 2 * Hkv) * HD + (g * G + c16) * HD;
+            float x1[8], x2[8], cs[16];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                *(float4*)&x1[4 * t] = *(const float4*)(qh + i0 + 4 * t);
+                *(float4*)&x2[4 * t] = *(const float4*)(qh + i0 + HD / 2 + 4 * t);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) *(float4*)&cs[4 * t] = *(const float4*)(a.rope_cs + 2 * i0 + 4 * t);
+            const bool lo = e0 < HD / 2;
+            uint32_t o[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                float r2[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int m = 2 * t + u;
+                    const float c = cs[2 * m], sn = cs[2 * m + 1];
+                    r2[u] = lo ? rope_lo(x1[m], x2[m], c, sn) : rope_hi(x1[m], x2[m], c, sn);
+                }
+                // the float16 kernels take the rotated float32 q with one rounding
+                o[t] = HALF ? ((uint32_t)f2h_bits(r2[0]) | ((uint32_t)f2h_bits(r2[1]) << 16)) : pack_bf2(r2[0], r2[1]);
+            }
+            v = make_uint4(o[0], o[1], o[2], o[3]);
+        } else if (hvalid) {
+            v = *(const uint4*)(a.q + (long long)b * a.H * HD + (g * G + c16) * HD + kslice(j));
+        }
+        if (HALF && !a.fuse_kv && !a.q_half) {  // bf16 -> f16
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                o[t] = (uint32_t)f2h_bits(__uint_as_float(wv[t] << 16)) |
+                       ((uint32_t)f2h_bits(__uint_as_float(wv[t] & 0xFFFF0000u)) << 16);
+            v = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        qop[j] = v;
+    }
+}
+
 template <int HD, int G, int RT>
 __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
     constexpr bool I8 = RT == RT_I8;
@@ -606,191 +808,16 @@ __global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
     }
     if (LIVE && *a.live == 0) return;  // no sequence left in the loops: the write only
 
-    // int8 rows (hd >= 64): lane (key, kgrp) reads 16 bytes at 64h + 16 kgrp of its K row
-    // for h < NQ / 2, so every load covers 64 contiguous bytes of each key; k-step j
-    // takes elements 64 (j/2) + 16 kgrp + 8 (j%2) .. +8.  Other rows: 32 j + 8 kgrp.
-    constexpr bool KPERM = I8 && NQ % 2 == 0;
-    auto kslice = [&](int j) { return KPERM ? 64 * (j >> 1) + 16 * kgrp + 8 * (j & 1) : 32 * j + 8 * kgrp; };
-    // Q^T operand: lane (head c16, kgrp) holds q[h][kslice(j) .. +8]
     uint4 qop[NQ];
+    decode_q<HD, G, RT>(a, b, g, c16, kgrp, qop);
     const bool hvalid = c16 < G;
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (hvalid && a.fuse_kv) {  // rotate the float32 projection here
-            // the 8 elements e0.. are pairs i0.. (one half of the head): 16-byte loads
-            const int e0 = kslice(j), i0 = e0 % (HD / 2);
-            const float* qh = a.qkv + (long long)b * (a.H + 2 * Hkv) * HD + (g * G + c16) * HD;
-            float x1[8], x2[8], cs[16];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                *(float4*)&x1[4 * t] = *(const float4*)(qh + i0 + 4 * t);
-                *(float4*)&x2[4 * t] = *(const float4*)(qh + i0 + HD / 2 + 4 * t);
-            }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) *(float4*)&cs[4 * t] = *(const float4*)(a.rope_cs + 2 * i0 + 4 * t);
-            const bool lo = e0 < HD / 2;
-            uint32_t o[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                float r2[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int m = 2 * t + u;
-                    const float c = cs[2 * m], sn = cs[2 * m + 1];
-                    r2[u] = lo ? rope_lo(x1[m], x2[m], c, sn) : rope_hi(x1[m], x2[m], c, sn);
-                }
-                // the float16 kernels take the rotated float32 q with one rounding
-                o[t] = HALF ? ((uint32_t)f2h_bits(r2[0]) | ((uint32_t)f2h_bits(r2[1]) << 16)) : pack_bf2(r2[0], r2[1]);
-            }
-            v = make_uint4(o[0], o[1], o[2], o[3]);
-        } else if (hvalid) {
-            v = *(const uint4*)(a.q + (long long)b * a.H * HD + (g * G + c16) * HD + kslice(j));
-        }
-        if (HALF && !a.fuse_kv && !a.q_half) {  // bf16 -> f16
-            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-            uint32_t o[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                o[t] = (uint32_t)f2h_bits(__uint_as_float(wv[t] << 16)) |
-                       ((uint32_t)f2h_bits(__uint_as_float(wv[t] & 0xFFFF0000u)) << 16);
-            v = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-        qop[j] = v;
-    }
     f32x4 oacc[NE];
 #pragma unroll
     for (int et = 0; et < NE; ++et) oacc[et] = (f32x4){0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.f;
 
-    for (int kb = c_begin + 32 * w; kb < c_end; kb += 128) {
-        // V operands of the tile are loaded first, so that K and V are in flight together.
-        // int8 V: one 16-byte load per pair of O^T tiles; tile et's row r is head dim
-        // vdim(et, r) = 32 (et/2) + 2 r + et%2 (the 8 keys of dims e and e + 1 are adjacent)
-        const int pos0 = row_of(min(kb + 8 * kgrp, ((c_end - 1) >> 3) << 3));
-        uint4 vraw[I8 ? NE / 2 : NE], vsc[I8 ? NE / 2 : 1];
-        if (I8) {
-#pragma unroll
-            for (int pp = 0; pp < NE / 2; ++pp) {
-                vraw[pp] = *(const uint4*)((const int8_t*)kv.base[1] + v_elem(kv, b, g, pos0, 32 * pp + 2 * c16));
-                vsc[pp] = *(const uint4*)(kv.base_scale[1] + v_scale_idx(kv, b, g, pos0, pp));
-            }
-        } else {
-#pragma unroll
-            for (int et = 0; et < NE; ++et) vraw[et] = *(const uint4*)((const u16*)kv.base[1] + v_elem(kv, b, g, pos0, 16 * et + c16));
-        }
-        // ---- S^T = K Q^T: n-tile nt covers keys kb + 8*(r/4) + 4*nt + r%4 for row r
-        f32x4 sacc[2];
-        long long krow[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-            krow[nt] = kv_row(kv, b, g, row_of(min(kb + 8 * (c16 >> 2) + 4 * nt + (c16 & 3), c_end - 1)));
-        uint4 kraw[2][KPERM ? NQ / 2 : 1];
-        uint32_t kscl[2][KPERM ? NQ / 2 : 1];
-        if (KPERM) {  // all K codes and scales of the tile first
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int hh = 0; hh < NQ / 2; ++hh) {
-                    kraw[nt][hh] = *(const uint4*)((const int8_t*)kv.base[0] + krow[nt] * HD + 64 * hh + 16 * kgrp);
-                    kscl[nt][hh] = kv.base_scale[0][krow[nt] * NQ + 2 * hh + (kgrp >> 1)];
-                }
-        }
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const long long row = krow[nt];
-            sacc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            if (KPERM) {
-#pragma unroll
-                for (int j = 0; j < NQ; ++j) {
-                    const uint4 c4 = kraw[nt][j >> 1];
-                    const uint2 c = (j & 1) ? make_uint2(c4.z, c4.w) : make_uint2(c4.x, c4.y);
-                    const uint32_t sp = kscl[nt][j >> 1] | (kscl[nt][j >> 1] << 16);
-                    const uint4 kf = i8x8_to_f16(c, make_uint4(sp, sp, sp, sp));
-                    sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kf), as_half8(qop[j]), sacc[nt], 0, 0, 0);
-                }
-            } else if (I8) {
-                const u16* ks = kv.base_scale[0] + row * NQ;
-#pragma unroll
-                for (int j = 0; j < NQ; ++j) {
-                    const uint2 c = *(const uint2*)((const int8_t*)kv.base[0] + row * HD + 32 * j + 8 * kgrp);
-                    const uint32_t s1 = ks[j];
-                    const uint32_t sp = s1 | (s1 << 16);
-                    const uint4 kf = i8x8_to_f16(c, make_uint4(sp, sp, sp, sp));
-                    sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kf), as_half8(qop[j]), sacc[nt], 0, 0, 0);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < NQ; ++j) {
-                    const uint4 kf = *(const uint4*)((const u16*)kv.base[0] + row * HD + 32 * j + 8 * kgrp);
-                    if (HALF)
-                        sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kf), as_half8(qop[j]), sacc[nt], 0, 0, 0);
-                    else
-                        sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qop[j]), sacc[nt], 0, 0, 0);
-                }
-            }
-        }
-        // lane (kgrp, head c16) holds keys kb + 8kgrp + 4nt + i
-        float s[8];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = kb + 8 * kgrp + 4 * nt + i;
-                const float v = (key >= c_lo && key < c_end) ? sacc[nt][i] * sl2 : -INFINITY;
-                s[nt * 4 + i] = v;
-                mx = fmaxf(mx, v);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m, mx);
-        const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - m_new);
-        float p[8];
-        float rs = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            p[j] = (s[j] == -INFINITY) ? 0.f : exp2f(s[j] - m_new);
-            rs += p[j];
-        }
-        rs += __shfl_xor(rs, 16);
-        rs += __shfl_xor(rs, 32);
-        l = l * alpha + rs;
-        m = m_new;
-#pragma unroll
-        for (int et = 0; et < NE; ++et) oacc[et] *= alpha;
-        // ---- O^T += V^T P^T; lane (e, kgrp): V[keys kb+8kgrp .. +8][e] is one contiguous run
-        uint4 pu;
-        if (HALF) {
-            pu.x = (uint32_t)f2h_bits(p[0]) | ((uint32_t)f2h_bits(p[1]) << 16);
-            pu.y = (uint32_t)f2h_bits(p[2]) | ((uint32_t)f2h_bits(p[3]) << 16);
-            pu.z = (uint32_t)f2h_bits(p[4]) | ((uint32_t)f2h_bits(p[5]) << 16);
-            pu.w = (uint32_t)f2h_bits(p[6]) | ((uint32_t)f2h_bits(p[7]) << 16);
-        } else {
-            pu.x = pack_bf2(p[0], p[1]);
-            pu.y = pack_bf2(p[2], p[3]);
-            pu.z = pack_bf2(p[4], p[5]);
-            pu.w = pack_bf2(p[6], p[7]);
-        }
-        const int valid = c_end - (kb + 8 * kgrp);
-        // rows past the end of the context are unwritten: clamp the block address, zero the values
-#pragma unroll
-        for (int et = 0; et < NE; ++et) {
-            uint4 vf;
-            if (I8) {
-                const uint4 c4 = vraw[et >> 1];
-                const uint2 c = (et & 1) ? make_uint2(c4.z, c4.w) : make_uint2(c4.x, c4.y);
-                vf = i8x8_to_f16(c, vsc[et >> 1]);
-            } else {
-                vf = vraw[et];
-            }
-            vf = mask_tail8(vf, valid);
-            if (HALF)
-                oacc[et] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(vf), as_half8(pu), oacc[et], 0, 0, 0);
-            else
-                oacc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), as_bf16x8(pu), oacc[et], 0, 0, 0);
-        }
-    }
+    for (int kb = c_begin + 32 * w; kb < c_end; kb += 128)
+        decode_tile<HD, G, RT>(kv, b, g, kb, c_lo, c_end, row_of, qop, oacc, m, l, sl2, c16, kgrp);
     // ---- merge the four waves: O^T lane holds row r = 4kgrp + i of tile et for head c16
     //      (head dim 16et + r; int8 rows: 32 (et/2) + 2r + et%2)
     __shared__ float sm_m[4][16], sm_l[4][16];

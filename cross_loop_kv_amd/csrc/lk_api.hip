@@ -80,11 +80,19 @@ static const char* kTimedNames[TC_COUNT] = {"attn_decode_dense", "attn_decode_sp
                                             "gemm_prefill"};
 
 struct EventTimer {
-    int cls = TC_NONE;
-    int per_call = 0;   // launches of the class timed per prefill / decode call (0: all)
-    int in_call = 0;    // launches of the class seen in the current call
+    unsigned mask = 0;  // bit c: kernel class c is timed
+    int per_call = 0;   // launches of each class timed per prefill / decode call (0: all)
+    int in_call[TC_COUNT] = {};  // launches of each class seen in the current call
     std::vector<hipEvent_t> pool;  // pairs (start, end), one per timed launch
+    std::vector<int> pair_cls;     // class of each pair
     size_t used = 0;
+    bool wants(int cls) {
+        if (cls < 0 || !((mask >> cls) & 1u)) return false;
+        return per_call == 0 || in_call[cls]++ < per_call;
+    }
+    void new_call() {
+        for (int& c : in_call) c = 0;
+    }
     hipError_t mark(hipStream_t st) {
         if (used == pool.size()) {
             hipEvent_t e;
@@ -93,6 +101,11 @@ struct EventTimer {
             pool.push_back(e);
         }
         return hipEventRecord(pool[used++], st);
+    }
+    hipError_t begin(hipStream_t st, int cls) {
+        if (pair_cls.size() < used / 2 + 1) pair_cls.resize(used / 2 + 1);
+        pair_cls[used / 2] = cls;
+        return mark(st);
     }
     ~EventTimer() {
         for (hipEvent_t e : pool) (void)hipEventDestroy(e);
@@ -107,12 +120,13 @@ struct DecodeGraph {
     struct Seg {
         hipGraphExec_t exec = nullptr;           // a captured run of launches, or
         std::function<hipError_t()> direct;      // one timed launch
+        int cls = -1;                            // its kernel class
     };
     std::vector<Seg> segs;
     const void* store = nullptr;
     const void* ws = nullptr;
     hipStream_t stream = nullptr;
-    int timer_cls = -2;
+    long long timer_mask = -1;
     int timer_per_call = -1;
     int keep_codes = 0;
     void reset() {
@@ -121,7 +135,7 @@ struct DecodeGraph {
         segs.clear();
         store = ws = nullptr;
         stream = nullptr;
-        timer_cls = -2;
+        timer_mask = -1;
     }
     ~DecodeGraph() { reset(); }
 };
@@ -573,17 +587,17 @@ int cut_segment(lk_handle* h, hipStream_t st) {
 // of the step instead (`fn` captures its arguments by value).
 template <typename F>
 int timed(lk_handle* h, int cls, hipStream_t st, F fn) {
-    bool on = h->timer.cls == cls;
-    if (on) on = h->timer.per_call == 0 || h->timer.in_call++ < h->timer.per_call;
+    const bool on = h->timer.wants(cls);
     if (on && h->building) {
         LK_TRY(cut_segment(h, st));
         DecodeGraph::Seg seg;
         seg.direct = fn;
+        seg.cls = cls;
         h->building->segs.push_back(std::move(seg));
         LK_HIP(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal));
         return LK_OK;
     }
-    if (on) LK_HIP(h->timer.mark(st));
+    if (on) LK_HIP(h->timer.begin(st, cls));
     LK_HIP(fn());
     if (on) LK_HIP(h->timer.mark(st));
     return LK_OK;
@@ -1127,7 +1141,7 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
     const int P = c.n_prelude, R = c.n_shared, K = s->K, Q = c.n_coda, d = c.d_model;
     const int M = B * T;
     const bool inject = c.input_reinject != 0;
-    h->timer.in_call = 0;
+    h->timer.new_call();
     if (h->lazy())
         LK_HIP(lk::fill_i32(slot_map(s, 2), -1, (long long)(K - 1) * B * s->Tpad, st));
     s->t = 0;
@@ -1298,7 +1312,7 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
     const bool inject = c.input_reinject != 0;
     const int32_t* dpos = dev_pos(s);
     const bool skip = h->lazy() && h->z.skip_tau > 0.f && K >= 2;
-    h->timer.in_call = 0;
+    h->timer.new_call();
     // The layer applications of one step, in order.
     struct App {
         int li;
@@ -1502,14 +1516,14 @@ int lk_looped_decode_step(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, fl
     LK_HIP(hipMemcpyAsync(w.ids, d_ids, (size_t)B * 4, hipMemcpyDeviceToDevice, st));
     if (st && h->use_graphs) {
         DecodeGraph& g = h->graph;
-        if (g.store != s || g.ws != d_ws || g.stream != st || g.timer_cls != h->timer.cls ||
+        if (g.store != s || g.ws != d_ws || g.stream != st || g.timer_mask != (long long)h->timer.mask ||
             g.timer_per_call != h->timer.per_call || g.keep_codes != s->keep_codes) {
             g.reset();
             LK_TRY(capture_decode(h, s, w, st));
             g.store = s;
             g.ws = d_ws;
             g.stream = st;
-            g.timer_cls = h->timer.cls;
+            g.timer_mask = h->timer.mask;
             g.timer_per_call = h->timer.per_call;
             g.keep_codes = s->keep_codes;
         }
@@ -1517,7 +1531,7 @@ int lk_looped_decode_step(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, fl
             if (seg.exec) {
                 LK_HIP(hipGraphLaunch(seg.exec, st));
             } else {
-                LK_HIP(h->timer.mark(st));
+                LK_HIP(h->timer.begin(st, seg.cls));
                 LK_HIP(seg.direct());
                 LK_HIP(h->timer.mark(st));
             }
@@ -1582,14 +1596,24 @@ int lk_set_decode_graphs(lk_handle* h, int32_t enable) {
 
 int lk_timing_enable(lk_handle* h, const char* kernel_class) {
     if (!h) return fail(LK_ERR_INVALID_ARG, "null handle");
-    int cls = TC_NONE;
+    unsigned mask = 0;
     if (kernel_class) {
-        for (int i = 0; i < TC_COUNT; ++i)
-            if (std::strcmp(kernel_class, kTimedNames[i]) == 0) cls = i;
-        if (cls == TC_NONE) return fail(LK_ERR_INVALID_ARG, std::string("unknown kernel class ") + kernel_class);
+        std::string list(kernel_class);
+        size_t a = 0;
+        while (a <= list.size()) {
+            size_t b = list.find(',', a);
+            if (b == std::string::npos) b = list.size();
+            const std::string name = list.substr(a, b - a);
+            int cls = TC_NONE;
+            for (int i = 0; i < TC_COUNT; ++i)
+                if (name == kTimedNames[i]) cls = i;
+            if (cls == TC_NONE) return fail(LK_ERR_INVALID_ARG, "unknown kernel class " + name);
+            mask |= 1u << cls;
+            a = b + 1;
+        }
     }
     h->timer.used = 0;
-    h->timer.cls = cls;
+    h->timer.mask = mask;
     return LK_OK;
 }
 
@@ -1599,20 +1623,40 @@ int lk_timing_sample(lk_handle* h, int32_t per_call) {
     return LK_OK;
 }
 
-int lk_timing_read(lk_handle* h, int32_t* launches, double* total_ms) {
-    if (!h || !launches || !total_ms) return fail(LK_ERR_INVALID_ARG, "null argument");
+namespace {
+// Launches and summed event time of the recorded pairs of class cls (-1: every class).
+int timing_sum(lk_handle* h, int cls, int32_t* launches, double* total_ms) {
     double tot = 0.0;
-    const size_t n = h->timer.used / 2;
-    for (size_t i = 0; i < n; ++i) {
+    int32_t n = 0;
+    const size_t pairs = h->timer.used / 2;
+    for (size_t i = 0; i < pairs; ++i) {
+        if (cls >= 0 && h->timer.pair_cls[i] != cls) continue;
         LK_HIP(hipEventSynchronize(h->timer.pool[2 * i + 1]));
         float ms = 0.f;
         LK_HIP(hipEventElapsedTime(&ms, h->timer.pool[2 * i], h->timer.pool[2 * i + 1]));
         tot += ms;
+        ++n;
     }
-    h->timer.used = 0;
-    *launches = (int32_t)n;
+    *launches = n;
     *total_ms = tot;
     return LK_OK;
+}
+}  // namespace
+
+int lk_timing_read(lk_handle* h, int32_t* launches, double* total_ms) {
+    if (!h || !launches || !total_ms) return fail(LK_ERR_INVALID_ARG, "null argument");
+    LK_TRY(timing_sum(h, -1, launches, total_ms));
+    h->timer.used = 0;
+    return LK_OK;
+}
+
+int lk_timing_read_class(lk_handle* h, const char* kernel_class, int32_t* launches, double* total_ms) {
+    if (!h || !kernel_class || !launches || !total_ms) return fail(LK_ERR_INVALID_ARG, "null argument");
+    int cls = TC_NONE;
+    for (int i = 0; i < TC_COUNT; ++i)
+        if (std::strcmp(kernel_class, kTimedNames[i]) == 0) cls = i;
+    if (cls == TC_NONE) return fail(LK_ERR_INVALID_ARG, std::string("unknown kernel class ") + kernel_class);
+    return timing_sum(h, cls, launches, total_ms);
 }
 
 // ---- test entry points ----------------------------------------------------------
@@ -1733,8 +1777,8 @@ int lk_dbg_attention(const lk_dbg_attn_args* x, size_t* ws_need, void* stream) {
             }
             need = (size_t)B * H * a.n_splits * (hd + 2) * 4;
             if (!x->ws) {
-                if (!ws_need) return fail(LK_ERR_INVALID_ARG, "null workspace");
-                break;
+                if (ws_need) break;
+                return fail(LK_ERR_INVALID_ARG, "null workspace");
             }
             if (x->ws_bytes < need) return fail(LK_ERR_CAPACITY, "workspace too small");
             a.part = (float*)x->ws;

@@ -289,13 +289,14 @@ int lk_effective_depth(const lk_handle *h, int32_t *depth);
 
 const char *lk_last_error(void);
 
-/* Instrumentation: bracket every launch of one kernel class with HIP events on
- * the stream of the call that launches it.  Classes: "attn_decode_dense" (decode
- * attention over dense / base rows), "attn_decode_sparse", "attn_prefill",
- * "column_mass", "attn_prefill_sparse", "gemm_decode", "gemm_prefill"; NULL
- * disables.  Enabling clears the record.  Not thread-safe per handle. */
+/* Instrumentation: bracket every launch of the given kernel classes with HIP events
+ * on the stream of the call that launches it.  kernel_class is one class name or a
+ * comma-separated list of them: "attn_decode_dense" (decode attention over dense /
+ * base rows), "attn_decode_sparse", "attn_prefill", "column_mass",
+ * "attn_prefill_sparse", "gemm_decode", "gemm_prefill"; NULL disables.  Enabling
+ * clears the record.  Not thread-safe per handle. */
 int lk_timing_enable(lk_handle *h, const char *kernel_class);
-/* Time only the first per_call launches of the class in each prefill or decode
+/* Time only the first per_call launches of each class in each prefill or decode
  * call (0, the default: all of them).  Fewer timed launches cut the decode step
  * into fewer replayed graphs. */
 int lk_timing_sample(lk_handle *h, int32_t per_call);
@@ -304,6 +305,8 @@ int lk_timing_sample(lk_handle *h, int32_t per_call);
  * A replayed decode step launches its timed-class kernels directly between two
  * events and the rest of the step from captured graphs. */
 int lk_timing_read(lk_handle *h, int32_t *launches, double *total_ms);
+/* The same for one of the enabled classes, without clearing the record. */
+int lk_timing_read_class(lk_handle *h, const char *kernel_class, int32_t *launches, double *total_ms);
 
 /* ---------------------------------------------------------------------------
  * Test and inspection entry points (same error conventions).
@@ -401,11 +404,12 @@ int lk_dbg_gemm_epi(const void *d_a, const void *d_w, int32_t epi, float *d_c, v
  *     int8 kernel takes as is; else bf16).  out bf16 [B][H*hd], out32 float32 (same).
  *   LK_DBG_ATTN_DECODE_SEG: one query per sequence at position t over
  *     (S intersect [0, t - window]) union [max(0, t - window + 1), t], S = cols
- *     [B][Hkv][n_cols] ascending, as a decode step's loop k >= 2: the stable
- *     columns are read from a float16 cache (s_k / s_v: row i holds column cols[i],
- *     s_cap rows per (b, g), a multiple of 128, >= n_cols) and the window from a
- *     float16 ring (r_k / r_v: position p at row p % r_cap, r_cap a multiple of 128,
- *     > window + 8).  q and outputs as LK_DBG_ATTN_DECODE.
+ *     [B][Hkv][n_cols] ascending, as a decode step's loop k >= 2 (split into
+ *     128-row pieces, then merged): the stable columns are read from a float16
+ *     cache (s_k / s_v: row i holds column cols[i], s_cap rows per (b, g), a
+ *     multiple of 128, >= n_cols) and the window from a float16 ring (r_k / r_v:
+ *     position p at row p % r_cap, r_cap a multiple of 128, >= window + 8).  q and
+ *     outputs as LK_DBG_ATTN_DECODE.
  *   LK_DBG_ATTN_PREFILL: causal attention of T prompt tokens (query i over keys
  *     [0, i]; kv_format 0 or 1, T <= tmax); q bf16 [B][T][H*hd]; out bf16
  *     [B][T][H*hd]; lse float32 [B][H][T], the log2 of each row's softmax
@@ -419,8 +423,9 @@ int lk_dbg_gemm_epi(const void *d_a, const void *d_w, int32_t epi, float *d_c, v
  *     float16 cache s_k / s_v (as above, s_cap a multiple of 8), the window from
  *     float16 rows at every position r_k / r_v (r_cap = positions, a multiple of 8);
  *     q bf16 [B][n_rows][H*hd]; out bf16 [B][n_rows][H*hd].
- * ws: device scratch of ws_bytes (split partials; lk_dbg_attention with ws == NULL
- * writes the bytes a call needs to *ws_need and launches nothing).  head_dim 32, 64
+ * ws: device scratch of ws_bytes (the split partials of the two decode kinds; the
+ * other kinds need none).  With ws == NULL and ws_need != NULL, lk_dbg_attention writes the
+ * bytes the call needs to *ws_need and launches nothing.  head_dim 32, 64
  * or 128 (128 only for PREFILL_SPARSE); H / Hkv in {1, 2, 4, 8}. */
 #define LK_DBG_ATTN_DECODE 0
 #define LK_DBG_ATTN_DECODE_SEG 1
