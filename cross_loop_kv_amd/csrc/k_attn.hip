@@ -87,22 +87,14 @@ __device__ __forceinline__ uint4 i8x8_to_f16(uint2 c, uint4 scale_pairs) {
 }
 
 // 8 consecutive K elements of row (b, g, pos) as operands: bf16 rows as they are, int8
-// codes times their group scale as float16.
+// codes times their group scale as float16 (the exact product rounded once).
 template <int HD, bool I8>
 __device__ __forceinline__ uint4 load_k8(const KVLayer& kv, int b, int g, int pos, int e0) {
     const long long row = kv_row(kv, b, g, pos);
     if (!I8) return *(const uint4*)((const u16*)kv.base[0] + row * HD + e0);
     const uint2 c = *(const uint2*)((const int8_t*)kv.base[0] + row * HD + e0);
-    const float s = h2f(kv.base_scale[0][row * (HD / 32) + e0 / 32]);
-    const uint32_t wv[2] = {c.x, c.y};
-    uint32_t o[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t word = wv[q >> 1];
-        const int sh = (q & 1) * 16;
-        o[q] = pack_op2<true>((float)(int8_t)((word >> sh) & 0xFF) * s, (float)(int8_t)((word >> (sh + 8)) & 0xFF) * s);
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
+    const uint32_t s2 = (uint32_t)kv.base_scale[0][row * (HD / 32) + e0 / 32] * 0x10001u;
+    return i8x8_to_f16(c, make_uint4(s2, s2, s2, s2));
 }
 
 // Zero the bf16/f16 elements j >= valid of an 8-element operand.
@@ -127,17 +119,8 @@ __device__ __forceinline__ uint4 load_v8(const KVLayer& kv, int b, int g, int po
         out = *(const uint4*)((const u16*)kv.base[1] + idx);
     } else {
         const uint2 c = *(const uint2*)((const int8_t*)kv.base[1] + idx);
-        const u16* sp = kv.base_scale[1] + v_scale_idx(kv, b, g, pos0, e / 32);
-        const uint32_t wv[2] = {c.x, c.y};
-        uint32_t o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t word = wv[q >> 1];
-            const int sh = (q & 1) * 16;
-            o[q] = pack_op2<true>((float)(int8_t)((word >> sh) & 0xFF) * h2f(sp[2 * q]),
-                                  (float)(int8_t)((word >> (sh + 8)) & 0xFF) * h2f(sp[2 * q + 1]));
-        }
-        out = make_uint4(o[0], o[1], o[2], o[3]);
+        // the scales of keys pos0..pos0+7 in this 32-wide group are 8 consecutive float16
+        out = i8x8_to_f16(c, *(const uint4*)(kv.base_scale[1] + v_scale_idx(kv, b, g, pos0, e / 32)));
     }
     return mask_tail8(out, valid);
 }
@@ -467,18 +450,27 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_fa_kernel(const u16* __re
 }
 
 // ---------------------------------------------------------------- column mass
-template <int HD, bool I8>
-__global__ __launch_bounds__(256) void column_mass_kernel(const u16* __restrict__ Q, KVLayer kv,
-                                                          const float* __restrict__ LSE, int T, int H,
-                                                          float* __restrict__ mass, float sl2) {
+// mass[b, g, j] = sum over the group's heads h and queries q >= j of 2^(s_qj sl2 - lse_qh).
+// NW waves per workgroup, 32 keys each, K held in registers as the A operand.  The query
+// tiles (one head and 32 queries at a time) stream through double-buffered LDS, the next
+// tile's global loads issued before the current tile's products; every staged tile serves
+// 32 NW keys.  Per score: one FMA, one v_exp_f32 and one add; the causal mask is applied only
+// on tiles that reach the diagonal.
+template <int HD, bool I8, int NW>
+__global__ __launch_bounds__(64 * NW) void column_mass_kernel(const u16* __restrict__ Q, KVLayer kv,
+                                                              const float* __restrict__ LSE, int T, int H,
+                                                              float* __restrict__ mass, float sl2) {
     constexpr int LDQ = HD + 8;
     constexpr int CPR = HD / 8;
-    __shared__ __attribute__((aligned(16))) u16 Qs[32 * LDQ];
+    constexpr int NQC = 32 * CPR;  // 16-byte chunks of one query tile
+    constexpr int NT = 64 * NW;
+    constexpr int PER = (NQC + NT - 1) / NT;
+    __shared__ __attribute__((aligned(16))) u16 Qs[2][32 * LDQ];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int kg = lane >> 5, l32 = lane & 31;
     const int g = blockIdx.y, b = blockIdx.z;
     const int Hkv = kv.Hkv, G = H / Hkv;
-    const int kblk = blockIdx.x * 128;
+    const int kblk = blockIdx.x * 32 * NW;
     const int j0 = kblk + w * 32;
     const long long ldq = (long long)H * HD;
     uint4 kf[HD / 16];
@@ -494,37 +486,56 @@ __global__ __launch_bounds__(256) void column_mass_kernel(const u16* __restrict_
     float cs[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) cs[i] = 0.f;
-    const int nqt = (T + 31) / 32;
-    for (int hh = 0; hh < G; ++hh) {
-        const int h = g * G + hh;
-        for (int qt = kblk / 32; qt < nqt; ++qt) {
-            __syncthreads();
-            for (int c = tid; c < 32 * CPR; c += 256) {
-                const int r = c / CPR, ch = c % CPR;
-                const int q = qt * 32 + r;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (q < T) v = *(const uint4*)(Q + ((long long)b * T + q) * ldq + h * HD + ch * 8);
-                *(uint4*)&Qs[r * LDQ + ch * 8] = I8 ? bf8_to_h8(v) : v;
-            }
-            __syncthreads();
-            if (qt * 32 + 31 < j0) continue;
-            f32x16 s;
+    // iteration it covers head g*G + it/nq and query tile qt0 + it%nq
+    const int qt0 = kblk / 32, nq = (T + 31) / 32 - qt0, nit = G * nq;
+    uint4 regs[PER];
+    auto load_tile = [&](int it) {
+        const int h = g * G + it / nq, qt = qt0 + it % nq;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = 0.f;
+        for (int p = 0; p < PER; ++p) {
+            const int c = tid + p * NT;
+            regs[p] = make_uint4(0, 0, 0, 0);
+            const int q = qt * 32 + c / CPR;
+            if (c < NQC && q < T) regs[p] = *(const uint4*)(Q + ((long long)b * T + q) * ldq + h * HD + (c % CPR) * 8);
+        }
+    };
+    auto store_tile = [&](int buf) {
 #pragma unroll
-            for (int ks = 0; ks < HD / 16; ++ks) {
-                s = mfma32<I8>(kf[ks], *(const uint4*)&Qs[l32 * LDQ + ks * 16 + kg * 8], s);
-            }
-            const int q = qt * 32 + l32;
-            if (q < T) {
-                const float lse2 = LSE[((long long)b * H + h) * T + q];
+        for (int p = 0; p < PER; ++p) {
+            const int c = tid + p * NT;
+            if (c < NQC) *(uint4*)&Qs[buf][(c / CPR) * LDQ + (c % CPR) * 8] = I8 ? bf8_to_h8(regs[p]) : regs[p];
+        }
+    };
+    load_tile(0);
+    store_tile(0);
+    for (int it = 0; it < nit; ++it) {
+        const int cur = it & 1;
+        __syncthreads();
+        if (it + 1 < nit) load_tile(it + 1);
+        const int h = g * G + it / nq, qt = qt0 + it % nq;
+        const int q = qt * 32 + l32;
+        if (qt * 32 + 31 >= j0) {
+            const float lse2 = (q < T) ? LSE[((long long)b * H + h) * T + q] : 0.f;
+            f32x16 sv;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sv[i] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < HD / 16; ++ks)
+                sv = mfma32<I8>(kf[ks], *(const uint4*)&Qs[cur][l32 * LDQ + ks * 16 + kg * 8], sv);
+            if (qt * 32 >= j0 + 31) {  // every key of this wave precedes every query of the tile
+                if (q < T) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) cs[i] += __builtin_amdgcn_exp2f(fmaf(sv[i], sl2, -lse2));
+                }
+            } else if (q < T) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = j0 + 8 * (i >> 2) + 4 * kg + (i & 3);
-                    if (key <= q) cs[i] += exp2f(s[i] * sl2 - lse2);
+                    if (key <= q) cs[i] += __builtin_amdgcn_exp2f(fmaf(sv[i], sl2, -lse2));
                 }
             }
         }
+        if (it + 1 < nit) store_tile(cur ^ 1);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -750,8 +761,10 @@ __device__ __forceinline__ void decode_q(const RowsAttn& a, int b, int g, int c1
     }
 }
 
+// The int8 row type streams the loop-1 base from HBM and wants three waves per SIMD in
+// flight; its register count sits just above that limit unless the bound asks for it.
 template <int HD, int G, int RT>
-__global__ __launch_bounds__(256) void attn_decode_dense_kernel(RowsAttn a) {
+__global__ __launch_bounds__(256, RT == RT_I8 || RT == RT_F16_2SEG || RT == RT_F16_2SEG_LIVE ? 3 : 1) void attn_decode_dense_kernel(RowsAttn a) {
     constexpr bool I8 = RT == RT_I8;
     constexpr bool HALF = RT != RT_BF16;  // f16 MFMA (int8 codes are converted to f16)
     constexpr bool SEG = RT == RT_F16_2SEG || RT == RT_F16_2SEG_LIVE;
@@ -1609,12 +1622,21 @@ hipError_t prefill_hd(const u16* q, const KVLayer& kv, int B, int T, int H, u16*
 template <int HD>
 hipError_t mass_hd(const u16* q, const KVLayer& kv, const float* lse, int B, int T, int H, float* mass,
                    hipStream_t st) {
-    dim3 grid((T + 127) / 128, kv.Hkv, B);
     const float sl2 = kLog2e / sqrtf((float)HD);
-    if (kv.lazy && kv.base_bits == 8)
-        hipLaunchKernelGGL((column_mass_kernel<HD, true>), grid, dim3(256), 0, st, q, kv, lse, T, H, mass, sl2);
+    const bool i8 = kv.lazy && kv.base_bits == 8;
+    if (T >= 4096) {  // long prompts: 256 keys per workgroup
+        dim3 grid((T + 255) / 256, kv.Hkv, B);
+        if (i8)
+            hipLaunchKernelGGL((column_mass_kernel<HD, true, 8>), grid, dim3(512), 0, st, q, kv, lse, T, H, mass, sl2);
+        else
+            hipLaunchKernelGGL((column_mass_kernel<HD, false, 8>), grid, dim3(512), 0, st, q, kv, lse, T, H, mass, sl2);
+        return hipGetLastError();
+    }
+    dim3 grid((T + 127) / 128, kv.Hkv, B);
+    if (i8)
+        hipLaunchKernelGGL((column_mass_kernel<HD, true, 4>), grid, dim3(256), 0, st, q, kv, lse, T, H, mass, sl2);
     else
-        hipLaunchKernelGGL((column_mass_kernel<HD, false>), grid, dim3(256), 0, st, q, kv, lse, T, H, mass, sl2);
+        hipLaunchKernelGGL((column_mass_kernel<HD, false, 4>), grid, dim3(256), 0, st, q, kv, lse, T, H, mass, sl2);
     return hipGetLastError();
 }
 
