@@ -41,8 +41,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(half8, v); }
 
 // Operand type of the prefill kernels: float16 over int8 rows (code * scale rounded
-// once to float16; q converted from bf16, exact inside the float16 range) and bf16
-// over bf16 rows.  Eight operand elements travel as one uint4.
+// once to float16; q converted from bf16) and bf16 over bf16 rows.  Eight operand
+// elements travel as one uint4.  The float16 forms assume magnitudes inside the float16
+// range: a bf16 q above 65504 or an int8 element (code * scale) above it becomes inf, and
+// bf16 values below 2^-14 lose bits as float16 subnormals.
 template <bool F16>
 __device__ __forceinline__ uint32_t pack_op2(float a, float b) {
     if constexpr (F16) return (uint32_t)f2h_bits(a) | ((uint32_t)f2h_bits(b) << 16);
@@ -53,7 +55,8 @@ __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
     if constexpr (F16) return __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(a), as_half8(b), c, 0, 0, 0);
     else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
-// Eight bf16 values as float16 (exact for magnitudes in the float16 normal range).
+// Eight bf16 values as float16: exact for magnitudes in [2^-14, 65504]; larger ones
+// become inf, smaller ones float16 subnormals.
 __device__ __forceinline__ uint4 bf8_to_h8(uint4 v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t o[4];
@@ -1069,7 +1072,7 @@ __global__ __launch_bounds__(256) void gather_recon_kernel(RowsAttn a, int mode,
 // so every K/V tile is read once for the G heads.  Tiles: first the cache rows with a
 // column at or below (last row's position - w), then the positions from the first row's
 // window start to the last row's position; per query both are masked exactly.  f16 MFMAs
-// (q converted from bf16 exactly), online softmax as in the flash prefill, output written
+// (q converted from bf16: exact for magnitudes in [2^-14, 65504]), online softmax as in the flash prefill, output written
 // directly (no split partials).
 template <int G>
 __global__ __launch_bounds__(G > 4 ? 64 * G : 256) void attn_rows_pf_kernel(RowsAttn a, KVLayer sc, KVLayer fr,
