@@ -325,7 +325,44 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_fa_kernel(const u16* __re
     const int kend = min(T, qblk + 128);
     const int ntiles = (kend + KT - 1) / KT;
     uint4 regs[PER];
+    // A tile whose 64 keys all lie below T is loaded without bounds checks: chunk p < 4
+    // of this thread holds key k0 + 16 p of the tile (LDS row tid/16 + 16 p), chunk
+    // p >= 4 the 8 keys of V block tid/128 + 2 (p - 4) at head dim tid % 128, so every
+    // address is a fixed per-thread offset plus the tile's row offset, which the whole
+    // workgroup shares.  Only a last partial tile takes the checked loads.
+    const long long row0 = (long long)(b * kv.Hkv + g) * kv.Tmax;
+    const int k0 = flash_key_of_row(tid / CPR);
+    const int koff = k0 * HD + (tid % CPR) * 8;                              // elements
+    const int ksoff = k0 * (HD / 32) + (tid % CPR) / 4;                      // K scale index
+    const int voff = (tid / HD) * HD * 8 + (tid % HD) * 8;                   // elements
+    const int vsoff = ((tid / HD) * (HD / 32) + (tid % HD) / 32) * 8;        // V scale index
     auto load_tile = [&](int t) {
+        if ((t + 1) * KT <= T) {
+            const long long r = row0 + (long long)t * KT;
+            if constexpr (I8) {
+                const int8_t* kc = (const int8_t*)kv.base[0] + r * HD;
+                const int8_t* vc = (const int8_t*)kv.base[1] + r * HD;
+                const u16* ks = kv.base_scale[0] + r * (HD / 32);
+                const u16* vs = kv.base_scale[1] + r * (HD / 32);
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t s2 = (uint32_t)ks[ksoff + p * 16 * (HD / 32)] * 0x10001u;
+                    regs[p] = i8x8_to_f16(*(const uint2*)(kc + koff + p * 16 * HD), make_uint4(s2, s2, s2, s2));
+                }
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    regs[4 + p] = i8x8_to_f16(*(const uint2*)(vc + voff + p * 16 * HD),
+                                              *(const uint4*)(vs + vsoff + p * 16 * (HD / 32)));
+            } else {
+                const u16* kb = (const u16*)kv.base[0] + r * HD;
+                const u16* vb = (const u16*)kv.base[1] + r * HD;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) regs[p] = *(const uint4*)(kb + koff + p * 16 * HD);
+#pragma unroll
+                for (int p = 0; p < 4; ++p) regs[4 + p] = *(const uint4*)(vb + voff + p * 16 * HD);
+            }
+            return;
+        }
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * 256;
