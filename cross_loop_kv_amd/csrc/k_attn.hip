@@ -279,31 +279,37 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const u16* __restrict
 }
 
 // ---------------------------------------------------------------- flash prefill, hd 128
-// 64-key tiles, one head and 128 queries per workgroup (4 waves x 32 queries), K/V staged
-// through registers into double-buffered LDS.  S^T = K Q^T for each 32-key half (LDS rows
-// permuted by flash_key_of_row so the score accumulator is already the B operand of
-// O^T += V^T P^T).  Per tile and lane: one FMA and one v_exp_f32 per score; the output is
-// rescaled only when some query's running max grows (a wave-uniform branch); tiles below
-// the diagonal skip the causal mask.  Workgroups take query blocks from the last one
-// down, so the longest causal spans start first.
-template <bool I8>
-__global__ __launch_bounds__(256, 2) void attn_prefill_fa_kernel(const u16* __restrict__ Q, KVLayer kv, int T,
-                                                                 int H, u16* __restrict__ O,
-                                                                 float* __restrict__ LSE, float sl2) {
-    constexpr int HD = 128, KT = 64;
+// 64-key tiles, one head and 32 NW queries per workgroup (NW waves x 32 queries), K/V
+// staged through registers into double-buffered LDS.  S^T = K Q^T for each 32-key half
+// (LDS rows permuted by flash_key_of_row so the score accumulator is already the B
+// operand of O^T += V^T P^T).  Per tile and lane: one FMA and one v_exp_f32 per score;
+// the output is rescaled only when some query's running max grows (a wave-uniform
+// branch); tiles below the diagonal skip the causal mask.  Workgroups take query blocks
+// from the last one down, so the longest causal spans start first.
+//
+// NW 4: each thread stages 8 of a tile's 16-byte chunks, one tile ahead.  NW 8: each
+// thread stages 4 chunks, into two register sets in turn, so a tile's loads are issued
+// two tiles before it is stored to LDS (the same registers as NW 4, twice the time to
+// land).
+template <bool I8, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_fa_kernel(const u16* __restrict__ Q, KVLayer kv,
+                                                                           int T, int H, u16* __restrict__ O,
+                                                                           float* __restrict__ LSE, float sl2) {
+    constexpr int HD = 128, KT = 64, NT = 64 * NW;
     constexpr int LDK = HD + 8;
     constexpr int LDV = KT + 8;
     constexpr int CPR = HD / 8;             // 16-byte chunks per K row
     constexpr int NKC = KT * CPR;           // 1024 K chunks per tile
     constexpr int NVC = (KT / 8) * HD;      // 1024 V chunks per tile
-    constexpr int PER = (NKC + NVC) / 256;  // 8 per thread
+    constexpr int PER = (NKC + NVC) / NT;   // chunks per thread
+    constexpr int PK = NKC / NT;            // of which K chunks
     __shared__ __attribute__((aligned(16))) u16 Ks[2][KT * LDK];
     __shared__ __attribute__((aligned(16))) u16 Vt[2][HD * LDV];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int kg = lane >> 5, l32 = lane & 31;
     const int h = blockIdx.y, b = blockIdx.z;
     const int G = H / kv.Hkv, g = h / G;
-    const int qblk = (gridDim.x - 1 - blockIdx.x) * 128;
+    const int qblk = (gridDim.x - 1 - blockIdx.x) * (32 * NW);
     const int q0 = qblk + w * 32;
     const int qi = q0 + l32;
     const long long ldq = (long long)H * HD;
@@ -322,21 +328,20 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_fa_kernel(const u16* __re
         for (int i = 0; i < 16; ++i) oacc[c][i] = 0.f;
     float m_i = -INFINITY, l_i = 0.f;
 
-    const int kend = min(T, qblk + 128);
+    const int kend = min(T, qblk + 32 * NW);
     const int ntiles = (kend + KT - 1) / KT;
-    uint4 regs[PER];
-    // A tile whose 64 keys all lie below T is loaded without bounds checks: chunk p < 4
-    // of this thread holds key k0 + 16 p of the tile (LDS row tid/16 + 16 p), chunk
-    // p >= 4 the 8 keys of V block tid/128 + 2 (p - 4) at head dim tid % 128, so every
-    // address is a fixed per-thread offset plus the tile's row offset, which the whole
-    // workgroup shares.  Only a last partial tile takes the checked loads.
+    // A tile whose 64 keys all lie below T is loaded without bounds checks: K chunk p of
+    // this thread (LDS row tid/16 + (NT/16) p) holds key k0 + (NT/16) p of the tile, V
+    // chunk p the 8 keys of V block tid/128 + (NT/128) (p - PK) at head dim tid % 128, so
+    // every address is a fixed per-thread offset plus the tile's row offset, which the
+    // whole workgroup shares.  Only a last partial tile takes the checked loads.
     const long long row0 = (long long)(b * kv.Hkv + g) * kv.Tmax;
     const int k0 = flash_key_of_row(tid / CPR);
     const int koff = k0 * HD + (tid % CPR) * 8;                              // elements
     const int ksoff = k0 * (HD / 32) + (tid % CPR) / 4;                      // K scale index
     const int voff = (tid / HD) * HD * 8 + (tid % HD) * 8;                   // elements
     const int vsoff = ((tid / HD) * (HD / 32) + (tid % HD) / 32) * 8;        // V scale index
-    auto load_tile = [&](int t) {
+    auto load_tile = [&](uint4 (&regs)[PER], int t) {
         if ((t + 1) * KT <= T) {
             const long long r = row0 + (long long)t * KT;
             if constexpr (I8) {
@@ -345,27 +350,27 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_fa_kernel(const u16* __re
                 const u16* ks = kv.base_scale[0] + r * (HD / 32);
                 const u16* vs = kv.base_scale[1] + r * (HD / 32);
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const uint32_t s2 = (uint32_t)ks[ksoff + p * 16 * (HD / 32)] * 0x10001u;
-                    regs[p] = i8x8_to_f16(*(const uint2*)(kc + koff + p * 16 * HD), make_uint4(s2, s2, s2, s2));
+                for (int p = 0; p < PK; ++p) {
+                    const uint32_t s2 = (uint32_t)ks[ksoff + p * (NT / 16) * (HD / 32)] * 0x10001u;
+                    regs[p] = i8x8_to_f16(*(const uint2*)(kc + koff + p * (NT / 16) * HD), make_uint4(s2, s2, s2, s2));
                 }
 #pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    regs[4 + p] = i8x8_to_f16(*(const uint2*)(vc + voff + p * 16 * HD),
-                                              *(const uint4*)(vs + vsoff + p * 16 * (HD / 32)));
+                for (int p = 0; p < PER - PK; ++p)
+                    regs[PK + p] = i8x8_to_f16(*(const uint2*)(vc + voff + p * NT * 8),
+                                               *(const uint4*)(vs + vsoff + p * (NT / HD) * (HD / 32) * 8));
             } else {
                 const u16* kb = (const u16*)kv.base[0] + r * HD;
                 const u16* vb = (const u16*)kv.base[1] + r * HD;
 #pragma unroll
-                for (int p = 0; p < 4; ++p) regs[p] = *(const uint4*)(kb + koff + p * 16 * HD);
+                for (int p = 0; p < PK; ++p) regs[p] = *(const uint4*)(kb + koff + p * (NT / 16) * HD);
 #pragma unroll
-                for (int p = 0; p < 4; ++p) regs[4 + p] = *(const uint4*)(vb + voff + p * 16 * HD);
+                for (int p = 0; p < PER - PK; ++p) regs[PK + p] = *(const uint4*)(vb + voff + p * NT * 8);
             }
             return;
         }
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int c = tid + p * 256;
+            const int c = tid + p * NT;
             regs[p] = make_uint4(0, 0, 0, 0);
             if (c < NKC) {
                 const int r = c / CPR;
@@ -379,10 +384,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_fa_kernel(const u16* __re
             }
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](const uint4 (&regs)[PER], int buf) {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int c = tid + p * 256;
+            const int c = tid + p * NT;
             if (c < NKC) {
                 *(uint4*)&Ks[buf][(c / CPR) * LDK + (c % CPR) * 8] = regs[p];
             } else {
@@ -391,86 +396,111 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_fa_kernel(const u16* __re
             }
         }
     };
-    load_tile(0);
-    store_tile(0);
-    for (int t = 0; t < ntiles; ++t) {
-        const int cur = t & 1;
-        __syncthreads();
-        if (t + 1 < ntiles) load_tile(t + 1);
+    // one tile from LDS buffer cur: scores, online softmax, P V
+    auto attend_tile = [&](int t, int cur) {
         const int kbase = t * KT;
-        if (kbase <= q0 + 31) {
-            f32x16 sc[2];
+        if (kbase > q0 + 31) return;
+        f32x16 sc[2];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
+        for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sc[hh][i] = 0.f;
+            for (int i = 0; i < 16; ++i) sc[hh][i] = 0.f;
 #pragma unroll
-                for (int ks = 0; ks < HD / 16; ++ks) {
-                    sc[hh] = mfma32<I8>(*(const uint4*)&Ks[cur][(32 * hh + l32) * LDK + ks * 16 + kg * 8], qf[ks], sc[hh]);
-                }
+            for (int ks = 0; ks < HD / 16; ++ks) {
+                sc[hh] = mfma32<I8>(*(const uint4*)&Ks[cur][(32 * hh + l32) * LDK + ks * 16 + kg * 8], qf[ks], sc[hh]);
             }
-            // causal / length mask only where the tile reaches the diagonal or the end
-            const bool full = kbase + KT - 1 <= q0 && kbase + KT <= T;
-            if (!full) {
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = kbase + 32 * hh + ((i < 8) ? 8 * kg + i : 16 + 8 * kg + (i - 8));
-                        if (key > qi || key >= T) sc[hh][i] = -INFINITY;
-                    }
-            }
-            float mx = -INFINITY;
+        }
+        // causal / length mask only where the tile reaches the diagonal or the end
+        const bool full = kbase + KT - 1 <= q0 && kbase + KT <= T;
+        if (!full) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[hh][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_i, mx * sl2);
-            if (__builtin_amdgcn_ballot_w64(m_new > m_i)) {
-                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_i - m_new);
-                l_i *= alpha;
-#pragma unroll
-                for (int c = 0; c < HD / 32; ++c)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[c][i] *= alpha;
-            }
-            m_i = m_new;
-            const float nm = -m_new;
-            float rs = 0.f;
-            uint4 pb[2][2];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                float p[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    p[i] = __builtin_amdgcn_exp2f(fmaf(sc[hh][i], sl2, nm));
-                    rs += p[i];
-                }
-                uint4 pu0, pu1;
-                pu0.x = pack_op2<I8>(p[0], p[1]);
-                pu0.y = pack_op2<I8>(p[2], p[3]);
-                pu0.z = pack_op2<I8>(p[4], p[5]);
-                pu0.w = pack_op2<I8>(p[6], p[7]);
-                pu1.x = pack_op2<I8>(p[8], p[9]);
-                pu1.y = pack_op2<I8>(p[10], p[11]);
-                pu1.z = pack_op2<I8>(p[12], p[13]);
-                pu1.w = pack_op2<I8>(p[14], p[15]);
-                pb[hh][0] = pu0;
-                pb[hh][1] = pu1;
-            }
-            rs += __shfl_xor(rs, 32);
-            l_i += rs;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int c = 0; c < HD / 32; ++c) {
-                    const u16* vrow = &Vt[cur][(c * 32 + l32) * LDV + 32 * hh];
-                    oacc[c] = mfma32<I8>(*(const uint4*)(vrow + 8 * kg), pb[hh][0], oacc[c]);
-                    oacc[c] = mfma32<I8>(*(const uint4*)(vrow + 16 + 8 * kg), pb[hh][1], oacc[c]);
+                    const int key = kbase + 32 * hh + ((i < 8) ? 8 * kg + i : 16 + 8 * kg + (i - 8));
+                    if (key > qi || key >= T) sc[hh][i] = -INFINITY;
                 }
         }
-        if (t + 1 < ntiles) store_tile(cur ^ 1);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[hh][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_i, mx * sl2);
+        if (__builtin_amdgcn_ballot_w64(m_new > m_i)) {
+            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_i - m_new);
+            l_i *= alpha;
+#pragma unroll
+            for (int c = 0; c < HD / 32; ++c)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[c][i] *= alpha;
+        }
+        m_i = m_new;
+        const float nm = -m_new;
+        float rs = 0.f;
+        uint4 pb[2][2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            float p[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                p[i] = __builtin_amdgcn_exp2f(fmaf(sc[hh][i], sl2, nm));
+                rs += p[i];
+            }
+            uint4 pu0, pu1;
+            pu0.x = pack_op2<I8>(p[0], p[1]);
+            pu0.y = pack_op2<I8>(p[2], p[3]);
+            pu0.z = pack_op2<I8>(p[4], p[5]);
+            pu0.w = pack_op2<I8>(p[6], p[7]);
+            pu1.x = pack_op2<I8>(p[8], p[9]);
+            pu1.y = pack_op2<I8>(p[10], p[11]);
+            pu1.z = pack_op2<I8>(p[12], p[13]);
+            pu1.w = pack_op2<I8>(p[14], p[15]);
+            pb[hh][0] = pu0;
+            pb[hh][1] = pu1;
+        }
+        rs += __shfl_xor(rs, 32);
+        l_i += rs;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int c = 0; c < HD / 32; ++c) {
+                const u16* vrow = &Vt[cur][(c * 32 + l32) * LDV + 32 * hh];
+                oacc[c] = mfma32<I8>(*(const uint4*)(vrow + 8 * kg), pb[hh][0], oacc[c]);
+                oacc[c] = mfma32<I8>(*(const uint4*)(vrow + 16 + 8 * kg), pb[hh][1], oacc[c]);
+            }
+    };
+    if constexpr (NW == 4) {
+        uint4 regs[PER];
+        load_tile(regs, 0);
+        store_tile(regs, 0);
+        for (int t = 0; t < ntiles; ++t) {
+            const int cur = t & 1;
+            __syncthreads();
+            if (t + 1 < ntiles) load_tile(regs, t + 1);
+            attend_tile(t, cur);
+            if (t + 1 < ntiles) store_tile(regs, cur ^ 1);
+        }
+    } else {
+        // tile t sits in LDS buffer t & 1; register set A carries the odd tiles, B the
+        // even ones from tile 2 on, each loaded two tiles before it is stored
+        uint4 ra[PER], rb[PER];
+        load_tile(ra, 0);
+        store_tile(ra, 0);
+        if (ntiles > 1) load_tile(ra, 1);
+        if (ntiles > 2) load_tile(rb, 2);
+        for (int t = 0; t < ntiles; t += 2) {
+            __syncthreads();
+            attend_tile(t, 0);
+            if (t + 1 < ntiles) store_tile(ra, 1);
+            if (t + 3 < ntiles) load_tile(ra, t + 3);
+            if (t + 1 >= ntiles) break;
+            __syncthreads();
+            attend_tile(t + 1, 1);
+            if (t + 2 < ntiles) store_tile(rb, 0);
+            if (t + 4 < ntiles) load_tile(rb, t + 4);
+        }
     }
     if (qi < T) {
         const float inv = 1.f / l_i;
@@ -1640,16 +1670,23 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
     }
 }
 
+// waves per workgroup of the hd-128 flash prefill
+constexpr int kFlashWaves = 8;
+
 template <int HD>
 hipError_t prefill_hd(const u16* q, const KVLayer& kv, int B, int T, int H, u16* out, float* lse,
                       hipStream_t st) {
     dim3 grid((T + 127) / 128, H, B);
     const float sl2 = kLog2e / sqrtf((float)HD);
     if (HD == 128) {
+        constexpr int NW = kFlashWaves;
+        dim3 fgrid((T + 32 * NW - 1) / (32 * NW), H, B);
         if (kv.lazy && kv.base_bits == 8)
-            hipLaunchKernelGGL((attn_prefill_fa_kernel<true>), grid, dim3(256), 0, st, q, kv, T, H, out, lse, sl2);
+            hipLaunchKernelGGL((attn_prefill_fa_kernel<true, NW>), fgrid, dim3(64 * NW), 0, st, q, kv, T, H, out, lse,
+                               sl2);
         else
-            hipLaunchKernelGGL((attn_prefill_fa_kernel<false>), grid, dim3(256), 0, st, q, kv, T, H, out, lse, sl2);
+            hipLaunchKernelGGL((attn_prefill_fa_kernel<false, NW>), fgrid, dim3(64 * NW), 0, st, q, kv, T, H, out, lse,
+                               sl2);
         return hipGetLastError();
     }
     if (kv.lazy && kv.base_bits == 8)
