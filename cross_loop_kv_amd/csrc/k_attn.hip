@@ -556,17 +556,22 @@ __global__ __launch_bounds__(64 * NW) void column_mass_kernel(const u16* __restr
     float cs[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) cs[i] = 0.f;
-    // iteration it covers head g*G + it/nq and query tile qt0 + it%nq
-    const int qt0 = kblk / 32, nq = (T + 31) / 32 - qt0, nit = G * nq;
+    // The loop walks (head hh, query tile qt) with qt fastest, from the tile holding the
+    // workgroup's first key to the last one.  Query chunk p of this thread is row
+    // tid/16 + (NT/16) p of the tile at elements (tid % 16) 8: a fixed offset from the
+    // tile's first row; a full tile loads without bounds checks.
+    const int qt0 = kblk / 32, nqt = (T + 31) / 32, nit = G * (nqt - qt0);
+    const int qr = tid / CPR;
+    const long long qoff = (long long)qr * ldq + (tid % CPR) * 8;
     uint4 regs[PER];
-    auto load_tile = [&](int it) {
-        const int h = g * G + it / nq, qt = qt0 + it % nq;
+    auto load_tile = [&](int hh, int qt) {
+        const u16* qb = Q + ((long long)b * T + qt * 32) * ldq + (g * G + hh) * HD;
+        const bool full = qt * 32 + 32 <= T;
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int c = tid + p * NT;
             regs[p] = make_uint4(0, 0, 0, 0);
-            const int q = qt * 32 + c / CPR;
-            if (c < NQC && q < T) regs[p] = *(const uint4*)(Q + ((long long)b * T + q) * ldq + h * HD + (c % CPR) * 8);
+            if (tid + p * NT < NQC && (full || qt * 32 + qr + p * (NT / CPR) < T))
+                regs[p] = *(const uint4*)(qb + qoff + (long long)p * (NT / CPR) * ldq);
         }
     };
     auto store_tile = [&](int buf) {
@@ -576,13 +581,19 @@ __global__ __launch_bounds__(64 * NW) void column_mass_kernel(const u16* __restr
             if (c < NQC) *(uint4*)&Qs[buf][(c / CPR) * LDQ + (c % CPR) * 8] = I8 ? bf8_to_h8(regs[p]) : regs[p];
         }
     };
-    load_tile(0);
+    int hh = 0, qt = qt0;  // the tile in LDS buffer it & 1
+    load_tile(hh, qt);
     store_tile(0);
     for (int it = 0; it < nit; ++it) {
         const int cur = it & 1;
+        int hn = hh, qn = qt + 1;
+        if (qn == nqt) {
+            qn = qt0;
+            ++hn;
+        }
         __syncthreads();
-        if (it + 1 < nit) load_tile(it + 1);
-        const int h = g * G + it / nq, qt = qt0 + it % nq;
+        if (it + 1 < nit) load_tile(hn, qn);
+        const int h = g * G + hh;
         const int q = qt * 32 + l32;
         if (qt * 32 + 31 >= j0) {
             const float lse2 = (q < T) ? LSE[((long long)b * H + h) * T + q] : 0.f;
@@ -606,6 +617,8 @@ __global__ __launch_bounds__(64 * NW) void column_mass_kernel(const u16* __restr
             }
         }
         if (it + 1 < nit) store_tile(cur ^ 1);
+        hh = hn;
+        qt = qn;
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
