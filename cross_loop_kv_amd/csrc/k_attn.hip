@@ -1658,11 +1658,8 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
         const int k = head * HD + e;
         const long long oi = packed ? pk_index((int)qrow, k, H * HD) : qrow * H * HD + k;
         const long long di = qrow * H * HD + k;
-        // packed (decode products): a hi/lo bf16 pair, lo 8 H hd elements on
-        auto put = [&](float y) {
-            if (packed) split_bf2(y, &out[oi], &out[8LL * H * HD + oi]);
-            else out[oi] = f2bf(y);
-        };
+        // packed (decode products): float16 in the lane-packed order
+        auto put = [&](float y) { out[oi] = packed ? f2h_bits(y) : f2bf(y); };
         switch (df.mode) {
             case DIFF_ADD32: put(o + df.d32[di]); break;
             case DIFF_SET32:

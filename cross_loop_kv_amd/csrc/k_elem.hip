@@ -21,8 +21,8 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(const int32_t* ids, con
     for (int j = threadIdx.x; j < d; j += kThreads) dst[j] = bf2f(tok[src + j]);
 }
 
-// x += add (optional); xg = x * gain as a lane-packed hi/lo bf16 pair (hi at xg, lo at
-// xg + 8 d); ps[r] = sum of x^2 over the row.
+// x += add (optional); xg = x * gain as lane-packed float16; ps[r] = sum of x^2 over the
+// row.
 __global__ __launch_bounds__(kThreads) void norm_prep_kernel(float* x, const u16* add, const u16* gain, int d,
                                                              u16* xg, float* ps) {
     __shared__ float red[16];
@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kThreads) void norm_prep_kernel(float* x, const u16
             row[j] = v;
         }
         const long long pi = pk_index(r, j, d);
-        split_bf2(v * bf2f(gain[j]), &xg[pi], &xg[8LL * d + pi]);
+        xg[pi] = f2h_bits(v * bf2f(gain[j]));
         ss += v * v;
     }
     ss = block_sum(ss, red);

@@ -250,13 +250,16 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(const u16* __restrict_
 }
 
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
 // ---------------------------------------------------------------- folded skinny kernel
 // Requires M <= 8 and K % 64 == 0.  Wave w takes the 32-element k chunks c = w, w + 8,
 // ... of each half, NL chunks per batch of loads.
 //
-// PK (lane-packed operands, the decode products): A is a hi/lo pair of bf16 operands,
-// hi at A and lo at A + 8 K (x = hi + lo to 2^-16), and the bf16 outputs (xg_out, Obf)
-// are written the same way; otherwise A and the outputs are plain bf16, row-major.
+// PK (lane-packed operands, the decode products): W is the float16 decode copy of the
+// weights, A float16 in the same lane-packed order (one rounding of the float32 value),
+// and the 16-bit outputs (xg_out, Obf) are written that way; otherwise A, W and the
+// outputs are bf16, row-major.
 // NORM (RMSNorm folded in): A holds x * gain and ps_in [nparts][8] partial sums of x^2
 // per row; the product is scaled by 1 / sqrt(sum / K + eps).
 // PREP (with EPI_ADD): besides x += A W^T (+ add_vec), write what the next NORM
@@ -311,12 +314,16 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
         if (PREP && io.add_vec) addv = bf2f(io.add_vec[col]);
         if (PREP) gainv = bf2f(io.next_gain[col]);
     }
-    // PK: the activation is a hi/lo bf16 pair (lo at A + 8 K); both halves meet the same
-    // weight operand, so the product carries the float32 activation to 2^-16.
-    const long long lo_off = 8LL * K;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    // float16 operands on the lane-packed path, bf16 on the row-major one
+    auto mma = [](uint4 a, uint4 b, f32x4 c) {
+        if constexpr (PK)
+            return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                          0, 0, 0);
+        else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+    };
     for (int c0 = w; c0 < nch; c0 += NWV * NL) {
-        uint4 wv[NL], wv1[NL], av[NL], al[NL];
+        uint4 wv[NL], wv1[NL], av[NL];
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             const int c = c0 + j * NWV;
@@ -329,17 +336,11 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
             const int c = c0 + j * NWV;
             const bool ok = c < nch && mvalid;
             av[j] = ok ? *(const uint4*)(ar + (long long)c * wstep) : make_uint4(0, 0, 0, 0);
-            if (PK) al[j] = ok ? *(const uint4*)(ar + lo_off + (long long)c * wstep) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[j]), as_bf16x8(wv[j]), acc0, 0, 0, 0);
-            if (PK) acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al[j]), as_bf16x8(wv[j]), acc0, 0, 0, 0);
-            if (DUAL) {
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[j]), as_bf16x8(wv1[j]), acc1, 0, 0, 0);
-                if (PK)
-                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al[j]), as_bf16x8(wv1[j]), acc1, 0, 0, 0);
-            }
+            acc0 = mma(av[j], wv[j], acc0);
+            if (DUAL) acc1 = mma(av[j], wv1[j], acc1);
         }
     }
     if (norm_wave) {  // wave w: row w's sum of squares, partials in a fixed order
@@ -386,8 +387,7 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
             C[o] = x;
             if (PREP) {
                 if (PK) {
-                    const long long pi = pk_index(m, col, N);
-                    split_bf2(x * gainv, &io.xg_out[pi], &io.xg_out[8LL * N + pi]);
+                    io.xg_out[pk_index(m, col, N)] = f2h_bits(x * gainv);
                 } else {
                     io.xg_out[o] = f2bf(x * gainv);
                 }
@@ -396,8 +396,7 @@ __global__ __launch_bounds__(512) void gemm_fold_kernel(const u16* __restrict__ 
         } else {
             const float y = EPI == EPI_SWIGLU ? silu_f(v0) * ((s1[i] + o1[i]) * inv) : gelu_f(v0);
             if (PK) {
-                const long long pi = pk_index(m, col, N);
-                split_bf2(y, &Obf[pi], &Obf[8LL * N + pi]);
+                Obf[pk_index(m, col, N)] = f2h_bits(y);
             } else {
                 Obf[o] = f2bf(y);
             }
@@ -431,12 +430,23 @@ void launch_fold(const u16* A, const u16* W, int M, int N, int K, float* c, u16*
         hipLaunchKernelGGL((gemm_fold_kernel<EPI, 4, NORM, PREP, PK, false>), grid, dim3(512), 0, st, A, W, M, N, K, c, out_bf, io);
 }
 
+// The decode copy of a bf16 weight matrix: float16 in the lane-packed order.  A bf16
+// value converts exactly when its magnitude lies in [2^-17, 65504] (float16 has three
+// more mantissa bits; below 2^-14 it keeps 2^-24 steps); smaller magnitudes round to
+// the nearest 2^-24 step (an error below 3e-8), larger ones become inf.
 __global__ void pack_rows_kernel(const u16* __restrict__ W, long long rows, int K, u16* __restrict__ Wp) {
     const long long n8 = rows * K / 8;  // 16-byte pieces
     for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n8; i += (long long)gridDim.x * blockDim.x) {
         const long long row = i / (K / 8);
         const int k = (int)(i % (K / 8)) * 8;
-        *(uint4*)(Wp + pk_index((int)row, k, K)) = *(const uint4*)(W + row * K + k);
+        const uint4 v = *(const uint4*)(W + row * K + k);
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            o[t] = (uint32_t)f2h_bits(__uint_as_float(wv[t] << 16)) |
+                   ((uint32_t)f2h_bits(__uint_as_float(wv[t] & 0xFFFF0000u)) << 16);
+        *(uint4*)(Wp + pk_index((int)row, k, K)) = make_uint4(o[0], o[1], o[2], o[3]);
     }
 }
 

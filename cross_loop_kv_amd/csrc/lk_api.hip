@@ -430,15 +430,13 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
     w.h = (float*)take(M * d * 4);
     w.h0 = (float*)take(hd_->lazy() || c.input_reinject ? M * d * 4 : 0);
     w.xc = (float*)take(hd_->lazy() ? (long long)B * n * d * 4 : 0);
-    // bf16 operands of the decode products are lane-packed over 8 rows (at least 8 rows)
-    // and held as hi/lo pairs (twice the elements)
+    // 16-bit operands of the decode products are lane-packed over 8 rows (at least 8 rows)
     const long long M8 = M < 8 ? 8 : M;
-    const long long pair = T == 1 ? 2 : 1;
-    w.xn = (u16*)take(pair * M8 * d * 2);
+    w.xn = (u16*)take(M8 * d * 2);
     w.qkv = (float*)take(M * hd_->qkv_w() * 4);
     w.q = (u16*)take(M * Hhd * 2);
-    w.att = (u16*)take(pair * M8 * Hhd * 2);
-    w.act = (u16*)take(pair * M8 * (long long)c.ffn_dim * 2);
+    w.att = (u16*)take(M8 * Hhd * 2);
+    w.act = (u16*)take(M8 * (long long)c.ffn_dim * 2);
     w.lse = (float*)take(M * c.n_heads * 4);
     w.mass = (float*)take(hd_->lazy() ? M * c.n_kv_heads * 4 : 0);
     w.keys = (float*)take(hd_->lazy() ? M * 4 : 0);

@@ -52,16 +52,6 @@ __device__ __forceinline__ float rope_hi(float x1, float x2, float c, float sn) 
     return x2 * c + x1 * sn;
 }
 
-// ---------------------------------------------------------------- split operands
-// A float32 value as the sum of two bfloat16 values: hi = bf16(x), lo = bf16(x - hi)
-// (x - hi is exact).  hi + lo is within 2^-16 |x| of x, so a product that takes both
-// halves through bf16 MFMAs is as accurate as a float32 operand to that level.
-__device__ __forceinline__ void split_bf2(float x, u16* hi, u16* lo) {
-    const u16 h = f2bf(x);
-    *hi = h;
-    *lo = f2bf(x - bf2f(h));
-}
-
 // ---------------------------------------------------------------- reductions
 // Butterfly reductions: every lane ends with the same, run-to-run identical value.
 __device__ __forceinline__ float wave_sum(float v) {

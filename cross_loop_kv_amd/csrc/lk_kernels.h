@@ -188,9 +188,8 @@ hipError_t gemm_rmsnorm(const float* X, const u16* gain, float eps, const u16* W
 // the consumer multiplies xg by W and scales by 1 / sqrt(sum(ps) / K + eps).
 // Weights (Wp) and activations (xg, A, and the activation outputs) are in the
 // lane-packed order of pk_index (weights: rows = N, or 2N for SwiGLU's [gate; up]).
-// Every activation operand of these products is a hi/lo pair of bf16 values
-// (split_bf2): hi in the first 8 K elements of the buffer, lo in the next 8 K, so the
-// decode projections see their float32 inputs to 2^-16 (the weights are bf16 as given).
+// Operands are float16: the weights as converted from bf16 by pack_weights (exact for
+// magnitudes in [2^-17, 65504]) and every activation rounded once from float32.
 struct FoldIO {
     const float* ps_in;    // NORM: partial sums of x^2 [nparts][8]
     int nparts;
@@ -199,7 +198,7 @@ struct FoldIO {
     const float* add_rows; // PREP: float32 [M, N] added to x after the product, before add_vec
     float* x_save;         // PREP: float32 [M, N] receives x after the product, before the adds
     const u16* next_gain;  // PREP: bf16 [N] gain of the next RMSNorm
-    u16* xg_out;           // PREP: bf16 [M, N]
+    u16* xg_out;           // PREP: float16 [M, N], lane-packed
     float* ps_out;         // PREP: [N / 8][8]
     const int32_t* live;   // nonzero *live or nullptr: run; *live == 0: return at once
 };
@@ -211,10 +210,10 @@ hipError_t gemm_fold_norm(const u16* xg, const float* ps, int nparts, float eps,
 hipError_t gemm_fold_add(const u16* A, const u16* Wp, int M, int N, int K, float* x, const u16* add_vec,
                          const u16* next_gain, u16* xg_out, float* ps_out, hipStream_t st,
                          const float* add_rows = nullptr, float* x_save = nullptr, const int32_t* live = nullptr);
-// Row-major W [rows, K] -> lane-packed Wp (rows % 8 == 0, K % 64 == 0).
+// Row-major bf16 W [rows, K] -> lane-packed float16 Wp (rows % 8 == 0, K % 64 == 0).
 hipError_t pack_weights(const u16* W, long long rows, int K, u16* Wp, hipStream_t st);
-// x += add (optional); xg = x * gain as a lane-packed hi/lo bf16 pair (hi at xg, lo at
-// xg + 8 d); ps[0][r] = sum of x^2 of row r.
+// x += add (optional); xg = x * gain as lane-packed float16; ps[0][r] = sum of x^2 of
+// row r.
 hipError_t norm_prep(float* x, const u16* add, const u16* gain, int rows, int d, u16* xg, float* ps,
                      hipStream_t st);
 
@@ -294,8 +293,8 @@ hipError_t gather_recon(const RowsAttn& a, int mode, int ncap, u16* kc, u16* vc,
 hipError_t attn_rows_prefill(const RowsAttn& a, const KVLayer& sc, const KVLayer& fr, hipStream_t st);
 // attn_rows_main writes the per-split partials; attn_rows_combine merges them into `out`.
 hipError_t attn_rows_main(const RowsAttn& a, hipStream_t st);
-// packed_out: out in the lane-packed order of the decode products (at most 8 rows), as a
-// hi/lo bf16 pair (lo at out + 8 H hd).
+// packed_out: out in the lane-packed order of the decode products (at most 8 rows), as
+// float16.
 hipError_t attn_rows_combine(const RowsAttn& a, hipStream_t st, bool packed_out = false);
 
 }  // namespace lk

@@ -218,8 +218,10 @@ int lk_set_decode_graphs(lk_handle *h, int32_t enable);
 
 /* Device bytes of the decode copy of the layer projections (0 if the shapes do
  * not take it: it needs d_model, heads*head_dim and ffn_dim multiples of 64).
- * Decode steps with at most 8 sequences multiply by the weights in an operand
- * order packed for the MFMA lanes (every wave load reads 1 KB contiguous). */
+ * Decode steps with at most 8 sequences multiply by this copy: the weights as
+ * float16 (converted from bf16: exact for magnitudes in [2^-17, 65504], smaller ones
+ * rounded to 2^-24 steps), in an operand order packed for the MFMA lanes (every wave
+ * load reads 1 KB contiguous), with float16 activations. */
 int lk_decode_weight_bytes(const lk_handle *h, size_t *bytes);
 
 /* Give the handle a caller-owned device buffer of at least lk_decode_weight_bytes

@@ -522,8 +522,8 @@ def test_full_depth_decode_at_full_context():
     about 1) imported through a snapshot; the last sequence (the sample) against the
     oracle holding the same state, within 2e-2.  192 layer applications of random
     weights over a random context amplify any rounding; the decode products take their
-    activations as hi/lo bf16 pairs and the attention its queries in float16, which
-    keeps the step within the bound at this depth."""
+    activations and weights in float16 (not bf16) and the attention its queries in
+    float16, which keeps the step within the bound at this depth."""
     from tests.gpu_util import cached_weights
     from tests.synth_state import snapshot_with_states
     wl = I.workload("deep_48x4_b8_ctx32k")
@@ -735,8 +735,8 @@ def test_decode_graph_replay_matches_eager_launches(mode, timed, Bsz):
 
 
 def test_decode_packed_weights_match_row_major_weights():
-    """Decode with the packed decode copy of the weights (the folded products, hi/lo
-    activations) against decode with the buffer detached (row-major weights, the
+    """Decode with the packed decode copy of the weights (the folded products, float16
+    weights and activations) against decode with the buffer detached (row-major weights, the
     unfolded kernels, bf16 activations): both against the oracle, and each other within
     the bound.  Detaching and re-attaching the buffer drops the captured step; the size
     query and the capacity check hold."""
