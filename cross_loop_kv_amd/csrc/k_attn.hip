@@ -47,7 +47,7 @@ __device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(h
 // bf16 values below 2^-14 lose bits as float16 subnormals.
 template <bool F16>
 __device__ __forceinline__ uint32_t pack_op2(float a, float b) {
-    if constexpr (F16) return (uint32_t)f2h_bits(a) | ((uint32_t)f2h_bits(b) << 16);
+    if constexpr (F16) return pack_h2(a, b);
     else return pack_bf2(a, b);
 }
 template <bool F16>
@@ -62,7 +62,7 @@ __device__ __forceinline__ uint4 bf8_to_h8(uint4 v) {
     uint32_t o[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-        o[t] = (uint32_t)f2h_bits(__uint_as_float(w[t] << 16)) | ((uint32_t)f2h_bits(__uint_as_float(w[t] & 0xFFFF0000u)) << 16);
+        o[t] = pack_h2(__uint_as_float(w[t] << 16), __uint_as_float(w[t] & 0xFFFF0000u));
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
@@ -305,7 +305,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_fa_kernel(const 
     constexpr int PK = NKC / NT;            // of which K chunks
     __shared__ __attribute__((aligned(16))) u16 Ks[2][KT * LDK];
     __shared__ __attribute__((aligned(16))) u16 Vt[2][HD * LDV];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // the wave index through readfirstlane: the per-wave tests below (a tile above the
+    // wave's queries, a tile that needs the causal mask) are then scalar branches, not
+    // lane-masked regions that every tile would step through
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = lane >> 5, l32 = lane & 31;
     const int h = blockIdx.y, b = blockIdx.z;
     const int G = H / kv.Hkv, g = h / G;
@@ -536,7 +539,8 @@ __global__ __launch_bounds__(64 * NW) void column_mass_kernel(const u16* __restr
     constexpr int NT = 64 * NW;
     constexpr int PER = (NQC + NT - 1) / NT;
     __shared__ __attribute__((aligned(16))) u16 Qs[2][32 * LDQ];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // wave index through readfirstlane: the diagonal tests are scalar branches
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = lane >> 5, l32 = lane & 31;
     const int g = blockIdx.y, b = blockIdx.z;
     const int Hkv = kv.Hkv, G = H / Hkv;
@@ -752,10 +756,10 @@ __device__ __forceinline__ void decode_tile(const KVLayer& kv, int b, int g, int
     // ---- O^T += V^T P^T; lane (e, kgrp): V[keys kb+8kgrp .. +8][e] is one contiguous run
     uint4 pu;
     if (HALF) {
-        pu.x = (uint32_t)f2h_bits(p[0]) | ((uint32_t)f2h_bits(p[1]) << 16);
-        pu.y = (uint32_t)f2h_bits(p[2]) | ((uint32_t)f2h_bits(p[3]) << 16);
-        pu.z = (uint32_t)f2h_bits(p[4]) | ((uint32_t)f2h_bits(p[5]) << 16);
-        pu.w = (uint32_t)f2h_bits(p[6]) | ((uint32_t)f2h_bits(p[7]) << 16);
+        pu.x = pack_h2(p[0], p[1]);
+        pu.y = pack_h2(p[2], p[3]);
+        pu.z = pack_h2(p[4], p[5]);
+        pu.w = pack_h2(p[6], p[7]);
     } else {
         pu.x = pack_bf2(p[0], p[1]);
         pu.y = pack_bf2(p[2], p[3]);
@@ -825,7 +829,7 @@ __device__ __forceinline__ void decode_q(const RowsAttn& a, int b, int g, int c1
                     r2[u] = lo ? rope_lo(x1[m], x2[m], c, sn) : rope_hi(x1[m], x2[m], c, sn);
                 }
                 // the float16 kernels take the rotated float32 q with one rounding
-                o[t] = HALF ? ((uint32_t)f2h_bits(r2[0]) | ((uint32_t)f2h_bits(r2[1]) << 16)) : pack_bf2(r2[0], r2[1]);
+                o[t] = HALF ? (pack_h2(r2[0], r2[1])) : pack_bf2(r2[0], r2[1]);
             }
             v = make_uint4(o[0], o[1], o[2], o[3]);
         } else if (hvalid) {
@@ -836,8 +840,7 @@ __device__ __forceinline__ void decode_q(const RowsAttn& a, int b, int g, int c1
             uint32_t o[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                o[t] = (uint32_t)f2h_bits(__uint_as_float(wv[t] << 16)) |
-                       ((uint32_t)f2h_bits(__uint_as_float(wv[t] & 0xFFFF0000u)) << 16);
+                o[t] = pack_h2(__uint_as_float(wv[t] << 16), __uint_as_float(wv[t] & 0xFFFF0000u));
             v = make_uint4(o[0], o[1], o[2], o[3]);
         }
         qop[j] = v;
@@ -1074,7 +1077,7 @@ __global__ __launch_bounds__(256) void gather_recon_kernel(RowsAttn a, int mode,
             uint32_t o[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                o[q] = (uint32_t)f2h_bits(x[8 * j8 + 2 * q]) | ((uint32_t)f2h_bits(x[8 * j8 + 2 * q + 1]) << 16);
+                o[q] = pack_h2(x[8 * j8 + 2 * q], x[8 * j8 + 2 * q + 1]);
             *(uint4*)(dst + 8 * j8) = make_uint4(o[0], o[1], o[2], o[3]);
         }
     }
@@ -1137,7 +1140,7 @@ __global__ __launch_bounds__(256) void gather_recon_kernel(RowsAttn a, int mode,
             uint32_t o[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                o[j] = (uint32_t)f2h_bits(vx[2 * j][q]) | ((uint32_t)f2h_bits(vx[2 * j + 1][q]) << 16);
+                o[j] = pack_h2(vx[2 * j][q], vx[2 * j + 1][q]);
             *(uint4*)(vc + (blk * HD + e0 + q) * 8) = make_uint4(o[0], o[1], o[2], o[3]);
         }
     }
@@ -1366,8 +1369,8 @@ __global__ __launch_bounds__(G > 4 ? 64 * G : 256) void attn_rows_pf_kernel(Rows
                         v.y = pack_bf2(x[2], x[3]);
                         *(uint2*)(orow + e0) = v;
                     } else {
-                        v.x = (uint32_t)f2h_bits(x[0]) | ((uint32_t)f2h_bits(x[1]) << 16);
-                        v.y = (uint32_t)f2h_bits(x[2]) | ((uint32_t)f2h_bits(x[3]) << 16);
+                        v.x = pack_h2(x[0], x[1]);
+                        v.y = pack_h2(x[2], x[3]);
                         *(uint2*)(drow + e0) = v;
                     }
                 }

@@ -444,8 +444,7 @@ __global__ void pack_rows_kernel(const u16* __restrict__ W, long long rows, int 
         uint32_t o[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-            o[t] = (uint32_t)f2h_bits(__uint_as_float(wv[t] << 16)) |
-                   ((uint32_t)f2h_bits(__uint_as_float(wv[t] & 0xFFFF0000u)) << 16);
+            o[t] = pack_h2(__uint_as_float(wv[t] << 16), __uint_as_float(wv[t] & 0xFFFF0000u));
         *(uint4*)(Wp + pk_index((int)row, k, K)) = make_uint4(o[0], o[1], o[2], o[3]);
     }
 }

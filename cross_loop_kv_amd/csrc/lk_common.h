@@ -15,15 +15,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // ---------------------------------------------------------------- bfloat16
 __device__ __forceinline__ float bf2f(u16 v) { return __uint_as_float((uint32_t)v << 16); }
 
-// Round to nearest even (inputs are finite).
-__device__ __forceinline__ u16 f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (u16)(u >> 16);
-}
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
 
+// Round to nearest even (v_cvt_pk_bf16_f32; NaN stays NaN).
+__device__ __forceinline__ u16 f2bf(float f) { return __builtin_bit_cast(u16, (__bf16)f); }
+
+// Two floats as packed bf16, a in the low half (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-    return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, bf16x2v));
 }
 
 // Eight bf16 (16 bytes) reinterpreted as an MFMA operand.
@@ -36,6 +37,11 @@ __device__ __forceinline__ u16 f2h_bits(float f) {
 }
 __device__ __forceinline__ float h2f(u16 bits) {
     return (float)__builtin_bit_cast(_Float16, bits);
+}
+// Two floats as packed float16, a in the low half, round to nearest even (one
+// v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, f16x2v));
 }
 
 // ---------------------------------------------------------------- rotary embedding
