@@ -429,7 +429,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_fa_kernel(const 
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[hh][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        {  // the row's other half sits 32 lanes away: exchange the halves in registers
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        }
         const float m_new = fmaxf(m_i, mx * sl2);
         if (__builtin_amdgcn_ballot_w64(m_new > m_i)) {
             const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_i - m_new);
@@ -463,8 +466,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_fa_kernel(const 
             pb[hh][0] = pu0;
             pb[hh][1] = pu1;
         }
-        rs += __shfl_xor(rs, 32);
-        l_i += rs;
+        l_i += rs;  // this lane's half of the row sum; the halves are added once at the end
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -505,6 +507,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_fa_kernel(const 
             if (t + 4 < ntiles) load_tile(rb, t + 4);
         }
     }
+    l_i += __shfl_xor(l_i, 32);
     if (qi < T) {
         const float inv = 1.f / l_i;
         u16* orow = O + ((long long)b * T + qi) * ldq + h * HD;
