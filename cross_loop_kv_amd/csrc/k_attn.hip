@@ -1161,7 +1161,7 @@ __global__ __launch_bounds__(256) void gather_recon_kernel(RowsAttn a, int mode,
 // (q converted from bf16: exact for magnitudes in [2^-14, 65504]), online softmax as in the flash prefill, output written
 // directly (no split partials).
 template <int G>
-__global__ __launch_bounds__(G > 4 ? 64 * G : 256) void attn_rows_pf_kernel(RowsAttn a, KVLayer sc, KVLayer fr,
+__global__ __launch_bounds__(G > 4 ? 64 * G : 256, 2) void attn_rows_pf_kernel(RowsAttn a, KVLayer sc, KVLayer fr,
                                                                             float sl2) {
     constexpr int HD = 128, KT = 64, LDK = HD + 8, LDV = KT + 8, CPR = HD / 8;
     constexpr int NW = G > 4 ? G : 4, NT = NW * 64;
@@ -1172,7 +1172,9 @@ __global__ __launch_bounds__(G > 4 ? 64 * G : 256) void attn_rows_pf_kernel(Rows
     __shared__ __attribute__((aligned(16))) u16 Vt[2][HD * LDV];
     __shared__ int s_col[2][KT];
     __shared__ int s_pos[RB];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    __shared__ int s_cnt[NW];
+    // wave index through readfirstlane: the per-wave tests are scalar branches
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = lane >> 5, l32 = lane & 31;
     const int g = blockIdx.y, b = blockIdx.z, Hkv = a.kv.Hkv, H = a.H;
     const int bg = b * Hkv + g, n = a.n_rows, W = a.window;
@@ -1181,22 +1183,29 @@ __global__ __launch_bounds__(G > 4 ? 64 * G : 256) void attn_rows_pf_kernel(Rows
     for (int i = tid; i < RB; i += NT) s_pos[i] = j0 + i < n ? a.qpos[(long long)b * n + j0 + i] : -1;
     __syncthreads();
     const int jl = min(j0 + RB, n) - 1;
-    const int Pf = s_pos[0], Pl = s_pos[jl - j0];
+    const int Pf = __builtin_amdgcn_readfirstlane(s_pos[0]), Pl = __builtin_amdgcn_readfirstlane(s_pos[jl - j0]);
     const int32_t* S = a.cols + (long long)bg * a.n_cols;
-    int lo = 0, hi = a.n_cols;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (S[mid] <= Pl - W) lo = mid + 1;
-        else hi = mid;
+    // columns at or below Pl - W (S ascending): counted by every thread over a stride,
+    // one round of loads instead of a binary search's chain
+    {
+        int c = 0;
+        for (int i = tid; i < a.n_cols; i += NT) c += S[i] <= Pl - W;
+        for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+        if (lane == 0) s_cnt[w] = c;
     }
-    const int cnt1 = lo, nt1 = (cnt1 + KT - 1) / KT;
+    __syncthreads();
+    int cnt1 = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) cnt1 += s_cnt[i];
+    cnt1 = __builtin_amdgcn_readfirstlane(cnt1);
+    const int nt1 = (cnt1 + KT - 1) / KT;
     const int lo2 = max(0, Pf - W + 1) & ~7;
     const int ntiles = nt1 + (Pl - lo2) / KT + 1;
     const int jr = j0 + rs * 32 + l32;
     const int P = jr < n ? s_pos[rs * 32 + l32] : -1;
     const bool wave_rows = j0 + rs * 32 < n;
-    const int wPf = wave_rows ? s_pos[rs * 32] : 0;
-    const int wPl = wave_rows ? s_pos[min(j0 + rs * 32 + 31, n - 1) - j0] : -1;
+    const int wPf = __builtin_amdgcn_readfirstlane(wave_rows ? s_pos[rs * 32] : 0);
+    const int wPl = __builtin_amdgcn_readfirstlane(wave_rows ? s_pos[min(j0 + rs * 32 + 31, n - 1) - j0] : -1);
     const long long ldq = (long long)H * HD;
 
     half8 qf[HD / 16];
@@ -1222,11 +1231,29 @@ __global__ __launch_bounds__(G > 4 ? 64 * G : 256) void attn_rows_pf_kernel(Rows
 
     uint4 regs[PER];
     int colr = INT_MAX;  // tile column of key tid (seg 1), staged like the operands
+    // A tile whose 64 keys all exist loads from fixed per-thread offsets (as the flash
+    // prefill): K chunk p holds key k0 + (NT/16) p of the tile, V chunk p the 8 keys of
+    // block tid/128 + (NT/128) (p - PK) at head dim tid % 128.
+    constexpr int PK = NKC / NT;
+    const int k0 = flash_key_of_row(tid / CPR);
+    const int koff = k0 * HD + (tid % CPR) * 8;
+    const int voff = (tid / HD) * HD * 8 + (tid % HD) * 8;
     auto load_tile = [&](int t) {
         const bool seg1 = t < nt1;
         const int base = seg1 ? t * KT : lo2 + (t - nt1) * KT;
         const int lim = seg1 ? cnt1 : Pl + 1;  // keys (rows or positions) below lim exist
         const KVLayer& L = seg1 ? sc : fr;
+        if (tid < KT) colr = (seg1 && base + tid < cnt1) ? S[base + tid] : INT_MAX;
+        if (base + KT <= lim) {
+            const long long r = (long long)bg * L.Tmax + base;
+            const u16* kb = (const u16*)L.base[0] + r * HD;
+            const u16* vb = (const u16*)L.base[1] + r * HD;
+#pragma unroll
+            for (int p = 0; p < PK; ++p) regs[p] = *(const uint4*)(kb + koff + p * (NT / 16) * HD);
+#pragma unroll
+            for (int p = 0; p < PER - PK; ++p) regs[PK + p] = *(const uint4*)(vb + voff + p * NT * 8);
+            return;
+        }
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * NT;
@@ -1239,11 +1266,10 @@ __global__ __launch_bounds__(G > 4 ? 64 * G : 256) void attn_rows_pf_kernel(Rows
             } else {
                 const int cc = c - NKC;
                 const int blk = cc / HD, e = cc % HD;
-                const int k0 = base + blk * 8;
-                if (k0 < lim) regs[p] = mask_tail8(*(const uint4*)((const u16*)L.base[1] + v_elem(L, b, g, k0, e)), lim - k0);
+                const int p0 = base + blk * 8;
+                if (p0 < lim) regs[p] = mask_tail8(*(const uint4*)((const u16*)L.base[1] + v_elem(L, b, g, p0, e)), lim - p0);
             }
         }
-        if (tid < KT) colr = (seg1 && base + tid < cnt1) ? S[base + tid] : INT_MAX;
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
@@ -1280,16 +1306,25 @@ __global__ __launch_bounds__(G > 4 ? 64 * G : 256) void attn_rows_pf_kernel(Rows
                     sv[hf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k8, qf[ks], sv[hf], 0, 0, 0);
                 }
             }
+            // every key of the tile visible to every row of the wave: no per-score mask
+            const bool full = seg1 ? s_col[cur][KT - 1] <= wPf - W : (pb > wPl - W && pb + KT - 1 <= wPf);
             float mx = -INFINITY;
+            if (full) {
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
+                for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int kx = 32 * hf + ((i < 8) ? 8 * kg + i : 16 + 8 * kg + (i - 8));
-                    const bool ok = seg1 ? s_col[cur][kx] <= P - W : (pb + kx <= P && pb + kx > P - W);
-                    if (!ok) sv[hf][i] = -INFINITY;
-                    mx = fmaxf(mx, sv[hf][i]);
-                }
+                    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[hf][i]);
+            } else {
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int kx = 32 * hf + ((i < 8) ? 8 * kg + i : 16 + 8 * kg + (i - 8));
+                        const bool ok = seg1 ? s_col[cur][kx] <= P - W : (pb + kx <= P && pb + kx > P - W);
+                        if (!ok) sv[hf][i] = -INFINITY;
+                        mx = fmaxf(mx, sv[hf][i]);
+                    }
+            }
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float m_new = fmaxf(m_i, mx * sl2);
             if (__builtin_amdgcn_ballot_w64(m_new > m_i)) {
