@@ -50,6 +50,42 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(float* x, const u16* 
     const int r = blockIdx.x;
     float* row = x + (long long)r * d;
     float ss = 0.f;
+    constexpr int MV = 4;  // float4 per thread held in registers (d <= 4096)
+    if (d % (4 * kThreads) == 0 && d <= MV * 4 * kThreads) {
+        const int nv = d / (4 * kThreads);
+        float4 v[MV];
+#pragma unroll
+        for (int k = 0; k < MV; ++k) {
+            if (k >= nv) break;
+            const int j = (k * kThreads + threadIdx.x) * 4;
+            float4 a = *(const float4*)(row + j);
+            if (add) {
+                const uint2 ad = *(const uint2*)(add + j);
+                a.x = a.x + __uint_as_float(ad.x << 16);
+                a.y = a.y + __uint_as_float(ad.x & 0xFFFF0000u);
+                a.z = a.z + __uint_as_float(ad.y << 16);
+                a.w = a.w + __uint_as_float(ad.y & 0xFFFF0000u);
+                *(float4*)(row + j) = a;
+            }
+            v[k] = a;
+            ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+        }
+        ss = block_sum(ss, red);
+        const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+        for (int k = 0; k < MV; ++k) {
+            if (k >= nv) break;
+            const int j = (k * kThreads + threadIdx.x) * 4;
+            const uint2 gv = *(const uint2*)(gain + j);
+            const float y0 = (v[k].x * inv) * __uint_as_float(gv.x << 16);
+            const float y1 = (v[k].y * inv) * __uint_as_float(gv.x & 0xFFFF0000u);
+            const float y2 = (v[k].z * inv) * __uint_as_float(gv.y << 16);
+            const float y3 = (v[k].w * inv) * __uint_as_float(gv.y & 0xFFFF0000u);
+            if (out_bf) *(uint2*)(out_bf + (long long)r * d + j) = make_uint2(pack_bf2(y0, y1), pack_bf2(y2, y3));
+            else *(float4*)(out_f32 + (long long)r * d + j) = make_float4(y0, y1, y2, y3);
+        }
+        return;
+    }
     for (int j = threadIdx.x; j < d; j += kThreads) {
         float v = row[j];
         if (add) {
@@ -318,6 +354,7 @@ __global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, in
     const float* src = qkv + (long long)r * (H + 2 * Hkv) * hd;
     const int qpb = 256 / hd;
     const int nq = (H + qpb - 1) / qpb;
+    const bool tab = w.rope_tab && pos < w.rope_rows;
     if (u < nq) {
         const int hh = u * qpb + t / half, i = t % half;
         if (hh >= H) return;
@@ -325,6 +362,9 @@ __global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, in
         if (w.rope_cs) {
             c = w.rope_cs[2 * i];
             sn = w.rope_cs[2 * i + 1];
+        } else if (tab) {
+            c = w.rope_tab[((long long)pos * half + i) * 2];
+            sn = w.rope_tab[((long long)pos * half + i) * 2 + 1];
         } else {
             double sd, cd;
             sincos((double)pos * inv.v[i], &sd, &cd);
@@ -347,6 +387,9 @@ __global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, in
         if (w.rope_cs) {
             c = w.rope_cs[2 * i];
             sn = w.rope_cs[2 * i + 1];
+        } else if (tab) {
+            c = w.rope_tab[((long long)pos * half + i) * 2];
+            sn = w.rope_tab[((long long)pos * half + i) * 2 + 1];
         } else {
             double sd, cd;
             sincos((double)pos * inv.v[i], &sd, &cd);
@@ -474,6 +517,24 @@ hipError_t rope_angles(const int32_t* dpos, const double* inv_freq, int hd, floa
     InvFreq inv;
     for (int i = 0; i < hd / 2; ++i) inv.v[i] = inv_freq[i];
     hipLaunchKernelGGL(rope_angles_kernel, dim3(1), dim3(64), 0, st, dpos, inv, hd / 2, cs);
+    return hipGetLastError();
+}
+
+__global__ void rope_table_kernel(InvFreq inv, int T, int half, float* tab) {
+    const long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+    if (i >= (long long)T * half) return;
+    const int p = (int)(i / half), k = (int)(i % half);
+    double sd, cd;
+    sincos((double)p * inv.v[k], &sd, &cd);
+    tab[2 * i] = (float)cd;
+    tab[2 * i + 1] = (float)sd;
+}
+
+hipError_t rope_table(const double* inv_freq, int T, int hd, float* tab, hipStream_t st) {
+    InvFreq inv;
+    for (int i = 0; i < hd / 2; ++i) inv.v[i] = inv_freq[i];
+    const long long n = (long long)T * (hd / 2);
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, inv, T, hd / 2, tab);
     return hipGetLastError();
 }
 

@@ -395,8 +395,10 @@ struct WS {
     float* ps;         // decode: per-workgroup row sums of x^2 for the next RMSNorm ([d/8][8])
     float* tokrec;     // decode, lazy: float32 K/V reconstruction of the step's rows [R][B][2][Hkv][hd]
     float* rope;       // decode: cos and sin of the step's position, [hd/2][2]
+    float* rope_tab;   // prefill: cos and sin of every prompt position, [T][hd/2][2]
     u16 *frk, *frv;    // prefill, lazy loops >= 2 (hd 128): float16 loop-k K/V at every prompt position
     int fr_cap;        // rows per (b, g) of frk / frv (T rounded up to 64; 0: none)
+    int rope_rows;     // prefill: positions in rope_tab (T; 0: none)
     // difference-corrected sparse attention: each row's loop-1 dense minus sparse output
     // per shared layer; prefill float16 [R][B][T][H hd], decode float32 [R][B][H hd]
     u16* dprompt;
@@ -466,6 +468,8 @@ WS ws_layout(const lk_handle* hd_, int B, int T, char* base) {
     w.frv = (u16*)take(fr_elems * 2);
     w.out = (float*)take((long long)B * d * 4);
     w.rope = (float*)take(T == 1 ? (long long)c.head_dim * 4 : 0);
+    w.rope_tab = (float*)take(T > 1 ? (long long)T * c.head_dim * 4 : 0);
+    w.rope_rows = T > 1 ? T : 0;
     w.dprompt = (u16*)take(diff ? (long long)c.n_shared * M * Hhd * 2 : 0);
     w.dstep = (float*)take(diff && T == 1 ? (long long)c.n_shared * B * Hhd * 4 : 0);
     const bool skip = hd_->lazy() && hd_->z.skip_tau > 0.f && c.n_loops >= 2 && T == 1;
@@ -636,6 +640,10 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
     lk::KVWrite kw = kvw;
     kw.dpos = io.dpos;
     if (decode && !io.pos && io.rows_per_seq == 1) kw.rope_cs = w.rope;  // decode: one position
+    if (!decode && w.rope_tab) {  // prefill: the table of every prompt position
+        kw.rope_tab = w.rope_tab;
+        kw.rope_rows = w.rope_rows;
+    }
     // decode, loops >= 2: the sparse attention launch rotates q and writes the new
     // token's K/V itself.  (The dense launches could too, and the step time would be
     // the same: their writing workgroup gets longer by about what the separate launch
@@ -1144,6 +1152,7 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
         LK_HIP(lk::fill_i32(slot_map(s, 2), -1, (long long)(K - 1) * B * s->Tpad, st));
     s->t = 0;
     s->prefilled = false;
+    if (w.rope_rows) LK_HIP(lk::rope_table(h->inv_freq, w.rope_rows, c.head_dim, w.rope_tab, st));
     LK_HIP(lk::embed(d_ids, h->tok, w.h, M, d, c.vocab, st));
 
     LayerIO io{w.h, M, T, nullptr, 0, nullptr};

@@ -70,6 +70,11 @@ struct KVWrite {
     // decode (every row at position *dpos): cos and sin of the rotation angles of that
     // position, [hd/2][2] (rope_angles), in place of evaluating them per element
     const float* rope_cs;
+    // prefill: cos and sin of every prompt position p < rope_rows, [p][hd/2][2]
+    // (rope_table, the same float64 evaluation rounded once), in place of evaluating
+    // them per element.  nullptr: evaluated per element.
+    const float* rope_tab;
+    int rope_rows;
     // kind 2 decode with loop skipping: act[b] == 0 marks a sequence whose token left the
     // loops; its row stores nothing (slot map entry -1), keeps the previous loop's
     // reconstruction and puts that into the ring.  nullptr: every row stores.
@@ -78,6 +83,9 @@ struct KVWrite {
 // cos and sin (float64 evaluation, rounded to float32) of position *dpos times each
 // inverse frequency into cs [hd/2][2].
 hipError_t rope_angles(const int32_t* dpos, const double* inv_freq, int hd, float* cs, hipStream_t st);
+// cos and sin of the rotation angles of positions 0..T-1: tab [T][hd/2][2] (float32 of
+// the float64 values).
+hipError_t rope_table(const double* inv_freq, int T, int hd, float* tab, hipStream_t st);
 // q_half: q_out receives float16 bits instead of bfloat16 (decode, for the float16 MFMA
 // attention kernels, which then take q with one rounding).
 hipError_t rope_kv_write(const float* qkv, int rows, int rows_per_seq, const int32_t* pos,
