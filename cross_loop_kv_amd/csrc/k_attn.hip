@@ -532,16 +532,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_fa_kernel(const 
 // tile's global loads issued before the current tile's products; every staged tile serves
 // 32 NW keys.  Per score: one FMA, one v_exp_f32 and one add; the causal mask is applied only
 // on tiles that reach the diagonal.
-template <int HD, bool I8, int NW>
+template <int HD, bool I8, int NW, int QS>
 __global__ __launch_bounds__(64 * NW) void column_mass_kernel(const u16* __restrict__ Q, KVLayer kv,
                                                               const float* __restrict__ LSE, int T, int H,
                                                               float* __restrict__ mass, float sl2) {
     constexpr int LDQ = HD + 8;
     constexpr int CPR = HD / 8;
-    constexpr int NQC = 32 * CPR;  // 16-byte chunks of one query tile
+    constexpr int QR = 32 * QS;    // query rows per staged tile (QS MFMA tiles of 32)
+    constexpr int NQC = QR * CPR;  // 16-byte chunks of one query tile
     constexpr int NT = 64 * NW;
     constexpr int PER = (NQC + NT - 1) / NT;
-    __shared__ __attribute__((aligned(16))) u16 Qs[2][32 * LDQ];
+    __shared__ __attribute__((aligned(16))) u16 Qs[2][QR * LDQ];
     // wave index through readfirstlane: the diagonal tests are scalar branches
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = lane >> 5, l32 = lane & 31;
@@ -567,17 +568,17 @@ __global__ __launch_bounds__(64 * NW) void column_mass_kernel(const u16* __restr
     // workgroup's first key to the last one.  Query chunk p of this thread is row
     // tid/16 + (NT/16) p of the tile at elements (tid % 16) 8: a fixed offset from the
     // tile's first row; a full tile loads without bounds checks.
-    const int qt0 = kblk / 32, nqt = (T + 31) / 32, nit = G * (nqt - qt0);
+    const int qt0 = kblk / QR, nqt = (T + QR - 1) / QR, nit = G * (nqt - qt0);
     const int qr = tid / CPR;
     const long long qoff = (long long)qr * ldq + (tid % CPR) * 8;
     uint4 regs[PER];
     auto load_tile = [&](int hh, int qt) {
-        const u16* qb = Q + ((long long)b * T + qt * 32) * ldq + (g * G + hh) * HD;
-        const bool full = qt * 32 + 32 <= T;
+        const u16* qb = Q + ((long long)b * T + qt * QR) * ldq + (g * G + hh) * HD;
+        const bool full = qt * QR + QR <= T;
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             regs[p] = make_uint4(0, 0, 0, 0);
-            if (tid + p * NT < NQC && (full || qt * 32 + qr + p * (NT / CPR) < T))
+            if (tid + p * NT < NQC && (full || qt * QR + qr + p * (NT / CPR) < T))
                 regs[p] = *(const uint4*)(qb + qoff + (long long)p * (NT / CPR) * ldq);
         }
     };
@@ -601,16 +602,18 @@ __global__ __launch_bounds__(64 * NW) void column_mass_kernel(const u16* __restr
         __syncthreads();
         if (it + 1 < nit) load_tile(hn, qn);
         const int h = g * G + hh;
-        const int q = qt * 32 + l32;
-        if (qt * 32 + 31 >= j0) {
+#pragma unroll
+        for (int sq = 0; sq < QS; ++sq) {
+            const int q0 = qt * QR + sq * 32, q = q0 + l32;
+            if (q0 + 31 < j0) continue;
             const float lse2 = (q < T) ? LSE[((long long)b * H + h) * T + q] : 0.f;
             f32x16 sv;
 #pragma unroll
             for (int i = 0; i < 16; ++i) sv[i] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < HD / 16; ++ks)
-                sv = mfma32<I8>(kf[ks], *(const uint4*)&Qs[cur][l32 * LDQ + ks * 16 + kg * 8], sv);
-            if (qt * 32 >= j0 + 31) {  // every key of this wave precedes every query of the tile
+                sv = mfma32<I8>(kf[ks], *(const uint4*)&Qs[cur][(sq * 32 + l32) * LDQ + ks * 16 + kg * 8], sv);
+            if (q0 >= j0 + 31) {  // every key of this wave precedes every query of the tile
                 if (q < T) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) cs[i] += __builtin_amdgcn_exp2f(fmaf(sv[i], sl2, -lse2));
@@ -1755,16 +1758,16 @@ hipError_t mass_hd(const u16* q, const KVLayer& kv, const float* lse, int B, int
     if (T >= 4096) {  // long prompts: 256 keys per workgroup
         dim3 grid((T + 255) / 256, kv.Hkv, B);
         if (i8)
-            hipLaunchKernelGGL((column_mass_kernel<HD, true, 8>), grid, dim3(512), 0, st, q, kv, lse, T, H, mass, sl2);
+            hipLaunchKernelGGL((column_mass_kernel<HD, true, 8, 4>), grid, dim3(512), 0, st, q, kv, lse, T, H, mass, sl2);
         else
-            hipLaunchKernelGGL((column_mass_kernel<HD, false, 8>), grid, dim3(512), 0, st, q, kv, lse, T, H, mass, sl2);
+            hipLaunchKernelGGL((column_mass_kernel<HD, false, 8, 4>), grid, dim3(512), 0, st, q, kv, lse, T, H, mass, sl2);
         return hipGetLastError();
     }
     dim3 grid((T + 127) / 128, kv.Hkv, B);
     if (i8)
-        hipLaunchKernelGGL((column_mass_kernel<HD, true, 4>), grid, dim3(256), 0, st, q, kv, lse, T, H, mass, sl2);
+        hipLaunchKernelGGL((column_mass_kernel<HD, true, 4, 1>), grid, dim3(256), 0, st, q, kv, lse, T, H, mass, sl2);
     else
-        hipLaunchKernelGGL((column_mass_kernel<HD, false, 4>), grid, dim3(256), 0, st, q, kv, lse, T, H, mass, sl2);
+        hipLaunchKernelGGL((column_mass_kernel<HD, false, 4, 1>), grid, dim3(256), 0, st, q, kv, lse, T, H, mass, sl2);
     return hipGetLastError();
 }
 
