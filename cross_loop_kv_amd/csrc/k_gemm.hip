@@ -475,14 +475,18 @@ void launch_skinny(const u16* A, const float* X, const u16* gain, float eps, con
 // staging): a tile row is 64 bf16 = one 128-byte line, one load instruction moves 8
 // whole rows, and the k offset rides in the scalar offset, so a load costs one M0 move.
 // Two LDS stages of 64 KB: the next slab streams in while the current one is consumed.
-// Within a stage, 16-byte chunk c of row r sits at slot c ^ (r % 8), so the rows read by
-// eight consecutive lanes land in distinct banks.  The k loop is unrolled over the two
-// stages (stage indices are compile-time, which keeps the compiler's LDS-DMA tracking
-// exact), the LDS reads of the next k-slice are interleaved with the MFMAs of the
-// current one, and there is one barrier per slab.  Tiles go to workgroups XCD by XCD,
-// grouped 8 M-tiles tall.  Rows past M load as zeros (buffer range check).  SwiGLU: the
-// 256 W rows of a tile are [gate 0..63 | up 0..63 | gate 64..127 | up 64..127] of 128
-// output columns, so each wave holds gate and up of its 64 output columns.
+// Within a stage, 16-byte chunk c of row r sits at slot c ^ f(r), f(r) = (r % 8) ^ (r / 8 % 2):
+// the LDS serves a 16-byte read 16 lanes at a time over 64 banks, and the 16 rows read by
+// 16 consecutive lanes cover every (row parity, slot) pair once, so they land in distinct
+// banks.  The k loop is unrolled over the two stages (stage indices are compile-time,
+// which keeps the compiler's LDS-DMA tracking exact), the LDS reads of the next k-slice
+// are interleaved with the MFMAs of the current one, and there is one barrier per slab.
+// The workgroup is persistent over tiles, XCD by XCD, grouped 8 M-tiles tall; the first
+// two slabs of its next tile go out as soon as each stage is free, before the current
+// tile's epilogue, so the epilogue's stores overlap the next tile's first loads.  Rows
+// past M load as zeros and are not stored (buffer range checks).  SwiGLU: the 256 W rows
+// of a tile are [gate 0..63 | up 0..63 | gate 64..127 | up 64..127] of 128 output
+// columns, so each wave holds gate and up of its 64 output columns.
 // Requires K % 128 == 0 and N % 256 == 0 (SwiGLU: N % 128 == 0).
 constexpr int GB_M = 256, GB_N = 256, GB_K = 64, GB_STAGE = (GB_M + GB_N) * GB_K;
 
@@ -513,6 +517,9 @@ __device__ __forceinline__ void bare_barrier() {
 template <int U>
 __device__ __forceinline__ u16* gb_stage() { return U == 0 ? gb_s0 : gb_s1; }
 
+// LDS slot permutation of the 16-byte chunks of stage row r.
+__device__ __forceinline__ int gb_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 // Buffer resources of the A and W rows of one tile and this lane's byte offsets.
 struct GbSrc {
     __amdgpu_buffer_rsrc_t ra, rb;
@@ -535,13 +542,13 @@ __device__ __forceinline__ void gb_read(const u16* st, bf16x8 (&fa)[4], bf16x8 (
                                         int c) {
     auto ra = [&](int i) {
         const int r = wm * 128 + 32 * i + l32;
-        fa[i] = as_bf16x8(*(const uint4*)(st + r * GB_K + ((c ^ (r & 7)) * 8)));
+        fa[i] = as_bf16x8(*(const uint4*)(st + r * GB_K + ((c ^ gb_swz(r)) * 8)));
     };
     ra(0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = wn * 128 + 32 * j + l32;
-        fb[j] = as_bf16x8(*(const uint4*)(st + GB_M * GB_K + r * GB_K + ((c ^ (r & 7)) * 8)));
+        fb[j] = as_bf16x8(*(const uint4*)(st + GB_M * GB_K + r * GB_K + ((c ^ gb_swz(r)) * 8)));
     }
 #pragma unroll
     for (int i = 1; i < 4; ++i) ra(i);
@@ -566,12 +573,13 @@ __device__ __forceinline__ void gb_sched_reads() {
 }
 
 // One slab in stage U.  On entry x holds k-slice 0 of the slab.  NEXT: another slab
-// follows (wait for it, barrier, read its k-slice 0 into x); DMA: refill stage U with
-// the slab after next once every wave is past the barrier.
+// follows in stage U ^ 1 (wait for it, barrier, read its k-slice 0 into x); DMA: once
+// every wave is past that barrier, refill stage U with slab k0 of the operands in dsrc
+// (the slab after next, or the first slab of the next tile).
 template <int U, bool NEXT, bool DMA>
 __device__ __forceinline__ void gb_slab(f32x16 (&acc)[4][4], bf16x8 (&xa)[4], bf16x8 (&xb)[4], bf16x8 (&ya)[4],
-                                        bf16x8 (&yb)[4], const GbSrc& src, int s, int ws, int wm, int wn, int l32,
-                                        int kg) {
+                                        bf16x8 (&yb)[4], const GbSrc& dsrc, int k0, int ws, int wm, int wn,
+                                        int l32, int kg) {
     gb_read(gb_stage<U>(), ya, yb, wm, wn, l32, 2 + kg);
     gb_mma(acc, xa, xb);
     gb_sched_reads();
@@ -582,9 +590,9 @@ __device__ __forceinline__ void gb_slab(f32x16 (&acc)[4][4], bf16x8 (&xa)[4], bf
     gb_mma(acc, xa, xb);
     gb_sched_reads();
     if (NEXT) {
-        wait_vmcnt<0>();  // this wave's part of slab s + 1 is in LDS
+        wait_vmcnt<0>();  // this wave's part of the next slab is in LDS
         bare_barrier();   // ... and every wave's; every wave is done reading stage U
-        if (DMA) gb_issue(gb_stage<U>(), src, (s + 2) * GB_K, ws);
+        if (DMA) gb_issue(gb_stage<U>(), dsrc, k0, ws);
         gb_read(gb_stage<U ^ 1>(), xa, xb, wm, wn, l32, kg);
     }
     gb_mma(acc, ya, yb);
@@ -604,25 +612,135 @@ __device__ __forceinline__ void gb_slab(f32x16 (&acc)[4][4], bf16x8 (&xa)[4], bf
     }
 }
 
-// One 256 x 256 output tile (tm, tn).
+// Tile t of the persistent order: groups of 8 M-tiles, N-tiles inside a group.
+struct GbTile {
+    int tm, tn;
+};
+__device__ __forceinline__ GbTile gb_tile_at(int t, int tiles_m, int tiles_n) {
+    constexpr int GROUP = 8;
+    const int group_size = GROUP * tiles_n;
+    const int gid = t / group_size, first_m = gid * GROUP;
+    const int gm = min(tiles_m - first_m, GROUP);
+    return {first_m + (t % group_size) % gm, (t % group_size) / gm};
+}
+
+// Buffer resource over `rows` rows of `pitch` bytes from base: loads past the end return
+// zeros and stores past it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gb_rows_rsrc(const void* base, int rows, int pitch) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, rows * pitch, 0x00020000);
+}
+
+// Operand resources of tile (tm, tn); the lane offsets in va / vb do not depend on the tile.
+template <bool DUAL>
+__device__ __forceinline__ void gb_src_rsrc(GbSrc& d, const u16* A, const u16* W, int M, int N, int K, int tm,
+                                            int tn) {
+    const int row0 = tm * GB_M;
+    d.ra = gb_rows_rsrc(A + (long long)row0 * K, min(M - row0, GB_M), K * 2);
+    const long long wrow0 = DUAL ? (long long)tn * 128 : (long long)tn * GB_N;
+    const int wspan = DUAL ? N + 128 : GB_N;  // W rows the tile reaches from wrow0
+    d.rb = gb_rows_rsrc(W + wrow0 * K, wspan, K * 2);
+}
+
+// x * sigmoid(x) from the hardware base-2 exponential and reciprocal (about 1 ulp each;
+// the product is rounded to bf16).
+__device__ __forceinline__ float silu_fast(float g) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
+
+// Epilogue of tile (tm, tn): acc[i][j][e] is C[row0 + wm*128 + 32 i + 8 (e/4) + 4 kg + e%4][col(j) + l32].
+// Every access goes through a buffer resource over the tile's valid rows.
 template <int EPI>
-__device__ __forceinline__ void gb_tile(const u16* __restrict__ A, const u16* __restrict__ W, int M, int N, int K,
-                                        float* __restrict__ C, u16* __restrict__ Obf, int tm, int tn) {
+__device__ __forceinline__ void gb_epilogue(const f32x16 (&acc)[4][4], float* __restrict__ C, u16* __restrict__ Obf,
+                                            int M, int N, int tm, int tn, int wm, int wn, int l32, int kg) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    const int row0 = tm * GB_M, rows = min(M - row0, GB_M);
+    // byte offset of row 32 i + 8 (e/4) + e%4 of this lane's (wm, kg) rows
+    auto roff = [&](int i, int e, int esz) { return (32 * i + 8 * (e >> 2) + (e & 3)) * N * esz; };
+    if (DUAL) {
+        const __amdgpu_buffer_rsrc_t ro = gb_rows_rsrc(Obf + (long long)row0 * N, rows, N * 2);
+        const int base = ((wm * 128 + 4 * kg) * N + tn * 128 + wn * 64 + l32) * 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int o = base + roff(i, e, 2);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b16(f2bf(silu_fast(acc[i][j][e]) * acc[i][j + 2][e]), ro,
+                                                          o + 64 * j, 0, 0);
+            }
+        return;
+    }
+    const __amdgpu_buffer_rsrc_t rc = gb_rows_rsrc(C + (long long)row0 * N, rows, N * 4);
+    const int base = ((wm * 128 + 4 * kg) * N + tn * GB_N + wn * 128 + l32) * 4;
+    if (EPI == EPI_ADD) {
+        // residual add, software-pipelined over the four 32-row groups: the 64 loads of
+        // group i + 1 are issued before the stores of group i
+        float cv[2][16][4];
+        auto load_group = [&](int i, float (&dst)[16][4]) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    dst[e][j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                                              rc, base + roff(i, e, 4) + 128 * j, 0, 0));
+        };
+        load_group(0, cv[0]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i + 1 < 4) load_group(i + 1, cv[(i + 1) & 1]);
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cv[i & 1][e][j] + acc[i][j][e]),
+                                                          rc, base + roff(i, e, 4) + 128 * j, 0, 0);
+        }
+    } else if (EPI == EPI_STORE) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][e]), rc,
+                                                          base + roff(i, e, 4) + 128 * j, 0, 0);
+    } else {  // GELU to bf16
+        const __amdgpu_buffer_rsrc_t ro = gb_rows_rsrc(Obf + (long long)row0 * N, rows, N * 2);
+        const int obase = base / 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b16(f2bf(gelu_f(acc[i][j][e])), ro,
+                                                          obase + roff(i, e, 2) + 64 * j, 0, 0);
+    }
+}
+
+// Persistent over tiles: workgroup b stays on XCD b % 8 and takes that XCD's share of
+// the tiles (a contiguous range of the tile order) in turn, so a CU goes from one tile's
+// epilogue straight to the next tile's loads, and CUs drift out of step instead of all
+// storing at once.
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_big_kernel(const u16* __restrict__ A, const u16* __restrict__ W,
+                                                          int M, int N, int K, float* __restrict__ C,
+                                                          u16* __restrict__ Obf, int tiles_m, int tiles_n) {
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    const int ntiles = tiles_m * tiles_n;
+    const int per_xcd = (ntiles + 7) / 8;
+    const int xcd = blockIdx.x % 8, slots = gridDim.x / 8;
+    int local = blockIdx.x / 8;
+    if (local >= per_xcd || xcd * per_xcd + local >= ntiles) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int ws = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = ws >> 1, wn = ws & 1, l32 = lane & 31, kg = lane >> 5;
-    const int row0 = tm * GB_M;
     GbSrc src;
-    src.ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long long)row0 * K), (short)0,
-                                               min(M - row0, GB_M) * K * 2, 0x00020000);
-    const long long wrow0 = DUAL ? (long long)tn * 128 : (long long)tn * GB_N;
-    const int wspan = DUAL ? N + 128 : GB_N;  // W rows the tile reaches from wrow0
-    src.rb = __builtin_amdgcn_make_buffer_rsrc((void*)(W + wrow0 * K), (short)0, wspan * K * 2, 0x00020000);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const int r = 8 * (ws + 4 * q) + lane / 8;  // tile row of this lane's 16 bytes
-        const int c = (lane % 8) ^ (r & 7);         // the chunk that lands in slot lane % 8
+        const int c = (lane % 8) ^ gb_swz(r);       // the chunk that lands in slot lane % 8
         src.va[q] = (uint32_t)(r * K * 2 + c * 16);
         int wr = r;
         if (DUAL) {
@@ -631,102 +749,47 @@ __device__ __forceinline__ void gb_tile(const u16* __restrict__ A, const u16* __
         }
         src.vb[q] = (uint32_t)(wr * K * 2 + c * 16);
     }
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    const int ns = K / GB_K;  // even, >= 2
+    GbTile tile = gb_tile_at(xcd * per_xcd + local, tiles_m, tiles_n);
+    gb_src_rsrc<DUAL>(src, A, W, M, N, K, tile.tm, tile.tn);
     gb_issue(gb_s0, src, 0, ws);
     gb_issue(gb_s1, src, GB_K, ws);
-    wait_vmcnt<16>();
-    bare_barrier();
-    bf16x8 xa[4], xb[4], ya[4], yb[4];
-    gb_read(gb_s0, xa, xb, wm, wn, l32, kg);
-    int s = 0;
-    for (; s < ns - 2; s += 2) {
-        gb_slab<0, true, true>(acc, xa, xb, ya, yb, src, s, ws, wm, wn, l32, kg);
-        gb_slab<1, true, true>(acc, xa, xb, ya, yb, src, s + 1, ws, wm, wn, l32, kg);
-    }
-    gb_slab<0, true, false>(acc, xa, xb, ya, yb, src, s, ws, wm, wn, l32, kg);
-    gb_slab<1, false, false>(acc, xa, xb, ya, yb, src, s + 1, ws, wm, wn, l32, kg);
-    // epilogue: acc[i][j][e] = C[row0 + wm*128 + 32 i + 8 (e/4) + 4 kg + e%4][col(j) + l32]
-    if (EPI == EPI_ADD) {
-        // residual add, software-pipelined over the four 32-row groups: the 64 loads of
-        // group i + 1 are issued before the stores of group i, so only the first group's
-        // loads cost a full memory round trip
-        float cv[2][16][4];
-        auto load_group = [&](int i, float (&dst)[16][4]) {
+    const int ns = K / GB_K;  // even, >= 2
+    for (bool first = true;; first = false) {
+        f32x16 acc[4][4];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int r = row0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * kg + (e & 3);
-                const float* crow = C + (long long)min(r, M - 1) * N + tn * GB_N + wn * 128 + l32;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) dst[e][j] = crow[32 * j];
-            }
-        };
-        load_group(0, cv[0]);
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (i + 1 < 4) load_group(i + 1, cv[(i + 1) & 1]);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int r = row0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * kg + (e & 3);
-                if (r >= M) continue;
-                float* crow = C + (long long)r * N + tn * GB_N + wn * 128 + l32;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) crow[32 * j] = cv[i & 1][e][j] + acc[i][j][e];
-            }
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+        if (first) wait_vmcnt<16>();  // slab 0 is in
+        else wait_vmcnt<0>();         // slabs 0 and 1 (and the last epilogue's stores)
+        bare_barrier();
+        bf16x8 xa[4], xb[4], ya[4], yb[4];
+        gb_read(gb_s0, xa, xb, wm, wn, l32, kg);
+        int s = 0;
+        for (; s < ns - 2; s += 2) {
+            gb_slab<0, true, true>(acc, xa, xb, ya, yb, src, (s + 2) * GB_K, ws, wm, wn, l32, kg);
+            gb_slab<1, true, true>(acc, xa, xb, ya, yb, src, (s + 3) * GB_K, ws, wm, wn, l32, kg);
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int r = row0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * kg + (e & 3);
-                if (r >= M) continue;
-                if (DUAL) {
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int col = tn * 128 + wn * 64 + 32 * j + l32;
-                        Obf[(long long)r * N + col] = f2bf(silu_f(acc[i][j][e]) * acc[i][j + 2][e]);
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int col = tn * GB_N + wn * 128 + 32 * j + l32;
-                        const long long o = (long long)r * N + col;
-                        if (EPI == EPI_STORE) C[o] = acc[i][j][e];
-                        else Obf[o] = f2bf(gelu_f(acc[i][j][e]));
-                    }
-                }
-            }
-        }
-    }
-}
-
-// Persistent over tiles: workgroup b stays on XCD b % 8 and takes that XCD's share of
-// the tiles (a contiguous range of the tile order) in turn, so a CU goes from one tile's
-// epilogue straight to the next tile's loads, and CUs drift out of step instead of all
-// storing at once.  Tile order within the range: groups of 8 M-tiles, N-tiles inside.
-template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_big_kernel(const u16* __restrict__ A, const u16* __restrict__ W,
-                                                          int M, int N, int K, float* __restrict__ C,
-                                                          u16* __restrict__ Obf, int tiles_m, int tiles_n) {
-    const int ntiles = tiles_m * tiles_n;
-    const int per_xcd = (ntiles + 7) / 8;
-    const int xcd = blockIdx.x % 8, slots = gridDim.x / 8;
-    constexpr int GROUP = 8;
-    const int group_size = GROUP * tiles_n;
-    for (int local = blockIdx.x / 8; local < per_xcd; local += slots) {
-        const int t = xcd * per_xcd + local;
-        if (t >= ntiles) break;
-        if (local != (int)blockIdx.x / 8) bare_barrier();  // every wave is done with the LDS stages
-        const int gid = t / group_size, first_m = gid * GROUP;
-        const int gm = min(tiles_m - first_m, GROUP);
-        gb_tile<EPI>(A, W, M, N, K, C, Obf, first_m + (t % group_size) % gm, (t % group_size) / gm);
+        // the next tile of this workgroup: its slab 0 goes into stage 0 as soon as every
+        // wave is done with it, its slab 1 into stage 1 after the last slab.  Without a
+        // next tile the loads go through empty resources: no memory access, and the
+        // zeros they leave in the stages are never read.
+        const int nlocal = local + slots;
+        const bool more = nlocal < per_xcd && xcd * per_xcd + nlocal < ntiles;
+        GbSrc nsrc = src;
+        const GbTile ntile = gb_tile_at(more ? xcd * per_xcd + nlocal : 0, tiles_m, tiles_n);
+        gb_src_rsrc<DUAL>(nsrc, A, W, more ? M : 0, N, more ? K : 0, ntile.tm, ntile.tn);
+        gb_slab<0, true, true>(acc, xa, xb, ya, yb, nsrc, 0, ws, wm, wn, l32, kg);
+        gb_slab<1, false, false>(acc, xa, xb, ya, yb, nsrc, 0, ws, wm, wn, l32, kg);
+        bare_barrier();  // every wave is done reading stage 1
+        gb_issue(gb_s1, nsrc, GB_K, ws);
+        gb_epilogue<EPI>(acc, C, Obf, M, N, tile.tm, tile.tn, wm, wn, l32, kg);
+        if (!more) break;
+        local = nlocal;
+        tile = ntile;
+        src = nsrc;
     }
 }
 
@@ -737,6 +800,7 @@ bool launch_big(const u16* A, const u16* W, int M, int N, int K, float* c, u16* 
     // buffer offsets and ranges are 32-bit: the rows one tile reaches must stay below 2 GiB
     const long long wspan = (EPI == EPI_SWIGLU) ? (long long)N + 128 : GB_N;
     if (wspan * K * 2 >= (1LL << 31) || (long long)GB_M * K * 2 >= (1LL << 31)) return false;
+    if ((long long)GB_M * N * 4 >= (1LL << 31)) return false;  // the output rows of one tile
     const int tiles_m = (M + GB_M - 1) / GB_M, tiles_n = N / nspan;
     // grid: a multiple of 8 (workgroups per XCD), at most one workgroup per CU
     const int per_xcd = (tiles_m * tiles_n + 7) / 8;
