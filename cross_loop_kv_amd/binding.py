@@ -99,6 +99,7 @@ _SIGS = {
     "lk_kv_store_bytes_used": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
     "lk_kv_store_cache_bytes": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t)]),
     "lk_kv_store_length": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32)]),
+    "lk_kv_store_range_check": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.c_void_p]),
     "lk_kv_store_set_loops": (C.c_int, [C.c_void_p, C.c_int32]),
     "lk_kv_store_export": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.POINTER(C.c_size_t), C.c_void_p]),
     "lk_kv_store_import": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
@@ -207,6 +208,12 @@ def lk_kv_store_length(s: int) -> int:
     t = C.c_int32()
     _check(lib().lk_kv_store_length(s, C.byref(t)))
     return t.value
+
+
+def lk_kv_store_range_check(s: int, clear: bool = False, stream=None) -> bool:
+    flag = C.c_int32()
+    _check(lib().lk_kv_store_range_check(s, 1 if clear else 0, C.byref(flag), _stream(stream)))
+    return bool(flag.value)
 
 
 def lk_kv_store_set_loops(s: int, n: int) -> None:
@@ -373,6 +380,10 @@ class Store:
 
     def length(self) -> int:
         return lk_kv_store_length(self.s)
+
+    def out_of_f16_range(self, clear: bool = False) -> bool:
+        """Whether the writer met a q/K/V element outside the float16 range."""
+        return lk_kv_store_range_check(self.s, clear)
 
     def export(self) -> np.ndarray:
         """Snapshot of the store's state (host uint8 array)."""

@@ -374,6 +374,7 @@ __global__ __launch_bounds__(128) void rope_kv_write_kernel(const float* qkv, in
         const float x1 = src[hh * hd + i], x2 = src[hh * hd + i + half];
         u16* dq = q_out + (long long)r * H * hd + hh * hd;
         const float r1 = rope_lo(x1, x2, c, sn), r2 = rope_hi(x1, x2, c, sn);
+        if (w.range_flag && !(fabsf(r1) <= 65504.f && fabsf(r2) <= 65504.f)) *w.range_flag = 1u;
         dq[i] = q_half ? f2h_bits(r1) : f2bf(r1);
         dq[i + half] = q_half ? f2h_bits(r2) : f2bf(r2);
         return;

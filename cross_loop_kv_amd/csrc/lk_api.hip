@@ -354,6 +354,8 @@ int32_t* slot_map(const lk_kv_store* s, int k) {
     return (int32_t*)(s->buf + s->lay.slot) + (long long)(k - 2) * s->B * s->Tpad;
 }
 int32_t* dev_pos(const lk_kv_store* s) { return (int32_t*)(s->buf + s->lay.state); }
+// The store's float16-range flag (KVWrite::range_flag), beside the decode position.
+uint32_t* range_flag(const lk_kv_store* s) { return (uint32_t*)(s->buf + s->lay.state + 4); }
 
 // Stable-column cache (ring == false) or window ring (ring == true) of loop k >= ck0,
 // shared layer r, as float16 plain rows.
@@ -974,11 +976,12 @@ int lk_kv_store_alloc(lk_handle* h, int32_t batch, int32_t prompt_tokens, int32_
     s->f_tok = s->f_cols = nullptr;
     s->keep_codes = 0;
     if (h->lazy()) {
-        hipError_t e = lk::fill_i32(slot_map(s, 2), -1, (long long)(h->c.n_loops - 1) * batch * s->Tpad,
-                                    (hipStream_t)stream);
+        hipError_t e = lk::fill_i32((int32_t*)range_flag(s), 0, 1, (hipStream_t)stream);
+        if (e == hipSuccess)
+            e = lk::fill_i32(slot_map(s, 2), -1, (long long)(h->c.n_loops - 1) * batch * s->Tpad, (hipStream_t)stream);
         if (e != hipSuccess) {
             delete s;
-            return fail(LK_ERR_HIP, std::string("slot map clear: ") + hipGetErrorString(e));
+            return fail(LK_ERR_HIP, std::string("store clear: ") + hipGetErrorString(e));
         }
     }
     *out = s;
@@ -1017,6 +1020,19 @@ int lk_kv_store_set_loops(lk_kv_store* s, int32_t n_loops) {
 int lk_kv_store_length(const lk_kv_store* s, int32_t* tokens) {
     if (!s || !tokens) return fail(LK_ERR_INVALID_ARG, "null argument");
     *tokens = s->t;
+    return LK_OK;
+}
+
+int lk_kv_store_range_check(lk_kv_store* s, int32_t clear, int32_t* out_of_range, void* stream) {
+    if (!s || !out_of_range) return fail(LK_ERR_INVALID_ARG, "null argument");
+    *out_of_range = 0;
+    if (!s->h->lazy()) return LK_OK;  // bf16 rows only: the flag is never raised
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t flag = 0;
+    LK_HIP(hipMemcpyAsync(&flag, range_flag(s), sizeof(flag), hipMemcpyDeviceToHost, st));
+    LK_HIP(hipStreamSynchronize(st));
+    *out_of_range = flag != 0;
+    if (clear) LK_HIP(lk::fill_i32((int32_t*)range_flag(s), 0, 1, st));
     return LK_OK;
 }
 
@@ -1187,6 +1203,7 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
             kw.kind = 1;
             kw.layer = ap.read;
             kw.keep_codes = s->keep_codes;
+            kw.range_flag = range_flag(s);
             LK_TRY(run_layer(h, P + r, io, kw, ap, w, st));
             int32_t* cols = col_sets(s, r);
             const int nc = s->lay.n_cols;
@@ -1241,6 +1258,7 @@ int lk_looped_prefill(lk_handle* h, lk_kv_store* s, const int32_t* d_ids, int32_
                 kw.loop = k;
                 kw.slot_base = 0;
                 kw.keep_codes = s->keep_codes;
+                kw.range_flag = range_flag(s);
                 LK_TRY(run_layer(h, P + r, cio, kw, ap, w, st));
             }
             if (k < K) {
@@ -1355,6 +1373,7 @@ int enqueue_decode(lk_handle* h, lk_kv_store* s, const WS& w, hipStream_t st) {
             lk::KVWrite kw{};
             kw.layer = ap.read;
             kw.keep_codes = s->keep_codes;
+            kw.range_flag = range_flag(s);
             if (skip) kw.active = w.sk_act;
             kw.tok_recon = w.tokrec + (long long)r * B * 2 * c.n_kv_heads * c.head_dim;
             if (h->z.diff_attn && K >= 2) {
@@ -1850,6 +1869,7 @@ int lk_dbg_kv_write(lk_kv_store* s, int32_t layer, int32_t loop, const float* d_
     kw.loop = loop;
     kw.kind = loop == 1 ? 1 : 2;
     kw.keep_codes = 0;
+    kw.range_flag = range_flag(s);
     if (d_pos) {
         if (rows_per_seq < 1 || rows_per_seq > s->Tpad || (loop >= 2 && rows_per_seq > s->lay.slots))
             return fail(LK_ERR_INVALID_ARG, "rows_per_seq out of range");

@@ -79,6 +79,11 @@ struct KVWrite {
     // loops; its row stores nothing (slot map entry -1), keeps the previous loop's
     // reconstruction and puts that into the ring.  nullptr: every row stores.
     const int32_t* active;
+    // set to 1 when an element this write handles (a rotated q, a rotated K or a V
+    // element) is not finite or exceeds the float16 range (|x| > 65504), where the
+    // float16 forms of the shared block (int8-base attention operands, decode caches,
+    // float16 q) would hold inf; nullptr: no check
+    uint32_t* range_flag;
 };
 // cos and sin (float64 evaluation, rounded to float32) of position *dpos times each
 // inverse frequency into cs [hd/2][2].
@@ -110,6 +115,7 @@ __device__ __forceinline__ void kv_write_elem(const float* __restrict__ src, int
     } else {
         x = src[(H + Hkv + g) * hd + e];
     }
+    if (w.range_flag && !(fabsf(x) <= 65504.f)) *w.range_flag = 1u;
     const KVLayer& L = w.layer;
     const long long slot = w.slot_base + (w.dpos ? *w.dpos : 0) + iseq;
     const long long row = kv_row(L, b, g, pos);

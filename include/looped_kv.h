@@ -177,6 +177,21 @@ int lk_kv_store_bytes_used(const lk_kv_store *s, size_t *shared, size_t *total);
 int lk_kv_store_cache_bytes(const lk_kv_store *s, size_t *bytes);
 /* Current tokens per sequence (0 before prefill). */
 int lk_kv_store_length(const lk_kv_store *s, int32_t *tokens);
+/* Float16 range check of the lazy store.  The pages fix no number format for the
+ * attention operands (FlashLoop abstract: KV stored as low-bit residuals); this
+ * library keeps the shared block's int8-base operands (code x scale), its loop-k
+ * decode caches and q in float16.  The writer raises a flag on the device when an
+ * element it handles -- a rotated q, a rotated K or a V element of a shared layer, as
+ * the projections produced it -- is not finite or has |x| > 65504: those forms would
+ * hold inf for it, and the outputs that depend on them are then not to be trusted
+ * (codes and scales in the store stay finite; scales saturate at 65504).
+ * *out_of_range receives 1 if the flag was raised since lk_kv_store_alloc or the
+ * last call with clear != 0, else 0; clear != 0 then lowers it.  The call orders
+ * itself after the work already on `stream` and waits for it (a device-to-host copy
+ * of 4 bytes).  Snapshots carry the flag.  Dense prelude/coda layers (bf16 rows)
+ * and the per_loop / last_loop modes never raise it.  LK_ERR_INVALID_ARG for a
+ * null argument; LK_ERR_HIP when the copy fails. */
+int lk_kv_store_range_check(lk_kv_store *s, int32_t clear, int32_t *out_of_range, void *stream);
 
 /* Workspace bytes for a prefill of batch x tokens (tokens = 1 for decode). */
 int lk_workspace_bytes(lk_handle *h, int32_t batch, int32_t tokens, size_t *bytes);

@@ -536,6 +536,7 @@ def test_full_depth_decode_at_full_context():
     store.import_(snapshot_with_states(store, s, lz, states))
     g = _gpu_decode(model, store, ids)
     assert np.isfinite(g).all()
+    assert not store.out_of_f16_range(), "K/V/q of the decode step inside the float16 range"
     seq = Bn - 1
     e = max_abs_rel(g[seq], outs[seq])
     log(f"  sequence {seq}: GPU vs fp32 oracle {e:.3e}")

@@ -16,7 +16,7 @@ Two call patterns are covered: the prefill pattern (many rows per sequence at gi
 positions, residuals in consecutive slots) and the decode pattern the throughput
 figure's decode step runs (one row per sequence at the store length, the previous
 loop's reconstruction carried in float32 from loop to loop, the float16 window-ring
-row written alongside)."""
+row written alongside).  A last test covers the store's float16-range flag."""
 import numpy as np
 import pytest
 import torch
@@ -251,3 +251,42 @@ def test_decode_pattern_writer_is_bit_exact():
                 assert np.all(rd.slot_map(k)[:, t] == n), f"loop {k} slot map"
     assert st.length() == T
     log("  decode writer: bit-exact over 2 layers x 4 loops")
+
+
+def test_writer_flags_elements_outside_float16_range():
+    """The store's float16-range flag (lk_kv_store_range_check): raised when a rotated q,
+    a rotated K or a V element that the writer handles is not finite or exceeds 65504 in
+    magnitude (the int8-base attention operands, the decode caches and q are float16,
+    where such an element is inf); not raised by in-range rows or by +-65504 itself;
+    lowered by a clearing read.  The element under test sits in the row at position 0,
+    whose rotation angle is 0, so the rotated value is the projection itself."""
+    s = _shape()
+    lz = I.Lazy(mode="lazy", rho=0.3, top_s=16, window=8, base_bits=8, res_bits=4)
+    Bn, T = 1, 32
+    rng = np.random.default_rng(11)
+    model = B.LoopedModel(s, lz, I.gen_weights(s, seed=1))
+    st = model.store(Bn, T, T + 4)
+    H, Hkv, hd = s.n_heads, s.n_kv_heads, s.head_dim
+    pos = torch.arange(T, dtype=torch.int32, device="cuda")
+    q_out = torch.zeros(Bn * T, H * hd, dtype=torch.int16, device="cuda")
+
+    def write(qkv):
+        d = torch.from_numpy(qkv).cuda()
+        B.lk_dbg_kv_write(st.s, 0, 1, d.data_ptr(), T, pos.data_ptr(), q_out.data_ptr(), 0)
+        torch.cuda.synchronize()
+        return st.out_of_f16_range(clear=True)
+
+    assert not st.out_of_f16_range(), "a new store"
+    base = _projections(rng, Bn * T, s)
+    assert not write(base), "in-range rows"
+    qcol, kcol, vcol = 17, H * hd + hd + 3, (H + Hkv) * hd + 5
+    cases = [("V at 65504", vcol, 65504.0, False), ("V at -65504", vcol, -65504.0, False),
+             ("K at 65504", kcol, 65504.0, False), ("V above", vcol, 65520.0, True),
+             ("K above", kcol, -7.0e4, True), ("q above", qcol, 1.0e5, True),
+             ("V NaN", vcol, np.nan, True), ("K inf", kcol, np.inf, True)]
+    for name, col, val, flagged in cases:
+        x = base.copy()
+        x[0, col] = val
+        log(f"  range flag: {name}")
+        assert write(x) == flagged, name
+    assert not st.out_of_f16_range(), "the clearing reads left the flag lowered"
