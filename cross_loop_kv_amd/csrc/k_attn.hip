@@ -310,9 +310,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_fa_kernel(const 
     // lane-masked regions that every tile would step through
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = lane >> 5, l32 = lane & 31;
-    const int h = blockIdx.y, b = blockIdx.z;
+    // workgroups of one sequence in order of causal work: every head's last query
+    // block, then every head's second last, ... (the dispatch runs x, then y)
+    const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+    const int h = lin % gridDim.y, b = blockIdx.z;
     const int G = H / kv.Hkv, g = h / G;
-    const int qblk = (gridDim.x - 1 - blockIdx.x) * (32 * NW);
+    const int qblk = (gridDim.x - 1 - lin / gridDim.y) * (32 * NW);
     const int q0 = qblk + w * 32;
     const int qi = q0 + l32;
     const long long ldq = (long long)H * HD;
@@ -546,9 +549,12 @@ __global__ __launch_bounds__(64 * NW) void column_mass_kernel(const u16* __restr
     // wave index through readfirstlane: the diagonal tests are scalar branches
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = lane >> 5, l32 = lane & 31;
-    const int g = blockIdx.y, b = blockIdx.z;
+    // workgroups of one sequence in order of causal work: every KV head's first key
+    // block (all queries see it), then every head's second, ... (the dispatch runs x, then y)
+    const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+    const int g = lin % gridDim.y, b = blockIdx.z;
     const int Hkv = kv.Hkv, G = H / Hkv;
-    const int kblk = blockIdx.x * 32 * NW;
+    const int kblk = (lin / gridDim.y) * 32 * NW;
     const int j0 = kblk + w * 32;
     const long long ldq = (long long)H * HD;
     uint4 kf[HD / 16];
