@@ -475,7 +475,9 @@ def main():
     store = model.store(Bsz, T, total_tokens)
     log(f"store: {store.need / 1e9:.2f} GB allocated for {total_tokens} tokens")
     ids = torch.from_numpy(I.gen_prompt_ids(s, Bsz, T)).cuda()
-    dec = torch.from_numpy(I.gen_decode_ids(s, Bsz, args.warmup + args.steps)).cuda()
+    # decode tokens for the timed run and for the baselines (8 warm-up + baseline steps)
+    n_dec = max(args.warmup + args.steps, 8 + args.baseline_steps)
+    dec = torch.from_numpy(I.gen_decode_ids(s, Bsz, n_dec)).cuda()
     torch.cuda.synchronize()
     # every projection GEMM, dense attention and column-mass launch of the prefill runs
     # between two HIP events

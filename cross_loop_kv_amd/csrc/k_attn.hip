@@ -840,6 +840,9 @@ __device__ __forceinline__ void decode_q(const RowsAttn& a, int b, int g, int c1
                     const float c = cs[2 * m], sn = cs[2 * m + 1];
                     r2[u] = lo ? rope_lo(x1[m], x2[m], c, sn) : rope_hi(x1[m], x2[m], c, sn);
                 }
+                // the rotated q outside the float16 range raises the store's range flag
+                if (a.kvw.range_flag && !(fabsf(r2[0]) <= 65504.f && fabsf(r2[1]) <= 65504.f))
+                    *a.kvw.range_flag = 1u;
                 // the float16 kernels take the rotated float32 q with one rounding
                 o[t] = HALF ? (pack_h2(r2[0], r2[1])) : pack_bf2(r2[0], r2[1]);
             }
