@@ -840,9 +840,6 @@ __device__ __forceinline__ void decode_q(const RowsAttn& a, int b, int g, int c1
                     const float c = cs[2 * m], sn = cs[2 * m + 1];
                     r2[u] = lo ? rope_lo(x1[m], x2[m], c, sn) : rope_hi(x1[m], x2[m], c, sn);
                 }
-                // the rotated q outside the float16 range raises the store's range flag
-                if (a.kvw.range_flag && !(fabsf(r2[0]) <= 65504.f && fabsf(r2[1]) <= 65504.f))
-                    *a.kvw.range_flag = 1u;
                 // the float16 kernels take the rotated float32 q with one rounding
                 o[t] = HALF ? (pack_h2(r2[0], r2[1])) : pack_bf2(r2[0], r2[1]);
             }
@@ -878,38 +875,73 @@ __global__ __launch_bounds__(256, RT == RT_I8 || RT == RT_F16_2SEG || RT == RT_F
     const int Hkv = kv.Hkv, b = bg / Hkv, g = bg % Hkv;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int c16 = lane & 15, kgrp = lane >> 4;
-    // keys [c_lo, c_end) of rows [c_begin, c_begin + chunk) take part
-    int c_begin, c_lo, c_end, ring0 = 0;
-    if (!SEG) {
-        const int ncols = a.lens ? a.lens[bg] : (a.dpos ? *a.dpos : a.pos) + 1;
-        c_begin = c_lo = split * a.chunk;
-        c_end = min(ncols, c_begin + a.chunk);
-    } else if (!seg2) {  // S rows: the ascending columns up to pos - window form a prefix
-        const int pos = a.dpos ? *a.dpos : a.pos;
-        __shared__ int s_cnt[4];
-        c_begin = c_lo = split * a.chunk;
-        const int i = c_begin + threadIdx.x;
-        const bool in = threadIdx.x < a.chunk && i < a.n_cols && a.cols[(long long)bg * a.n_cols + i] <= pos - a.window;
-        const unsigned long long bal = __ballot(in);
-        if (lane == 0) s_cnt[w] = __popcll(bal);
-        __syncthreads();
-        c_end = c_begin + s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
-    } else {  // window keys start at the 8-aligned position below the window
-        const int pos = a.dpos ? *a.dpos : a.pos;
-        const int wlo = max(0, pos - a.window + 1);
-        ring0 = wlo & ~7;
-        c_begin = (split - a.seg_split) * a.chunk;
-        c_lo = max(c_begin, wlo - ring0);
-        c_end = min(c_begin + a.chunk, pos - ring0 + 1);
-    }
-    // row of key `key` in kv (window ring: position ring0 + key at row % Tmax)
-    auto row_of = [&](int key) { return seg2 ? (ring0 + key) % kv.Tmax : key; };
     const float sl2 = kLog2e / sqrtf((float)HD);
-    if (a.fuse_kv) {
-        // the new token's K/V row goes to the store first when this workgroup reads it
+    // Two segments, new-key split on: this workgroup writes the new token's K/V row and
+    // forms that one key's partial from the values it wrote, with no load after the
+    // write: thread (kv, e) holds K or V element e as the ring stores it (float16), the
+    // K threads also the G float16 queries at e.  Score s_h = sum_e q_h[e] k[e] in
+    // float32, weight exp2(0) = 1, output the V row.
+    if (SEG && a.nk_split > 0 && split == a.nk_split) {
         const int pos = *a.dpos;
-        const int key = SEG ? pos - ring0 : pos;
-        if ((!SEG || seg2) && key >= c_begin && key < c_begin + a.chunk) {
+        const int kvh = threadIdx.x >> 7, e = threadIdx.x & 127;
+        float val = 0.f, qf[G];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) qf[hh] = 0.f;
+        if (e < HD) {
+            const int i = e % (HD / 2);
+            const float c = kvh == 0 ? a.rope_cs[2 * i] : 1.f;
+            const float sn = kvh == 0 ? a.rope_cs[2 * i + 1] : 0.f;
+            const float* src = a.qkv + (long long)b * (a.H + 2 * Hkv) * HD;
+            if (kvh == 0) {  // the queries of the group's heads, rotated and rounded as decode_q does
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) {
+                    const float* qh = src + (g * G + hh) * HD;
+                    const float r = e < HD / 2 ? rope_lo(qh[i], qh[i + HD / 2], c, sn) : rope_hi(qh[i], qh[i + HD / 2], c, sn);
+                    // a rotated q outside the float16 range raises the store's range flag
+                    // (this workgroup rotates every q element of its group, once)
+                    if (a.kvw.range_flag && !(fabsf(r) <= 65504.f)) *a.kvw.range_flag = 1u;
+                    qf[hh] = h2f(f2h_bits(r));
+                }
+            }
+            val = h2f(f2h_bits(kv_write_elem(src, a.H, Hkv, HD, b, g, kvh, e, pos, 0, c, sn, a.kvw,
+                                             kvh == 0 && g == 0 && e == 0)));
+        }
+        if (LIVE && *a.live == 0) return;  // no sequence left in the loops: the write only
+        __shared__ float sm_s[2][G];
+        if (kvh == 0) {
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+                const float t = wave_sum(qf[hh] * val);
+                if (lane == 0) sm_s[w][hh] = t;
+            }
+        }
+        __syncthreads();
+        float* P = a.part + ((long long)bg * a.n_splits + split) * G * (HD + 2);
+        if (kvh == 1 && e < HD) {
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) P[hh * (HD + 2) + e] = val;
+        }
+        if (threadIdx.x < G) {
+            P[threadIdx.x * (HD + 2) + HD] = (sm_s[0][threadIdx.x] + sm_s[1][threadIdx.x]) * sl2;
+            P[threadIdx.x * (HD + 2) + HD + 1] = 1.f;
+        }
+        return;
+    }
+    // S rows: the column of each thread's entry is loaded before the query, so that the
+    // two loads are in flight together
+    int s_col = 0x7fffffff;
+    if (SEG && !seg2) {
+        const int i = split * a.chunk + threadIdx.x;
+        if (threadIdx.x < a.chunk && i < a.n_cols) s_col = a.cols[(long long)bg * a.n_cols + i];
+    }
+    // the new token's K/V row goes to the store first when this workgroup reads it
+    // (without a new-key split)
+    if (a.fuse_kv && a.nk_split == 0 && (!SEG || seg2)) {
+        const int pos = *a.dpos;
+        const int ring0 = SEG ? max(0, pos - a.window + 1) & ~7 : 0;
+        const int key = pos - ring0;
+        const int cb = (SEG ? split - a.seg_split : split) * a.chunk;
+        if (key >= cb && key < cb + a.chunk) {
             const int kvh = threadIdx.x >> 7, e = threadIdx.x & 127;
             if (e < HD) {
                 const float c = kvh == 0 ? a.rope_cs[2 * (e % (HD / 2))] : 1.f;
@@ -924,6 +956,31 @@ __global__ __launch_bounds__(256, RT == RT_I8 || RT == RT_F16_2SEG || RT == RT_F
 
     uint4 qop[NQ];
     decode_q<HD, G, RT>(a, b, g, c16, kgrp, qop);
+    // keys [c_lo, c_end) of rows [c_begin, c_begin + chunk) take part
+    int c_begin, c_lo, c_end, ring0 = 0;
+    if (!SEG) {
+        const int ncols = a.lens ? a.lens[bg] : (a.dpos ? *a.dpos : a.pos) + 1;
+        c_begin = c_lo = split * a.chunk;
+        c_end = min(ncols, c_begin + a.chunk);
+    } else if (!seg2) {  // S rows: the ascending columns up to pos - window form a prefix
+        const int pos = a.dpos ? *a.dpos : a.pos;
+        __shared__ int s_cnt[4];
+        c_begin = c_lo = split * a.chunk;
+        const unsigned long long bal = __ballot(s_col <= pos - a.window);
+        if (lane == 0) s_cnt[w] = __popcll(bal);
+        __syncthreads();
+        c_end = c_begin + s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+    } else {  // window keys start at the 8-aligned position below the window
+        const int pos = a.dpos ? *a.dpos : a.pos;
+        const int wlo = max(0, pos - a.window + 1);
+        ring0 = wlo & ~7;
+        c_begin = (split - a.seg_split) * a.chunk;
+        c_lo = max(c_begin, wlo - ring0);
+        // with a new-key split, the new key (the last window key) is that split's
+        c_end = min(c_begin + a.chunk, pos - ring0 + (a.nk_split > 0 ? 0 : 1));
+    }
+    // row of key `key` in kv (window ring: position ring0 + key at row % Tmax)
+    auto row_of = [&](int key) { return seg2 ? (ring0 + key) % kv.Tmax : key; };
     const bool hvalid = c16 < G;
     f32x4 oacc[NE];
 #pragma unroll

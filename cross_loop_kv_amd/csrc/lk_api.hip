@@ -702,6 +702,8 @@ int run_layer(lk_handle* h, int li, const LayerIO& io, const lk::KVWrite& kvw, c
             d.chunk = kSegChunk;
             d.seg_split = ap.scache.Tmax / kSegChunk;
             d.n_splits = d.seg_split + ap.ring.Tmax / kSegChunk;
+            // the launch writes the new token's K/V in a split of its own per (b, g)
+            if (fuse_kv) d.nk_split = d.n_splits++;
             if ((long long)a.B * H * d.n_splits * (hd + 2) > w.part_floats)
                 return fail(LK_ERR_CAPACITY, "workspace too small for attention partials");
             if (ap.d32) {

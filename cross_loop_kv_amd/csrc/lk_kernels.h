@@ -103,7 +103,10 @@ hipError_t rope_kv_write(const float* qkv, int rows, int rows_per_seq, const int
 // iseq: its row within the sequence's rows of this call.  Threads e = 0..hd-1 of a
 // (token, kv, g) must be consecutive lanes of one wave from a 32-lane boundary: groups
 // of 32 quantize together.  `lead` (one thread per call) writes the slot map entry.
-__device__ __forceinline__ void kv_write_elem(const float* __restrict__ src, int H, int Hkv, int hd, int b, int g,
+// Returns the element's reconstruction at this write's loop (the value the store and
+// the window ring now hold before their 16-bit rounding; 0 for an int8 base row whose
+// codes are kept, outside decode).
+__device__ __forceinline__ float kv_write_elem(const float* __restrict__ src, int H, int Hkv, int hd, int b, int g,
                                               int kv, int e, int pos, int iseq, float c, float sn, const KVWrite& w,
                                               bool lead) {
     const int half = hd / 2;
@@ -133,6 +136,7 @@ __device__ __forceinline__ void kv_write_elem(const float* __restrict__ src, int
         ((u16*)L.base[kv])[idx] = xb;
         if (tr) *tr = bf2f(xb);
         if (w.kind == 1 && w.ring_on) ring_write(bf2f(xb));
+        return bf2f(xb);
     } else if (w.kind == 1) {  // int8 base: residual against a zero reconstruction
         float recon;
         if (!w.keep_codes) {
@@ -149,10 +153,12 @@ __device__ __forceinline__ void kv_write_elem(const float* __restrict__ src, int
         }
         if (tr) *tr = recon;
         if (w.ring_on) ring_write(recon);
+        return recon;
     } else if (w.active && !w.active[b]) {  // the token left the loops: carried row
         const float recon = tr ? *tr : kv_recon_elem(L, kv, b, g, pos, e, w.loop - 1);
         if (w.ring_on) ring_write(recon);
         if (w.slot_map_k && lead) w.slot_map_k[(long long)b * L.Tmax + pos] = -1;
+        return recon;
     } else {
         const long long rr = res_row(L, b, g, slot);
         float recon;  // the row's loop-k reconstruction
@@ -182,6 +188,7 @@ __device__ __forceinline__ void kv_write_elem(const float* __restrict__ src, int
         if (tr) *tr = recon;
         if (w.ring_on) ring_write(recon);
         if (w.slot_map_k && lead) w.slot_map_k[(long long)b * L.Tmax + pos] = (int32_t)slot;
+        return recon;
     }
 }
 
@@ -272,6 +279,11 @@ struct RowsAttn {
     const float* rope_cs;
     KVWrite kvw;
     int fuse_kv;
+    // New-key split of the two-segment decode (fuse_kv; nk_split = n_splits - 1, 0: off):
+    // split nk_split of every (b, g) writes the new token's K/V row and forms that one
+    // key's partial from the values it wrote (score in float32 from the float16 q and K,
+    // weight 1, output the float16 V); the window splits stop below the new key.
+    int nk_split;
     // Difference-corrected sparse attention: the normalized output o of query row
     // (b, i), heads h, meets a correction row (DIFF_NONE: out = o).
     //   DIFF_ADD32  out = o + d32[b * n_rows + i]
