@@ -76,6 +76,17 @@ def parse():
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
+# warm-up steps of each dense / bf16-base baseline decode
+BASELINE_WARMUP = 8
+
+
+def decode_tokens_needed(warmup, steps, baseline_steps, baselines=True):
+    """Decode steps the seeded token draw has to cover: the timed run's warm-up and
+    timed steps and, with the baselines, each baseline's warm-up and timed steps."""
+    n = warmup + steps
+    return max(n, BASELINE_WARMUP + baseline_steps) if baselines else n
+
+
 def kept_rows(rho, T):
     """Tokens recomputed per sequence at loops k >= 2: ceil(rho T) clamped to [1, T]."""
     return max(1, min(T, math.ceil(rho * T - 1e-9)))
@@ -475,8 +486,8 @@ def main():
     store = model.store(Bsz, T, total_tokens)
     log(f"store: {store.need / 1e9:.2f} GB allocated for {total_tokens} tokens")
     ids = torch.from_numpy(I.gen_prompt_ids(s, Bsz, T)).cuda()
-    # decode tokens for the timed run and for the baselines (8 warm-up + baseline steps)
-    n_dec = max(args.warmup + args.steps, 8 + args.baseline_steps)
+    # decode tokens for the timed run and for the baselines
+    n_dec = decode_tokens_needed(args.warmup, args.steps, args.baseline_steps, not args.no_baselines)
     dec = torch.from_numpy(I.gen_decode_ids(s, Bsz, n_dec)).cuda()
     torch.cuda.synchronize()
     # every projection GEMM, dense attention and column-mass launch of the prefill runs
@@ -612,7 +623,7 @@ def main():
         base = []
         for blz in (I.Lazy(mode="per_loop"), I.Lazy(mode="last_loop"),
                     I.Lazy(**{**lz.__dict__, "base_bits": 16})):
-            base.append(decode_baseline(model, wl, blz, ids, dec, 8, args.baseline_steps))
+            base.append(decode_baseline(model, wl, blz, ids, dec, BASELINE_WARMUP, args.baseline_steps))
         res["baselines"] = {b["mode"] + ("_bf16_base" if b.get("base_bits") == 16 else ""): b for b in base}
         res["baselines"]["lazy_speedup_vs_per_loop"] = round(value / base[0]["tokens_per_s"], 3)
         store = None

@@ -1687,18 +1687,15 @@ __global__ __launch_bounds__(64) void attn_rows_kernel(RowsAttn a) {
     }
 }
 
-// One block per (query row, KV head, query head of the group); thread e merges the
-// split partials of head dim e in split order.
-// One workgroup per (query row, KV head): the split weights exp2(m_s - M) of every
-// head go to LDS first, then each (head, e) output sums its splits with independent
-// loads.  Splits that saw no key carry m = -inf and weigh 0.
+// Split merge of the decode attention.  Splits that saw no key carry m = -inf and
+// weigh 0.
 constexpr int kCombineMaxSplits = 256, kCombineMaxG = 8;
 // One block per (query row, query head), 128 threads.  Split s holds, for each of the G
 // heads of its KV group, the unnormalised output o_s (hd floats) followed by its running
 // max m_s (log2 units) and sum l_s.  Weights w_s = 2^(m_s - max m); out = sum w_s o_s /
 // sum w_s l_s.  Every load of the first 32 splits (o_s[e] per thread and output dim,
-// m_s and l_s per thread and split) is issued before the block reductions, so a launch
-// with up to 32 splits waits on one memory round trip.
+// m_s and l_s per lane and split) is issued before any arithmetic, so a launch with up
+// to 32 splits waits on one memory round trip.
 constexpr int kCombinePre = 32;
 // The difference correction of the merged rows (RowsAttn's diff_* fields).
 struct DiffOut {
@@ -1714,55 +1711,44 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
                                                            int HD, int H, int Hkv, u16* __restrict__ out,
                                                            bool packed, DiffOut df) {
     if (LIVE && *df.live == 0) return;  // no sequence left in the loops
-    __shared__ float wts[kCombineMaxSplits];
-    __shared__ float red[2];
     const long long qrow = blockIdx.x;
     const int head = blockIdx.y, g = head / G, hh = head % G;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x;
     const long long stride = (long long)G * (HD + 2);
     const float* ph = part + (qrow * Hkv + g) * (long long)n_splits * stride + hh * (HD + 2);
     const bool has_e = tid < HD;
     const float* pe = ph + (has_e ? tid : 0);
+    const int lane = tid & 63;
+    // Each wave forms the split weights by itself, with no exchange through LDS and no
+    // barrier: lane l reads the (m, l) pairs of splits l, l + 64, ..., the wave reduces
+    // the maximum and the weighted sum, and the weights of splits below 64 are read back
+    // from their lanes.  The partial outputs of the thread's own element are loaded first.
     float v[kCombinePre];
 #pragma unroll
     for (int u = 0; u < kCombinePre; ++u) v[u] = (has_e && u < n_splits) ? pe[u * stride] : 0.f;
-    float m_own = -INFINITY, l_own = 0.f;
-    if (tid < n_splits) {
-        m_own = ph[tid * stride + HD];
-        l_own = ph[tid * stride + HD + 1];
-    }
-    float mx = m_own;
-    for (int s = tid + 128; s < n_splits; s += 128) mx = fmaxf(mx, ph[s * stride + HD]);
-    mx = wave_max(mx);
-    if (lane == 0) red[w] = mx;
-    __syncthreads();
-    const float M = fmaxf(red[0], red[1]);
-    __syncthreads();
-    float l = 0.f;
-    if (tid < n_splits) {
-        const float wgt = (m_own == -INFINITY) ? 0.f : exp2f(m_own - M);
-        wts[tid] = wgt;
-        l = wgt * l_own;
-    }
-    for (int s = tid + 128; s < n_splits; s += 128) {
-        const float ms = ph[s * stride + HD];
-        const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-        wts[s] = wgt;
-        l += wgt * ph[s * stride + HD + 1];
-    }
-    l = wave_sum(l);
-    if (lane == 0) red[w] = l;
-    __syncthreads();
-    const float inv = 1.0f / (red[0] + red[1]);
+    const float m_own = lane < n_splits ? ph[lane * stride + HD] : -INFINITY;
+    const float l_own = lane < n_splits ? ph[lane * stride + HD + 1] : 0.f;
+    float mloc = m_own;
+    for (int s = lane + 64; s < n_splits; s += 64) mloc = fmaxf(mloc, ph[s * stride + HD]);
+    const float M = wave_max(mloc);
+    auto weight = [&](float m_s) { return (m_s == -INFINITY) ? 0.f : exp2f(m_s - M); };
+    const float w_own = weight(m_own);
+    float lloc = w_own * l_own;
+    for (int s = lane + 64; s < n_splits; s += 64) lloc += weight(ph[s * stride + HD]) * ph[s * stride + HD + 1];
+    const float inv = 1.0f / wave_sum(lloc);
+    auto split_weight = [&](int s) {
+        return s < 64 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_own), s))
+                      : weight(ph[s * stride + HD]);
+    };
     for (int e = tid; e < HD; e += 128) {
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         if (e == tid) {
 #pragma unroll
             for (int u = 0; u < kCombinePre; ++u)
-                if (u < n_splits) acc[u & 3] += wts[u] * v[u];
-            for (int s = kCombinePre; s < n_splits; ++s) acc[s & 3] += wts[s] * ph[s * stride + e];
+                if (u < n_splits) acc[u & 3] += split_weight(u) * v[u];
+            for (int s = kCombinePre; s < n_splits; ++s) acc[s & 3] += split_weight(s) * ph[s * stride + e];
         } else {
-            for (int s = 0; s < n_splits; ++s) acc[s & 3] += wts[s] * ph[s * stride + e];
+            for (int s = 0; s < n_splits; ++s) acc[s & 3] += split_weight(s) * ph[s * stride + e];
         }
         const float o = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * inv;
         const int k = head * HD + e;
