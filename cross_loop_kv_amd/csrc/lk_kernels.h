@@ -272,9 +272,10 @@ struct RowsAttn {
     int seg_split;
     // Decode (one row per sequence at position *dpos) with fuse_kv: q comes from the
     // float32 projections qkv [B][(H + 2 Hkv) hd], rotated here with rope_cs
-    // ([hd/2][cos, sin] of the position), and the workgroup whose keys include the new
-    // position first writes that token's K/V row as kvw describes (the work a separate
-    // rope_kv_write launch does otherwise).
+    // ([hd/2][cos, sin] of the position), and that token's K/V row is written as kvw
+    // describes (the work a separate rope_kv_write launch does otherwise): by the
+    // new-key split below when it is on, else first by the workgroup whose keys include
+    // the new position.
     const float* qkv;
     const float* rope_cs;
     KVWrite kvw;
