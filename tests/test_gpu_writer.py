@@ -290,3 +290,40 @@ def test_writer_flags_elements_outside_float16_range():
         log(f"  range flag: {name}")
         assert write(x) == flagged, name
     assert not st.out_of_f16_range(), "the clearing reads left the flag lowered"
+
+
+def test_decode_flags_a_loop_two_query_outside_float16_range():
+    """The range flag in a decode step's loops >= 2, where the attention launch rotates q
+    itself (its new-key split checks every rotated q element of its KV-head group).
+    One shared-layer weight W_q[i, j] = 8000 and a loop-2 embedding of 1000 in model
+    dimension j: at loop 1 RMSNorm keeps that input near 1 in magnitude (q_i about
+    8000 · |a_j|, inside the float16 range); at loop 2 the embedding dominates the row,
+    a_j is about sqrt(d) and q_i about 1.8e5, whose rotation leaves at least
+    1.8e5 / sqrt(2) in one of the pair's two elements.  K and V stay small, and so does
+    the residual stream: the decode products take it times the norm gain in float16, so
+    an element above 65504 there (an embedding of 1e6, say) makes K and V non-finite,
+    which raises the flag on its own.  The prefill's loop 2 raises the flag through the
+    store writer; after it is cleared, one decode step must raise it again.  The same
+    model without the large weight leaves it lowered."""
+    s = _shape(n_loops=2)
+    lz = I.Lazy(mode="lazy", rho=0.3, top_s=16, window=8, base_bits=8, res_bits=4)
+    Bn, T, j, i = 2, 32, 5, 3
+    ids = torch.from_numpy(I.gen_prompt_ids(s, Bn, T))
+    dec = torch.from_numpy(I.gen_decode_ids(s, Bn, 1))
+    for big_q in (True, False):
+        W = I.gen_weights(s, seed=1)
+        W["loop_emb"][1, j] = 1000.0
+        if big_q:
+            W["layers"][0]["wq"][i, j] = 8000.0
+        model = B.LoopedModel(s, lz, W)
+        st = model.store(Bn, T, T + 4)
+        model.prefill(st, ids)
+        torch.cuda.synchronize()
+        assert st.out_of_f16_range(clear=True) == big_q, "prefill loop 2"
+        assert not st.out_of_f16_range(), "the clearing read left the flag lowered"
+        model.decode(st, dec[0])
+        torch.cuda.synchronize()
+        log(f"  decode range flag with W_q[{i}, {j}] {'= 8000' if big_q else 'unchanged'}")
+        assert st.out_of_f16_range() == big_q, "decode loop 2"
+        st = None
+        model.close()
