@@ -25,3 +25,16 @@ def test_decode_tokens_cover_the_timed_run_and_the_baselines(warmup, steps, base
     assert n >= warmup + steps
     assert n >= b.BASELINE_WARMUP + baseline_steps
     assert b.decode_tokens_needed(warmup, steps, baseline_steps, baselines=False) == warmup + steps
+
+
+def test_committed_traffic_summary_is_of_the_current_kernel_source():
+    """The bench line's roofline traffic comes from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary of the loop-1 decode attention, which records a hash of the
+    source that kernel is built from; the summary must be of the current source (else
+    the bench reports the traffic as null until the counters are taken again)."""
+    b = _bench()
+    t = b.measured_traffic("deep_48x4_b8_ctx32k")
+    assert t is not None, "re-take the counters: the kernel source changed since they were taken"
+    # within 2 % of the algorithmic bytes at the summary's context (8 x 4 x 32771 x 272 + q)
+    alg = 8 * 4 * 32771 * 272 + 8 * 16 * 128 * 2
+    assert alg <= t <= 1.02 * alg
